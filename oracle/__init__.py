@@ -1,0 +1,201 @@
+"""CPU oracle (test infrastructure only).
+
+Python face of oracle/oracle.c, a plain fp64 C statement of the sparse
+embedding + DIN attention forward.  Only tests, the smoke check and the
+benchmark's CPU-baseline leg may import this package; the HIP library never
+does, and this package imports nothing from it.
+
+Inputs are numpy arrays from the seeded generator (synth); results are fp64.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+P64 = C.POINTER(C.c_int64)
+P32 = C.POINTER(C.c_int32)
+PF = C.POINTER(C.c_float)
+PD = C.POINTER(C.c_double)
+
+
+class OrcTable(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("pad_", C.c_int32), ("rows", C.c_int64),
+                ("values", PF), ("sorted_keys", P64), ("sorted_slots", P64),
+                ("count", C.c_int64)]
+
+
+def build(src: str = SRC, out: str = LIB) -> str:
+    """gcc -O2, no fast-math: IEEE fp64 in source order."""
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
+           "-Wall", "-Wextra", "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _ptr(a: np.ndarray, t):
+    return a.ctypes.data_as(t)
+
+
+class Oracle:
+    def __init__(self, path: Optional[str] = None):
+        path = path or LIB
+        if path == LIB and (not os.path.exists(LIB) or
+                            os.path.getmtime(LIB) < os.path.getmtime(SRC)):
+            build()
+        self.lib = L = C.CDLL(path)
+        L.orc_lengths_to_offsets.argtypes = [P32, C.c_int64, P64]
+        L.orc_lengths_to_offsets.restype = None
+        L.orc_floor_mod.argtypes = [C.c_int64, C.c_int64]
+        L.orc_floor_mod.restype = C.c_int64
+        L.orc_hash_index.argtypes = [P64, C.c_int64, P64, P64]
+        L.orc_hash_index.restype = C.c_int64
+        L.orc_hash_find.argtypes = [P64, P64, C.c_int64, C.c_int64]
+        L.orc_hash_find.restype = C.c_int64
+        L.orc_resolve_many.argtypes = [C.POINTER(OrcTable), P64, C.c_int64, P64]
+        L.orc_resolve_many.restype = None
+        L.orc_embbag.argtypes = [C.c_int32, C.c_int64, C.POINTER(OrcTable), P64, P32, P64,
+                                 P64, C.c_int64, PD]
+        L.orc_embbag.restype = None
+        L.orc_din.argtypes = [C.POINTER(OrcTable), P64, C.c_int64, P64, P32, C.c_int32,
+                              PD, PD, PD, PD, PD, PD, C.c_double, P64, C.c_int64, PD, PD, PD]
+        L.orc_din.restype = None
+        self._keep = []
+
+    # -- bookkeeping ---------------------------------------------------------
+    def lengths_to_offsets(self, lengths: np.ndarray) -> np.ndarray:
+        lengths = np.ascontiguousarray(lengths, dtype=np.int32)
+        out = np.empty(lengths.size + 1, dtype=np.int64)
+        self.lib.orc_lengths_to_offsets(_ptr(lengths, P32), lengths.size, _ptr(out, P64))
+        return out
+
+    def floor_mod(self, raw: int, n: int) -> int:
+        return int(self.lib.orc_floor_mod(int(raw), int(n)))
+
+    # -- tables --------------------------------------------------------------
+    def table(self, tab: dict) -> OrcTable:
+        """Wrap one generator table (dict from synth) for the C side."""
+        vals = np.ascontiguousarray(tab["values"], dtype=np.float32)
+        t = OrcTable()
+        t.rows = int(tab["rows"])
+        t.values = _ptr(vals, PF)
+        keep = [vals]
+        if tab["kind"] == "hash":
+            keys = np.ascontiguousarray(tab["keys"], dtype=np.int64)
+            sk = np.empty(keys.size, dtype=np.int64)
+            sl = np.empty(keys.size, dtype=np.int64)
+            cnt = self.lib.orc_hash_index(_ptr(keys, P64), keys.size, _ptr(sk, P64), _ptr(sl, P64))
+            t.kind = 1
+            t.sorted_keys = _ptr(sk, P64)
+            t.sorted_slots = _ptr(sl, P64)
+            t.count = cnt
+            keep += [keys, sk, sl]
+        else:
+            t.kind = 0
+            t.count = 0
+        t._keep = keep
+        return t
+
+    def tables(self, tabs: Sequence[dict]):
+        arr = (OrcTable * len(tabs))()
+        keep = []
+        for i, tab in enumerate(tabs):
+            w = self.table(tab)
+            arr[i] = w
+            keep.append(w._keep)
+        arr._keep = keep
+        return arr
+
+    def resolve(self, tab: dict, raw: np.ndarray, wrapped=None) -> np.ndarray:
+        raw = np.ascontiguousarray(raw, dtype=np.int64)
+        t = wrapped if wrapped is not None else self.table(tab)
+        out = np.empty(raw.size, dtype=np.int64)
+        self.lib.orc_resolve_many(C.byref(t), _ptr(raw, P64), raw.size, _ptr(out, P64))
+        return out
+
+    # -- forward pieces ------------------------------------------------------
+    def embbag(self, tabs, B: int, values, lengths, offsets, samples=None, wrapped=None):
+        T = len(tabs)
+        values = np.ascontiguousarray(values, dtype=np.int64)
+        lengths = np.ascontiguousarray(lengths, dtype=np.int32)
+        offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+        samples = np.arange(B, dtype=np.int64) if samples is None else \
+            np.ascontiguousarray(samples, dtype=np.int64)
+        arr = wrapped if wrapped is not None else self.tables(tabs)
+        out = np.empty((samples.size, T * 16), dtype=np.float64)
+        self.lib.orc_embbag(T, B, arr, _ptr(values, P64), _ptr(lengths, P32),
+                            _ptr(offsets, P64), _ptr(samples, P64), samples.size,
+                            _ptr(out, PD))
+        return out
+
+    def din(self, seq_tabs, seq_values, seq_stride, seq_offsets, seq_lengths, max_len,
+            query, w1, b1, w2, b2, w3, b3, samples=None, wrapped=None,
+            want_scores=False):
+        """query: [ns][48] fp64 for the sampled samples (in `samples` order)."""
+        seq_values = np.ascontiguousarray(seq_values, dtype=np.int64)
+        seq_offsets = np.ascontiguousarray(seq_offsets, dtype=np.int64)
+        seq_lengths = np.ascontiguousarray(seq_lengths, dtype=np.int32)
+        B = seq_lengths.size
+        samples = np.arange(B, dtype=np.int64) if samples is None else \
+            np.ascontiguousarray(samples, dtype=np.int64)
+        q = np.ascontiguousarray(query, dtype=np.float64).reshape(samples.size, 48)
+        d = [np.ascontiguousarray(a, dtype=np.float64) for a in (w1, b1, w2, b2, w3)]
+        assert d[0].shape == (256, 192) and d[2].shape == (64, 256)
+        arr = wrapped if wrapped is not None else self.tables(seq_tabs)
+        att = np.empty((samples.size, 48), dtype=np.float64)
+        sc = np.empty((samples.size, max(max_len, 1)), dtype=np.float64) if want_scores else None
+        wt = np.empty((samples.size, max(max_len, 1)), dtype=np.float64) if want_scores else None
+        self.lib.orc_din(arr, _ptr(seq_values, P64), int(seq_stride), _ptr(seq_offsets, P64),
+                         _ptr(seq_lengths, P32), int(max_len), _ptr(q, PD),
+                         _ptr(d[0], PD), _ptr(d[1], PD), _ptr(d[2], PD), _ptr(d[3], PD),
+                         _ptr(d[4], PD), float(b3), _ptr(samples, P64), samples.size,
+                         _ptr(att, PD), _ptr(sc, PD) if sc is not None else None,
+                         _ptr(wt, PD) if wt is not None else None)
+        if want_scores:
+            return att, sc, wt
+        return att
+
+
+_DEFAULT: Optional[Oracle] = None
+
+
+def get() -> Oracle:
+    global _DEFAULT
+    if _DEFAULT is None:
+        _DEFAULT = Oracle()
+    return _DEFAULT
+
+
+# ---------------------------------------------------------------------------
+# Whole-forward convenience used by tests and the CPU-baseline leg.
+def forward(model, batch, samples=None, orc: Optional[Oracle] = None, want_scores=False):
+    """Oracle forward for one generator batch: returns dict with offsets,
+    pooled [ns, 256], att [ns, 48] (+ scores/weights) for `samples`."""
+    import synth
+    orc = orc or get()
+    B = batch.B
+    samples = np.arange(B, dtype=np.int64) if samples is None else np.asarray(samples, np.int64)
+    offsets = orc.lengths_to_offsets(batch.lengths)
+    wrapped = orc.tables(model.tables)
+    pooled = orc.embbag(model.tables, B, batch.values, batch.lengths, offsets, samples,
+                        wrapped=wrapped)
+    q = np.concatenate([pooled[:, c:c + 16] for c in synth.QUERY_COL], axis=1)
+    seq_off = orc.lengths_to_offsets(batch.seq_lengths)[:-1]
+    seq_tabs = [model.tables[k] for k in synth.SEQ_KEYS]
+    seq_wrapped = orc.tables(seq_tabs)
+    r = orc.din(seq_tabs, batch.seq_values, batch.seq_stride, seq_off, batch.seq_lengths,
+                model.cfg.max_len, q, model.w1, model.b1, model.w2, model.b2, model.w3,
+                model.b3, samples=samples, wrapped=seq_wrapped, want_scores=want_scores)
+    out = dict(offsets=offsets, pooled=pooled, query=q)
+    if want_scores:
+        out["att"], out["scores"], out["weights"] = r
+    else:
+        out["att"] = r
+    return out

@@ -1,0 +1,217 @@
+/*
+ * CPU oracle for the sparse embedding + DIN attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously correct
+ * statement of what the forward computes, in fp64.  Only the tests, the smoke
+ * check and the benchmark's CPU-baseline leg may load it.  It shares no code,
+ * header, table or constant with the HIP library, and the library never calls
+ * it.
+ *
+ * Pages followed (title, section):
+ *   [P1] "MultiTowerDIN：当前现状分析"
+ *        §2   id features arrive as (values, lengths) and become a
+ *             KeyedJaggedTensor
+ *        §3   num_buckets: a [N,16] table, row = raw_id % num_buckets
+ *        §4.2 DIN attention: cat [q, s, q-s, q*s] on the last dim, attn MLP
+ *             (hidden 256, 64), linear to one score, mask + softmax, weighted
+ *             sum of the sequence
+ *        §4.4 compute graph: pooled deep features; query [B,48]; sequence
+ *             [B,100,48]; attn input [B,100,192]; output [B,48]
+ *   [P2] "MultiTowerDIN：集成 DynamicEmb"
+ *        §3.2 lookup is an O(1) open-addressing hash table; an unseen id gives
+ *             the constant 0 vector
+ *        §4.3 unseen id -> not in the table -> zero embedding
+ *   [P3] DLRM essay (wmrh.cn/news/12459) §3.2: EmbeddingBag pools each bag
+ *        (mode sum)
+ *
+ * Readings where the pages are silent (each also listed in the design notes):
+ *   - '%' on a negative id is the floor modulo (result in [0, N)), the
+ *     semantics of the Python pseudo-code the page prints.
+ *   - pooling is a sum; an empty bag pools to 0.
+ *   - ReLU after the 256- and 64-wide layers, none after the score layer;
+ *     biases on all three layers.
+ *   - the mask has -inf semantics: masked positions get weight exactly 0; a
+ *     sample with no positions gets output 0.
+ *   - only the first max_len positions of a longer sequence are used.
+ *   - no softmax temperature or 1/sqrt(d); max-subtracted for range.
+ *   - W1 columns: 0-47 q, 48-95 s, 96-143 q-s, 144-191 q*s; inside each block
+ *     the sub-features adgroup, cate, brand, 16 each.
+ *   - hash lookup: the key is the raw id; a key is present iff some slot holds
+ *     it.  The oracle finds it by scanning every slot once (sorted index), so
+ *     it depends on no hash function or probe order.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_DIM 16
+#define ORC_EMPTY_KEY ((int64_t)-1)
+
+/* ---- jagged bookkeeping ([P1] §2: values + lengths -> offsets) ---------- */
+void orc_lengths_to_offsets(const int32_t* lengths, int64_t n, int64_t* offsets) {
+    offsets[0] = 0;
+    for (int64_t i = 0; i < n; ++i) offsets[i + 1] = offsets[i] + (int64_t)lengths[i];
+}
+
+/* ---- direct index ([P1] §3: row = raw_id % num_buckets, floor modulo) --- */
+int64_t orc_floor_mod(int64_t raw, int64_t n) {
+    int64_t r = raw % n;           /* C truncates toward zero: |r| < n */
+    if (r < 0) r += n;
+    return r;
+}
+
+/* ---- hash index ([P2] §3.2, §4.3) ---------------------------------------
+ * Scan every slot; collect (key, slot) for occupied slots; sort by key.  A
+ * lookup is a binary search in that list: present -> its slot, else -1.     */
+typedef struct { int64_t key, slot; } orc_pair;
+
+static int orc_pair_cmp(const void* a, const void* b) {
+    int64_t x = ((const orc_pair*)a)->key, y = ((const orc_pair*)b)->key;
+    return (x > y) - (x < y);
+}
+
+/* Fills sorted_keys/sorted_slots (each of room >= capacity); returns count. */
+int64_t orc_hash_index(const int64_t* slot_keys, int64_t capacity,
+                       int64_t* sorted_keys, int64_t* sorted_slots) {
+    orc_pair* p = (orc_pair*)malloc(sizeof(orc_pair) * (size_t)(capacity > 0 ? capacity : 1));
+    int64_t n = 0;
+    for (int64_t s = 0; s < capacity; ++s)
+        if (slot_keys[s] != ORC_EMPTY_KEY) { p[n].key = slot_keys[s]; p[n].slot = s; ++n; }
+    qsort(p, (size_t)n, sizeof(orc_pair), orc_pair_cmp);
+    for (int64_t i = 0; i < n; ++i) { sorted_keys[i] = p[i].key; sorted_slots[i] = p[i].slot; }
+    free(p);
+    return n;
+}
+
+int64_t orc_hash_find(const int64_t* sorted_keys, const int64_t* sorted_slots,
+                      int64_t count, int64_t key) {
+    int64_t lo = 0, hi = count;               /* search [lo, hi) */
+    while (lo < hi) {
+        int64_t mid = lo + (hi - lo) / 2;
+        if (sorted_keys[mid] < key) lo = mid + 1; else hi = mid;
+    }
+    return (lo < count && sorted_keys[lo] == key) ? sorted_slots[lo] : -1;
+}
+
+/* One table as the oracle sees it. */
+typedef struct {
+    int32_t kind;                 /* 0 direct, 1 hash */
+    int32_t pad_;
+    int64_t rows;                 /* direct: num_buckets; hash: capacity */
+    const float* values;          /* [rows][16] */
+    const int64_t* sorted_keys;   /* hash: index built by orc_hash_index */
+    const int64_t* sorted_slots;
+    int64_t count;
+} orc_table;
+
+/* Row of a raw id in a table: direct -> floor mod; hash -> slot or -1. */
+int64_t orc_resolve(const orc_table* t, int64_t raw) {
+    if (t->kind == 0) return orc_floor_mod(raw, t->rows);
+    return orc_hash_find(t->sorted_keys, t->sorted_slots, t->count, raw);
+}
+
+void orc_resolve_many(const orc_table* t, const int64_t* raw, int64_t n, int64_t* rows) {
+    for (int64_t i = 0; i < n; ++i) rows[i] = orc_resolve(t, raw[i]);
+}
+
+/* Embedding of a raw id: the table row, or the zero vector on a hash miss. */
+static void orc_emb(const orc_table* t, int64_t raw, double* out16) {
+    int64_t r = orc_resolve(t, raw);
+    for (int d = 0; d < ORC_DIM; ++d) out16[d] = r < 0 ? 0.0 : (double)t->values[r * ORC_DIM + d];
+}
+
+/* ---- sum-pooled embedding bags ([P1] §3, §4.4; [P3] §3.2) ---------------
+ * pooled[s][16k + d] = sum over the ids of bag (k, b) of table k's row[d],
+ * for b = samples[s]; bag (k, b) is values[offsets[k*B+b] .. + lengths[k*B+b]).
+ * An empty bag pools to 0.                                                  */
+void orc_embbag(int32_t T, int64_t B, const orc_table* tables,
+                const int64_t* values, const int32_t* lengths, const int64_t* offsets,
+                const int64_t* samples, int64_t ns, double* pooled) {
+    for (int64_t s = 0; s < ns; ++s) {
+        int64_t b = samples[s];
+        for (int32_t k = 0; k < T; ++k) {
+            int64_t bag = (int64_t)k * B + b;
+            double acc[ORC_DIM];
+            for (int d = 0; d < ORC_DIM; ++d) acc[d] = 0.0;
+            for (int64_t i = 0; i < lengths[bag]; ++i) {
+                int64_t r = orc_resolve(&tables[k], values[offsets[bag] + i]);
+                if (r < 0) continue;                 /* hash miss: the zero vector */
+                for (int d = 0; d < ORC_DIM; ++d) acc[d] += (double)tables[k].values[r * ORC_DIM + d];
+            }
+            for (int d = 0; d < ORC_DIM; ++d) pooled[s * (int64_t)T * ORC_DIM + k * ORC_DIM + d] = acc[d];
+        }
+    }
+}
+
+/* ---- DIN target attention ([P1] §4.2, §4.4) -----------------------------
+ * For sample b = samples[s], with L = min(seq_lengths[b], max_len):
+ *   s_j   = rows of the three sub-features at position j (48 values)
+ *   x_j   = [q, s_j, q - s_j, q * s_j]                    (192)
+ *   h1    = relu(W1 x_j + b1)   W1 [256][192]
+ *   h2    = relu(W2 h1 + b2)    W2 [64][256]
+ *   e_j   = w3 . h2 + b3
+ *   p_j   = exp(e_j - max e) / sum_k exp(e_k - max e)
+ *   att   = sum_j p_j s_j                                  (48)
+ * L = 0 gives att = 0.  query[s] is sample b's 48-value query.
+ * scores / weights (optional, [ns][max_len]) receive e_j and p_j.          */
+void orc_din(const orc_table* seq_tables /* 3: adgroup, cate, brand */,
+             const int64_t* seq_values, int64_t seq_stride,
+             const int64_t* seq_offsets, const int32_t* seq_lengths, int32_t max_len,
+             const double* query,
+             const double* w1, const double* b1, const double* w2, const double* b2,
+             const double* w3, double b3,
+             const int64_t* samples, int64_t ns,
+             double* att, double* scores, double* weights) {
+    double* sj = (double*)malloc(sizeof(double) * 48 * (size_t)(max_len > 0 ? max_len : 1));
+    double* e = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    double x[192], h1[256], h2[64];
+    for (int64_t s = 0; s < ns; ++s) {
+        int64_t b = samples[s];
+        int64_t L = seq_lengths[b] < max_len ? seq_lengths[b] : max_len;
+        const double* q = query + s * 48;
+        double* out = att + s * 48;
+        if (scores) for (int j = 0; j < max_len; ++j) scores[s * max_len + j] = 0.0;
+        if (weights) for (int j = 0; j < max_len; ++j) weights[s * max_len + j] = 0.0;
+        if (L <= 0) { for (int c = 0; c < 48; ++c) out[c] = 0.0; continue; }
+        for (int64_t j = 0; j < L; ++j) {
+            for (int f = 0; f < 3; ++f) {
+                int64_t raw = seq_values[f * seq_stride + seq_offsets[b] + j];
+                orc_emb(&seq_tables[f], raw, sj + j * 48 + f * 16);
+            }
+            for (int c = 0; c < 48; ++c) {
+                double qc = q[c], sc = sj[j * 48 + c];
+                x[c] = qc;
+                x[48 + c] = sc;
+                x[96 + c] = qc - sc;
+                x[144 + c] = qc * sc;
+            }
+            for (int o = 0; o < 256; ++o) {
+                double a = b1[o];
+                for (int i = 0; i < 192; ++i) a += w1[o * 192 + i] * x[i];
+                h1[o] = a > 0.0 ? a : 0.0;
+            }
+            for (int o = 0; o < 64; ++o) {
+                double a = b2[o];
+                for (int i = 0; i < 256; ++i) a += w2[o * 256 + i] * h1[i];
+                h2[o] = a > 0.0 ? a : 0.0;
+            }
+            double a = b3;
+            for (int i = 0; i < 64; ++i) a += w3[i] * h2[i];
+            e[j] = a;
+        }
+        double m = e[0];
+        for (int64_t j = 1; j < L; ++j) if (e[j] > m) m = e[j];
+        double den = 0.0;
+        for (int64_t j = 0; j < L; ++j) den += exp(e[j] - m);
+        for (int c = 0; c < 48; ++c) out[c] = 0.0;
+        for (int64_t j = 0; j < L; ++j) {
+            double p = exp(e[j] - m) / den;
+            for (int c = 0; c < 48; ++c) out[c] += p * sj[j * 48 + c];
+            if (scores) scores[s * max_len + j] = e[j];
+            if (weights) weights[s * max_len + j] = p;
+        }
+    }
+    free(sj);
+    free(e);
+}

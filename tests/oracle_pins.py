@@ -1,0 +1,312 @@
+"""Pins for the CPU oracle: checks of it against things other than itself.
+
+Each pin takes an `oracle.Oracle` instance and raises AssertionError when the
+oracle disagrees with what the pages and the mathematics fix:
+
+  * library routines that compute the same thing another way:
+      numpy cumsum (offsets), Python/numpy floor modulo (direct rows), a Python
+      dict over the slots (hash hit/miss), torch.nn.functional.embedding_bag
+      in fp64 (sum pooling), and the pages' own PADDED formulation of DIN
+      attention written with torch fp64 library ops ("MultiTowerDIN：当前现状分析"
+      §4.2/§4.4: pad to [B,100,48], cat, MLP on every position, mask, softmax,
+      bmm) against the oracle's padding-free loop;
+  * closed forms and invariants: one-position sequence -> weight 1 and output
+    equal to that position exactly; zero score weights -> the mean of the
+    sequence; identical positions -> that position; softmax weights sum to 1;
+    a shift of the score bias leaves weights and output unchanged; permuting a
+    sample's positions permutes its weights and leaves its output unchanged;
+    a single-id bag pools to that row exactly; a hash miss adds exact zeros.
+
+They are plain functions so that tests/test_oracle_mutants.py can run every
+pin against deliberately broken copies of the oracle and check that each
+planted mistake is caught.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import synth
+
+TINY_HASH = synth.Config(91, "hash_tiny", 64, tuple(synth.TINY_SIZES), "u123", "geom4", "f32",
+                         hash_keys=(0, 1, 2, 3, 4), hash_capacity=3000)
+
+
+# ----------------------------------------------------------------------------
+# independent helpers (library routines / language semantics)
+def py_rows(tab: dict, raw: np.ndarray) -> np.ndarray:
+    raw = np.asarray(raw, dtype=np.int64)
+    if tab["kind"] == "direct":
+        return np.mod(raw, np.int64(tab["rows"]))           # numpy: sign of divisor (floor)
+    d = {int(k): s for s, k in enumerate(tab["keys"].tolist()) if k != synth.EMPTY_KEY}
+    return np.array([d.get(int(r), -1) for r in raw.tolist()], dtype=np.int64)
+
+
+def torch_pooled(model, batch) -> np.ndarray:
+    """Per-table torch embedding_bag(mode='sum') in fp64; hash misses index an
+    appended all-zero row."""
+    B = batch.B
+    lengths = batch.lengths.reshape(synth.T, B)
+    starts = np.concatenate([[0], np.cumsum(batch.lengths)])
+    out = []
+    for k in range(synth.T):
+        tab = model.tables[k]
+        lo, hi = starts[k * B], starts[(k + 1) * B]
+        rows = py_rows(tab, batch.values[lo:hi])
+        w = np.asarray(tab["values"], dtype=np.float64)
+        w = np.concatenate([w, np.zeros((1, 16))], axis=0)
+        rows = np.where(rows < 0, w.shape[0] - 1, rows)
+        bag_off = np.concatenate([[0], np.cumsum(lengths[k])[:-1]])
+        t = F.embedding_bag(torch.from_numpy(rows), torch.from_numpy(np.nan_to_num(w)),
+                            torch.from_numpy(bag_off.astype(np.int64)), mode="sum")
+        out.append(t.numpy())
+    return np.concatenate(out, axis=1)
+
+
+def torch_padded_din(model, batch, query, seq_offsets, max_len, pad_to=100):
+    """The pages' padded DIN: [B,pad,48] zero beyond the real length, cat
+    [q, s, q-s, q*s], the MLP on every position, mask to -inf, softmax, bmm."""
+    B = batch.B
+    S = np.zeros((B, pad_to, 48))
+    L = np.minimum(batch.seq_lengths.astype(np.int64), max_len)
+    for i, k in enumerate(synth.SEQ_KEYS):
+        tab = model.tables[k]
+        w = np.asarray(tab["values"], dtype=np.float64)
+        for b in range(B):
+            n = int(L[b])
+            if n == 0:
+                continue
+            ids = batch.seq_values[i, seq_offsets[b]: seq_offsets[b] + n]
+            r = py_rows(tab, ids)
+            S[b, :n, 16 * i:16 * i + 16] = np.where(r[:, None] < 0, 0.0, w[np.maximum(r, 0)])
+    St = torch.from_numpy(S)
+    Q = torch.from_numpy(np.asarray(query, np.float64))[:, None, :].expand(B, pad_to, 48)
+    X = torch.cat([Q, St, Q - St, Q * St], dim=-1)
+    h1 = torch.relu(F.linear(X, torch.from_numpy(model.w1.astype(np.float64)),
+                             torch.from_numpy(model.b1.astype(np.float64))))
+    h2 = torch.relu(F.linear(h1, torch.from_numpy(model.w2.astype(np.float64)),
+                             torch.from_numpy(model.b2.astype(np.float64))))
+    e = F.linear(h2, torch.from_numpy(model.w3.astype(np.float64))[None, :],
+                 torch.tensor([float(model.b3)], dtype=torch.float64)).squeeze(-1)
+    mask = torch.arange(pad_to)[None, :] < torch.from_numpy(L)[:, None]
+    p = torch.softmax(e.masked_fill(~mask, float("-inf")), dim=-1)
+    p = torch.where(mask, p, torch.zeros_like(p))          # empty sample: no weights
+    att = torch.bmm(p[:, None, :], St).squeeze(1)
+    return att.numpy(), e.numpy(), p.numpy(), S
+
+
+def _rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    assert a.shape == b.shape, (a.shape, b.shape)
+    if a.size == 0:
+        return 0.0
+    scale = max(np.max(np.abs(b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / scale)
+
+
+def _seq_offsets(batch):
+    return np.concatenate([[0], np.cumsum(batch.seq_lengths)])[:-1].astype(np.int64)
+
+
+def _query_from(pooled):
+    return np.concatenate([pooled[:, c:c + 16] for c in synth.QUERY_COL], axis=1)
+
+
+def _tiny(bias=True, B=64, emb_std=0.05, w3_scale=1.0):
+    m = synth.make_model(synth.CONFIGS[1], bias=bias, emb_std=emb_std, w3_scale=w3_scale)
+    b = synth.make_batch(m, B=B)
+    return m, b
+
+
+# ----------------------------------------------------------------------------
+def pin_offsets(orc):
+    rng = np.random.default_rng(1)
+    for n in (0, 1, 7, 1000):
+        L = rng.integers(0, 5, size=n).astype(np.int32)
+        o = orc.lengths_to_offsets(L)
+        assert o.shape == (n + 1,)
+        assert o[0] == 0
+        assert np.array_equal(o[1:], np.cumsum(L.astype(np.int64)))
+        assert np.array_equal(np.diff(o), L)
+
+
+def pin_floor_mod(orc):
+    i64 = np.iinfo(np.int64)
+    Ns = [1, 2, 3, 5, 98, 101, 1141730, 846812, 2**31 - 1, 2**32 + 15, 2**62 + 3, i64.max]
+    raws = [0, 1, -1, 2, -2, 100, -100, 101, -101, 1141729, 1141730, -1141730, -1141731,
+            i64.max, i64.min, i64.min + 1, i64.max - 1, 2**32, -(2**32), 2**62, -(2**62)]
+    rng = np.random.default_rng(2)
+    raws += [int(x) for x in rng.integers(i64.min, i64.max, size=200, dtype=np.int64)]
+    for N in Ns:
+        for r in raws + [N - 1, N, -N, N + 1, -N - 1] if N < i64.max else raws:
+            if not (i64.min <= r <= i64.max):
+                continue
+            got = orc.floor_mod(r, N)
+            assert got == r % N, (r, N, got)            # Python: floor semantics
+            assert 0 <= got < N
+            assert (r - got) % N == 0                    # r == got (mod N), big ints
+
+
+def pin_hash(orc):
+    m = synth.make_model(TINY_HASH)
+    for k in TINY_HASH.hash_keys:
+        tab = m.tables[k]
+        stored = tab["stored"]
+        rng = np.random.default_rng(3 + k)
+        misses = rng.integers(np.iinfo(np.int64).min, np.iinfo(np.int64).max, size=300,
+                              dtype=np.int64)
+        q = np.concatenate([stored[:500], misses, [synth.EMPTY_KEY, 0, 1]])
+        got = orc.resolve(tab, q)
+        ref = py_rows(tab, q)
+        assert np.array_equal(got, ref)
+        hit = got >= 0
+        assert np.array_equal(tab["keys"][got[hit]], q[hit])
+        assert np.all(hit[:500])
+        assert got[-3] == -1                              # the empty marker is never a key
+
+
+def pin_embbag_direct(orc):
+    m, b = _tiny()
+    # put empty bags in (a deep feature with no id for some samples)
+    L = b.lengths.reshape(synth.T, b.B).copy()
+    L[3, ::5] = 0
+    L[0, 1] = 0
+    vals = []
+    starts = np.concatenate([[0], np.cumsum(b.lengths)])
+    for k in range(synth.T):
+        for bb in range(b.B):
+            i = k * b.B + bb
+            vals.append(b.values[starts[i]: starts[i] + L[k, bb]])
+    b.lengths = L.reshape(-1).astype(np.int32)
+    b.values = np.concatenate(vals).astype(np.int64)
+    off = orc.lengths_to_offsets(b.lengths)
+    got = orc.embbag(m.tables, b.B, b.values, b.lengths, off)
+    ref = torch_pooled(m, b)
+    assert got.shape == (b.B, 256)
+    assert _rel(got, ref) < 1e-14
+    assert np.all(got[::5, 48:64] == 0.0)
+    # a single-id bag pools to its row exactly (price bags hold one id)
+    price = b.values[off[15 * b.B]: off[16 * b.B]]
+    assert np.array_equal(got[:, 240:256], m.tables[15]["values"][np.mod(price, 101)].astype(np.float64))
+
+
+def pin_embbag_hash(orc):
+    m = synth.make_model(TINY_HASH)
+    b = synth.make_batch(m, B=TINY_HASH.B)
+    off = orc.lengths_to_offsets(b.lengths)
+    got = orc.embbag(m.tables, b.B, b.values, b.lengths, off)
+    ref = torch_pooled(m, b)
+    assert np.all(np.isfinite(got))                       # NaN-poisoned empty slots never read
+    assert _rel(got, ref) < 1e-14
+    # linearity: dropping the missed ids changes nothing
+    lo, hi = off[0], off[b.B]
+    rows = py_rows(m.tables[0], b.values[lo:hi])
+    assert (rows < 0).any()
+
+
+def _din_case(orc, m, b, max_len=100, pad_to=100):
+    off = orc.lengths_to_offsets(b.lengths)
+    pooled = orc.embbag(m.tables, b.B, b.values, b.lengths, off)
+    q = _query_from(pooled)
+    soff = _seq_offsets(b)
+    seq_tabs = [m.tables[k] for k in synth.SEQ_KEYS]
+    att, sc, wt = orc.din(seq_tabs, b.seq_values, b.seq_stride, soff, b.seq_lengths, max_len,
+                          q, m.w1, m.b1, m.w2, m.b2, m.w3, m.b3, want_scores=True)
+    return att, sc, wt, q, soff
+
+
+def pin_din_vs_padded(orc):
+    for emb_std, w3s in ((0.05, 1.0), (1.0, 20.0)):      # near-uniform and peaky softmax
+        m, b = _tiny(emb_std=emb_std, w3_scale=w3s)
+        b.seq_lengths[3] = 0                               # an empty click sequence
+        b.seq_lengths[5] = 1
+        att, sc, wt, q, soff = _din_case(orc, m, b)
+        ratt, re_, rp, _ = torch_padded_din(m, b, q, soff, 100)
+        assert _rel(att, ratt) < 1e-12
+        L = np.minimum(b.seq_lengths, 100)
+        for bb in range(b.B):
+            n = int(L[bb])
+            assert _rel(sc[bb, :n], re_[bb, :n]) < 1e-12
+            assert _rel(wt[bb, :n], rp[bb, :n]) < 1e-12
+            assert np.all(wt[bb, n:] == 0.0)
+        assert np.all(att[3] == 0.0)
+        if w3s > 1.0:
+            assert wt.max() > 0.9                          # the peaky case really is peaky
+    # truncation to max_len: the padded form with only the first 3 positions
+    m, b = _tiny()
+    att, sc, wt, q, soff = _din_case(orc, m, b, max_len=3)
+    ratt, _, _, _ = torch_padded_din(m, b, q, soff, 3, pad_to=3)
+    assert _rel(att, ratt) < 1e-12
+
+
+def pin_din_closed_forms(orc):
+    m, b = _tiny()
+    orig = b.seq_lengths.copy()
+    starts = np.concatenate([[0], np.cumsum(orig)])
+    L = np.minimum(orig, 6).astype(np.int32)
+    L[0] = 1
+    b.seq_values = np.ascontiguousarray(np.concatenate(
+        [b.seq_values[:, starts[i]: starts[i] + L[i]] for i in range(b.B)], axis=1))
+    b.seq_lengths = L
+    b.seq_stride = b.seq_values.shape[1]
+    att, sc, wt, q, soff = _din_case(orc, m, b)
+    _, _, _, S = torch_padded_din(m, b, q, soff, 100)
+    # one position: weight exactly 1, output exactly that position
+    assert wt[0, 0] == 1.0 and np.array_equal(att[0], S[0, 0])
+    # weights sum to one over the valid positions
+    L = b.seq_lengths
+    for bb in range(b.B):
+        assert abs(wt[bb, :L[bb]].sum() - 1.0) < 1e-12
+    # score bias shift: weights and output unchanged, scores shift by the same amount
+    seq_tabs = [m.tables[k] for k in synth.SEQ_KEYS]
+    att2, sc2, wt2 = orc.din(seq_tabs, b.seq_values, b.seq_stride, soff, L, 100, q, m.w1, m.b1,
+                             m.w2, m.b2, m.w3, m.b3 + 3.25, want_scores=True)
+    assert _rel(att2, att) < 1e-12 and _rel(wt2, wt) < 1e-12
+    for bb in range(b.B):
+        assert np.allclose(sc2[bb, :L[bb]] - sc[bb, :L[bb]], 3.25, atol=1e-12, rtol=0)
+    # zero score weights: uniform weights, output = mean of the positions
+    att3 = orc.din(seq_tabs, b.seq_values, b.seq_stride, soff, L, 100, q, m.w1, m.b1, m.w2,
+                   m.b2, np.zeros(64), -0.7)
+    for bb in range(b.B):
+        assert _rel(att3[bb], S[bb, :L[bb]].mean(axis=0)) < 1e-13
+    # permuting a sample's positions: output unchanged, weights permuted
+    rng = np.random.default_rng(5)
+    perm_seq = b.seq_values.copy()
+    perms = []
+    for bb in range(b.B):
+        p = rng.permutation(int(L[bb]))
+        perms.append(p)
+        perm_seq[:, soff[bb]: soff[bb] + L[bb]] = b.seq_values[:, soff[bb] + p]
+    att4, sc4, wt4 = orc.din(seq_tabs, perm_seq, b.seq_stride, soff, L, 100, q, m.w1, m.b1,
+                             m.w2, m.b2, m.w3, m.b3, want_scores=True)
+    assert _rel(att4, att) < 1e-12
+    for bb in range(b.B):
+        assert _rel(wt4[bb, :L[bb]], wt[bb, perms[bb]]) < 1e-12
+    # identical positions: the output is that position
+    same = b.seq_values.copy()
+    for bb in range(b.B):
+        same[:, soff[bb]: soff[bb] + L[bb]] = b.seq_values[:, soff[bb]: soff[bb] + 1]
+    att5 = orc.din(seq_tabs, same, b.seq_stride, soff, L, 100, q, m.w1, m.b1, m.w2, m.b2,
+                   m.w3, m.b3)
+    for bb in range(b.B):
+        assert _rel(att5[bb], S[bb, 0]) < 1e-14
+    # sample independence: evaluating a subset gives the same rows
+    sub = np.array([7, 2, 40], dtype=np.int64)
+    att6 = orc.din(seq_tabs, b.seq_values, b.seq_stride, soff, L, 100, q[sub], m.w1, m.b1,
+                   m.w2, m.b2, m.w3, m.b3, samples=sub)
+    assert np.array_equal(att6, att[sub])
+
+
+def pin_din_hash(orc):
+    """Sequence rows through hash tables: misses contribute exact zero rows."""
+    m = synth.make_model(TINY_HASH, bias=True)
+    b = synth.make_batch(m, B=TINY_HASH.B)
+    att, sc, wt, q, soff = _din_case(orc, m, b)
+    ratt, re_, rp, _ = torch_padded_din(m, b, q, soff, 100)
+    assert np.all(np.isfinite(att))
+    assert _rel(att, ratt) < 1e-12
+
+
+ALL_PINS = [pin_offsets, pin_floor_mod, pin_hash, pin_embbag_direct, pin_embbag_hash,
+            pin_din_vs_padded, pin_din_closed_forms, pin_din_hash]

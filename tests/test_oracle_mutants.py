@@ -1,0 +1,65 @@
+"""Plant plausible mistakes in copies of the CPU oracle (on the CPU only) and
+check that the pins catch every one: a dropped term, a wrong sign, a wrong or
+transposed index, a missing bias, cap or mask.  Each mutant must fail at least
+one pin in tests/oracle_pins.py.  (Equivalent mutants, such as taking the
+softmax shift from the minimum instead of the maximum, change no result and
+are not listed.)"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = [
+    ("offsets drop the running sum",
+     "offsets[i + 1] = offsets[i] + (int64_t)lengths[i];", "offsets[i + 1] = (int64_t)lengths[i];"),
+    ("floor mod takes |r|", "if (r < 0) r += n;", "if (r < 0) r = -r;"),
+    ("truncating mod", "if (r < 0) r += n;", "(void)n;"),
+    ("hash search off by one", "if (sorted_keys[mid] < key) lo = mid + 1;",
+     "if (sorted_keys[mid] <= key) lo = mid + 1;"),
+    ("hash miss reads slot 0", "if (r < 0) continue;                 /* hash miss",
+     "if (r < 0) r = 0;                 /* hash miss"),
+    ("pool from the wrong table", "int64_t r = orc_resolve(&tables[k], values[offsets[bag] + i]);",
+     "int64_t r = orc_resolve(&tables[0], values[offsets[bag] + i]);"),
+    ("pool drops the last id", "for (int64_t i = 0; i < lengths[bag]; ++i) {",
+     "for (int64_t i = 0; i + 1 < lengths[bag]; ++i) {"),
+    ("q - s sign flipped", "x[96 + c] = qc - sc;", "x[96 + c] = sc - qc;"),
+    ("q * s replaced by q + s", "x[144 + c] = qc * sc;", "x[144 + c] = qc + sc;"),
+    ("q and s blocks swapped", "x[c] = qc;\n                x[48 + c] = sc;",
+     "x[c] = sc;\n                x[48 + c] = qc;"),
+    ("W1 read transposed", "a += w1[o * 192 + i] * x[i];", "a += w1[i * 256 + o] * x[i];"),
+    ("b1 dropped", "double a = b1[o];", "double a = 0.0;"),
+    ("b2 dropped", "double a = b2[o];", "double a = 0.0;"),
+    ("b3 dropped", "double a = b3;", "double a = 0.0;"),
+    ("no ReLU after 64", "h2[o] = a > 0.0 ? a : 0.0;", "h2[o] = a;"),
+    ("no ReLU after 256", "h1[o] = a > 0.0 ? a : 0.0;", "h1[o] = a;"),
+    ("softmax denominator without max shift", "den += exp(e[j] - m);", "den += exp(e[j]);"),
+    ("cap one short of max_len", "int64_t L = seq_lengths[b] < max_len ? seq_lengths[b] : max_len;",
+     "int64_t L = seq_lengths[b] < max_len ? seq_lengths[b] : max_len - 1;"),
+    ("sub-feature rows reversed", "orc_emb(&seq_tables[f], raw, sj + j * 48 + f * 16);",
+     "orc_emb(&seq_tables[f], raw, sj + j * 48 + (2 - f) * 16);"),
+    ("sequence position off by one", "int64_t raw = seq_values[f * seq_stride + seq_offsets[b] + j];",
+     "int64_t raw = seq_values[f * seq_stride + seq_offsets[b] + (j > 0 ? j - 1 : 0)];"),
+    ("weighted sum uses x not s", "out[c] += p * sj[j * 48 + c];", "out[c] += p * x[c];"),
+    ("weights not normalised", "double p = exp(e[j] - m) / den;", "double p = exp(e[j] - m);"),
+]
+
+
+@pytest.mark.parametrize("name,orig,repl", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, orig, repl):
+    src = open(oracle.SRC).read()
+    assert src.count(orig) == 1, f"mutation site not unique/present: {orig!r}"
+    msrc = os.path.join(tmp_path, "oracle_mutant.c")
+    mlib = os.path.join(tmp_path, "liboracle_mutant.so")
+    with open(msrc, "w") as f:
+        f.write(src.replace(orig, repl))
+    oracle.build(msrc, mlib)
+    orc = oracle.Oracle(mlib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"mutant '{name}' passed every pin"
