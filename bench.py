@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark: samples/s of the sparse embedding + DIN attention forward on one
+MI355X, on seeded synthetic Taobao-shaped inputs.
+
+A step is one pass of the whole path over one batch already resident in HBM:
+lengths -> offsets, sequence plan, sum-pooled embedding bags (16 tables,
+3.14M rows), padding-free DIN attention (bf16 matrix cores, fp32 accumulate).
+Steps are replayed from HIP graphs (one per batch; 4 batches rotate so the
+L2 does not hold one batch's rows).  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--config 2]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "samples/s for embedding+DIN fwd at B=8192; HBM GB/s and MFMA util vs peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 matrix/vector
+
+# algorithmic bytes (what the method must move) and flops per unit
+EMB_BYTES_PER_ID = 8 + 64                  # raw id + one 64-byte row
+EMB_BYTES_PER_BAG = 4 + 8 + 64             # length + offset + pooled output
+DIN_BYTES_PER_POS = 3 * (8 + 64)           # three ids + three rows
+DIN_BYTES_PER_SAMPLE = 4 + 8 + 4 + 192 + 192   # length, offset, packed start, query, output
+DIN_BYTES_WEIGHTS = 256 * 192 * 2 + 64 * 256 * 2 + (256 + 64 + 64) * 4
+DIN_FLOPS_PER_POS = 2 * (192 * 256 + 256 * 64 + 64)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", type=int, default=2)
+    p.add_argument("--batches", type=int, default=4)
+    p.add_argument("--task-positions", type=int, default=0)
+    p.add_argument("--kernel-reps", type=int, default=100)
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+def src_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "sparse_embedding_din_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, shash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("src_hash") != shash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
+              "(the forward is data-parallel over samples with replicated tables and needs no "
+              "collective; multi-GPU runs are not part of it)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth
+    from sparse_embedding_din_amd import pipeline as PL
+    from sparse_embedding_din_amd import rec as R
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    R.lib()
+    dev = torch.device("cuda")
+    cfg = synth.CONFIGS[a.config]
+    B = cfg.B
+    t_gen = time.perf_counter()
+    model = synth.make_model(cfg)
+    batches = [synth.make_batch(model, batch_index=i) for i in range(a.batches)]
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    tabs = PL.DeviceTables(model.tables, dev)
+    mlp = PL.DeviceMLP(model, dev)
+    # one set of buffers (offsets, plan, outputs) per resident batch, so any
+    # call can be replayed for any batch without stale bookkeeping
+    dbs = [PL.DeviceBatch(b, dev) for b in batches]
+    fwds = [PL.SparseDinForward(tabs, mlp, B, cfg.max_len, dev, task_positions=a.task_positions)
+            for _ in dbs]
+    nb = len(dbs)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for f, db in zip(fwds, dbs):
+            f.run(db)
+    torch.cuda.synchronize()
+
+    graphs = None
+    if not a.no_graph:
+        graphs = []
+        for f, db in zip(fwds, dbs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                f.run(db)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def step(k):
+        if graphs is not None:
+            graphs[k % nb].replay()
+        else:
+            fwds[k % nb].run(dbs[k % nb])
+
+    with torch.cuda.stream(stream):
+        for k in range(a.warmup):
+            step(k)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for k in range(a.steps):
+            step(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / a.steps
+    gpu_ms = e0.elapsed_time(e1) / a.steps
+    ms_per_step = wall_ms
+    print(f"[bench] timed {a.steps} steps: wall {wall_ms*1e3:.2f} us/step, "
+          f"gpu {gpu_ms*1e3:.2f} us/step", file=sys.stderr, flush=True)
+
+    # Per-call kernel durations, from HIP events recorded on the launch stream
+    # around each call; a spin kernel holds the GPU while the calls are
+    # enqueued so that host enqueue time does not show up between the events.
+    calls = {
+        "offsets": lambda f, db: f.offsets_step(db),
+        "plan": lambda f, db: f.plan_step(db),
+        "embbag": lambda f, db: f.embbag_step(db),
+        "din": lambda f, db: f.din_step(db),
+    }
+    reps = a.kernel_reps
+    kern_us = {}
+    with torch.cuda.stream(stream):
+        for name, fn in calls.items():
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps)]
+            torch.cuda.synchronize()
+            torch.cuda._sleep(20_000_000)
+            for r in range(reps):
+                evs[r][0].record(stream)
+                fn(fwds[r % nb], dbs[r % nb])
+                evs[r][1].record(stream)
+            torch.cuda.synchronize()
+            d = np.array([s.elapsed_time(e) * 1e3 for s, e in evs])
+            kern_us[name] = dict(mean=float(d.mean()), median=float(np.median(d)),
+                                 p10=float(np.percentile(d, 10)), p90=float(np.percentile(d, 90)))
+    print(f"[bench] per-call us: " + ", ".join(f"{k}={v['median']:.2f}" for k, v in kern_us.items()),
+          file=sys.stderr, flush=True)
+
+    # algorithmic work of the average batch
+    nnz = float(np.mean([b.values.size for b in batches]))
+    P = float(np.mean([np.minimum(b.seq_lengths, cfg.max_len).sum() for b in batches]))
+    emb_bytes = nnz * EMB_BYTES_PER_ID + synth.T * B * EMB_BYTES_PER_BAG
+    din_bytes = P * DIN_BYTES_PER_POS + B * DIN_BYTES_PER_SAMPLE + DIN_BYTES_WEIGHTS
+    din_flops = P * DIN_FLOPS_PER_POS
+    emb_t = kern_us["embbag"]["mean"] * 1e-6
+    din_t = kern_us["din"]["mean"] * 1e-6
+    peak_mfma = BF16_PEAK_TFLOPS if mlp.dtype == R.REC_BF16 else FP32_PEAK_TFLOPS
+    emb_gbs = emb_bytes / emb_t / 1e9
+    din_tflops = din_flops / din_t / 1e12
+    shash = src_hash()
+    if din_t >= emb_t:
+        roof = {"kernel": "k_din_attn", "bound": "mfma", "achieved": round(din_tflops, 2),
+                "peak": peak_mfma, "unit": "TFLOP/s", "frac": round(din_tflops / peak_mfma, 4),
+                "traffic": load_traffic("k_din_attn", shash),
+                "per_launch": {"flops": din_flops, "bytes": din_bytes, "positions": P, "samples": B},
+                "avg_launch_us": round(kern_us["din"]["mean"], 3)}
+    else:
+        roof = {"kernel": "k_embbag_fwd", "bound": "hbm", "achieved": round(emb_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(emb_gbs / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic("k_embbag_fwd", shash),
+                "per_launch": {"bytes": emb_bytes, "ids": nnz, "bags": synth.T * B},
+                "avg_launch_us": round(kern_us["embbag"]["mean"], 3)}
+
+    cpu = None
+    if not a.no_cpu:
+        import oracle
+        orc = oracle.get()
+        t0 = time.perf_counter()
+        reps_cpu = 0
+        while True:
+            oracle.forward(model, batches[0], orc=orc)
+            reps_cpu += 1
+            el = time.perf_counter() - t0
+            if el >= a.cpu_seconds or reps_cpu >= 20:
+                break
+        cpu = {"value": round(reps_cpu * B / el, 1), "unit": "samples/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{reps_cpu} oracle forwards (fp64 C, single thread: offsets, embedding "
+                         f"bags, DIN attention) of batch 0 ({B} samples) of {cfg.name}, {el:.1f} s"}
+
+    value = B / (ms_per_step * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if mlp.dtype == R.REC_BF16 else "f32",
+        "data": "synthetic: seeded Taobao-shaped ids, tables N(0,0.05), Xavier MLP",
+        "config": {"workload": f"{cfg.name}: 16 dim-16 fp32 tables ({sum(cfg.sizes)} rows), "
+                               f"bags U{{1,2,3}} (price 1), click sequences Geom(mean 4) cap 100, "
+                               f"attn MLP 192-256-64-1 "
+                               f"{'bf16 with fp32 accumulate' if mlp.dtype == R.REC_BF16 else 'fp32'}",
+                   "global_batch": B, "parallelism": "single GPU",
+                   "graph_replay": graphs is not None, "rotating_batches": len(dbs)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "gpu_ms_per_step": round(gpu_ms, 5),
+        "kernels_us": kern_us,
+        "embbag": {"gb_s": round(emb_gbs, 1), "hbm_frac": round(emb_gbs / HBM_PEAK_GBS, 4)},
+        "din": {"tflops": round(din_tflops, 2), "mfma_frac": round(din_tflops / peak_mfma, 4),
+                "gb_s": round(din_bytes / din_t / 1e9, 1)},
+        "src_hash": shash,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

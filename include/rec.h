@@ -1,0 +1,260 @@
+/*
+ * rec.h — C ABI of librec, the gfx950 (MI355X) sparse embedding + DIN
+ * attention forward.
+ *
+ * What is computed (pages; title and section):
+ *   "MultiTowerDIN：当前现状分析" (MultiTowerDIN: current state)
+ *     §2    id features arrive as jagged values + lengths (KeyedJaggedTensor)
+ *     §3    each id feature owns a dense [num_buckets, 16] table; the row of a
+ *           raw id is raw_id % num_buckets
+ *     §4.1  click sequences are capped at 100 positions, real lengths ~3-5;
+ *           padding them to 100 is the main waste — this library never pads
+ *     §4.2  DIN attention: [q, s, q-s, q*s] -> attn MLP (256, 64) -> one
+ *           score per position -> masked softmax -> weighted sum
+ *     §4.4  shapes: pooled deep features, query [B,48], output [B,48]
+ *   "MultiTowerDIN：集成 DynamicEmb" (integrating DynamicEmb)
+ *     §1    a hash-table slot is key (8 B) + score (8 B) + digest (1 B) +
+ *           16 fp32 values; §3.2 lookup is O(1) open addressing and an unseen
+ *           id returns the constant 0 vector; §3.3 lookups stay fp32
+ *   DLRM essay (wmrh.cn/news/12459) §3.2: EmbeddingBag sum pooling.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns and
+ *     allocates every buffer, including workspaces; the library allocates
+ *     nothing and keeps no state besides a thread-local error message.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     null stream).  Device buffers must stay alive until that work is done.
+ *     Host structs and host arrays are read during the call only.
+ *   - Arguments are checked on the host before anything is launched; a bad
+ *     argument returns its error code, sets rec_last_error() and launches
+ *     nothing.  Nothing throws across the ABI.  Zero-size work (B == 0,
+ *     n == 0) returns REC_OK and launches nothing.
+ *   - Preconditions the library does NOT check (device data): lengths >= 0;
+ *     offsets consistent with lengths; sequence runs in bounds of their
+ *     arrays; hash tables laid out as described below.  Violations are
+ *     undefined behaviour.
+ *   - Results are deterministic: no atomics; the same inputs give bit-identical
+ *     outputs run to run.
+ */
+#ifndef REC_H
+#define REC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    REC_OK = 0,
+    REC_EINVAL = -1,        /* a null required pointer, bad size/kind/dtype/alignment */
+    REC_EUNSUPPORTED = -2,  /* valid but beyond this library's limits (see below) */
+    REC_EHIP = -3,          /* a HIP runtime call failed; message holds hipGetErrorString */
+    REC_EWORKSPACE = -4     /* workspace/plan missing or smaller than required */
+} rec_status;
+
+enum { REC_DIRECT = 0, REC_HASH = 1 };   /* rec_table.kind */
+enum { REC_F32 = 0, REC_BF16 = 1 };      /* rec_din_mlp.dtype */
+
+#define REC_DIM 16                        /* embedding width of every table */
+#define REC_EMPTY_KEY ((int64_t)-1)       /* empty hash slot; never a valid key */
+#define REC_MAX_TABLES 32                 /* tables per rec_embbag_fwd call */
+#define REC_MAX_SEQ_LEN 128               /* largest max_len for the DIN call */
+#define REC_MAX_B 16777215                /* largest batch for the DIN plan */
+
+/*
+ * One embedding table (host struct; the arrays inside are device memory).
+ *
+ * kind == REC_DIRECT ("当前现状分析" §3): values is [rows][16] fp32; the row of
+ *   raw id x is floor_mod(x, rows), i.e. the x % num_buckets of the page taken
+ *   with Python semantics, always in [0, rows).  keys/digests/scores unused.
+ *
+ * kind == REC_HASH ("集成 DynamicEmb" §1, §3.2): a lookup-only open-addressing
+ *   table of `rows` slots (the capacity), structure of arrays:
+ *     keys[rows]     int64   stored key, or REC_EMPTY_KEY
+ *     digests[rows]  uint8   0 exactly where the slot is empty, else digest(key)
+ *     scores[rows]   uint64  carried for the owner, never read here (may be NULL)
+ *     values[rows][16] fp32  the slot's embedding
+ *   Placement convention (the builder must follow it): with
+ *     h      = SplitMix64 output mix of the key's 64 bits (Steele, Lea, Flood,
+ *              OOPSLA 2014; Stafford's Mix13 shifts 30/27/31 and multipliers
+ *              0xbf58476d1ce4e5b9, 0x94d049bb133111eb),
+ *     home   = floor(h * rows / 2^64),
+ *     digest = h & 0xff, or 1 if that is 0,
+ *   every stored key sits at the first free slot of the linear, wrapping probe
+ *   sequence home, home+1, ... at the time it was inserted (no deletes).  A
+ *   lookup of key x returns the slot holding x, or -1 (a miss) on reaching an
+ *   empty slot or after `rows` probes.  A miss yields the zero vector
+ *   (§3.2 "CONSTANT=0").  The raw id is the key (no modulo).
+ *
+ * Every table: dim == 16, rows >= 1 (REC_HASH: rows <= 2^31 - 1), values
+ * 16-byte aligned (each row is 64 contiguous bytes).
+ */
+typedef struct {
+    int32_t kind;
+    int32_t dim;
+    int64_t rows;
+    const float* values;
+    const int64_t* keys;
+    const uint8_t* digests;
+    const uint64_t* scores;
+} rec_table;
+
+/*
+ * Attention-MLP parameters for DIN ("当前现状分析" §4.2, §4.4; hidden units
+ * [256, 64] as in "集成 DynamicEmb" §7), all device memory:
+ *   w1 [256][192] (output-major, like torch.nn.Linear.weight), dtype `dtype`
+ *      columns 0-47 q, 48-95 s, 96-143 q-s, 144-191 q*s; in each block the
+ *      sub-features adgroup, cate, brand (16 each)
+ *   b1 [256] fp32;  w2 [64][256] dtype `dtype`;  b2 [64] fp32
+ *   w3 [64] fp32 (the 64 -> 1 score layer), b3 a host float
+ * ReLU follows the 256- and 64-wide layers; the score has no activation.
+ * dtype REC_BF16: w1/w2 are bf16 bit patterns; q-s and q*s are formed in fp32,
+ * the 192 inputs and the 256 hidden activations are rounded to bf16 (round to
+ * nearest even) and multiplied on the matrix cores with fp32 accumulation; the
+ * 64-wide layer, score, softmax and weighted sum stay fp32.
+ * dtype REC_F32: every product and sum is fp32.
+ * w1 and w2 16-byte aligned.
+ */
+typedef struct {
+    int32_t dtype;
+    int32_t reserved;
+    const void* w1;
+    const float* b1;
+    const void* w2;
+    const float* b2;
+    const float* w3;
+    float b3;
+} rec_din_mlp;
+
+/* Bytes of workspace rec_lengths_to_offsets needs for n lengths. */
+size_t rec_scan_workspace_bytes(int64_t n);
+
+/*
+ * offsets = exclusive prefix sum of lengths ("当前现状分析" §2: a jagged
+ * feature is values + lengths; offsets locate each bag/sequence).
+ *   lengths  int32[n], each >= 0
+ *   offsets  int64[n+1]: offsets[0] = 0, offsets[i+1] = offsets[i] + lengths[i]
+ *   workspace >= rec_scan_workspace_bytes(n) bytes of device memory (scratch,
+ *            contents on entry ignored), 8-byte aligned
+ * Errors: REC_EINVAL (null lengths/offsets, n < 0), REC_EWORKSPACE.
+ * n == 0 writes offsets[0] = 0 (one tiny kernel).
+ */
+rec_status rec_lengths_to_offsets(const int32_t* lengths, int64_t n, int64_t* offsets,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sum-pooled embedding bags over T tables ("当前现状分析" §3, §4.4; DLRM
+ * essay §3.2).  The KeyedJaggedTensor is key-major: bag i = t*B + b holds
+ * values[offsets[i] .. offsets[i] + lengths[i]).
+ *   tables   host array of T descriptors (table t pools feature t)
+ *   values   int64[nnz] raw ids;  lengths int32[T*B];  offsets int64[T*B]
+ *            (offsets[T*B] is not read)
+ *   out      fp32 [B][T*16]: out[b][16t + d] = sum over bag (t, b) of row[d]
+ *            (the KeyedTensor layout); an empty bag, and every hash miss,
+ *            contributes +0.0; the sum runs in id order, fp32.  16-byte aligned.
+ *   rows_out int64[nnz] or NULL: the resolved row of each id (REC_DIRECT: the
+ *            floor-mod row; REC_HASH: the slot or -1)
+ * Errors: REC_EINVAL (null pointers, T < 1, B < 0, bad table), REC_EUNSUPPORTED
+ * (T > REC_MAX_TABLES).
+ */
+rec_status rec_embbag_fwd(const rec_table* tables, int32_t T, int64_t B,
+                          const int64_t* values, const int32_t* lengths,
+                          const int64_t* offsets, float* out, int64_t* rows_out,
+                          void* stream);
+
+/*
+ * Lookup-only hash probe ("集成 DynamicEmb" §3.2, §4.3) for n keys.
+ *   table     host descriptor, kind REC_HASH
+ *   keys      int64[n]
+ *   slot_out  int64[n] or NULL: slot holding the key, or -1 on a miss
+ *   rows_out  fp32 [n][16] or NULL: the slot's values, or 16 x +0.0 on a miss;
+ *             16-byte aligned
+ * At least one output must be non-NULL.
+ * Errors: REC_EINVAL.
+ */
+rec_status rec_hash_lookup(const rec_table* table, const int64_t* keys, int64_t n,
+                           int64_t* slot_out, float* rows_out, void* stream);
+
+/* Bytes of the DIN plan buffer for B samples capped at max_len positions. */
+size_t rec_din_plan_bytes(int64_t B, int32_t max_len);
+
+/*
+ * Sequence bookkeeping for the padding-free DIN ("当前现状分析" §4.1: real
+ * lengths are ~3-5 of a cap of 100, so positions are packed, not padded).
+ * From seq_lengths int32[B] it computes, on the device:
+ *   - the packed start of every sample over min(len, max_len) positions,
+ *   - a partition of the samples into tasks of about `task_positions`
+ *     positions each (0 = choose from the batch), each a run of whole samples,
+ * into `plan` (>= rec_din_plan_bytes(B, max_len) bytes, 16-byte aligned,
+ * opaque, read by rec_din_attn_fwd).  If seq_offsets_out is non-NULL it also
+ * receives the jagged offsets: int64[B+1], the exclusive prefix sum of the
+ * unclamped seq_lengths.
+ * The plan depends only on (seq_lengths, B, max_len, task_positions), so the
+ * same plan serves any sequence layout with those lengths.
+ * Errors: REC_EINVAL (null seq_lengths/plan, B < 0, max_len outside
+ * [1, REC_MAX_SEQ_LEN], task_positions not 0 or a multiple of 16 in [16, 64]),
+ * REC_EUNSUPPORTED (B > REC_MAX_B), REC_EWORKSPACE.
+ */
+rec_status rec_din_plan(const int32_t* seq_lengths, int64_t B, int32_t max_len,
+                        int32_t task_positions, int64_t* seq_offsets_out,
+                        void* plan, size_t plan_bytes, void* stream);
+
+/*
+ * DIN target attention, padding-free ("当前现状分析" §4.2, §4.4).
+ * For sample b with L = min(seq_lengths[b], max_len) positions j < L:
+ *   s_j = [adgroup row | cate row | brand row] of ids
+ *         seq_values[f*seq_stride + seq_offsets[b] + j], f = 0, 1, 2, looked up
+ *         in seq_tables[f] (direct or hash; a miss is the zero row)
+ *   q   = query[b*query_ld + query_col[f] + d] (f = 0..2, d < 16), the pooled
+ *         target features (for the pooled output of rec_embbag_fwd with the
+ *         16 deep features in page order: query_ld 256, query_col {16, 80, 48})
+ *   e_j = w3 . relu(W2 relu(W1 [q, s_j, q - s_j, q*s_j] + b1) + b2) + b3
+ *   p_j = softmax over j < L of e_j (max-subtracted, no temperature)
+ *   out[b][0..48) = sum_j p_j s_j;  L == 0 gives 48 x +0.0
+ * Positions j >= L are never read, so a padded layout (seq_offsets[b] = b*100)
+ * and a packed one (seq_offsets = the jagged offsets) give bit-identical output.
+ *   seq_tables  host array of 3 descriptors (adgroup, cate, brand)
+ *   plan        from rec_din_plan for the same seq_lengths, B and max_len
+ *   mlp         host struct (device arrays inside)
+ *   out         fp32 [B][48], 16-byte aligned
+ *   scores_out  fp32, indexed like seq_values' positions (seq_offsets[b] + j),
+ *               or NULL: e_j
+ *   weights_out same indexing or NULL: p_j (requires scores_out)
+ *   rows_out    int64 [3][seq_stride] or NULL: the resolved row/slot of each id
+ * query and query_ld/query_col must give 16-byte aligned rows (query_ld and
+ * query_col[f] multiples of 4).
+ * Errors: REC_EINVAL (null pointers, bad table/mlp, misalignment, B < 0,
+ * max_len out of range, weights_out without scores_out), REC_EWORKSPACE
+ * (plan too small for B, max_len).
+ */
+rec_status rec_din_attn_fwd(const rec_table* seq_tables, const int64_t* seq_values,
+                            int64_t seq_stride, const int64_t* seq_offsets,
+                            const int32_t* seq_lengths, int32_t max_len, int64_t B,
+                            const float* query, int64_t query_ld, const int32_t* query_col,
+                            const rec_din_mlp* mlp, const void* plan, size_t plan_bytes,
+                            float* out, float* scores_out, float* weights_out,
+                            int64_t* rows_out, void* stream);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* rec_last_error(void);
+
+/* ABI version (major*100 + minor). */
+int32_t rec_version(void);
+
+/*
+ * Host-side twins of the device index arithmetic, for testing that
+ * arithmetic without a GPU: the same inline functions the kernels run.
+ *   rec_host_floor_mod: row of raw id x in a direct table of n rows (n >= 1)
+ *   rec_host_hash_home: home slot of key x in a table of `capacity` slots;
+ *                       *digest receives the key's digest byte
+ */
+int64_t rec_host_floor_mod(int64_t x, int64_t n);
+int64_t rec_host_hash_home(int64_t x, int64_t capacity, uint8_t* digest);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REC_H */

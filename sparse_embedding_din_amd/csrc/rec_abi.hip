@@ -1,0 +1,256 @@
+// The extern "C" entry points of librec: host-side argument checks, table
+// descriptor preparation, and kernel launches on the caller's stream.  Every
+// check runs before the first HIP call, so a rejected call touches no device.
+#include <string.h>
+
+#include <string>
+
+#include "rec_internal.h"
+
+using namespace rec;
+
+namespace {
+
+thread_local std::string g_err;
+
+rec_status fail(rec_status s, const std::string& msg) {
+    g_err = msg;
+    return s;
+}
+
+rec_status ok() {
+    g_err.clear();
+    return REC_OK;
+}
+
+rec_status hip_status(hipError_t e, const char* where) {
+    if (e == hipSuccess) return ok();
+    return fail(REC_EHIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validate one table and build its kernel descriptor.
+rec_status prep_table(const rec_table& t, const char* what, TabDev* out) {
+    if (t.kind != REC_DIRECT && t.kind != REC_HASH)
+        return fail(REC_EINVAL, std::string(what) + ": unknown kind");
+    if (t.dim != REC_DIM) return fail(REC_EINVAL, std::string(what) + ": dim must be 16");
+    if (t.rows < 1) return fail(REC_EINVAL, std::string(what) + ": rows must be >= 1");
+    if (!t.values) return fail(REC_EINVAL, std::string(what) + ": values is NULL");
+    if (!aligned16(t.values)) return fail(REC_EINVAL, std::string(what) + ": values not 16-byte aligned");
+    memset(out, 0, sizeof(*out));
+    out->values = t.values;
+    out->rows = t.rows;
+    out->kind = t.kind;
+    if (t.kind == REC_HASH) {
+        if (!t.keys || !t.digests) return fail(REC_EINVAL, std::string(what) + ": hash table needs keys and digests");
+        if (t.rows > 2147483647LL) return fail(REC_EINVAL, std::string(what) + ": hash capacity above 2^31-1");
+        out->keys = t.keys;
+        out->digests = t.digests;
+    } else {
+        floor_mod_prepare(t.rows, &out->magic, &out->shift);
+    }
+    return REC_OK;
+}
+
+int num_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return -1;
+    if (dev >= 0 && dev < 64) cache[dev] = n;
+    return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rec_last_error(void) { return g_err.c_str(); }
+
+int32_t rec_version(void) { return 100; }
+
+int64_t rec_host_floor_mod(int64_t x, int64_t n) {
+    if (n < 1) return -1;
+    uint64_t m;
+    int32_t s;
+    floor_mod_prepare(n, &m, &s);
+    return floor_mod_magic(x, n, m, s);
+}
+
+int64_t rec_host_hash_home(int64_t x, int64_t capacity, uint8_t* digest) {
+    const uint64_t h = mix64((uint64_t)x);
+    if (digest) *digest = (uint8_t)hash_digest(h);
+    return capacity >= 1 ? hash_home(h, capacity) : -1;
+}
+
+size_t rec_scan_workspace_bytes(int64_t n) {
+    return n > 0 ? (size_t)scan_blocks(n) * sizeof(int64_t) : 0;
+}
+
+rec_status rec_lengths_to_offsets(const int32_t* lengths, int64_t n, int64_t* offsets,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (n < 0) return fail(REC_EINVAL, "rec_lengths_to_offsets: n < 0");
+    if (!offsets) return fail(REC_EINVAL, "rec_lengths_to_offsets: offsets is NULL");
+    if (n > 0 && !lengths) return fail(REC_EINVAL, "rec_lengths_to_offsets: lengths is NULL");
+    const size_t need = rec_scan_workspace_bytes(n);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(REC_EWORKSPACE, "rec_lengths_to_offsets: workspace smaller than rec_scan_workspace_bytes(n)");
+    if (need > 0 && ((uintptr_t)workspace & 7u))
+        return fail(REC_EINVAL, "rec_lengths_to_offsets: workspace not 8-byte aligned");
+    return hip_status(launch_lengths_to_offsets(lengths, n, offsets, (int64_t*)workspace,
+                                                (hipStream_t)stream),
+                      "rec_lengths_to_offsets");
+}
+
+rec_status rec_embbag_fwd(const rec_table* tables, int32_t T, int64_t B, const int64_t* values,
+                          const int32_t* lengths, const int64_t* offsets, float* out,
+                          int64_t* rows_out, void* stream) {
+    if (!tables) return fail(REC_EINVAL, "rec_embbag_fwd: tables is NULL");
+    if (T < 1) return fail(REC_EINVAL, "rec_embbag_fwd: T < 1");
+    if (T > REC_MAX_TABLES) return fail(REC_EUNSUPPORTED, "rec_embbag_fwd: T > REC_MAX_TABLES");
+    if (B < 0) return fail(REC_EINVAL, "rec_embbag_fwd: B < 0");
+    if (!values || !lengths || !offsets || !out)
+        return fail(REC_EINVAL, "rec_embbag_fwd: values, lengths, offsets and out are required");
+    if (!aligned16(out)) return fail(REC_EINVAL, "rec_embbag_fwd: out not 16-byte aligned");
+    EmbArgs a;
+    memset(&a, 0, sizeof(a));
+    for (int t = 0; t < T; ++t) {
+        rec_status s = prep_table(tables[t], "rec_embbag_fwd: table", &a.tab[t]);
+        if (s != REC_OK) return s;
+    }
+    if (B == 0) return ok();
+    a.values = values;
+    a.lengths = lengths;
+    a.offsets = offsets;
+    a.out = out;
+    a.rows_out = rows_out;
+    a.B = B;
+    a.T = T;
+    a.chunks = (T + 15) / 16;
+    return hip_status(launch_embbag(a, (hipStream_t)stream), "rec_embbag_fwd");
+}
+
+rec_status rec_hash_lookup(const rec_table* table, const int64_t* keys, int64_t n,
+                           int64_t* slot_out, float* rows_out, void* stream) {
+    if (!table) return fail(REC_EINVAL, "rec_hash_lookup: table is NULL");
+    if (table->kind != REC_HASH) return fail(REC_EINVAL, "rec_hash_lookup: table kind is not REC_HASH");
+    if (n < 0) return fail(REC_EINVAL, "rec_hash_lookup: n < 0");
+    if (!slot_out && !rows_out) return fail(REC_EINVAL, "rec_hash_lookup: no output requested");
+    if (n > 0 && !keys) return fail(REC_EINVAL, "rec_hash_lookup: keys is NULL");
+    if (rows_out && !aligned16(rows_out)) return fail(REC_EINVAL, "rec_hash_lookup: rows_out not 16-byte aligned");
+    HashArgs a;
+    memset(&a, 0, sizeof(a));
+    rec_status s = prep_table(*table, "rec_hash_lookup: table", &a.tab);
+    if (s != REC_OK) return s;
+    if (n == 0) return ok();
+    a.keys = keys;
+    a.n = n;
+    a.slot_out = slot_out;
+    a.rows_out = rows_out;
+    return hip_status(launch_hash_lookup(a, (hipStream_t)stream), "rec_hash_lookup");
+}
+
+size_t rec_din_plan_bytes(int64_t B, int32_t max_len) {
+    if (B < 0 || max_len < 1 || max_len > REC_MAX_SEQ_LEN || B > REC_MAX_B) return 0;
+    return plan_layout(B, max_len).bytes;
+}
+
+rec_status rec_din_plan(const int32_t* seq_lengths, int64_t B, int32_t max_len,
+                        int32_t task_positions, int64_t* seq_offsets_out, void* plan,
+                        size_t plan_bytes, void* stream) {
+    if (B < 0) return fail(REC_EINVAL, "rec_din_plan: B < 0");
+    if (B > REC_MAX_B) return fail(REC_EUNSUPPORTED, "rec_din_plan: B > REC_MAX_B");
+    if (max_len < 1 || max_len > REC_MAX_SEQ_LEN)
+        return fail(REC_EINVAL, "rec_din_plan: max_len outside [1, REC_MAX_SEQ_LEN]");
+    if (task_positions != 0 &&
+        (task_positions % 16 != 0 || task_positions < kMinTaskPositions || task_positions > kMaxTaskPositions))
+        return fail(REC_EINVAL, "rec_din_plan: task_positions must be 0, 16, 32, 48 or 64");
+    if (B > 0 && !seq_lengths) return fail(REC_EINVAL, "rec_din_plan: seq_lengths is NULL");
+    if (!plan) return fail(REC_EINVAL, "rec_din_plan: plan is NULL");
+    if (!aligned16(plan)) return fail(REC_EINVAL, "rec_din_plan: plan not 16-byte aligned");
+    if (plan_bytes < rec_din_plan_bytes(B, max_len))
+        return fail(REC_EWORKSPACE, "rec_din_plan: plan smaller than rec_din_plan_bytes(B, max_len)");
+    if (B == 0) return ok();
+    const int cus = num_cus();
+    if (cus < 1) return fail(REC_EHIP, "rec_din_plan: cannot query the device");
+    return hip_status(launch_din_plan(seq_lengths, B, max_len, task_positions, cus * kDinWaves,
+                                      seq_offsets_out, plan, (hipStream_t)stream),
+                      "rec_din_plan");
+}
+
+rec_status rec_din_attn_fwd(const rec_table* seq_tables, const int64_t* seq_values,
+                            int64_t seq_stride, const int64_t* seq_offsets,
+                            const int32_t* seq_lengths, int32_t max_len, int64_t B,
+                            const float* query, int64_t query_ld, const int32_t* query_col,
+                            const rec_din_mlp* mlp, const void* plan, size_t plan_bytes,
+                            float* out, float* scores_out, float* weights_out,
+                            int64_t* rows_out, void* stream) {
+    if (B < 0) return fail(REC_EINVAL, "rec_din_attn_fwd: B < 0");
+    if (B > REC_MAX_B) return fail(REC_EUNSUPPORTED, "rec_din_attn_fwd: B > REC_MAX_B");
+    if (max_len < 1 || max_len > REC_MAX_SEQ_LEN)
+        return fail(REC_EINVAL, "rec_din_attn_fwd: max_len outside [1, REC_MAX_SEQ_LEN]");
+    if (!seq_tables) return fail(REC_EINVAL, "rec_din_attn_fwd: seq_tables is NULL");
+    if (!seq_values || !seq_offsets || !seq_lengths)
+        return fail(REC_EINVAL, "rec_din_attn_fwd: seq_values, seq_offsets and seq_lengths are required");
+    if (seq_stride < 0) return fail(REC_EINVAL, "rec_din_attn_fwd: seq_stride < 0");
+    if (!query || !query_col) return fail(REC_EINVAL, "rec_din_attn_fwd: query and query_col are required");
+    if (!aligned16(query) || query_ld < 16 || (query_ld & 3))
+        return fail(REC_EINVAL, "rec_din_attn_fwd: query rows must be 16-byte aligned (query_ld a multiple of 4)");
+    for (int f = 0; f < 3; ++f)
+        if (query_col[f] < 0 || (query_col[f] & 3) || query_col[f] + 16 > query_ld)
+            return fail(REC_EINVAL, "rec_din_attn_fwd: query_col must be multiples of 4 inside query_ld");
+    if (!mlp) return fail(REC_EINVAL, "rec_din_attn_fwd: mlp is NULL");
+    if (mlp->dtype != REC_F32 && mlp->dtype != REC_BF16)
+        return fail(REC_EINVAL, "rec_din_attn_fwd: unknown mlp dtype");
+    if (!mlp->w1 || !mlp->b1 || !mlp->w2 || !mlp->b2 || !mlp->w3)
+        return fail(REC_EINVAL, "rec_din_attn_fwd: mlp arrays are required");
+    if (!aligned16(mlp->w1) || !aligned16(mlp->w2))
+        return fail(REC_EINVAL, "rec_din_attn_fwd: w1/w2 not 16-byte aligned");
+    if (!out) return fail(REC_EINVAL, "rec_din_attn_fwd: out is NULL");
+    if (!aligned16(out)) return fail(REC_EINVAL, "rec_din_attn_fwd: out not 16-byte aligned");
+    if (weights_out && !scores_out)
+        return fail(REC_EINVAL, "rec_din_attn_fwd: weights_out requires scores_out");
+    if (!plan) return fail(REC_EINVAL, "rec_din_attn_fwd: plan is NULL");
+    if (plan_bytes < rec_din_plan_bytes(B, max_len))
+        return fail(REC_EWORKSPACE, "rec_din_attn_fwd: plan smaller than rec_din_plan_bytes(B, max_len)");
+    DinArgs a;
+    memset(&a, 0, sizeof(a));
+    for (int f = 0; f < 3; ++f) {
+        rec_status s = prep_table(seq_tables[f], "rec_din_attn_fwd: seq table", &a.tab[f]);
+        if (s != REC_OK) return s;
+    }
+    if (B == 0) return ok();
+    const int cus = num_cus();
+    if (cus < 1) return fail(REC_EHIP, "rec_din_attn_fwd: cannot query the device");
+    const PlanLayout L = plan_layout(B, max_len);
+    const char* p = (const char*)plan;
+    a.seq_values = seq_values;
+    a.seq_stride = seq_stride;
+    a.seq_offsets = seq_offsets;
+    a.query = query;
+    a.query_ld = query_ld;
+    for (int f = 0; f < 3; ++f) a.qcol[f] = query_col[f];
+    a.max_len = max_len;
+    a.w1 = mlp->w1;
+    a.b1 = mlp->b1;
+    a.w2 = mlp->w2;
+    a.b2 = mlp->b2;
+    a.w3 = mlp->w3;
+    a.b3 = mlp->b3;
+    a.dtype = mlp->dtype;
+    a.plan_hdr = (const int32_t*)p;
+    a.pos_start = (const int32_t*)(p + L.off_pos);
+    a.task_first = (const int32_t*)(p + L.off_task);
+    a.out = out;
+    a.scores = scores_out;
+    a.weights = weights_out;
+    a.rows_out = rows_out;
+    a.B = B;
+    a.max_tasks = L.max_tasks;
+    return hip_status(launch_din(a, cus, (hipStream_t)stream), "rec_din_attn_fwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,193 @@
+// Internal declarations shared by librec's translation units: table
+// descriptors as the kernels see them, the index arithmetic (host and
+// device), and the kernel launchers each .hip file provides.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rec.h"
+
+namespace rec {
+
+// ---------------------------------------------------------------------------
+// A table as the kernels see it (48 bytes, passed in kernel arguments).
+struct TabDev {
+    const float* values;      // [rows][16]
+    const int64_t* keys;      // hash: [rows]
+    const uint8_t* digests;   // hash: [rows], 0 = empty slot
+    int64_t rows;             // direct: num_buckets; hash: capacity
+    uint64_t magic;           // direct: multiplier for the floor modulo (0 when rows == 1)
+    int32_t shift;            // direct: post-shift of the multiply-high
+    int32_t kind;             // REC_DIRECT / REC_HASH
+};
+
+__host__ __device__ inline uint64_t mulhi64(uint64_t a, uint64_t b) {
+    return (uint64_t)(((unsigned __int128)a * (unsigned __int128)b) >> 64);
+}
+
+// Floor modulo by an invariant divisor n >= 2 through one multiply-high
+// (Granlund & Montgomery, "Division by invariant integers using
+// multiplication", PLDI 1994, Thm 4.2, specialised to 63-bit dividends):
+// with l = ceil(log2 n) and m = ceil(2^(63+l) / n) (< 2^64), every
+// v < 2^63 has floor(v / n) = mulhi(v, m) >> (l - 1).
+inline void floor_mod_prepare(int64_t n, uint64_t* magic, int32_t* shift) {
+    if (n <= 1) { *magic = 0; *shift = 0; return; }
+    int l = 0;
+    while (l < 63 && ((int64_t)1 << l) < n) ++l;           // 2^(l-1) < n <= 2^l
+    unsigned __int128 num = (unsigned __int128)1 << (63 + l);
+    *magic = (uint64_t)((num + (unsigned __int128)(n - 1)) / (unsigned __int128)n);
+    *shift = l - 1;
+}
+
+// Row of raw id x in a table of n rows: x mod n in [0, n).  A negative x is
+// handled through its one's complement v = -x - 1 (< 2^63): x mod n =
+// n - 1 - (v mod n).
+__host__ __device__ inline int64_t floor_mod_magic(int64_t x, int64_t n, uint64_t magic,
+                                                   int32_t shift) {
+    if (magic == 0) return 0;                                // n == 1
+    const bool neg = x < 0;
+    const uint64_t v = neg ? ~(uint64_t)x : (uint64_t)x;
+    const uint64_t q = mulhi64(v, magic) >> shift;
+    const int64_t r = (int64_t)(v - q * (uint64_t)n);
+    return neg ? (n - 1 - r) : r;
+}
+
+// SplitMix64's output mixing function (Steele, Lea & Flood, OOPSLA 2014, with
+// Stafford's Mix13 constants): a bijection on 64-bit words.
+__host__ __device__ inline uint64_t mix64(uint64_t z) {
+    z ^= z >> 30;
+    z *= 0xbf58476d1ce4e5b9ULL;
+    z ^= z >> 27;
+    z *= 0x94d049bb133111ebULL;
+    z ^= z >> 31;
+    return z;
+}
+
+// Home slot: floor(h * capacity / 2^64) (Lemire's multiply-high range map).
+__host__ __device__ inline int64_t hash_home(uint64_t h, int64_t capacity) {
+    return (int64_t)mulhi64(h, (uint64_t)capacity);
+}
+
+__host__ __device__ inline uint32_t hash_digest(uint64_t h) {
+    const uint32_t d = (uint32_t)(h & 0xffu);
+    return d ? d : 1u;
+}
+
+// Linear probe from the home slot: the slot holding `key`, or -1 on reaching
+// an empty slot (digest 0) or after `rows` probes.  Keys are compared only
+// where the digest matches.
+__device__ inline int64_t hash_probe(const TabDev& t, int64_t key) {
+    const uint64_t h = mix64((uint64_t)key);
+    const uint32_t d = hash_digest(h);
+    int64_t s = hash_home(h, t.rows);
+    for (int64_t c = 0; c < t.rows; ++c) {
+        const uint32_t ds = t.digests[s];
+        if (ds == 0u) return -1;
+        if (ds == d && t.keys[s] == key) return s;
+        s = (s + 1 == t.rows) ? 0 : s + 1;
+    }
+    return -1;
+}
+
+__device__ inline int64_t resolve_row(const TabDev& t, int64_t raw) {
+    if (t.kind == REC_DIRECT) return floor_mod_magic(raw, t.rows, t.magic, t.shift);
+    return hash_probe(t, raw);
+}
+
+// ---------------------------------------------------------------------------
+// Scan / plan
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 16;
+constexpr int kScanChunk = kScanThreads * kScanItems;     // 4096 lengths per block
+
+inline int64_t scan_blocks(int64_t n) { return (n + kScanChunk - 1) / kScanChunk; }
+
+// DIN plan buffer layout (bytes from the start)
+//   [0, 64)            int32 header: B, max_len, C (positions per task),
+//                      num_tasks, P (total packed positions), nblocks
+//   [64, 64+16*nb)     int64 pairs: per-block sums (clamped, raw)
+//   pos_start          int32[B+1], 16-byte aligned
+//   task_first         int32[max_tasks+1]
+enum { kHdrB = 0, kHdrMaxLen, kHdrC, kHdrNumTasks, kHdrP, kHdrNBlocks };
+constexpr int kMinTaskPositions = 16;
+constexpr int kMaxTaskPositions = 64;
+
+struct PlanLayout {
+    int64_t nblocks, max_tasks;
+    size_t off_sums, off_pos, off_task, bytes;
+};
+
+inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+inline PlanLayout plan_layout(int64_t B, int32_t max_len) {
+    PlanLayout p;
+    p.nblocks = scan_blocks(B);
+    p.max_tasks = (B * (int64_t)max_len) / kMinTaskPositions + 1;
+    p.off_sums = 64;
+    p.off_pos = align16(p.off_sums + 16 * (size_t)p.nblocks);
+    p.off_task = align16(p.off_pos + 4 * (size_t)(B + 1));
+    p.bytes = align16(p.off_task + 4 * (size_t)(p.max_tasks + 1));
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (return the hipError_t of the launch)
+hipError_t launch_lengths_to_offsets(const int32_t* lengths, int64_t n, int64_t* offsets,
+                                     int64_t* block_sums, hipStream_t s);
+hipError_t launch_din_plan(const int32_t* seq_lengths, int64_t B, int32_t max_len,
+                           int32_t task_positions, int32_t total_waves,
+                           int64_t* seq_offsets_out, void* plan, hipStream_t s);
+
+struct EmbArgs {
+    TabDev tab[REC_MAX_TABLES];
+    const int64_t* values;
+    const int32_t* lengths;
+    const int64_t* offsets;
+    float* out;
+    int64_t* rows_out;
+    int64_t B;
+    int32_t T;
+    int32_t chunks;     // ceil(T / 16): waves per sample
+};
+hipError_t launch_embbag(const EmbArgs& a, hipStream_t s);
+
+struct HashArgs {
+    TabDev tab;
+    const int64_t* keys;
+    int64_t n;
+    int64_t* slot_out;
+    float* rows_out;
+};
+hipError_t launch_hash_lookup(const HashArgs& a, hipStream_t s);
+
+struct DinArgs {
+    TabDev tab[3];
+    const int64_t* seq_values;
+    int64_t seq_stride;
+    const int64_t* seq_offsets;
+    const float* query;
+    int64_t query_ld;
+    int32_t qcol[3];
+    int32_t max_len;
+    const void* w1;
+    const float* b1;
+    const void* w2;
+    const float* b2;
+    const float* w3;
+    float b3;
+    int32_t dtype;
+    const int32_t* plan_hdr;
+    const int32_t* pos_start;
+    const int32_t* task_first;
+    float* out;
+    float* scores;
+    float* weights;
+    int64_t* rows_out;
+    int64_t B;
+    int64_t max_tasks;
+};
+constexpr int kDinWaves = 8;                 // waves per workgroup
+hipError_t launch_din(const DinArgs& a, int num_cus, hipStream_t s);
+
+}  // namespace rec

@@ -1,0 +1,139 @@
+"""Device-resident tables, MLP and batches, and the whole sparse forward as
+four C-ABI calls:
+
+    rec_lengths_to_offsets  (deep KJT lengths -> offsets)
+    rec_din_plan            (sequence lengths -> packed starts, tasks, offsets)
+    rec_embbag_fwd          (pooled [B, 256])
+    rec_din_attn_fwd        (attention [B, 48], query read from the pooled output)
+
+torch provides device memory and the stream; every step runs in librec.
+Inputs are plain numpy arrays / dicts (as the seeded generator produces).
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import rec as R
+
+SEQ_KEYS = (1, 5, 3)             # adgroup, cate, brand: the seq group's sub-features
+
+
+def _to(a: np.ndarray, device, dtype=None) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(device)
+
+
+class DeviceTables:
+    """Tables on the device plus their rec_table descriptors."""
+
+    def __init__(self, tables: Sequence[dict], device):
+        self.tensors = []
+        self.desc = []
+        for tab in tables:
+            vals = _to(np.asarray(tab["values"], np.float32), device)
+            if tab["kind"] == "hash":
+                keys = _to(np.asarray(tab["keys"], np.int64), device)
+                dig = _to(np.asarray(tab["digests"], np.uint8), device)
+                sc = _to(np.asarray(tab["scores"], np.uint64).view(np.int64), device)
+                self.tensors.append((vals, keys, dig, sc))
+                self.desc.append(R.table(R.REC_HASH, int(tab["rows"]), vals, keys, dig, sc))
+            else:
+                self.tensors.append((vals,))
+                self.desc.append(R.table(R.REC_DIRECT, int(tab["rows"]), vals))
+
+    def array(self, idx: Optional[Sequence[int]] = None):
+        sel = self.desc if idx is None else [self.desc[i] for i in idx]
+        arr = (R.rec_table * len(sel))()
+        for i, d in enumerate(sel):
+            arr[i] = d
+        return arr
+
+
+class DeviceMLP:
+    def __init__(self, model, device, dtype: Optional[str] = None):
+        dt = dtype or getattr(model, "mlp_dtype", "f32")
+        if dt == "bf16":
+            self.dtype = R.REC_BF16
+            self.w1 = _to(np.asarray(model.w1_bf16).view(np.int16), device)
+            self.w2 = _to(np.asarray(model.w2_bf16).view(np.int16), device)
+        else:
+            self.dtype = R.REC_F32
+            self.w1 = _to(np.asarray(model.w1, np.float32), device)
+            self.w2 = _to(np.asarray(model.w2, np.float32), device)
+        self.b1 = _to(np.asarray(model.b1, np.float32), device)
+        self.b2 = _to(np.asarray(model.b2, np.float32), device)
+        self.w3 = _to(np.asarray(model.w3, np.float32), device)
+        self.b3 = float(model.b3)
+        self.desc = R.din_mlp(self.dtype, self.w1, self.b1, self.w2, self.b2, self.w3, self.b3)
+
+
+class DeviceBatch:
+    def __init__(self, batch, device, seq_values=None, seq_offsets=None, seq_stride=None):
+        self.B = int(batch.B)
+        self.lengths = _to(np.asarray(batch.lengths, np.int32), device)
+        self.values = _to(np.asarray(batch.values, np.int64), device)
+        self.nnz = int(batch.values.size)
+        self.seq_lengths = _to(np.asarray(batch.seq_lengths, np.int32), device)
+        sv = batch.seq_values if seq_values is None else seq_values
+        self.seq_values = _to(np.asarray(sv, np.int64), device)
+        self.seq_stride = int(batch.seq_stride if seq_stride is None else seq_stride)
+        # an explicit sequence layout (e.g. padded); None = packed offsets from the plan
+        self.seq_offsets = None if seq_offsets is None else _to(np.asarray(seq_offsets, np.int64), device)
+
+
+class SparseDinForward:
+    """Buffers for batches of up to B_max samples and the four-call forward."""
+
+    def __init__(self, tables: DeviceTables, mlp: DeviceMLP, B_max: int, max_len: int = 100,
+                 device="cuda", task_positions: int = 0, T: int = 16):
+        self.T = T
+        self.tables = tables
+        self.mlp = mlp
+        self.max_len = max_len
+        self.task_positions = task_positions
+        self.B_max = B_max
+        self.tab_arr = tables.array(list(range(T)))
+        self.seq_arr = tables.array(list(SEQ_KEYS))
+        self.query_col = (C.c_int32 * 3)(*[16 * k for k in SEQ_KEYS])
+        self.offsets = torch.empty(T * B_max + 1, dtype=torch.int64, device=device)
+        self.ws_bytes = max(R.rec_scan_workspace_bytes(T * B_max), 8)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.plan_bytes = R.rec_din_plan_bytes(B_max, max_len)
+        self.plan = torch.empty(self.plan_bytes, dtype=torch.uint8, device=device)
+        self.seq_offsets = torch.empty(B_max + 1, dtype=torch.int64, device=device)
+        self.pooled = torch.empty(B_max, T * 16, dtype=torch.float32, device=device)
+        self.att = torch.empty(B_max, 48, dtype=torch.float32, device=device)
+
+    # the four steps, each one C-ABI call
+    def offsets_step(self, b: DeviceBatch, stream=None):
+        R.rec_lengths_to_offsets(b.lengths, self.T * b.B, self.offsets, self.ws, self.ws_bytes, stream)
+
+    def plan_step(self, b: DeviceBatch, stream=None):
+        R.rec_din_plan(b.seq_lengths, b.B, self.max_len, self.task_positions, self.seq_offsets,
+                       self.plan, self.plan_bytes, stream)
+
+    def embbag_step(self, b: DeviceBatch, rows_out=None, stream=None):
+        R.rec_embbag_fwd(self.tab_arr, self.T, b.B, b.values, b.lengths, self.offsets, self.pooled,
+                         rows_out, stream)
+
+    def din_step(self, b: DeviceBatch, scores=None, weights=None, rows=None, stream=None):
+        so = self.seq_offsets if b.seq_offsets is None else b.seq_offsets
+        R.rec_din_attn_fwd(self.seq_arr, b.seq_values, b.seq_stride, so, b.seq_lengths,
+                           self.max_len, b.B, self.pooled, self.T * 16, self.query_col,
+                           self.mlp.desc, self.plan, self.plan_bytes, self.att, scores, weights,
+                           rows, stream)
+
+    def run(self, b: DeviceBatch, stream=None, debug: Optional[dict] = None):
+        assert b.B <= self.B_max
+        d = debug or {}
+        self.offsets_step(b, stream)
+        self.plan_step(b, stream)
+        self.embbag_step(b, d.get("emb_rows"), stream)
+        self.din_step(b, d.get("scores"), d.get("weights"), d.get("seq_rows"), stream)
+        return self.pooled[: b.B], self.att[: b.B]

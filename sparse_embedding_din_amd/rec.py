@@ -1,0 +1,185 @@
+"""Thin ctypes binding over librec.so (include/rec.h).
+
+Argument marshalling only: every function here has the C entry point's name
+and arguments; device buffers are torch tensors (or raw integer addresses),
+host structs are built from plain Python values, and the stream defaults to
+torch's current stream.  All computation happens in the HIP library; if it
+is not built this module raises on first use, it never falls back.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librec.so")
+
+REC_OK, REC_EINVAL, REC_EUNSUPPORTED, REC_EHIP, REC_EWORKSPACE = 0, -1, -2, -3, -4
+REC_DIRECT, REC_HASH = 0, 1
+REC_F32, REC_BF16 = 0, 1
+REC_DIM = 16
+REC_EMPTY_KEY = -1
+REC_MAX_TABLES = 32
+REC_MAX_SEQ_LEN = 128
+REC_MAX_B = 16777215
+
+EXPORTS = ["rec_scan_workspace_bytes", "rec_lengths_to_offsets", "rec_embbag_fwd",
+           "rec_hash_lookup", "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_fwd",
+           "rec_last_error", "rec_version", "rec_host_floor_mod", "rec_host_hash_home"]
+
+
+class RecError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn} -> {status}: {msg}")
+        self.status = status
+
+
+class rec_table(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("dim", C.c_int32), ("rows", C.c_int64),
+                ("values", C.c_void_p), ("keys", C.c_void_p), ("digests", C.c_void_p),
+                ("scores", C.c_void_p)]
+
+
+class rec_din_mlp(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("reserved", C.c_int32), ("w1", C.c_void_p),
+                ("b1", C.c_void_p), ("w2", C.c_void_p), ("b2", C.c_void_p),
+                ("w3", C.c_void_p), ("b3", C.c_float)]
+
+
+_LIB = None
+
+
+def lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m sparse_embedding_din_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        vp, i64, i32, sz = C.c_void_p, C.c_int64, C.c_int32, C.c_size_t
+        L.rec_scan_workspace_bytes.argtypes = [i64]
+        L.rec_scan_workspace_bytes.restype = sz
+        L.rec_lengths_to_offsets.argtypes = [vp, i64, vp, vp, sz, vp]
+        L.rec_embbag_fwd.argtypes = [C.POINTER(rec_table), i32, i64, vp, vp, vp, vp, vp, vp]
+        L.rec_hash_lookup.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, vp]
+        L.rec_din_plan_bytes.argtypes = [i64, i32]
+        L.rec_din_plan_bytes.restype = sz
+        L.rec_din_plan.argtypes = [vp, i64, i32, i32, vp, vp, sz, vp]
+        L.rec_din_attn_fwd.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, i32, i64, vp, i64,
+                                       C.POINTER(C.c_int32), C.POINTER(rec_din_mlp), vp, sz, vp,
+                                       vp, vp, vp, vp]
+        for f in ("rec_lengths_to_offsets", "rec_embbag_fwd", "rec_hash_lookup", "rec_din_plan",
+                  "rec_din_attn_fwd"):
+            getattr(L, f).restype = C.c_int
+        L.rec_last_error.argtypes = []
+        L.rec_last_error.restype = C.c_char_p
+        L.rec_version.restype = C.c_int32
+        L.rec_host_floor_mod.argtypes = [i64, i64]
+        L.rec_host_floor_mod.restype = i64
+        L.rec_host_hash_home.argtypes = [i64, i64, C.POINTER(C.c_uint8)]
+        L.rec_host_hash_home.restype = i64
+        _LIB = L
+    return _LIB
+
+
+def _p(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, fn: str):
+    if status != REC_OK:
+        raise RecError(status, fn, lib().rec_last_error().decode())
+
+
+def table(kind: int, rows: int, values, keys=None, digests=None, scores=None,
+          dim: int = REC_DIM) -> rec_table:
+    """A host rec_table descriptor over device tensors (kept alive by the caller)."""
+    return rec_table(kind, dim, rows, _p(values), _p(keys), _p(digests), _p(scores))
+
+
+def din_mlp(dtype: int, w1, b1, w2, b2, w3, b3: float) -> rec_din_mlp:
+    return rec_din_mlp(dtype, 0, _p(w1), _p(b1), _p(w2), _p(b2), _p(w3), float(b3))
+
+
+def _tables(tabs: Sequence[rec_table]):
+    arr = (rec_table * len(tabs))()
+    for i, t in enumerate(tabs):
+        arr[i] = t
+    return arr
+
+
+# -- entry points (same names and arguments as include/rec.h) ----------------
+def rec_version() -> int:
+    return int(lib().rec_version())
+
+
+def rec_last_error() -> str:
+    return lib().rec_last_error().decode()
+
+
+def rec_scan_workspace_bytes(n: int) -> int:
+    return int(lib().rec_scan_workspace_bytes(n))
+
+
+def rec_lengths_to_offsets(lengths, n: int, offsets, workspace, workspace_bytes: int, stream=None):
+    _check(lib().rec_lengths_to_offsets(_p(lengths), n, _p(offsets), _p(workspace),
+                                        workspace_bytes, _stream(stream)), "rec_lengths_to_offsets")
+
+
+def rec_embbag_fwd(tables: Sequence[rec_table], T: int, B: int, values, lengths, offsets, out,
+                   rows_out=None, stream=None):
+    _check(lib().rec_embbag_fwd(_tables(tables), T, B, _p(values), _p(lengths), _p(offsets),
+                                _p(out), _p(rows_out), _stream(stream)), "rec_embbag_fwd")
+
+
+def rec_hash_lookup(table_: rec_table, keys, n: int, slot_out=None, rows_out=None, stream=None):
+    _check(lib().rec_hash_lookup(C.byref(table_), _p(keys), n, _p(slot_out), _p(rows_out),
+                                 _stream(stream)), "rec_hash_lookup")
+
+
+def rec_din_plan_bytes(B: int, max_len: int) -> int:
+    return int(lib().rec_din_plan_bytes(B, max_len))
+
+
+def rec_din_plan(seq_lengths, B: int, max_len: int, task_positions: int, seq_offsets_out, plan,
+                 plan_bytes: int, stream=None):
+    _check(lib().rec_din_plan(_p(seq_lengths), B, max_len, task_positions, _p(seq_offsets_out),
+                              _p(plan), plan_bytes, _stream(stream)), "rec_din_plan")
+
+
+def rec_din_attn_fwd(seq_tables: Sequence[rec_table], seq_values, seq_stride: int, seq_offsets,
+                     seq_lengths, max_len: int, B: int, query, query_ld: int,
+                     query_col: Sequence[int], mlp: rec_din_mlp, plan, plan_bytes: int, out,
+                     scores_out=None, weights_out=None, rows_out=None, stream=None):
+    qc = None if query_col is None else (C.c_int32 * 3)(*query_col)
+    _check(lib().rec_din_attn_fwd(_tables(seq_tables), _p(seq_values), seq_stride,
+                                  _p(seq_offsets), _p(seq_lengths), max_len, B, _p(query),
+                                  query_ld, qc, C.byref(mlp) if mlp is not None else None,
+                                  _p(plan), plan_bytes, _p(out), _p(scores_out),
+                                  _p(weights_out), _p(rows_out), _stream(stream)),
+           "rec_din_attn_fwd")
+
+
+def rec_host_floor_mod(x: int, n: int) -> int:
+    return int(lib().rec_host_floor_mod(x, n))
+
+
+def rec_host_hash_home(x: int, capacity: int):
+    d = C.c_uint8(0)
+    home = int(lib().rec_host_hash_home(x, capacity, C.byref(d)))
+    return home, int(d.value)

@@ -1,0 +1,110 @@
+"""Shared helpers for the GPU parity tests: run the HIP forward through the
+C ABI on seeded inputs, run the oracle on the same inputs, compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+from sparse_embedding_din_amd import pipeline as PL
+
+DEV = torch.device("cuda")
+
+FP32_TOL = 1e-5     # max per-row relative error, fp32 MLP
+BF16_TOL = 2e-2     # max per-row relative error, bf16 MLP (fp32 accumulate)
+
+
+def say(*a):
+    print("[gpu]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max over rows of ||got - ref||_inf / ||ref||_inf; rows where the
+    reference is all zero must be exactly zero."""
+    got = np.asarray(got, np.float64).reshape(ref.shape[0], -1)
+    ref = np.asarray(ref, np.float64).reshape(ref.shape[0], -1)
+    assert np.all(np.isfinite(got)), "non-finite GPU output"
+    scale = np.max(np.abs(ref), axis=1)
+    zero = scale == 0
+    assert np.all(got[zero] == 0.0), "reference-zero rows are not exactly zero"
+    if (~zero).sum() == 0:
+        return 0.0
+    err = np.max(np.abs(got[~zero] - ref[~zero]), axis=1) / scale[~zero]
+    return float(err.max())
+
+
+class Run:
+    """One forward on the GPU with every debug output requested."""
+
+    def __init__(self, model, batch, task_positions=0, layout=None, debug=True, mlp_dtype=None):
+        self.model, self.batch = model, batch
+        B = batch.B
+        say(f"cfg={model.cfg.name} B={B} P={batch.seq_stride} nnz={batch.values.size} "
+            f"layout={'padded' if layout else 'packed'} C={task_positions}")
+        self.tabs = PL.DeviceTables(model.tables, DEV)
+        self.mlp = PL.DeviceMLP(model, DEV, dtype=mlp_dtype)
+        self.fwd = PL.SparseDinForward(self.tabs, self.mlp, B, model.cfg.max_len, DEV,
+                                       task_positions=task_positions)
+        if layout is None:
+            self.db = PL.DeviceBatch(batch, DEV)
+            stride = batch.seq_stride
+        else:
+            sv, so, stride = layout
+            self.db = PL.DeviceBatch(batch, DEV, seq_values=sv, seq_offsets=so, seq_stride=stride)
+        self.stride = stride
+        dbg = None
+        if debug:
+            dbg = dict(emb_rows=torch.full((max(batch.values.size, 1),), -7, dtype=torch.int64, device=DEV),
+                       scores=torch.full((max(stride, 1),), np.nan, dtype=torch.float32, device=DEV),
+                       weights=torch.full((max(stride, 1),), np.nan, dtype=torch.float32, device=DEV),
+                       seq_rows=torch.full((3 * max(stride, 1),), -7, dtype=torch.int64, device=DEV))
+        self.dbg = dbg
+        self.fwd.run(self.db, debug=dbg)
+        torch.cuda.synchronize()
+        self.offsets = self.fwd.offsets[: synth.T * B + 1].cpu().numpy()
+        self.seq_offsets = self.fwd.seq_offsets[: B + 1].cpu().numpy()
+        self.pooled = self.fwd.pooled[:B].cpu().numpy()
+        self.att = self.fwd.att[:B].cpu().numpy()
+        if debug:
+            self.emb_rows = dbg["emb_rows"].cpu().numpy()[: batch.values.size]
+            self.scores = dbg["scores"].cpu().numpy()
+            self.weights = dbg["weights"].cpu().numpy()
+            self.seq_rows = dbg["seq_rows"].cpu().numpy().reshape(3, -1)
+        say("done")
+
+
+def oracle_forward(model, batch, samples=None, want_scores=True):
+    return oracle.forward(model, batch, samples=samples, want_scores=want_scores)
+
+
+def oracle_rows(model, batch):
+    """Resolved rows of every deep id (key-major) and every sequence id."""
+    orc = oracle.get()
+    B = batch.B
+    off = orc.lengths_to_offsets(batch.lengths)
+    rows = np.empty(batch.values.size, np.int64)
+    for k in range(synth.T):
+        lo, hi = off[k * B], off[(k + 1) * B]
+        rows[lo:hi] = orc.resolve(model.tables[k], batch.values[lo:hi])
+    seq = np.empty_like(batch.seq_values)
+    for i, k in enumerate(synth.SEQ_KEYS):
+        seq[i] = orc.resolve(model.tables[k], batch.seq_values[i])
+    return rows, seq
+
+
+def gpu_scores_by_sample(run: Run, samples, max_len):
+    """GPU scores/weights rearranged to [ns][max_len] (packed layout only)."""
+    b = run.batch
+    starts = run.seq_offsets
+    ns = len(samples)
+    sc = np.zeros((ns, max_len))
+    wt = np.zeros((ns, max_len))
+    for i, s in enumerate(samples):
+        L = min(int(b.seq_lengths[s]), max_len)
+        sc[i, :L] = run.scores[starts[s]: starts[s] + L]
+        wt[i, :L] = run.weights[starts[s]: starts[s] + L]
+    return sc, wt

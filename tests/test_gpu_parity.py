@@ -1,0 +1,302 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Integers (offsets, resolved rows, hash slots) must match
+bit-exactly; floats within the per-row relative tolerance of the MLP's
+precision (1e-5 fp32, 2e-2 bf16 matrix cores with fp32 accumulation)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import (BF16_TOL, DEV, FP32_TOL, Run, gpu_scores_by_sample, oracle_forward,
+                         oracle_rows, row_rel_err, say)
+from sparse_embedding_din_amd import rec as R
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def models():
+    cache = {}
+
+    def get(i, **kw):
+        key = (i, tuple(sorted(kw.items())))
+        if key not in cache:
+            cache[key] = synth.make_model(synth.CONFIGS[i], **kw)
+        return cache[key]
+    return get
+
+
+def _tol(model):
+    return FP32_TOL if model.mlp_dtype == "f32" else BF16_TOL
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [0, 1, 5, 4095, 4096, 4097, 131089])
+def test_lengths_to_offsets(n):
+    rng = np.random.default_rng(n)
+    L = rng.integers(0, 4, size=n).astype(np.int32)
+    say(f"scan n={n}")
+    lt = torch.from_numpy(L).to(DEV)
+    off = torch.full((n + 1,), -5, dtype=torch.int64, device=DEV)
+    wsb = max(R.rec_scan_workspace_bytes(n), 8)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    R.rec_lengths_to_offsets(lt, n, off, ws, wsb)
+    torch.cuda.synchronize()
+    assert np.array_equal(off.cpu().numpy(), oracle.get().lengths_to_offsets(L))
+
+
+@pytest.mark.parametrize("B,max_len,C", [(1, 100, 0), (37, 100, 16), (4096, 100, 32),
+                                          (4097, 7, 64), (10000, 128, 48)])
+def test_din_plan(B, max_len, C):
+    rng = np.random.default_rng(B)
+    L = rng.integers(0, 140, size=B).astype(np.int32)
+    L[::7] = 0
+    say(f"plan B={B} max_len={max_len} C={C}")
+    lt = torch.from_numpy(L).to(DEV)
+    pb = R.rec_din_plan_bytes(B, max_len)
+    plan = torch.zeros(pb, dtype=torch.uint8, device=DEV)
+    so = torch.full((B + 1,), -5, dtype=torch.int64, device=DEV)
+    R.rec_din_plan(lt, B, max_len, C, so, plan, pb)
+    torch.cuda.synchronize()
+    orc = oracle.get()
+    assert np.array_equal(so.cpu().numpy(), orc.lengths_to_offsets(L))
+    p = plan.cpu().numpy()
+    hdr = p[:64].view(np.int32)
+    clamped = np.minimum(L, max_len)
+    P = int(clamped.sum())
+    assert hdr[0] == B and hdr[1] == max_len and hdr[4] == P
+    Cg = int(hdr[2])
+    assert Cg % 16 == 0 and 16 <= Cg <= 64 and (C == 0 or Cg == C)
+    nb = (B + 4095) // 4096
+    off_pos = (64 + 16 * nb + 15) // 16 * 16
+    pos = p[off_pos: off_pos + 4 * (B + 1)].view(np.int32)
+    assert np.array_equal(pos, orc.lengths_to_offsets(clamped))
+    off_task = (off_pos + 4 * (B + 1) + 15) // 16 * 16
+    nt = int(hdr[3])
+    assert nt == P // Cg + 1
+    tf = p[off_task: off_task + 4 * (nt + 1)].view(np.int32)
+    # tasks partition the samples: task t holds exactly the samples starting in [tC, (t+1)C)
+    assert tf[0] == 0 and tf[nt] == B and np.all(np.diff(tf) >= 0)
+    task_of = np.repeat(np.arange(nt), np.diff(tf))
+    assert np.array_equal(task_of, pos[:B] // Cg)
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg,B", [(1, 256), (1, 37), (2, 8192), (4, 65536), (5, 8192)])
+def test_embbag_parity(models, cfg, B):
+    m = models(cfg)
+    b = synth.make_batch(m, B=B)
+    r = Run(m, b)
+    orc = oracle.get()
+    assert np.array_equal(r.offsets, orc.lengths_to_offsets(b.lengths))
+    rows, _ = oracle_rows(m, b)
+    assert np.array_equal(r.emb_rows, rows)
+    ref = orc.embbag(m.tables, B, b.values, b.lengths, r.offsets)
+    assert row_rel_err(r.pooled, ref) <= 1e-6
+
+
+def test_embbag_edges(models):
+    """Empty bags, a single id per bag, every id of the signed range's edges."""
+    m = models(1)
+    b = synth.make_batch(m, B=33)
+    L = b.lengths.reshape(synth.T, 33).copy()
+    L[:, 0] = 0                       # sample 0: every bag empty
+    L[2, 5:9] = 0
+    L[4, 10:14] = 1
+    i64 = np.iinfo(np.int64)
+    edge = np.array([i64.min, i64.max, -1, 0, 1, i64.min + 1, i64.max - 1], np.int64)
+    vals = []
+    starts = np.concatenate([[0], np.cumsum(b.lengths)])
+    for k in range(synth.T):
+        for s in range(33):
+            i = k * 33 + s
+            v = b.values[starts[i]: starts[i] + L[k, s]].copy()
+            if k < 15 and v.size:
+                v[0] = edge[(k + s) % edge.size]
+            vals.append(v)
+    b.lengths = L.reshape(-1).astype(np.int32)
+    b.values = np.concatenate(vals)
+    r = Run(m, b)
+    rows, _ = oracle_rows(m, b)
+    assert np.array_equal(r.emb_rows, rows)
+    ref = oracle.get().embbag(m.tables, 33, b.values, b.lengths, r.offsets)
+    assert np.all(r.pooled[0] == 0.0)
+    assert row_rel_err(r.pooled, ref) <= 1e-6
+
+
+def test_hash_lookup(models):
+    m = models(5)
+    orc = oracle.get()
+    for k in m.cfg.hash_keys:
+        tab = m.tables[k]
+        rng = np.random.default_rng(k)
+        hits = tab["stored"][rng.integers(0, tab["stored"].size, 5000)]
+        miss = rng.integers(np.iinfo(np.int64).min, np.iinfo(np.int64).max, 3000, dtype=np.int64)
+        keys = np.concatenate([hits, miss, [synth.EMPTY_KEY]])
+        rng.shuffle(keys)
+        say(f"hash table {k} n={keys.size}")
+        vals = torch.from_numpy(tab["values"]).to(DEV)
+        kd = torch.from_numpy(tab["keys"]).to(DEV)
+        dg = torch.from_numpy(tab["digests"]).to(DEV)
+        desc = R.table(R.REC_HASH, tab["rows"], vals, kd, dg, None)
+        kt = torch.from_numpy(keys).to(DEV)
+        slot = torch.full((keys.size,), -9, dtype=torch.int64, device=DEV)
+        rows = torch.full((keys.size, 16), np.nan, dtype=torch.float32, device=DEV)
+        R.rec_hash_lookup(desc, kt, keys.size, slot, rows)
+        torch.cuda.synchronize()
+        ref = orc.resolve(tab, keys)
+        got = slot.cpu().numpy()
+        assert np.array_equal(got, ref)
+        rg = rows.cpu().numpy()
+        hit = ref >= 0
+        assert np.array_equal(rg[hit], tab["values"][ref[hit]])
+        assert np.all(rg[~hit] == 0.0) and not np.any(np.signbit(rg[~hit]))
+
+
+# ---------------------------------------------------------------------------
+DIN_CASES = [
+    (1, 256, None), (1, 1, None), (1, 37, None),
+    (2, 8192, None),
+    (3, 8192, 384),      # long sequences: sampled samples for the oracle
+    (4, 65536, 768),
+    (5, 8192, 2048),
+]
+
+
+@pytest.mark.parametrize("cfg,B,nsample", DIN_CASES)
+def test_din_parity(models, cfg, B, nsample):
+    m = models(cfg, bias=True)
+    b = synth.make_batch(m, B=B)
+    r = Run(m, b)
+    samples = None
+    if nsample is not None:
+        rng = np.random.default_rng(cfg)
+        samples = np.sort(rng.choice(B, size=nsample, replace=False))
+        samples[0] = 0
+        samples[-1] = B - 1
+    idx = np.arange(B) if samples is None else samples
+    o = oracle_forward(m, b, samples=samples)
+    tol = _tol(m)
+    assert row_rel_err(r.pooled[idx], o["pooled"]) <= 1e-6
+    assert row_rel_err(r.att[idx], o["att"]) <= tol
+    # score-level parity and softmax weights
+    sc, wt = gpu_scores_by_sample(r, idx, m.cfg.max_len)
+    L = np.minimum(b.seq_lengths[idx], m.cfg.max_len)
+    mask = np.arange(m.cfg.max_len)[None, :] < L[:, None]
+    escale = np.max(np.abs(o["scores"][mask]))
+    assert np.max(np.abs(sc[mask] - o["scores"][mask])) <= tol * escale
+    assert np.max(np.abs(wt[mask] - o["weights"][mask])) <= tol
+    sums = wt.sum(axis=1)
+    assert np.all(np.abs(sums[L > 0] - 1.0) <= 1e-5)
+    # resolved sequence rows, bit-exact
+    _, seq = oracle_rows(m, b)
+    assert np.array_equal(r.seq_rows[:, : b.seq_stride], seq)
+
+
+def test_din_sharp_fp32(models):
+    """Peaky softmax (embedding std 1, score weights x20) with the fp32 MLP:
+    MLP mistakes cannot hide behind near-uniform weights.  Scores must match
+    to the fp32 tolerance; the output bound is the one that score tolerance
+    implies: with p = softmax(e), |d att| <= 2 max|de| max_j |s_j| per
+    feature, so rows may deviate by 2 * (1e-5 * max|e|) * max|s| / |att|."""
+    m = synth.make_model(synth.CONFIGS[1], bias=True, emb_std=1.0, w3_scale=20.0)
+    b = synth.make_batch(m, B=200)
+    r = Run(m, b)
+    o = oracle_forward(m, b)
+    assert o["weights"].max() > 0.9
+    sc, _ = gpu_scores_by_sample(r, np.arange(200), 100)
+    mask = np.arange(100)[None, :] < b.seq_lengths[:, None]
+    emax = np.max(np.abs(o["scores"][mask]))
+    assert np.max(np.abs(sc[mask] - o["scores"][mask])) <= FP32_TOL * emax
+    _, _, _, S = __import__("oracle_pins").torch_padded_din(m, b, o["query"],
+                                                             r.seq_offsets[:-1], 100)
+    de = FP32_TOL * emax
+    for s in range(200):
+        if b.seq_lengths[s] == 0:
+            continue
+        bound = 2 * de * np.abs(S[s, : b.seq_lengths[s]]).max()
+        assert np.max(np.abs(r.att[s] - o["att"][s])) <= bound + FP32_TOL * np.abs(o["att"][s]).max()
+
+
+def test_din_sharp_bf16_scores(models):
+    """Peaky case through the bf16 matrix cores: score-level parity."""
+    m = synth.make_model(synth.CONFIGS[2], bias=True, emb_std=1.0, w3_scale=20.0)
+    b = synth.make_batch(m, B=512)
+    r = Run(m, b)
+    o = oracle_forward(m, b)
+    sc, _ = gpu_scores_by_sample(r, np.arange(512), 100)
+    mask = np.arange(100)[None, :] < b.seq_lengths[:, None]
+    assert np.max(np.abs(sc[mask] - o["scores"][mask])) <= BF16_TOL * np.max(np.abs(o["scores"][mask]))
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_din_padded_equals_packed(models, cfg):
+    """Padding-free means padding-blind: the same samples laid out with a
+    stride of 100 positions (garbage ids in the padding) give bit-identical
+    output, scores and weights."""
+    m = models(cfg, bias=True)
+    b = synth.make_batch(m, B=300)
+    r1 = Run(m, b)
+    lay = synth.padded_seq_layout(b, 100)
+    r2 = Run(m, b, layout=lay)
+    assert np.array_equal(r1.att, r2.att)
+    for s in range(0, 300, 7):
+        L = int(b.seq_lengths[s])
+        assert np.array_equal(r1.scores[r1.seq_offsets[s]: r1.seq_offsets[s] + L],
+                              r2.scores[100 * s: 100 * s + L])
+
+
+@pytest.mark.parametrize("C", [16, 32, 48, 64])
+def test_din_task_sizes(models, C):
+    """Every task size gives the same scores and a result within tolerance."""
+    m = models(2, bias=True)
+    b = synth.make_batch(m, B=1000)
+    r = Run(m, b, task_positions=C)
+    o = oracle_forward(m, b)
+    assert row_rel_err(r.att, o["att"]) <= BF16_TOL
+
+
+def test_din_edges(models):
+    """Empty sequences, length 1, lengths at and past the cap, one sample."""
+    m = models(1, bias=True)
+    b = synth.make_batch(m, B=64)
+    orig = b.seq_lengths.copy()
+    starts = np.concatenate([[0], np.cumsum(orig)])
+    L = orig.copy()
+    L[0] = 0
+    L[1] = 1
+    L[2] = 100
+    L[3] = 130        # longer than max_len: only the first 100 positions count
+    L[10:20] = 0
+    L[20:40] = 17
+    rng = np.random.default_rng(3)
+    parts = []
+    for s in range(64):
+        if L[s] <= orig[s]:
+            parts.append(b.seq_values[:, starts[s]: starts[s] + L[s]])
+        else:
+            parts.append(rng.integers(-2**62, 2**62, size=(3, L[s]), dtype=np.int64))
+    b.seq_values = np.ascontiguousarray(np.concatenate(parts, axis=1))
+    b.seq_lengths = L.astype(np.int32)
+    b.seq_stride = b.seq_values.shape[1]
+    r = Run(m, b)
+    o = oracle_forward(m, b)
+    assert np.all(r.att[0] == 0.0) and np.all(r.att[10:20] == 0.0)
+    assert row_rel_err(r.att, o["att"]) <= FP32_TOL
+    # one position: weight exactly 1, output equal to that position's rows
+    assert r.weights[r.seq_offsets[1]] == 1.0
+    _, seq = oracle_rows(m, b)
+    s1 = np.concatenate([m.tables[k]["values"][seq[i, r.seq_offsets[1]]]
+                         for i, k in enumerate(synth.SEQ_KEYS)])
+    assert np.array_equal(r.att[1], s1)
+
+
+def test_din_deterministic(models):
+    m = models(2, bias=True)
+    b = synth.make_batch(m, B=4096)
+    r1 = Run(m, b)
+    r2 = Run(m, b)
+    assert np.array_equal(r1.att, r2.att)
+    assert np.array_equal(r1.pooled, r2.pooled)
+    assert np.array_equal(r1.scores[: b.seq_stride], r2.scores[: b.seq_stride])
