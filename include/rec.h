@@ -55,13 +55,14 @@ typedef enum {
 } rec_status;
 
 enum { REC_DIRECT = 0, REC_HASH = 1 };   /* rec_table.kind */
-enum { REC_F32 = 0, REC_BF16 = 1 };      /* rec_din_mlp.dtype */
+enum { REC_F32 = 0, REC_BF16 = 1, REC_BF16_PACKED = 2 };   /* rec_din_mlp.dtype */
 
 #define REC_DIM 16                        /* embedding width of every table */
 #define REC_EMPTY_KEY ((int64_t)-1)       /* empty hash slot; never a valid key */
 #define REC_MAX_TABLES 32                 /* tables per rec_embbag_fwd call */
 #define REC_MAX_SEQ_LEN 128               /* largest max_len for the DIN call */
 #define REC_MAX_B 16777215                /* largest batch for the DIN plan */
+#define REC_DIN_PACKED_BYTES 131072       /* packed bf16 W1+W2 (rec_din_pack_mlp) */
 
 /*
  * One embedding table (host struct; the arrays inside are device memory).
@@ -115,6 +116,9 @@ typedef struct {
  * nearest even) and multiplied on the matrix cores with fp32 accumulation; the
  * 64-wide layer, score, softmax and weighted sum stay fp32.
  * dtype REC_F32: every product and sum is fp32.
+ * dtype REC_BF16_PACKED: as REC_BF16, but w1 points to the REC_DIN_PACKED_BYTES
+ * image written by rec_din_pack_mlp (both layers, in the order the attention
+ * kernel keeps them on chip) and w2 is not read.  Same results as REC_BF16.
  * w1 and w2 16-byte aligned.
  */
 typedef struct {
@@ -127,6 +131,17 @@ typedef struct {
     const float* w3;
     float b3;
 } rec_din_mlp;
+
+/*
+ * Pre-pack the bf16 attention-MLP weights once (e.g. at model load) for the
+ * attention kernel: reads mlp->w1 [256][192] and mlp->w2 [64][256] (dtype
+ * REC_BF16, plain layout) and writes their matrix-core operand order into
+ * `packed` (device, 16-byte aligned, >= REC_DIN_PACKED_BYTES bytes).  Use it
+ * with dtype REC_BF16_PACKED.  The values are copied unchanged.
+ * Errors: REC_EINVAL (null/misaligned pointers, dtype not REC_BF16),
+ * REC_EWORKSPACE (packed_bytes too small).
+ */
+rec_status rec_din_pack_mlp(const rec_din_mlp* mlp, void* packed, size_t packed_bytes, void* stream);
 
 /* Bytes of workspace rec_lengths_to_offsets needs for n lengths. */
 size_t rec_scan_workspace_bytes(int64_t n);

@@ -153,6 +153,18 @@ rec_status rec_hash_lookup(const rec_table* table, const int64_t* keys, int64_t 
     return hip_status(launch_hash_lookup(a, (hipStream_t)stream), "rec_hash_lookup");
 }
 
+rec_status rec_din_pack_mlp(const rec_din_mlp* mlp, void* packed, size_t packed_bytes, void* stream) {
+    if (!mlp) return fail(REC_EINVAL, "rec_din_pack_mlp: mlp is NULL");
+    if (mlp->dtype != REC_BF16) return fail(REC_EINVAL, "rec_din_pack_mlp: dtype must be REC_BF16");
+    if (!mlp->w1 || !mlp->w2) return fail(REC_EINVAL, "rec_din_pack_mlp: w1 and w2 are required");
+    if (!packed) return fail(REC_EINVAL, "rec_din_pack_mlp: packed is NULL");
+    if (!aligned16(mlp->w1) || !aligned16(mlp->w2) || !aligned16(packed))
+        return fail(REC_EINVAL, "rec_din_pack_mlp: pointers must be 16-byte aligned");
+    if (packed_bytes < REC_DIN_PACKED_BYTES)
+        return fail(REC_EWORKSPACE, "rec_din_pack_mlp: packed smaller than REC_DIN_PACKED_BYTES");
+    return hip_status(launch_din_pack(mlp->w1, mlp->w2, packed, (hipStream_t)stream), "rec_din_pack_mlp");
+}
+
 size_t rec_din_plan_bytes(int64_t B, int32_t max_len) {
     if (B < 0 || max_len < 1 || max_len > REC_MAX_SEQ_LEN || B > REC_MAX_B) return 0;
     return plan_layout(B, max_len).bytes;
@@ -203,11 +215,12 @@ rec_status rec_din_attn_fwd(const rec_table* seq_tables, const int64_t* seq_valu
         if (query_col[f] < 0 || (query_col[f] & 3) || query_col[f] + 16 > query_ld)
             return fail(REC_EINVAL, "rec_din_attn_fwd: query_col must be multiples of 4 inside query_ld");
     if (!mlp) return fail(REC_EINVAL, "rec_din_attn_fwd: mlp is NULL");
-    if (mlp->dtype != REC_F32 && mlp->dtype != REC_BF16)
+    if (mlp->dtype != REC_F32 && mlp->dtype != REC_BF16 && mlp->dtype != REC_BF16_PACKED)
         return fail(REC_EINVAL, "rec_din_attn_fwd: unknown mlp dtype");
-    if (!mlp->w1 || !mlp->b1 || !mlp->w2 || !mlp->b2 || !mlp->w3)
+    const bool packed = mlp->dtype == REC_BF16_PACKED;
+    if (!mlp->w1 || !mlp->b1 || (!packed && !mlp->w2) || !mlp->b2 || !mlp->w3)
         return fail(REC_EINVAL, "rec_din_attn_fwd: mlp arrays are required");
-    if (!aligned16(mlp->w1) || !aligned16(mlp->w2))
+    if (!aligned16(mlp->w1) || (!packed && !aligned16(mlp->w2)))
         return fail(REC_EINVAL, "rec_din_attn_fwd: w1/w2 not 16-byte aligned");
     if (!out) return fail(REC_EINVAL, "rec_din_attn_fwd: out is NULL");
     if (!aligned16(out)) return fail(REC_EINVAL, "rec_din_attn_fwd: out not 16-byte aligned");
@@ -243,7 +256,7 @@ rec_status rec_din_attn_fwd(const rec_table* seq_tables, const int64_t* seq_valu
     a.dtype = mlp->dtype;
     a.plan_hdr = (const int32_t*)p;
     a.pos_start = (const int32_t*)(p + L.off_pos);
-    a.task_first = (const int32_t*)(p + L.off_task);
+    a.task_info = (const int2*)(p + L.off_task);
     a.out = out;
     a.scores = scores_out;
     a.weights = weights_out;

@@ -6,57 +6,90 @@
 // gives the zero vector); DLRM essay (wmrh.cn/news/12459) §3.2 (EmbeddingBag
 // sum pooling).
 //
-// Layout on the GPU: one wave pools one sample's 16 bags.  Lane l serves
-// bag t = l/4 and the 16-byte quarter q = l%4 of each 64-byte row, so a
-// wave's row loads are 16 rows x 64 B and its output store is the sample's
-// whole 1 KiB KeyedTensor row in one coalesced write.  Ids are taken four at a
-// time so that four independent row loads per lane are in flight.
+// Layout on the GPU: a wave pools two tables (2p, 2p+1) for 32 consecutive
+// samples: lanes 0-31 take table 2p, lanes 32-63 table 2p+1, one bag per lane.
+// Both descriptors are wave-uniform, the lengths/offsets of a wave are two
+// 128-byte runs of the key-major KJT, and each sample's two 64-byte outputs
+// form one full 128-byte line.  Every load is issued unconditionally (indices
+// are clamped into the bag, rows of misses point at row 0) and masked
+// afterwards, so a lane has all of a round's id loads and then all of its row
+// loads in flight at once.
 #include "rec_internal.h"
 
 namespace rec {
 namespace {
 
-constexpr int kWaves = 4;            // waves (samples) per workgroup
-constexpr int kUnroll = 4;           // ids resolved per round
+constexpr int kWaves = 4;            // waves per workgroup
+constexpr int kUnroll = 3;           // ids per bag resolved per round
 
+template <bool kHash>
 __global__ __launch_bounds__(64 * kWaves) void k_embbag_fwd(const EmbArgs a) {
     const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const int64_t b = item / a.chunks;
-    const int t = (int)(item % a.chunks) * 16 + (lane >> 2);
-    const int q = lane & 3;
-    if (b >= a.B || t >= a.T) return;
-    const TabDev& tab = a.tab[t];
-    const int64_t bag = (int64_t)t * a.B + b;
-    const int32_t len = a.lengths[bag];
+    const int64_t w = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int64_t nbw = (a.B + 31) / 32;
+    const int tp = (int)(w / nbw);
+    if (2 * tp >= a.T) return;                               // wave-uniform
+    const int64_t b = (w % nbw) * 32 + (lane & 31);
+    const int t = 2 * tp + (lane >> 5);
+    const bool live = b < a.B && t < a.T;
+    const TabDev& t0 = a.tab[2 * tp];
+    const TabDev& t1 = a.tab[2 * tp + 1];                    // zeroed past T
+    // lanes of a missing odd table read table 2p's rows (masked out below)
+    const bool hi = lane >= 32 && 2 * tp + 1 < a.T;
+    const float* vals = hi ? t1.values : t0.values;
+    const int64_t rows = hi ? t1.rows : t0.rows;
+    const uint64_t magic = hi ? t1.magic : t0.magic;
+    const int32_t shift = hi ? t1.shift : t0.shift;
+    const int64_t bag = (int64_t)min(t, a.T - 1) * a.B + min(b, a.B - 1);
+    int32_t len = a.lengths[bag];
     const int64_t off = a.offsets[bag];
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j0 = 0; j0 < len; j0 += kUnroll) {
-        int64_t row[kUnroll];
+    if (!live) len = 0;
+    float4 acc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0; __ballot(j0 < len) != 0; j0 += kUnroll) {
+        int64_t raw[kUnroll], row[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            row[u] = (j0 + u < len) ? resolve_row(tab, a.values[off + j0 + u]) : -1;
-        float4 v[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            v[u] = row[u] >= 0 ? *(const float4*)(tab.values + row[u] * 16 + 4 * q)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+            raw[u] = a.values[len > 0 ? off + min(j0 + u, len - 1) : 0];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            if (j0 + u < len) {
-                acc.x += v[u].x;
-                acc.y += v[u].y;
-                acc.z += v[u].z;
-                acc.w += v[u].w;
+            if (kHash) {
+                const TabDev& tb = hi ? t1 : t0;
+                row[u] = tb.kind == REC_HASH ? hash_probe(tb, raw[u]) : floor_mod_magic(raw[u], rows, magic, shift);
+            } else {
+                row[u] = floor_mod_magic(raw[u], rows, magic, shift);
             }
         }
-        if (a.rows_out && q == 0) {
+        float4 v[kUnroll][4];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const float4* src = (const float4*)(vals + (row[u] >= 0 ? row[u] : 0) * 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[u][r] = src[r];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const bool use = j0 + u < len && row[u] >= 0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                acc[r].x += use ? v[u][r].x : 0.f;
+                acc[r].y += use ? v[u][r].y : 0.f;
+                acc[r].z += use ? v[u][r].z : 0.f;
+                acc[r].w += use ? v[u][r].w : 0.f;
+            }
+        }
+        if (a.rows_out) {
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
                 if (j0 + u < len) a.rows_out[off + j0 + u] = row[u];
         }
     }
-    *(float4*)(a.out + b * (int64_t)a.T * 16 + t * 16 + 4 * q) = acc;
+    if (live) {
+        float4* o = (float4*)(a.out + b * (int64_t)a.T * 16 + t * 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = acc[r];
+    }
 }
 
 __global__ __launch_bounds__(64 * kWaves) void k_hash_lookup(const HashArgs a) {
@@ -76,9 +109,12 @@ __global__ __launch_bounds__(64 * kWaves) void k_hash_lookup(const HashArgs a) {
 }  // namespace
 
 hipError_t launch_embbag(const EmbArgs& a, hipStream_t s) {
-    const int64_t items = a.B * a.chunks;
-    const int64_t blocks = (items + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL(k_embbag_fwd, dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, a);
+    const int64_t waves = (int64_t)((a.T + 1) / 2) * ((a.B + 31) / 32);
+    const int64_t blocks = (waves + kWaves - 1) / kWaves;
+    bool hash = false;
+    for (int t = 0; t < a.T; ++t) hash = hash || a.tab[t].kind == REC_HASH;
+    if (hash) hipLaunchKernelGGL(k_embbag_fwd<true>, dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, a);
+    else hipLaunchKernelGGL(k_embbag_fwd<false>, dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, a);
     return hipGetLastError();
 }
 

@@ -108,7 +108,10 @@ inline int64_t scan_blocks(int64_t n) { return (n + kScanChunk - 1) / kScanChunk
 //                      num_tasks, P (total packed positions), nblocks
 //   [64, 64+16*nb)     int64 pairs: per-block sums (clamped, raw)
 //   pos_start          int32[B+1], 16-byte aligned
-//   task_first         int32[max_tasks+1]
+//   task_info          int32 pairs [max_tasks+1][2]: (first sample of the
+//                      task, packed start of that sample); task t holds
+//                      samples [info[t].x, info[t+1].x) and positions
+//                      [info[t].y, info[t+1].y)
 enum { kHdrB = 0, kHdrMaxLen, kHdrC, kHdrNumTasks, kHdrP, kHdrNBlocks };
 constexpr int kMinTaskPositions = 16;
 constexpr int kMaxTaskPositions = 64;
@@ -127,7 +130,7 @@ inline PlanLayout plan_layout(int64_t B, int32_t max_len) {
     p.off_sums = 64;
     p.off_pos = align16(p.off_sums + 16 * (size_t)p.nblocks);
     p.off_task = align16(p.off_pos + 4 * (size_t)(B + 1));
-    p.bytes = align16(p.off_task + 4 * (size_t)(p.max_tasks + 1));
+    p.bytes = align16(p.off_task + 8 * (size_t)(p.max_tasks + 1));
     return p;
 }
 
@@ -179,7 +182,7 @@ struct DinArgs {
     int32_t dtype;
     const int32_t* plan_hdr;
     const int32_t* pos_start;
-    const int32_t* task_first;
+    const int2* task_info;
     float* out;
     float* scores;
     float* weights;
@@ -187,7 +190,8 @@ struct DinArgs {
     int64_t B;
     int64_t max_tasks;
 };
-constexpr int kDinWaves = 8;                 // waves per workgroup
+constexpr int kDinWaves = 4;                 // waves per workgroup (one per SIMD)
 hipError_t launch_din(const DinArgs& a, int num_cus, hipStream_t s);
+hipError_t launch_din_pack(const void* w1, const void* w2, void* packed, hipStream_t s);
 
 }  // namespace rec

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_apply(const int32_t* __re
                                                             int64_t* __restrict__ seq_off,
                                                             int32_t* __restrict__ hdr,
                                                             int32_t* __restrict__ pos_start,
-                                                            int32_t* __restrict__ task_first) {
+                                                            int2* __restrict__ task_info) {
     __shared__ int32_t sl[kScanChunk + kScanChunk / 16];
     __shared__ int64_t red[kScanThreads / 64];
     const int64_t base = (int64_t)blockIdx.x * kScanChunk;
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_apply(const int32_t* __re
     }
     int64_t pc = block_excl_scan(rc, red) + bc;     // clamped prefix before this thread
     int64_t pr = block_excl_scan(rr, red) + br;     // raw prefix before this thread
-    if (blockIdx.x == 0 && t == 0) task_first[0] = 0;
+    if (blockIdx.x == 0 && t == 0) task_info[0] = make_int2(0, 0);
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
         const int64_t b = base + t * kScanItems + k;
@@ -176,7 +176,7 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_apply(const int32_t* __re
         // pc < t*C <= next; the last sample also closes the task list.
         int64_t t_hi = next / C;
         if (b == B - 1) t_hi += 1;
-        for (int64_t tt = pc / C + 1; tt <= t_hi; ++tt) task_first[tt] = (int32_t)(b + 1);
+        for (int64_t tt = pc / C + 1; tt <= t_hi; ++tt) task_info[tt] = make_int2((int32_t)(b + 1), (int32_t)next);
         if (b == B - 1) {
             pos_start[B] = (int32_t)next;
             if (seq_off) seq_off[B] = pr + v[k];
@@ -217,7 +217,7 @@ hipError_t launch_din_plan(const int32_t* seq_lengths, int64_t B, int32_t max_le
     hipLaunchKernelGGL(k_plan_apply, dim3((unsigned)L.nblocks), dim3(kScanThreads), 0, s,
                        seq_lengths, B, max_len, task_positions, total_waves, L.nblocks, sums,
                        seq_offsets_out, (int32_t*)p, (int32_t*)(p + L.off_pos),
-                       (int32_t*)(p + L.off_task));
+                       (int2*)(p + L.off_task));
     return hipGetLastError();
 }
 

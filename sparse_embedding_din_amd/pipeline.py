@@ -56,7 +56,10 @@ class DeviceTables:
 
 
 class DeviceMLP:
-    def __init__(self, model, device, dtype: Optional[str] = None):
+    """Attention-MLP weights on the device.  bf16 weights are pre-packed once
+    (rec_din_pack_mlp) unless packed=False."""
+
+    def __init__(self, model, device, dtype: Optional[str] = None, packed: bool = True):
         dt = dtype or getattr(model, "mlp_dtype", "f32")
         if dt == "bf16":
             self.dtype = R.REC_BF16
@@ -71,6 +74,11 @@ class DeviceMLP:
         self.w3 = _to(np.asarray(model.w3, np.float32), device)
         self.b3 = float(model.b3)
         self.desc = R.din_mlp(self.dtype, self.w1, self.b1, self.w2, self.b2, self.w3, self.b3)
+        if self.dtype == R.REC_BF16 and packed:
+            self.packed = torch.empty(R.REC_DIN_PACKED_BYTES, dtype=torch.uint8, device=device)
+            R.rec_din_pack_mlp(self.desc, self.packed, R.REC_DIN_PACKED_BYTES)
+            self.dtype = R.REC_BF16_PACKED
+            self.desc = R.din_mlp(self.dtype, self.packed, self.b1, None, self.b2, self.w3, self.b3)
 
 
 class DeviceBatch:
@@ -129,9 +137,22 @@ class SparseDinForward:
                            self.mlp.desc, self.plan, self.plan_bytes, self.att, scores, weights,
                            rows, stream)
 
-    def run(self, b: DeviceBatch, stream=None, debug: Optional[dict] = None):
+    def run(self, b: DeviceBatch, stream=None, debug: Optional[dict] = None, side=None):
+        """The forward on torch's current stream.  With `side` (another
+        torch stream), the sequence plan runs there, concurrently with the
+        offsets scan and the embedding bags, and joins before the attention."""
         assert b.B <= self.B_max
         d = debug or {}
+        if side is not None:
+            main = torch.cuda.current_stream()
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                self.plan_step(b)
+            self.offsets_step(b)
+            self.embbag_step(b, d.get("emb_rows"))
+            main.wait_stream(side)
+            self.din_step(b, d.get("scores"), d.get("weights"), d.get("seq_rows"))
+            return self.pooled[: b.B], self.att[: b.B]
         self.offsets_step(b, stream)
         self.plan_step(b, stream)
         self.embbag_step(b, d.get("emb_rows"), stream)

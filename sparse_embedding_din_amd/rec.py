@@ -17,14 +17,15 @@ LIB_PATH = os.path.join(HERE, "librec.so")
 
 REC_OK, REC_EINVAL, REC_EUNSUPPORTED, REC_EHIP, REC_EWORKSPACE = 0, -1, -2, -3, -4
 REC_DIRECT, REC_HASH = 0, 1
-REC_F32, REC_BF16 = 0, 1
+REC_F32, REC_BF16, REC_BF16_PACKED = 0, 1, 2
+REC_DIN_PACKED_BYTES = 131072
 REC_DIM = 16
 REC_EMPTY_KEY = -1
 REC_MAX_TABLES = 32
 REC_MAX_SEQ_LEN = 128
 REC_MAX_B = 16777215
 
-EXPORTS = ["rec_scan_workspace_bytes", "rec_lengths_to_offsets", "rec_embbag_fwd",
+EXPORTS = ["rec_din_pack_mlp", "rec_scan_workspace_bytes", "rec_lengths_to_offsets", "rec_embbag_fwd",
            "rec_hash_lookup", "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_fwd",
            "rec_last_error", "rec_version", "rec_host_floor_mod", "rec_host_hash_home"]
 
@@ -68,8 +69,9 @@ def lib():
         L.rec_din_attn_fwd.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, i32, i64, vp, i64,
                                        C.POINTER(C.c_int32), C.POINTER(rec_din_mlp), vp, sz, vp,
                                        vp, vp, vp, vp]
+        L.rec_din_pack_mlp.argtypes = [C.POINTER(rec_din_mlp), vp, sz, vp]
         for f in ("rec_lengths_to_offsets", "rec_embbag_fwd", "rec_hash_lookup", "rec_din_plan",
-                  "rec_din_attn_fwd"):
+                  "rec_din_attn_fwd", "rec_din_pack_mlp"):
             getattr(L, f).restype = C.c_int
         L.rec_last_error.argtypes = []
         L.rec_last_error.restype = C.c_char_p
@@ -150,6 +152,11 @@ def rec_embbag_fwd(tables: Sequence[rec_table], T: int, B: int, values, lengths,
 def rec_hash_lookup(table_: rec_table, keys, n: int, slot_out=None, rows_out=None, stream=None):
     _check(lib().rec_hash_lookup(C.byref(table_), _p(keys), n, _p(slot_out), _p(rows_out),
                                  _stream(stream)), "rec_hash_lookup")
+
+
+def rec_din_pack_mlp(mlp: rec_din_mlp, packed, packed_bytes: int, stream=None):
+    _check(lib().rec_din_pack_mlp(C.byref(mlp) if mlp is not None else None, _p(packed),
+                                  packed_bytes, _stream(stream)), "rec_din_pack_mlp")
 
 
 def rec_din_plan_bytes(B: int, max_len: int) -> int:

@@ -40,13 +40,14 @@ def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
 class Run:
     """One forward on the GPU with every debug output requested."""
 
-    def __init__(self, model, batch, task_positions=0, layout=None, debug=True, mlp_dtype=None):
+    def __init__(self, model, batch, task_positions=0, layout=None, debug=True, mlp_dtype=None,
+                 packed=True):
         self.model, self.batch = model, batch
         B = batch.B
         say(f"cfg={model.cfg.name} B={B} P={batch.seq_stride} nnz={batch.values.size} "
             f"layout={'padded' if layout else 'packed'} C={task_positions}")
         self.tabs = PL.DeviceTables(model.tables, DEV)
-        self.mlp = PL.DeviceMLP(model, DEV, dtype=mlp_dtype)
+        self.mlp = PL.DeviceMLP(model, DEV, dtype=mlp_dtype, packed=packed)
         self.fwd = PL.SparseDinForward(self.tabs, self.mlp, B, model.cfg.max_len, DEV,
                                        task_positions=task_positions)
         if layout is None:

@@ -75,9 +75,11 @@ def test_din_plan(B, max_len, C):
     off_task = (off_pos + 4 * (B + 1) + 15) // 16 * 16
     nt = int(hdr[3])
     assert nt == P // Cg + 1
-    tf = p[off_task: off_task + 4 * (nt + 1)].view(np.int32)
+    ti = p[off_task: off_task + 8 * (nt + 1)].view(np.int32).reshape(nt + 1, 2)
+    tf = ti[:, 0]
     # tasks partition the samples: task t holds exactly the samples starting in [tC, (t+1)C)
     assert tf[0] == 0 and tf[nt] == B and np.all(np.diff(tf) >= 0)
+    assert np.array_equal(ti[:, 1], pos[tf])
     task_of = np.repeat(np.arange(nt), np.diff(tf))
     assert np.array_equal(task_of, pos[:B] // Cg)
 
@@ -169,6 +171,10 @@ def test_din_parity(models, cfg, B, nsample):
     m = models(cfg, bias=True)
     b = synth.make_batch(m, B=B)
     r = Run(m, b)
+    if m.mlp_dtype == "bf16" and B <= 8192:
+        # the plain bf16 weight layout (permuted on chip) gives identical results
+        r2 = Run(m, b, packed=False)
+        assert np.array_equal(r.att, r2.att)
     samples = None
     if nsample is not None:
         rng = np.random.default_rng(cfg)
