@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=2)
     p.add_argument("--batches", type=int, default=4)
-    p.add_argument("--task-positions", type=int, default=0)
+    p.add_argument("--range-positions", type=int, default=0)
     p.add_argument("--kernel-reps", type=int, default=100)
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-graph", action="store_true")
@@ -105,7 +105,7 @@ def main():
     # one set of buffers (offsets, plan, outputs) per resident batch, so any
     # call can be replayed for any batch without stale bookkeeping
     dbs = [PL.DeviceBatch(b, dev) for b in batches]
-    fwds = [PL.SparseDinForward(tabs, mlp, B, cfg.max_len, dev, task_positions=a.task_positions)
+    fwds = [PL.SparseDinForward(tabs, mlp, B, cfg.max_len, dev, range_positions=a.range_positions)
             for _ in dbs]
     nb = len(dbs)
     stream = torch.cuda.Stream()

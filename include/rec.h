@@ -87,7 +87,7 @@ enum { REC_F32 = 0, REC_BF16 = 1, REC_BF16_PACKED = 2 };   /* rec_din_mlp.dtype 
  *   sequence home, home+1, ... at the time it was inserted (no deletes).  A
  *   lookup of key x returns the slot holding x, or -1 (a miss) on reaching an
  *   empty slot or after `rows` probes.  A miss yields the zero vector
- *   (§3.2 "CONSTANT=0").  The raw id is the key (no modulo).
+ *   (§3.2: the constant zero vector).  The raw id is the key (no modulo).
  *
  * Every table: dim == 16, rows >= 1 (REC_HASH: rows <= 2^31 - 1), values
  * 16-byte aligned (each row is 64 contiguous bytes).
@@ -192,65 +192,82 @@ rec_status rec_embbag_fwd(const rec_table* tables, int32_t T, int64_t B,
 rec_status rec_hash_lookup(const rec_table* table, const int64_t* keys, int64_t n,
                            int64_t* slot_out, float* rows_out, void* stream);
 
-/* Bytes of the DIN plan buffer for B samples capped at max_len positions. */
+/* Bytes of the DIN plan buffer for B samples capped at max_len positions
+ * (about 20 bytes per possible position, B * max_len, plus per-sample data);
+ * 0 for invalid arguments. */
 size_t rec_din_plan_bytes(int64_t B, int32_t max_len);
 
 /*
- * Sequence bookkeeping for the padding-free DIN ("当前现状分析" §4.1: real
- * lengths are ~3-5 of a cap of 100, so positions are packed, not padded).
- * From seq_lengths int32[B] it computes, on the device:
- *   - the packed start of every sample over min(len, max_len) positions,
- *   - a partition of the samples into tasks of about `task_positions`
- *     positions each (0 = choose from the batch), each a run of whole samples,
- * into `plan` (>= rec_din_plan_bytes(B, max_len) bytes, 16-byte aligned,
- * opaque, read by rec_din_attn_fwd).  If seq_offsets_out is non-NULL it also
- * receives the jagged offsets: int64[B+1], the exclusive prefix sum of the
- * unclamped seq_lengths.
- * The plan depends only on (seq_lengths, B, max_len, task_positions), so the
- * same plan serves any sequence layout with those lengths.
- * Errors: REC_EINVAL (null seq_lengths/plan, B < 0, max_len outside
- * [1, REC_MAX_SEQ_LEN], task_positions not 0 or a multiple of 16 in [16, 64]),
- * REC_EUNSUPPORTED (B > REC_MAX_B), REC_EWORKSPACE.
+ * Sequence side of the forward, before the attention ("当前现状分析" §4.1:
+ * real lengths are ~3-5 of a cap of 100, so positions are packed, not padded;
+ * §3 / "集成 DynamicEmb" §3.2 for the id -> row rule).  On the device it
+ *   - packs the positions: sample b, step j < L_b = min(seq_lengths[b],
+ *     max_len) becomes packed position pos_start(b) + j, where pos_start is
+ *     the exclusive prefix sum of the L_b;
+ *   - records how rec_din_attn_fwd splits the P = sum L_b packed positions
+ *     over its waves: ranges of `range_positions` positions (0 = P split
+ *     evenly over every wave the device runs at once, rounded up to 16);
+ *   - resolves the three sub-feature ids of every packed position to its row
+ *     (direct: floor modulo; hash: probe, -1 on a miss).
+ * Inputs:
+ *   seq_tables  host array of 3 descriptors (adgroup, cate, brand); each at
+ *               most 2^31 - 1 rows
+ *   seq_values  int64 [3][seq_stride]: sub-feature f's id at step j of sample b
+ *               is seq_values[f*seq_stride + off_b + j]
+ *   seq_offsets int64[B] giving off_b (any layout, e.g. padded off_b = 100 b),
+ *               or NULL for the packed jagged layout (off_b = exclusive prefix
+ *               sum of the unclamped seq_lengths)
+ *   seq_lengths int32[B], each >= 0
+ * Outputs:
+ *   plan            >= rec_din_plan_bytes(B, max_len) bytes, 16-byte aligned,
+ *                   opaque; used by rec_din_attn_fwd
+ *   seq_offsets_out int64[B+1] or NULL: exclusive prefix sum of the unclamped
+ *                   seq_lengths (the jagged offsets)
+ *   rows_out        int64 [3][seq_stride] or NULL: the row/slot of every id
+ *                   read (positions past L_b are never read or written)
+ * Errors: REC_EINVAL (null seq_tables/seq_values/seq_lengths/plan, bad table,
+ * B < 0, max_len outside [1, REC_MAX_SEQ_LEN], range_positions not 0 or a
+ * multiple of 16 in [16, 2^20]), REC_EUNSUPPORTED (B > REC_MAX_B, a table
+ * above 2^31 - 1 rows), REC_EWORKSPACE.
  */
-rec_status rec_din_plan(const int32_t* seq_lengths, int64_t B, int32_t max_len,
-                        int32_t task_positions, int64_t* seq_offsets_out,
+rec_status rec_din_plan(const rec_table* seq_tables, const int64_t* seq_values,
+                        int64_t seq_stride, const int64_t* seq_offsets,
+                        const int32_t* seq_lengths, int64_t B, int32_t max_len,
+                        int32_t range_positions, int64_t* seq_offsets_out, int64_t* rows_out,
                         void* plan, size_t plan_bytes, void* stream);
 
 /*
- * DIN target attention, padding-free ("当前现状分析" §4.2, §4.4).
- * For sample b with L = min(seq_lengths[b], max_len) positions j < L:
- *   s_j = [adgroup row | cate row | brand row] of ids
- *         seq_values[f*seq_stride + seq_offsets[b] + j], f = 0, 1, 2, looked up
- *         in seq_tables[f] (direct or hash; a miss is the zero row)
+ * DIN target attention, padding-free ("当前现状分析" §4.2, §4.4), over a plan
+ * from rec_din_plan (same seq_tables, B and max_len).  For sample b with L_b
+ * positions (rows resolved by the plan):
+ *   s_j = [adgroup row | cate row | brand row] (48 floats; a miss is zeros)
  *   q   = query[b*query_ld + query_col[f] + d] (f = 0..2, d < 16), the pooled
- *         target features (for the pooled output of rec_embbag_fwd with the
- *         16 deep features in page order: query_ld 256, query_col {16, 80, 48})
+ *         target features (for rec_embbag_fwd's output with the 16 deep
+ *         features in page order: query_ld 256, query_col {16, 80, 48})
  *   e_j = w3 . relu(W2 relu(W1 [q, s_j, q - s_j, q*s_j] + b1) + b2) + b3
- *   p_j = softmax over j < L of e_j (max-subtracted, no temperature)
- *   out[b][0..48) = sum_j p_j s_j;  L == 0 gives 48 x +0.0
- * Positions j >= L are never read, so a padded layout (seq_offsets[b] = b*100)
- * and a packed one (seq_offsets = the jagged offsets) give bit-identical output.
- *   seq_tables  host array of 3 descriptors (adgroup, cate, brand)
- *   plan        from rec_din_plan for the same seq_lengths, B and max_len
+ *   p_j = softmax over j < L_b of e_j (max-subtracted, no temperature)
+ *   out[b][0..48) = sum_j p_j s_j;  L_b == 0 gives 48 x +0.0
+ * Positions past L_b are never read, so any sequence layout with the same
+ * lengths gives bit-identical output.  A sample cut by a range edge is merged
+ * from per-range partial sums, so a different range_positions may change the
+ * last bits of its output (not of scores_out).
+ * The plan's partial-sum area is written: calls that share a plan must not
+ * overlap.
+ *   seq_tables  host array of 3 descriptors (the same as for the plan)
  *   mlp         host struct (device arrays inside)
  *   out         fp32 [B][48], 16-byte aligned
- *   scores_out  fp32, indexed like seq_values' positions (seq_offsets[b] + j),
- *               or NULL: e_j
- *   weights_out same indexing or NULL: p_j (requires scores_out)
- *   rows_out    int64 [3][seq_stride] or NULL: the resolved row/slot of each id
+ *   scores_out  fp32 [P] or NULL: e at each packed position (P = sum L_b)
+ *   weights_out fp32 [P] or NULL: p at each packed position (needs scores_out)
  * query and query_ld/query_col must give 16-byte aligned rows (query_ld and
  * query_col[f] multiples of 4).
  * Errors: REC_EINVAL (null pointers, bad table/mlp, misalignment, B < 0,
  * max_len out of range, weights_out without scores_out), REC_EWORKSPACE
  * (plan too small for B, max_len).
  */
-rec_status rec_din_attn_fwd(const rec_table* seq_tables, const int64_t* seq_values,
-                            int64_t seq_stride, const int64_t* seq_offsets,
-                            const int32_t* seq_lengths, int32_t max_len, int64_t B,
-                            const float* query, int64_t query_ld, const int32_t* query_col,
-                            const rec_din_mlp* mlp, const void* plan, size_t plan_bytes,
-                            float* out, float* scores_out, float* weights_out,
-                            int64_t* rows_out, void* stream);
+rec_status rec_din_attn_fwd(const rec_table* seq_tables, void* plan, size_t plan_bytes,
+                            int64_t B, int32_t max_len, const float* query, int64_t query_ld,
+                            const int32_t* query_col, const rec_din_mlp* mlp, float* out,
+                            float* scores_out, float* weights_out, void* stream);
 
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* rec_last_error(void);

@@ -170,44 +170,60 @@ size_t rec_din_plan_bytes(int64_t B, int32_t max_len) {
     return plan_layout(B, max_len).bytes;
 }
 
-rec_status rec_din_plan(const int32_t* seq_lengths, int64_t B, int32_t max_len,
-                        int32_t task_positions, int64_t* seq_offsets_out, void* plan,
-                        size_t plan_bytes, void* stream) {
+rec_status rec_din_plan(const rec_table* seq_tables, const int64_t* seq_values,
+                        int64_t seq_stride, const int64_t* seq_offsets,
+                        const int32_t* seq_lengths, int64_t B, int32_t max_len,
+                        int32_t range_positions, int64_t* seq_offsets_out, int64_t* rows_out,
+                        void* plan, size_t plan_bytes, void* stream) {
     if (B < 0) return fail(REC_EINVAL, "rec_din_plan: B < 0");
     if (B > REC_MAX_B) return fail(REC_EUNSUPPORTED, "rec_din_plan: B > REC_MAX_B");
     if (max_len < 1 || max_len > REC_MAX_SEQ_LEN)
         return fail(REC_EINVAL, "rec_din_plan: max_len outside [1, REC_MAX_SEQ_LEN]");
-    if (task_positions != 0 &&
-        (task_positions % 16 != 0 || task_positions < kMinTaskPositions || task_positions > kMaxTaskPositions))
-        return fail(REC_EINVAL, "rec_din_plan: task_positions must be 0, 16, 32, 48 or 64");
-    if (B > 0 && !seq_lengths) return fail(REC_EINVAL, "rec_din_plan: seq_lengths is NULL");
+    if (range_positions != 0 &&
+        (range_positions % 16 != 0 || range_positions < kMinRange || range_positions > kMaxRange))
+        return fail(REC_EINVAL, "rec_din_plan: range_positions must be 0 or a multiple of 16 in [16, 2^20]");
+    if (!seq_tables) return fail(REC_EINVAL, "rec_din_plan: seq_tables is NULL");
+    if (B > 0 && (!seq_lengths || !seq_values))
+        return fail(REC_EINVAL, "rec_din_plan: seq_lengths and seq_values are required");
+    if (seq_stride < 0) return fail(REC_EINVAL, "rec_din_plan: seq_stride < 0");
     if (!plan) return fail(REC_EINVAL, "rec_din_plan: plan is NULL");
     if (!aligned16(plan)) return fail(REC_EINVAL, "rec_din_plan: plan not 16-byte aligned");
     if (plan_bytes < rec_din_plan_bytes(B, max_len))
         return fail(REC_EWORKSPACE, "rec_din_plan: plan smaller than rec_din_plan_bytes(B, max_len)");
+    PlanArgs a;
+    memset(&a, 0, sizeof(a));
+    for (int f = 0; f < 3; ++f) {
+        rec_status st = prep_table(seq_tables[f], "rec_din_plan: seq table", &a.tab[f]);
+        if (st != REC_OK) return st;
+        if (seq_tables[f].rows > 2147483647LL)
+            return fail(REC_EUNSUPPORTED, "rec_din_plan: sequence tables are limited to 2^31-1 rows");
+    }
     if (B == 0) return ok();
     const int cus = num_cus();
     if (cus < 1) return fail(REC_EHIP, "rec_din_plan: cannot query the device");
-    return hip_status(launch_din_plan(seq_lengths, B, max_len, task_positions, cus * kDinWaves,
-                                      seq_offsets_out, plan, (hipStream_t)stream),
-                      "rec_din_plan");
+    a.seq_values = seq_values;
+    a.seq_stride = seq_stride;
+    a.seq_offsets = seq_offsets;
+    a.seq_lengths = seq_lengths;
+    a.B = B;
+    a.max_len = max_len;
+    a.range_positions = range_positions;
+    a.num_cus = cus;
+    a.seq_offsets_out = seq_offsets_out;
+    a.rows_out = rows_out;
+    a.plan = plan;
+    return hip_status(launch_din_plan(a, (hipStream_t)stream), "rec_din_plan");
 }
 
-rec_status rec_din_attn_fwd(const rec_table* seq_tables, const int64_t* seq_values,
-                            int64_t seq_stride, const int64_t* seq_offsets,
-                            const int32_t* seq_lengths, int32_t max_len, int64_t B,
-                            const float* query, int64_t query_ld, const int32_t* query_col,
-                            const rec_din_mlp* mlp, const void* plan, size_t plan_bytes,
-                            float* out, float* scores_out, float* weights_out,
-                            int64_t* rows_out, void* stream) {
+rec_status rec_din_attn_fwd(const rec_table* seq_tables, void* plan, size_t plan_bytes,
+                            int64_t B, int32_t max_len, const float* query, int64_t query_ld,
+                            const int32_t* query_col, const rec_din_mlp* mlp, float* out,
+                            float* scores_out, float* weights_out, void* stream) {
     if (B < 0) return fail(REC_EINVAL, "rec_din_attn_fwd: B < 0");
     if (B > REC_MAX_B) return fail(REC_EUNSUPPORTED, "rec_din_attn_fwd: B > REC_MAX_B");
     if (max_len < 1 || max_len > REC_MAX_SEQ_LEN)
         return fail(REC_EINVAL, "rec_din_attn_fwd: max_len outside [1, REC_MAX_SEQ_LEN]");
     if (!seq_tables) return fail(REC_EINVAL, "rec_din_attn_fwd: seq_tables is NULL");
-    if (!seq_values || !seq_offsets || !seq_lengths)
-        return fail(REC_EINVAL, "rec_din_attn_fwd: seq_values, seq_offsets and seq_lengths are required");
-    if (seq_stride < 0) return fail(REC_EINVAL, "rec_din_attn_fwd: seq_stride < 0");
     if (!query || !query_col) return fail(REC_EINVAL, "rec_din_attn_fwd: query and query_col are required");
     if (!aligned16(query) || query_ld < 16 || (query_ld & 3))
         return fail(REC_EINVAL, "rec_din_attn_fwd: query rows must be 16-byte aligned (query_ld a multiple of 4)");
@@ -239,10 +255,7 @@ rec_status rec_din_attn_fwd(const rec_table* seq_tables, const int64_t* seq_valu
     const int cus = num_cus();
     if (cus < 1) return fail(REC_EHIP, "rec_din_attn_fwd: cannot query the device");
     const PlanLayout L = plan_layout(B, max_len);
-    const char* p = (const char*)plan;
-    a.seq_values = seq_values;
-    a.seq_stride = seq_stride;
-    a.seq_offsets = seq_offsets;
+    char* p = (char*)plan;
     a.query = query;
     a.query_ld = query_ld;
     for (int f = 0; f < 3; ++f) a.qcol[f] = query_col[f];
@@ -256,14 +269,17 @@ rec_status rec_din_attn_fwd(const rec_table* seq_tables, const int64_t* seq_valu
     a.dtype = mlp->dtype;
     a.plan_hdr = (const int32_t*)p;
     a.pos_start = (const int32_t*)(p + L.off_pos);
-    a.task_info = (const int2*)(p + L.off_task);
+    a.pos_b = (const int32_t*)(p + L.off_pb);
+    a.pos_jr = (const int32_t*)(p + L.off_pjr);
+    a.pos_rows = (const int32_t*)(p + L.off_prows);
+    a.partials = (float*)(p + L.off_part);
+    a.pmax = L.pmax;
     a.out = out;
     a.scores = scores_out;
     a.weights = weights_out;
-    a.rows_out = rows_out;
     a.B = B;
-    a.max_tasks = L.max_tasks;
-    return hip_status(launch_din(a, cus, (hipStream_t)stream), "rec_din_attn_fwd");
+    a.waves = din_waves(cus);
+    return hip_status(launch_din(a, (hipStream_t)stream), "rec_din_attn_fwd");
 }
 
 }  // extern "C"

@@ -98,49 +98,84 @@ __device__ inline int64_t resolve_row(const TabDev& t, int64_t raw) {
 // ---------------------------------------------------------------------------
 // Scan / plan
 constexpr int kScanThreads = 256;
-constexpr int kScanItems = 16;
-constexpr int kScanChunk = kScanThreads * kScanItems;     // 4096 lengths per block
+constexpr int kScanItems = 4;
+constexpr int kScanChunk = kScanThreads * kScanItems;     // 1024 lengths per block
 
-inline int64_t scan_blocks(int64_t n) { return (n + kScanChunk - 1) / kScanChunk; }
+__host__ __device__ inline int64_t scan_blocks(int64_t n) { return (n + kScanChunk - 1) / kScanChunk; }
 
-// DIN plan buffer layout (bytes from the start)
-//   [0, 64)            int32 header: B, max_len, C (positions per task),
-//                      num_tasks, P (total packed positions), nblocks
-//   [64, 64+16*nb)     int64 pairs: per-block sums (clamped, raw)
-//   pos_start          int32[B+1], 16-byte aligned
-//   task_info          int32 pairs [max_tasks+1][2]: (first sample of the
-//                      task, packed start of that sample); task t holds
-//                      samples [info[t].x, info[t+1].x) and positions
-//                      [info[t].y, info[t+1].y)
-enum { kHdrB = 0, kHdrMaxLen, kHdrC, kHdrNumTasks, kHdrP, kHdrNBlocks };
-constexpr int kMinTaskPositions = 16;
-constexpr int kMaxTaskPositions = 64;
+// DIN plan buffer layout (bytes from the start).  Pmax = B * max_len bounds
+// the packed positions P = sum_b min(len_b, max_len); packed position p of
+// sample b, step j is pos_start[b] + j.  The attention splits [0, P) into
+// ranges of R positions (one per wave and pass); a sample cut by a range
+// edge leaves partial softmax states that a finalize pass merges.
+//   [0, 64)        int32 header: B, max_len, R requested (0 = even split),
+//                  R used, P, nblocks, number of ranges
+//   sums           int64 pairs [nblocks]: per-block sums (clamped, raw)
+//   pos_start      int32[B+1]
+//   sample_base    int64[B]: index in seq_values of sample b's first position
+//   pos_b          int32[Pmax]: sample of packed position p
+//   pos_jr         int32[Pmax]: j | (L - 1 - j) << 16 (step, steps left)
+//   pos_rows       int32[3][Pmax]: resolved row of the adgroup/cate/brand id
+//                  (a hash miss is -1)
+//   partials       float[max_ranges][2][52]: per range, the state of the sample
+//                  entering it (in) and of the sample leaving it (out):
+//                  max, sum, 2 pad, 48 weighted sums
+enum { kHdrB = 0, kHdrMaxLen, kHdrRReq, kHdrR, kHdrP, kHdrNBlocks, kHdrNRanges };
+constexpr int kMinRange = 16;
+constexpr int kMaxRange = 1 << 20;
+constexpr int kPartialFloats = 52;
 
 struct PlanLayout {
-    int64_t nblocks, max_tasks;
-    size_t off_sums, off_pos, off_task, bytes;
+    int64_t nblocks, pmax, max_ranges;
+    size_t off_sums, off_pos, off_sbase, off_pb, off_pjr, off_prows, off_part, bytes;
 };
 
-inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+__host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
-inline PlanLayout plan_layout(int64_t B, int32_t max_len) {
+__host__ __device__ inline PlanLayout plan_layout(int64_t B, int32_t max_len) {
     PlanLayout p;
     p.nblocks = scan_blocks(B);
-    p.max_tasks = (B * (int64_t)max_len) / kMinTaskPositions + 1;
+    p.pmax = B * (int64_t)max_len;
+    p.max_ranges = p.pmax / kMinRange + 1;
     p.off_sums = 64;
     p.off_pos = align16(p.off_sums + 16 * (size_t)p.nblocks);
-    p.off_task = align16(p.off_pos + 4 * (size_t)(B + 1));
-    p.bytes = align16(p.off_task + 8 * (size_t)(p.max_tasks + 1));
+    p.off_sbase = align16(p.off_pos + 4 * (size_t)(B + 1));
+    p.off_pb = align16(p.off_sbase + 8 * (size_t)B);
+    p.off_pjr = align16(p.off_pb + 4 * (size_t)p.pmax);
+    p.off_prows = align16(p.off_pjr + 4 * (size_t)p.pmax);
+    p.off_part = align16(p.off_prows + 12 * (size_t)p.pmax);
+    p.bytes = align16(p.off_part + sizeof(float) * 2 * kPartialFloats * (size_t)p.max_ranges);
     return p;
+}
+
+// Positions per range: the requested multiple of 16, else an even split of P
+// over `waves`, rounded up to a multiple of 16.
+__host__ __device__ inline int64_t din_range(int64_t P, int32_t req, int64_t waves) {
+    if (req > 0) return req;
+    int64_t r = (P + waves - 1) / waves;
+    r = (r + 15) / 16 * 16;
+    return r < kMinRange ? kMinRange : r;
 }
 
 // ---------------------------------------------------------------------------
 // Launchers (return the hipError_t of the launch)
 hipError_t launch_lengths_to_offsets(const int32_t* lengths, int64_t n, int64_t* offsets,
                                      int64_t* block_sums, hipStream_t s);
-hipError_t launch_din_plan(const int32_t* seq_lengths, int64_t B, int32_t max_len,
-                           int32_t task_positions, int32_t total_waves,
-                           int64_t* seq_offsets_out, void* plan, hipStream_t s);
+struct PlanArgs {
+    TabDev tab[3];
+    const int64_t* seq_values;
+    int64_t seq_stride;
+    const int64_t* seq_offsets;      // caller's layout, or NULL = packed
+    const int32_t* seq_lengths;
+    int64_t B;
+    int32_t max_len;
+    int32_t range_positions;   // stored in the header: 0 = even split
+    int32_t num_cus;
+    int64_t* seq_offsets_out;
+    int64_t* rows_out;
+    void* plan;
+};
+hipError_t launch_din_plan(const PlanArgs& a, hipStream_t s);
 
 struct EmbArgs {
     TabDev tab[REC_MAX_TABLES];
@@ -166,9 +201,6 @@ hipError_t launch_hash_lookup(const HashArgs& a, hipStream_t s);
 
 struct DinArgs {
     TabDev tab[3];
-    const int64_t* seq_values;
-    int64_t seq_stride;
-    const int64_t* seq_offsets;
     const float* query;
     int64_t query_ld;
     int32_t qcol[3];
@@ -182,16 +214,20 @@ struct DinArgs {
     int32_t dtype;
     const int32_t* plan_hdr;
     const int32_t* pos_start;
-    const int2* task_info;
+    const int32_t* pos_b;
+    const int32_t* pos_jr;
+    const int32_t* pos_rows;
+    float* partials;
+    int64_t pmax;
     float* out;
     float* scores;
     float* weights;
-    int64_t* rows_out;
     int64_t B;
-    int64_t max_tasks;
+    int32_t waves;          // waves of the attention launch (sets the even split)
 };
 constexpr int kDinWaves = 4;                 // waves per workgroup (one per SIMD)
-hipError_t launch_din(const DinArgs& a, int num_cus, hipStream_t s);
+int din_waves(int num_cus);
+hipError_t launch_din(const DinArgs& a, hipStream_t s);
 hipError_t launch_din_pack(const void* w1, const void* w2, void* packed, hipStream_t s);
 
 }  // namespace rec

@@ -6,8 +6,9 @@
 // attention works on packed positions instead of a [B,100] padding).
 //
 // Two launches, no inter-block waiting: a reduce pass writes one sum per
-// 4096-length block; an apply pass has every block add up the sums before
-// it, scan its own block through LDS, and write the results.
+// 1024-length block; an apply pass has every block add up the sums before
+// it, scan its own block through LDS, and write the results.  The DIN plan
+// adds a third pass over the packed positions.
 #include "rec_internal.h"
 
 namespace rec {
@@ -54,14 +55,16 @@ __device__ inline int64_t block_excl_scan(int64_t v, int64_t* red) {
     return before + inc - v;
 }
 
-// Load the block's 4096 lengths into LDS (coalesced), padded so that each
-// thread's 16 consecutive values sit in distinct banks.
+// Load the block's lengths into LDS (coalesced), padded by one word per
+// kScanItems so that each thread's consecutive values sit in distinct banks.
+__device__ inline int sl_index(int e) { return e + e / kScanItems; }
+
 __device__ inline void stage_chunk(const int32_t* len, int64_t n, int64_t base, int32_t* sl) {
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
         const int e = k * kScanThreads + (int)threadIdx.x;
         const int64_t idx = base + e;
-        sl[e + (e >> 4)] = idx < n ? len[idx] : 0;
+        sl[sl_index(e)] = idx < n ? len[idx] : 0;
     }
     __syncthreads();
 }
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(kScanThreads) void k_offsets_apply(const int32_t* _
                                                                int64_t n,
                                                                const int64_t* __restrict__ sums,
                                                                int64_t* __restrict__ offsets) {
-    __shared__ int32_t sl[kScanChunk + kScanChunk / 16];
+    __shared__ int32_t sl[kScanChunk + kScanChunk / kScanItems];
     __shared__ int64_t red[kScanThreads / 64];
     const int64_t base = (int64_t)blockIdx.x * kScanChunk;
     int64_t before = 0;
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(kScanThreads) void k_offsets_apply(const int32_t* _
     int64_t run = 0;
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
-        run += sl[t * 17 + k];
+        run += sl[sl_index(t * kScanItems + k)];
         loc[k] = run;
     }
     const int64_t excl = block_excl_scan(run, red) + before;
@@ -122,48 +125,37 @@ __global__ __launch_bounds__(kScanThreads) void k_offsets_apply(const int32_t* _
     }
 }
 
-__global__ __launch_bounds__(kScanThreads) void k_plan_apply(const int32_t* __restrict__ len,
-                                                            int64_t B, int32_t max_len,
-                                                            int32_t task_positions,
-                                                            int32_t total_waves, int64_t nblocks,
-                                                            const int64_t* __restrict__ sums,
-                                                            int64_t* __restrict__ seq_off,
-                                                            int32_t* __restrict__ hdr,
-                                                            int32_t* __restrict__ pos_start,
-                                                            int2* __restrict__ task_info) {
-    __shared__ int32_t sl[kScanChunk + kScanChunk / 16];
+__global__ __launch_bounds__(kScanThreads) void k_plan_apply(const PlanArgs a, int64_t nblocks) {
+    __shared__ int32_t sl[kScanChunk + kScanChunk / kScanItems];
     __shared__ int64_t red[kScanThreads / 64];
+    const PlanLayout Lo = plan_layout(a.B, a.max_len);
+    char* pb = (char*)a.plan;
+    const int64_t* sums = (const int64_t*)(pb + Lo.off_sums);
+    int32_t* hdr = (int32_t*)pb;
+    int32_t* pos_start = (int32_t*)(pb + Lo.off_pos);
+    int64_t* sbase = (int64_t*)(pb + Lo.off_sbase);
+    const int64_t B = a.B;
+    const int32_t max_len = a.max_len;
     const int64_t base = (int64_t)blockIdx.x * kScanChunk;
-    int64_t bc = 0, br = 0, tot = 0;
-    for (int64_t j = threadIdx.x; j < nblocks; j += kScanThreads) {
-        const int64_t c = sums[2 * j];
-        if (j < (int64_t)blockIdx.x) { bc += c; br += sums[2 * j + 1]; }
-        tot += c;
+    int64_t bc = 0, br = 0;
+    for (int64_t j = threadIdx.x; j < (int64_t)blockIdx.x; j += kScanThreads) {
+        bc += sums[2 * j];
+        br += sums[2 * j + 1];
     }
     bc = block_sum(bc, red);
     br = block_sum(br, red);
-    const int64_t P = block_sum(tot, red);
-    // Positions per task: the requested value, or an even split of P over
-    // every wave the attention kernel runs, rounded to the 16-row tile.
-    int64_t C = task_positions;
-    if (C == 0) {
-        C = (P + total_waves - 1) / total_waves;
-        C = (C + kMinTaskPositions - 1) / kMinTaskPositions * kMinTaskPositions;
-        C = C < kMinTaskPositions ? kMinTaskPositions : (C > kMaxTaskPositions ? kMaxTaskPositions : C);
-    }
-    stage_chunk(len, B, base, sl);
+    stage_chunk(a.seq_lengths, B, base, sl);
     const int t = threadIdx.x;
     int32_t v[kScanItems];
     int64_t rc = 0, rr = 0;
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
-        v[k] = sl[t * 17 + k];
+        v[k] = sl[sl_index(t * kScanItems + k)];
         rr += v[k];
         rc += v[k] < 0 ? 0 : (v[k] < max_len ? v[k] : max_len);
     }
     int64_t pc = block_excl_scan(rc, red) + bc;     // clamped prefix before this thread
     int64_t pr = block_excl_scan(rr, red) + br;     // raw prefix before this thread
-    if (blockIdx.x == 0 && t == 0) task_info[0] = make_int2(0, 0);
 #pragma unroll
     for (int k = 0; k < kScanItems; ++k) {
         const int64_t b = base + t * kScanItems + k;
@@ -171,24 +163,55 @@ __global__ __launch_bounds__(kScanThreads) void k_plan_apply(const int32_t* __re
         const int64_t c = v[k] < 0 ? 0 : (v[k] < max_len ? v[k] : max_len);
         const int64_t next = pc + c;
         pos_start[b] = (int32_t)pc;
-        if (seq_off) seq_off[b] = pr;
-        // sample b+1 is the first sample of every task t with
-        // pc < t*C <= next; the last sample also closes the task list.
-        int64_t t_hi = next / C;
-        if (b == B - 1) t_hi += 1;
-        for (int64_t tt = pc / C + 1; tt <= t_hi; ++tt) task_info[tt] = make_int2((int32_t)(b + 1), (int32_t)next);
+        if (a.seq_offsets_out) a.seq_offsets_out[b] = pr;
+        sbase[b] = a.seq_offsets ? a.seq_offsets[b] : pr;
         if (b == B - 1) {
             pos_start[B] = (int32_t)next;
-            if (seq_off) seq_off[B] = pr + v[k];
+            if (a.seq_offsets_out) a.seq_offsets_out[B] = pr + v[k];
             hdr[kHdrB] = (int32_t)B;
             hdr[kHdrMaxLen] = max_len;
-            hdr[kHdrC] = (int32_t)C;
-            hdr[kHdrNumTasks] = (int32_t)(next / C + 1);
+            hdr[kHdrRReq] = a.range_positions;
             hdr[kHdrP] = (int32_t)next;
             hdr[kHdrNBlocks] = (int32_t)nblocks;
         }
         pc = next;
         pr += v[k];
+    }
+}
+
+// Per packed position: its sample and step, and the rows of its three ids.
+// A 64-lane group serves one sample (positions j = lane, lane + 64, ...), so
+// the id reads and the entry writes of a group are contiguous.
+template <bool kHash>
+__global__ __launch_bounds__(256) void k_plan_positions(const PlanArgs a) {
+    const PlanLayout Lo = plan_layout(a.B, a.max_len);
+    char* pb = (char*)a.plan;
+    const int32_t* pos_start = (const int32_t*)(pb + Lo.off_pos);
+    const int64_t* sbase = (const int64_t*)(pb + Lo.off_sbase);
+    int32_t* pos_b = (int32_t*)(pb + Lo.off_pb);
+    int32_t* pos_jr = (int32_t*)(pb + Lo.off_pjr);
+    int32_t* pos_rows = (int32_t*)(pb + Lo.off_prows);
+    const int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (b >= a.B) return;
+    const int lane = threadIdx.x & 63;
+    const int32_t ps = pos_start[b];
+    const int32_t L = pos_start[b + 1] - ps;
+    const int64_t g0 = sbase[b];
+    for (int j = lane; j < L; j += 64) {
+        const int64_t p = ps + j;
+        const int64_t g = g0 + j;
+        pos_b[p] = (int32_t)b;
+        pos_jr[p] = j | ((L - 1 - j) << 16);
+        int64_t raw[3];
+#pragma unroll
+        for (int f = 0; f < 3; ++f) raw[f] = a.seq_values[f * a.seq_stride + g];
+#pragma unroll
+        for (int f = 0; f < 3; ++f) {
+            const TabDev& tb = a.tab[f];
+            const int64_t row = kHash ? resolve_row(tb, raw[f]) : floor_mod_magic(raw[f], tb.rows, tb.magic, tb.shift);
+            pos_rows[f * Lo.pmax + p] = (int32_t)row;
+            if (a.rows_out) a.rows_out[f * a.seq_stride + g] = row;
+        }
     }
 }
 
@@ -206,18 +229,17 @@ hipError_t launch_lengths_to_offsets(const int32_t* lengths, int64_t n, int64_t*
     return hipGetLastError();
 }
 
-hipError_t launch_din_plan(const int32_t* seq_lengths, int64_t B, int32_t max_len,
-                           int32_t task_positions, int32_t total_waves,
-                           int64_t* seq_offsets_out, void* plan, hipStream_t s) {
-    const PlanLayout L = plan_layout(B, max_len);
-    char* p = (char*)plan;
+hipError_t launch_din_plan(const PlanArgs& a, hipStream_t s) {
+    const PlanLayout L = plan_layout(a.B, a.max_len);
+    char* p = (char*)a.plan;
     int64_t* sums = (int64_t*)(p + L.off_sums);
     hipLaunchKernelGGL(k_scan_reduce<true>, dim3((unsigned)L.nblocks), dim3(kScanThreads), 0, s,
-                       seq_lengths, B, max_len, sums);
-    hipLaunchKernelGGL(k_plan_apply, dim3((unsigned)L.nblocks), dim3(kScanThreads), 0, s,
-                       seq_lengths, B, max_len, task_positions, total_waves, L.nblocks, sums,
-                       seq_offsets_out, (int32_t*)p, (int32_t*)(p + L.off_pos),
-                       (int2*)(p + L.off_task));
+                       a.seq_lengths, a.B, a.max_len, sums);
+    hipLaunchKernelGGL(k_plan_apply, dim3((unsigned)L.nblocks), dim3(kScanThreads), 0, s, a, L.nblocks);
+    const bool hash = a.tab[0].kind == REC_HASH || a.tab[1].kind == REC_HASH || a.tab[2].kind == REC_HASH;
+    const dim3 grid((unsigned)((a.B + 3) / 4));
+    if (hash) hipLaunchKernelGGL(k_plan_positions<true>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_plan_positions<false>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

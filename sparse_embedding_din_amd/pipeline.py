@@ -2,7 +2,7 @@
 four C-ABI calls:
 
     rec_lengths_to_offsets  (deep KJT lengths -> offsets)
-    rec_din_plan            (sequence lengths -> packed starts, tasks, offsets)
+    rec_din_plan            (sequence lengths/ids -> packed positions, rows)
     rec_embbag_fwd          (pooled [B, 256])
     rec_din_attn_fwd        (attention [B, 48], query read from the pooled output)
 
@@ -99,12 +99,12 @@ class SparseDinForward:
     """Buffers for batches of up to B_max samples and the four-call forward."""
 
     def __init__(self, tables: DeviceTables, mlp: DeviceMLP, B_max: int, max_len: int = 100,
-                 device="cuda", task_positions: int = 0, T: int = 16):
+                 device="cuda", range_positions: int = 0, T: int = 16):
         self.T = T
         self.tables = tables
         self.mlp = mlp
         self.max_len = max_len
-        self.task_positions = task_positions
+        self.range_positions = range_positions
         self.B_max = B_max
         self.tab_arr = tables.array(list(range(T)))
         self.seq_arr = tables.array(list(SEQ_KEYS))
@@ -122,20 +122,19 @@ class SparseDinForward:
     def offsets_step(self, b: DeviceBatch, stream=None):
         R.rec_lengths_to_offsets(b.lengths, self.T * b.B, self.offsets, self.ws, self.ws_bytes, stream)
 
-    def plan_step(self, b: DeviceBatch, stream=None):
-        R.rec_din_plan(b.seq_lengths, b.B, self.max_len, self.task_positions, self.seq_offsets,
+    def plan_step(self, b: DeviceBatch, rows_out=None, stream=None):
+        R.rec_din_plan(self.seq_arr, b.seq_values, b.seq_stride, b.seq_offsets, b.seq_lengths,
+                       b.B, self.max_len, self.range_positions, self.seq_offsets, rows_out,
                        self.plan, self.plan_bytes, stream)
 
     def embbag_step(self, b: DeviceBatch, rows_out=None, stream=None):
         R.rec_embbag_fwd(self.tab_arr, self.T, b.B, b.values, b.lengths, self.offsets, self.pooled,
                          rows_out, stream)
 
-    def din_step(self, b: DeviceBatch, scores=None, weights=None, rows=None, stream=None):
-        so = self.seq_offsets if b.seq_offsets is None else b.seq_offsets
-        R.rec_din_attn_fwd(self.seq_arr, b.seq_values, b.seq_stride, so, b.seq_lengths,
-                           self.max_len, b.B, self.pooled, self.T * 16, self.query_col,
-                           self.mlp.desc, self.plan, self.plan_bytes, self.att, scores, weights,
-                           rows, stream)
+    def din_step(self, b: DeviceBatch, scores=None, weights=None, stream=None):
+        R.rec_din_attn_fwd(self.seq_arr, self.plan, self.plan_bytes, b.B, self.max_len,
+                           self.pooled, self.T * 16, self.query_col, self.mlp.desc, self.att,
+                           scores, weights, stream)
 
     def run(self, b: DeviceBatch, stream=None, debug: Optional[dict] = None, side=None):
         """The forward on torch's current stream.  With `side` (another
@@ -147,14 +146,14 @@ class SparseDinForward:
             main = torch.cuda.current_stream()
             side.wait_stream(main)
             with torch.cuda.stream(side):
-                self.plan_step(b)
+                self.plan_step(b, d.get("seq_rows"))
             self.offsets_step(b)
             self.embbag_step(b, d.get("emb_rows"))
             main.wait_stream(side)
-            self.din_step(b, d.get("scores"), d.get("weights"), d.get("seq_rows"))
+            self.din_step(b, d.get("scores"), d.get("weights"))
             return self.pooled[: b.B], self.att[: b.B]
         self.offsets_step(b, stream)
-        self.plan_step(b, stream)
+        self.plan_step(b, d.get("seq_rows"), stream)
         self.embbag_step(b, d.get("emb_rows"), stream)
-        self.din_step(b, d.get("scores"), d.get("weights"), d.get("seq_rows"), stream)
+        self.din_step(b, d.get("scores"), d.get("weights"), stream)
         return self.pooled[: b.B], self.att[: b.B]

@@ -65,10 +65,11 @@ def lib():
         L.rec_hash_lookup.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, vp]
         L.rec_din_plan_bytes.argtypes = [i64, i32]
         L.rec_din_plan_bytes.restype = sz
-        L.rec_din_plan.argtypes = [vp, i64, i32, i32, vp, vp, sz, vp]
-        L.rec_din_attn_fwd.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, i32, i64, vp, i64,
-                                       C.POINTER(C.c_int32), C.POINTER(rec_din_mlp), vp, sz, vp,
-                                       vp, vp, vp, vp]
+        L.rec_din_plan.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, i64, i32, i32, vp, vp,
+                                   vp, sz, vp]
+        L.rec_din_attn_fwd.argtypes = [C.POINTER(rec_table), vp, sz, i64, i32, vp, i64,
+                                       C.POINTER(C.c_int32), C.POINTER(rec_din_mlp), vp, vp, vp,
+                                       vp]
         L.rec_din_pack_mlp.argtypes = [C.POINTER(rec_din_mlp), vp, sz, vp]
         for f in ("rec_lengths_to_offsets", "rec_embbag_fwd", "rec_hash_lookup", "rec_din_plan",
                   "rec_din_attn_fwd", "rec_din_pack_mlp"):
@@ -118,7 +119,9 @@ def din_mlp(dtype: int, w1, b1, w2, b2, w3, b3: float) -> rec_din_mlp:
     return rec_din_mlp(dtype, 0, _p(w1), _p(b1), _p(w2), _p(b2), _p(w3), float(b3))
 
 
-def _tables(tabs: Sequence[rec_table]):
+def _tables(tabs):
+    if isinstance(tabs, C.Array):
+        return tabs
     arr = (rec_table * len(tabs))()
     for i, t in enumerate(tabs):
         arr[i] = t
@@ -163,22 +166,23 @@ def rec_din_plan_bytes(B: int, max_len: int) -> int:
     return int(lib().rec_din_plan_bytes(B, max_len))
 
 
-def rec_din_plan(seq_lengths, B: int, max_len: int, task_positions: int, seq_offsets_out, plan,
-                 plan_bytes: int, stream=None):
-    _check(lib().rec_din_plan(_p(seq_lengths), B, max_len, task_positions, _p(seq_offsets_out),
-                              _p(plan), plan_bytes, _stream(stream)), "rec_din_plan")
+def rec_din_plan(seq_tables: Sequence[rec_table], seq_values, seq_stride: int, seq_offsets,
+                 seq_lengths, B: int, max_len: int, range_positions: int, seq_offsets_out,
+                 rows_out, plan, plan_bytes: int, stream=None):
+    _check(lib().rec_din_plan(_tables(seq_tables), _p(seq_values), seq_stride, _p(seq_offsets),
+                              _p(seq_lengths), B, max_len, range_positions, _p(seq_offsets_out),
+                              _p(rows_out), _p(plan), plan_bytes, _stream(stream)),
+           "rec_din_plan")
 
 
-def rec_din_attn_fwd(seq_tables: Sequence[rec_table], seq_values, seq_stride: int, seq_offsets,
-                     seq_lengths, max_len: int, B: int, query, query_ld: int,
-                     query_col: Sequence[int], mlp: rec_din_mlp, plan, plan_bytes: int, out,
-                     scores_out=None, weights_out=None, rows_out=None, stream=None):
+def rec_din_attn_fwd(seq_tables: Sequence[rec_table], plan, plan_bytes: int, B: int,
+                     max_len: int, query, query_ld: int, query_col: Sequence[int],
+                     mlp: rec_din_mlp, out, scores_out=None, weights_out=None, stream=None):
     qc = None if query_col is None else (C.c_int32 * 3)(*query_col)
-    _check(lib().rec_din_attn_fwd(_tables(seq_tables), _p(seq_values), seq_stride,
-                                  _p(seq_offsets), _p(seq_lengths), max_len, B, _p(query),
-                                  query_ld, qc, C.byref(mlp) if mlp is not None else None,
-                                  _p(plan), plan_bytes, _p(out), _p(scores_out),
-                                  _p(weights_out), _p(rows_out), _stream(stream)),
+    _check(lib().rec_din_attn_fwd(_tables(seq_tables), _p(plan), plan_bytes, B, max_len,
+                                  _p(query), query_ld, qc,
+                                  C.byref(mlp) if mlp is not None else None, _p(out),
+                                  _p(scores_out), _p(weights_out), _stream(stream)),
            "rec_din_attn_fwd")
 
 

@@ -40,16 +40,16 @@ def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
 class Run:
     """One forward on the GPU with every debug output requested."""
 
-    def __init__(self, model, batch, task_positions=0, layout=None, debug=True, mlp_dtype=None,
+    def __init__(self, model, batch, range_positions=0, layout=None, debug=True, mlp_dtype=None,
                  packed=True):
         self.model, self.batch = model, batch
         B = batch.B
         say(f"cfg={model.cfg.name} B={B} P={batch.seq_stride} nnz={batch.values.size} "
-            f"layout={'padded' if layout else 'packed'} C={task_positions}")
+            f"layout={'padded' if layout else 'packed'} C={range_positions}")
         self.tabs = PL.DeviceTables(model.tables, DEV)
         self.mlp = PL.DeviceMLP(model, DEV, dtype=mlp_dtype, packed=packed)
         self.fwd = PL.SparseDinForward(self.tabs, self.mlp, B, model.cfg.max_len, DEV,
-                                       task_positions=task_positions)
+                                       range_positions=range_positions)
         if layout is None:
             self.db = PL.DeviceBatch(batch, DEV)
             stride = batch.seq_stride
@@ -59,9 +59,10 @@ class Run:
         self.stride = stride
         dbg = None
         if debug:
+            npos = int(np.minimum(batch.seq_lengths, model.cfg.max_len).sum())
             dbg = dict(emb_rows=torch.full((max(batch.values.size, 1),), -7, dtype=torch.int64, device=DEV),
-                       scores=torch.full((max(stride, 1),), np.nan, dtype=torch.float32, device=DEV),
-                       weights=torch.full((max(stride, 1),), np.nan, dtype=torch.float32, device=DEV),
+                       scores=torch.full((max(npos, 1),), np.nan, dtype=torch.float32, device=DEV),
+                       weights=torch.full((max(npos, 1),), np.nan, dtype=torch.float32, device=DEV),
                        seq_rows=torch.full((3 * max(stride, 1),), -7, dtype=torch.int64, device=DEV))
         self.dbg = dbg
         self.fwd.run(self.db, debug=dbg)
@@ -70,6 +71,9 @@ class Run:
         self.seq_offsets = self.fwd.seq_offsets[: B + 1].cpu().numpy()
         self.pooled = self.fwd.pooled[:B].cpu().numpy()
         self.att = self.fwd.att[:B].cpu().numpy()
+        # packed position of (b, j) = packed_start[b] + j over min(len, max_len)
+        self.packed_start = oracle.get().lengths_to_offsets(
+            np.minimum(batch.seq_lengths, model.cfg.max_len))
         if debug:
             self.emb_rows = dbg["emb_rows"].cpu().numpy()[: batch.values.size]
             self.scores = dbg["scores"].cpu().numpy()
@@ -98,9 +102,9 @@ def oracle_rows(model, batch):
 
 
 def gpu_scores_by_sample(run: Run, samples, max_len):
-    """GPU scores/weights rearranged to [ns][max_len] (packed layout only)."""
+    """GPU scores/weights (packed positions) rearranged to [ns][max_len]."""
     b = run.batch
-    starts = run.seq_offsets
+    starts = run.packed_start
     ns = len(samples)
     sc = np.zeros((ns, max_len))
     wt = np.zeros((ns, max_len))
