@@ -52,6 +52,11 @@ def parse():
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--no-side-stream", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run a plain 64 MiB elementwise copy (for counter scaling)")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write profiles/traffic_*.json from two rocprofv3 --pmc counter CSVs "
+                        "(FETCH_SIZE, WRITE_SIZE) of a --calibrate-copy run, then exit")
     return p.parse_args()
 
 
@@ -63,21 +68,70 @@ def src_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, shash: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        d = json.load(f)
-    if d.get("src_hash") != shash:
-        return None
-    return d.get("bytes_per_launch")
+CAL_BYTES = 64 << 20            # bytes read (and written) by the calibration copy
+KERNELS = {"k_din_attn": "k_din_attn", "k_din_finalize": "k_din_finalize",
+           "k_embbag_fwd": "k_embbag_fwd", "copy": "MulFunctor"}
+
+
+def load_traffic(kernels, shash: str, config: str):
+    """HBM bytes per launch (summed over `kernels`) from committed rocprofv3
+    counter runs, if they were taken on the current kernel sources and this
+    workload; else None."""
+    tot = 0.0
+    for k in kernels:
+        path = os.path.join(ROOT, "profiles", f"traffic_{k}_{config}.json")
+        if not os.path.exists(path):
+            return None
+        with open(path) as f:
+            d = json.load(f)
+        if d.get("src_hash") != shash:
+            return None
+        tot += d["bytes_per_launch"]
+    return tot
+
+
+def traffic_from(fetch_csv: str, write_csv: str, config: str):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each kernel, each
+    scaled by the same counter's reading for the calibration copy (CAL_BYTES
+    read, CAL_BYTES written)."""
+    import csv
+
+    def per_kernel(path, counter):
+        acc = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row["Kernel_Name"]
+                for key, pat in KERNELS.items():
+                    if pat in name:
+                        acc.setdefault(key, []).append(float(row["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+    fetch, nf = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, nw = per_kernel(write_csv, "WRITE_SIZE")
+    f_cal = fetch["copy"] * 1024.0 / CAL_BYTES
+    w_cal = write["copy"] * 1024.0 / CAL_BYTES
+    shash = src_hash()
+    for k in KERNELS:
+        if k == "copy" or k not in fetch or k not in write:
+            continue
+        b = fetch[k] * 1024.0 / f_cal + write[k] * 1024.0 / w_cal
+        d = {"kernel": k, "config": config, "src_hash": shash, "bytes_per_launch": b,
+             "fetch_kib_raw": fetch[k], "write_kib_raw": write[k], "dispatches": [nf[k], nw[k]],
+             "copy_scale": {"fetch": f_cal, "write": w_cal, "bytes": CAL_BYTES}}
+        with open(os.path.join(ROOT, "profiles", f"traffic_{k}_{config}.json"), "w") as f:
+            json.dump(d, f, indent=1)
+        print(f"{k}: {b / 1e6:.3f} MB per launch (fetch {fetch[k]:.0f} KiB, write {write[k]:.0f} KiB)")
+    print(f"copy scale: fetch {f_cal:.3f}, write {w_cal:.3f}")
 
 
 def main():
     a = parse()
+    if a.traffic_from:
+        import synth
+        traffic_from(a.traffic_from[0], a.traffic_from[1], synth.CONFIGS[a.config].name)
+        return
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
               "(the forward is data-parallel over samples with replicated tables and needs no "
@@ -189,20 +243,22 @@ def main():
     din_flops = P * DIN_FLOPS_PER_POS
     emb_t = kern_us["embbag"]["mean"] * 1e-6
     din_t = kern_us["din"]["mean"] * 1e-6
-    peak_mfma = BF16_PEAK_TFLOPS if mlp.dtype == R.REC_BF16 else FP32_PEAK_TFLOPS
+    bf16 = mlp.dtype in (R.REC_BF16, R.REC_BF16_PACKED)
+    peak_mfma = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
     emb_gbs = emb_bytes / emb_t / 1e9
     din_tflops = din_flops / din_t / 1e12
     shash = src_hash()
     if din_t >= emb_t:
-        roof = {"kernel": "k_din_attn", "bound": "mfma", "achieved": round(din_tflops, 2),
+        roof = {"kernel": "rec_din_attn_fwd = k_din_attn + k_din_finalize", "bound": "mfma",
+                "achieved": round(din_tflops, 2),
                 "peak": peak_mfma, "unit": "TFLOP/s", "frac": round(din_tflops / peak_mfma, 4),
-                "traffic": load_traffic("k_din_attn", shash),
+                "traffic": load_traffic(["k_din_attn", "k_din_finalize"], shash, cfg.name),
                 "per_launch": {"flops": din_flops, "bytes": din_bytes, "positions": P, "samples": B},
                 "avg_launch_us": round(kern_us["din"]["mean"], 3)}
     else:
         roof = {"kernel": "k_embbag_fwd", "bound": "hbm", "achieved": round(emb_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(emb_gbs / HBM_PEAK_GBS, 4),
-                "traffic": load_traffic("k_embbag_fwd", shash),
+                "traffic": load_traffic(["k_embbag_fwd"], shash, cfg.name),
                 "per_launch": {"bytes": emb_bytes, "ids": nnz, "bags": synth.T * B},
                 "avg_launch_us": round(kern_us["embbag"]["mean"], 3)}
 
@@ -235,12 +291,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if mlp.dtype == R.REC_BF16 else "f32",
+        "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic: seeded Taobao-shaped ids, tables N(0,0.05), Xavier MLP",
-        "config": {"workload": f"{cfg.name}: 16 dim-16 fp32 tables ({sum(cfg.sizes)} rows), "
-                               f"bags U{{1,2,3}} (price 1), click sequences Geom(mean 4) cap 100, "
-                               f"attn MLP 192-256-64-1 "
-                               f"{'bf16 with fp32 accumulate' if mlp.dtype == R.REC_BF16 else 'fp32'}",
+        "config": {"workload": f"{cfg.name}: {synth.describe(cfg)}",
                    "global_batch": B, "parallelism": "single GPU",
                    "graph_replay": graph is not None, "rotating_batches": len(dbs),
                    "plan_on_side_stream": side is not None},
@@ -253,6 +306,12 @@ def main():
                 "gb_s": round(din_bytes / din_t / 1e9, 1)},
         "src_hash": shash,
     }
+    if a.calibrate_copy:
+        src = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
     print(json.dumps(out), flush=True)
 
 

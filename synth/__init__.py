@@ -83,6 +83,25 @@ CONFIGS: Dict[int, Config] = {
 }
 
 
+_BAG_DESC = {"u123": "bags U{1,2,3} ids", "binom": "bags 1+Bin(4,1/4) ids (mean 2)"}
+_SEQ_DESC = {"geom4": "click sequences Geom(mean 4)", "geom5": "click sequences Geom(mean 5)",
+             "unif100": "click sequences U{1..100}"}
+
+
+def describe(cfg: Config) -> str:
+    """One-line description of a workload's shapes and laws."""
+    s = (f"B={cfg.B}, 16 dim-16 fp32 tables ({sum(cfg.sizes)} rows), {_BAG_DESC[cfg.bag_law]} "
+         f"(price 1), {_SEQ_DESC[cfg.seq_law]} cap {cfg.max_len}, 3 sub-features")
+    if cfg.zipf_keys:
+        s += f", Zipf(1.05) ids for tables {list(cfg.zipf_keys)}"
+    if cfg.hash_keys:
+        s += (f", tables {list(cfg.hash_keys)} as lookup-only hash tables (capacity "
+              f"{cfg.hash_capacity}, load {cfg.hash_load}, {int(cfg.hash_hit * 100)}% hits)")
+    s += (", attn MLP 192-256-64-1 " +
+          ("bf16 with fp32 accumulate" if cfg.mlp_dtype == "bf16" else "fp32"))
+    return s
+
+
 # ----------------------------------------------------------------------------
 # Hash-table layout convention (a data format, documented in include/rec.h):
 #   h      = SplitMix64 output mix of the key's 64 bits (Steele, Lea & Flood,

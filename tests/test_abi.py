@@ -1,0 +1,251 @@
+"""The C ABI without a GPU: librec.so loads, exports every function that
+include/rec.h declares, agrees with the binding's constants, rejects bad
+arguments with the documented status before touching a device, and its
+host twins of the device index arithmetic (floor modulo by an invariant
+divisor, the hash home slot and digest) agree with independent definitions.
+
+Device pointers here are fake aligned addresses: every call below fails (or
+is a documented no-op) in host validation, before the first HIP call."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from sparse_embedding_din_amd import build as BUILD
+from sparse_embedding_din_amd import rec as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rec.h")
+FAKE = 0x10000          # a 16-byte aligned, never dereferenced address
+FAKE_ODD = 0x10004      # 4-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(R.LIB_PATH):
+        BUILD.build()
+    return R.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(rec_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in rec.h but not exported"
+    assert sorted(R.EXPORTS) == names
+
+
+def test_header_constants_match_binding(lib):
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"#define\s+(REC_\w+)\s+\(?(-?\w+)", text))
+    for name in ("REC_DIM", "REC_MAX_TABLES", "REC_MAX_SEQ_LEN", "REC_MAX_B", "REC_DIN_PACKED_BYTES"):
+        assert int(defs[name], 0) == getattr(R, name), name
+    enums = dict((k, int(v)) for k, v in re.findall(r"\b(REC_[A-Z0-9_]+)\s*=\s*(-?\d+)", text))
+    for name in ("REC_OK", "REC_EINVAL", "REC_EUNSUPPORTED", "REC_EHIP", "REC_EWORKSPACE",
+                 "REC_DIRECT", "REC_HASH", "REC_F32", "REC_BF16", "REC_BF16_PACKED"):
+        assert enums[name] == getattr(R, name), name
+    assert lib.rec_version() >= 100
+
+
+def _status(fn, *args):
+    s = fn(*args)
+    return s, R.rec_last_error()
+
+
+def _table(kind=R.REC_DIRECT, rows=100, dim=16, values=FAKE, keys=None, digests=None):
+    return R.table(kind, rows, values, keys, digests, None, dim=dim)
+
+
+def test_scan_errors(lib):
+    s, msg = _status(lib.rec_lengths_to_offsets, FAKE, -1, FAKE, FAKE, 64, None)
+    assert s == R.REC_EINVAL and "n < 0" in msg
+    s, msg = _status(lib.rec_lengths_to_offsets, FAKE, 10, None, FAKE, 64, None)
+    assert s == R.REC_EINVAL and "offsets" in msg
+    s, msg = _status(lib.rec_lengths_to_offsets, None, 10, FAKE, FAKE, 64, None)
+    assert s == R.REC_EINVAL and "lengths" in msg
+    need = R.rec_scan_workspace_bytes(5000)
+    assert need > 0 and R.rec_scan_workspace_bytes(0) == 0
+    s, msg = _status(lib.rec_lengths_to_offsets, FAKE, 5000, FAKE, FAKE, need - 1, None)
+    assert s == R.REC_EWORKSPACE
+    s, msg = _status(lib.rec_lengths_to_offsets, FAKE, 5000, FAKE, None, need, None)
+    assert s == R.REC_EWORKSPACE
+
+
+def test_embbag_errors(lib):
+    tabs = R._tables([_table() for _ in range(16)])
+    ok = dict(tables=tabs, T=16, B=4, values=FAKE, lengths=FAKE, offsets=FAKE, out=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return _status(lib.rec_embbag_fwd, a["tables"], a["T"], a["B"], a["values"], a["lengths"],
+                       a["offsets"], a["out"], None, None)
+    assert call(tables=None)[0] == R.REC_EINVAL
+    assert call(T=0)[0] == R.REC_EINVAL
+    assert call(T=R.REC_MAX_TABLES + 1)[0] == R.REC_EUNSUPPORTED
+    assert call(B=-1)[0] == R.REC_EINVAL
+    assert call(values=None)[0] == R.REC_EINVAL
+    assert call(out=FAKE_ODD)[0] == R.REC_EINVAL
+    bad = R._tables([_table() for _ in range(15)] + [_table(dim=8)])
+    s, msg = call(tables=bad)
+    assert s == R.REC_EINVAL and "dim" in msg
+    bad = R._tables([_table(rows=0)] + [_table() for _ in range(15)])
+    assert call(tables=bad)[0] == R.REC_EINVAL
+    bad = R._tables([_table(kind=7)] + [_table() for _ in range(15)])
+    assert call(tables=bad)[0] == R.REC_EINVAL
+    bad = R._tables([_table(kind=R.REC_HASH)] + [_table() for _ in range(15)])
+    s, msg = call(tables=bad)
+    assert s == R.REC_EINVAL and "keys" in msg
+    bad = R._tables([_table(values=FAKE_ODD)] + [_table() for _ in range(15)])
+    assert call(tables=bad)[0] == R.REC_EINVAL
+    # B == 0 is a documented no-op (no device work)
+    s, msg = call(B=0)
+    assert s == R.REC_OK and msg == ""
+
+
+def test_hash_lookup_errors(lib):
+    h = _table(kind=R.REC_HASH, keys=FAKE, digests=FAKE)
+    d = _table()
+    assert _status(lib.rec_hash_lookup, None, FAKE, 4, FAKE, None, None)[0] == R.REC_EINVAL
+    s, msg = _status(lib.rec_hash_lookup, C.byref(d), FAKE, 4, FAKE, None, None)
+    assert s == R.REC_EINVAL and "REC_HASH" in msg
+    assert _status(lib.rec_hash_lookup, C.byref(h), FAKE, 4, None, None, None)[0] == R.REC_EINVAL
+    assert _status(lib.rec_hash_lookup, C.byref(h), None, 4, FAKE, None, None)[0] == R.REC_EINVAL
+    assert _status(lib.rec_hash_lookup, C.byref(h), FAKE, -1, FAKE, None, None)[0] == R.REC_EINVAL
+    assert _status(lib.rec_hash_lookup, C.byref(h), FAKE, 4, None, FAKE_ODD, None)[0] == R.REC_EINVAL
+    assert _status(lib.rec_hash_lookup, C.byref(h), FAKE, 0, FAKE, None, None)[0] == R.REC_OK
+
+
+def test_din_pack_errors(lib):
+    m = R.din_mlp(R.REC_F32, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0)
+    assert _status(lib.rec_din_pack_mlp, C.byref(m), FAKE, R.REC_DIN_PACKED_BYTES, None)[0] == R.REC_EINVAL
+    m = R.din_mlp(R.REC_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0)
+    assert _status(lib.rec_din_pack_mlp, None, FAKE, R.REC_DIN_PACKED_BYTES, None)[0] == R.REC_EINVAL
+    assert _status(lib.rec_din_pack_mlp, C.byref(m), None, R.REC_DIN_PACKED_BYTES, None)[0] == R.REC_EINVAL
+    assert _status(lib.rec_din_pack_mlp, C.byref(m), FAKE_ODD, R.REC_DIN_PACKED_BYTES, None)[0] == R.REC_EINVAL
+    assert (_status(lib.rec_din_pack_mlp, C.byref(m), FAKE, R.REC_DIN_PACKED_BYTES - 16, None)[0]
+            == R.REC_EWORKSPACE)
+
+
+def test_din_plan_errors(lib):
+    seq = R._tables([_table() for _ in range(3)])
+    B, ml = 64, 100
+    pb = R.rec_din_plan_bytes(B, ml)
+    assert pb > 20 * B * ml
+    assert R.rec_din_plan_bytes(-1, 100) == 0 and R.rec_din_plan_bytes(4, 0) == 0
+    assert R.rec_din_plan_bytes(4, R.REC_MAX_SEQ_LEN + 1) == 0
+    assert R.rec_din_plan_bytes(R.REC_MAX_B + 1, 1) == 0
+
+    def call(**kw):
+        a = dict(tables=seq, values=FAKE, stride=B * 4, offsets=None, lengths=FAKE, B=B, ml=ml,
+                 rp=0, plan=FAKE, pb=pb)
+        a.update(kw)
+        return _status(lib.rec_din_plan, a["tables"], a["values"], a["stride"], a["offsets"],
+                       a["lengths"], a["B"], a["ml"], a["rp"], None, None, a["plan"], a["pb"], None)
+    assert call(B=-1)[0] == R.REC_EINVAL
+    assert call(B=R.REC_MAX_B + 1)[0] == R.REC_EUNSUPPORTED
+    assert call(ml=0)[0] == R.REC_EINVAL
+    assert call(ml=R.REC_MAX_SEQ_LEN + 1)[0] == R.REC_EINVAL
+    for rp in (8, 24, -16, (1 << 20) + 16):
+        s, msg = call(rp=rp)
+        assert s == R.REC_EINVAL and "range_positions" in msg
+    assert call(tables=None)[0] == R.REC_EINVAL
+    assert call(lengths=None)[0] == R.REC_EINVAL
+    assert call(values=None)[0] == R.REC_EINVAL
+    assert call(stride=-1)[0] == R.REC_EINVAL
+    assert call(plan=None)[0] == R.REC_EINVAL
+    assert call(plan=FAKE_ODD)[0] == R.REC_EINVAL
+    assert call(pb=pb - 1)[0] == R.REC_EWORKSPACE
+    bad = R._tables([_table(), _table(dim=4), _table()])
+    assert call(tables=bad)[0] == R.REC_EINVAL
+    assert call(B=0, pb=R.rec_din_plan_bytes(0, ml))[0] == R.REC_OK
+
+
+def test_din_attn_errors(lib):
+    seq = R._tables([_table() for _ in range(3)])
+    B, ml = 64, 100
+    pb = R.rec_din_plan_bytes(B, ml)
+    good = R.din_mlp(R.REC_BF16_PACKED, FAKE, FAKE, None, FAKE, FAKE, 0.0)
+
+    def call(**kw):
+        a = dict(tables=seq, plan=FAKE, pb=pb, B=B, ml=ml, q=FAKE, qld=256, qcol=(16, 80, 48),
+                 mlp=good, out=FAKE, scores=None, weights=None)
+        a.update(kw)
+        qc = None if a["qcol"] is None else (C.c_int32 * 3)(*a["qcol"])
+        mlp = None if a["mlp"] is None else C.byref(a["mlp"])
+        return _status(lib.rec_din_attn_fwd, a["tables"], a["plan"], a["pb"], a["B"], a["ml"],
+                       a["q"], a["qld"], qc, mlp, a["out"], a["scores"], a["weights"], None)
+    assert call(B=-1)[0] == R.REC_EINVAL
+    assert call(B=R.REC_MAX_B + 1)[0] == R.REC_EUNSUPPORTED
+    assert call(ml=0)[0] == R.REC_EINVAL
+    assert call(q=None)[0] == R.REC_EINVAL
+    assert call(qcol=None)[0] == R.REC_EINVAL
+    assert call(q=FAKE_ODD)[0] == R.REC_EINVAL
+    assert call(qld=250)[0] == R.REC_EINVAL
+    assert call(qcol=(16, 82, 48))[0] == R.REC_EINVAL
+    assert call(qcol=(16, 80, 248))[0] == R.REC_EINVAL
+    assert call(mlp=None)[0] == R.REC_EINVAL
+    assert call(mlp=R.din_mlp(9, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0))[0] == R.REC_EINVAL
+    assert call(mlp=R.din_mlp(R.REC_BF16, FAKE, FAKE, None, FAKE, FAKE, 0.0))[0] == R.REC_EINVAL
+    assert call(mlp=R.din_mlp(R.REC_F32, FAKE_ODD, FAKE, FAKE, FAKE, FAKE, 0.0))[0] == R.REC_EINVAL
+    assert call(out=None)[0] == R.REC_EINVAL
+    assert call(out=FAKE_ODD)[0] == R.REC_EINVAL
+    s, msg = call(weights=FAKE)
+    assert s == R.REC_EINVAL and "scores_out" in msg
+    assert call(plan=None)[0] == R.REC_EINVAL
+    assert call(pb=pb - 1)[0] == R.REC_EWORKSPACE
+    assert call(B=0, pb=R.rec_din_plan_bytes(0, ml))[0] == R.REC_OK
+
+
+def test_binding_raises_with_message(lib):
+    with pytest.raises(R.RecError) as ei:
+        R.rec_hash_lookup(_table(), FAKE, 4, FAKE)
+    assert ei.value.status == R.REC_EINVAL and "REC_HASH" in str(ei.value)
+
+
+# -- host twins of the device index arithmetic --------------------------------
+I64 = np.iinfo(np.int64)
+EDGE_X = [0, 1, -1, 2, -2, 99, 100, 101, -100, -101, I64.max, I64.min, I64.min + 1, I64.max - 1,
+          2**32, -2**32, 2**62 + 12345, -(2**62) - 12345]
+EDGE_N = [1, 2, 3, 5, 7, 98, 101, 12961, 255877, 846812, 1141730, 2**31 - 1, 2**32 + 15,
+          2**62 + 1, I64.max]
+
+
+def test_host_floor_mod_edges(lib):
+    """Invariant-divisor floor modulo against Python's % (floor semantics)."""
+    for n in EDGE_N:
+        for x in EDGE_X:
+            assert R.rec_host_floor_mod(x, n) == x % n, (x, n)
+
+
+def test_host_floor_mod_random(lib):
+    rng = np.random.default_rng(7)
+    ns = np.concatenate([rng.integers(1, 2**20, 40), rng.integers(1, I64.max, 40, dtype=np.int64)])
+    xs = rng.integers(I64.min, I64.max, 60, dtype=np.int64, endpoint=True)
+    for n in ns:
+        for x in xs:
+            assert R.rec_host_floor_mod(int(x), int(n)) == int(x) % int(n)
+
+
+def test_host_hash_home_matches_generator(lib):
+    """Home slot and digest against the generator's table layout (the format
+    both sides of a hash table share)."""
+    rng = np.random.default_rng(11)
+    keys = np.concatenate([rng.integers(I64.min, I64.max, 500, dtype=np.int64),
+                           np.array([0, 1, -2, I64.max, I64.min], np.int64)])
+    for cap in (1, 7, 300000, 2**31 - 1):
+        h = synth.splitmix64_mix(keys)
+        home = synth.home_slot(h, cap)
+        dig = synth.digest_of(h)
+        for k, h, d in zip(keys, home, dig):
+            got_h, got_d = R.rec_host_hash_home(int(k), cap)
+            assert got_h == int(h) and got_d == int(d)
+            assert 0 <= got_h < cap and got_d != 0
