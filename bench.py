@@ -6,9 +6,10 @@ A step is one pass of the whole path over one batch already resident in HBM:
 lengths -> offsets, sequence plan, sum-pooled embedding bags (16 tables,
 3.14M rows), padding-free DIN attention (bf16 matrix cores, fp32 accumulate).
 Four resident batches rotate (so the L2 does not keep one batch's rows); one
-HIP graph holds a step for each of them and is replayed.  The sequence plan
-runs on a second stream, concurrently with the offsets scan and the
-embedding bags.  Prints one JSON line.
+HIP graph holds a step for each of them and is replayed.  Everything runs on
+one stream: inside a graph, a fork/join to a second stream costs more than
+the overlap it buys for the short plan (--side-stream to compare).  Prints
+one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config 2]
 """
@@ -50,7 +51,9 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=100)
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-graph", action="store_true")
-    p.add_argument("--no-side-stream", action="store_true")
+    p.add_argument("--side-stream", action="store_true",
+                   help="run the sequence plan on a second stream (pays off when the plan is long, "
+                        "e.g. hash-table sequence ids)")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 64 MiB elementwise copy (for counter scaling)")
@@ -163,7 +166,7 @@ def main():
             for _ in dbs]
     nb = len(dbs)
     stream = torch.cuda.Stream()
-    side = None if a.no_side_stream else torch.cuda.Stream()
+    side = torch.cuda.Stream() if a.side_stream else None
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for f, db in zip(fwds, dbs):

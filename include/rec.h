@@ -179,6 +179,39 @@ rec_status rec_embbag_fwd(const rec_table* tables, int32_t T, int64_t B,
                           const int64_t* offsets, float* out, int64_t* rows_out,
                           void* stream);
 
+/* Bytes of the KJT sums for T tables of B samples (about 0.26 B per bag); 0
+ * for invalid arguments. */
+size_t rec_kjt_sums_bytes(int32_t T, int64_t B);
+
+/*
+ * First half of the key-major offsets scan ("当前现状分析" §2), for callers
+ * that hold only the KJT lengths: per table and 1024-sample block the block
+ * sum, and per 32-sample chunk the chunk sum, written to `sums` (opaque,
+ * >= rec_kjt_sums_bytes(T, B) bytes, 8-byte aligned).  rec_embbag_fwd_kjt
+ * finishes the scan inside the embedding bags.
+ *   lengths  int32[T*B], each >= 0
+ * Errors: REC_EINVAL (null pointers, T < 1, B < 0, misalignment),
+ * REC_EUNSUPPORTED (T > REC_MAX_TABLES), REC_EWORKSPACE.  B == 0 is a no-op.
+ */
+rec_status rec_kjt_sums(const int32_t* lengths, int32_t T, int64_t B, void* sums,
+                        size_t sums_bytes, void* stream);
+
+/*
+ * rec_embbag_fwd for a KJT given by its lengths alone: each bag's offset is
+ * derived on the device from `sums` (rec_kjt_sums of the same lengths, T and
+ * B, earlier on the stream), so the offsets scan and the pooling take two
+ * launches in all.  Same tables, values, lengths, out and rows_out as
+ * rec_embbag_fwd, and bit-identical output.
+ *   offsets_out int64[T*B+1] or NULL: the derived offsets (offsets[0] = 0,
+ *               offsets[i+1] = offsets[i] + lengths[i])
+ * Errors: as rec_embbag_fwd, plus REC_EINVAL (null or misaligned sums) and
+ * REC_EWORKSPACE (sums_bytes too small).
+ */
+rec_status rec_embbag_fwd_kjt(const rec_table* tables, int32_t T, int64_t B,
+                              const int64_t* values, const int32_t* lengths, const void* sums,
+                              size_t sums_bytes, int64_t* offsets_out, float* out,
+                              int64_t* rows_out, void* stream);
+
 /*
  * Lookup-only hash probe ("集成 DynamicEmb" §3.2, §4.3) for n keys.
  *   table     host descriptor, kind REC_HASH

@@ -129,8 +129,62 @@ rec_status rec_embbag_fwd(const rec_table* tables, int32_t T, int64_t B, const i
     a.rows_out = rows_out;
     a.B = B;
     a.T = T;
-    a.chunks = (T + 15) / 16;
     return hip_status(launch_embbag(a, (hipStream_t)stream), "rec_embbag_fwd");
+}
+
+size_t rec_kjt_sums_bytes(int32_t T, int64_t B) {
+    if (T < 1 || T > REC_MAX_TABLES || B < 0) return 0;
+    return kjt_layout(T, B).bytes;
+}
+
+rec_status rec_kjt_sums(const int32_t* lengths, int32_t T, int64_t B, void* sums,
+                        size_t sums_bytes, void* stream) {
+    if (T < 1) return fail(REC_EINVAL, "rec_kjt_sums: T < 1");
+    if (T > REC_MAX_TABLES) return fail(REC_EUNSUPPORTED, "rec_kjt_sums: T > REC_MAX_TABLES");
+    if (B < 0) return fail(REC_EINVAL, "rec_kjt_sums: B < 0");
+    if (B > 0 && !lengths) return fail(REC_EINVAL, "rec_kjt_sums: lengths is NULL");
+    if (!sums) return fail(REC_EINVAL, "rec_kjt_sums: sums is NULL");
+    if ((uintptr_t)sums & 7u) return fail(REC_EINVAL, "rec_kjt_sums: sums not 8-byte aligned");
+    if (sums_bytes < rec_kjt_sums_bytes(T, B))
+        return fail(REC_EWORKSPACE, "rec_kjt_sums: sums smaller than rec_kjt_sums_bytes(T, B)");
+    if (B == 0) return ok();
+    return hip_status(launch_kjt_sums(lengths, T, B, sums, (hipStream_t)stream), "rec_kjt_sums");
+}
+
+rec_status rec_embbag_fwd_kjt(const rec_table* tables, int32_t T, int64_t B,
+                              const int64_t* values, const int32_t* lengths, const void* sums,
+                              size_t sums_bytes, int64_t* offsets_out, float* out,
+                              int64_t* rows_out, void* stream) {
+    if (!tables) return fail(REC_EINVAL, "rec_embbag_fwd_kjt: tables is NULL");
+    if (T < 1) return fail(REC_EINVAL, "rec_embbag_fwd_kjt: T < 1");
+    if (T > REC_MAX_TABLES) return fail(REC_EUNSUPPORTED, "rec_embbag_fwd_kjt: T > REC_MAX_TABLES");
+    if (B < 0) return fail(REC_EINVAL, "rec_embbag_fwd_kjt: B < 0");
+    if (!values || !lengths || !sums || !out)
+        return fail(REC_EINVAL, "rec_embbag_fwd_kjt: values, lengths, sums and out are required");
+    if (!aligned16(out)) return fail(REC_EINVAL, "rec_embbag_fwd_kjt: out not 16-byte aligned");
+    if ((uintptr_t)sums & 7u) return fail(REC_EINVAL, "rec_embbag_fwd_kjt: sums not 8-byte aligned");
+    if (sums_bytes < rec_kjt_sums_bytes(T, B))
+        return fail(REC_EWORKSPACE, "rec_embbag_fwd_kjt: sums smaller than rec_kjt_sums_bytes(T, B)");
+    EmbArgs a;
+    memset(&a, 0, sizeof(a));
+    for (int t = 0; t < T; ++t) {
+        rec_status s = prep_table(tables[t], "rec_embbag_fwd_kjt: table", &a.tab[t]);
+        if (s != REC_OK) return s;
+    }
+    if (B == 0) return ok();
+    const KjtLayout k = kjt_layout(T, B);
+    a.values = values;
+    a.lengths = lengths;
+    a.offsets = nullptr;
+    a.kjt_bs = (const int64_t*)sums;
+    a.kjt_cs = (const int64_t*)((const char*)sums + k.off_cs);
+    a.nK = k.nK;
+    a.offsets_out = offsets_out;
+    a.out = out;
+    a.rows_out = rows_out;
+    a.B = B;
+    a.T = T;
+    return hip_status(launch_embbag(a, (hipStream_t)stream), "rec_embbag_fwd_kjt");
 }
 
 rec_status rec_hash_lookup(const rec_table* table, const int64_t* keys, int64_t n,
@@ -199,8 +253,6 @@ rec_status rec_din_plan(const rec_table* seq_tables, const int64_t* seq_values,
             return fail(REC_EUNSUPPORTED, "rec_din_plan: sequence tables are limited to 2^31-1 rows");
     }
     if (B == 0) return ok();
-    const int cus = num_cus();
-    if (cus < 1) return fail(REC_EHIP, "rec_din_plan: cannot query the device");
     a.seq_values = seq_values;
     a.seq_stride = seq_stride;
     a.seq_offsets = seq_offsets;
@@ -208,7 +260,6 @@ rec_status rec_din_plan(const rec_table* seq_tables, const int64_t* seq_values,
     a.B = B;
     a.max_len = max_len;
     a.range_positions = range_positions;
-    a.num_cus = cus;
     a.seq_offsets_out = seq_offsets_out;
     a.rows_out = rows_out;
     a.plan = plan;
@@ -273,6 +324,7 @@ rec_status rec_din_attn_fwd(const rec_table* seq_tables, void* plan, size_t plan
     a.pos_jr = (const int32_t*)(p + L.off_pjr);
     a.pos_rows = (const int32_t*)(p + L.off_prows);
     a.partials = (float*)(p + L.off_part);
+    a.empty = (const int32_t*)(p + L.off_empty);
     a.pmax = L.pmax;
     a.out = out;
     a.scores = scores_out;

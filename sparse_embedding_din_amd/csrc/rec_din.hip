@@ -24,9 +24,13 @@
 //      segmented softmax: DPP row shifts scan max and sums within each
 //      sample's run of lanes, and one open sample carries its running max,
 //      sum and weighted sum into the next tile.
-// A sample cut by a range edge leaves its partial (max, sum, weighted sum)
-// in the plan; k_din_finalize merges those (the standard rescaling of
-// partial softmax sums) and writes the zero output of empty samples.
+// A sample cut by range edges leaves one partial (max, sum, weighted sum) per
+// piece in the plan, and k_din_finalize merges the pieces with the standard
+// rescaling of partial softmax sums.  (Merging inside this kernel would need
+// a device-wide release/acquire per wave; on a chip whose L2 is per XCD that
+// costs far more than a second small launch.)  Samples without positions
+// (listed by the plan) get their zero output from whichever wave the list
+// assigns.
 // Inside an MFMA the order of the K index is free as long as the A and B
 // operands agree, so each lane's 48 inputs are laid out to match its own 12
 // features, and the weights are permuted to the same order (rec_din_pack_mlp,
@@ -170,69 +174,48 @@ __device__ inline float score_from_h2(const f32x4 (&acc2)[4], const float* b2s, 
     return p + b3;
 }
 
-// A fragments of one hidden block hb: 12 of W1 (6 k-blocks x 2 row tiles)
-// and 4 of W2, read from LDS in one batch so their latency is paid once per
-// block; the next block's batch is issued before this block's products.
-struct Frags {
-    uint4 w1[12];
-    uint4 w2[4];
-};
-
-__device__ inline void load_frags(Frags& f, const uint4* w1p, const uint4* w2p, int hb, int lane) {
-#pragma unroll
-    for (int i = 0; i < 12; ++i) f.w1[i] = w1p[(hb * 12 + i) * 64 + lane];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) f.w2[mt] = w2p[(hb * 4 + mt) * 64 + lane];
+// max(RNE(a), 0), max(RNE(b), 0) as a bf16 pair.  Rounding to nearest keeps
+// the sign, so ReLU after rounding equals rounding after ReLU; on the bit
+// patterns a negative bf16 (or -0) is a negative int16, so the ReLU is one
+// packed integer max for two values.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t relu_pk_bf16(float a, float b) {
+    bf16x2 p;
+    p[0] = (__bf16)a;
+    p[1] = (__bf16)b;
+    s16x2 v = __builtin_bit_cast(s16x2, p);
+    v = __builtin_elementwise_max(v, (s16x2){0, 0});
+    return __builtin_bit_cast(uint32_t, v);
 }
 
-// One hidden block hb of both layers for NSUB position tiles: the 256-wide
-// layer's 32 units of hb (A fragments in `cur`), then bias, ReLU, bf16, and
-// their contribution to the 64-wide layer.  The next block's fragments are
-// read from LDS into `nxt` before this block's products are issued.
+// Layer 1 for one hidden block: two 16-row tiles x NSUB position tiles, the
+// K loop (6 steps of 32) innermost in issue order so 2*NSUB independent
+// accumulations are in flight.
 template <int NSUB>
-__device__ inline void mlp_block(const bf16x8 (&xf)[NSUB][6], f32x4 (&acc2)[NSUB][4],
-                                 const Frags& cur, Frags& nxt, bool load_next,
-                                 const uint4* w1p, const uint4* w2p, const float* b1s, int hb,
-                                 int lane) {
-    const int g = lane >> 4;
-    if (load_next) load_frags(nxt, w1p, w2p, hb + 1, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 acc1[NSUB][2];
+__device__ inline void l1_block(const bf16x8 (&xf)[NSUB][6], const uint4 (&w1)[12],
+                                f32x4 (&acc1)[NSUB][2]) {
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
         acc1[s][0] = f32x4{0.f, 0.f, 0.f, 0.f};
         acc1[s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
-    for (int kb = 0; kb < 6; ++kb) {
-        const bf16x8 a0 = __builtin_bit_cast(bf16x8, cur.w1[kb * 2 + 0]);
-        const bf16x8 a1 = __builtin_bit_cast(bf16x8, cur.w1[kb * 2 + 1]);
+    for (int kb = 0; kb < 6; ++kb)
 #pragma unroll
-        for (int s = 0; s < NSUB; ++s) {
-            acc1[s][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, xf[s][kb], acc1[s][0], 0, 0, 0);
-            acc1[s][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, xf[s][kb], acc1[s][1], 0, 0, 0);
-        }
-    }
-    const float4 bA = *(const float4*)(b1s + hb * 32 + 4 * g);
-    const float4 bB = *(const float4*)(b1s + hb * 32 + 16 + 4 * g);
+        for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-        bf16x8 h;
-        h[0] = (__bf16)fmaxf(acc1[s][0][0] + bA.x, 0.f);
-        h[1] = (__bf16)fmaxf(acc1[s][0][1] + bA.y, 0.f);
-        h[2] = (__bf16)fmaxf(acc1[s][0][2] + bA.z, 0.f);
-        h[3] = (__bf16)fmaxf(acc1[s][0][3] + bA.w, 0.f);
-        h[4] = (__bf16)fmaxf(acc1[s][1][0] + bB.x, 0.f);
-        h[5] = (__bf16)fmaxf(acc1[s][1][1] + bB.y, 0.f);
-        h[6] = (__bf16)fmaxf(acc1[s][1][2] + bB.z, 0.f);
-        h[7] = (__bf16)fmaxf(acc1[s][1][3] + bB.w, 0.f);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-            acc2[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, cur.w2[mt]), h, acc2[s][mt], 0, 0, 0);
-    }
+            for (int rt = 0; rt < 2; ++rt)
+                acc1[s][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, w1[kb * 2 + rt]), xf[s][kb], acc1[s][rt], 0, 0, 0);
 }
 
+// The bf16 MLP for NSUB position tiles, software-pipelined over the eight
+// hidden blocks: while block hb's layer-1 results go through bias, ReLU and
+// bf16 into its layer-2 products, block hb+1's layer-1 products are already
+// issued.  W1 fragments are read from LDS one block ahead of use; a
+// scheduling fence per block keeps the compiler from hoisting every block's
+// reads (which would not fit in registers).
 template <int NSUB>
 __device__ inline void mlp_bf16(const Sub* S, const uint4* w1p, const uint4* w2p, const float* b1s,
                                 const float* b2s, const float* w3s, float b3, int lane,
@@ -248,15 +231,41 @@ __device__ inline void mlp_bf16(const Sub* S, const uint4* w1p, const uint4* w2p
     for (int s = 0; s < NSUB; ++s)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) acc2[s][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // the eight hidden blocks as four rolled iterations of a ping-pong pair,
-    // which keeps the code (run about once per wave) small
-    Frags fa, fb;
-    load_frags(fa, w1p, w2p, 0, lane);
-#pragma unroll 1
-    for (int hb = 0; hb < 8; hb += 2) {
-        mlp_block<NSUB>(xf, acc2, fa, fb, true, w1p, w2p, b1s, hb, lane);
-        mlp_block<NSUB>(xf, acc2, fb, fa, hb + 2 < 8, w1p, w2p, b1s, hb + 1, lane);
+    uint4 fw1[2][12], fw2[4];
+    f32x4 acc1[2][NSUB][2];
+#pragma unroll
+    for (int i = 0; i < 12; ++i) fw1[0][i] = w1p[i * 64 + lane];
+    l1_block<NSUB>(xf, fw1[0], acc1[0]);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) fw1[1][i] = w1p[(12 + i) * 64 + lane];
+#pragma unroll
+    for (int hb = 0; hb < 8; ++hb) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int cur = hb & 1, nxt = cur ^ 1;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) fw2[mt] = w2p[(hb * 4 + mt) * 64 + lane];
+        if (hb + 1 < 8) l1_block<NSUB>(xf, fw1[nxt], acc1[nxt]);
+        if (hb + 2 < 8) {
+#pragma unroll
+            for (int i = 0; i < 12; ++i) fw1[cur][i] = w1p[((hb + 2) * 12 + i) * 64 + lane];
+        }
+        const float4 bA = *(const float4*)(b1s + hb * 32 + 4 * g);
+        const float4 bB = *(const float4*)(b1s + hb * 32 + 16 + 4 * g);
+#pragma unroll
+        for (int s = 0; s < NSUB; ++s) {
+            uint4 hp;
+            hp.x = relu_pk_bf16(acc1[cur][s][0][0] + bA.x, acc1[cur][s][0][1] + bA.y);
+            hp.y = relu_pk_bf16(acc1[cur][s][0][2] + bA.z, acc1[cur][s][0][3] + bA.w);
+            hp.z = relu_pk_bf16(acc1[cur][s][1][0] + bB.x, acc1[cur][s][1][1] + bB.y);
+            hp.w = relu_pk_bf16(acc1[cur][s][1][2] + bB.z, acc1[cur][s][1][3] + bB.w);
+            const bf16x8 h = __builtin_bit_cast(bf16x8, hp);
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                acc2[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, fw2[mt]), h, acc2[s][mt], 0, 0, 0);
+        }
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) e[s] = score_from_h2(acc2[s], b2s, w3s, b3, g);
 }
@@ -325,7 +334,8 @@ __device__ inline void mlp_f32(const Sub* S, const float* __restrict__ w1,
 // r.  A sample's run inside the range ends at the lane where rl == 0: a
 // sample wholly inside the range writes its output there; one cut by the
 // range's start (head, slot 0) or end (tail, slot 1) leaves its unnormalised
-// state for k_din_finalize.
+// state in the plan; a tail piece also records its sample and where the
+// sample ends, which is all k_din_finalize needs to find the other pieces.
 __device__ inline void softmax_tile(const DinArgs& a, const Sub& S, float e, int lane, int r,
                                     float& m_open, float& l_open, float (&acc_open)[12]) {
     const int n = lane & 15, g = lane >> 4;
@@ -361,8 +371,11 @@ __device__ inline void softmax_tile(const DinArgs& a, const Sub& S, float e, int
             for (int q = 0; q < 3; ++q)
                 o[q] = make_float4(A[4 * q] * inv, A[4 * q + 1] * inv, A[4 * q + 2] * inv, A[4 * q + 3] * inv);
         } else {
-            float* ps = a.partials + ((int64_t)r * 2 + (S.j > S.jl ? 0 : 1)) * kPartialFloats;
-            if (g == 0) *(float2*)ps = make_float2(mref, l);
+            const bool is_head = S.j > S.jl;
+            float* ps = a.partials + ((int64_t)r * 2 + (is_head ? 0 : 1)) * kPartialFloats;
+            if (g == 0)
+                *(float4*)ps = make_float4(mref, l, __int_as_float(S.b),
+                                           __int_as_float((int)S.pos + S.rem + 1));
             float4* o = (float4*)(ps + 4 + 12 * g);
 #pragma unroll
             for (int q = 0; q < 3; ++q) o[q] = make_float4(A[4 * q], A[4 * q + 1], A[4 * q + 2], A[4 * q + 3]);
@@ -542,6 +555,15 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
     // Rounds of up to 32 positions.  While one round's MLP runs, the next
     // round's entries are in flight; its s and q loads are issued before this
     // round's softmax.
+    // samples without positions: zero output, spread over every wave
+    {
+        const int32_t ne = a.plan_hdr[kHdrNEmpty];
+        for (int i = (blockIdx.x * kDinWaves + wave) * 64 + lane; i < ne; i += stride * 64) {
+            float4* o = (float4*)(a.out + (int64_t)a.empty[i] * 48);
+#pragma unroll
+            for (int q = 0; q < 12; ++q) o[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
     float m_open = -INFINITY, l_open = 0.f, acc_open[12];
 #pragma unroll
     for (int f = 0; f < 12; ++f) acc_open[f] = 0.f;
@@ -591,48 +613,46 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
     }
 }
 
-// One thread per sample b (zero output when it has no positions) and per
-// range edge r*R (the sample cut there, if it starts in range r-1: merge the
-// tail state of range r-1 with the head states of the ranges it reaches).
+// One thread per range edge e (between ranges e-1 and e).  The sample cut
+// there is merged here if it starts in range e-1: then range e-1 holds its
+// tail piece (with the sample and its end) and ranges e .. (end-1)/R hold
+// head pieces.  The edge's first position and the tail piece are read
+// together, so the merge costs three dependent rounds of loads.
 __global__ __launch_bounds__(256) void k_din_finalize(const DinArgs a) {
     const int64_t P = a.plan_hdr[kHdrP];
     const int64_t R = din_range(P, a.plan_hdr[kHdrRReq], a.waves);
     const int64_t nr = (P + R - 1) / R;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < a.B && a.pos_start[i + 1] == a.pos_start[i]) {
-        float4* o = (float4*)(a.out + i * 48);
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x + 1; e < nr; e += (int64_t)gridDim.x * 256) {
+        const int64_t p = e * R;
+        const int j = a.pos_jr[p] & 0xffff;
+        const float4 t = *(const float4*)(a.partials + ((e - 1) * 2 + 1) * kPartialFloats);
+        if (j == 0 || p - j < (e - 1) * R) continue;
+        const int b = __float_as_int(t.z);
+        const int64_t pe = __float_as_int(t.w), ps = p - j;
+        const int64_t r1 = (pe - 1) / R;
+        const float* tp = a.partials + ((e - 1) * 2 + 1) * kPartialFloats;
+        float m = t.x, l = t.y;
+        float acc[48];
 #pragma unroll
-        for (int q = 0; q < 12; ++q) o[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int f = 0; f < 48; ++f) acc[f] = tp[4 + f];
+        for (int64_t r = e; r <= r1; ++r) {
+            const float* h = a.partials + (r * 2) * kPartialFloats;
+            const float mh = h[0];
+            const float mn = fmaxf(m, mh);
+            const float sa = __expf(m - mn), sh = __expf(mh - mn);
+            l = l * sa + h[1] * sh;
+#pragma unroll
+            for (int f = 0; f < 48; ++f) acc[f] = acc[f] * sa + h[4 + f] * sh;
+            m = mn;
+        }
+        const float inv = 1.f / l;
+        float4* o = (float4*)(a.out + (int64_t)b * 48);
+#pragma unroll
+        for (int q = 0; q < 12; ++q)
+            o[q] = make_float4(acc[4 * q] * inv, acc[4 * q + 1] * inv, acc[4 * q + 2] * inv, acc[4 * q + 3] * inv);
+        if (a.weights)
+            for (int64_t q = ps; q < pe; ++q) a.weights[q] = __expf(a.scores[q] - m) / l;
     }
-    if (i < 1 || i >= nr) return;
-    const int64_t p = i * R;
-    const int j = a.pos_jr[p] & 0xffff;
-    if (j == 0 || p - j < (i - 1) * R) return;
-    const int b = a.pos_b[p];
-    const int64_t ps = p - j, pe = a.pos_start[b + 1];
-    const int64_t r1 = (pe - 1) / R;
-    const float* t = a.partials + ((i - 1) * 2 + 1) * kPartialFloats;
-    float m = t[0], l = t[1];
-    float acc[48];
-#pragma unroll
-    for (int f = 0; f < 48; ++f) acc[f] = t[4 + f];
-    for (int64_t r = i; r <= r1; ++r) {
-        const float* h = a.partials + (r * 2) * kPartialFloats;
-        const float mh = h[0];
-        const float mn = fmaxf(m, mh);
-        const float sa = __expf(m - mn), sh = __expf(mh - mn);
-        l = l * sa + h[1] * sh;
-#pragma unroll
-        for (int f = 0; f < 48; ++f) acc[f] = acc[f] * sa + h[4 + f] * sh;
-        m = mn;
-    }
-    const float inv = 1.f / l;
-    float4* o = (float4*)(a.out + (int64_t)b * 48);
-#pragma unroll
-    for (int q = 0; q < 12; ++q)
-        o[q] = make_float4(acc[4 * q] * inv, acc[4 * q + 1] * inv, acc[4 * q + 2] * inv, acc[4 * q + 3] * inv);
-    if (a.weights)
-        for (int64_t q = ps; q < pe; ++q) a.weights[q] = __expf(a.scores[q] - m) / l;
 }
 
 }  // namespace
@@ -649,10 +669,13 @@ hipError_t launch_din(const DinArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(k_din_attn<REC_F32>, grid, block, 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // threads cover every sample and every range edge
-    const int64_t max_ranges = a.pmax / kMinRange + 1;
-    const int64_t n = a.B > max_ranges ? a.B : max_ranges;
-    hipLaunchKernelGGL(k_din_finalize, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    // enough threads for the edges of the even split; a grid-stride loop
+    // covers the many more edges a small requested range can make
+    const int64_t edges = a.pmax / kMinRange + 1;
+    int64_t blocks = (edges + 255) / 256;
+    const int64_t cap = (a.waves + 255) / 256 * 4;
+    if (blocks > cap) blocks = cap;
+    hipLaunchKernelGGL(k_din_finalize, dim3((unsigned)blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

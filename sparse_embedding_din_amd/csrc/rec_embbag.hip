@@ -14,6 +14,12 @@
 // are clamped into the bag, rows of misses point at row 0) and masked
 // afterwards, so a lane has all of a round's id loads and then all of its row
 // loads in flight at once.
+//
+// Given only the lengths (offsets == NULL), a wave derives its 64 bag offsets
+// itself from the KJT sums: the sum of the block sums before its block and of
+// the 32-sample chunk sums before its chunk, then a scan of its own 32
+// lengths per table.  Those loads are independent of the lengths, so the
+// offsets cost no extra round trip to memory.
 #include "rec_internal.h"
 
 namespace rec {
@@ -22,7 +28,7 @@ namespace {
 constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kUnroll = 3;           // ids per bag resolved per round
 
-template <bool kHash>
+template <bool kHash, bool kFused>
 __global__ __launch_bounds__(64 * kWaves) void k_embbag_fwd(const EmbArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t w = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -40,10 +46,37 @@ __global__ __launch_bounds__(64 * kWaves) void k_embbag_fwd(const EmbArgs a) {
     const int64_t rows = hi ? t1.rows : t0.rows;
     const uint64_t magic = hi ? t1.magic : t0.magic;
     const int32_t shift = hi ? t1.shift : t0.shift;
-    const int64_t bag = (int64_t)min(t, a.T - 1) * a.B + min(b, a.B - 1);
+    const int tc = min(t, a.T - 1);
+    const int64_t bag = (int64_t)tc * a.B + min(b, a.B - 1);
     int32_t len = a.lengths[bag];
-    const int64_t off = a.offsets[bag];
-    if (!live) len = 0;
+    int64_t off;
+    if (kFused) {
+        const int64_t kc = w % nbw;                              // 32-sample chunk of table tc
+        const int64_t blk = kc / (kScanChunk / kKjtChunk);      // 1024-sample block
+        const int c = (int)(kc % (kScanChunk / kKjtChunk));     // chunk inside it
+        const int l = lane & 31;
+        const int64_t nflat = (int64_t)tc * a.nK + blk;
+        int64_t s = 0;
+        for (int64_t i = l; i < nflat; i += 32) s += a.kjt_bs[i];
+        if (l < c) s += a.kjt_cs[nflat * (kScanChunk / kKjtChunk) + l];
+        if (!live) len = 0;
+        int64_t inc = len;
+#pragma unroll
+        for (int d = 1; d < 32; d <<= 1) {
+            const int64_t u = __shfl_up(inc, d, 32);
+            if (l >= d) inc += u;
+        }
+#pragma unroll
+        for (int d = 16; d >= 1; d >>= 1) s += __shfl_xor(s, d, 32);
+        off = s + inc - len;
+        if (a.offsets_out) {
+            if (live) a.offsets_out[bag] = off;
+            if (live && t == a.T - 1 && b == a.B - 1) a.offsets_out[(int64_t)a.T * a.B] = off + len;
+        }
+    } else {
+        off = a.offsets[bag];
+        if (!live) len = 0;
+    }
     float4 acc[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -113,8 +146,14 @@ hipError_t launch_embbag(const EmbArgs& a, hipStream_t s) {
     const int64_t blocks = (waves + kWaves - 1) / kWaves;
     bool hash = false;
     for (int t = 0; t < a.T; ++t) hash = hash || a.tab[t].kind == REC_HASH;
-    if (hash) hipLaunchKernelGGL(k_embbag_fwd<true>, dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, a);
-    else hipLaunchKernelGGL(k_embbag_fwd<false>, dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, a);
+    const dim3 grid((unsigned)blocks), block(64 * kWaves);
+    if (a.offsets) {
+        if (hash) hipLaunchKernelGGL((k_embbag_fwd<true, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_embbag_fwd<false, false>), grid, block, 0, s, a);
+    } else {
+        if (hash) hipLaunchKernelGGL((k_embbag_fwd<true, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_embbag_fwd<false, true>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

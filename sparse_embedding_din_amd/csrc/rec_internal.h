@@ -103,6 +103,24 @@ constexpr int kScanChunk = kScanThreads * kScanItems;     // 1024 lengths per bl
 
 __host__ __device__ inline int64_t scan_blocks(int64_t n) { return (n + kScanChunk - 1) / kScanChunk; }
 
+// Sums of key-major KJT lengths [T][B] for the embedding bags to derive their
+// own offsets: per table t and 1024-sample block K, the block sum
+// bs[t*nK + K] (flat: the sum of every length before block (t, K) is the sum
+// of bs[0 .. t*nK + K)), and per 32-sample chunk kc = b / 32 of table t, the
+// chunk sum cs[(t*nK) * 32 + kc].
+constexpr int kKjtChunk = 32;
+struct KjtLayout {
+    int64_t nK;            // 1024-sample blocks per table
+    size_t off_cs, bytes;  // bs at 0
+};
+__host__ __device__ inline KjtLayout kjt_layout(int32_t T, int64_t B) {
+    KjtLayout k;
+    k.nK = scan_blocks(B);
+    k.off_cs = 8 * (size_t)T * (size_t)k.nK;
+    k.bytes = k.off_cs + 8 * (size_t)T * (size_t)k.nK * (kScanChunk / kKjtChunk);
+    return k;
+}
+
 // DIN plan buffer layout (bytes from the start).  Pmax = B * max_len bounds
 // the packed positions P = sum_b min(len_b, max_len); packed position p of
 // sample b, step j is pos_start[b] + j.  The attention splits [0, P) into
@@ -110,7 +128,8 @@ __host__ __device__ inline int64_t scan_blocks(int64_t n) { return (n + kScanChu
 // edge leaves partial softmax states that a finalize pass merges.
 //   [0, 64)        int32 header: B, max_len, R requested (0 = even split),
 //                  R used, P, nblocks, number of ranges
-//   sums           int64 pairs [nblocks]: per-block sums (clamped, raw)
+//   sums           per 1024-sample block: int64 (clamped, raw) block sums, then
+//                  64 pairs of 16-sample chunk sums (kPlanSumWords words)
 //   pos_start      int32[B+1]
 //   sample_base    int64[B]: index in seq_values of sample b's first position
 //   pos_b          int32[Pmax]: sample of packed position p
@@ -118,16 +137,20 @@ __host__ __device__ inline int64_t scan_blocks(int64_t n) { return (n + kScanChu
 //   pos_rows       int32[3][Pmax]: resolved row of the adgroup/cate/brand id
 //                  (a hash miss is -1)
 //   partials       float[max_ranges][2][52]: per range, the state of the sample
-//                  entering it (in) and of the sample leaving it (out):
-//                  max, sum, 2 pad, 48 weighted sums
-enum { kHdrB = 0, kHdrMaxLen, kHdrRReq, kHdrR, kHdrP, kHdrNBlocks, kHdrNRanges };
+//                  entering it (slot 0, head) and of the sample leaving it
+//                  (slot 1, tail): max, sum, sample and its end (tail only,
+//                  as int bits), 48 weighted sums
+//   empty          int32[B]: the samples with no positions (header: count)
+enum { kHdrB = 0, kHdrMaxLen, kHdrRReq, kHdrR, kHdrP, kHdrNBlocks, kHdrNRanges, kHdrNEmpty };
+constexpr int kPlanChunk = 16;                                  // samples per build block
+constexpr int kPlanSumWords = 2 + 2 * (kScanChunk / kPlanChunk);   // 130
 constexpr int kMinRange = 16;
 constexpr int kMaxRange = 1 << 20;
 constexpr int kPartialFloats = 52;
 
 struct PlanLayout {
     int64_t nblocks, pmax, max_ranges;
-    size_t off_sums, off_pos, off_sbase, off_pb, off_pjr, off_prows, off_part, bytes;
+    size_t off_sums, off_pos, off_sbase, off_pb, off_pjr, off_prows, off_part, off_empty, bytes;
 };
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -138,13 +161,14 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t B, int32_t max_len) {
     p.pmax = B * (int64_t)max_len;
     p.max_ranges = p.pmax / kMinRange + 1;
     p.off_sums = 64;
-    p.off_pos = align16(p.off_sums + 16 * (size_t)p.nblocks);
+    p.off_pos = align16(p.off_sums + 8 * (size_t)kPlanSumWords * (size_t)p.nblocks);
     p.off_sbase = align16(p.off_pos + 4 * (size_t)(B + 1));
     p.off_pb = align16(p.off_sbase + 8 * (size_t)B);
     p.off_pjr = align16(p.off_pb + 4 * (size_t)p.pmax);
     p.off_prows = align16(p.off_pjr + 4 * (size_t)p.pmax);
     p.off_part = align16(p.off_prows + 12 * (size_t)p.pmax);
-    p.bytes = align16(p.off_part + sizeof(float) * 2 * kPartialFloats * (size_t)p.max_ranges);
+    p.off_empty = align16(p.off_part + sizeof(float) * 2 * kPartialFloats * (size_t)p.max_ranges);
+    p.bytes = align16(p.off_empty + 4 * (size_t)B);
     return p;
 }
 
@@ -170,7 +194,6 @@ struct PlanArgs {
     int64_t B;
     int32_t max_len;
     int32_t range_positions;   // stored in the header: 0 = even split
-    int32_t num_cus;
     int64_t* seq_offsets_out;
     int64_t* rows_out;
     void* plan;
@@ -181,14 +204,18 @@ struct EmbArgs {
     TabDev tab[REC_MAX_TABLES];
     const int64_t* values;
     const int32_t* lengths;
-    const int64_t* offsets;
+    const int64_t* offsets;       // given offsets, or NULL: derived from the KJT sums
+    const int64_t* kjt_bs;        // KJT sums (kjt_layout) when offsets is NULL
+    const int64_t* kjt_cs;
+    int64_t nK;
+    int64_t* offsets_out;         // derived offsets [T*B+1], or NULL
     float* out;
     int64_t* rows_out;
     int64_t B;
     int32_t T;
-    int32_t chunks;     // ceil(T / 16): waves per sample
 };
 hipError_t launch_embbag(const EmbArgs& a, hipStream_t s);
+hipError_t launch_kjt_sums(const int32_t* lengths, int32_t T, int64_t B, void* sums, hipStream_t s);
 
 struct HashArgs {
     TabDev tab;
@@ -218,6 +245,7 @@ struct DinArgs {
     const int32_t* pos_jr;
     const int32_t* pos_rows;
     float* partials;
+    const int32_t* empty;
     int64_t pmax;
     float* out;
     float* scores;

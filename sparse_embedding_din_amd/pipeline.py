@@ -1,10 +1,12 @@
 """Device-resident tables, MLP and batches, and the whole sparse forward as
 four C-ABI calls:
 
-    rec_lengths_to_offsets  (deep KJT lengths -> offsets)
+    rec_kjt_sums            (deep KJT lengths -> block and chunk sums)
     rec_din_plan            (sequence lengths/ids -> packed positions, rows)
-    rec_embbag_fwd          (pooled [B, 256])
+    rec_embbag_fwd_kjt      (offsets and pooled [B, 256])
     rec_din_attn_fwd        (attention [B, 48], query read from the pooled output)
+
+With fused=False the deep side is rec_lengths_to_offsets + rec_embbag_fwd.
 
 torch provides device memory and the stream; every step runs in librec.
 Inputs are plain numpy arrays / dicts (as the seeded generator produces).
@@ -99,8 +101,9 @@ class SparseDinForward:
     """Buffers for batches of up to B_max samples and the four-call forward."""
 
     def __init__(self, tables: DeviceTables, mlp: DeviceMLP, B_max: int, max_len: int = 100,
-                 device="cuda", range_positions: int = 0, T: int = 16):
+                 device="cuda", range_positions: int = 0, T: int = 16, fused: bool = True):
         self.T = T
+        self.fused = fused
         self.tables = tables
         self.mlp = mlp
         self.max_len = max_len
@@ -112,6 +115,8 @@ class SparseDinForward:
         self.offsets = torch.empty(T * B_max + 1, dtype=torch.int64, device=device)
         self.ws_bytes = max(R.rec_scan_workspace_bytes(T * B_max), 8)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.kjt_bytes = R.rec_kjt_sums_bytes(T, B_max)
+        self.kjt = torch.empty(max(self.kjt_bytes, 8), dtype=torch.uint8, device=device)
         self.plan_bytes = R.rec_din_plan_bytes(B_max, max_len)
         self.plan = torch.empty(self.plan_bytes, dtype=torch.uint8, device=device)
         self.seq_offsets = torch.empty(B_max + 1, dtype=torch.int64, device=device)
@@ -120,7 +125,11 @@ class SparseDinForward:
 
     # the four steps, each one C-ABI call
     def offsets_step(self, b: DeviceBatch, stream=None):
-        R.rec_lengths_to_offsets(b.lengths, self.T * b.B, self.offsets, self.ws, self.ws_bytes, stream)
+        if self.fused:
+            R.rec_kjt_sums(b.lengths, self.T, b.B, self.kjt, self.kjt_bytes, stream)
+        else:
+            R.rec_lengths_to_offsets(b.lengths, self.T * b.B, self.offsets, self.ws, self.ws_bytes,
+                                     stream)
 
     def plan_step(self, b: DeviceBatch, rows_out=None, stream=None):
         R.rec_din_plan(self.seq_arr, b.seq_values, b.seq_stride, b.seq_offsets, b.seq_lengths,
@@ -128,8 +137,12 @@ class SparseDinForward:
                        self.plan, self.plan_bytes, stream)
 
     def embbag_step(self, b: DeviceBatch, rows_out=None, stream=None):
-        R.rec_embbag_fwd(self.tab_arr, self.T, b.B, b.values, b.lengths, self.offsets, self.pooled,
-                         rows_out, stream)
+        if self.fused:
+            R.rec_embbag_fwd_kjt(self.tab_arr, self.T, b.B, b.values, b.lengths, self.kjt,
+                                 self.kjt_bytes, self.offsets, self.pooled, rows_out, stream)
+        else:
+            R.rec_embbag_fwd(self.tab_arr, self.T, b.B, b.values, b.lengths, self.offsets,
+                             self.pooled, rows_out, stream)
 
     def din_step(self, b: DeviceBatch, scores=None, weights=None, stream=None):
         R.rec_din_attn_fwd(self.seq_arr, self.plan, self.plan_bytes, b.B, self.max_len,

@@ -26,7 +26,7 @@ REC_MAX_SEQ_LEN = 128
 REC_MAX_B = 16777215
 
 EXPORTS = ["rec_din_pack_mlp", "rec_scan_workspace_bytes", "rec_lengths_to_offsets", "rec_embbag_fwd",
-           "rec_hash_lookup", "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_fwd",
+           "rec_kjt_sums_bytes", "rec_kjt_sums", "rec_embbag_fwd_kjt", "rec_hash_lookup", "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_fwd",
            "rec_last_error", "rec_version", "rec_host_floor_mod", "rec_host_hash_home"]
 
 
@@ -62,6 +62,11 @@ def lib():
         L.rec_scan_workspace_bytes.restype = sz
         L.rec_lengths_to_offsets.argtypes = [vp, i64, vp, vp, sz, vp]
         L.rec_embbag_fwd.argtypes = [C.POINTER(rec_table), i32, i64, vp, vp, vp, vp, vp, vp]
+        L.rec_kjt_sums_bytes.argtypes = [i32, i64]
+        L.rec_kjt_sums_bytes.restype = sz
+        L.rec_kjt_sums.argtypes = [vp, i32, i64, vp, sz, vp]
+        L.rec_embbag_fwd_kjt.argtypes = [C.POINTER(rec_table), i32, i64, vp, vp, vp, sz, vp, vp, vp,
+                                         vp]
         L.rec_hash_lookup.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, vp]
         L.rec_din_plan_bytes.argtypes = [i64, i32]
         L.rec_din_plan_bytes.restype = sz
@@ -71,7 +76,8 @@ def lib():
                                        C.POINTER(C.c_int32), C.POINTER(rec_din_mlp), vp, vp, vp,
                                        vp]
         L.rec_din_pack_mlp.argtypes = [C.POINTER(rec_din_mlp), vp, sz, vp]
-        for f in ("rec_lengths_to_offsets", "rec_embbag_fwd", "rec_hash_lookup", "rec_din_plan",
+        for f in ("rec_lengths_to_offsets", "rec_embbag_fwd", "rec_kjt_sums", "rec_embbag_fwd_kjt",
+                  "rec_hash_lookup", "rec_din_plan",
                   "rec_din_attn_fwd", "rec_din_pack_mlp"):
             getattr(L, f).restype = C.c_int
         L.rec_last_error.argtypes = []
@@ -150,6 +156,22 @@ def rec_embbag_fwd(tables: Sequence[rec_table], T: int, B: int, values, lengths,
                    rows_out=None, stream=None):
     _check(lib().rec_embbag_fwd(_tables(tables), T, B, _p(values), _p(lengths), _p(offsets),
                                 _p(out), _p(rows_out), _stream(stream)), "rec_embbag_fwd")
+
+
+def rec_kjt_sums_bytes(T: int, B: int) -> int:
+    return int(lib().rec_kjt_sums_bytes(T, B))
+
+
+def rec_kjt_sums(lengths, T: int, B: int, sums, sums_bytes: int, stream=None):
+    _check(lib().rec_kjt_sums(_p(lengths), T, B, _p(sums), sums_bytes, _stream(stream)),
+           "rec_kjt_sums")
+
+
+def rec_embbag_fwd_kjt(tables: Sequence[rec_table], T: int, B: int, values, lengths, sums,
+                       sums_bytes: int, offsets_out, out, rows_out=None, stream=None):
+    _check(lib().rec_embbag_fwd_kjt(_tables(tables), T, B, _p(values), _p(lengths), _p(sums),
+                                    sums_bytes, _p(offsets_out), _p(out), _p(rows_out),
+                                    _stream(stream)), "rec_embbag_fwd_kjt")
 
 
 def rec_hash_lookup(table_: rec_table, keys, n: int, slot_out=None, rows_out=None, stream=None):

@@ -41,15 +41,15 @@ class Run:
     """One forward on the GPU with every debug output requested."""
 
     def __init__(self, model, batch, range_positions=0, layout=None, debug=True, mlp_dtype=None,
-                 packed=True):
+                 packed=True, fused=True):
         self.model, self.batch = model, batch
         B = batch.B
         say(f"cfg={model.cfg.name} B={B} P={batch.seq_stride} nnz={batch.values.size} "
-            f"layout={'padded' if layout else 'packed'} C={range_positions}")
+            f"layout={'padded' if layout else 'packed'} R={range_positions} fused={fused}")
         self.tabs = PL.DeviceTables(model.tables, DEV)
         self.mlp = PL.DeviceMLP(model, DEV, dtype=mlp_dtype, packed=packed)
         self.fwd = PL.SparseDinForward(self.tabs, self.mlp, B, model.cfg.max_len, DEV,
-                                       range_positions=range_positions)
+                                       range_positions=range_positions, fused=fused)
         if layout is None:
             self.db = PL.DeviceBatch(batch, DEV)
             stride = batch.seq_stride

@@ -111,6 +111,36 @@ def test_embbag_errors(lib):
     assert s == R.REC_OK and msg == ""
 
 
+def test_kjt_errors(lib):
+    assert R.rec_kjt_sums_bytes(16, 8192) >= 8 * 16 * 8 * 33
+    assert R.rec_kjt_sums_bytes(0, 10) == 0 and R.rec_kjt_sums_bytes(4, -1) == 0
+    sb = R.rec_kjt_sums_bytes(16, 100)
+    assert _status(lib.rec_kjt_sums, FAKE, 0, 100, FAKE, sb, None)[0] == R.REC_EINVAL
+    assert _status(lib.rec_kjt_sums, FAKE, 33, 100, FAKE, sb, None)[0] == R.REC_EUNSUPPORTED
+    assert _status(lib.rec_kjt_sums, FAKE, 16, -1, FAKE, sb, None)[0] == R.REC_EINVAL
+    assert _status(lib.rec_kjt_sums, None, 16, 100, FAKE, sb, None)[0] == R.REC_EINVAL
+    assert _status(lib.rec_kjt_sums, FAKE, 16, 100, None, sb, None)[0] == R.REC_EINVAL
+    assert _status(lib.rec_kjt_sums, FAKE, 16, 100, FAKE + 4, sb, None)[0] == R.REC_EINVAL
+    assert _status(lib.rec_kjt_sums, FAKE, 16, 100, FAKE, sb - 8, None)[0] == R.REC_EWORKSPACE
+    assert _status(lib.rec_kjt_sums, FAKE, 16, 0, FAKE, 0, None)[0] == R.REC_OK
+    tabs = R._tables([_table() for _ in range(16)])
+
+    def call(**kw):
+        a = dict(tables=tabs, T=16, B=100, values=FAKE, lengths=FAKE, sums=FAKE, sb=sb, out=FAKE)
+        a.update(kw)
+        return _status(lib.rec_embbag_fwd_kjt, a["tables"], a["T"], a["B"], a["values"],
+                       a["lengths"], a["sums"], a["sb"], None, a["out"], None, None)
+    assert call(tables=None)[0] == R.REC_EINVAL
+    assert call(T=0)[0] == R.REC_EINVAL
+    assert call(T=33)[0] == R.REC_EUNSUPPORTED
+    assert call(B=-3)[0] == R.REC_EINVAL
+    assert call(sums=None)[0] == R.REC_EINVAL
+    assert call(sums=FAKE + 4)[0] == R.REC_EINVAL
+    assert call(sb=sb - 8)[0] == R.REC_EWORKSPACE
+    assert call(out=FAKE_ODD)[0] == R.REC_EINVAL
+    assert call(B=0, sb=0)[0] == R.REC_OK
+
+
 def test_hash_lookup_errors(lib):
     h = _table(kind=R.REC_HASH, keys=FAKE, digests=FAKE)
     d = _table()

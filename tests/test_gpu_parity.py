@@ -80,7 +80,7 @@ def test_din_plan(models, B, max_len, C):
     assert hdr[2] == C
     a16 = lambda x: (x + 15) // 16 * 16
     nb = (B + 1023) // 1024
-    off_pos = a16(64 + 16 * nb)
+    off_pos = a16(64 + 8 * 130 * nb)
     pos = p[off_pos: off_pos + 4 * (B + 1)].view(np.int32)
     assert np.array_equal(pos, orc.lengths_to_offsets(clamped))
     pmax = B * max_len
@@ -111,9 +111,16 @@ def test_din_plan(models, B, max_len, C):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("cfg,B", [(1, 256), (1, 37), (2, 8192), (4, 65536), (5, 8192)])
 def test_embbag_parity(models, cfg, B):
+    """Offsets derived inside the embedding bags (from the KJT sums), pooled
+    output and resolved rows against the oracle; the two-call form (offsets
+    scan, then bags) gives bit-identical results."""
     m = models(cfg)
     b = synth.make_batch(m, B=B)
     r = Run(m, b)
+    r2 = Run(m, b, fused=False)
+    assert np.array_equal(r.offsets, r2.offsets)
+    assert np.array_equal(r.pooled, r2.pooled)
+    assert np.array_equal(r.emb_rows, r2.emb_rows)
     orc = oracle.get()
     assert np.array_equal(r.offsets, orc.lengths_to_offsets(b.lengths))
     rows, _ = oracle_rows(m, b)
@@ -144,11 +151,44 @@ def test_embbag_edges(models):
     b.lengths = L.reshape(-1).astype(np.int32)
     b.values = np.concatenate(vals)
     r = Run(m, b)
+    assert np.array_equal(r.offsets, oracle.get().lengths_to_offsets(b.lengths))
     rows, _ = oracle_rows(m, b)
     assert np.array_equal(r.emb_rows, rows)
     ref = oracle.get().embbag(m.tables, 33, b.values, b.lengths, r.offsets)
     assert np.all(r.pooled[0] == 0.0)
     assert row_rel_err(r.pooled, ref) <= 1e-6
+
+
+@pytest.mark.parametrize("T,B", [(1, 1), (5, 2500), (16, 1025), (32, 3000), (3, 4096)])
+def test_embbag_kjt_shapes(models, T, B):
+    """Offsets derived in the bags for odd table counts, batches that are not
+    a multiple of the 32-sample chunk or the 1024-sample block, and up to 32
+    tables (the tiny model's tables repeated): bit-exact offsets, pooled
+    output against the oracle."""
+    m = models(1)
+    tables = [m.tables[k % synth.T] for k in range(T)]
+    rng = np.random.default_rng(T * 7919 + B)
+    L = rng.integers(0, 6, size=T * B).astype(np.int32)
+    L[rng.random(T * B) < 0.2] = 0
+    nnz = int(L.sum())
+    vals = rng.integers(np.iinfo(np.int64).min, np.iinfo(np.int64).max, size=max(nnz, 1),
+                        dtype=np.int64)
+    say(f"kjt T={T} B={B} nnz={nnz}")
+    tabs = PL.DeviceTables(tables, DEV)
+    lt = torch.from_numpy(L).to(DEV)
+    vt = torch.from_numpy(vals).to(DEV)
+    sb = R.rec_kjt_sums_bytes(T, B)
+    sums = torch.full((sb,), 0x5A, dtype=torch.uint8, device=DEV)
+    off = torch.full((T * B + 1,), -5, dtype=torch.int64, device=DEV)
+    out = torch.full((B, T * 16), np.nan, dtype=torch.float32, device=DEV)
+    R.rec_kjt_sums(lt, T, B, sums, sb)
+    R.rec_embbag_fwd_kjt(tabs.array(), T, B, vt, lt, sums, sb, off, out)
+    torch.cuda.synchronize()
+    orc = oracle.get()
+    ref_off = orc.lengths_to_offsets(L)
+    assert np.array_equal(off.cpu().numpy(), ref_off)
+    ref = orc.embbag(tables, B, vals[:nnz], L, ref_off)
+    assert row_rel_err(out.cpu().numpy(), ref) <= 1e-6
 
 
 def test_hash_lookup(models):
@@ -339,3 +379,32 @@ def test_din_deterministic(models):
     assert np.array_equal(r1.att, r2.att)
     assert np.array_equal(r1.pooled, r2.pooled)
     assert np.array_equal(r1.scores, r2.scores)
+
+
+@pytest.mark.parametrize("R_pos", [16, 0])
+def test_din_repeat_same_plan(models, R_pos):
+    """The attention run three times over one plan (the arrival counters
+    must come back to zero after every call) with long sequences cut into up
+    to seven pieces, a block of empty sequences, and the output buffer
+    poisoned between calls: identical results every time, within tolerance
+    of the oracle."""
+    m = models(1, bias=True)
+    b = synth.make_batch(m, B=700, seq_law="unif100")
+    L = b.seq_lengths.copy()
+    starts = np.concatenate([[0], np.cumsum(L)])
+    keep = np.ones(700, bool)
+    keep[100:140] = False                      # 40 empty sequences
+    parts = [b.seq_values[:, starts[s]: starts[s + 1]] for s in range(700) if keep[s]]
+    b.seq_values = np.ascontiguousarray(np.concatenate(parts, axis=1))
+    b.seq_lengths = np.where(keep, L, 0).astype(np.int32)
+    b.seq_stride = b.seq_values.shape[1]
+    r = Run(m, b, range_positions=R_pos)
+    o = oracle_forward(m, b)
+    assert row_rel_err(r.att, o["att"]) <= FP32_TOL
+    assert np.all(r.att[100:140] == 0.0)
+    att0 = r.fwd.att[:700].clone()
+    for _ in range(2):
+        r.fwd.att.fill_(np.nan)
+        r.fwd.din_step(r.db)
+        torch.cuda.synchronize()
+        assert torch.equal(r.fwd.att[:700], att0)
