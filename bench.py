@@ -4,7 +4,8 @@ MI355X, on seeded synthetic Taobao-shaped inputs.
 
 A step is one pass of the whole path over one batch already resident in HBM:
 lengths -> offsets, sequence plan, sum-pooled embedding bags (16 tables,
-3.14M rows), padding-free DIN attention (bf16 matrix cores, fp32 accumulate).
+3.14M rows), padding-free DIN attention (bf16 matrix cores, fp32 accumulate),
+made as one rec_sparse_din_fwd call (four kernel launches).
 Four resident batches rotate (so the L2 does not keep one batch's rows); one
 HIP graph holds a step for each of them and is replayed.  Everything runs on
 one stream: inside a graph, a fork/join to a second stream costs more than
@@ -51,6 +52,8 @@ def parse():
     p.add_argument("--kernel-reps", type=int, default=100)
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-graph", action="store_true")
+    p.add_argument("--calls", action="store_true",
+                   help="run a step as the four separate calls instead of one rec_sparse_din_fwd")
     p.add_argument("--side-stream", action="store_true",
                    help="run the sequence plan on a second stream (pays off when the plan is long, "
                         "e.g. hash-table sequence ids)")
@@ -167,10 +170,16 @@ def main():
     nb = len(dbs)
     stream = torch.cuda.Stream()
     side = torch.cuda.Stream() if a.side_stream else None
+    def step(f, db):
+        if a.calls or side is not None:
+            f.run(db, side=side)
+        else:
+            f.run_whole(db)
+
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for f, db in zip(fwds, dbs):
-            f.run(db, side=side)
+            step(f, db)
     torch.cuda.synchronize()
 
     # One graph holds one step per resident batch (the launch-bound loop of
@@ -180,7 +189,7 @@ def main():
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             for f, db in zip(fwds, dbs):
-                f.run(db, side=side)
+                step(f, db)
         torch.cuda.synchronize()
         a.steps = (a.steps + nb - 1) // nb * nb
         a.warmup = (a.warmup + nb - 1) // nb * nb
@@ -191,7 +200,7 @@ def main():
                 graph.replay()
         else:
             for k in range(n):
-                fwds[k % nb].run(dbs[k % nb], side=side)
+                step(fwds[k % nb], dbs[k % nb])
 
     with torch.cuda.stream(stream):
         run_steps(a.warmup)
@@ -299,7 +308,8 @@ def main():
         "config": {"workload": f"{cfg.name}: {synth.describe(cfg)}",
                    "global_batch": B, "parallelism": "single GPU",
                    "graph_replay": graph is not None, "rotating_batches": len(dbs),
-                   "plan_on_side_stream": side is not None},
+                   "plan_on_side_stream": side is not None,
+                   "entry": "separate calls" if (a.calls or side is not None) else "rec_sparse_din_fwd"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "gpu_ms_per_step": round(gpu_ms, 5),

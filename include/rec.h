@@ -302,6 +302,50 @@ rec_status rec_din_attn_fwd(const rec_table* seq_tables, void* plan, size_t plan
                             const int32_t* query_col, const rec_din_mlp* mlp, float* out,
                             float* scores_out, float* weights_out, void* stream);
 
+/*
+ * The whole sparse forward in one call: rec_kjt_sums + rec_din_plan +
+ * rec_embbag_fwd_kjt + rec_din_attn_fwd, with the query read from the pooled
+ * output.  The deep and sequence sides share launches (four in all instead
+ * of six).  Results are bit-identical to the four calls made one by one.
+ * Every pointer is a device pointer except `tables`, `seq_tables` and `mlp`
+ * (host); arrays are as the four calls document them.
+ */
+typedef struct {
+    int32_t T;                    /* deep tables, 1..REC_MAX_TABLES */
+    int32_t max_len;              /* sequence cap, 1..REC_MAX_SEQ_LEN */
+    int64_t B;                    /* samples, 0..REC_MAX_B */
+    const rec_table* tables;      /* host [T] */
+    const int64_t* values;        /* [nnz] key-major raw ids */
+    const int32_t* lengths;       /* [T*B] */
+    const rec_table* seq_tables;  /* host [3]: adgroup, cate, brand */
+    const int64_t* seq_values;    /* [3][seq_stride] */
+    int64_t seq_stride;
+    const int64_t* seq_offsets;   /* [B], or NULL for the packed jagged layout */
+    const int32_t* seq_lengths;   /* [B] */
+    int32_t query_col[3];         /* pooled columns of the query (16 k per table k) */
+    int32_t range_positions;      /* as rec_din_plan; 0 = even split */
+    const rec_din_mlp* mlp;       /* host */
+    float* pooled;                /* [B][T*16], 16-byte aligned */
+    float* att;                   /* [B][48], 16-byte aligned */
+    int64_t* offsets_out;         /* [T*B+1] or NULL */
+    int64_t* rows_out;            /* [nnz] or NULL */
+    int64_t* seq_offsets_out;     /* [B+1] or NULL */
+    int64_t* seq_rows_out;        /* [3][seq_stride] or NULL */
+    float* scores_out;            /* [P] or NULL */
+    float* weights_out;           /* [P] or NULL (needs scores_out) */
+    void* workspace;              /* >= rec_sparse_din_fwd_workspace_bytes, 16-byte aligned */
+    size_t workspace_bytes;
+} rec_fwd_args;
+
+/* Workspace bytes of rec_sparse_din_fwd (KJT sums + plan); 0 for invalid
+ * arguments. */
+size_t rec_sparse_din_fwd_workspace_bytes(int32_t T, int64_t B, int32_t max_len);
+
+/* Errors: those of the four calls (messages name rec_sparse_din_fwd), plus
+ * REC_EINVAL (args or workspace NULL or misaligned) and REC_EWORKSPACE.
+ * B == 0 is a no-op. */
+rec_status rec_sparse_din_fwd(const rec_fwd_args* args, void* stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* rec_last_error(void);
 

@@ -64,6 +64,164 @@ int num_cus() {
     return n;
 }
 
+// Checks of rec_din_plan's arguments (messages prefixed with `fn`) and its
+// kernel arguments; *work is false when there is nothing to launch.  The
+// prep functions make no HIP call (the caller sets `waves` once every check
+// has passed).
+rec_status prep_plan(const char* fn, const rec_table* seq_tables, const int64_t* seq_values,
+                     int64_t seq_stride, const int64_t* seq_offsets, const int32_t* seq_lengths,
+                     int64_t B, int32_t max_len, int32_t range_positions, int64_t* seq_offsets_out,
+                     int64_t* rows_out, void* plan, size_t plan_bytes, PlanArgs* a, bool* work) {
+    const std::string f(fn);
+    *work = false;
+    if (B < 0) return fail(REC_EINVAL, f + ": B < 0");
+    if (B > REC_MAX_B) return fail(REC_EUNSUPPORTED, f + ": B > REC_MAX_B");
+    if (max_len < 1 || max_len > REC_MAX_SEQ_LEN)
+        return fail(REC_EINVAL, f + ": max_len outside [1, REC_MAX_SEQ_LEN]");
+    if (range_positions != 0 &&
+        (range_positions % 16 != 0 || range_positions < kMinRange || range_positions > kMaxRange))
+        return fail(REC_EINVAL, f + ": range_positions must be 0 or a multiple of 16 in [16, 2^20]");
+    if (!seq_tables) return fail(REC_EINVAL, f + ": seq_tables is NULL");
+    if (B > 0 && (!seq_lengths || !seq_values))
+        return fail(REC_EINVAL, f + ": seq_lengths and seq_values are required");
+    if (seq_stride < 0) return fail(REC_EINVAL, f + ": seq_stride < 0");
+    if (!plan) return fail(REC_EINVAL, f + ": plan is NULL");
+    if (!aligned16(plan)) return fail(REC_EINVAL, f + ": plan not 16-byte aligned");
+    if (plan_bytes < rec_din_plan_bytes(B, max_len))
+        return fail(REC_EWORKSPACE, f + ": plan smaller than rec_din_plan_bytes(B, max_len)");
+    memset(a, 0, sizeof(*a));
+    for (int t = 0; t < 3; ++t) {
+        rec_status st = prep_table(seq_tables[t], (f + ": seq table").c_str(), &a->tab[t]);
+        if (st != REC_OK) return st;
+        if (seq_tables[t].rows > 2147483647LL)
+            return fail(REC_EUNSUPPORTED, f + ": sequence tables are limited to 2^31-1 rows");
+    }
+    if (B == 0) return REC_OK;
+    a->seq_values = seq_values;
+    a->seq_stride = seq_stride;
+    a->seq_offsets = seq_offsets;
+    a->seq_lengths = seq_lengths;
+    a->B = B;
+    a->max_len = max_len;
+    a->range_positions = range_positions;
+    a->seq_offsets_out = seq_offsets_out;
+    a->rows_out = rows_out;
+    a->plan = plan;
+    *work = true;
+    return REC_OK;
+}
+
+// The same for rec_din_attn_fwd.
+rec_status prep_attn(const char* fn, const rec_table* seq_tables, void* plan, size_t plan_bytes,
+                     int64_t B, int32_t max_len, const float* query, int64_t query_ld,
+                     const int32_t* query_col, const rec_din_mlp* mlp, float* out,
+                     float* scores_out, float* weights_out, DinArgs* a, bool* work) {
+    const std::string f(fn);
+    *work = false;
+    if (B < 0) return fail(REC_EINVAL, f + ": B < 0");
+    if (B > REC_MAX_B) return fail(REC_EUNSUPPORTED, f + ": B > REC_MAX_B");
+    if (max_len < 1 || max_len > REC_MAX_SEQ_LEN)
+        return fail(REC_EINVAL, f + ": max_len outside [1, REC_MAX_SEQ_LEN]");
+    if (!seq_tables) return fail(REC_EINVAL, f + ": seq_tables is NULL");
+    if (!query || !query_col) return fail(REC_EINVAL, f + ": query and query_col are required");
+    if (!aligned16(query) || query_ld < 16 || (query_ld & 3))
+        return fail(REC_EINVAL, f + ": query rows must be 16-byte aligned (query_ld a multiple of 4)");
+    for (int t = 0; t < 3; ++t)
+        if (query_col[t] < 0 || (query_col[t] & 3) || query_col[t] + 16 > query_ld)
+            return fail(REC_EINVAL, f + ": query_col must be multiples of 4 inside query_ld");
+    if (!mlp) return fail(REC_EINVAL, f + ": mlp is NULL");
+    if (mlp->dtype != REC_F32 && mlp->dtype != REC_BF16 && mlp->dtype != REC_BF16_PACKED)
+        return fail(REC_EINVAL, f + ": unknown mlp dtype");
+    const bool packed = mlp->dtype == REC_BF16_PACKED;
+    if (!mlp->w1 || !mlp->b1 || (!packed && !mlp->w2) || !mlp->b2 || !mlp->w3)
+        return fail(REC_EINVAL, f + ": mlp arrays are required");
+    if (!aligned16(mlp->w1) || (!packed && !aligned16(mlp->w2)))
+        return fail(REC_EINVAL, f + ": w1/w2 not 16-byte aligned");
+    if (!out) return fail(REC_EINVAL, f + ": out is NULL");
+    if (!aligned16(out)) return fail(REC_EINVAL, f + ": out not 16-byte aligned");
+    if (weights_out && !scores_out)
+        return fail(REC_EINVAL, f + ": weights_out requires scores_out");
+    if (!plan) return fail(REC_EINVAL, f + ": plan is NULL");
+    if (plan_bytes < rec_din_plan_bytes(B, max_len))
+        return fail(REC_EWORKSPACE, f + ": plan smaller than rec_din_plan_bytes(B, max_len)");
+    memset(a, 0, sizeof(*a));
+    for (int t = 0; t < 3; ++t) {
+        rec_status s = prep_table(seq_tables[t], (f + ": seq table").c_str(), &a->tab[t]);
+        if (s != REC_OK) return s;
+    }
+    if (B == 0) return REC_OK;
+    const PlanLayout L = plan_layout(B, max_len);
+    char* p = (char*)plan;
+    a->query = query;
+    a->query_ld = query_ld;
+    for (int t = 0; t < 3; ++t) a->qcol[t] = query_col[t];
+    a->max_len = max_len;
+    a->w1 = mlp->w1;
+    a->b1 = mlp->b1;
+    a->w2 = mlp->w2;
+    a->b2 = mlp->b2;
+    a->w3 = mlp->w3;
+    a->b3 = mlp->b3;
+    a->dtype = mlp->dtype;
+    a->plan_hdr = (const int32_t*)p;
+    a->pos_start = (const int32_t*)(p + L.off_pos);
+    a->pos_b = (const int32_t*)(p + L.off_pb);
+    a->pos_jr = (const int32_t*)(p + L.off_pjr);
+    a->pos_rows = (const int32_t*)(p + L.off_prows);
+    a->partials = (float*)(p + L.off_part);
+    a->empty = (const int32_t*)(p + L.off_empty);
+    a->pmax = L.pmax;
+    a->out = out;
+    a->scores = scores_out;
+    a->weights = weights_out;
+    a->B = B;
+    *work = true;
+    return REC_OK;
+}
+
+// Checks of rec_embbag_fwd_kjt's arguments (messages prefixed with `fn`) and
+// its kernel arguments; *work is false when there is nothing to launch.
+rec_status prep_embbag_kjt(const char* fn, const rec_table* tables, int32_t T, int64_t B,
+                           const int64_t* values, const int32_t* lengths, const void* sums,
+                           size_t sums_bytes, int64_t* offsets_out, float* out, int64_t* rows_out,
+                           EmbArgs* a, bool* work) {
+    const std::string f(fn);
+    *work = false;
+    if (!tables) return fail(REC_EINVAL, f + ": tables is NULL");
+    if (T < 1) return fail(REC_EINVAL, f + ": T < 1");
+    if (T > REC_MAX_TABLES) return fail(REC_EUNSUPPORTED, f + ": T > REC_MAX_TABLES");
+    if (B < 0) return fail(REC_EINVAL, f + ": B < 0");
+    if (!values || !lengths || !sums || !out)
+        return fail(REC_EINVAL, f + ": values, lengths, sums and out are required");
+    if (!aligned16(out)) return fail(REC_EINVAL, f + ": out not 16-byte aligned");
+    if ((uintptr_t)sums & 7u) return fail(REC_EINVAL, f + ": sums not 8-byte aligned");
+    if (sums_bytes < rec_kjt_sums_bytes(T, B))
+        return fail(REC_EWORKSPACE, f + ": sums smaller than rec_kjt_sums_bytes(T, B)");
+    memset(a, 0, sizeof(*a));
+    for (int t = 0; t < T; ++t) {
+        rec_status s = prep_table(tables[t], (f + ": table").c_str(), &a->tab[t]);
+        if (s != REC_OK) return s;
+    }
+    const KjtLayout k = kjt_layout(T, B);
+    a->values = values;
+    a->lengths = lengths;
+    a->offsets = nullptr;
+    a->kjt_bs = (const int64_t*)sums;
+    a->kjt_segp = (const int64_t*)((const char*)sums + k.off_segp);
+    a->kjt_chp = (const int64_t*)((const char*)sums + k.off_chp);
+    a->nK = k.nK;
+    a->G = k.G;
+    a->offsets_out = offsets_out;
+    a->out = out;
+    a->rows_out = rows_out;
+    a->B = B;
+    a->T = T;
+    *work = B > 0;
+    return REC_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace
 
 extern "C" {
@@ -151,42 +309,6 @@ rec_status rec_kjt_sums(const int32_t* lengths, int32_t T, int64_t B, void* sums
     return hip_status(launch_kjt_sums(lengths, T, B, sums, (hipStream_t)stream), "rec_kjt_sums");
 }
 
-rec_status rec_embbag_fwd_kjt(const rec_table* tables, int32_t T, int64_t B,
-                              const int64_t* values, const int32_t* lengths, const void* sums,
-                              size_t sums_bytes, int64_t* offsets_out, float* out,
-                              int64_t* rows_out, void* stream) {
-    if (!tables) return fail(REC_EINVAL, "rec_embbag_fwd_kjt: tables is NULL");
-    if (T < 1) return fail(REC_EINVAL, "rec_embbag_fwd_kjt: T < 1");
-    if (T > REC_MAX_TABLES) return fail(REC_EUNSUPPORTED, "rec_embbag_fwd_kjt: T > REC_MAX_TABLES");
-    if (B < 0) return fail(REC_EINVAL, "rec_embbag_fwd_kjt: B < 0");
-    if (!values || !lengths || !sums || !out)
-        return fail(REC_EINVAL, "rec_embbag_fwd_kjt: values, lengths, sums and out are required");
-    if (!aligned16(out)) return fail(REC_EINVAL, "rec_embbag_fwd_kjt: out not 16-byte aligned");
-    if ((uintptr_t)sums & 7u) return fail(REC_EINVAL, "rec_embbag_fwd_kjt: sums not 8-byte aligned");
-    if (sums_bytes < rec_kjt_sums_bytes(T, B))
-        return fail(REC_EWORKSPACE, "rec_embbag_fwd_kjt: sums smaller than rec_kjt_sums_bytes(T, B)");
-    EmbArgs a;
-    memset(&a, 0, sizeof(a));
-    for (int t = 0; t < T; ++t) {
-        rec_status s = prep_table(tables[t], "rec_embbag_fwd_kjt: table", &a.tab[t]);
-        if (s != REC_OK) return s;
-    }
-    if (B == 0) return ok();
-    const KjtLayout k = kjt_layout(T, B);
-    a.values = values;
-    a.lengths = lengths;
-    a.offsets = nullptr;
-    a.kjt_bs = (const int64_t*)sums;
-    a.kjt_cs = (const int64_t*)((const char*)sums + k.off_cs);
-    a.nK = k.nK;
-    a.offsets_out = offsets_out;
-    a.out = out;
-    a.rows_out = rows_out;
-    a.B = B;
-    a.T = T;
-    return hip_status(launch_embbag(a, (hipStream_t)stream), "rec_embbag_fwd_kjt");
-}
-
 rec_status rec_hash_lookup(const rec_table* table, const int64_t* keys, int64_t n,
                            int64_t* slot_out, float* rows_out, void* stream) {
     if (!table) return fail(REC_EINVAL, "rec_hash_lookup: table is NULL");
@@ -229,40 +351,16 @@ rec_status rec_din_plan(const rec_table* seq_tables, const int64_t* seq_values,
                         const int32_t* seq_lengths, int64_t B, int32_t max_len,
                         int32_t range_positions, int64_t* seq_offsets_out, int64_t* rows_out,
                         void* plan, size_t plan_bytes, void* stream) {
-    if (B < 0) return fail(REC_EINVAL, "rec_din_plan: B < 0");
-    if (B > REC_MAX_B) return fail(REC_EUNSUPPORTED, "rec_din_plan: B > REC_MAX_B");
-    if (max_len < 1 || max_len > REC_MAX_SEQ_LEN)
-        return fail(REC_EINVAL, "rec_din_plan: max_len outside [1, REC_MAX_SEQ_LEN]");
-    if (range_positions != 0 &&
-        (range_positions % 16 != 0 || range_positions < kMinRange || range_positions > kMaxRange))
-        return fail(REC_EINVAL, "rec_din_plan: range_positions must be 0 or a multiple of 16 in [16, 2^20]");
-    if (!seq_tables) return fail(REC_EINVAL, "rec_din_plan: seq_tables is NULL");
-    if (B > 0 && (!seq_lengths || !seq_values))
-        return fail(REC_EINVAL, "rec_din_plan: seq_lengths and seq_values are required");
-    if (seq_stride < 0) return fail(REC_EINVAL, "rec_din_plan: seq_stride < 0");
-    if (!plan) return fail(REC_EINVAL, "rec_din_plan: plan is NULL");
-    if (!aligned16(plan)) return fail(REC_EINVAL, "rec_din_plan: plan not 16-byte aligned");
-    if (plan_bytes < rec_din_plan_bytes(B, max_len))
-        return fail(REC_EWORKSPACE, "rec_din_plan: plan smaller than rec_din_plan_bytes(B, max_len)");
     PlanArgs a;
-    memset(&a, 0, sizeof(a));
-    for (int f = 0; f < 3; ++f) {
-        rec_status st = prep_table(seq_tables[f], "rec_din_plan: seq table", &a.tab[f]);
-        if (st != REC_OK) return st;
-        if (seq_tables[f].rows > 2147483647LL)
-            return fail(REC_EUNSUPPORTED, "rec_din_plan: sequence tables are limited to 2^31-1 rows");
-    }
-    if (B == 0) return ok();
-    a.seq_values = seq_values;
-    a.seq_stride = seq_stride;
-    a.seq_offsets = seq_offsets;
-    a.seq_lengths = seq_lengths;
-    a.B = B;
-    a.max_len = max_len;
-    a.range_positions = range_positions;
-    a.seq_offsets_out = seq_offsets_out;
-    a.rows_out = rows_out;
-    a.plan = plan;
+    bool work;
+    rec_status s = prep_plan("rec_din_plan", seq_tables, seq_values, seq_stride, seq_offsets,
+                             seq_lengths, B, max_len, range_positions, seq_offsets_out, rows_out,
+                             plan, plan_bytes, &a, &work);
+    if (s != REC_OK) return s;
+    if (!work) return ok();
+    const int cus = num_cus();
+    if (cus < 1) return fail(REC_EHIP, "rec_din_plan: cannot query the device");
+    a.waves = din_waves(cus);
     return hip_status(launch_din_plan(a, (hipStream_t)stream), "rec_din_plan");
 }
 
@@ -270,68 +368,71 @@ rec_status rec_din_attn_fwd(const rec_table* seq_tables, void* plan, size_t plan
                             int64_t B, int32_t max_len, const float* query, int64_t query_ld,
                             const int32_t* query_col, const rec_din_mlp* mlp, float* out,
                             float* scores_out, float* weights_out, void* stream) {
-    if (B < 0) return fail(REC_EINVAL, "rec_din_attn_fwd: B < 0");
-    if (B > REC_MAX_B) return fail(REC_EUNSUPPORTED, "rec_din_attn_fwd: B > REC_MAX_B");
-    if (max_len < 1 || max_len > REC_MAX_SEQ_LEN)
-        return fail(REC_EINVAL, "rec_din_attn_fwd: max_len outside [1, REC_MAX_SEQ_LEN]");
-    if (!seq_tables) return fail(REC_EINVAL, "rec_din_attn_fwd: seq_tables is NULL");
-    if (!query || !query_col) return fail(REC_EINVAL, "rec_din_attn_fwd: query and query_col are required");
-    if (!aligned16(query) || query_ld < 16 || (query_ld & 3))
-        return fail(REC_EINVAL, "rec_din_attn_fwd: query rows must be 16-byte aligned (query_ld a multiple of 4)");
-    for (int f = 0; f < 3; ++f)
-        if (query_col[f] < 0 || (query_col[f] & 3) || query_col[f] + 16 > query_ld)
-            return fail(REC_EINVAL, "rec_din_attn_fwd: query_col must be multiples of 4 inside query_ld");
-    if (!mlp) return fail(REC_EINVAL, "rec_din_attn_fwd: mlp is NULL");
-    if (mlp->dtype != REC_F32 && mlp->dtype != REC_BF16 && mlp->dtype != REC_BF16_PACKED)
-        return fail(REC_EINVAL, "rec_din_attn_fwd: unknown mlp dtype");
-    const bool packed = mlp->dtype == REC_BF16_PACKED;
-    if (!mlp->w1 || !mlp->b1 || (!packed && !mlp->w2) || !mlp->b2 || !mlp->w3)
-        return fail(REC_EINVAL, "rec_din_attn_fwd: mlp arrays are required");
-    if (!aligned16(mlp->w1) || (!packed && !aligned16(mlp->w2)))
-        return fail(REC_EINVAL, "rec_din_attn_fwd: w1/w2 not 16-byte aligned");
-    if (!out) return fail(REC_EINVAL, "rec_din_attn_fwd: out is NULL");
-    if (!aligned16(out)) return fail(REC_EINVAL, "rec_din_attn_fwd: out not 16-byte aligned");
-    if (weights_out && !scores_out)
-        return fail(REC_EINVAL, "rec_din_attn_fwd: weights_out requires scores_out");
-    if (!plan) return fail(REC_EINVAL, "rec_din_attn_fwd: plan is NULL");
-    if (plan_bytes < rec_din_plan_bytes(B, max_len))
-        return fail(REC_EWORKSPACE, "rec_din_attn_fwd: plan smaller than rec_din_plan_bytes(B, max_len)");
     DinArgs a;
-    memset(&a, 0, sizeof(a));
-    for (int f = 0; f < 3; ++f) {
-        rec_status s = prep_table(seq_tables[f], "rec_din_attn_fwd: seq table", &a.tab[f]);
-        if (s != REC_OK) return s;
-    }
-    if (B == 0) return ok();
+    bool work;
+    rec_status s = prep_attn("rec_din_attn_fwd", seq_tables, plan, plan_bytes, B, max_len, query,
+                             query_ld, query_col, mlp, out, scores_out, weights_out, &a, &work);
+    if (s != REC_OK) return s;
+    if (!work) return ok();
     const int cus = num_cus();
     if (cus < 1) return fail(REC_EHIP, "rec_din_attn_fwd: cannot query the device");
-    const PlanLayout L = plan_layout(B, max_len);
-    char* p = (char*)plan;
-    a.query = query;
-    a.query_ld = query_ld;
-    for (int f = 0; f < 3; ++f) a.qcol[f] = query_col[f];
-    a.max_len = max_len;
-    a.w1 = mlp->w1;
-    a.b1 = mlp->b1;
-    a.w2 = mlp->w2;
-    a.b2 = mlp->b2;
-    a.w3 = mlp->w3;
-    a.b3 = mlp->b3;
-    a.dtype = mlp->dtype;
-    a.plan_hdr = (const int32_t*)p;
-    a.pos_start = (const int32_t*)(p + L.off_pos);
-    a.pos_b = (const int32_t*)(p + L.off_pb);
-    a.pos_jr = (const int32_t*)(p + L.off_pjr);
-    a.pos_rows = (const int32_t*)(p + L.off_prows);
-    a.partials = (float*)(p + L.off_part);
-    a.empty = (const int32_t*)(p + L.off_empty);
-    a.pmax = L.pmax;
-    a.out = out;
-    a.scores = scores_out;
-    a.weights = weights_out;
-    a.B = B;
     a.waves = din_waves(cus);
     return hip_status(launch_din(a, (hipStream_t)stream), "rec_din_attn_fwd");
+}
+
+rec_status rec_embbag_fwd_kjt(const rec_table* tables, int32_t T, int64_t B,
+                              const int64_t* values, const int32_t* lengths, const void* sums,
+                              size_t sums_bytes, int64_t* offsets_out, float* out,
+                              int64_t* rows_out, void* stream) {
+    EmbArgs a;
+    bool work;
+    rec_status s = prep_embbag_kjt("rec_embbag_fwd_kjt", tables, T, B, values, lengths, sums,
+                                   sums_bytes, offsets_out, out, rows_out, &a, &work);
+    if (s != REC_OK) return s;
+    if (!work) return ok();
+    return hip_status(launch_embbag(a, (hipStream_t)stream), "rec_embbag_fwd_kjt");
+}
+
+size_t rec_sparse_din_fwd_workspace_bytes(int32_t T, int64_t B, int32_t max_len) {
+    const size_t k = rec_kjt_sums_bytes(T, B), p = rec_din_plan_bytes(B, max_len);
+    if ((k == 0 && B > 0) || p == 0) return 0;
+    return align256(k) + p;
+}
+
+rec_status rec_sparse_din_fwd(const rec_fwd_args* x, void* stream) {
+    if (!x) return fail(REC_EINVAL, "rec_sparse_din_fwd: args is NULL");
+    const char* fn = "rec_sparse_din_fwd";
+    if (!x->workspace) return fail(REC_EINVAL, "rec_sparse_din_fwd: workspace is NULL");
+    if (!aligned16(x->workspace)) return fail(REC_EINVAL, "rec_sparse_din_fwd: workspace not 16-byte aligned");
+    const size_t need = rec_sparse_din_fwd_workspace_bytes(x->T, x->B, x->max_len);
+    if (need == 0 && (x->T < 1 || x->T > REC_MAX_TABLES || x->B < 0))
+        return fail(REC_EINVAL, "rec_sparse_din_fwd: T or B out of range");
+    if (x->workspace_bytes < need)
+        return fail(REC_EWORKSPACE, "rec_sparse_din_fwd: workspace smaller than rec_sparse_din_fwd_workspace_bytes");
+    char* ws = (char*)x->workspace;
+    const size_t kb = align256(rec_kjt_sums_bytes(x->T, x->B));
+    EmbArgs e;
+    PlanArgs p;
+    DinArgs d;
+    bool we, wp, wd;
+    rec_status s = prep_embbag_kjt(fn, x->tables, x->T, x->B, x->values, x->lengths, ws, kb,
+                                   x->offsets_out, x->pooled, x->rows_out, &e, &we);
+    if (s != REC_OK) return s;
+    s = prep_plan(fn, x->seq_tables, x->seq_values, x->seq_stride, x->seq_offsets, x->seq_lengths,
+                  x->B, x->max_len, x->range_positions, x->seq_offsets_out, x->seq_rows_out,
+                  ws + kb, x->workspace_bytes - kb, &p, &wp);
+    if (s != REC_OK) return s;
+    s = prep_attn(fn, x->seq_tables, ws + kb, x->workspace_bytes - kb, x->B, x->max_len, x->pooled,
+                  (int64_t)x->T * 16, x->query_col, x->mlp, x->att, x->scores_out, x->weights_out,
+                  &d, &wd);
+    if (s != REC_OK) return s;
+    if (!we || !wp || !wd) return ok();
+    const int cus = num_cus();
+    if (cus < 1) return fail(REC_EHIP, "rec_sparse_din_fwd: cannot query the device");
+    p.waves = d.waves = din_waves(cus);
+    hipError_t h = launch_fwd_front(p, e, (hipStream_t)stream);
+    if (h == hipSuccess) h = launch_din(d, (hipStream_t)stream);
+    return hip_status(h, fn);
 }
 
 }  // extern "C"

@@ -334,9 +334,9 @@ __device__ inline void mlp_f32(const Sub* S, const float* __restrict__ w1,
 // r.  A sample's run inside the range ends at the lane where rl == 0: a
 // sample wholly inside the range writes its output there; one cut by the
 // range's start (head, slot 0) or end (tail, slot 1) leaves its unnormalised
-// state in the plan; a tail piece also records its sample and where the
-// sample ends, which is all k_din_finalize needs to find the other pieces.
-__device__ inline void softmax_tile(const DinArgs& a, const Sub& S, float e, int lane, int r,
+// state in the plan; a tail piece also records its sample and the last range
+// the sample reaches, which is all k_din_finalize needs to find the others.
+__device__ inline void softmax_tile(const DinArgs& a, const Sub& S, float e, int lane, int r, int R,
                                     float& m_open, float& l_open, float (&acc_open)[12]) {
     const int n = lane & 15, g = lane >> 4;
     const int j = S.valid ? S.jl : 0;
@@ -375,7 +375,7 @@ __device__ inline void softmax_tile(const DinArgs& a, const Sub& S, float e, int
             float* ps = a.partials + ((int64_t)r * 2 + (is_head ? 0 : 1)) * kPartialFloats;
             if (g == 0)
                 *(float4*)ps = make_float4(mref, l, __int_as_float(S.b),
-                                           __int_as_float((int)S.pos + S.rem + 1));
+                                           __int_as_float(((int)S.pos + S.rem) / R));
             float4* o = (float4*)(ps + 4 + 12 * g);
 #pragma unroll
             for (int q = 0; q < 3; ++q) o[q] = make_float4(A[4 * q], A[4 * q + 1], A[4 * q + 2], A[4 * q + 3]);
@@ -596,8 +596,8 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) load_data(a, E[s], p0n, cntn, sbn + 16 * s + n, lane, Sn[s]);
         }
-        softmax_tile(a, S[0], e[0], lane, r, m_open, l_open, acc_open);
-        if (two) softmax_tile(a, S[1], e[1], lane, r, m_open, l_open, acc_open);
+        softmax_tile(a, S[0], e[0], lane, r, R, m_open, l_open, acc_open);
+        if (two) softmax_tile(a, S[1], e[1], lane, r, R, m_open, l_open, acc_open);
         if (rn != r) {
             m_open = -INFINITY;
             l_open = 0.f;
@@ -613,45 +613,65 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
     }
 }
 
-// One thread per range edge e (between ranges e-1 and e).  The sample cut
-// there is merged here if it starts in range e-1: then range e-1 holds its
-// tail piece (with the sample and its end) and ranges e .. (end-1)/R hold
-// head pieces.  The edge's first position and the tail piece are read
-// together, so the merge costs three dependent rounds of loads.
-__global__ __launch_bounds__(256) void k_din_finalize(const DinArgs a) {
-    const int64_t P = a.plan_hdr[kHdrP];
-    const int64_t R = din_range(P, a.plan_hdr[kHdrRReq], a.waves);
-    const int64_t nr = (P + R - 1) / R;
-    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x + 1; e < nr; e += (int64_t)gridDim.x * 256) {
-        const int64_t p = e * R;
-        const int j = a.pos_jr[p] & 0xffff;
-        const float4 t = *(const float4*)(a.partials + ((e - 1) * 2 + 1) * kPartialFloats);
-        if (j == 0 || p - j < (e - 1) * R) continue;
-        const int b = __float_as_int(t.z);
-        const int64_t pe = __float_as_int(t.w), ps = p - j;
-        const int64_t r1 = (pe - 1) / R;
-        const float* tp = a.partials + ((e - 1) * 2 + 1) * kPartialFloats;
-        float m = t.x, l = t.y;
-        float acc[48];
+// One thread per range r that may hold a tail piece (a sample that starts in
+// r and runs on into r+1 .. r1): the slot says whether it does, with the
+// sample and r1.  A thread's first slot is read together with the header's
+// count of slots the plan cleared (the slot exists whatever the count), so
+// the usual case, one slot per thread, costs two dependent rounds of loads;
+// the head pieces of r+1 .. r1 are the second.
+__device__ inline void finalize_range(const DinArgs& a, int64_t r, const float4 t) {
+    const float* tp = a.partials + (r * 2 + 1) * kPartialFloats;
+    const int b = __float_as_int(t.z);
+    const int64_t r1 = __float_as_int(t.w);
+    float m = t.x, l = t.y;
+    float acc[48];
 #pragma unroll
-        for (int f = 0; f < 48; ++f) acc[f] = tp[4 + f];
-        for (int64_t r = e; r <= r1; ++r) {
-            const float* h = a.partials + (r * 2) * kPartialFloats;
-            const float mh = h[0];
-            const float mn = fmaxf(m, mh);
-            const float sa = __expf(m - mn), sh = __expf(mh - mn);
-            l = l * sa + h[1] * sh;
+    for (int q = 0; q < 12; ++q) {
+        const float4 v = *(const float4*)(tp + 4 + 4 * q);
+        acc[4 * q] = v.x;
+        acc[4 * q + 1] = v.y;
+        acc[4 * q + 2] = v.z;
+        acc[4 * q + 3] = v.w;
+    }
+    for (int64_t h = r + 1; h <= r1; ++h) {
+        const float* hp = a.partials + (h * 2) * kPartialFloats;
+        const float2 ml = *(const float2*)hp;
+        const float mn = fmaxf(m, ml.x);
+        const float sa = __expf(m - mn), sh = __expf(ml.x - mn);
+        l = l * sa + ml.y * sh;
 #pragma unroll
-            for (int f = 0; f < 48; ++f) acc[f] = acc[f] * sa + h[4 + f] * sh;
-            m = mn;
+        for (int q = 0; q < 12; ++q) {
+            const float4 v = *(const float4*)(hp + 4 + 4 * q);
+            acc[4 * q] = acc[4 * q] * sa + v.x * sh;
+            acc[4 * q + 1] = acc[4 * q + 1] * sa + v.y * sh;
+            acc[4 * q + 2] = acc[4 * q + 2] * sa + v.z * sh;
+            acc[4 * q + 3] = acc[4 * q + 3] * sa + v.w * sh;
         }
-        const float inv = 1.f / l;
-        float4* o = (float4*)(a.out + (int64_t)b * 48);
+        m = mn;
+    }
+    const float inv = 1.f / l;
+    float4* o = (float4*)(a.out + (int64_t)b * 48);
 #pragma unroll
-        for (int q = 0; q < 12; ++q)
-            o[q] = make_float4(acc[4 * q] * inv, acc[4 * q + 1] * inv, acc[4 * q + 2] * inv, acc[4 * q + 3] * inv);
-        if (a.weights)
-            for (int64_t q = ps; q < pe; ++q) a.weights[q] = __expf(a.scores[q] - m) / l;
+    for (int q = 0; q < 12; ++q)
+        o[q] = make_float4(acc[4 * q] * inv, acc[4 * q + 1] * inv, acc[4 * q + 2] * inv, acc[4 * q + 3] * inv);
+    if (a.weights) {
+        const int64_t ps = a.pos_start[b], pe = a.pos_start[b + 1];
+        for (int64_t q = ps; q < pe; ++q) a.weights[q] = __expf(a.scores[q] - m) / l;
+    }
+}
+
+
+__global__ __launch_bounds__(256) void k_din_finalize(const DinArgs a, int64_t max_ranges) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (r >= max_ranges) return;
+    float4 t = *(const float4*)(a.partials + (r * 2 + 1) * kPartialFloats);
+    const int64_t nclear = a.plan_hdr[kHdrNClear];
+    while (r < nclear) {
+        if (__float_as_int(t.z) >= 0) finalize_range(a, r, t);
+        r += stride;
+        if (r >= nclear) break;
+        t = *(const float4*)(a.partials + (r * 2 + 1) * kPartialFloats);
     }
 }
 
@@ -669,13 +689,12 @@ hipError_t launch_din(const DinArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(k_din_attn<REC_F32>, grid, block, 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // enough threads for the edges of the even split; a grid-stride loop
-    // covers the many more edges a small requested range can make
-    const int64_t edges = a.pmax / kMinRange + 1;
-    int64_t blocks = (edges + 255) / 256;
-    const int64_t cap = (a.waves + 255) / 256 * 4;
-    if (blocks > cap) blocks = cap;
-    hipLaunchKernelGGL(k_din_finalize, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    // one thread per range of the even split; a requested small range size
+    // makes more ranges, which the threads then loop over
+    const int64_t max_ranges = a.pmax / kMinRange + 1;
+    int64_t threads = a.waves < max_ranges ? a.waves : max_ranges;
+    hipLaunchKernelGGL(k_din_finalize, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a,
+                       max_ranges);
     return hipGetLastError();
 }
 

@@ -20,109 +20,14 @@
 // the 32-sample chunk sums before its chunk, then a scan of its own 32
 // lengths per table.  Those loads are independent of the lengths, so the
 // offsets cost no extra round trip to memory.
-#include "rec_internal.h"
+#include "rec_embbag_dev.h"
 
 namespace rec {
 namespace {
 
-constexpr int kWaves = 4;            // waves per workgroup
-constexpr int kUnroll = 3;           // ids per bag resolved per round
-
 template <bool kHash, bool kFused>
 __global__ __launch_bounds__(64 * kWaves) void k_embbag_fwd(const EmbArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t w = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    const int64_t nbw = (a.B + 31) / 32;
-    const int tp = (int)(w / nbw);
-    if (2 * tp >= a.T) return;                               // wave-uniform
-    const int64_t b = (w % nbw) * 32 + (lane & 31);
-    const int t = 2 * tp + (lane >> 5);
-    const bool live = b < a.B && t < a.T;
-    const TabDev& t0 = a.tab[2 * tp];
-    const TabDev& t1 = a.tab[2 * tp + 1];                    // zeroed past T
-    // lanes of a missing odd table read table 2p's rows (masked out below)
-    const bool hi = lane >= 32 && 2 * tp + 1 < a.T;
-    const float* vals = hi ? t1.values : t0.values;
-    const int64_t rows = hi ? t1.rows : t0.rows;
-    const uint64_t magic = hi ? t1.magic : t0.magic;
-    const int32_t shift = hi ? t1.shift : t0.shift;
-    const int tc = min(t, a.T - 1);
-    const int64_t bag = (int64_t)tc * a.B + min(b, a.B - 1);
-    int32_t len = a.lengths[bag];
-    int64_t off;
-    if (kFused) {
-        const int64_t kc = w % nbw;                              // 32-sample chunk of table tc
-        const int64_t blk = kc / (kScanChunk / kKjtChunk);      // 1024-sample block
-        const int c = (int)(kc % (kScanChunk / kKjtChunk));     // chunk inside it
-        const int l = lane & 31;
-        const int64_t nflat = (int64_t)tc * a.nK + blk;
-        int64_t s = 0;
-        for (int64_t i = l; i < nflat; i += 32) s += a.kjt_bs[i];
-        if (l < c) s += a.kjt_cs[nflat * (kScanChunk / kKjtChunk) + l];
-        if (!live) len = 0;
-        int64_t inc = len;
-#pragma unroll
-        for (int d = 1; d < 32; d <<= 1) {
-            const int64_t u = __shfl_up(inc, d, 32);
-            if (l >= d) inc += u;
-        }
-#pragma unroll
-        for (int d = 16; d >= 1; d >>= 1) s += __shfl_xor(s, d, 32);
-        off = s + inc - len;
-        if (a.offsets_out) {
-            if (live) a.offsets_out[bag] = off;
-            if (live && t == a.T - 1 && b == a.B - 1) a.offsets_out[(int64_t)a.T * a.B] = off + len;
-        }
-    } else {
-        off = a.offsets[bag];
-        if (!live) len = 0;
-    }
-    float4 acc[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j0 = 0; __ballot(j0 < len) != 0; j0 += kUnroll) {
-        int64_t raw[kUnroll], row[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            raw[u] = a.values[len > 0 ? off + min(j0 + u, len - 1) : 0];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            if (kHash) {
-                const TabDev& tb = hi ? t1 : t0;
-                row[u] = tb.kind == REC_HASH ? hash_probe(tb, raw[u]) : floor_mod_magic(raw[u], rows, magic, shift);
-            } else {
-                row[u] = floor_mod_magic(raw[u], rows, magic, shift);
-            }
-        }
-        float4 v[kUnroll][4];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const float4* src = (const float4*)(vals + (row[u] >= 0 ? row[u] : 0) * 16);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[u][r] = src[r];
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const bool use = j0 + u < len && row[u] >= 0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                acc[r].x += use ? v[u][r].x : 0.f;
-                acc[r].y += use ? v[u][r].y : 0.f;
-                acc[r].z += use ? v[u][r].z : 0.f;
-                acc[r].w += use ? v[u][r].w : 0.f;
-            }
-        }
-        if (a.rows_out) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                if (j0 + u < len) a.rows_out[off + j0 + u] = row[u];
-        }
-    }
-    if (live) {
-        float4* o = (float4*)(a.out + b * (int64_t)a.T * 16 + t * 16);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = acc[r];
-    }
+    k_embbag_fwd_body<kHash, kFused>(a, blockIdx.x);
 }
 
 __global__ __launch_bounds__(64 * kWaves) void k_hash_lookup(const HashArgs a) {

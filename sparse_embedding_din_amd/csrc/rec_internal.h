@@ -104,20 +104,30 @@ constexpr int kScanChunk = kScanThreads * kScanItems;     // 1024 lengths per bl
 __host__ __device__ inline int64_t scan_blocks(int64_t n) { return (n + kScanChunk - 1) / kScanChunk; }
 
 // Sums of key-major KJT lengths [T][B] for the embedding bags to derive their
-// own offsets: per table t and 1024-sample block K, the block sum
-// bs[t*nK + K] (flat: the sum of every length before block (t, K) is the sum
-// of bs[0 .. t*nK + K)), and per 32-sample chunk kc = b / 32 of table t, the
-// chunk sum cs[(t*nK) * 32 + kc].
+// own offsets, in three levels per table t: blocks of G*1024 samples (G chosen
+// so that T * blocks <= 128), segments of 1024 samples, chunks of 32.
+//   bs[t*nK + K]             block sums (flat: everything before block (t, K)
+//                            is the sum of bs[0 .. t*nK + K))
+//   segp[(t*nK + K)*G + g]   sum of the segments of the block before g
+//   chp[((t*nK + K)*G + g)*32 + c]   sum of the chunks of the segment before c
+// so a bag wave needs at most 4 strided loads per lane plus two values.
 constexpr int kKjtChunk = 32;
+constexpr int kKjtSegChunks = kScanChunk / kKjtChunk;      // 32 chunks per segment
 struct KjtLayout {
-    int64_t nK;            // 1024-sample blocks per table
-    size_t off_cs, bytes;  // bs at 0
+    int64_t nK;            // blocks per table
+    int64_t G;             // 1024-sample segments per block
+    size_t off_segp, off_chp, bytes;   // bs at 0
 };
 __host__ __device__ inline KjtLayout kjt_layout(int32_t T, int64_t B) {
     KjtLayout k;
-    k.nK = scan_blocks(B);
-    k.off_cs = 8 * (size_t)T * (size_t)k.nK;
-    k.bytes = k.off_cs + 8 * (size_t)T * (size_t)k.nK * (kScanChunk / kKjtChunk);
+    const int64_t nseg = scan_blocks(B);                  // 1024-sample segments per table
+    k.G = ((int64_t)T * nseg + 127) / 128;
+    if (k.G < 1) k.G = 1;
+    k.nK = (nseg + k.G - 1) / k.G;
+    const size_t blocks = (size_t)T * (size_t)k.nK;
+    k.off_segp = 8 * blocks;
+    k.off_chp = k.off_segp + 8 * blocks * (size_t)k.G;
+    k.bytes = k.off_chp + 8 * blocks * (size_t)k.G * kKjtSegChunks;
     return k;
 }
 
@@ -138,10 +148,14 @@ __host__ __device__ inline KjtLayout kjt_layout(int32_t T, int64_t B) {
 //                  (a hash miss is -1)
 //   partials       float[max_ranges][2][52]: per range, the state of the sample
 //                  entering it (slot 0, head) and of the sample leaving it
-//                  (slot 1, tail): max, sum, sample and its end (tail only,
-//                  as int bits), 48 weighted sums
+//                  (slot 1, tail): max, sum, then (tail only, as int bits)
+//                  the sample and the last range it reaches, 48 weighted
+//                  sums.  The plan marks the tail slots of every range the
+//                  attention can form as empty (sample -1), their count in
+//                  the header.
 //   empty          int32[B]: the samples with no positions (header: count)
-enum { kHdrB = 0, kHdrMaxLen, kHdrRReq, kHdrR, kHdrP, kHdrNBlocks, kHdrNRanges, kHdrNEmpty };
+enum { kHdrB = 0, kHdrMaxLen, kHdrRReq, kHdrR, kHdrP, kHdrNBlocks, kHdrNRanges, kHdrNEmpty,
+       kHdrNClear };
 constexpr int kPlanChunk = 16;                                  // samples per build block
 constexpr int kPlanSumWords = 2 + 2 * (kScanChunk / kPlanChunk);   // 130
 constexpr int kMinRange = 16;
@@ -194,11 +208,20 @@ struct PlanArgs {
     int64_t B;
     int32_t max_len;
     int32_t range_positions;   // stored in the header: 0 = even split
+    int32_t waves;             // waves of the attention launch on this device
     int64_t* seq_offsets_out;
     int64_t* rows_out;
     void* plan;
 };
 hipError_t launch_din_plan(const PlanArgs& a, hipStream_t s);
+
+// Tail slots the plan clears: every range the attention can form (the even
+// split makes at most one per wave, a requested size ceil(pmax / size)).
+inline int64_t plan_nclear(const PlanArgs& a, const PlanLayout& L) {
+    const int64_t n = a.range_positions > 0 ? (L.pmax + a.range_positions - 1) / a.range_positions
+                                            : (int64_t)a.waves;
+    return n < L.max_ranges ? n : L.max_ranges;
+}
 
 struct EmbArgs {
     TabDev tab[REC_MAX_TABLES];
@@ -206,8 +229,9 @@ struct EmbArgs {
     const int32_t* lengths;
     const int64_t* offsets;       // given offsets, or NULL: derived from the KJT sums
     const int64_t* kjt_bs;        // KJT sums (kjt_layout) when offsets is NULL
-    const int64_t* kjt_cs;
-    int64_t nK;
+    const int64_t* kjt_segp;
+    const int64_t* kjt_chp;
+    int64_t nK, G;
     int64_t* offsets_out;         // derived offsets [T*B+1], or NULL
     float* out;
     int64_t* rows_out;
@@ -255,6 +279,9 @@ struct DinArgs {
 };
 constexpr int kDinWaves = 4;                 // waves per workgroup (one per SIMD)
 int din_waves(int num_cus);
+// The whole forward's first two launches: KJT and plan sums together, then the
+// plan's build pass and the embedding bags together (rec_fwd.hip).
+hipError_t launch_fwd_front(const PlanArgs& p, const EmbArgs& e, hipStream_t s);
 hipError_t launch_din(const DinArgs& a, hipStream_t s);
 hipError_t launch_din_pack(const void* w1, const void* w2, void* packed, hipStream_t s);
 

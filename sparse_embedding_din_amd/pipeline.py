@@ -7,6 +7,8 @@ four C-ABI calls:
     rec_din_attn_fwd        (attention [B, 48], query read from the pooled output)
 
 With fused=False the deep side is rec_lengths_to_offsets + rec_embbag_fwd.
+run_whole() makes the same forward one rec_sparse_din_fwd call (four
+launches instead of six, bit-identical results).
 
 torch provides device memory and the stream; every step runs in librec.
 Inputs are plain numpy arrays / dicts (as the seeded generator produces).
@@ -121,6 +123,8 @@ class SparseDinForward:
         self.plan = torch.empty(self.plan_bytes, dtype=torch.uint8, device=device)
         self.seq_offsets = torch.empty(B_max + 1, dtype=torch.int64, device=device)
         self.pooled = torch.empty(B_max, T * 16, dtype=torch.float32, device=device)
+        self.fwd_ws_bytes = R.rec_sparse_din_fwd_workspace_bytes(T, B_max, max_len)
+        self.fwd_ws = torch.empty(max(self.fwd_ws_bytes, 16), dtype=torch.uint8, device=device)
         self.att = torch.empty(B_max, 48, dtype=torch.float32, device=device)
 
     # the four steps, each one C-ABI call
@@ -148,6 +152,23 @@ class SparseDinForward:
         R.rec_din_attn_fwd(self.seq_arr, self.plan, self.plan_bytes, b.B, self.max_len,
                            self.pooled, self.T * 16, self.query_col, self.mlp.desc, self.att,
                            scores, weights, stream)
+
+    def whole_args(self, b: DeviceBatch, debug: Optional[dict] = None) -> R.rec_fwd_args:
+        """The rec_fwd_args of a batch."""
+        d = debug or {}
+        return R.fwd_args(self.T, b.B, self.max_len, self.tab_arr, b.values, b.lengths,
+                          self.seq_arr, b.seq_values, b.seq_stride, b.seq_offsets,
+                          b.seq_lengths, [16 * k for k in SEQ_KEYS], self.range_positions,
+                          self.mlp.desc, self.pooled, self.att, self.fwd_ws, self.fwd_ws_bytes,
+                          offsets_out=self.offsets, rows_out=d.get("emb_rows"),
+                          seq_offsets_out=self.seq_offsets, seq_rows_out=d.get("seq_rows"),
+                          scores_out=d.get("scores"), weights_out=d.get("weights"))
+
+    def run_whole(self, b: DeviceBatch, stream=None, debug: Optional[dict] = None):
+        """The forward as one rec_sparse_din_fwd call."""
+        assert b.B <= self.B_max
+        R.rec_sparse_din_fwd(self.whole_args(b, debug), stream)
+        return self.pooled[: b.B], self.att[: b.B]
 
     def run(self, b: DeviceBatch, stream=None, debug: Optional[dict] = None, side=None):
         """The forward on torch's current stream.  With `side` (another

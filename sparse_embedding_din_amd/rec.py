@@ -26,7 +26,9 @@ REC_MAX_SEQ_LEN = 128
 REC_MAX_B = 16777215
 
 EXPORTS = ["rec_din_pack_mlp", "rec_scan_workspace_bytes", "rec_lengths_to_offsets", "rec_embbag_fwd",
-           "rec_kjt_sums_bytes", "rec_kjt_sums", "rec_embbag_fwd_kjt", "rec_hash_lookup", "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_fwd",
+           "rec_kjt_sums_bytes", "rec_kjt_sums", "rec_embbag_fwd_kjt", "rec_hash_lookup",
+           "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_fwd",
+           "rec_sparse_din_fwd_workspace_bytes", "rec_sparse_din_fwd",
            "rec_last_error", "rec_version", "rec_host_floor_mod", "rec_host_hash_home"]
 
 
@@ -46,6 +48,19 @@ class rec_din_mlp(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("reserved", C.c_int32), ("w1", C.c_void_p),
                 ("b1", C.c_void_p), ("w2", C.c_void_p), ("b2", C.c_void_p),
                 ("w3", C.c_void_p), ("b3", C.c_float)]
+
+
+class rec_fwd_args(C.Structure):
+    _fields_ = [("T", C.c_int32), ("max_len", C.c_int32), ("B", C.c_int64),
+                ("tables", C.POINTER(rec_table)), ("values", C.c_void_p), ("lengths", C.c_void_p),
+                ("seq_tables", C.POINTER(rec_table)), ("seq_values", C.c_void_p),
+                ("seq_stride", C.c_int64), ("seq_offsets", C.c_void_p), ("seq_lengths", C.c_void_p),
+                ("query_col", C.c_int32 * 3), ("range_positions", C.c_int32),
+                ("mlp", C.POINTER(rec_din_mlp)), ("pooled", C.c_void_p), ("att", C.c_void_p),
+                ("offsets_out", C.c_void_p), ("rows_out", C.c_void_p),
+                ("seq_offsets_out", C.c_void_p), ("seq_rows_out", C.c_void_p),
+                ("scores_out", C.c_void_p), ("weights_out", C.c_void_p),
+                ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t)]
 
 
 _LIB = None
@@ -76,9 +91,12 @@ def lib():
                                        C.POINTER(C.c_int32), C.POINTER(rec_din_mlp), vp, vp, vp,
                                        vp]
         L.rec_din_pack_mlp.argtypes = [C.POINTER(rec_din_mlp), vp, sz, vp]
+        L.rec_sparse_din_fwd_workspace_bytes.argtypes = [i32, i64, i32]
+        L.rec_sparse_din_fwd_workspace_bytes.restype = sz
+        L.rec_sparse_din_fwd.argtypes = [C.POINTER(rec_fwd_args), vp]
         for f in ("rec_lengths_to_offsets", "rec_embbag_fwd", "rec_kjt_sums", "rec_embbag_fwd_kjt",
                   "rec_hash_lookup", "rec_din_plan",
-                  "rec_din_attn_fwd", "rec_din_pack_mlp"):
+                  "rec_din_attn_fwd", "rec_din_pack_mlp", "rec_sparse_din_fwd"):
             getattr(L, f).restype = C.c_int
         L.rec_last_error.argtypes = []
         L.rec_last_error.restype = C.c_char_p
@@ -206,6 +224,39 @@ def rec_din_attn_fwd(seq_tables: Sequence[rec_table], plan, plan_bytes: int, B: 
                                   C.byref(mlp) if mlp is not None else None, _p(out),
                                   _p(scores_out), _p(weights_out), _stream(stream)),
            "rec_din_attn_fwd")
+
+
+def rec_sparse_din_fwd_workspace_bytes(T: int, B: int, max_len: int) -> int:
+    return int(lib().rec_sparse_din_fwd_workspace_bytes(T, B, max_len))
+
+
+def fwd_args(T: int, B: int, max_len: int, tables, values, lengths, seq_tables, seq_values,
+             seq_stride: int, seq_offsets, seq_lengths, query_col: Sequence[int],
+             range_positions: int, mlp: rec_din_mlp, pooled, att, workspace, workspace_bytes: int,
+             offsets_out=None, rows_out=None, seq_offsets_out=None, seq_rows_out=None,
+             scores_out=None, weights_out=None) -> rec_fwd_args:
+    """A host rec_fwd_args; `tables`/`seq_tables`/`mlp` must stay alive with it."""
+    a = rec_fwd_args()
+    a.T, a.max_len, a.B = T, max_len, B
+    a.tables = C.cast(_tables(tables), C.POINTER(rec_table))
+    a.seq_tables = C.cast(_tables(seq_tables), C.POINTER(rec_table))
+    a.values, a.lengths = _p(values), _p(lengths)
+    a.seq_values, a.seq_stride = _p(seq_values), seq_stride
+    a.seq_offsets, a.seq_lengths = _p(seq_offsets), _p(seq_lengths)
+    a.query_col = (C.c_int32 * 3)(*query_col)
+    a.range_positions = range_positions
+    a.mlp = C.pointer(mlp)
+    a.pooled, a.att = _p(pooled), _p(att)
+    a.offsets_out, a.rows_out = _p(offsets_out), _p(rows_out)
+    a.seq_offsets_out, a.seq_rows_out = _p(seq_offsets_out), _p(seq_rows_out)
+    a.scores_out, a.weights_out = _p(scores_out), _p(weights_out)
+    a.workspace, a.workspace_bytes = _p(workspace), workspace_bytes
+    return a
+
+
+def rec_sparse_din_fwd(args: Optional[rec_fwd_args], stream=None):
+    _check(lib().rec_sparse_din_fwd(C.byref(args) if args is not None else None, _stream(stream)),
+           "rec_sparse_din_fwd")
 
 
 def rec_host_floor_mod(x: int, n: int) -> int:

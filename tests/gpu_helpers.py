@@ -41,11 +41,11 @@ class Run:
     """One forward on the GPU with every debug output requested."""
 
     def __init__(self, model, batch, range_positions=0, layout=None, debug=True, mlp_dtype=None,
-                 packed=True, fused=True):
+                 packed=True, fused=True, whole=False):
         self.model, self.batch = model, batch
         B = batch.B
         say(f"cfg={model.cfg.name} B={B} P={batch.seq_stride} nnz={batch.values.size} "
-            f"layout={'padded' if layout else 'packed'} R={range_positions} fused={fused}")
+            f"layout={'padded' if layout else 'packed'} R={range_positions} fused={fused} whole={whole}")
         self.tabs = PL.DeviceTables(model.tables, DEV)
         self.mlp = PL.DeviceMLP(model, DEV, dtype=mlp_dtype, packed=packed)
         self.fwd = PL.SparseDinForward(self.tabs, self.mlp, B, model.cfg.max_len, DEV,
@@ -65,7 +65,10 @@ class Run:
                        weights=torch.full((max(npos, 1),), np.nan, dtype=torch.float32, device=DEV),
                        seq_rows=torch.full((3 * max(stride, 1),), -7, dtype=torch.int64, device=DEV))
         self.dbg = dbg
-        self.fwd.run(self.db, debug=dbg)
+        if whole:
+            self.fwd.run_whole(self.db, debug=dbg)
+        else:
+            self.fwd.run(self.db, debug=dbg)
         torch.cuda.synchronize()
         self.offsets = self.fwd.offsets[: synth.T * B + 1].cpu().numpy()
         self.seq_offsets = self.fwd.seq_offsets[: B + 1].cpu().numpy()

@@ -235,6 +235,39 @@ def test_din_attn_errors(lib):
     assert call(B=0, pb=R.rec_din_plan_bytes(0, ml))[0] == R.REC_OK
 
 
+def test_whole_forward_errors(lib):
+    tabs = R._tables([_table() for _ in range(16)])
+    seq = R._tables([_table() for _ in range(3)])
+    B, ml = 64, 100
+    wb = R.rec_sparse_din_fwd_workspace_bytes(16, B, ml)
+    assert wb >= R.rec_kjt_sums_bytes(16, B) + R.rec_din_plan_bytes(B, ml)
+    assert R.rec_sparse_din_fwd_workspace_bytes(0, B, ml) == 0
+    assert R.rec_sparse_din_fwd_workspace_bytes(16, B, 0) == 0
+    mlp = R.din_mlp(R.REC_BF16_PACKED, FAKE, FAKE, None, FAKE, FAKE, 0.0)
+
+    def args(**kw):
+        a = dict(T=16, B=B, max_len=ml, tables=tabs, values=FAKE, lengths=FAKE, seq_tables=seq,
+                 seq_values=FAKE, seq_stride=B * 4, seq_offsets=None, seq_lengths=FAKE,
+                 query_col=(16, 80, 48), range_positions=0, mlp=mlp, pooled=FAKE, att=FAKE,
+                 workspace=FAKE, workspace_bytes=wb)
+        a.update(kw)
+        return R.fwd_args(**a)
+    assert lib.rec_sparse_din_fwd(None, None) == R.REC_EINVAL
+    assert lib.rec_sparse_din_fwd(C.byref(args(workspace=None)), None) == R.REC_EINVAL
+    assert lib.rec_sparse_din_fwd(C.byref(args(workspace=FAKE_ODD)), None) == R.REC_EINVAL
+    assert lib.rec_sparse_din_fwd(C.byref(args(workspace_bytes=wb - 16)), None) == R.REC_EWORKSPACE
+    assert lib.rec_sparse_din_fwd(C.byref(args(T=0)), None) == R.REC_EINVAL
+    assert lib.rec_sparse_din_fwd(C.byref(args(pooled=FAKE_ODD)), None) == R.REC_EINVAL
+    assert lib.rec_sparse_din_fwd(C.byref(args(range_positions=8)), None) == R.REC_EINVAL
+    assert lib.rec_sparse_din_fwd(C.byref(args(query_col=(16, 80, 250))), None) == R.REC_EINVAL
+    s, msg = _status(lib.rec_sparse_din_fwd, C.byref(args(weights_out=FAKE)), None)
+    assert s == R.REC_EINVAL and "rec_sparse_din_fwd" in msg and "scores_out" in msg
+    bad = R._tables([_table(), _table(dim=3), _table()])
+    assert lib.rec_sparse_din_fwd(C.byref(args(seq_tables=bad)), None) == R.REC_EINVAL
+    zb = R.rec_sparse_din_fwd_workspace_bytes(16, 0, ml)
+    assert lib.rec_sparse_din_fwd(C.byref(args(B=0, workspace_bytes=zb)), None) == R.REC_OK
+
+
 def test_binding_raises_with_message(lib):
     with pytest.raises(R.RecError) as ei:
         R.rec_hash_lookup(_table(), FAKE, 4, FAKE)

@@ -408,3 +408,23 @@ def test_din_repeat_same_plan(models, R_pos):
         r.fwd.din_step(r.db)
         torch.cuda.synchronize()
         assert torch.equal(r.fwd.att[:700], att0)
+
+
+@pytest.mark.parametrize("cfg,B,R_pos", [(1, 256, 0), (1, 37, 16), (2, 8192, 0), (3, 2000, 0),
+                                         (4, 65536, 0), (5, 8192, 0), (5, 300, 16)])
+def test_whole_forward_equals_calls(models, cfg, B, R_pos):
+    """rec_sparse_din_fwd (four launches) against the calls one by one:
+    bit-identical offsets, rows, pooled output, attention, scores and
+    weights; and the oracle on the pooled output and attention."""
+    m = models(cfg, bias=True)
+    b = synth.make_batch(m, B=B)
+    r1 = Run(m, b, range_positions=R_pos)
+    r2 = Run(m, b, range_positions=R_pos, whole=True)
+    for name in ("offsets", "seq_offsets", "pooled", "att", "emb_rows", "scores", "weights",
+                 "seq_rows"):
+        x, y = getattr(r1, name), getattr(r2, name)
+        assert np.array_equal(x, y, equal_nan=True), name
+    idx = np.arange(B) if B <= 8192 else np.sort(np.random.default_rng(0).choice(B, 512, replace=False))
+    o = oracle_forward(m, b, samples=None if B <= 8192 else idx)
+    assert row_rel_err(r2.pooled[idx], o["pooled"]) <= 1e-6
+    assert row_rel_err(r2.att[idx], o["att"]) <= _tol(m)
