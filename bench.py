@@ -76,7 +76,8 @@ def src_hash() -> str:
 
 CAL_BYTES = 64 << 20            # bytes read (and written) by the calibration copy
 KERNELS = {"k_din_attn": "k_din_attn", "k_din_finalize": "k_din_finalize",
-           "k_embbag_fwd": "k_embbag_fwd", "copy": "MulFunctor"}
+           "k_embbag_fwd": "k_embbag_fwd<", "k_fwd_gather": "k_fwd_gather", "k_fwd_sums": "k_fwd_sums",
+           "copy": "MulFunctor"}
 
 
 def load_traffic(kernels, shash: str, config: str):
