@@ -3,7 +3,9 @@
     python -m sparse_embedding_din_amd.build
 
 Every HIP source is compiled with -packed-fp32-ops disabled (no packed fp32
-instructions are generated)."""
+instructions are generated) and with matrix-core results kept in ordinary
+VGPRs where they fit (-amdgpu-mfma-vgpr-form): the attention's epilogues read
+every accumulator, and reading them from AGPRs costs a copy per value."""
 from __future__ import annotations
 
 import glob
@@ -30,6 +32,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-mllvm", "-amdgpu-mfma-vgpr-form",
            "-Wall", "-I", os.path.join(ROOT, "include"), "-o", tmp] + srcs
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -44,7 +44,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct Sub {
-    float q[12];
+    float q[12];     // as loaded until masked (mask_sub)
     float s[12];
     int64_t pos;     // packed position
     int32_t b;
@@ -52,6 +52,7 @@ struct Sub {
     int32_t rem;     // steps left in the sample
     int32_t jl;      // steps of the sample before this one inside the range
     int32_t rl;      // steps of the sample after this one inside the range
+    uint32_t keep;   // bit r: the 4 floats r of s are a real row (valid and not a miss)
     bool valid;
 };
 
@@ -102,20 +103,56 @@ struct Ent {
     int32_t b, jr, ra, rb;
 };
 
-__device__ inline void load_entries(const DinArgs& a, int base, int cnt, int idx, int lane, Ent& E) {
-    const int g = lane >> 4;
-    const int64_t p = base + min(idx, cnt - 1);
-    const int fa = (3 * g) >> 2, fb = (3 * g + 2) >> 2;
-    E.b = a.pos_b[p];
-    E.jr = a.pos_jr[p];
-    E.ra = a.pos_rows[fa * a.pmax + p];
-    E.rb = a.pos_rows[fb * a.pmax + p];
+// A lane's 12 features span two of the three sub-features (fa, fb); their
+// table and query-column are selected once per wave from values pinned to
+// scalar registers (readfirstlane), so the compiler cannot turn the per-lane
+// choice into a load from the kernel arguments inside the loop.
+struct LaneSrc {
+    const float* va;
+    const float* vb;
+    int32_t qa, qb, fa, fb;
+};
+
+typedef const float __attribute__((address_space(1))) gfloat;
+
+__device__ inline const float* uniform_ptr(const float* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    // back to a global-memory pointer, so its loads stay global (not flat)
+    return (const float*)(gfloat*)(((uint64_t)hi << 32) | lo);
 }
 
-__device__ inline void load_data(const DinArgs& a, const Ent& E, int base, int cnt, int idx,
-                                 int lane, Sub& S) {
+__device__ inline LaneSrc lane_src(const DinArgs& a, int lane) {
     const int g = lane >> 4;
-    const int fa = (3 * g) >> 2;
+    LaneSrc L;
+    L.fa = (3 * g) >> 2;
+    L.fb = (3 * g + 2) >> 2;
+    const float* t0 = uniform_ptr(a.tab[0].values);
+    const float* t1 = uniform_ptr(a.tab[1].values);
+    const float* t2 = uniform_ptr(a.tab[2].values);
+    const int q0 = __builtin_amdgcn_readfirstlane(a.qcol[0]);
+    const int q1 = __builtin_amdgcn_readfirstlane(a.qcol[1]);
+    const int q2 = __builtin_amdgcn_readfirstlane(a.qcol[2]);
+    L.va = L.fa == 0 ? t0 : (L.fa == 1 ? t1 : t2);
+    L.vb = L.fb == 0 ? t0 : (L.fb == 1 ? t1 : t2);
+    L.qa = L.fa == 0 ? q0 : (L.fa == 1 ? q1 : q2);
+    L.qb = L.fb == 0 ? q0 : (L.fb == 1 ? q1 : q2);
+    return L;
+}
+
+__device__ inline void load_entries(const DinArgs& a, const LaneSrc& L, int base, int cnt, int idx,
+                                    Ent& E) {
+    const int64_t p = base + min(idx, cnt - 1);
+    E.b = a.pos_b[p];
+    E.jr = a.pos_jr[p];
+    E.ra = a.pos_rows[L.fa * a.pmax + p];
+    E.rb = a.pos_rows[L.fb * a.pmax + p];
+}
+
+__device__ inline void load_data(const DinArgs& a, const LaneSrc& L, const Ent& E, int base, int cnt,
+                                 int idx, int lane, Sub& S) {
+    const int g = lane >> 4;
     const int ic = min(idx, cnt - 1);
     S.valid = idx < cnt;
     S.pos = base + ic;
@@ -125,29 +162,41 @@ __device__ inline void load_data(const DinArgs& a, const Ent& E, int base, int c
     S.jl = min(S.j, ic);
     S.rl = min(S.rem, cnt - 1 - ic);
     const float* qrow = a.query + (int64_t)E.b * a.query_ld;
-    float4 sv[3], qv[3];
-    bool keep[3];
+    S.keep = 0;
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
         const int c4 = 3 * g + r;
-        const int ff = c4 >> 2, w = c4 & 3;
-        const int32_t rr = (ff == fa) ? E.ra : E.rb;
-        const float* vb = ff == 0 ? a.tab[0].values : (ff == 1 ? a.tab[1].values : a.tab[2].values);
-        const int qc = ff == 0 ? a.qcol[0] : (ff == 1 ? a.qcol[1] : a.qcol[2]);
-        keep[r] = S.valid && rr >= 0;
-        sv[r] = *(const float4*)(vb + (int64_t)(rr >= 0 ? rr : 0) * 16 + 4 * w);
-        qv[r] = *(const float4*)(qrow + qc + 4 * w);
+        const int w = c4 & 3;
+        const bool first = (c4 >> 2) == L.fa;
+        const int32_t rr = first ? E.ra : E.rb;
+        gfloat* vb = (gfloat*)(first ? L.va : L.vb);
+        const int qc = first ? L.qa : L.qb;
+        S.keep |= (S.valid && rr >= 0) ? 1u << r : 0u;
+        const f32x4 sv = *(const __attribute__((address_space(1))) f32x4*)(vb + (int64_t)(rr >= 0 ? rr : 0) * 16 + 4 * w);
+        const float4 qv = *(const float4*)(qrow + qc + 4 * w);
+        S.s[4 * r + 0] = sv[0];
+        S.s[4 * r + 1] = sv[1];
+        S.s[4 * r + 2] = sv[2];
+        S.s[4 * r + 3] = sv[3];
+        S.q[4 * r + 0] = qv.x;
+        S.q[4 * r + 1] = qv.y;
+        S.q[4 * r + 2] = qv.z;
+        S.q[4 * r + 3] = qv.w;
     }
+}
+
+// Zero what load_data fetched for a lane past the range (q and s) or a hash
+// miss (s).  Done just before the values are first used, not when the loads
+// are issued, so the wait for them falls after the previous round's work.
+__device__ inline void mask_sub(Sub& S) {
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
-        S.s[4 * r + 0] = keep[r] ? sv[r].x : 0.f;
-        S.s[4 * r + 1] = keep[r] ? sv[r].y : 0.f;
-        S.s[4 * r + 2] = keep[r] ? sv[r].z : 0.f;
-        S.s[4 * r + 3] = keep[r] ? sv[r].w : 0.f;
-        S.q[4 * r + 0] = S.valid ? qv[r].x : 0.f;
-        S.q[4 * r + 1] = S.valid ? qv[r].y : 0.f;
-        S.q[4 * r + 2] = S.valid ? qv[r].z : 0.f;
-        S.q[4 * r + 3] = S.valid ? qv[r].w : 0.f;
+        const bool k = (S.keep >> r) & 1u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            S.s[4 * r + i] = k ? S.s[4 * r + i] : 0.f;
+            S.q[4 * r + i] = S.valid ? S.q[4 * r + i] : 0.f;
+        }
     }
 }
 
@@ -158,15 +207,16 @@ __device__ inline float x_in(const Sub& S, int i) {
     return tau == 0 ? S.q[f] : (tau == 1 ? S.s[f] : (tau == 2 ? S.q[f] - S.s[f] : S.q[f] * S.s[f]));
 }
 
-__device__ inline float score_from_h2(const f32x4 (&acc2)[4], const float* b2s, const float* w3s,
-                                      float b3, int g) {
+// e = w3 . relu(h2) + b3 for a lane's 16 units of h2 (bias already in),
+// summed over the four lane groups.
+__device__ inline float score_from_h2(const f32x4 (&acc2)[4], const float* w3s, float b3, int g) {
     float p = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int u = mt * 16 + 4 * g + i;
-            p += fmaxf(acc2[mt][i] + b2s[u], 0.f) * w3s[u];
+            p += fmaxf(acc2[mt][i], 0.f) * w3s[u];
         }
     }
     p += __shfl_xor(p, 16, 64);
@@ -191,14 +241,15 @@ __device__ inline uint32_t relu_pk_bf16(float a, float b) {
 
 // Layer 1 for one hidden block: two 16-row tiles x NSUB position tiles, the
 // K loop (6 steps of 32) innermost in issue order so 2*NSUB independent
-// accumulations are in flight.
+// accumulations are in flight.  The accumulators start from the block's bias
+// (the first product's C operand), so no separate bias add is needed.
 template <int NSUB>
-__device__ inline void l1_block(const bf16x8 (&xf)[NSUB][6], const uint4 (&w1)[12],
-                                f32x4 (&acc1)[NSUB][2]) {
+__device__ inline void l1_block(const bf16x8 (&xf)[NSUB][6], const uint4 (&w1)[12], const f32x4 bA,
+                                const f32x4 bB, f32x4 (&acc1)[NSUB][2]) {
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
-        acc1[s][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc1[s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc1[s][0] = bA;
+        acc1[s][1] = bB;
     }
 #pragma unroll
     for (int kb = 0; kb < 6; ++kb)
@@ -211,11 +262,12 @@ __device__ inline void l1_block(const bf16x8 (&xf)[NSUB][6], const uint4 (&w1)[1
 }
 
 // The bf16 MLP for NSUB position tiles, software-pipelined over the eight
-// hidden blocks: while block hb's layer-1 results go through bias, ReLU and
-// bf16 into its layer-2 products, block hb+1's layer-1 products are already
+// hidden blocks: while block hb's layer-1 results go through ReLU and bf16
+// into its layer-2 products, block hb+1's layer-1 products are already
 // issued.  W1 fragments are read from LDS one block ahead of use; a
 // scheduling fence per block keeps the compiler from hoisting every block's
-// reads (which would not fit in registers).
+// reads (which would not fit in registers).  Layer-2 accumulators start from
+// b2 the same way.
 template <int NSUB>
 __device__ inline void mlp_bf16(const Sub* S, const uint4* w1p, const uint4* w2p, const float* b1s,
                                 const float* b2s, const float* w3s, float b3, int lane,
@@ -228,14 +280,16 @@ __device__ inline void mlp_bf16(const Sub* S, const uint4* w1p, const uint4* w2p
         for (int i = 0; i < 48; ++i) xf[s][i >> 3][i & 7] = (__bf16)x_in(S[s], i);
     f32x4 acc2[NSUB][4];
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s)
+    for (int mt = 0; mt < 4; ++mt) {
+        const f32x4 b2v = *(const f32x4*)(b2s + mt * 16 + 4 * g);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc2[s][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < NSUB; ++s) acc2[s][mt] = b2v;
+    }
     uint4 fw1[2][12], fw2[4];
     f32x4 acc1[2][NSUB][2];
 #pragma unroll
     for (int i = 0; i < 12; ++i) fw1[0][i] = w1p[i * 64 + lane];
-    l1_block<NSUB>(xf, fw1[0], acc1[0]);
+    l1_block<NSUB>(xf, fw1[0], *(const f32x4*)(b1s + 4 * g), *(const f32x4*)(b1s + 16 + 4 * g), acc1[0]);
 #pragma unroll
     for (int i = 0; i < 12; ++i) fw1[1][i] = w1p[(12 + i) * 64 + lane];
 #pragma unroll
@@ -244,20 +298,20 @@ __device__ inline void mlp_bf16(const Sub* S, const uint4* w1p, const uint4* w2p
         const int cur = hb & 1, nxt = cur ^ 1;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) fw2[mt] = w2p[(hb * 4 + mt) * 64 + lane];
-        if (hb + 1 < 8) l1_block<NSUB>(xf, fw1[nxt], acc1[nxt]);
+        if (hb + 1 < 8)
+            l1_block<NSUB>(xf, fw1[nxt], *(const f32x4*)(b1s + (hb + 1) * 32 + 4 * g),
+                           *(const f32x4*)(b1s + (hb + 1) * 32 + 16 + 4 * g), acc1[nxt]);
         if (hb + 2 < 8) {
 #pragma unroll
             for (int i = 0; i < 12; ++i) fw1[cur][i] = w1p[((hb + 2) * 12 + i) * 64 + lane];
         }
-        const float4 bA = *(const float4*)(b1s + hb * 32 + 4 * g);
-        const float4 bB = *(const float4*)(b1s + hb * 32 + 16 + 4 * g);
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
             uint4 hp;
-            hp.x = relu_pk_bf16(acc1[cur][s][0][0] + bA.x, acc1[cur][s][0][1] + bA.y);
-            hp.y = relu_pk_bf16(acc1[cur][s][0][2] + bA.z, acc1[cur][s][0][3] + bA.w);
-            hp.z = relu_pk_bf16(acc1[cur][s][1][0] + bB.x, acc1[cur][s][1][1] + bB.y);
-            hp.w = relu_pk_bf16(acc1[cur][s][1][2] + bB.z, acc1[cur][s][1][3] + bB.w);
+            hp.x = relu_pk_bf16(acc1[cur][s][0][0], acc1[cur][s][0][1]);
+            hp.y = relu_pk_bf16(acc1[cur][s][0][2], acc1[cur][s][0][3]);
+            hp.z = relu_pk_bf16(acc1[cur][s][1][0], acc1[cur][s][1][1]);
+            hp.w = relu_pk_bf16(acc1[cur][s][1][2], acc1[cur][s][1][3]);
             const bf16x8 h = __builtin_bit_cast(bf16x8, hp);
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
@@ -267,7 +321,7 @@ __device__ inline void mlp_bf16(const Sub* S, const uint4* w1p, const uint4* w2p
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) e[s] = score_from_h2(acc2[s], b2s, w3s, b3, g);
+    for (int s = 0; s < NSUB; ++s) e[s] = score_from_h2(acc2[s], w3s, b3, g);
 }
 
 template <int NSUB>
@@ -284,7 +338,7 @@ __device__ inline void mlp_f32(const Sub* S, const float* __restrict__ w1,
 #pragma unroll
     for (int s = 0; s < NSUB; ++s)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc2[s][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < 4; ++mt) acc2[s][mt] = *(const f32x4*)(b2s + mt * 16 + 4 * (lane >> 4));
     for (int hb = 0; hb < 8; ++hb) {
         f32x4 acc1[NSUB][2];
 #pragma unroll
@@ -327,7 +381,7 @@ __device__ inline void mlp_f32(const Sub* S, const float* __restrict__ w1,
         }
     }
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s) e[s] = score_from_h2(acc2[s], b2s, w3s, b3, g);
+    for (int s = 0; s < NSUB; ++s) e[s] = score_from_h2(acc2[s], w3s, b3, g);
 }
 
 // Online segmented softmax and weighted sum for one 16-position tile of range
@@ -510,6 +564,7 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
 
     const int stride = gridDim.x * kDinWaves;
     const int n = lane & 15;
+    const LaneSrc src = lane_src(a, lane);
     int r = first + wave;
     int p0 = r < nr ? r * R : 0;
     int cnt = r < nr ? (int)min((int64_t)R, P - p0) : 0;
@@ -518,9 +573,9 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
     if (cnt > 0) {
         Ent E[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) load_entries(a, p0, cnt, 16 * s + n, lane, E[s]);
+        for (int s = 0; s < 2; ++s) load_entries(a, src, p0, cnt, 16 * s + n, E[s]);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) load_data(a, E[s], p0, cnt, 16 * s + n, lane, S[s]);
+        for (int s = 0; s < 2; ++s) load_data(a, src, E[s], p0, cnt, 16 * s + n, lane, S[s]);
     }
 
     if (kBF && !kPacked) {
@@ -580,10 +635,12 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
         Ent E[2];
         if (more) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) load_entries(a, p0n, cntn, sbn + 16 * s + n, lane, E[s]);
+            for (int s = 0; s < 2; ++s) load_entries(a, src, p0n, cntn, sbn + 16 * s + n, E[s]);
         }
         float e[2];
         const bool two = cnt - sb > 16;
+        mask_sub(S[0]);
+        mask_sub(S[1]);
         if (kBF) {
             if (two) mlp_bf16<2>(S, s_w1, s_w2, s_b1, s_b2, s_w3, a.b3, lane, e);
             else mlp_bf16<1>(S, s_w1, s_w2, s_b1, s_b2, s_w3, a.b3, lane, e);
@@ -594,7 +651,7 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
         Sub Sn[2];
         if (more) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) load_data(a, E[s], p0n, cntn, sbn + 16 * s + n, lane, Sn[s]);
+            for (int s = 0; s < 2; ++s) load_data(a, src, E[s], p0n, cntn, sbn + 16 * s + n, lane, Sn[s]);
         }
         softmax_tile(a, S[0], e[0], lane, r, R, m_open, l_open, acc_open);
         if (two) softmax_tile(a, S[1], e[1], lane, r, R, m_open, l_open, acc_open);
