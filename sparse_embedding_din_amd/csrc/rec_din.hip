@@ -86,12 +86,39 @@ __device__ inline float seg_max(float v, const SegMask& m) {
     return v;
 }
 
-__device__ inline float seg_sum(float v, const SegMask& m) {
-    v = fmaf(dpp_row_shr<1>(v), m.mk[0], v);
-    v = fmaf(dpp_row_shr<2>(v), m.mk[1], v);
-    v = fmaf(dpp_row_shr<4>(v), m.mk[2], v);
-    v = fmaf(dpp_row_shr<8>(v), m.mk[3], v);
-    return v;
+// N segmented sums at once, step-major: the N independent chains fill the
+// wait a DPP read of a just-written register needs.
+template <int D, int N>
+__device__ inline void seg_step(float (&v)[N], float mk) {
+    float t[N];
+#pragma unroll
+    for (int f = 0; f < N; ++f) t[f] = dpp_row_shr<D>(v[f]);
+#pragma unroll
+    for (int f = 0; f < N; ++f) v[f] = fmaf(t[f], mk, v[f]);
+}
+
+template <int N>
+__device__ inline void seg_sums(float (&v)[N], const SegMask& m) {
+    seg_step<1>(v, m.mk[0]);
+    seg_step<2>(v, m.mk[1]);
+    seg_step<4>(v, m.mk[2]);
+    seg_step<8>(v, m.mk[3]);
+}
+
+// lane 15 of each 16-lane row, in every lane of the row (DPP row_newbcast)
+__device__ inline float row_bcast15(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x15F, 0xF, 0xF, false));
+}
+
+// p + the value of the lane 16 (or 32) lanes away: the two halves returned by
+// a permlane swap of p with itself are p's own rows and their partners
+__device__ inline float add_xor16(float p) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float add_xor32(float p) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Gathering one tile for lane (n, g) takes two dependent rounds: its packed
@@ -219,8 +246,8 @@ __device__ inline float score_from_h2(const f32x4 (&acc2)[4], const float* w3s, 
             p += fmaxf(acc2[mt][i], 0.f) * w3s[u];
         }
     }
-    p += __shfl_xor(p, 16, 64);
-    p += __shfl_xor(p, 32, 64);
+    p = add_xor16(p);
+    p = add_xor32(p);
     return p + b3;
 }
 
@@ -405,10 +432,15 @@ __device__ inline void softmax_tile(const DinArgs& a, const Sub& S, float e, int
     const float mseg = __shfl(mx, (lane & 48) + en, 64);
     const float mref = cont ? fmaxf(mseg, m_open) : mseg;
     const float w = S.valid ? __expf(ev - mref) : 0.f;
-    float l = seg_sum(w, mk);
+    float v[13];
+    v[12] = w;
+#pragma unroll
+    for (int f = 0; f < 12; ++f) v[f] = w * S.s[f];
+    seg_sums(v, mk);
+    float l = v[12];
     float A[12];
 #pragma unroll
-    for (int f = 0; f < 12; ++f) A[f] = seg_sum(w * S.s[f], mk);
+    for (int f = 0; f < 12; ++f) A[f] = v[f];
     if (cont) {
         const float sc = __expf(m_open - mref);
         l += l_open * sc;
@@ -419,7 +451,7 @@ __device__ inline void softmax_tile(const DinArgs& a, const Sub& S, float e, int
     const bool whole = S.j == S.jl && S.rem == S.rl;
     if (end) {
         if (whole) {
-            const float inv = 1.f / l;
+            const float inv = __builtin_amdgcn_rcpf(l);
             float4* o = (float4*)(a.out + (int64_t)S.b * 48 + 12 * g);
 #pragma unroll
             for (int q = 0; q < 3; ++q)
@@ -441,9 +473,8 @@ __device__ inline void softmax_tile(const DinArgs& a, const Sub& S, float e, int
     if (open) {
         m_open = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mref), 15));
         l_open = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 15));
-        const int last = (lane & 48) + 15;
 #pragma unroll
-        for (int f = 0; f < 12; ++f) acc_open[f] = __shfl(A[f], last, 64);
+        for (int f = 0; f < 12; ++f) acc_open[f] = row_bcast15(A[f]);
     }
     if (a.weights) {
         __threadfence();
@@ -706,7 +737,7 @@ __device__ inline void finalize_range(const DinArgs& a, int64_t r, const float4 
         }
         m = mn;
     }
-    const float inv = 1.f / l;
+    const float inv = __builtin_amdgcn_rcpf(l);
     float4* o = (float4*)(a.out + (int64_t)b * 48);
 #pragma unroll
     for (int q = 0; q < 12; ++q)
