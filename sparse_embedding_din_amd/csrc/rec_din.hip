@@ -458,7 +458,7 @@ __device__ inline void softmax_tile(const DinArgs& a, const Sub& S, float e, int
                 o[q] = make_float4(A[4 * q] * inv, A[4 * q + 1] * inv, A[4 * q + 2] * inv, A[4 * q + 3] * inv);
         } else {
             const bool is_head = S.j > S.jl;
-            float* ps = a.partials + ((int64_t)r * 2 + (is_head ? 0 : 1)) * kPartialFloats;
+            float* ps = is_head ? head_slot(a.partials, r) : tail_slot(a.partials, r);
             if (g == 0)
                 *(float4*)ps = make_float4(mref, l, __int_as_float(S.b),
                                            __int_as_float(((int)S.pos + S.rem) / R));
@@ -702,64 +702,74 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
 }
 
 // One thread per range r that may hold a tail piece (a sample that starts in
-// r and runs on into r+1 .. r1): the slot says whether it does, with the
-// sample and r1.  A thread's first slot is read together with the header's
-// count of slots the plan cleared (the slot exists whatever the count), so
-// the usual case, one slot per thread, costs two dependent rounds of loads;
-// the head pieces of r+1 .. r1 are the second.
-__device__ inline void finalize_range(const DinArgs& a, int64_t r, const float4 t) {
-    const float* tp = a.partials + (r * 2 + 1) * kPartialFloats;
-    const int b = __float_as_int(t.z);
-    const int64_t r1 = __float_as_int(t.w);
-    float m = t.x, l = t.y;
-    float acc[48];
+// r and runs on into r+1 .. r1).  The tail piece and the head piece of r+1
+// sit next to each other and are read in one round, together with the
+// header's count of slots the plan cleared (the slots exist whatever the
+// count); only a sample reaching past r+1 needs a second round.
+struct Piece {
+    float2 ml;
+    float4 v[12];
+};
+
+__device__ inline void load_piece(Piece& p, const float* hp) {
+    p.ml = *(const float2*)hp;
 #pragma unroll
-    for (int q = 0; q < 12; ++q) {
-        const float4 v = *(const float4*)(tp + 4 + 4 * q);
-        acc[4 * q] = v.x;
-        acc[4 * q + 1] = v.y;
-        acc[4 * q + 2] = v.z;
-        acc[4 * q + 3] = v.w;
-    }
-    for (int64_t h = r + 1; h <= r1; ++h) {
-        const float* hp = a.partials + (h * 2) * kPartialFloats;
-        const float2 ml = *(const float2*)hp;
-        const float mn = fmaxf(m, ml.x);
-        const float sa = __expf(m - mn), sh = __expf(ml.x - mn);
-        l = l * sa + ml.y * sh;
-#pragma unroll
-        for (int q = 0; q < 12; ++q) {
-            const float4 v = *(const float4*)(hp + 4 + 4 * q);
-            acc[4 * q] = acc[4 * q] * sa + v.x * sh;
-            acc[4 * q + 1] = acc[4 * q + 1] * sa + v.y * sh;
-            acc[4 * q + 2] = acc[4 * q + 2] * sa + v.z * sh;
-            acc[4 * q + 3] = acc[4 * q + 3] * sa + v.w * sh;
-        }
-        m = mn;
-    }
-    const float inv = __builtin_amdgcn_rcpf(l);
-    float4* o = (float4*)(a.out + (int64_t)b * 48);
-#pragma unroll
-    for (int q = 0; q < 12; ++q)
-        o[q] = make_float4(acc[4 * q] * inv, acc[4 * q + 1] * inv, acc[4 * q + 2] * inv, acc[4 * q + 3] * inv);
-    if (a.weights) {
-        const int64_t ps = a.pos_start[b], pe = a.pos_start[b + 1];
-        for (int64_t q = ps; q < pe; ++q) a.weights[q] = __expf(a.scores[q] - m) / l;
-    }
+    for (int q = 0; q < 12; ++q) p.v[q] = *(const float4*)(hp + 4 + 4 * q);
 }
 
+__device__ inline void merge_piece(float& m, float& l, float (&acc)[48], const Piece& p) {
+    const float mn = fmaxf(m, p.ml.x);
+    const float sa = __expf(m - mn), sh = __expf(p.ml.x - mn);
+    l = l * sa + p.ml.y * sh;
+#pragma unroll
+    for (int q = 0; q < 12; ++q) {
+        acc[4 * q] = acc[4 * q] * sa + p.v[q].x * sh;
+        acc[4 * q + 1] = acc[4 * q + 1] * sa + p.v[q].y * sh;
+        acc[4 * q + 2] = acc[4 * q + 2] * sa + p.v[q].z * sh;
+        acc[4 * q + 3] = acc[4 * q + 3] * sa + p.v[q].w * sh;
+    }
+    m = mn;
+}
 
 __global__ __launch_bounds__(256) void k_din_finalize(const DinArgs a, int64_t max_ranges) {
     const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (r >= max_ranges) return;
-    float4 t = *(const float4*)(a.partials + (r * 2 + 1) * kPartialFloats);
     const int64_t nclear = a.plan_hdr[kHdrNClear];
-    while (r < nclear) {
-        if (__float_as_int(t.z) >= 0) finalize_range(a, r, t);
-        r += stride;
+    for (int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x; r < max_ranges; r += stride) {
+        // the tail piece of r and the head piece of r+1 (next to it), read
+        // before knowing whether r has a tail: both slots always exist
+        const float* tp = tail_slot(a.partials, r);
+        const float4 t = *(const float4*)tp;
+        float acc[48];
+#pragma unroll
+        for (int q = 0; q < 12; ++q) {
+            const float4 v = *(const float4*)(tp + 4 + 4 * q);
+            acc[4 * q] = v.x;
+            acc[4 * q + 1] = v.y;
+            acc[4 * q + 2] = v.z;
+            acc[4 * q + 3] = v.w;
+        }
+        Piece h1;
+        load_piece(h1, head_slot(a.partials, r + 1));
         if (r >= nclear) break;
-        t = *(const float4*)(a.partials + (r * 2 + 1) * kPartialFloats);
+        const int b = __float_as_int(t.z);
+        if (b < 0) continue;
+        const int64_t r1 = __float_as_int(t.w);
+        float m = t.x, l = t.y;
+        merge_piece(m, l, acc, h1);
+        for (int64_t h = r + 2; h <= r1; ++h) {
+            Piece ph;
+            load_piece(ph, head_slot(a.partials, h));
+            merge_piece(m, l, acc, ph);
+        }
+        const float inv = __builtin_amdgcn_rcpf(l);
+        float4* o = (float4*)(a.out + (int64_t)b * 48);
+#pragma unroll
+        for (int q = 0; q < 12; ++q)
+            o[q] = make_float4(acc[4 * q] * inv, acc[4 * q + 1] * inv, acc[4 * q + 2] * inv, acc[4 * q + 3] * inv);
+        if (a.weights) {
+            const int64_t ps = a.pos_start[b], pe = a.pos_start[b + 1];
+            for (int64_t q = ps; q < pe; ++q) a.weights[q] = __expf(a.scores[q] - m) / l;
+        }
     }
 }
 

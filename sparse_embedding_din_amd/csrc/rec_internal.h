@@ -146,13 +146,14 @@ __host__ __device__ inline KjtLayout kjt_layout(int32_t T, int64_t B) {
 //   pos_jr         int32[Pmax]: j | (L - 1 - j) << 16 (step, steps left)
 //   pos_rows       int32[3][Pmax]: resolved row of the adgroup/cate/brand id
 //                  (a hash miss is -1)
-//   partials       float[max_ranges][2][52]: per range, the state of the sample
-//                  entering it (slot 0, head) and of the sample leaving it
-//                  (slot 1, tail): max, sum, then (tail only, as int bits)
-//                  the sample and the last range it reaches, 48 weighted
-//                  sums.  The plan marks the tail slots of every range the
-//                  attention can form as empty (sample -1), their count in
-//                  the header.
+//   partials       float[max_ranges + 1][2][52]: per range edge e, the state of
+//                  the sample leaving range e-1 (tail piece of e-1) and then
+//                  of the sample entering range e (head piece of e): max,
+//                  sum, then (tail only, as int bits) the sample and the last
+//                  range it reaches, 48 weighted sums.  A sample cut at edge e
+//                  so has both its pieces next to each other.  The plan marks
+//                  the tail slots of every range the attention can form as
+//                  empty (sample -1), their count in the header.
 //   empty          int32[B]: the samples with no positions (header: count)
 enum { kHdrB = 0, kHdrMaxLen, kHdrRReq, kHdrR, kHdrP, kHdrNBlocks, kHdrNRanges, kHdrNEmpty,
        kHdrNClear };
@@ -161,6 +162,13 @@ constexpr int kPlanSumWords = 2 + 2 * (kScanChunk / kPlanChunk);   // 130
 constexpr int kMinRange = 16;
 constexpr int kMaxRange = 1 << 20;
 constexpr int kPartialFloats = 52;
+// the tail piece of range r and the head piece of range r (see the layout)
+__host__ __device__ inline float* tail_slot(float* partials, int64_t r) {
+    return partials + (r + 1) * 2 * kPartialFloats;
+}
+__host__ __device__ inline float* head_slot(float* partials, int64_t r) {
+    return partials + (r * 2 + 1) * kPartialFloats;
+}
 
 struct PlanLayout {
     int64_t nblocks, pmax, max_ranges;
@@ -181,7 +189,7 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t B, int32_t max_len) {
     p.off_pjr = align16(p.off_pb + 4 * (size_t)p.pmax);
     p.off_prows = align16(p.off_pjr + 4 * (size_t)p.pmax);
     p.off_part = align16(p.off_prows + 12 * (size_t)p.pmax);
-    p.off_empty = align16(p.off_part + sizeof(float) * 2 * kPartialFloats * (size_t)p.max_ranges);
+    p.off_empty = align16(p.off_part + sizeof(float) * 2 * kPartialFloats * (size_t)(p.max_ranges + 1));
     p.bytes = align16(p.off_empty + 4 * (size_t)B);
     return p;
 }

@@ -145,7 +145,7 @@ __device__ inline void k_plan_sums_body(const int32_t* __restrict__ len,
     // every tail slot the attention may use starts empty
     for (int64_t r = (int64_t)bid * kScanThreads + threadIdx.x; r < nclear;
          r += (int64_t)nblk * kScanThreads)
-        *(float4*)(partials + (r * 2 + 1) * kPartialFloats) = make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
+        *(float4*)tail_slot(partials, r) = make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
 }
 
 // The plan for 16 samples per block.  Wave 0 adds up the sums before the
