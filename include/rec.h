@@ -90,7 +90,8 @@ enum { REC_F32 = 0, REC_BF16 = 1, REC_BF16_PACKED = 2 };   /* rec_din_mlp.dtype 
  *   (§3.2: the constant zero vector).  The raw id is the key (no modulo).
  *
  * Every table: dim == 16, rows >= 1 (REC_HASH: rows <= 2^31 - 1), values
- * 16-byte aligned (each row is 64 contiguous bytes).
+ * 16-byte aligned (each row is 64 contiguous bytes); REC_HASH: digests
+ * 16-byte aligned (the probe reads them 32 at a time), keys 8-byte aligned.
  */
 typedef struct {
     int32_t kind;
@@ -358,9 +359,15 @@ int32_t rec_version(void);
  *   rec_host_floor_mod: row of raw id x in a direct table of n rows (n >= 1)
  *   rec_host_hash_home: home slot of key x in a table of `capacity` slots;
  *                       *digest receives the key's digest byte
+ *   rec_host_hash_probe: the slot holding `key` in a hash table given by its
+ *                       host arrays keys[capacity] and digests[capacity]
+ *                       (16-byte aligned), -1 if absent, -2 for invalid
+ *                       arguments: the device's windowed probe, run on the host
  */
 int64_t rec_host_floor_mod(int64_t x, int64_t n);
 int64_t rec_host_hash_home(int64_t x, int64_t capacity, uint8_t* digest);
+int64_t rec_host_hash_probe(const int64_t* keys, const uint8_t* digests, int64_t capacity,
+                            int64_t key);
 
 #ifdef __cplusplus
 }

@@ -44,6 +44,8 @@ rec_status prep_table(const rec_table& t, const char* what, TabDev* out) {
     out->kind = t.kind;
     if (t.kind == REC_HASH) {
         if (!t.keys || !t.digests) return fail(REC_EINVAL, std::string(what) + ": hash table needs keys and digests");
+        if (!aligned16(t.digests) || ((uintptr_t)t.keys & 7u))
+            return fail(REC_EINVAL, std::string(what) + ": digests must be 16-byte and keys 8-byte aligned");
         if (t.rows > 2147483647LL) return fail(REC_EINVAL, std::string(what) + ": hash capacity above 2^31-1");
         out->keys = t.keys;
         out->digests = t.digests;
@@ -236,6 +238,18 @@ int64_t rec_host_floor_mod(int64_t x, int64_t n) {
     int32_t s;
     floor_mod_prepare(n, &m, &s);
     return floor_mod_magic(x, n, m, s);
+}
+
+int64_t rec_host_hash_probe(const int64_t* keys, const uint8_t* digests, int64_t capacity,
+                            int64_t key) {
+    if (!keys || !digests || capacity < 1 || !aligned16(digests)) return -2;
+    TabDev t;
+    memset(&t, 0, sizeof(t));
+    t.keys = keys;
+    t.digests = digests;
+    t.rows = capacity;
+    t.kind = REC_HASH;
+    return hash_probe(t, key);
 }
 
 int64_t rec_host_hash_home(int64_t x, int64_t capacity, uint8_t* digest) {

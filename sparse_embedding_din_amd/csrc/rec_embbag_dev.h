@@ -30,24 +30,61 @@ namespace {
 constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kUnroll = 3;           // ids per bag resolved per round
 
+// A table descriptor whose fields are pinned to scalar registers.  Choosing
+// between two of them per lane is then a register select; choosing between
+// two descriptors in the kernel arguments would compile into per-lane loads
+// of the chosen descriptor's fields, a dependent round trip before any id.
+__device__ inline uint64_t uniform64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ inline TabDev uniform_tab(const TabDev& t) {
+    TabDev u;
+    u.values = (const float*)(const float __attribute__((address_space(1)))*)uniform64((uint64_t)t.values);
+    u.keys = (const int64_t*)(const int64_t __attribute__((address_space(1)))*)uniform64((uint64_t)t.keys);
+    u.digests = (const uint8_t*)(const uint8_t __attribute__((address_space(1)))*)uniform64((uint64_t)t.digests);
+    u.rows = (int64_t)uniform64((uint64_t)t.rows);
+    u.magic = uniform64(t.magic);
+    u.shift = __builtin_amdgcn_readfirstlane(t.shift);
+    u.kind = __builtin_amdgcn_readfirstlane(t.kind);
+    return u;
+}
+
+__device__ inline TabDev pick_tab(bool hi, const TabDev& t1, const TabDev& t0) {
+    TabDev r;
+    r.values = hi ? t1.values : t0.values;
+    r.keys = hi ? t1.keys : t0.keys;
+    r.digests = hi ? t1.digests : t0.digests;
+    r.rows = hi ? t1.rows : t0.rows;
+    r.magic = hi ? t1.magic : t0.magic;
+    r.shift = hi ? t1.shift : t0.shift;
+    r.kind = hi ? t1.kind : t0.kind;
+    return r;
+}
+
 template <bool kHash, bool kFused>
 __device__ inline void k_embbag_fwd_body(const EmbArgs& a, int64_t bid) {
     const int lane = threadIdx.x & 63;
-    const int64_t w = (int64_t)bid * kWaves + (threadIdx.x >> 6);
+    // the wave index is uniform: pinning it lets the table descriptors be read
+    // with scalar loads and chosen per lane by a register select
+    const int64_t w = (int64_t)bid * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nbw = (a.B + 31) / 32;
     const int tp = (int)(w / nbw);
     if (2 * tp >= a.T) return;                               // wave-uniform
     const int64_t b = (w % nbw) * 32 + (lane & 31);
     const int t = 2 * tp + (lane >> 5);
     const bool live = b < a.B && t < a.T;
-    const TabDev& t0 = a.tab[2 * tp];
-    const TabDev& t1 = a.tab[2 * tp + 1];                    // zeroed past T
+    const TabDev t0 = uniform_tab(a.tab[2 * tp]);
+    const TabDev t1 = uniform_tab(a.tab[2 * tp + 1]);        // zeroed past T
     // lanes of a missing odd table read table 2p's rows (masked out below)
     const bool hi = lane >= 32 && 2 * tp + 1 < a.T;
-    const float* vals = hi ? t1.values : t0.values;
-    const int64_t rows = hi ? t1.rows : t0.rows;
-    const uint64_t magic = hi ? t1.magic : t0.magic;
-    const int32_t shift = hi ? t1.shift : t0.shift;
+    const TabDev tl = pick_tab(hi, t1, t0);
+    const float* vals = tl.values;
+    const int64_t rows = tl.rows;
+    const uint64_t magic = tl.magic;
+    const int32_t shift = tl.shift;
     const int tc = min(t, a.T - 1);
     const int64_t bag = (int64_t)tc * a.B + min(b, a.B - 1);
     int32_t len = a.lengths[bag];
@@ -92,8 +129,7 @@ __device__ inline void k_embbag_fwd_body(const EmbArgs& a, int64_t bid) {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             if (kHash) {
-                const TabDev& tb = hi ? t1 : t0;
-                row[u] = tb.kind == REC_HASH ? hash_probe(tb, raw[u]) : floor_mod_magic(raw[u], rows, magic, shift);
+                row[u] = tl.kind == REC_HASH ? hash_probe(tl, raw[u]) : floor_mod_magic(raw[u], rows, magic, shift);
             } else {
                 row[u] = floor_mod_magic(raw[u], rows, magic, shift);
             }

@@ -75,17 +75,69 @@ __host__ __device__ inline uint32_t hash_digest(uint64_t h) {
 }
 
 // Linear probe from the home slot: the slot holding `key`, or -1 on reaching
-// an empty slot (digest 0) or after `rows` probes.  Keys are compared only
-// where the digest matches.
-__device__ inline int64_t hash_probe(const TabDev& t, int64_t key) {
+// an empty slot (digest 0) or after `rows` probes.  Digests are read 32 at a
+// time (two aligned 16-byte loads covering the probe position) and scanned in
+// registers; a key is read only where the digest matches.  Near the end of
+// the table, where 32 bytes would run past it, the window is read byte by
+// byte with the probe's wrap-around.
+__host__ __device__ inline int64_t hash_probe(const TabDev& t, int64_t key) {
     const uint64_t h = mix64((uint64_t)key);
     const uint32_t d = hash_digest(h);
-    int64_t s = hash_home(h, t.rows);
-    for (int64_t c = 0; c < t.rows; ++c) {
-        const uint32_t ds = t.digests[s];
-        if (ds == 0u) return -1;
-        if (ds == d && t.keys[s] == key) return s;
-        s = (s + 1 == t.rows) ? 0 : s + 1;
+    const int64_t n = t.rows;
+    int64_t s = hash_home(h, n);                 // next slot to examine
+    int64_t left = n;                            // slots not yet examined
+    while (left > 0) {
+        const int64_t w = s & ~(int64_t)15;      // window [w, w + 32)
+        uint32_t dw[8];
+        if (w + 32 <= n) {
+            const uint4 a = *(const uint4*)(t.digests + w);
+            const uint4 b = *(const uint4*)(t.digests + w + 16);
+            dw[0] = a.x; dw[1] = a.y; dw[2] = a.z; dw[3] = a.w;
+            dw[4] = b.x; dw[5] = b.y; dw[6] = b.z; dw[7] = b.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                uint32_t v = 0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    int64_t i = w + 4 * k + c;
+                    if (i >= n) i -= n;              // w < n, so one wrap suffices
+                    if (i >= n) i = 0;               // tables smaller than the window
+                    v |= (uint32_t)t.digests[i] << (8 * c);
+                }
+                dw[k] = v;
+            }
+        }
+        // masks over the window: empty slots, digest matches, and the
+        // positions this window examines (from s, at most `left` of them)
+        uint32_t E = 0, M = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t by = (dw[k] >> (8 * c)) & 0xffu;
+                E |= (by == 0u ? 1u : 0u) << (4 * k + c);
+                M |= (by == d ? 1u : 0u) << (4 * k + c);
+            }
+        const int lo = (int)(s - w);
+        const int span = left < 32 - lo ? (int)left : 32 - lo;
+        const uint32_t win = (span >= 32 ? 0xffffffffu : ((1u << span) - 1u)) << lo;
+        E &= win;
+        M &= win;
+        // candidates: digest matches before the first empty slot, in order
+        uint32_t cand = M & (E ? (E & (~E + 1u)) - 1u : 0xffffffffu);
+        while (cand) {
+            const int i = __builtin_ffs((int)cand) - 1;
+            cand &= cand - 1u;
+            int64_t slot = w + i;
+            if (slot >= n) slot -= n;
+            if (t.keys[slot] == key) return slot;
+        }
+        if (E) return -1;
+        left -= span;
+        s = w + 32;
+        if (s >= n) s -= n;
+        if (s >= n) s = 0;
     }
     return -1;
 }

@@ -29,7 +29,8 @@ EXPORTS = ["rec_din_pack_mlp", "rec_scan_workspace_bytes", "rec_lengths_to_offse
            "rec_kjt_sums_bytes", "rec_kjt_sums", "rec_embbag_fwd_kjt", "rec_hash_lookup",
            "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_fwd",
            "rec_sparse_din_fwd_workspace_bytes", "rec_sparse_din_fwd",
-           "rec_last_error", "rec_version", "rec_host_floor_mod", "rec_host_hash_home"]
+           "rec_last_error", "rec_version", "rec_host_floor_mod", "rec_host_hash_home",
+           "rec_host_hash_probe"]
 
 
 class RecError(RuntimeError):
@@ -105,6 +106,8 @@ def lib():
         L.rec_host_floor_mod.restype = i64
         L.rec_host_hash_home.argtypes = [i64, i64, C.POINTER(C.c_uint8)]
         L.rec_host_hash_home.restype = i64
+        L.rec_host_hash_probe.argtypes = [vp, vp, i64, i64]
+        L.rec_host_hash_probe.restype = i64
         _LIB = L
     return _LIB
 
@@ -261,6 +264,11 @@ def rec_sparse_din_fwd(args: Optional[rec_fwd_args], stream=None):
 
 def rec_host_floor_mod(x: int, n: int) -> int:
     return int(lib().rec_host_floor_mod(x, n))
+
+
+def rec_host_hash_probe(keys, digests, capacity: int, key: int) -> int:
+    """keys/digests: host numpy arrays (int64, uint8; digests 16-byte aligned)."""
+    return int(lib().rec_host_hash_probe(keys.ctypes.data, digests.ctypes.data, capacity, key))
 
 
 def rec_host_hash_home(x: int, capacity: int):

@@ -312,3 +312,39 @@ def test_host_hash_home_matches_generator(lib):
             got_h, got_d = R.rec_host_hash_home(int(k), cap)
             assert got_h == int(h) and got_d == int(d)
             assert 0 <= got_h < cap and got_d != 0
+
+
+def _aligned_u8(n):
+    buf = np.zeros(n + 64, np.uint8)
+    off = (-buf.ctypes.data) % 16
+    return buf[off: off + n]
+
+
+@pytest.mark.parametrize("cap,nkeys", [(1, 0), (2, 1), (5, 4), (16, 15), (17, 16), (31, 20),
+                                       (32, 31), (33, 32), (37, 30), (64, 60), (100, 70),
+                                       (1000, 700), (4099, 4000)])
+def test_host_hash_probe_windowed(lib, cap, nkeys):
+    """The device's windowed probe (32 digests per read, byte reads with wrap
+    near the table's end), run on the host, against set membership on tables
+    of every size around the window, including full and nearly full ones:
+    every stored key is found in its slot, every other key misses.  (The
+    table layout needs at least one empty slot.)"""
+    rng = np.random.default_rng(cap * 1000 + nkeys)
+    I64 = np.iinfo(np.int64)
+    stored = np.unique(rng.integers(I64.min, I64.max, size=nkeys * 2 + 1, dtype=np.int64))
+    stored = stored[stored != synth.EMPTY_KEY][:nkeys]
+    vals = np.zeros((max(stored.size, 1), 16), np.float32)
+    tab = synth.build_hash_table(stored, vals[: stored.size], cap)
+    keys = np.ascontiguousarray(tab["keys"], np.int64)
+    dig = _aligned_u8(cap)
+    dig[:] = tab["digests"]
+    for k in stored:
+        slot = R.rec_host_hash_probe(keys, dig, cap, int(k))
+        assert slot >= 0 and keys[slot] == k
+    misses = rng.integers(I64.min, I64.max, size=300, dtype=np.int64)
+    for k in misses:
+        if k in set(stored.tolist()):
+            continue
+        assert R.rec_host_hash_probe(keys, dig, cap, int(k)) == -1
+    if cap > 1:
+        assert R.rec_host_hash_probe(keys, dig[1:], cap - 1, 0) == -2     # misaligned digests

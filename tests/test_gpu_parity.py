@@ -220,6 +220,35 @@ def test_hash_lookup(models):
         assert np.all(rg[~hit] == 0.0) and not np.any(np.signbit(rg[~hit]))
 
 
+@pytest.mark.parametrize("cap,nkeys", [(2, 1), (17, 16), (33, 32), (37, 30), (100, 70), (4099, 4000)])
+def test_hash_lookup_small_tables(cap, nkeys):
+    """Tables around the 32-digest window and nearly full (probes that wrap
+    past the end), on the device against the oracle: bit-exact slots, exact
+    rows, exact zero rows for misses."""
+    rng = np.random.default_rng(cap)
+    I64 = np.iinfo(np.int64)
+    stored = np.unique(rng.integers(I64.min, I64.max, size=2 * nkeys, dtype=np.int64))
+    stored = stored[stored != synth.EMPTY_KEY][:nkeys]
+    vals = rng.standard_normal((stored.size, 16)).astype(np.float32)
+    tab = synth.build_hash_table(stored, vals, cap)
+    miss = rng.integers(I64.min, I64.max, size=500, dtype=np.int64)
+    keys = np.concatenate([stored, miss, [synth.EMPTY_KEY]])
+    say(f"hash small cap={cap} n={keys.size}")
+    dt = PL.DeviceTables([tab], DEV)
+    kt = torch.from_numpy(keys).to(DEV)
+    slot = torch.full((keys.size,), -9, dtype=torch.int64, device=DEV)
+    rows = torch.full((keys.size, 16), np.nan, dtype=torch.float32, device=DEV)
+    R.rec_hash_lookup(dt.desc[0], kt, keys.size, slot, rows)
+    torch.cuda.synchronize()
+    ref = oracle.get().resolve(tab, keys)
+    got = slot.cpu().numpy()
+    assert np.array_equal(got, ref)
+    rg = rows.cpu().numpy()
+    hit = ref >= 0
+    assert np.array_equal(rg[hit], tab["values"][ref[hit]])
+    assert np.all(rg[~hit] == 0.0)
+
+
 # ---------------------------------------------------------------------------
 DIN_CASES = [
     (1, 256, None), (1, 1, None), (1, 37, None),
