@@ -67,6 +67,9 @@ class Oracle:
         L.orc_din.argtypes = [C.POINTER(OrcTable), P64, C.c_int64, P64, P32, C.c_int32,
                               PD, PD, PD, PD, PD, PD, C.c_double, P64, C.c_int64, PD, PD, PD]
         L.orc_din.restype = None
+        L.orc_towers.argtypes = [C.c_int64, PD, C.c_int64, PD, PD, PD, PD, PD, PD, PD, PD, PD,
+                                 PD, C.c_double, PD, PD, PD]
+        L.orc_towers.restype = None
         self._keep = []
 
     # -- bookkeeping ---------------------------------------------------------
@@ -163,6 +166,28 @@ class Oracle:
         return att
 
 
+    def towers(self, pooled, att, tw):
+        """Deep tower + final MLP.  pooled: [ns][>=256] (the first 256 columns
+        are the deep input), att: [ns][48]; tw has wd1, bd1, wd2, bd2, wd3, bd3,
+        wf, bf, wo, bo (values as the GPU receives them).  Returns deep_out
+        [ns][128], logit [ns] and prob [ns], fp64."""
+        x = np.ascontiguousarray(pooled, dtype=np.float64)
+        a = np.ascontiguousarray(att, dtype=np.float64).reshape(x.shape[0], 48)
+        assert x.ndim == 2 and x.shape[1] >= 256
+        ns = x.shape[0]
+        d = [np.ascontiguousarray(getattr(tw, k), dtype=np.float64)
+             for k in ("wd1", "bd1", "wd2", "bd2", "wd3", "bd3", "wf", "bf", "wo")]
+        assert d[0].shape == (512, 256) and d[2].shape == (256, 512)
+        assert d[4].shape == (128, 256) and d[6].shape == (64, 176) and d[8].shape == (64,)
+        deep = np.empty((ns, 128), dtype=np.float64)
+        logit = np.empty(ns, dtype=np.float64)
+        prob = np.empty(ns, dtype=np.float64)
+        self.lib.orc_towers(ns, _ptr(x, PD), x.shape[1], _ptr(a, PD),
+                            *[_ptr(v, PD) for v in d], float(tw.bo),
+                            _ptr(deep, PD), _ptr(logit, PD), _ptr(prob, PD))
+        return deep, logit, prob
+
+
 _DEFAULT: Optional[Oracle] = None
 
 
@@ -175,9 +200,11 @@ def get() -> Oracle:
 
 # ---------------------------------------------------------------------------
 # Whole-forward convenience used by tests and the CPU-baseline leg.
-def forward(model, batch, samples=None, orc: Optional[Oracle] = None, want_scores=False):
+def forward(model, batch, samples=None, orc: Optional[Oracle] = None, want_scores=False,
+            towers=False):
     """Oracle forward for one generator batch: returns dict with offsets,
-    pooled [ns, 256], att [ns, 48] (+ scores/weights) for `samples`."""
+    pooled [ns, 256], att [ns, 48] (+ scores/weights) for `samples`; with
+    towers=True also deep [ns, 128], logit [ns] and prob [ns]."""
     import synth
     orc = orc or get()
     B = batch.B
@@ -198,4 +225,6 @@ def forward(model, batch, samples=None, orc: Optional[Oracle] = None, want_score
         out["att"], out["scores"], out["weights"] = r
     else:
         out["att"] = r
+    if towers:
+        out["deep"], out["logit"], out["prob"] = orc.towers(pooled, out["att"], model.towers)
     return out

@@ -16,11 +16,14 @@
  *             (hidden 256, 64), linear to one score, mask + softmax, weighted
  *             sum of the sequence
  *        §4.4 compute graph: pooled deep features; query [B,48]; sequence
- *             [B,100,48]; attn input [B,100,192]; output [B,48]
+ *             [B,100,48]; attn input [B,100,192]; output [B,48]; then the
+ *             deep MLP to [B,128], the concat to [B,176] and the final MLP
  *   [P2] "MultiTowerDIN：集成 DynamicEmb"
  *        §3.2 lookup is an O(1) open-addressing hash table; an unseen id gives
  *             the constant 0 vector
  *        §4.3 unseen id -> not in the table -> zero embedding
+ *        §7   model config: tower hidden units [512, 256, 128], attention MLP
+ *             [256, 64], final [64], binary cross entropy loss
  *   [P3] DLRM essay (wmrh.cn/news/12459) §3.2: EmbeddingBag pools each bag
  *        (mode sum)
  *
@@ -214,4 +217,50 @@ void orc_din(const orc_table* seq_tables /* 3: adgroup, cate, brand */,
     }
     free(sj);
     free(e);
+}
+
+/* ------------------------------------------------------------------------
+ * Deep tower and final MLP: the rest of the MultiTowerDIN forward
+ * ([P1] §4.4 compute graph: the deep MLP 512 -> 256 -> 128 on the pooled deep
+ * features, the concat of its [B,128] output with the [B,48] attention
+ * output into [B,176], the final MLP 176 -> 64 -> 1; [P2] §7 model config:
+ * tower hidden units [512, 256, 128], final hidden units [64]; the loss is
+ * binary cross entropy, so the last unit is a logit).
+ *   d1    = relu(Wd1 x  + bd1)    Wd1 [512][256], x = pooled deep row (256)
+ *   d2    = relu(Wd2 d1 + bd2)    Wd2 [256][512]
+ *   d3    = relu(Wd3 d2 + bd3)    Wd3 [128][256]      -> deep_out
+ *   z     = [d3, att]                                 (176)
+ *   f     = relu(Wf z + bf)       Wf  [64][176]
+ *   logit = wo . f + bo;  prob = 1 / (1 + exp(-logit))
+ * Readings: ReLU after every hidden layer, none on the logit; biases on every
+ * layer; the deep output comes first in the concat (the page's order).
+ * pooled has row stride `ld` (>= 256); att is [ns][48]; deep_out [ns][128],
+ * logit [ns] and prob [ns] (deep_out and prob may be NULL).               */
+static void orc_layer(const double* W, const double* bias, const double* in, int nin,
+                      int nout, double* out) {
+    for (int o = 0; o < nout; ++o) {
+        double acc = bias[o];
+        for (int i = 0; i < nin; ++i) acc += W[(int64_t)o * nin + i] * in[i];
+        out[o] = acc > 0.0 ? acc : 0.0;
+    }
+}
+
+void orc_towers(int64_t ns, const double* pooled, int64_t ld, const double* att,
+                const double* wd1, const double* bd1, const double* wd2, const double* bd2,
+                const double* wd3, const double* bd3, const double* wf, const double* bf,
+                const double* wo, double bo,
+                double* deep_out, double* logit, double* prob) {
+    double d1[512], d2[256], z[176], f[64];
+    for (int64_t s = 0; s < ns; ++s) {
+        orc_layer(wd1, bd1, pooled + s * ld, 256, 512, d1);
+        orc_layer(wd2, bd2, d1, 512, 256, d2);
+        orc_layer(wd3, bd3, d2, 256, 128, z);
+        for (int c = 0; c < 48; ++c) z[128 + c] = att[s * 48 + c];
+        orc_layer(wf, bf, z, 176, 64, f);
+        double lg = bo;
+        for (int i = 0; i < 64; ++i) lg += wo[i] * f[i];
+        if (deep_out) for (int c = 0; c < 128; ++c) deep_out[s * 128 + c] = z[c];
+        logit[s] = lg;
+        if (prob) prob[s] = 1.0 / (1.0 + exp(-lg));
+    }
 }

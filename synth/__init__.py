@@ -47,6 +47,9 @@ TINY_SIZES = [11417, 8468, 4234, 4615, 2559, 1296, 98, 14, 3, 8, 5, 5, 3, 6,
               20, 101]
 
 HIDDEN1, HIDDEN2, DIN_IN = 256, 64, 192
+# deep tower [256] -> 512 -> 256 -> 128; final MLP [128 + 48] -> 64 -> 1
+TOWER_IN, TOWER_H = 256, (512, 256, 128)
+FINAL_IN, FINAL_H = 176, 64
 MAX_LEN = 100
 EMPTY_KEY = -1
 SEED_BASE = 20261202
@@ -188,6 +191,25 @@ class Model:
     w2_bf16: Optional[np.ndarray] = None
     zipf_perm: Optional[dict] = None
     zipf_cdf: Optional[dict] = None
+    towers: Optional["Towers"] = None
+
+
+@dataclasses.dataclass
+class Towers:
+    """Deep-tower and final-MLP parameters, output-major like nn.Linear.weight.
+    Matrices hold the values the GPU receives (bf16-representable when the
+    model's MLP dtype is bf16); *_bits are their bf16 bit patterns then."""
+    wd1: np.ndarray             # fp32 [512,256]
+    bd1: np.ndarray             # fp32 [512]
+    wd2: np.ndarray             # fp32 [256,512]
+    bd2: np.ndarray
+    wd3: np.ndarray             # fp32 [128,256]
+    bd3: np.ndarray
+    wf: np.ndarray              # fp32 [64,176]
+    bf: np.ndarray
+    wo: np.ndarray              # fp32 [64]
+    bo: float
+    bits: Optional[dict] = None  # name -> uint16 bit patterns (bf16 models)
 
 
 @dataclasses.dataclass
@@ -267,7 +289,33 @@ def make_model(cfg: Config, *, emb_std: float = 0.05, bias: bool = False,
         w2 = bf16_bits_to_f32(w2b)
     m = Model(cfg, tables, w1, b1, w2, b2, w3, b3, w1b, w2b, zipf_perm, zipf_cdf)
     m.mlp_dtype = dt
+    m.towers = make_towers(cfg, bias=bias, mlp_dtype=dt, seed_offset=seed_offset)
     return m
+
+
+def make_towers(cfg: Config, *, bias: bool = False, mlp_dtype: Optional[str] = None,
+                seed_offset: int = 0) -> Towers:
+    """Xavier-uniform tower weights from a seed stream of their own (the
+    tables and the attention MLP draw nothing different because of them)."""
+    rng = np.random.default_rng(np.random.SeedSequence(
+        [SEED_BASE + cfg.index + 1000 * seed_offset, 4096]))
+    dims = [(TOWER_H[0], TOWER_IN), (TOWER_H[1], TOWER_H[0]), (TOWER_H[2], TOWER_H[1]),
+            (FINAL_H, FINAL_IN)]
+    ws = [_xavier(rng, o, i) for o, i in dims]
+    wo = _xavier(rng, 1, FINAL_H).reshape(FINAL_H)
+    if bias:
+        bs = [rng.uniform(-0.1, 0.1, o).astype(np.float32) for o, _ in dims]
+        bo = float(np.float32(rng.uniform(-0.1, 0.1)))
+    else:
+        bs = [np.zeros(o, np.float32) for o, _ in dims]
+        bo = 0.0
+    bits = None
+    if (mlp_dtype or cfg.mlp_dtype) == "bf16":
+        bits = {}
+        for name, k in zip(("wd1", "wd2", "wd3", "wf"), range(4)):
+            bits[name] = _round_bf16(ws[k])
+            ws[k] = bf16_bits_to_f32(bits[name])
+    return Towers(ws[0], bs[0], ws[1], bs[1], ws[2], bs[2], ws[3], bs[3], wo, bo, bits)
 
 
 def _distinct_keys(rng, n):

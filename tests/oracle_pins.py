@@ -308,5 +308,100 @@ def pin_din_hash(orc):
     assert _rel(att, ratt) < 1e-12
 
 
+# ----------------------------------------------------------------------------
+# Deep tower + final MLP ("MultiTowerDIN：当前现状分析" §4.4 compute graph).
+def _sparse_towers(rng, ns):
+    """A tower whose every layer is a sparse integer-ish map, so each output
+    has a closed form in index arithmetic: every row of every matrix has one
+    or two non-zeros, biases are chosen so that the ReLUs clip some units."""
+    tw = synth.Towers(*(None,) * 10)
+    x = rng.uniform(0.0, 1.0, (ns, 300))             # row stride 300 > 256
+    x[:, 256:] = -7.0                                # columns past 256 must not be read
+    att = rng.uniform(-1.0, 1.0, (ns, 48))
+    p1 = rng.permutation(256)
+    tw.wd1 = np.zeros((512, 256)); tw.bd1 = np.zeros(512)
+    tw.wd1[np.arange(256), p1] = 1.0                 # d1[r] = x[p1[r]]
+    tw.wd1[256 + np.arange(256), p1] = -1.0          # d1[256 + r] = relu(0.5 - x[p1[r]])
+    tw.bd1[256:] = 0.5
+    p2 = rng.permutation(512)
+    a2, c2 = p2[:256], p2[256:]
+    tw.wd2 = np.zeros((256, 512)); tw.bd2 = np.full(256, 0.3)
+    tw.wd2[np.arange(256), a2] = 1.0                 # d2[r] = relu(0.3 + d1[a2] - 2 d1[c2])
+    tw.wd2[np.arange(256), c2] = -2.0
+    a3 = rng.permutation(256)[:128]
+    tw.wd3 = np.zeros((128, 256)); tw.bd3 = np.full(128, -0.1)
+    tw.wd3[np.arange(128), a3] = 1.5                 # d3[r] = relu(1.5 d2[a3] - 0.1)
+    pf = rng.permutation(176)
+    af = np.concatenate([pf[:40], 128 + rng.permutation(48)[:24]])  # 24 rows start in att
+    cf = rng.permutation(176)[:64]
+    cf = np.where(cf == af, (cf + 1) % 176, cf)
+    tw.wf = np.zeros((64, 176)); tw.bf = np.full(64, 0.05)
+    tw.wf[np.arange(64), af] = 1.0                   # f[r] = relu(0.05 + z[af] - z[cf])
+    tw.wf[np.arange(64), cf] = -1.0
+    tw.wo = rng.uniform(-1.0, 1.0, 64); tw.bo = 0.25
+    d1 = np.concatenate([x[:, p1], np.maximum(0.5 - x[:, p1], 0.0)], axis=1)
+    d2 = np.maximum(0.3 + d1[:, a2] - 2.0 * d1[:, c2], 0.0)
+    d3 = np.maximum(1.5 * d2[:, a3] - 0.1, 0.0)
+    z = np.concatenate([d3, att], axis=1)
+    f = np.maximum(0.05 + z[:, af] - z[:, cf], 0.0)
+    logit = (f * tw.wo[None, :]).sum(axis=1) + tw.bo
+    return tw, x, att, d3, logit
+
+
+def pin_towers_closed_forms(orc):
+    rng = np.random.default_rng(11)
+    tw, x, att, d3, logit = _sparse_towers(rng, 40)
+    assert np.mean(d3 == 0.0) > 0.05 and np.mean(d3 > 0.0) > 0.3   # the ReLUs clip
+    deep, lg, pr = orc.towers(x, att, tw)
+    assert _rel(deep, d3) < 1e-14
+    assert _rel(lg, logit) < 1e-14
+    assert np.max(np.abs(lg - logit)) < 1e-13
+    # the logit goes through the logistic function: exact special values
+    z = synth.Towers(np.zeros((512, 256)), np.zeros(512), np.zeros((256, 512)), np.zeros(256),
+                     np.zeros((128, 256)), np.zeros(128), np.zeros((64, 176)), np.zeros(64),
+                     np.ones(64), 0.0)
+    for bo, want in ((0.0, 0.5), (np.log(3.0), 0.75), (-np.log(3.0), 0.25), (np.log(9.0), 0.9)):
+        z.bo = float(bo)
+        _, lg0, pr0 = orc.towers(x[:3], att[:3], z)
+        assert np.all(lg0 == bo) and np.all(np.abs(pr0 - want) < 1e-15), (bo, pr0)
+    # zero weights: every layer passes only its ReLU'd bias
+    z.bd1 = rng.uniform(-1, 1, 512); z.bd3 = rng.uniform(-1, 1, 128)
+    z.bf = rng.uniform(-1, 1, 64); z.wo = rng.uniform(-1, 1, 64); z.bo = 0.125
+    deep0, lg0, _ = orc.towers(x[:2], att[:2], z)
+    assert np.array_equal(deep0, np.broadcast_to(np.maximum(z.bd3, 0.0), (2, 128)))
+    assert np.all(np.abs(lg0 - (0.125 + np.dot(z.wo, np.maximum(z.bf, 0.0)))) < 1e-15)
+
+
+def pin_towers_library(orc):
+    """torch fp64 Linear/ReLU/sigmoid on the generator's weights; positive
+    homogeneity without biases; rows are independent."""
+    m, b = _tiny(bias=True, B=48, emb_std=1.0)
+    tw = m.towers
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((48, 256)) * 0.5
+    att = rng.standard_normal((48, 48)) * 0.5
+    deep, lg, pr = orc.towers(x, att, tw)
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    h = F.relu(F.linear(t(x), t(tw.wd1), t(tw.bd1)))
+    h = F.relu(F.linear(h, t(tw.wd2), t(tw.bd2)))
+    d3 = F.relu(F.linear(h, t(tw.wd3), t(tw.bd3)))
+    f = F.relu(F.linear(torch.cat([d3, t(att)], dim=1), t(tw.wf), t(tw.bf)))
+    rl = F.linear(f, t(tw.wo)[None, :]).squeeze(1) + tw.bo
+    assert _rel(deep, d3.numpy()) < 1e-12
+    assert _rel(lg, rl.numpy()) < 1e-12
+    assert np.max(np.abs(pr - torch.sigmoid(rl).numpy())) < 1e-14
+    # no biases: f(2x) = 2 f(x) (ReLU nets are positively homogeneous)
+    nb = synth.Towers(tw.wd1, np.zeros(512), tw.wd2, np.zeros(256), tw.wd3, np.zeros(128),
+                      tw.wf, np.zeros(64), tw.wo, 0.0)
+    d_a, l_a, _ = orc.towers(x, att, nb)
+    d_b, l_b, _ = orc.towers(2.0 * x, 2.0 * att, nb)
+    assert _rel(d_b, 2.0 * d_a) < 1e-14 and _rel(l_b, 2.0 * l_a) < 1e-14
+    assert _rel(d_a, deep) > 1e-3                      # the biases do matter
+    sub = np.array([9, 0, 31])
+    d_s, l_s, _ = orc.towers(x[sub], att[sub], tw)
+    assert np.array_equal(d_s, deep[sub]) and np.array_equal(l_s, lg[sub])
+
+
 ALL_PINS = [pin_offsets, pin_floor_mod, pin_hash, pin_embbag_direct, pin_embbag_hash,
-            pin_din_vs_padded, pin_din_closed_forms, pin_din_hash]
+            pin_din_vs_padded, pin_din_closed_forms, pin_din_hash, pin_towers_closed_forms,
+            pin_towers_library]

@@ -43,6 +43,20 @@ MUTANTS = [
      "int64_t raw = seq_values[f * seq_stride + seq_offsets[b] + (j > 0 ? j - 1 : 0)];"),
     ("weighted sum uses x not s", "out[c] += p * sj[j * 48 + c];", "out[c] += p * x[c];"),
     ("weights not normalised", "double p = exp(e[j] - m) / den;", "double p = exp(e[j] - m);"),
+    ("tower layers without ReLU", "out[o] = acc > 0.0 ? acc : 0.0;", "out[o] = acc;"),
+    ("tower weights read transposed", "acc += W[(int64_t)o * nin + i] * in[i];",
+     "acc += W[(int64_t)i * nout + o] * in[i];"),
+    ("tower biases dropped", "double acc = bias[o];", "double acc = 0.0;"),
+    ("deep rows read at stride 256", "pooled + s * ld, 256, 512, d1);",
+     "pooled + s * 256, 256, 512, d1);"),
+    ("attention output left out of the concat", "z[128 + c] = att[s * 48 + c];",
+     "z[128 + c] = 0.0;"),
+    ("attention written over the deep output", "z[128 + c] = att[s * 48 + c];",
+     "z[c] = att[s * 48 + c];"),
+    ("logit bias dropped", "double lg = bo;", "double lg = 0.0;"),
+    ("logistic sign flipped", "prob[s] = 1.0 / (1.0 + exp(-lg));", "prob[s] = 1.0 / (1.0 + exp(lg));"),
+    ("deep tower skips its last layer", "orc_layer(wd3, bd3, d2, 256, 128, z);",
+     "for (int c = 0; c < 128; ++c) z[c] = d2[c];"),
 ]
 
 
