@@ -63,6 +63,7 @@ enum { REC_F32 = 0, REC_BF16 = 1, REC_BF16_PACKED = 2 };   /* rec_din_mlp.dtype 
 #define REC_MAX_SEQ_LEN 128               /* largest max_len for the DIN call */
 #define REC_MAX_B 16777215                /* largest batch for the DIN plan */
 #define REC_DIN_PACKED_BYTES 131072       /* packed bf16 W1+W2 (rec_din_pack_mlp) */
+#define REC_TOWER_PACKED_BYTES 614400     /* packed bf16 tower weights (rec_tower_pack_mlp) */
 
 /*
  * One embedding table (host struct; the arrays inside are device memory).
@@ -346,6 +347,71 @@ size_t rec_sparse_din_fwd_workspace_bytes(int32_t T, int64_t B, int32_t max_len)
  * REC_EINVAL (args or workspace NULL or misaligned) and REC_EWORKSPACE.
  * B == 0 is a no-op. */
 rec_status rec_sparse_din_fwd(const rec_fwd_args* args, void* stream);
+
+/*
+ * The rest of the MultiTowerDIN forward after the sparse part: the deep tower
+ * and the final MLP ("当前现状分析" §4.4 compute graph: deep MLP
+ * 512 -> 256 -> 128 over the pooled deep features, concat with the [B,48]
+ * attention output into [B,176], final MLP 176 -> 64 -> 1; "集成 DynamicEmb"
+ * §7 model config: tower hidden units [512, 256, 128], final [64], binary
+ * cross entropy, so the last unit is a logit):
+ *   d1 = relu(wd1 x + bd1)   x = pooled[b][0..255]       wd1 [512][256]
+ *   d2 = relu(wd2 d1 + bd2)                              wd2 [256][512]
+ *   d3 = relu(wd3 d2 + bd3)  -> deep_out[b]              wd3 [128][256]
+ *   f  = relu(wf [d3, att[b]] + bf)                      wf  [64][176]
+ *   logit[b] = wo . f + bo;  prob[b] = 1 / (1 + exp(-logit[b]))
+ * Matrices are output-major (torch.nn.Linear.weight), dtype `dtype`; biases
+ * and wo are fp32; bo is a host float.  In the concat the deep output comes
+ * first (wf columns 0-127), then att (columns 128-175).
+ * dtype REC_BF16: the inputs (pooled, att) and every hidden activation are
+ * rounded to bf16 (nearest even) and multiplied on the matrix cores with
+ * fp32 accumulation; biases, the 64 -> 1 logit and the logistic are fp32;
+ * deep_out is d3 before its bf16 rounding.  dtype REC_F32: fp32 throughout.
+ * dtype REC_BF16_PACKED: as REC_BF16, but wd1 points to the
+ * REC_TOWER_PACKED_BYTES image written by rec_tower_pack_mlp (all four
+ * matrices in the order the kernel reads them) and wd2, wd3, wf are not read.
+ * Same results as REC_BF16, several times faster.
+ */
+typedef struct {
+    int32_t dtype;                /* REC_F32, REC_BF16 or REC_BF16_PACKED */
+    int32_t reserved;
+    const void* wd1;
+    const float* bd1;
+    const void* wd2;
+    const float* bd2;
+    const void* wd3;
+    const float* bd3;
+    const void* wf;
+    const float* bf;
+    const float* wo;
+    float bo;
+} rec_tower_mlp;
+
+/*
+ *   mlp       host; every array 16-byte aligned device memory
+ *   pooled    fp32 [B][pooled_ld], pooled_ld >= 256 and a multiple of 4; the
+ *             first 256 columns are the deep input (16 tables x 16)
+ *   att       fp32 [B][48] (rec_din_attn_fwd's output)
+ *   deep_out  fp32 [B][128] or NULL;  logit fp32 [B];  prob fp32 [B] or NULL
+ * pooled, att and deep_out 16-byte aligned.
+ * Errors: REC_EINVAL (null required pointers, bad dtype, misalignment,
+ * pooled_ld, B < 0).  B == 0 is a no-op.
+ */
+rec_status rec_towers_fwd(const rec_tower_mlp* mlp, int64_t B, const float* pooled,
+                          int64_t pooled_ld, const float* att, float* deep_out, float* logit,
+                          float* prob, void* stream);
+
+/*
+ * Pre-pack the bf16 tower matrices once (e.g. at model load): reads wd1,
+ * wd2, wd3 and wf of `mlp` (dtype REC_BF16, plain layout) and writes their
+ * matrix-core operand order into `packed` (device, 16-byte aligned,
+ * >= REC_TOWER_PACKED_BYTES bytes; wf's columns are padded to 192 with
+ * zeros).  Use it with dtype REC_BF16_PACKED.  The values are copied
+ * unchanged.  Errors: REC_EINVAL (null/misaligned pointers, dtype not
+ * REC_BF16), REC_EWORKSPACE (packed_bytes too small).
+ */
+rec_status rec_tower_pack_mlp(const rec_tower_mlp* mlp, void* packed, size_t packed_bytes,
+                              void* stream);
 
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* rec_last_error(void);

@@ -68,7 +68,7 @@ class Oracle:
                               PD, PD, PD, PD, PD, PD, C.c_double, P64, C.c_int64, PD, PD, PD]
         L.orc_din.restype = None
         L.orc_towers.argtypes = [C.c_int64, PD, C.c_int64, PD, PD, PD, PD, PD, PD, PD, PD, PD,
-                                 PD, C.c_double, PD, PD, PD]
+                                 PD, C.c_double, PD, PD, PD, PD]
         L.orc_towers.restype = None
         self._keep = []
 
@@ -166,11 +166,12 @@ class Oracle:
         return att
 
 
-    def towers(self, pooled, att, tw):
+    def towers(self, pooled, att, tw, want_scale=False):
         """Deep tower + final MLP.  pooled: [ns][>=256] (the first 256 columns
         are the deep input), att: [ns][48]; tw has wd1, bd1, wd2, bd2, wd3, bd3,
         wf, bf, wo, bo (values as the GPU receives them).  Returns deep_out
-        [ns][128], logit [ns] and prob [ns], fp64."""
+        [ns][128], logit [ns] and prob [ns], fp64; with want_scale also
+        |bo| + sum_i |wo_i f_i| per sample (the size of the logit's terms)."""
         x = np.ascontiguousarray(pooled, dtype=np.float64)
         a = np.ascontiguousarray(att, dtype=np.float64).reshape(x.shape[0], 48)
         assert x.ndim == 2 and x.shape[1] >= 256
@@ -182,9 +183,12 @@ class Oracle:
         deep = np.empty((ns, 128), dtype=np.float64)
         logit = np.empty(ns, dtype=np.float64)
         prob = np.empty(ns, dtype=np.float64)
+        scale = np.empty(ns, dtype=np.float64)
         self.lib.orc_towers(ns, _ptr(x, PD), x.shape[1], _ptr(a, PD),
                             *[_ptr(v, PD) for v in d], float(tw.bo),
-                            _ptr(deep, PD), _ptr(logit, PD), _ptr(prob, PD))
+                            _ptr(deep, PD), _ptr(logit, PD), _ptr(prob, PD), _ptr(scale, PD))
+        if want_scale:
+            return deep, logit, prob, scale
         return deep, logit, prob
 
 
@@ -226,5 +230,6 @@ def forward(model, batch, samples=None, orc: Optional[Oracle] = None, want_score
     else:
         out["att"] = r
     if towers:
-        out["deep"], out["logit"], out["prob"] = orc.towers(pooled, out["att"], model.towers)
+        out["deep"], out["logit"], out["prob"], out["logit_scale"] = orc.towers(
+            pooled, out["att"], model.towers, want_scale=True)
     return out

@@ -235,7 +235,9 @@ void orc_din(const orc_table* seq_tables /* 3: adgroup, cate, brand */,
  * Readings: ReLU after every hidden layer, none on the logit; biases on every
  * layer; the deep output comes first in the concat (the page's order).
  * pooled has row stride `ld` (>= 256); att is [ns][48]; deep_out [ns][128],
- * logit [ns] and prob [ns] (deep_out and prob may be NULL).               */
+ * logit [ns] and prob [ns] (deep_out and prob may be NULL).  lscale [ns]
+ * (or NULL) receives |bo| + sum_i |wo_i f_i|, the size of the logit's terms:
+ * the yardstick for the error of a logit that cancels to near zero.       */
 static void orc_layer(const double* W, const double* bias, const double* in, int nin,
                       int nout, double* out) {
     for (int o = 0; o < nout; ++o) {
@@ -249,7 +251,7 @@ void orc_towers(int64_t ns, const double* pooled, int64_t ld, const double* att,
                 const double* wd1, const double* bd1, const double* wd2, const double* bd2,
                 const double* wd3, const double* bd3, const double* wf, const double* bf,
                 const double* wo, double bo,
-                double* deep_out, double* logit, double* prob) {
+                double* deep_out, double* logit, double* prob, double* lscale) {
     double d1[512], d2[256], z[176], f[64];
     for (int64_t s = 0; s < ns; ++s) {
         orc_layer(wd1, bd1, pooled + s * ld, 256, 512, d1);
@@ -257,8 +259,12 @@ void orc_towers(int64_t ns, const double* pooled, int64_t ld, const double* att,
         orc_layer(wd3, bd3, d2, 256, 128, z);
         for (int c = 0; c < 48; ++c) z[128 + c] = att[s * 48 + c];
         orc_layer(wf, bf, z, 176, 64, f);
-        double lg = bo;
-        for (int i = 0; i < 64; ++i) lg += wo[i] * f[i];
+        double lg = bo, mag = fabs(bo);
+        for (int i = 0; i < 64; ++i) {
+            lg += wo[i] * f[i];
+            mag += fabs(wo[i] * f[i]);
+        }
+        if (lscale) lscale[s] = mag;
         if (deep_out) for (int c = 0; c < 128; ++c) deep_out[s * 128 + c] = z[c];
         logit[s] = lg;
         if (prob) prob[s] = 1.0 / (1.0 + exp(-lg));

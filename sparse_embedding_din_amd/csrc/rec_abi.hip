@@ -224,6 +224,52 @@ rec_status prep_embbag_kjt(const char* fn, const rec_table* tables, int32_t T, i
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+rec_status prep_towers(const char* fn, const rec_tower_mlp* mlp, int64_t B, const float* pooled,
+                       int64_t pooled_ld, const float* att, float* deep_out, float* logit,
+                       float* prob, TowerArgs* a, bool* work) {
+    const std::string f(fn);
+    *work = false;
+    if (B < 0) return fail(REC_EINVAL, f + ": B < 0");
+    if (!mlp) return fail(REC_EINVAL, f + ": tower mlp is NULL");
+    if (mlp->dtype != REC_F32 && mlp->dtype != REC_BF16 && mlp->dtype != REC_BF16_PACKED)
+        return fail(REC_EINVAL, f + ": tower dtype must be REC_F32, REC_BF16 or REC_BF16_PACKED");
+    const bool packed = mlp->dtype == REC_BF16_PACKED;
+    const void* arrays[] = {mlp->wd1, mlp->bd1, mlp->bd2, mlp->bd3, mlp->bf, mlp->wo,
+                            packed ? mlp->wd1 : mlp->wd2, packed ? mlp->wd1 : mlp->wd3,
+                            packed ? mlp->wd1 : mlp->wf};
+    for (const void* p : arrays) {
+        if (!p) return fail(REC_EINVAL, f + ": tower weights, biases and wo are required");
+        if (!aligned16(p)) return fail(REC_EINVAL, f + ": tower arrays must be 16-byte aligned");
+    }
+    if (!pooled || !att || !logit) return fail(REC_EINVAL, f + ": pooled, att and logit are required");
+    if (pooled_ld < 256 || (pooled_ld & 3))
+        return fail(REC_EINVAL, f + ": pooled_ld must be >= 256 and a multiple of 4");
+    if (!aligned16(pooled) || !aligned16(att) || (deep_out && !aligned16(deep_out)))
+        return fail(REC_EINVAL, f + ": pooled, att and deep_out must be 16-byte aligned");
+    if ((B + kTowerSamples - 1) / kTowerSamples > 2147483647LL)
+        return fail(REC_EUNSUPPORTED, f + ": B too large for one launch");
+    a->w[0] = mlp->wd1;
+    a->w[1] = mlp->wd2;
+    a->w[2] = mlp->wd3;
+    a->w[3] = mlp->wf;
+    a->b[0] = mlp->bd1;
+    a->b[1] = mlp->bd2;
+    a->b[2] = mlp->bd3;
+    a->b[3] = mlp->bf;
+    a->wo = mlp->wo;
+    a->bo = mlp->bo;
+    a->dtype = mlp->dtype;
+    a->pooled = pooled;
+    a->pooled_ld = pooled_ld;
+    a->att = att;
+    a->deep_out = deep_out;
+    a->logit = logit;
+    a->prob = prob;
+    a->B = B;
+    *work = B > 0;
+    return REC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -447,6 +493,35 @@ rec_status rec_sparse_din_fwd(const rec_fwd_args* x, void* stream) {
     hipError_t h = launch_fwd_front(p, e, (hipStream_t)stream);
     if (h == hipSuccess) h = launch_din(d, (hipStream_t)stream);
     return hip_status(h, fn);
+}
+
+rec_status rec_tower_pack_mlp(const rec_tower_mlp* mlp, void* packed, size_t packed_bytes,
+                              void* stream) {
+    const char* fn = "rec_tower_pack_mlp";
+    if (!mlp) return fail(REC_EINVAL, std::string(fn) + ": mlp is NULL");
+    if (mlp->dtype != REC_BF16) return fail(REC_EINVAL, std::string(fn) + ": dtype must be REC_BF16");
+    const void* w[4] = {mlp->wd1, mlp->wd2, mlp->wd3, mlp->wf};
+    for (const void* p : w)
+        if (!p) return fail(REC_EINVAL, std::string(fn) + ": wd1, wd2, wd3 and wf are required");
+    if (!packed) return fail(REC_EINVAL, std::string(fn) + ": packed is NULL");
+    for (const void* p : w)
+        if (!aligned16(p)) return fail(REC_EINVAL, std::string(fn) + ": pointers must be 16-byte aligned");
+    if (!aligned16(packed)) return fail(REC_EINVAL, std::string(fn) + ": pointers must be 16-byte aligned");
+    if (packed_bytes < REC_TOWER_PACKED_BYTES)
+        return fail(REC_EWORKSPACE, std::string(fn) + ": packed smaller than REC_TOWER_PACKED_BYTES");
+    return hip_status(launch_tower_pack(w, packed, (hipStream_t)stream), fn);
+}
+
+rec_status rec_towers_fwd(const rec_tower_mlp* mlp, int64_t B, const float* pooled,
+                          int64_t pooled_ld, const float* att, float* deep_out, float* logit,
+                          float* prob, void* stream) {
+    TowerArgs a;
+    bool work;
+    rec_status s = prep_towers("rec_towers_fwd", mlp, B, pooled, pooled_ld, att, deep_out, logit,
+                               prob, &a, &work);
+    if (s != REC_OK) return s;
+    if (!work) return ok();
+    return hip_status(launch_towers(a, (hipStream_t)stream), "rec_towers_fwd");
 }
 
 }  // extern "C"

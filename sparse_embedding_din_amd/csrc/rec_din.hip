@@ -36,12 +36,10 @@
 // features, and the weights are permuted to the same order (rec_din_pack_mlp,
 // or on chip for unpacked weights).
 #include "rec_internal.h"
+#include "rec_mfma.h"
 
 namespace rec {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct Sub {
     float q[12];     // as loaded until masked (mask_sub)
@@ -251,20 +249,6 @@ __device__ inline float score_from_h2(const f32x4 (&acc2)[4], const float* w3s, 
     return p + b3;
 }
 
-// max(RNE(a), 0), max(RNE(b), 0) as a bf16 pair.  Rounding to nearest keeps
-// the sign, so ReLU after rounding equals rounding after ReLU; on the bit
-// patterns a negative bf16 (or -0) is a negative int16, so the ReLU is one
-// packed integer max for two values.
-typedef short s16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ inline uint32_t relu_pk_bf16(float a, float b) {
-    bf16x2 p;
-    p[0] = (__bf16)a;
-    p[1] = (__bf16)b;
-    s16x2 v = __builtin_bit_cast(s16x2, p);
-    v = __builtin_elementwise_max(v, (s16x2){0, 0});
-    return __builtin_bit_cast(uint32_t, v);
-}
 
 // Layer 1 for one hidden block: two 16-row tiles x NSUB position tiles, the
 // K loop (6 steps of 32) innermost in issue order so 2*NSUB independent

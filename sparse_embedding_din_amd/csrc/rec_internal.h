@@ -345,4 +345,25 @@ hipError_t launch_fwd_front(const PlanArgs& p, const EmbArgs& e, hipStream_t s);
 hipError_t launch_din(const DinArgs& a, hipStream_t s);
 hipError_t launch_din_pack(const void* w1, const void* w2, void* packed, hipStream_t s);
 
+// Deep tower + final MLP (rec_tower.hip).  Layers 0-2 are the deep tower
+// 256 -> 512 -> 256 -> 128, layer 3 the final hidden layer 176 -> 64; wo/bo
+// the 64 -> 1 logit.
+struct TowerArgs {
+    const void* w[4];
+    const float* b[4];
+    const float* wo;
+    float bo;
+    int32_t dtype;
+    const float* pooled;
+    int64_t pooled_ld;
+    const float* att;
+    float* deep_out;
+    float* logit;
+    float* prob;
+    int64_t B;
+};
+constexpr int kTowerSamples = 32;            // samples per workgroup
+hipError_t launch_towers(const TowerArgs& a, hipStream_t s);
+hipError_t launch_tower_pack(const void* const w[4], void* packed, hipStream_t s);
+
 }  // namespace rec

@@ -85,6 +85,35 @@ class DeviceMLP:
             self.desc = R.din_mlp(self.dtype, self.packed, self.b1, None, self.b2, self.w3, self.b3)
 
 
+class DeviceTowers:
+    """Deep-tower and final-MLP weights on the device (plain nn.Linear layout;
+    bf16 bit patterns for a bf16 model, pre-packed once with
+    rec_tower_pack_mlp unless packed=False)."""
+
+    def __init__(self, towers, device, dtype: str = "bf16", packed: bool = True):
+        if dtype == "bf16":
+            self.dtype = R.REC_BF16
+            mats = [_to(np.asarray(towers.bits[k]).view(np.int16), device)
+                    for k in ("wd1", "wd2", "wd3", "wf")]
+        else:
+            self.dtype = R.REC_F32
+            mats = [_to(np.asarray(getattr(towers, k), np.float32), device)
+                    for k in ("wd1", "wd2", "wd3", "wf")]
+        self.wd1, self.wd2, self.wd3, self.wf = mats
+        self.bd1, self.bd2, self.bd3, self.bf, self.wo = [
+            _to(np.asarray(getattr(towers, k), np.float32), device)
+            for k in ("bd1", "bd2", "bd3", "bf", "wo")]
+        self.bo = float(towers.bo)
+        self.desc = R.tower_mlp(self.dtype, self.wd1, self.bd1, self.wd2, self.bd2, self.wd3,
+                                self.bd3, self.wf, self.bf, self.wo, self.bo)
+        if self.dtype == R.REC_BF16 and packed:
+            self.packed = torch.empty(R.REC_TOWER_PACKED_BYTES, dtype=torch.uint8, device=device)
+            R.rec_tower_pack_mlp(self.desc, self.packed, R.REC_TOWER_PACKED_BYTES)
+            self.dtype = R.REC_BF16_PACKED
+            self.desc = R.tower_mlp(self.dtype, self.packed, self.bd1, None, self.bd2, None,
+                                    self.bd3, None, self.bf, self.wo, self.bo)
+
+
 class DeviceBatch:
     def __init__(self, batch, device, seq_values=None, seq_offsets=None, seq_stride=None):
         self.B = int(batch.B)
@@ -103,8 +132,10 @@ class SparseDinForward:
     """Buffers for batches of up to B_max samples and the four-call forward."""
 
     def __init__(self, tables: DeviceTables, mlp: DeviceMLP, B_max: int, max_len: int = 100,
-                 device="cuda", range_positions: int = 0, T: int = 16, fused: bool = True):
+                 device="cuda", range_positions: int = 0, T: int = 16, fused: bool = True,
+                 towers: Optional[DeviceTowers] = None):
         self.T = T
+        self.towers = towers
         self.fused = fused
         self.tables = tables
         self.mlp = mlp
@@ -126,6 +157,10 @@ class SparseDinForward:
         self.fwd_ws_bytes = R.rec_sparse_din_fwd_workspace_bytes(T, B_max, max_len)
         self.fwd_ws = torch.empty(max(self.fwd_ws_bytes, 16), dtype=torch.uint8, device=device)
         self.att = torch.empty(B_max, 48, dtype=torch.float32, device=device)
+        if towers is not None:
+            self.deep = torch.empty(B_max, 128, dtype=torch.float32, device=device)
+            self.logit = torch.empty(B_max, dtype=torch.float32, device=device)
+            self.prob = torch.empty(B_max, dtype=torch.float32, device=device)
 
     # the four steps, each one C-ABI call
     def offsets_step(self, b: DeviceBatch, stream=None):
@@ -153,6 +188,10 @@ class SparseDinForward:
                            self.pooled, self.T * 16, self.query_col, self.mlp.desc, self.att,
                            scores, weights, stream)
 
+    def tower_step(self, b: DeviceBatch, stream=None):
+        R.rec_towers_fwd(self.towers.desc, b.B, self.pooled, self.T * 16, self.att, self.logit,
+                         deep_out=self.deep, prob=self.prob, stream=stream)
+
     def whole_args(self, b: DeviceBatch, debug: Optional[dict] = None) -> R.rec_fwd_args:
         """The rec_fwd_args of a batch."""
         d = debug or {}
@@ -168,6 +207,8 @@ class SparseDinForward:
         """The forward as one rec_sparse_din_fwd call."""
         assert b.B <= self.B_max
         R.rec_sparse_din_fwd(self.whole_args(b, debug), stream)
+        if self.towers is not None:
+            self.tower_step(b, stream)
         return self.pooled[: b.B], self.att[: b.B]
 
     def run(self, b: DeviceBatch, stream=None, debug: Optional[dict] = None, side=None):
@@ -185,9 +226,13 @@ class SparseDinForward:
             self.embbag_step(b, d.get("emb_rows"))
             main.wait_stream(side)
             self.din_step(b, d.get("scores"), d.get("weights"))
+            if self.towers is not None:
+                self.tower_step(b)
             return self.pooled[: b.B], self.att[: b.B]
         self.offsets_step(b, stream)
         self.plan_step(b, d.get("seq_rows"), stream)
         self.embbag_step(b, d.get("emb_rows"), stream)
         self.din_step(b, d.get("scores"), d.get("weights"), stream)
+        if self.towers is not None:
+            self.tower_step(b, stream)
         return self.pooled[: b.B], self.att[: b.B]

@@ -19,6 +19,7 @@ REC_OK, REC_EINVAL, REC_EUNSUPPORTED, REC_EHIP, REC_EWORKSPACE = 0, -1, -2, -3, 
 REC_DIRECT, REC_HASH = 0, 1
 REC_F32, REC_BF16, REC_BF16_PACKED = 0, 1, 2
 REC_DIN_PACKED_BYTES = 131072
+REC_TOWER_PACKED_BYTES = 614400
 REC_DIM = 16
 REC_EMPTY_KEY = -1
 REC_MAX_TABLES = 32
@@ -28,7 +29,8 @@ REC_MAX_B = 16777215
 EXPORTS = ["rec_din_pack_mlp", "rec_scan_workspace_bytes", "rec_lengths_to_offsets", "rec_embbag_fwd",
            "rec_kjt_sums_bytes", "rec_kjt_sums", "rec_embbag_fwd_kjt", "rec_hash_lookup",
            "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_fwd",
-           "rec_sparse_din_fwd_workspace_bytes", "rec_sparse_din_fwd",
+           "rec_sparse_din_fwd_workspace_bytes", "rec_sparse_din_fwd", "rec_towers_fwd",
+           "rec_tower_pack_mlp",
            "rec_last_error", "rec_version", "rec_host_floor_mod", "rec_host_hash_home",
            "rec_host_hash_probe"]
 
@@ -49,6 +51,13 @@ class rec_din_mlp(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("reserved", C.c_int32), ("w1", C.c_void_p),
                 ("b1", C.c_void_p), ("w2", C.c_void_p), ("b2", C.c_void_p),
                 ("w3", C.c_void_p), ("b3", C.c_float)]
+
+
+class rec_tower_mlp(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("reserved", C.c_int32),
+                ("wd1", C.c_void_p), ("bd1", C.c_void_p), ("wd2", C.c_void_p), ("bd2", C.c_void_p),
+                ("wd3", C.c_void_p), ("bd3", C.c_void_p), ("wf", C.c_void_p), ("bf", C.c_void_p),
+                ("wo", C.c_void_p), ("bo", C.c_float)]
 
 
 class rec_fwd_args(C.Structure):
@@ -95,9 +104,12 @@ def lib():
         L.rec_sparse_din_fwd_workspace_bytes.argtypes = [i32, i64, i32]
         L.rec_sparse_din_fwd_workspace_bytes.restype = sz
         L.rec_sparse_din_fwd.argtypes = [C.POINTER(rec_fwd_args), vp]
+        L.rec_towers_fwd.argtypes = [C.POINTER(rec_tower_mlp), i64, vp, i64, vp, vp, vp, vp, vp]
+        L.rec_tower_pack_mlp.argtypes = [C.POINTER(rec_tower_mlp), vp, sz, vp]
         for f in ("rec_lengths_to_offsets", "rec_embbag_fwd", "rec_kjt_sums", "rec_embbag_fwd_kjt",
                   "rec_hash_lookup", "rec_din_plan",
-                  "rec_din_attn_fwd", "rec_din_pack_mlp", "rec_sparse_din_fwd"):
+                  "rec_din_attn_fwd", "rec_din_pack_mlp", "rec_sparse_din_fwd", "rec_towers_fwd",
+                  "rec_tower_pack_mlp"):
             getattr(L, f).restype = C.c_int
         L.rec_last_error.argtypes = []
         L.rec_last_error.restype = C.c_char_p
@@ -144,6 +156,11 @@ def table(kind: int, rows: int, values, keys=None, digests=None, scores=None,
 
 def din_mlp(dtype: int, w1, b1, w2, b2, w3, b3: float) -> rec_din_mlp:
     return rec_din_mlp(dtype, 0, _p(w1), _p(b1), _p(w2), _p(b2), _p(w3), float(b3))
+
+
+def tower_mlp(dtype: int, wd1, bd1, wd2, bd2, wd3, bd3, wf, bf, wo, bo: float) -> rec_tower_mlp:
+    return rec_tower_mlp(dtype, 0, _p(wd1), _p(bd1), _p(wd2), _p(bd2), _p(wd3), _p(bd3), _p(wf),
+                         _p(bf), _p(wo), float(bo))
 
 
 def _tables(tabs):
@@ -227,6 +244,20 @@ def rec_din_attn_fwd(seq_tables: Sequence[rec_table], plan, plan_bytes: int, B: 
                                   C.byref(mlp) if mlp is not None else None, _p(out),
                                   _p(scores_out), _p(weights_out), _stream(stream)),
            "rec_din_attn_fwd")
+
+
+def rec_towers_fwd(mlp: rec_tower_mlp, B: int, pooled, pooled_ld: int, att, logit,
+                   deep_out=None, prob=None, stream=None):
+    _check(lib().rec_towers_fwd(C.byref(mlp) if mlp is not None else None, B, _p(pooled),
+                                pooled_ld, _p(att), _p(deep_out), _p(logit), _p(prob),
+                                _stream(stream)),
+           "rec_towers_fwd")
+
+
+def rec_tower_pack_mlp(mlp: rec_tower_mlp, packed, packed_bytes: int, stream=None):
+    _check(lib().rec_tower_pack_mlp(C.byref(mlp) if mlp is not None else None, _p(packed),
+                                    packed_bytes, _stream(stream)),
+           "rec_tower_pack_mlp")
 
 
 def rec_sparse_din_fwd_workspace_bytes(T: int, B: int, max_len: int) -> int:

@@ -345,6 +345,7 @@ def _sparse_towers(rng, ns):
     z = np.concatenate([d3, att], axis=1)
     f = np.maximum(0.05 + z[:, af] - z[:, cf], 0.0)
     logit = (f * tw.wo[None, :]).sum(axis=1) + tw.bo
+    tw.expected_scale = np.abs(f * tw.wo[None, :]).sum(axis=1) + abs(tw.bo)
     return tw, x, att, d3, logit
 
 
@@ -352,7 +353,8 @@ def pin_towers_closed_forms(orc):
     rng = np.random.default_rng(11)
     tw, x, att, d3, logit = _sparse_towers(rng, 40)
     assert np.mean(d3 == 0.0) > 0.05 and np.mean(d3 > 0.0) > 0.3   # the ReLUs clip
-    deep, lg, pr = orc.towers(x, att, tw)
+    deep, lg, pr, sc = orc.towers(x, att, tw, want_scale=True)
+    assert _rel(sc, tw.expected_scale) < 1e-14
     assert _rel(deep, d3) < 1e-14
     assert _rel(lg, logit) < 1e-14
     assert np.max(np.abs(lg - logit)) < 1e-13

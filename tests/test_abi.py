@@ -268,6 +268,60 @@ def test_whole_forward_errors(lib):
     assert lib.rec_sparse_din_fwd(C.byref(args(B=0, workspace_bytes=zb)), None) == R.REC_OK
 
 
+def test_towers_errors(lib):
+    def mlp(**kw):
+        a = dict(dtype=R.REC_BF16, wd1=FAKE, bd1=FAKE, wd2=FAKE, bd2=FAKE, wd3=FAKE, bd3=FAKE,
+                 wf=FAKE, bf=FAKE, wo=FAKE, bo=0.0)
+        a.update(kw)
+        return R.tower_mlp(**a)
+
+    def call(m=None, B=64, pooled=FAKE, ld=256, att=FAKE, deep=None, logit=FAKE, prob=None):
+        return _status(lib.rec_towers_fwd, C.byref(m if m is not None else mlp()), B, pooled, ld,
+                       att, deep, logit, prob, None)
+    assert lib.rec_towers_fwd(None, 4, FAKE, 256, FAKE, None, FAKE, None, None) == R.REC_EINVAL
+    assert call(mlp(dtype=7))[0] == R.REC_EINVAL
+    # a packed image replaces wd2, wd3 and wf: they may be NULL then
+    pk = mlp(dtype=R.REC_BF16_PACKED, wd2=None, wd3=None, wf=None)
+    assert call(pk, B=0)[0] == R.REC_OK
+    assert call(mlp(dtype=R.REC_BF16_PACKED, wd1=None), B=0)[0] == R.REC_EINVAL
+    assert call(mlp(dtype=R.REC_BF16_PACKED, wd1=FAKE_ODD), B=0)[0] == R.REC_EINVAL
+    for k in ("wd1", "bd1", "wd2", "bd2", "wd3", "bd3", "wf", "bf", "wo"):
+        assert call(mlp(**{k: None}))[0] == R.REC_EINVAL, k
+        s, msg = call(mlp(**{k: FAKE_ODD}))
+        assert s == R.REC_EINVAL and "aligned" in msg, k
+    assert call(B=-1)[0] == R.REC_EINVAL
+    assert call(pooled=None)[0] == R.REC_EINVAL
+    assert call(att=None)[0] == R.REC_EINVAL
+    assert call(logit=None)[0] == R.REC_EINVAL
+    assert call(ld=255)[0] == R.REC_EINVAL
+    assert call(ld=258)[0] == R.REC_EINVAL
+    assert call(pooled=FAKE_ODD)[0] == R.REC_EINVAL
+    assert call(att=FAKE_ODD)[0] == R.REC_EINVAL
+    s, msg = call(deep=FAKE_ODD)
+    assert s == R.REC_EINVAL and "rec_towers_fwd" in msg
+    assert call(B=0)[0] == R.REC_OK
+    assert call(m=mlp(dtype=R.REC_F32), B=0)[0] == R.REC_OK
+
+
+def test_tower_pack_errors(lib):
+    def m(**kw):
+        a = dict(dtype=R.REC_BF16, wd1=FAKE, bd1=FAKE, wd2=FAKE, bd2=FAKE, wd3=FAKE, bd3=FAKE,
+                 wf=FAKE, bf=FAKE, wo=FAKE, bo=0.0)
+        a.update(kw)
+        return C.byref(R.tower_mlp(**a))
+    n = R.REC_TOWER_PACKED_BYTES
+    assert lib.rec_tower_pack_mlp(None, FAKE, n, None) == R.REC_EINVAL
+    assert lib.rec_tower_pack_mlp(m(dtype=R.REC_F32), FAKE, n, None) == R.REC_EINVAL
+    assert lib.rec_tower_pack_mlp(m(dtype=R.REC_BF16_PACKED), FAKE, n, None) == R.REC_EINVAL
+    for k in ("wd1", "wd2", "wd3", "wf"):
+        assert lib.rec_tower_pack_mlp(m(**{k: None}), FAKE, n, None) == R.REC_EINVAL, k
+        assert lib.rec_tower_pack_mlp(m(**{k: FAKE_ODD}), FAKE, n, None) == R.REC_EINVAL, k
+    assert lib.rec_tower_pack_mlp(m(), None, n, None) == R.REC_EINVAL
+    assert lib.rec_tower_pack_mlp(m(), FAKE_ODD, n, None) == R.REC_EINVAL
+    s, msg = _status(lib.rec_tower_pack_mlp, m(), FAKE, n - 16, None)
+    assert s == R.REC_EWORKSPACE and "REC_TOWER_PACKED_BYTES" in msg
+
+
 def test_binding_raises_with_message(lib):
     with pytest.raises(R.RecError) as ei:
         R.rec_hash_lookup(_table(), FAKE, 4, FAKE)

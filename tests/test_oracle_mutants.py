@@ -53,7 +53,8 @@ MUTANTS = [
      "z[128 + c] = 0.0;"),
     ("attention written over the deep output", "z[128 + c] = att[s * 48 + c];",
      "z[c] = att[s * 48 + c];"),
-    ("logit bias dropped", "double lg = bo;", "double lg = 0.0;"),
+    ("logit bias dropped", "double lg = bo, mag", "double lg = 0.0, mag"),
+    ("logit scale drops the bias", "mag = fabs(bo);", "mag = 0.0;"),
     ("logistic sign flipped", "prob[s] = 1.0 / (1.0 + exp(-lg));", "prob[s] = 1.0 / (1.0 + exp(lg));"),
     ("deep tower skips its last layer", "orc_layer(wd3, bd3, d2, 256, 128, z);",
      "for (int c = 0; c < 128; ++c) z[c] = d2[c];"),
