@@ -5,7 +5,9 @@ MI355X, on seeded synthetic Taobao-shaped inputs.
 A step is one pass of the whole path over one batch already resident in HBM:
 lengths -> offsets, sequence plan, sum-pooled embedding bags (16 tables,
 3.14M rows), padding-free DIN attention (bf16 matrix cores, fp32 accumulate),
-made as one rec_sparse_din_fwd call (four kernel launches).
+made as one rec_sparse_din_fwd call (four kernel launches).  The rest of the
+MultiTowerDIN forward (deep tower + final MLP, rec_towers_fwd) is timed
+beside it and reported under "towers"; it is not part of the timed step.
 Four resident batches rotate (so the L2 does not keep one batch's rows); one
 HIP graph holds a step for each of them and is replayed.  Everything runs on
 one stream: inside a graph, a fork/join to a second stream costs more than
@@ -39,6 +41,8 @@ DIN_BYTES_PER_POS = 3 * (8 + 64)           # three ids + three rows
 DIN_BYTES_PER_SAMPLE = 4 + 8 + 4 + 192 + 192   # length, offset, packed start, query, output
 DIN_BYTES_WEIGHTS = 256 * 192 * 2 + 64 * 256 * 2 + (256 + 64 + 64) * 4
 DIN_FLOPS_PER_POS = 2 * (192 * 256 + 256 * 64 + 64)
+TOWER_FLOPS_PER_SAMPLE = 2 * (256 * 512 + 512 * 256 + 256 * 128 + 176 * 64 + 64)
+TOWER_WEIGHT_BYTES = 2 * (256 * 512 + 512 * 256 + 256 * 128 + 176 * 64)
 
 
 def parse():
@@ -58,6 +62,8 @@ def parse():
                    help="run the sequence plan on a second stream (pays off when the plan is long, "
                         "e.g. hash-table sequence ids)")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-towers", action="store_true",
+                   help="skip the deep tower + final MLP measurement")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run a plain 64 MiB elementwise copy (for counter scaling)")
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -77,7 +83,7 @@ def src_hash() -> str:
 CAL_BYTES = 64 << 20            # bytes read (and written) by the calibration copy
 KERNELS = {"k_din_attn": "k_din_attn", "k_din_finalize": "k_din_finalize",
            "k_embbag_fwd": "k_embbag_fwd<", "k_fwd_gather": "k_fwd_gather", "k_fwd_sums": "k_fwd_sums",
-           "copy": "MulFunctor"}
+           "k_towers_bf16": "k_towers_bf16", "copy": "MulFunctor"}
 
 
 def load_traffic(kernels, shash: str, config: str):
@@ -169,6 +175,16 @@ def main():
     fwds = [PL.SparseDinForward(tabs, mlp, B, cfg.max_len, dev, range_positions=a.range_positions)
             for _ in dbs]
     nb = len(dbs)
+    tw = None if a.no_towers else PL.DeviceTowers(model.towers, dev)
+    if tw is not None:
+        tw_deep = torch.empty(B, 128, dtype=torch.float32, device=dev)
+        tw_logit = torch.empty(B, dtype=torch.float32, device=dev)
+        tw_prob = torch.empty(B, dtype=torch.float32, device=dev)
+
+    def towers_call(f, db):
+        R.rec_towers_fwd(tw.desc, db.B, f.pooled, f.T * 16, f.att, tw_logit, deep_out=tw_deep,
+                         prob=tw_prob)
+
     stream = torch.cuda.Stream()
     side = torch.cuda.Stream() if a.side_stream else None
     def step(f, db):
@@ -229,6 +245,8 @@ def main():
         "embbag": lambda f, db: f.embbag_step(db),
         "din": lambda f, db: f.din_step(db),
     }
+    if tw is not None:
+        calls["towers"] = towers_call
     reps = a.kernel_reps
     kern_us = {}
     with torch.cuda.stream(stream):
@@ -275,6 +293,45 @@ def main():
                 "per_launch": {"bytes": emb_bytes, "ids": nnz, "bags": synth.T * B},
                 "avg_launch_us": round(kern_us["embbag"]["mean"], 3)}
 
+    # The whole MultiTowerDIN forward (sparse step + towers), graph-replayed
+    # the same way, for the record; `value` stays the sparse step.
+    towers = None
+    if tw is not None:
+        full_ms = None
+        if graph is not None:
+            g2 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g2, stream=stream):
+                for f, db in zip(fwds, dbs):
+                    step(f, db)
+                    towers_call(f, db)
+            with torch.cuda.stream(stream):
+                for _ in range(a.warmup // nb):
+                    g2.replay()
+                torch.cuda.synchronize()
+                f0 = torch.cuda.Event(enable_timing=True)
+                f1 = torch.cuda.Event(enable_timing=True)
+                f0.record(stream)
+                for _ in range(a.steps // nb):
+                    g2.replay()
+                f1.record(stream)
+                torch.cuda.synchronize()
+            full_ms = f0.elapsed_time(f1) / a.steps
+        tt = kern_us["towers"]["mean"] * 1e-6
+        # workgroups of the launch: 32 samples each, 64 from 16384 samples on
+        tower_groups = (B + 31) // 32 if B < 16384 else (B + 63) // 64
+        tflops = TOWER_FLOPS_PER_SAMPLE * B / tt / 1e12
+        towers = {"entry": "rec_towers_fwd (deep 256->512->256->128, concat att, 176->64->1)",
+                  "avg_launch_us": round(kern_us["towers"]["mean"], 3),
+                  "flops_per_launch": TOWER_FLOPS_PER_SAMPLE * B,
+                  "achieved_tflops": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                  "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                  "weight_stream_tb_s": round(TOWER_WEIGHT_BYTES * tower_groups / tt / 1e12, 2),
+                  "bound": f"L2 -> CU weight stream: each workgroup of {B // tower_groups} samples "
+                           f"reads all {TOWER_WEIGHT_BYTES // 1024} KiB of bf16 weights",
+                  "traffic": load_traffic(["k_towers_bf16"], shash, cfg.name),
+                  "full_forward_ms_per_step": None if full_ms is None else round(full_ms, 5),
+                  "full_forward_samples_s": None if full_ms is None else round(B / (full_ms * 1e-3), 1)}
+
     cpu = None
     if not a.no_cpu:
         import oracle
@@ -318,6 +375,7 @@ def main():
         "embbag": {"gb_s": round(emb_gbs, 1), "hbm_frac": round(emb_gbs / HBM_PEAK_GBS, 4)},
         "din": {"tflops": round(din_tflops, 2), "mfma_frac": round(din_tflops / peak_mfma, 4),
                 "gb_s": round(din_bytes / din_t / 1e9, 1)},
+        "towers": towers,
         "src_hash": shash,
     }
     if a.calibrate_copy:
