@@ -5,7 +5,7 @@ MI355X, on seeded synthetic Taobao-shaped inputs.
 A step is one pass of the whole path over one batch already resident in HBM:
 lengths -> offsets, sequence plan, sum-pooled embedding bags (16 tables,
 3.14M rows), padding-free DIN attention (bf16 matrix cores, fp32 accumulate),
-made as one rec_sparse_din_fwd call (four kernel launches).  The rest of the
+made as one rec_sparse_din_fwd call (three kernel launches).  The rest of the
 MultiTowerDIN forward (deep tower + final MLP, rec_towers_fwd) is timed
 beside it and reported under "towers"; it is not part of the timed step.
 Four resident batches rotate (so the L2 does not keep one batch's rows); one
@@ -81,7 +81,7 @@ def src_hash() -> str:
 
 
 CAL_BYTES = 64 << 20            # bytes read (and written) by the calibration copy
-KERNELS = {"k_din_attn": "k_din_attn", "k_din_finalize": "k_din_finalize",
+KERNELS = {"k_din_attn": "k_din_attn",
            "k_embbag_fwd": "k_embbag_fwd<", "k_fwd_gather": "k_fwd_gather", "k_fwd_sums": "k_fwd_sums",
            "k_towers_bf16": "k_towers_bf16", "copy": "MulFunctor"}
 
@@ -280,10 +280,10 @@ def main():
     din_tflops = din_flops / din_t / 1e12
     shash = src_hash()
     if din_t >= emb_t:
-        roof = {"kernel": "rec_din_attn_fwd = k_din_attn + k_din_finalize", "bound": "mfma",
+        roof = {"kernel": "rec_din_attn_fwd (k_din_attn)", "bound": "mfma",
                 "achieved": round(din_tflops, 2),
                 "peak": peak_mfma, "unit": "TFLOP/s", "frac": round(din_tflops / peak_mfma, 4),
-                "traffic": load_traffic(["k_din_attn", "k_din_finalize"], shash, cfg.name),
+                "traffic": load_traffic(["k_din_attn"], shash, cfg.name),
                 "per_launch": {"flops": din_flops, "bytes": din_bytes, "positions": P, "samples": B},
                 "avg_launch_us": round(kern_us["din"]["mean"], 3)}
     else:

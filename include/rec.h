@@ -283,11 +283,10 @@ rec_status rec_din_plan(const rec_table* seq_tables, const int64_t* seq_values,
  *   p_j = softmax over j < L_b of e_j (max-subtracted, no temperature)
  *   out[b][0..48) = sum_j p_j s_j;  L_b == 0 gives 48 x +0.0
  * Positions past L_b are never read, so any sequence layout with the same
- * lengths gives bit-identical output.  A sample cut by a range edge is merged
- * from per-range partial sums, so a different range_positions may change the
- * last bits of its output (not of scores_out).
- * The plan's partial-sum area is written: calls that share a plan must not
- * overlap.
+ * lengths gives bit-identical output.  A sample whose positions the kernel
+ * splits between two waves is merged from their partial sums, so a different
+ * range_positions (or a device with another number of CUs) may change the
+ * last bits of its output (not of scores_out).  The plan is only read.
  *   seq_tables  host array of 3 descriptors (the same as for the plan)
  *   mlp         host struct (device arrays inside)
  *   out         fp32 [B][48], 16-byte aligned
@@ -299,7 +298,7 @@ rec_status rec_din_plan(const rec_table* seq_tables, const int64_t* seq_values,
  * max_len out of range, weights_out without scores_out), REC_EWORKSPACE
  * (plan too small for B, max_len).
  */
-rec_status rec_din_attn_fwd(const rec_table* seq_tables, void* plan, size_t plan_bytes,
+rec_status rec_din_attn_fwd(const rec_table* seq_tables, const void* plan, size_t plan_bytes,
                             int64_t B, int32_t max_len, const float* query, int64_t query_ld,
                             const int32_t* query_col, const rec_din_mlp* mlp, float* out,
                             float* scores_out, float* weights_out, void* stream);
@@ -307,8 +306,8 @@ rec_status rec_din_attn_fwd(const rec_table* seq_tables, void* plan, size_t plan
 /*
  * The whole sparse forward in one call: rec_kjt_sums + rec_din_plan +
  * rec_embbag_fwd_kjt + rec_din_attn_fwd, with the query read from the pooled
- * output.  The deep and sequence sides share launches (four in all instead
- * of six).  Results are bit-identical to the four calls made one by one.
+ * output.  The deep and sequence sides share launches (three in all instead
+ * of five).  Results are bit-identical to the four calls made one by one.
  * Every pointer is a device pointer except `tables`, `seq_tables` and `mlp`
  * (host); arrays are as the four calls document them.
  */

@@ -114,7 +114,7 @@ rec_status prep_plan(const char* fn, const rec_table* seq_tables, const int64_t*
 }
 
 // The same for rec_din_attn_fwd.
-rec_status prep_attn(const char* fn, const rec_table* seq_tables, void* plan, size_t plan_bytes,
+rec_status prep_attn(const char* fn, const rec_table* seq_tables, const void* plan, size_t plan_bytes,
                      int64_t B, int32_t max_len, const float* query, int64_t query_ld,
                      const int32_t* query_col, const rec_din_mlp* mlp, float* out,
                      float* scores_out, float* weights_out, DinArgs* a, bool* work) {
@@ -153,7 +153,7 @@ rec_status prep_attn(const char* fn, const rec_table* seq_tables, void* plan, si
     }
     if (B == 0) return REC_OK;
     const PlanLayout L = plan_layout(B, max_len);
-    char* p = (char*)plan;
+    const char* p = (const char*)plan;
     a->query = query;
     a->query_ld = query_ld;
     for (int t = 0; t < 3; ++t) a->qcol[t] = query_col[t];
@@ -170,7 +170,8 @@ rec_status prep_attn(const char* fn, const rec_table* seq_tables, void* plan, si
     a->pos_b = (const int32_t*)(p + L.off_pb);
     a->pos_jr = (const int32_t*)(p + L.off_pjr);
     a->pos_rows = (const int32_t*)(p + L.off_prows);
-    a->partials = (float*)(p + L.off_part);
+    a->group_start = (const int32_t*)(p + L.off_group);
+    a->ngroups = L.ngroups;
     a->empty = (const int32_t*)(p + L.off_empty);
     a->pmax = L.pmax;
     a->out = out;
@@ -424,7 +425,7 @@ rec_status rec_din_plan(const rec_table* seq_tables, const int64_t* seq_values,
     return hip_status(launch_din_plan(a, (hipStream_t)stream), "rec_din_plan");
 }
 
-rec_status rec_din_attn_fwd(const rec_table* seq_tables, void* plan, size_t plan_bytes,
+rec_status rec_din_attn_fwd(const rec_table* seq_tables, const void* plan, size_t plan_bytes,
                             int64_t B, int32_t max_len, const float* query, int64_t query_ld,
                             const int32_t* query_col, const rec_din_mlp* mlp, float* out,
                             float* scores_out, float* weights_out, void* stream) {

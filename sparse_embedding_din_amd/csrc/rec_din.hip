@@ -395,14 +395,27 @@ __device__ inline void mlp_f32(const Sub* S, const float* __restrict__ w1,
     for (int s = 0; s < NSUB; ++s) e[s] = score_from_h2(acc2[s], w3s, b3, g);
 }
 
-// Online segmented softmax and weighted sum for one 16-position tile of range
-// r.  A sample's run inside the range ends at the lane where rl == 0: a
-// sample wholly inside the range writes its output there; one cut by the
-// range's start (head, slot 0) or end (tail, slot 1) leaves its unnormalised
-// state in the plan; a tail piece also records its sample and the last range
-// the sample reaches, which is all k_din_finalize needs to find the others.
-__device__ inline void softmax_tile(const DinArgs& a, const Sub& S, float e, int lane, int r, int R,
-                                    float& m_open, float& l_open, float (&acc_open)[12]) {
+// A group of T tiles gives wave w the tiles [group_tile_lo(T, w),
+// group_tile_lo(T, w + 1)); group_wave_of is the wave holding tile t.
+__device__ inline int group_tile_lo(int T, int w) { return (T * w) / kDinWaves; }
+__device__ inline int group_wave_of(int T, int t) {
+    int w = 0;
+#pragma unroll
+    for (int k = 1; k < kDinWaves; ++k) w += t >= group_tile_lo(T, k) ? 1 : 0;
+    return w;
+}
+
+// Online segmented softmax and weighted sum for one 16-position tile of a
+// wave's range.  A sample's run inside the range ends at the lane where
+// rl == 0: a sample wholly inside the range writes its output there; one cut
+// by the range's start (head) or end (tail) leaves its unnormalised state in
+// the wave's LDS slot `pc` (head) or `pc + kPartialFloats` (tail); a tail
+// piece also records its sample and the wave whose range holds the sample's
+// last position (in a group starting at gA of T tiles), which is all the
+// merge needs to find the other pieces.
+__device__ inline void softmax_tile(const DinArgs& a, const Sub& S, float e, int lane, int64_t gA,
+                                    int T, float* pc, float& m_open, float& l_open,
+                                    float (&acc_open)[12]) {
     const int n = lane & 15, g = lane >> 4;
     const int j = S.valid ? S.jl : 0;
     const int rem = S.valid ? S.rl : 0;
@@ -442,10 +455,10 @@ __device__ inline void softmax_tile(const DinArgs& a, const Sub& S, float e, int
                 o[q] = make_float4(A[4 * q] * inv, A[4 * q + 1] * inv, A[4 * q + 2] * inv, A[4 * q + 3] * inv);
         } else {
             const bool is_head = S.j > S.jl;
-            float* ps = is_head ? head_slot(a.partials, r) : tail_slot(a.partials, r);
+            float* ps = is_head ? pc : pc + kPartialFloats;
             if (g == 0)
                 *(float4*)ps = make_float4(mref, l, __int_as_float(S.b),
-                                           __int_as_float(((int)S.pos + S.rem) / R));
+                                           __int_as_float(group_wave_of(T, (int)((S.pos + S.rem - gA) >> 4))));
             float4* o = (float4*)(ps + 4 + 12 * g);
 #pragma unroll
             for (int q = 0; q < 3; ++q) o[q] = make_float4(A[4 * q], A[4 * q + 1], A[4 * q + 2], A[4 * q + 3]);
@@ -539,12 +552,17 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
     uint4* s_w1 = s_wt;
     uint4* s_w2 = s_wt + 8 * 6 * 2 * 64;
 
+    __shared__ __attribute__((aligned(16))) float s_piece[kDinWaves * 2 * kPartialFloats];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // Workgroup k takes the groups k, k + gridDim.x, ...: a group is the
+    // positions between two sample starts about `span` apart, its tiles
+    // split over the four waves.  The first group's bounds are read with the header
+    // (every workgroup has a slot; one past the last group is not used).
     const int64_t P = a.plan_hdr[kHdrP];
-    const int R = (int)din_range(P, a.plan_hdr[kHdrRReq], a.waves);
-    const int nr = (int)((P + R - 1) / R);
-    const int first = blockIdx.x * kDinWaves;
-    if (first >= nr) return;
+    const int64_t span = din_span(P, a.plan_hdr[kHdrRReq], a.waves);
+    const int ng = (int)((P + span - 1) / span);
+    int gi = blockIdx.x;
+    int64_t gA = a.group_start[gi], gE = a.group_start[gi + 1];
 
     // Weight staging is issued first and completes under the first range's
     // bookkeeping and gathers.
@@ -580,12 +598,22 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
     const int stride = gridDim.x * kDinWaves;
     const int n = lane & 15;
     const LaneSrc src = lane_src(a, lane);
-    int r = first + wave;
-    int p0 = r < nr ? r * R : 0;
-    int cnt = r < nr ? (int)min((int64_t)R, P - p0) : 0;
-    int sb = 0;
+    // this wave's range of a group [A, E): the group's 16-position tiles
+    // split as evenly as they go, wave w taking tiles [tile_lo(w), tile_lo(w+1))
+    auto wave_range = [&](int64_t A, int64_t E, bool live, int64_t& p0, int& cnt) {
+        const int64_t N = live ? E - A : 0;
+        const int T = (int)((N + 15) / 16);
+        const int t0 = group_tile_lo(T, wave), t1 = group_tile_lo(T, wave + 1);
+        p0 = A + 16 * (int64_t)t0;
+        cnt = (int)(min((int64_t)16 * t1, N) - 16 * (int64_t)t0);
+        if (cnt < 0) cnt = 0;
+    };
+    int64_t p0;
+    int cnt;
+    wave_range(gA, gE, gi < ng, p0, cnt);
     Sub S[2];
-    if (cnt > 0) {
+    bool ready = cnt > 0;           // S holds the first round of the wave's range
+    if (ready) {
         Ent E[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) load_entries(a, src, p0, cnt, 16 * s + n, E[s]);
@@ -622,9 +650,6 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
     if (kPacked) __builtin_amdgcn_s_waitcnt(0);        // the LDS copies have landed
     __syncthreads();
 
-    // Rounds of up to 32 positions.  While one round's MLP runs, the next
-    // round's entries are in flight; its s and q loads are issued before this
-    // round's softmax.
     // samples without positions: zero output, spread over every wave
     {
         const int32_t ne = a.plan_hdr[kHdrNEmpty];
@@ -634,126 +659,103 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
             for (int q = 0; q < 12; ++q) o[q] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
     }
-    float m_open = -INFINITY, l_open = 0.f, acc_open[12];
+    float* const pc = s_piece + wave * 2 * kPartialFloats;     // this wave's head, tail
+    float acc_open[12];
+    // Groups (uniform over the workgroup), then the wave's rounds of up to 32
+    // positions.  While one round's MLP runs, the next round's entries are in
+    // flight -- the next round of this range, else this wave's first round of
+    // the next group -- and its s and q loads are issued before this round's
+    // softmax.
+    for (; gi < ng; gi += gridDim.x) {
+        const int gn = gi + gridDim.x;
+        int64_t nA = 0, nE = 0;
+        if (gn < ng) {
+            nA = a.group_start[gn];
+            nE = a.group_start[gn + 1];
+        }
+        int64_t p0n;
+        int cntn;
+        wave_range(nA, nE, gn < ng, p0n, cntn);
+        const int gT = (int)((gE - gA + 15) / 16);
+        float m_open = -INFINITY, l_open = 0.f;
 #pragma unroll
-    for (int f = 0; f < 12; ++f) acc_open[f] = 0.f;
-    while (r < nr) {
-        // the next round: the rest of this range, else the wave's next range
-        int rn = r, sbn = sb + 32, p0n = p0, cntn = cnt;
-        if (sbn >= cnt) {
-            rn = r + stride;
-            sbn = 0;
-            p0n = rn < nr ? rn * R : 0;
-            cntn = rn < nr ? (int)min((int64_t)R, P - p0n) : 0;
-        }
-        const bool more = sbn < cntn;
-        Ent E[2];
-        if (more) {
+        for (int f = 0; f < 12; ++f) acc_open[f] = 0.f;
+        if (lane == 0) pc[kPartialFloats + 2] = __int_as_float(-1);     // no tail piece yet
+        if (cnt > 0 && !ready) {
+            Ent E[2];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) load_entries(a, src, p0n, cntn, sbn + 16 * s + n, E[s]);
-        }
-        float e[2];
-        const bool two = cnt - sb > 16;
-        mask_sub(S[0]);
-        mask_sub(S[1]);
-        if (kBF) {
-            if (two) mlp_bf16<2>(S, s_w1, s_w2, s_b1, s_b2, s_w3, a.b3, lane, e);
-            else mlp_bf16<1>(S, s_w1, s_w2, s_b1, s_b2, s_w3, a.b3, lane, e);
-        } else {
-            if (two) mlp_f32<2>(S, (const float*)a.w1, (const float*)a.w2, s_b1, s_b2, s_w3, a.b3, lane, e);
-            else mlp_f32<1>(S, (const float*)a.w1, (const float*)a.w2, s_b1, s_b2, s_w3, a.b3, lane, e);
-        }
-        Sub Sn[2];
-        if (more) {
+            for (int s = 0; s < 2; ++s) load_entries(a, src, p0, cnt, 16 * s + n, E[s]);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) load_data(a, src, E[s], p0n, cntn, sbn + 16 * s + n, lane, Sn[s]);
+            for (int s = 0; s < 2; ++s) load_data(a, src, E[s], p0, cnt, 16 * s + n, lane, S[s]);
         }
-        softmax_tile(a, S[0], e[0], lane, r, R, m_open, l_open, acc_open);
-        if (two) softmax_tile(a, S[1], e[1], lane, r, R, m_open, l_open, acc_open);
-        if (rn != r) {
-            m_open = -INFINITY;
-            l_open = 0.f;
+        for (int sb = 0; sb < cnt; sb += 32) {
+            int64_t q0 = p0;
+            int qc = cnt, qs = sb + 32;
+            if (qs >= cnt) {
+                q0 = p0n;
+                qc = cntn;
+                qs = 0;
+            }
+            const bool more = qs < qc;
+            Ent E[2];
+            if (more) {
 #pragma unroll
-            for (int f = 0; f < 12; ++f) acc_open[f] = 0.f;
+                for (int s = 0; s < 2; ++s) load_entries(a, src, q0, qc, qs + 16 * s + n, E[s]);
+            }
+            float e[2];
+            const bool two = cnt - sb > 16;
+            mask_sub(S[0]);
+            mask_sub(S[1]);
+            if (kBF) {
+                if (two) mlp_bf16<2>(S, s_w1, s_w2, s_b1, s_b2, s_w3, a.b3, lane, e);
+                else mlp_bf16<1>(S, s_w1, s_w2, s_b1, s_b2, s_w3, a.b3, lane, e);
+            } else {
+                if (two) mlp_f32<2>(S, (const float*)a.w1, (const float*)a.w2, s_b1, s_b2, s_w3, a.b3, lane, e);
+                else mlp_f32<1>(S, (const float*)a.w1, (const float*)a.w2, s_b1, s_b2, s_w3, a.b3, lane, e);
+            }
+            Sub Sn[2];
+            if (more) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) load_data(a, src, E[s], q0, qc, qs + 16 * s + n, lane, Sn[s]);
+            }
+            softmax_tile(a, S[0], e[0], lane, gA, gT, pc, m_open, l_open, acc_open);
+            if (two) softmax_tile(a, S[1], e[1], lane, gA, gT, pc, m_open, l_open, acc_open);
+            S[0] = Sn[0];
+            S[1] = Sn[1];
         }
-        r = rn;
+        ready = cnt > 0 && cntn > 0;
+        __syncthreads();
+        // a sample cut between waves: its tail piece (waves 0-2) and the head
+        // pieces of the waves up to the one where it ends; lane c < 48 owns
+        // weighted sum c
+        if (wave < kDinWaves - 1) {
+            const float* tl = pc + kPartialFloats;
+            const int b = __float_as_int(tl[2]);
+            if (b >= 0) {
+                const int w1 = __float_as_int(tl[3]);
+                float m = tl[0], l = tl[1];
+                float acc = lane < 48 ? tl[4 + lane] : 0.f;
+                for (int h = wave + 1; h <= w1; ++h) {
+                    if (group_tile_lo(gT, h) == group_tile_lo(gT, h + 1)) continue;   // no tiles
+                    const float* hp = s_piece + h * 2 * kPartialFloats;
+                    const float mn = fmaxf(m, hp[0]);
+                    const float sa = __expf(m - mn), sh = __expf(hp[0] - mn);
+                    l = l * sa + hp[1] * sh;
+                    acc = acc * sa + (lane < 48 ? hp[4 + lane] : 0.f) * sh;
+                    m = mn;
+                }
+                if (lane < 48) a.out[(int64_t)b * 48 + lane] = acc * __builtin_amdgcn_rcpf(l);
+                if (a.weights) {
+                    const int64_t ps = a.pos_start[b], pe = a.pos_start[b + 1];
+                    for (int64_t q = ps + lane; q < pe; q += 64) a.weights[q] = __expf(a.scores[q] - m) / l;
+                }
+            }
+        }
+        __syncthreads();
+        gA = nA;
+        gE = nE;
         p0 = p0n;
         cnt = cntn;
-        sb = sbn;
-        S[0] = Sn[0];
-        S[1] = Sn[1];
-    }
-}
-
-// One thread per range r that may hold a tail piece (a sample that starts in
-// r and runs on into r+1 .. r1).  The tail piece and the head piece of r+1
-// sit next to each other and are read in one round, together with the
-// header's count of slots the plan cleared (the slots exist whatever the
-// count); only a sample reaching past r+1 needs a second round.
-struct Piece {
-    float2 ml;
-    float4 v[12];
-};
-
-__device__ inline void load_piece(Piece& p, const float* hp) {
-    p.ml = *(const float2*)hp;
-#pragma unroll
-    for (int q = 0; q < 12; ++q) p.v[q] = *(const float4*)(hp + 4 + 4 * q);
-}
-
-__device__ inline void merge_piece(float& m, float& l, float (&acc)[48], const Piece& p) {
-    const float mn = fmaxf(m, p.ml.x);
-    const float sa = __expf(m - mn), sh = __expf(p.ml.x - mn);
-    l = l * sa + p.ml.y * sh;
-#pragma unroll
-    for (int q = 0; q < 12; ++q) {
-        acc[4 * q] = acc[4 * q] * sa + p.v[q].x * sh;
-        acc[4 * q + 1] = acc[4 * q + 1] * sa + p.v[q].y * sh;
-        acc[4 * q + 2] = acc[4 * q + 2] * sa + p.v[q].z * sh;
-        acc[4 * q + 3] = acc[4 * q + 3] * sa + p.v[q].w * sh;
-    }
-    m = mn;
-}
-
-__global__ __launch_bounds__(256) void k_din_finalize(const DinArgs a, int64_t max_ranges) {
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    const int64_t nclear = a.plan_hdr[kHdrNClear];
-    for (int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x; r < max_ranges; r += stride) {
-        // the tail piece of r and the head piece of r+1 (next to it), read
-        // before knowing whether r has a tail: both slots always exist
-        const float* tp = tail_slot(a.partials, r);
-        const float4 t = *(const float4*)tp;
-        float acc[48];
-#pragma unroll
-        for (int q = 0; q < 12; ++q) {
-            const float4 v = *(const float4*)(tp + 4 + 4 * q);
-            acc[4 * q] = v.x;
-            acc[4 * q + 1] = v.y;
-            acc[4 * q + 2] = v.z;
-            acc[4 * q + 3] = v.w;
-        }
-        Piece h1;
-        load_piece(h1, head_slot(a.partials, r + 1));
-        if (r >= nclear) break;
-        const int b = __float_as_int(t.z);
-        if (b < 0) continue;
-        const int64_t r1 = __float_as_int(t.w);
-        float m = t.x, l = t.y;
-        merge_piece(m, l, acc, h1);
-        for (int64_t h = r + 2; h <= r1; ++h) {
-            Piece ph;
-            load_piece(ph, head_slot(a.partials, h));
-            merge_piece(m, l, acc, ph);
-        }
-        const float inv = __builtin_amdgcn_rcpf(l);
-        float4* o = (float4*)(a.out + (int64_t)b * 48);
-#pragma unroll
-        for (int q = 0; q < 12; ++q)
-            o[q] = make_float4(acc[4 * q] * inv, acc[4 * q + 1] * inv, acc[4 * q + 2] * inv, acc[4 * q + 3] * inv);
-        if (a.weights) {
-            const int64_t ps = a.pos_start[b], pe = a.pos_start[b + 1];
-            for (int64_t q = ps; q < pe; ++q) a.weights[q] = __expf(a.scores[q] - m) / l;
-        }
     }
 }
 
@@ -762,21 +764,15 @@ __global__ __launch_bounds__(256) void k_din_finalize(const DinArgs a, int64_t m
 int din_waves(int num_cus) { return num_cus * kDinWaves; }
 
 hipError_t launch_din(const DinArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)(a.waves / kDinWaves)), block(64 * kDinWaves);
+    // one workgroup per CU; the plan holds group bounds for up to
+    // kMaxDinGroups workgroups (more groups are looped over)
+    const dim3 grid((unsigned)din_groups(a.waves)), block(64 * kDinWaves);
     if (a.dtype == REC_BF16_PACKED)
         hipLaunchKernelGGL(k_din_attn<REC_BF16_PACKED>, grid, block, 0, s, a);
     else if (a.dtype == REC_BF16)
         hipLaunchKernelGGL(k_din_attn<REC_BF16>, grid, block, 0, s, a);
     else
         hipLaunchKernelGGL(k_din_attn<REC_F32>, grid, block, 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // one thread per range of the even split; a requested small range size
-    // makes more ranges, which the threads then loop over
-    const int64_t max_ranges = a.pmax / kMinRange + 1;
-    int64_t threads = a.waves < max_ranges ? a.waves : max_ranges;
-    hipLaunchKernelGGL(k_din_finalize, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a,
-                       max_ranges);
     return hipGetLastError();
 }
 

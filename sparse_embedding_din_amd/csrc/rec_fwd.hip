@@ -2,11 +2,10 @@
 // and the sequence side each need a sums pass and then a pass that consumes
 // the sums; the two sides are independent, so each pair runs as one launch
 // whose blocks split by index between the two kinds of work:
-//   1. KJT block/chunk sums | plan block/chunk sums (and clearing of the
-//      plan's tail slots);
-//   2. plan build (positions, entries, rows) | embedding bags with offsets
-//      derived in the bags;
-//   3. DIN attention, 4. its finalize (rec_din.hip).
+//   1. KJT block/chunk sums | plan block/chunk sums;
+//   2. plan build (positions, entries, rows, group starts) | embedding bags
+//      with offsets derived in the bags;
+//   3. DIN attention (rec_din.hip).
 // Every kernel on the path costs a fixed ~2 us inside a graph whatever its
 // size, so two fewer launches save about as much as the first pass costs.
 #include "rec_embbag_dev.h"
@@ -24,9 +23,7 @@ struct FwdSums {
     int64_t* chp;
     int64_t* plan_sums;
     int32_t* hdr;
-    float* partials;
-    int64_t nclear;
-    int64_t nkjt, nplan;        // blocks of each kind
+    int64_t nkjt;               // blocks of KJT sums (the rest are plan sums)
     int32_t max_len;
 };
 
@@ -34,8 +31,7 @@ __global__ __launch_bounds__(kScanThreads) void k_fwd_sums(const FwdSums a) {
     if ((int64_t)blockIdx.x < a.nkjt)
         k_kjt_sums_body(a.lengths, a.B, a.nK, a.G, a.bs, a.segp, a.chp, blockIdx.x);
     else
-        k_plan_sums_body(a.seq_lengths, a.B, a.max_len, a.plan_sums, a.hdr, a.partials, a.nclear,
-                         blockIdx.x - a.nkjt, a.nplan);
+        k_plan_sums_body(a.seq_lengths, a.B, a.max_len, a.plan_sums, a.hdr, blockIdx.x - a.nkjt);
 }
 
 template <bool kHashSeq, bool kHashEmb>
@@ -63,12 +59,9 @@ hipError_t launch_fwd_front(const PlanArgs& p, const EmbArgs& e, hipStream_t s) 
     a.chp = (int64_t*)e.kjt_chp;
     a.plan_sums = (int64_t*)(pl + L.off_sums);
     a.hdr = (int32_t*)pl;
-    a.partials = (float*)(pl + L.off_part);
-    a.nclear = plan_nclear(p, L);
     a.nkjt = (int64_t)e.T * k.nK;
-    a.nplan = L.nblocks;
     a.max_len = p.max_len;
-    hipLaunchKernelGGL(k_fwd_sums, dim3((unsigned)(a.nkjt + a.nplan)), dim3(kScanThreads), 0, s, a);
+    hipLaunchKernelGGL(k_fwd_sums, dim3((unsigned)(a.nkjt + L.nblocks)), dim3(kScanThreads), 0, s, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t nbuild = (p.B + kPlanChunk - 1) / kPlanChunk;

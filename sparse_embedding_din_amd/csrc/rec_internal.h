@@ -186,10 +186,12 @@ __host__ __device__ inline KjtLayout kjt_layout(int32_t T, int64_t B) {
 // DIN plan buffer layout (bytes from the start).  Pmax = B * max_len bounds
 // the packed positions P = sum_b min(len_b, max_len); packed position p of
 // sample b, step j is pos_start[b] + j.  The attention splits [0, P) into
-// ranges of R positions (one per wave and pass); a sample cut by a range
-// edge leaves partial softmax states that a finalize pass merges.
+// groups, one at a time per workgroup: group g nominally starts at g * span
+// (din_span: four requested ranges, else P over the workgroups) and really at
+// the nearest sample start, so that no sample is cut between workgroups (a
+// sample cut between two waves of one workgroup is merged in LDS).
 //   [0, 64)        int32 header: B, max_len, R requested (0 = even split),
-//                  R used, P, nblocks, number of ranges
+//                  (unused), P, nblocks, (unused), number of empty samples
 //   sums           per 1024-sample block: int64 (clamped, raw) block sums, then
 //                  64 pairs of 16-sample chunk sums (kPlanSumWords words)
 //   pos_start      int32[B+1]
@@ -198,33 +200,23 @@ __host__ __device__ inline KjtLayout kjt_layout(int32_t T, int64_t B) {
 //   pos_jr         int32[Pmax]: j | (L - 1 - j) << 16 (step, steps left)
 //   pos_rows       int32[3][Pmax]: resolved row of the adgroup/cate/brand id
 //                  (a hash miss is -1)
-//   partials       float[max_ranges + 1][2][52]: per range edge e, the state of
-//                  the sample leaving range e-1 (tail piece of e-1) and then
-//                  of the sample entering range e (head piece of e): max,
-//                  sum, then (tail only, as int bits) the sample and the last
-//                  range it reaches, 48 weighted sums.  A sample cut at edge e
-//                  so has both its pieces next to each other.  The plan marks
-//                  the tail slots of every range the attention can form as
-//                  empty (sample -1), their count in the header.
 //   empty          int32[B]: the samples with no positions (header: count)
-enum { kHdrB = 0, kHdrMaxLen, kHdrRReq, kHdrR, kHdrP, kHdrNBlocks, kHdrNRanges, kHdrNEmpty,
-       kHdrNClear };
+//   group_start    int32[ngroups]: group g's first position, the sample start
+//                  nearest to g * span (the earlier one on a tie; P for group
+//                  ceil(P / span)); entries past that one are not written
+enum { kHdrB = 0, kHdrMaxLen, kHdrRReq, kHdrUnused3, kHdrP, kHdrNBlocks, kHdrUnused6,
+       kHdrNEmpty };
 constexpr int kPlanChunk = 16;                                  // samples per build block
 constexpr int kPlanSumWords = 2 + 2 * (kScanChunk / kPlanChunk);   // 130
 constexpr int kMinRange = 16;
 constexpr int kMaxRange = 1 << 20;
-constexpr int kPartialFloats = 52;
-// the tail piece of range r and the head piece of range r (see the layout)
-__host__ __device__ inline float* tail_slot(float* partials, int64_t r) {
-    return partials + (r + 1) * 2 * kPartialFloats;
-}
-__host__ __device__ inline float* head_slot(float* partials, int64_t r) {
-    return partials + (r * 2 + 1) * kPartialFloats;
-}
+constexpr int kPartialFloats = 52;       // a cut sample's piece: max, sum, 2 words, 48 sums
+constexpr int kDinWaves = 4;             // waves per attention workgroup (one per SIMD)
+constexpr int kMaxDinGroups = 4096;      // attention workgroups the plan provides for
 
 struct PlanLayout {
-    int64_t nblocks, pmax, max_ranges;
-    size_t off_sums, off_pos, off_sbase, off_pb, off_pjr, off_prows, off_part, off_empty, bytes;
+    int64_t nblocks, pmax, ngroups;
+    size_t off_sums, off_pos, off_sbase, off_pb, off_pjr, off_prows, off_empty, off_group, bytes;
 };
 
 __host__ __device__ inline size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
@@ -233,26 +225,36 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t B, int32_t max_len) {
     PlanLayout p;
     p.nblocks = scan_blocks(B);
     p.pmax = B * (int64_t)max_len;
-    p.max_ranges = p.pmax / kMinRange + 1;
+    // groups: ceil(P / 4R) + 1 at the smallest R, and at least one per
+    // attention workgroup (each reads its first group's bounds before it
+    // knows P)
+    const int64_t ng = p.pmax / (kDinWaves * kMinRange) + 2;
+    p.ngroups = ng > kMaxDinGroups + 1 ? ng : kMaxDinGroups + 1;
     p.off_sums = 64;
     p.off_pos = align16(p.off_sums + 8 * (size_t)kPlanSumWords * (size_t)p.nblocks);
     p.off_sbase = align16(p.off_pos + 4 * (size_t)(B + 1));
     p.off_pb = align16(p.off_sbase + 8 * (size_t)B);
     p.off_pjr = align16(p.off_pb + 4 * (size_t)p.pmax);
     p.off_prows = align16(p.off_pjr + 4 * (size_t)p.pmax);
-    p.off_part = align16(p.off_prows + 12 * (size_t)p.pmax);
-    p.off_empty = align16(p.off_part + sizeof(float) * 2 * kPartialFloats * (size_t)(p.max_ranges + 1));
-    p.bytes = align16(p.off_empty + 4 * (size_t)B);
+    p.off_empty = align16(p.off_prows + 12 * (size_t)p.pmax);
+    p.off_group = align16(p.off_empty + 4 * (size_t)B);
+    p.bytes = align16(p.off_group + 4 * (size_t)p.ngroups);
     return p;
 }
 
-// Positions per range: the requested multiple of 16, else an even split of P
-// over `waves`, rounded up to a multiple of 16.
-__host__ __device__ inline int64_t din_range(int64_t P, int32_t req, int64_t waves) {
-    if (req > 0) return req;
-    int64_t r = (P + waves - 1) / waves;
-    r = (r + 15) / 16 * 16;
-    return r < kMinRange ? kMinRange : r;
+// Attention workgroups on a device with `waves` attention waves.
+__host__ __device__ inline int64_t din_groups(int64_t waves) {
+    const int64_t g = waves / kDinWaves;
+    return g < 1 ? 1 : (g > kMaxDinGroups ? kMaxDinGroups : g);
+}
+
+// Nominal positions per group (before its ends move to sample starts): four
+// requested ranges, else P spread over the attention's workgroups.
+__host__ __device__ inline int64_t din_span(int64_t P, int32_t req, int64_t waves) {
+    if (req > 0) return (int64_t)kDinWaves * req;
+    const int64_t g = din_groups(waves);
+    const int64_t s = (P + g - 1) / g;
+    return s < 1 ? 1 : s;
 }
 
 // ---------------------------------------------------------------------------
@@ -277,11 +279,6 @@ hipError_t launch_din_plan(const PlanArgs& a, hipStream_t s);
 
 // Tail slots the plan clears: every range the attention can form (the even
 // split makes at most one per wave, a requested size ceil(pmax / size)).
-inline int64_t plan_nclear(const PlanArgs& a, const PlanLayout& L) {
-    const int64_t n = a.range_positions > 0 ? (L.pmax + a.range_positions - 1) / a.range_positions
-                                            : (int64_t)a.waves;
-    return n < L.max_ranges ? n : L.max_ranges;
-}
 
 struct EmbArgs {
     TabDev tab[REC_MAX_TABLES];
@@ -328,7 +325,8 @@ struct DinArgs {
     const int32_t* pos_b;
     const int32_t* pos_jr;
     const int32_t* pos_rows;
-    float* partials;
+    const int32_t* group_start;
+    int64_t ngroups;
     const int32_t* empty;
     int64_t pmax;
     float* out;
@@ -337,7 +335,6 @@ struct DinArgs {
     int64_t B;
     int32_t waves;          // waves of the attention launch (sets the even split)
 };
-constexpr int kDinWaves = 4;                 // waves per workgroup (one per SIMD)
 int din_waves(int num_cus);
 // The whole forward's first two launches: KJT and plan sums together, then the
 // plan's build pass and the embedding bags together (rec_fwd.hip).

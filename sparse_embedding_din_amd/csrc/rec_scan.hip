@@ -71,10 +71,8 @@ __global__ __launch_bounds__(kScanThreads) void k_kjt_sums(const int32_t* __rest
 __global__ __launch_bounds__(kScanThreads) void k_plan_sums(const int32_t* __restrict__ len,
                                                            int64_t B, int32_t max_len,
                                                            int64_t* __restrict__ sums,
-                                                           int32_t* __restrict__ hdr,
-                                                           float* __restrict__ partials,
-                                                           int64_t nclear) {
-    k_plan_sums_body(len, B, max_len, sums, hdr, partials, nclear, blockIdx.x, gridDim.x);
+                                                           int32_t* __restrict__ hdr) {
+    k_plan_sums_body(len, B, max_len, sums, hdr, blockIdx.x);
 }
 
 template <bool kHash>
@@ -108,10 +106,8 @@ hipError_t launch_din_plan(const PlanArgs& a, hipStream_t s) {
     const PlanLayout L = plan_layout(a.B, a.max_len);
     char* p = (char*)a.plan;
     int64_t* sums = (int64_t*)(p + L.off_sums);
-    const int64_t nclear = plan_nclear(a, L);
     hipLaunchKernelGGL(k_plan_sums, dim3((unsigned)L.nblocks), dim3(kScanThreads), 0, s,
-                       a.seq_lengths, a.B, a.max_len, sums, (int32_t*)p, (float*)(p + L.off_part),
-                       nclear);
+                       a.seq_lengths, a.B, a.max_len, sums, (int32_t*)p);
     const bool hash = a.tab[0].kind == REC_HASH || a.tab[1].kind == REC_HASH || a.tab[2].kind == REC_HASH;
     const dim3 grid((unsigned)((a.B + kPlanChunk - 1) / kPlanChunk));
     if (hash) hipLaunchKernelGGL(k_plan_build<true>, grid, dim3(256), 0, s, a);

@@ -108,8 +108,7 @@ __device__ inline void k_plan_sums_body(const int32_t* __restrict__ len,
                                                            int64_t B, int32_t max_len,
                                                            int64_t* __restrict__ sums,
                                                            int32_t* __restrict__ hdr,
-                                                           float* __restrict__ partials,
-                                                           int64_t nclear, int64_t bid, int64_t nblk) {
+                                                           int64_t bid) {
     __shared__ int64_t red[kScanThreads / 64];
     const int64_t b0 = (int64_t)bid * kScanChunk + (int64_t)threadIdx.x * kScanItems;
     int64_t raw = 0, cl = 0;
@@ -138,25 +137,23 @@ __device__ inline void k_plan_sums_body(const int32_t* __restrict__ len,
         out[0] = cl;
         out[1] = raw;
     }
-    if (bid == 0 && threadIdx.x == 0) {
-        hdr[kHdrNEmpty] = 0;                        // k_plan_build appends
-        hdr[kHdrNClear] = (int32_t)nclear;
-    }
-    // every tail slot the attention may use starts empty
-    for (int64_t r = (int64_t)bid * kScanThreads + threadIdx.x; r < nclear;
-         r += (int64_t)nblk * kScanThreads)
-        *(float4*)tail_slot(partials, r) = make_float4(0.f, 0.f, __int_as_float(-1), 0.f);
+    if (bid == 0 && threadIdx.x == 0) hdr[kHdrNEmpty] = 0;   // k_plan_build appends
 }
 
 // The plan for 16 samples per block.  Wave 0 adds up the sums before the
-// block, scans the 16 lengths and writes the per-sample arrays (and, in the
-// block holding the last sample, the header); then every thread takes packed
-// positions of the block, finds its sample among the 16 starts in LDS, and
-// writes the position's sample, step and the rows of its three ids.
+// block (and all of them: P, hence the attention's group span), scans the 16 lengths
+// and writes the per-sample arrays (and, in the block holding the last
+// sample, the header); then every thread takes packed positions of the block,
+// finds its sample among the 16 starts in LDS, and writes the position's
+// sample, step and the rows of its three ids.  The position g * span of a
+// group boundary also writes where group g starts: at the start of the sample
+// holding that position or of the next one, whichever is nearer (a group's
+// ends then move by at most half a sample).
 template <bool kHash>
 __device__ inline void k_plan_build_body(const PlanArgs a, int64_t bid, int64_t nblk) {
     __shared__ int32_t s_start[kPlanChunk + 1];
     __shared__ int64_t s_base[kPlanChunk];
+    __shared__ int64_t s_span;
     const PlanLayout Lo = plan_layout(a.B, a.max_len);
     char* pb = (char*)a.plan;
     const int64_t* sums = (const int64_t*)(pb + Lo.off_sums);
@@ -167,6 +164,7 @@ __device__ inline void k_plan_build_body(const PlanArgs a, int64_t bid, int64_t 
     int32_t* pos_jr = (int32_t*)(pb + Lo.off_pjr);
     int32_t* pos_rows = (int32_t*)(pb + Lo.off_prows);
     int32_t* empty = (int32_t*)(pb + Lo.off_empty);
+    int32_t* group_start = (int32_t*)(pb + Lo.off_group);
     const int64_t B = a.B;
     const int32_t max_len = a.max_len;
     const int64_t b0 = (int64_t)bid * kPlanChunk;
@@ -175,11 +173,16 @@ __device__ inline void k_plan_build_body(const PlanArgs a, int64_t bid, int64_t 
         const int lane = threadIdx.x;
         const int64_t K = b0 / kScanChunk;
         const int c = (int)((b0 % kScanChunk) / kPlanChunk);
-        // sums of every sample before the block, clamped and raw
-        int64_t pc = 0, pr = 0;
-        for (int64_t i = lane; i < K; i += 64) {
-            pc += sums[i * kPlanSumWords];
-            pr += sums[i * kPlanSumWords + 1];
+        // sums of every sample before the block, clamped and raw, and the
+        // clamped total P
+        int64_t pc = 0, pr = 0, ptot = 0;
+        for (int64_t i = lane; i < Lo.nblocks; i += 64) {
+            const int64_t c = sums[i * kPlanSumWords];
+            ptot += c;
+            if (i < K) {
+                pc += c;
+                pr += sums[i * kPlanSumWords + 1];
+            }
         }
         if (lane < c) {
             pc += sums[K * kPlanSumWords + 2 + 2 * lane];
@@ -190,6 +193,9 @@ __device__ inline void k_plan_build_body(const PlanArgs a, int64_t bid, int64_t 
         const int64_t sb_given = a.seq_offsets ? a.seq_offsets[b] : 0;
         pc = wave_sum(pc);
         pr = wave_sum(pr);
+        ptot = wave_sum(ptot);
+        const int64_t span = din_span(ptot, a.range_positions, a.waves);
+        if (lane == 0) s_span = span;
         const int64_t vc = v < 0 ? 0 : (v < max_len ? v : max_len);
         const int64_t ic = wave_incl_scan(vc), ir = wave_incl_scan((int64_t)v);
         const int64_t ps = pc + ic - vc, pr0 = pr + ir - v;
@@ -220,11 +226,13 @@ __device__ inline void k_plan_build_body(const PlanArgs a, int64_t bid, int64_t 
                 hdr[kHdrRReq] = a.range_positions;
                 hdr[kHdrP] = (int32_t)(ps + vc);
                 hdr[kHdrNBlocks] = (int32_t)Lo.nblocks;
+                group_start[0] = 0;
+                group_start[(ptot + span - 1) / span] = (int32_t)ptot;   // ps + vc == ptot
             }
         }
     }
     __syncthreads();
-    const int64_t P0 = s_start[0], P1 = s_start[nval];
+    const int64_t P0 = s_start[0], P1 = s_start[nval], span = s_span;
     for (int64_t p = P0 + threadIdx.x; p < P1; p += 256) {
         int s = 0;
 #pragma unroll
@@ -237,6 +245,7 @@ __device__ inline void k_plan_build_body(const PlanArgs a, int64_t bid, int64_t 
         const int64_t g = s_base[s] + j;
         pos_b[p] = (int32_t)(b0 + s);
         pos_jr[p] = j | ((L - 1 - j) << 16);
+        if (p > 0 && p % span == 0) group_start[p / span] = 2 * j <= L ? st : st + L;
         int64_t raw[3];
 #pragma unroll
         for (int f = 0; f < 3; ++f) raw[f] = a.seq_values[f * a.seq_stride + g];

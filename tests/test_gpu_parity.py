@@ -106,6 +106,22 @@ def test_din_plan(models, B, max_len, C):
     mask = np.ones(max(stride, 1), bool)
     mask[gidx] = False
     assert np.all(rg[:, mask] == -9)
+    # attention groups: nominal spans of four requested ranges, else P over
+    # the workgroups (one per CU), each start moved forward to a sample start
+    groups = torch.cuda.get_device_properties(0).multi_processor_count
+    span = 4 * C if C > 0 else max(1, -(-P // groups))
+    ng = -(-P // span)
+    off_group = a16(a16(off_prows + 12 * pmax) + 4 * B)
+    gs = p[off_group: off_group + 4 * (ng + 1)].view(np.int32)
+    starts = np.append(pos[:B], P)
+    exp_gs = [0]
+    for g in range(1, ng):
+        t = g * span
+        nxt = int(starts[np.searchsorted(starts, t, "left")])      # first start >= t
+        prv = int(starts[np.searchsorted(starts, t, "right") - 1])  # last start <= t
+        exp_gs.append(prv if t - prv <= nxt - t else nxt)
+    exp_gs.append(P)
+    assert np.array_equal(gs[: ng + 1], np.array(exp_gs[: ng + 1], dtype=np.int32)), (gs, exp_gs)
 
 
 # ---------------------------------------------------------------------------
@@ -348,9 +364,10 @@ def test_din_padded_equals_packed(models, cfg):
                                         (1, "unif100", 4096), (2, None, 16), (2, None, 32),
                                         (2, None, 64), (2, "unif100", 128)])
 def test_din_range_sizes(models, cfg, law, C):
-    """Attention ranges small enough that samples are cut by one or many range
-    edges (merged by the finalize pass), and one range for the whole batch:
-    scores do not depend on the split and outputs stay within tolerance."""
+    """Attention ranges small enough that samples are cut between one or
+    several waves of a workgroup (merged in LDS), and one group for the whole
+    batch: scores do not depend on the split and outputs stay within
+    tolerance."""
     m = models(cfg, bias=True)
     b = synth.make_batch(m, B=600, seq_law=law)
     r = Run(m, b, range_positions=C)
@@ -398,6 +415,32 @@ def test_din_edges(models):
     s1 = np.concatenate([m.tables[k]["values"][seq[i, r.seq_offsets[1]]]
                          for i, k in enumerate(synth.SEQ_KEYS)])
     assert np.array_equal(r.att[1], s1)
+
+
+@pytest.mark.parametrize("B,nonempty", [(300, 0), (70000, 10)])
+def test_din_empty_samples_zeroed(models, B, nonempty):
+    """Samples without positions get exact zeros, whatever the output buffer
+    held, also when there are no positions at all and when the empty samples
+    outnumber the lanes of the whole launch."""
+    m = models(1, bias=True)
+    b = synth.make_batch(m, B=B)
+    L = np.zeros(B, np.int32)
+    L[:nonempty] = b.seq_lengths[:nonempty]
+    keep = int(L.sum())
+    b.seq_values = np.ascontiguousarray(b.seq_values[:, :max(keep, 1)])
+    b.seq_lengths = L
+    b.seq_stride = b.seq_values.shape[1]
+    say(f"empty samples B={B} nonempty={nonempty} P={keep}")
+    tabs = PL.DeviceTables(m.tables, DEV)
+    fwd = PL.SparseDinForward(tabs, PL.DeviceMLP(m, DEV), B, m.cfg.max_len, DEV)
+    fwd.att.fill_(float("nan"))
+    fwd.run(PL.DeviceBatch(b, DEV))
+    torch.cuda.synchronize()
+    att = fwd.att[:B].cpu().numpy()
+    assert np.all(att[nonempty:] == 0.0)
+    if nonempty:
+        o = oracle_forward(m, b, samples=np.arange(nonempty))
+        assert row_rel_err(att[:nonempty], o["att"]) <= FP32_TOL
 
 
 def test_din_deterministic(models):
