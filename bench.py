@@ -23,6 +23,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -73,10 +74,17 @@ def parse():
 
 
 def src_hash() -> str:
+    """Hash of the kernel sources with comments and blank space removed:
+    stored traffic figures stay valid across edits of the comments only
+    (the sources hold no string literal with a comment marker in it)."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "sparse_embedding_din_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
+        h.update(os.path.basename(f).encode() + b"\0" + code.encode() + b"\0")
     return h.hexdigest()[:16]
 
 

@@ -5,12 +5,15 @@
 // q*s]; attn MLP with hidden units 256 and 64; a linear score; mask and
 // softmax; weighted sum), §4.4 (query [B,48], output [B,48]).
 //
-// Work split.  rec_din_plan resolved every sequence id to its row and laid
-// the batch out as P packed positions.  The attention cuts [0, P) into equal
-// ranges (by default one per wave of a persistent grid: one 4-wave workgroup
-// per CU, one wave per SIMD), so every wave gets the same number of rows
-// whatever the length mix.  A wave walks its range in tiles of 16 (pairs
-// while two are left), and per tile:
+// Work split.  rec_din_plan resolved every sequence id to its row, laid the
+// batch out as P packed positions and cut [0, P) into groups: group g starts
+// at the sample start nearest to g * span (span = P over the workgroups of a
+// persistent grid, one 4-wave workgroup per CU, unless the caller asks for a
+// fixed range length), so no sample is cut between workgroups.  Workgroup k
+// takes groups k, k + grid, ...; a group's 16-position tiles are split as
+// evenly as possible over its four waves (one per SIMD), so every wave gets
+// about the same number of rows whatever the length mix.  A wave walks its
+// tiles (pairs while two are left), and per tile:
 //   1. reads the positions' sample, step and three resolved rows from the
 //      plan, then s (3 rows of 64 B) and q (3 x 16 floats of the pooled
 //      output); lane (n, g) holds features 12g..12g+11 of position n;
@@ -24,13 +27,12 @@
 //      segmented softmax: DPP row shifts scan max and sums within each
 //      sample's run of lanes, and one open sample carries its running max,
 //      sum and weighted sum into the next tile.
-// A sample cut by range edges leaves one partial (max, sum, weighted sum) per
-// piece in the plan, and k_din_finalize merges the pieces with the standard
-// rescaling of partial softmax sums.  (Merging inside this kernel would need
-// a device-wide release/acquire per wave; on a chip whose L2 is per XCD that
-// costs far more than a second small launch.)  Samples without positions
-// (listed by the plan) get their zero output from whichever wave the list
-// assigns.
+// A sample cut between two waves of a workgroup leaves one unnormalised
+// (max, sum, weighted sum) per piece in LDS; after a barrier the wave that
+// holds the sample's first piece merges the pieces with the standard
+// rescaling of partial softmax sums and writes the output.  Samples without
+// positions (listed by the plan) are zeroed by the workgroups before their
+// first group.
 // Inside an MFMA the order of the K index is free as long as the A and B
 // operands agree, so each lane's 48 inputs are laid out to match its own 12
 // features, and the weights are permuted to the same order (rec_din_pack_mlp,
@@ -556,16 +558,16 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // Workgroup k takes the groups k, k + gridDim.x, ...: a group is the
     // positions between two sample starts about `span` apart, its tiles
-    // split over the four waves.  The first group's bounds are read with the header
-    // (every workgroup has a slot; one past the last group is not used).
-    const int64_t P = a.plan_hdr[kHdrP];
-    const int64_t span = din_span(P, a.plan_hdr[kHdrRReq], a.waves);
-    const int ng = (int)((P + span - 1) / span);
+    // split over the four waves.  The group count (the plan computed it) and
+    // the first group's bounds are read at once (every workgroup has a slot;
+    // one past the last group is not used), ahead of the weight staging, so
+    // they are scalar loads that the staging's vector loads do not delay.
+    const int ng = a.plan_hdr[kHdrNGroups];
     int gi = blockIdx.x;
     int64_t gA = a.group_start[gi], gE = a.group_start[gi + 1];
-
-    // Weight staging is issued first and completes under the first range's
-    // bookkeeping and gathers.
+    __builtin_amdgcn_sched_barrier(0);      // keep those loads ahead of the staging
+    // Weight staging depends on nothing else and completes under the group
+    // bookkeeping and the first gathers.
     constexpr int kW1Per = (kBF && !kPacked) ? 256 * 24 / kThreads : 0;
     constexpr int kW2Per = (kBF && !kPacked) ? 64 * 32 / kThreads : 0;
     uint4 v1[kW1Per > 0 ? kW1Per : 1], v2[kW2Per > 0 ? kW2Per : 1];
@@ -687,6 +689,11 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
             for (int s = 0; s < 2; ++s) load_entries(a, src, p0, cnt, 16 * s + n, E[s]);
 #pragma unroll
             for (int s = 0; s < 2; ++s) load_data(a, src, E[s], p0, cnt, 16 * s + n, lane, S[s]);
+            // Wait here: the compiler's wait counting merges this path with
+            // the round loop's back edge, and loads still pending here would
+            // make it wait for every load in flight (the next round's
+            // prefetches included) at the first use of these registers.
+            __builtin_amdgcn_s_waitcnt(0);
         }
         for (int sb = 0; sb < cnt; sb += 32) {
             int64_t q0 = p0;

@@ -191,7 +191,7 @@ __host__ __device__ inline KjtLayout kjt_layout(int32_t T, int64_t B) {
 // the nearest sample start, so that no sample is cut between workgroups (a
 // sample cut between two waves of one workgroup is merged in LDS).
 //   [0, 64)        int32 header: B, max_len, R requested (0 = even split),
-//                  (unused), P, nblocks, (unused), number of empty samples
+//                  groups ceil(P / span), P, nblocks, (unused), empty samples
 //   sums           per 1024-sample block: int64 (clamped, raw) block sums, then
 //                  64 pairs of 16-sample chunk sums (kPlanSumWords words)
 //   pos_start      int32[B+1]
@@ -204,7 +204,7 @@ __host__ __device__ inline KjtLayout kjt_layout(int32_t T, int64_t B) {
 //   group_start    int32[ngroups]: group g's first position, the sample start
 //                  nearest to g * span (the earlier one on a tie; P for group
 //                  ceil(P / span)); entries past that one are not written
-enum { kHdrB = 0, kHdrMaxLen, kHdrRReq, kHdrUnused3, kHdrP, kHdrNBlocks, kHdrUnused6,
+enum { kHdrB = 0, kHdrMaxLen, kHdrRReq, kHdrNGroups, kHdrP, kHdrNBlocks, kHdrUnused6,
        kHdrNEmpty };
 constexpr int kPlanChunk = 16;                                  // samples per build block
 constexpr int kPlanSumWords = 2 + 2 * (kScanChunk / kPlanChunk);   // 130

@@ -226,6 +226,7 @@ __device__ inline void k_plan_build_body(const PlanArgs a, int64_t bid, int64_t 
                 hdr[kHdrRReq] = a.range_positions;
                 hdr[kHdrP] = (int32_t)(ps + vc);
                 hdr[kHdrNBlocks] = (int32_t)Lo.nblocks;
+                hdr[kHdrNGroups] = (int32_t)((ptot + span - 1) / span);
                 group_start[0] = 0;
                 group_start[(ptot + span - 1) / span] = (int32_t)ptot;   // ps + vc == ptot
             }

@@ -111,6 +111,7 @@ def test_din_plan(models, B, max_len, C):
     groups = torch.cuda.get_device_properties(0).multi_processor_count
     span = 4 * C if C > 0 else max(1, -(-P // groups))
     ng = -(-P // span)
+    assert hdr[3] == ng
     off_group = a16(a16(off_prows + 12 * pmax) + 4 * B)
     gs = p[off_group: off_group + 4 * (ng + 1)].view(np.int32)
     starts = np.append(pos[:B], P)
