@@ -383,6 +383,25 @@ def test_din_range_sizes(models, cfg, law, C):
     assert np.all(np.abs(wt.sum(axis=1)[L > 0] - 1.0) <= 1e-5)
 
 
+@pytest.mark.parametrize("B,C", [(16384, 48), (8192, 48), (16384, 32)])
+def test_din_three_tile_ranges(models, B, C):
+    """Ranges of 33 to 48 positions (four ranges of C per group), which run
+    as a round of 32 and one of 16; at B = 16384 there are more groups than
+    workgroups, so a wave's next group is prefetched across the group's
+    barriers.  Scores equal the default split's bit for bit; sampled outputs
+    match the oracle."""
+    m = models(2, bias=True)
+    b = synth.make_batch(m, B=B)
+    say(f"three-tile ranges B={B} C={C}")
+    r = Run(m, b, range_positions=C)
+    r0 = Run(m, b)
+    assert np.array_equal(r.scores, r0.scores)
+    samples = np.sort(np.random.default_rng(B).choice(B, size=1024, replace=False))
+    o = oracle_forward(m, b, samples=samples)
+    assert row_rel_err(r.att[samples], o["att"]) <= _tol(m)
+    assert row_rel_err(r0.att[samples], o["att"]) <= _tol(m)
+
+
 def test_din_edges(models):
     """Empty sequences, length 1, lengths at and past the cap, one sample."""
     m = models(1, bias=True)
