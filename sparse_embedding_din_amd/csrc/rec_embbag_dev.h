@@ -97,9 +97,21 @@ __device__ inline void k_embbag_fwd_body(const EmbArgs& a, int64_t bid) {
         const int l = lane & 31;
         const int64_t nflat = (int64_t)tc * a.nK + blk;
         const int64_t sidx = nflat * a.G + g;
+        // Every load of the prefix is issued before any sum waits on one: the
+        // segment and chunk prefixes, then the block sums of everything before
+        // this block (T * nK < 160, so at most five per lane) -- a loop that
+        // added each block sum as it arrived paid one round trip per five
+        // tables.
+        const int64_t sp = a.kjt_segp[sidx], cp = a.kjt_chp[sidx * kKjtSegChunks + c];
         int64_t s = 0;
-        for (int64_t i = l; i < nflat; i += 32) s += a.kjt_bs[i];
-        if (l == 0) s += a.kjt_segp[sidx] + a.kjt_chp[sidx * kKjtSegChunks + c];
+        for (int64_t i0 = l; i0 < nflat; i0 += 5 * 32) {
+            int64_t v[5];
+#pragma unroll
+            for (int u = 0; u < 5; ++u) v[u] = a.kjt_bs[i0 + 32 * u < nflat ? i0 + 32 * u : 0];
+#pragma unroll
+            for (int u = 0; u < 5; ++u) s += i0 + 32 * u < nflat ? v[u] : 0;
+        }
+        if (l == 0) s += sp + cp;
         if (!live) len = 0;
         int64_t inc = len;
 #pragma unroll

@@ -174,22 +174,20 @@ __device__ inline void k_plan_build_body(const PlanArgs a, int64_t bid, int64_t 
         const int64_t K = b0 / kScanChunk;
         const int c = (int)((b0 % kScanChunk) / kPlanChunk);
         // sums of every sample before the block, clamped and raw, and the
-        // clamped total P
-        int64_t pc = 0, pr = 0, ptot = 0;
-        for (int64_t i = lane; i < Lo.nblocks; i += 64) {
-            const int64_t c = sums[i * kPlanSumWords];
-            ptot += c;
-            if (i < K) {
-                pc += c;
-                pr += sums[i * kPlanSumWords + 1];
-            }
-        }
-        if (lane < c) {
-            pc += sums[K * kPlanSumWords + 2 + 2 * lane];
-            pr += sums[K * kPlanSumWords + 3 + 2 * lane];
-        }
+        // clamped total P.  The chunk sums and the block's lengths are loaded
+        // ahead of the block sums, so all of them are in flight at once.
         const int64_t b = b0 + min(lane, nval - 1);
         const int32_t v = lane < nval ? a.seq_lengths[b] : 0;
+        int64_t pc = lane < c ? sums[K * kPlanSumWords + 2 + 2 * lane] : 0;
+        int64_t pr = lane < c ? sums[K * kPlanSumWords + 3 + 2 * lane] : 0;
+        int64_t ptot = 0;
+        for (int64_t i = lane; i < Lo.nblocks; i += 64) {
+            const int64_t cs = sums[i * kPlanSumWords];
+            const int64_t rs = sums[i * kPlanSumWords + 1];
+            ptot += cs;
+            pc += i < K ? cs : 0;
+            pr += i < K ? rs : 0;
+        }
         const int64_t sb_given = a.seq_offsets ? a.seq_offsets[b] : 0;
         pc = wave_sum(pc);
         pr = wave_sum(pr);
