@@ -277,7 +277,8 @@ __device__ inline void l1_block(const bf16x8 (&xf)[NSUB][6], const uint4 (&w1)[1
 // The bf16 MLP for NSUB position tiles, software-pipelined over the eight
 // hidden blocks: while block hb's layer-1 results go through ReLU and bf16
 // into its layer-2 products, block hb+1's layer-1 products are already
-// issued.  W1 fragments are read from LDS one block ahead of use; a
+// issued.  W1 fragments and b1 slices are read from LDS one block ahead of
+// use (a b1 read at the block's start stalled its first product); a
 // scheduling fence per block keeps the compiler from hoisting every block's
 // reads (which would not fit in registers).  Layer-2 accumulators start from
 // b2 the same way.
@@ -299,10 +300,15 @@ __device__ inline void mlp_bf16(const Sub* S, const uint4* w1p, const uint4* w2p
         for (int s = 0; s < NSUB; ++s) acc2[s][mt] = b2v;
     }
     uint4 fw1[2][12], fw2[4];
+    f32x4 fb1[2][2];                // each block's b1 slice, read with its W1 fragments
     f32x4 acc1[2][NSUB][2];
 #pragma unroll
     for (int i = 0; i < 12; ++i) fw1[0][i] = w1p[i * 64 + lane];
-    l1_block<NSUB>(xf, fw1[0], *(const f32x4*)(b1s + 4 * g), *(const f32x4*)(b1s + 16 + 4 * g), acc1[0]);
+    fb1[0][0] = *(const f32x4*)(b1s + 4 * g);
+    fb1[0][1] = *(const f32x4*)(b1s + 16 + 4 * g);
+    l1_block<NSUB>(xf, fw1[0], fb1[0][0], fb1[0][1], acc1[0]);
+    fb1[1][0] = *(const f32x4*)(b1s + 32 + 4 * g);
+    fb1[1][1] = *(const f32x4*)(b1s + 48 + 4 * g);
 #pragma unroll
     for (int i = 0; i < 12; ++i) fw1[1][i] = w1p[(12 + i) * 64 + lane];
 #pragma unroll
@@ -311,10 +317,11 @@ __device__ inline void mlp_bf16(const Sub* S, const uint4* w1p, const uint4* w2p
         const int cur = hb & 1, nxt = cur ^ 1;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) fw2[mt] = w2p[(hb * 4 + mt) * 64 + lane];
-        if (hb + 1 < 8)
-            l1_block<NSUB>(xf, fw1[nxt], *(const f32x4*)(b1s + (hb + 1) * 32 + 4 * g),
-                           *(const f32x4*)(b1s + (hb + 1) * 32 + 16 + 4 * g), acc1[nxt]);
+        if (hb + 1 < 8) l1_block<NSUB>(xf, fw1[nxt], fb1[nxt][0], fb1[nxt][1], acc1[nxt]);
         if (hb + 2 < 8) {
+            // LDS reads complete in order: the b1 slice, needed first, goes first
+            fb1[cur][0] = *(const f32x4*)(b1s + (hb + 2) * 32 + 4 * g);
+            fb1[cur][1] = *(const f32x4*)(b1s + (hb + 2) * 32 + 16 + 4 * g);
 #pragma unroll
             for (int i = 0; i < 12; ++i) fw1[cur][i] = w1p[((hb + 2) * 12 + i) * 64 + lane];
         }
