@@ -24,6 +24,8 @@ P64 = C.POINTER(C.c_int64)
 P32 = C.POINTER(C.c_int32)
 PF = C.POINTER(C.c_float)
 PD = C.POINTER(C.c_double)
+P8 = C.POINTER(C.c_uint8)
+PU = C.POINTER(C.c_uint64)
 
 
 class OrcTable(C.Structure):
@@ -70,6 +72,11 @@ class Oracle:
         L.orc_towers.argtypes = [C.c_int64, PD, C.c_int64, PD, PD, PD, PD, PD, PD, PD, PD, PD,
                                  PD, C.c_double, PD, PD, PD, PD]
         L.orc_towers.restype = None
+        L.orc_hash_insert.argtypes = [P64, P8, PU, PF, C.c_int64, P64, PF, C.c_int64, C.c_int32,
+                                      C.c_uint64, P64]
+        L.orc_hash_insert.restype = None
+        L.orc_hash_check.argtypes = [P64, P8, C.c_int64]
+        L.orc_hash_check.restype = C.c_int64
         self._keep = []
 
     # -- bookkeeping ---------------------------------------------------------
@@ -81,6 +88,43 @@ class Oracle:
 
     def floor_mod(self, raw: int, n: int) -> int:
         return int(self.lib.orc_floor_mod(int(raw), int(n)))
+
+    # -- hash tables: the insert side ------------------------------------------
+    SCORE_NONE, SCORE_STEP, SCORE_LFU = 0, 1, 2
+
+    @staticmethod
+    def empty_hash_table(capacity: int) -> dict:
+        """An empty table in the generator's dict form (keys -1, digests 0,
+        scores 0; values NaN so that a read of an empty slot shows)."""
+        return dict(kind="hash", rows=capacity,
+                    keys=np.full(capacity, -1, np.int64), digests=np.zeros(capacity, np.uint8),
+                    scores=np.zeros(capacity, np.uint64),
+                    values=np.full((capacity, 16), np.nan, np.float32))
+
+    def hash_insert(self, tab: dict, keys: np.ndarray, vals: np.ndarray, mode: int = 0,
+                    step: int = 0) -> np.ndarray:
+        """Insert-or-assign (keys[i], vals[i]) in order into `tab` in place
+        (its keys, digests, scores and values arrays); returns each key's
+        slot, -1 when the table was full, -2 for the empty marker."""
+        keys = np.ascontiguousarray(keys, np.int64)
+        vals = np.ascontiguousarray(vals, np.float32).reshape(-1, 16)
+        assert vals.shape[0] == keys.size
+        for k, t in (("keys", np.int64), ("digests", np.uint8), ("scores", np.uint64),
+                     ("values", np.float32)):
+            assert tab[k].dtype == t and tab[k].flags.c_contiguous, k
+        cap = int(tab["rows"])
+        out = np.empty(keys.size, np.int64)
+        self.lib.orc_hash_insert(_ptr(tab["keys"], P64), _ptr(tab["digests"], P8),
+                                 _ptr(tab["scores"], PU), _ptr(tab["values"], PF), cap,
+                                 _ptr(keys, P64), _ptr(vals, PF), keys.size, int(mode),
+                                 int(step), _ptr(out, P64))
+        return out
+
+    def hash_check(self, keys: np.ndarray, digests: np.ndarray) -> int:
+        """Number of slots that break the table convention (0 for a valid table)."""
+        keys = np.ascontiguousarray(keys, np.int64)
+        digests = np.ascontiguousarray(digests, np.uint8)
+        return int(self.lib.orc_hash_check(_ptr(keys, P64), _ptr(digests, P8), keys.size))
 
     # -- tables --------------------------------------------------------------
     def table(self, tab: dict) -> OrcTable:

@@ -97,6 +97,94 @@ int64_t orc_hash_find(const int64_t* sorted_keys, const int64_t* sorted_slots,
     return (lo < count && sorted_keys[lo] == key) ? sorted_slots[lo] : -1;
 }
 
+/* ---- hash insert ([P2] §6.4: at start-up the tables are rebuilt by
+ * inserting stored key/value pairs; §4.2 score strategies STEP / LFU /
+ * NO_EVICTION; §1 slot = key, score, digest, 16 values) ----------------------
+ * Placement needs the table convention, a data format: h = SplitMix64's
+ * output mix of the key's 64 bits (Steele, Lea & Flood, OOPSLA 2014, with
+ * Stafford's "Mix13" shifts and multipliers), home = floor(h * capacity /
+ * 2^64), digest = the low byte of h (1 in place of 0, since 0 marks an empty
+ * slot), linear probing that wraps, no deletes.  Written here from those
+ * definitions, in 128-bit arithmetic.                                       */
+static uint64_t orc_mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * UINT64_C(0xbf58476d1ce4e5b9);
+    z = (z ^ (z >> 27)) * UINT64_C(0x94d049bb133111eb);
+    return z ^ (z >> 31);
+}
+
+static int64_t orc_home(uint64_t h, int64_t capacity) {
+    __extension__ typedef unsigned __int128 u128;
+    return (int64_t)(((u128)h * (u128)(uint64_t)capacity) >> 64);
+}
+
+static uint8_t orc_digest(uint64_t h) {
+    uint8_t d = (uint8_t)(h & 0xff);
+    return d ? d : 1;
+}
+
+enum { ORC_SCORE_NONE = 0, ORC_SCORE_STEP = 1, ORC_SCORE_LFU = 2 };
+
+/* Insert-or-assign, one pair after another in the given order.  A key that
+ * is stored keeps its slot and takes the new values; a new key takes the
+ * first empty slot of its probe sequence (digest and key written); with no
+ * empty slot on the whole sequence nothing is stored and its slot is -1
+ * (NO_EVICTION: a full table stops accepting keys).  The empty marker is
+ * never stored (slot -2).  Scores: STEP writes `step`, LFU adds one (a new
+ * slot starts from the empty slot's 0), NONE leaves them.                  */
+void orc_hash_insert(int64_t* tkeys, uint8_t* tdig, uint64_t* tscores, float* tvals,
+                     int64_t capacity, const int64_t* keys, const float* vals, int64_t n,
+                     int32_t mode, uint64_t step, int64_t* slot_out) {
+    for (int64_t i = 0; i < n; ++i) {
+        const int64_t key = keys[i];
+        if (key == ORC_EMPTY_KEY) { slot_out[i] = -2; continue; }
+        const uint64_t h = orc_mix64((uint64_t)key);
+        int64_t at = orc_home(h, capacity), slot = -1;
+        int is_new = 0;
+        for (int64_t probes = 0; probes < capacity; ++probes) {
+            if (tkeys[at] == key) { slot = at; break; }
+            if (tkeys[at] == ORC_EMPTY_KEY) { slot = at; is_new = 1; break; }
+            at = (at + 1 == capacity) ? 0 : at + 1;
+        }
+        slot_out[i] = slot;
+        if (slot < 0) continue;
+        if (is_new) {
+            tkeys[slot] = key;
+            tdig[slot] = orc_digest(h);
+        }
+        memcpy(tvals + slot * ORC_DIM, vals + i * ORC_DIM, sizeof(float) * ORC_DIM);
+        if (mode == ORC_SCORE_STEP) tscores[slot] = step;
+        if (mode == ORC_SCORE_LFU) tscores[slot] = tscores[slot] + 1;
+    }
+}
+
+static int orc_i64_cmp(const void* a, const void* b) {
+    int64_t x = *(const int64_t*)a, y = *(const int64_t*)b;
+    return (x > y) - (x < y);
+}
+
+/* Slots that break the convention: an empty slot with a nonzero digest, a
+ * stored key with the wrong digest, a stored key with an empty slot between
+ * its home and its slot (a lookup would miss it), or a key stored twice.    */
+int64_t orc_hash_check(const int64_t* tkeys, const uint8_t* tdig, int64_t capacity) {
+    int64_t bad = 0, n = 0;
+    int64_t* seen = (int64_t*)malloc(sizeof(int64_t) * (size_t)(capacity > 0 ? capacity : 1));
+    for (int64_t s = 0; s < capacity; ++s) {
+        if (tkeys[s] == ORC_EMPTY_KEY) {
+            if (tdig[s] != 0) ++bad;
+            continue;
+        }
+        seen[n++] = tkeys[s];
+        const uint64_t h = orc_mix64((uint64_t)tkeys[s]);
+        if (tdig[s] != orc_digest(h)) ++bad;
+        for (int64_t q = orc_home(h, capacity); q != s; q = (q + 1 == capacity) ? 0 : q + 1)
+            if (tkeys[q] == ORC_EMPTY_KEY) { ++bad; break; }
+    }
+    qsort(seen, (size_t)n, sizeof(int64_t), orc_i64_cmp);
+    for (int64_t i = 1; i < n; ++i) bad += seen[i] == seen[i - 1];
+    free(seen);
+    return bad;
+}
+
 /* One table as the oracle sees it. */
 typedef struct {
     int32_t kind;                 /* 0 direct, 1 hash */

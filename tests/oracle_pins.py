@@ -404,6 +404,104 @@ def pin_towers_library(orc):
     assert np.array_equal(d_s, deep[sub]) and np.array_equal(l_s, lg[sub])
 
 
+def _distinct_keys(rng, n):
+    I64 = np.iinfo(np.int64)
+    k = np.unique(rng.integers(I64.min, I64.max, size=2 * n + 8, dtype=np.int64))
+    return rng.permutation(k[k != synth.EMPTY_KEY])[:n]
+
+
+def _stored_map(tab):
+    occ = np.nonzero(tab["keys"] != synth.EMPTY_KEY)[0]
+    return {int(tab["keys"][s]): tab["values"][s].tobytes() for s in occ}
+
+
+def pin_hash_insert(orc):
+    """The insert side ("集成 DynamicEmb" §6.4 rebuild, §4.2 scores) against the
+    generator's own implementation of the table convention and its
+    round-based builder, dict semantics for insert-or-assign, and planted
+    breaks of the convention."""
+    rng = np.random.default_rng(2024)
+    vals = lambda n: rng.standard_normal((n, 16)).astype(np.float32)
+    # (1) a key into an empty table sits on its home slot with its digest, as
+    # the generator computes them; one key has a zero low byte (digest 1)
+    zero_low = next(k for k in range(1, 10**6)
+                    if int(synth.splitmix64_mix(np.array([k], np.int64))[0]) & 0xFF == 0)
+    keys1 = np.append(_distinct_keys(rng, 12), zero_low)
+    for cap in (1, 2, 7, 1000, 300000):
+        h = synth.splitmix64_mix(keys1)
+        for k, home, dig in zip(keys1, synth.home_slot(h, cap), synth.digest_of(h)):
+            t = orc.empty_hash_table(cap)
+            assert orc.hash_insert(t, np.array([k]), vals(1))[0] == home
+            assert t["keys"][home] == k and t["digests"][home] == dig
+    # (2) key by key against the generator's builder: the same stored map,
+    # every key where its slot says, both tables valid
+    cap, n = 3001, 2400
+    keys, v = _distinct_keys(rng, n), vals(n)
+    t = orc.empty_hash_table(cap)
+    slots = orc.hash_insert(t, keys, v)
+    g = synth.build_hash_table(keys, v, cap)
+    assert np.all(slots >= 0) and np.array_equal(t["keys"][slots], keys)
+    assert orc.hash_check(t["keys"], t["digests"]) == 0
+    assert orc.hash_check(g["keys"], g["digests"]) == 0
+    assert _stored_map(t) == _stored_map(g)
+    # (3) insert-or-assign is a dict update: old keys keep their slots and
+    # take the new values, new keys are added; LFU counts, STEP overwrites
+    expect = {int(k): x.tobytes() for k, x in zip(keys, v)}
+    upd, fresh = rng.choice(keys, 500, replace=False), _distinct_keys(rng, 200)
+    fresh = fresh[~np.isin(fresh, keys)][:100]
+    nu, nf = vals(upd.size), vals(fresh.size)
+    s2 = orc.hash_insert(t, np.concatenate([upd, fresh]), np.concatenate([nu, nf]),
+                         mode=orc.SCORE_LFU)
+    expect.update({int(k): x.tobytes() for k, x in zip(upd, nu)})
+    expect.update({int(k): x.tobytes() for k, x in zip(fresh, nf)})
+    assert _stored_map(t) == expect
+    where = {int(k): int(sl) for k, sl in zip(keys, slots)}
+    assert s2[: upd.size].tolist() == [where[int(k)] for k in upd]
+    assert orc.hash_check(t["keys"], t["digests"]) == 0
+    assert np.all(t["scores"][s2] == 1)
+    orc.hash_insert(t, upd[:50], nu[:50], mode=orc.SCORE_LFU)
+    assert np.all(t["scores"][s2[:50]] == 2) and np.all(t["scores"][s2[50:]] == 1)
+    orc.hash_insert(t, upd[:10], nu[:10], mode=orc.SCORE_STEP, step=77)
+    assert np.all(t["scores"][s2[:10]] == 77) and np.all(t["scores"][s2[10:50]] == 2)
+    # (4) a full table stores nothing more (NO_EVICTION) but still assigns
+    t4 = orc.empty_hash_table(16)
+    k4 = _distinct_keys(rng, 20)
+    s4 = orc.hash_insert(t4, k4, vals(20))
+    assert np.all(s4[:16] >= 0) and np.all(s4[16:] == -1)
+    assert set(t4["keys"].tolist()) == set(k4[:16].tolist())
+    before = t4["keys"].copy()
+    assert orc.hash_insert(t4, k4[3:4], vals(1))[0] == s4[3]
+    assert np.array_equal(t4["keys"], before) and orc.hash_check(t4["keys"], t4["digests"]) == 0
+    # (5) the probe wraps: two keys homed on the last slot take it and slot 0
+    cand = np.arange(1, 5000, dtype=np.int64)
+    last = cand[synth.home_slot(synth.splitmix64_mix(cand), 8) == 7][:2]
+    t5 = orc.empty_hash_table(8)
+    assert list(orc.hash_insert(t5, last, vals(2))) == [7, 0]
+    # (6) the empty marker is never stored
+    t6 = orc.empty_hash_table(5)
+    assert orc.hash_insert(t6, np.array([synth.EMPTY_KEY]), vals(1))[0] == -2
+    assert np.all(t6["keys"] == synth.EMPTY_KEY)
+    # (7) the check flags each kind of break, one at a time
+    occ = np.nonzero(g["keys"] != synth.EMPTY_KEY)[0]
+    homes = synth.home_slot(synth.splitmix64_mix(g["keys"][occ]), cap)
+    bad = g["digests"].copy()
+    bad[occ[0]] ^= 0x80
+    assert orc.hash_check(g["keys"], bad) == 1                        # wrong digest
+    moved = occ[np.nonzero(homes != occ)[0][0]]                       # a key off its home
+    gk, gd = g["keys"].copy(), g["digests"].copy()
+    gk[moved - 1], gd[moved - 1] = synth.EMPTY_KEY, 0                 # hole on its path
+    assert orc.hash_check(gk, gd) >= 1
+    gd2 = g["digests"].copy()
+    gd2[np.nonzero(g["keys"] == synth.EMPTY_KEY)[0][0]] = 5
+    assert orc.hash_check(g["keys"], gd2) == 1                        # digest on an empty slot
+    e = occ[0]                                                        # first empty slot after
+    while g["keys"][e] != synth.EMPTY_KEY:                            # key occ[0]'s cluster
+        e = (e + 1) % cap
+    gk3, gd3 = g["keys"].copy(), g["digests"].copy()
+    gk3[e], gd3[e] = g["keys"][occ[0]], g["digests"][occ[0]]          # a reachable second copy
+    assert orc.hash_check(gk3, gd3) == 1
+
+
 ALL_PINS = [pin_offsets, pin_floor_mod, pin_hash, pin_embbag_direct, pin_embbag_hash,
             pin_din_vs_padded, pin_din_closed_forms, pin_din_hash, pin_towers_closed_forms,
-            pin_towers_library]
+            pin_towers_library, pin_hash_insert]

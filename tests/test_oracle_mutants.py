@@ -58,6 +58,23 @@ MUTANTS = [
     ("logistic sign flipped", "prob[s] = 1.0 / (1.0 + exp(-lg));", "prob[s] = 1.0 / (1.0 + exp(lg));"),
     ("deep tower skips its last layer", "orc_layer(wd3, bd3, d2, 256, 128, z);",
      "for (int c = 0; c < 128; ++c) z[c] = d2[c];"),
+    ("insert probes every other slot", "at = (at + 1 == capacity) ? 0 : at + 1;",
+     "at = (at + 2 >= capacity) ? 0 : at + 2;"),
+    ("insert probe does not wrap", "at = (at + 1 == capacity) ? 0 : at + 1;",
+     "at = (at + 1 == capacity) ? at : at + 1;"),
+    ("home slot by modulo", "return (int64_t)(((u128)h * (u128)(uint64_t)capacity) >> 64);",
+     "return (int64_t)(h % (uint64_t)capacity);"),
+    ("digest keeps a zero byte", "return d ? d : 1;", "return d;"),
+    ("assign stores a second copy", "if (tkeys[at] == key) { slot = at; break; }",
+     "if (0) { slot = at; break; }"),
+    ("LFU overwrites the count", "tscores[slot] = tscores[slot] + 1;", "tscores[slot] = 1;"),
+    ("STEP score not written", "if (mode == ORC_SCORE_STEP) tscores[slot] = step;",
+     "if (0) tscores[slot] = step;"),
+    ("check ignores holes on the path", "if (tkeys[q] == ORC_EMPTY_KEY) { ++bad; break; }",
+     "if (0) { ++bad; break; }"),
+    ("check ignores duplicates", "bad += seen[i] == seen[i - 1];", "bad += 0;"),
+    ("check ignores digests of empty slots", "if (tdig[s] != 0) ++bad;", "if (0) ++bad;"),
+    ("check ignores wrong digests", "if (tdig[s] != orc_digest(h)) ++bad;", "if (0) ++bad;"),
 ]
 
 
