@@ -56,6 +56,7 @@ typedef enum {
 
 enum { REC_DIRECT = 0, REC_HASH = 1 };   /* rec_table.kind */
 enum { REC_F32 = 0, REC_BF16 = 1, REC_BF16_PACKED = 2 };   /* rec_din_mlp.dtype */
+enum { REC_SCORE_NONE = 0, REC_SCORE_STEP = 1, REC_SCORE_LFU = 2 };   /* rec_hash_insert */
 
 #define REC_DIM 16                        /* embedding width of every table */
 #define REC_EMPTY_KEY ((int64_t)-1)       /* empty hash slot; never a valid key */
@@ -226,6 +227,45 @@ rec_status rec_embbag_fwd_kjt(const rec_table* tables, int32_t T, int64_t B,
  */
 rec_status rec_hash_lookup(const rec_table* table, const int64_t* keys, int64_t n,
                            int64_t* slot_out, float* rows_out, void* stream);
+
+/*
+ * Insert-or-assign n (key, values) pairs into a hash table ("集成 DynamicEmb"
+ * §6.4: a service rebuilds its tables at start-up by inserting the stored
+ * key/value pairs; §4.2: score strategies; §1: the slot layout).  The
+ * table's keys, digests, values (and scores) arrays are written.
+ *   table      host descriptor, kind REC_HASH (the REC_HASH conditions above)
+ *   keys       int64[n]
+ *   values     fp32 [n][16], 16-byte aligned
+ *   score_mode REC_SCORE_NONE: scores untouched (table->scores may be NULL);
+ *              REC_SCORE_STEP: the slot's score becomes `step` (STEP evicts
+ *              the oldest); REC_SCORE_LFU: the slot's score grows by one per
+ *              insert (LFU evicts the least used); both need table->scores
+ *   slot_out   int64[n] or NULL: the slot the key is stored in, -1 when the
+ *              table had no empty slot on the key's probe sequence (the pair
+ *              is not stored: no eviction, the NO_EVICTION behaviour), -2 for
+ *              REC_EMPTY_KEY (never stored)
+ * A key already stored keeps its slot and gets the new values and score; a
+ * new key takes the first empty slot of its probe sequence, so the table
+ * keeps the placement convention above.  Which empty slot a new key takes
+ * can depend on the order in which concurrent lanes claim slots; every
+ * lookup result (found or not, and the values) does not.  A key given more
+ * than once in one call is stored once; its values are those of one of its
+ * occurrences (unspecified which) and LFU counts every occurrence.  Nothing
+ * else may read or write the table while the call runs.  Eviction and
+ * frequency admission are not performed.
+ * Errors: REC_EINVAL.
+ */
+rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const float* values,
+                           int64_t n, int32_t score_mode, uint64_t step, int64_t* slot_out,
+                           void* stream);
+
+/*
+ * Empties a hash table: every key becomes REC_EMPTY_KEY, every digest 0 and
+ * every score 0 (when table->scores is not NULL); values are left as they
+ * are.  The start of a rebuild ("集成 DynamicEmb" §6.4).
+ * Errors: REC_EINVAL.
+ */
+rec_status rec_hash_clear(const rec_table* table, void* stream);
 
 /* Bytes of the DIN plan buffer for B samples capped at max_len positions
  * (about 20 bytes per possible position, B * max_len, plus per-sample data);

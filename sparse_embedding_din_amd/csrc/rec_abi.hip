@@ -390,6 +390,54 @@ rec_status rec_hash_lookup(const rec_table* table, const int64_t* keys, int64_t 
     return hip_status(launch_hash_lookup(a, (hipStream_t)stream), "rec_hash_lookup");
 }
 
+rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const float* values,
+                           int64_t n, int32_t score_mode, uint64_t step, int64_t* slot_out,
+                           void* stream) {
+    if (!table) return fail(REC_EINVAL, "rec_hash_insert: table is NULL");
+    if (table->kind != REC_HASH) return fail(REC_EINVAL, "rec_hash_insert: table kind is not REC_HASH");
+    if (n < 0) return fail(REC_EINVAL, "rec_hash_insert: n < 0");
+    if (score_mode != REC_SCORE_NONE && score_mode != REC_SCORE_STEP && score_mode != REC_SCORE_LFU)
+        return fail(REC_EINVAL, "rec_hash_insert: unknown score_mode");
+    if (score_mode != REC_SCORE_NONE && !table->scores)
+        return fail(REC_EINVAL, "rec_hash_insert: this score_mode needs table scores");
+    if (table->scores && ((uintptr_t)table->scores & 7))
+        return fail(REC_EINVAL, "rec_hash_insert: scores not 8-byte aligned");
+    if (n > 0 && (!keys || !values)) return fail(REC_EINVAL, "rec_hash_insert: keys or values is NULL");
+    if (n > 0 && !aligned16(values)) return fail(REC_EINVAL, "rec_hash_insert: values not 16-byte aligned");
+    HashArgs t;
+    memset(&t, 0, sizeof(t));
+    rec_status s = prep_table(*table, "rec_hash_insert: table", &t.tab);
+    if (s != REC_OK) return s;
+    if (n == 0) return ok();
+    HashInsArgs a;
+    a.keys = const_cast<int64_t*>(table->keys);
+    a.digests = const_cast<uint8_t*>(table->digests);
+    a.scores = const_cast<uint64_t*>(table->scores);
+    a.values = const_cast<float*>(table->values);
+    a.capacity = table->rows;
+    a.in_keys = keys;
+    a.in_values = values;
+    a.n = n;
+    a.mode = score_mode;
+    a.step = step;
+    a.slot_out = slot_out;
+    return hip_status(launch_hash_insert(a, (hipStream_t)stream), "rec_hash_insert");
+}
+
+rec_status rec_hash_clear(const rec_table* table, void* stream) {
+    if (!table) return fail(REC_EINVAL, "rec_hash_clear: table is NULL");
+    if (table->kind != REC_HASH) return fail(REC_EINVAL, "rec_hash_clear: table kind is not REC_HASH");
+    if (table->scores && ((uintptr_t)table->scores & 7))
+        return fail(REC_EINVAL, "rec_hash_clear: scores not 8-byte aligned");
+    HashArgs t;
+    memset(&t, 0, sizeof(t));
+    rec_status s = prep_table(*table, "rec_hash_clear: table", &t.tab);
+    if (s != REC_OK) return s;
+    return hip_status(launch_hash_clear(const_cast<int64_t*>(table->keys), const_cast<uint8_t*>(table->digests),
+                                        const_cast<uint64_t*>(table->scores), table->rows, (hipStream_t)stream),
+                      "rec_hash_clear");
+}
+
 rec_status rec_din_pack_mlp(const rec_din_mlp* mlp, void* packed, size_t packed_bytes, void* stream) {
     if (!mlp) return fail(REC_EINVAL, "rec_din_pack_mlp: mlp is NULL");
     if (mlp->dtype != REC_BF16) return fail(REC_EINVAL, "rec_din_pack_mlp: dtype must be REC_BF16");

@@ -1,0 +1,91 @@
+// Hash-table write side: insert-or-assign of (key, values) pairs and clearing.
+//
+// Pages: "MultiTowerDIN：集成 DynamicEmb" §6.4 (at start-up a service rebuilds
+// each table by inserting its stored key/value pairs), §4.2 (score strategies
+// STEP / LFU / NO_EVICTION), §1 (a slot: key, score, digest, 16 values).
+//
+// One lane per pair walks the key's probe sequence (the table convention of
+// rec_internal.h: SplitMix64 mix, multiply-high home slot, linear wrapping
+// probes).  A slot holding the key is found; an empty slot is claimed with a
+// 64-bit compare-and-swap of its key, so two lanes never take the same slot,
+// and a lane that loses the swap to its own key (a duplicate in the batch)
+// has found it.  Keys only ever go from empty to a key, so a stale read can
+// only show a slot as empty; the swap then fails and reports the key that is
+// there.  The winner writes the digest; every lane that placed its key writes
+// the values and the score.  With no empty slot on the whole sequence the
+// pair is not stored (no eviction).
+#include "rec_internal.h"
+
+namespace rec {
+namespace {
+
+__global__ __launch_bounds__(256) void k_hash_insert(const HashInsArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.n) return;
+    const int64_t key = a.in_keys[i];
+    int64_t slot = -2;                        // the empty marker is never stored
+    if (key != REC_EMPTY_KEY) {
+        const uint64_t h = mix64((uint64_t)key);
+        int64_t at = hash_home(h, a.capacity);
+        bool claimed = false;
+        slot = -1;
+        for (int64_t probes = 0; probes < a.capacity; ++probes) {
+            const int64_t cur = __hip_atomic_load(a.keys + at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (cur == key) {
+                slot = at;
+                break;
+            }
+            if (cur == REC_EMPTY_KEY) {
+                int64_t seen = REC_EMPTY_KEY;
+                if (__hip_atomic_compare_exchange_strong(a.keys + at, &seen, key, __ATOMIC_RELAXED,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                    slot = at;
+                    claimed = true;
+                    break;
+                }
+                if (seen == key) {
+                    slot = at;
+                    break;
+                }
+            }
+            at = at + 1 == a.capacity ? 0 : at + 1;
+        }
+        if (slot >= 0) {
+            if (claimed) a.digests[slot] = (uint8_t)hash_digest(h);
+            const float4* src = (const float4*)(a.in_values + i * 16);
+            float4* dst = (float4*)(a.values + slot * 16);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[r] = src[r];
+            if (a.mode == REC_SCORE_STEP) a.scores[slot] = a.step;
+            if (a.mode == REC_SCORE_LFU)
+                __hip_atomic_fetch_add(a.scores + slot, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (a.slot_out) a.slot_out[i] = slot;
+}
+
+__global__ __launch_bounds__(256) void k_hash_clear(int64_t* keys, uint8_t* digests, uint64_t* scores,
+                                                    int64_t capacity) {
+    for (int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x; s < capacity; s += (int64_t)gridDim.x * 256) {
+        keys[s] = REC_EMPTY_KEY;
+        digests[s] = 0;
+        if (scores) scores[s] = 0;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_hash_insert(const HashInsArgs& a, hipStream_t s) {
+    const int64_t blocks = (a.n + 255) / 256;
+    hipLaunchKernelGGL(k_hash_insert, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_hash_clear(int64_t* keys, uint8_t* digests, uint64_t* scores, int64_t capacity,
+                             hipStream_t s) {
+    const int64_t blocks = min((capacity + 255) / 256, (int64_t)4096);
+    hipLaunchKernelGGL(k_hash_clear, dim3((unsigned)blocks), dim3(256), 0, s, keys, digests, scores, capacity);
+    return hipGetLastError();
+}
+
+}  // namespace rec

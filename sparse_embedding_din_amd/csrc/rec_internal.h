@@ -307,6 +307,23 @@ struct HashArgs {
 };
 hipError_t launch_hash_lookup(const HashArgs& a, hipStream_t s);
 
+struct HashInsArgs {
+    int64_t* keys;              // the table's arrays, written
+    uint8_t* digests;
+    uint64_t* scores;           // NULL unless mode != REC_SCORE_NONE
+    float* values;
+    int64_t capacity;
+    const int64_t* in_keys;     // the pairs
+    const float* in_values;
+    int64_t n;
+    int32_t mode;
+    uint64_t step;
+    int64_t* slot_out;
+};
+hipError_t launch_hash_insert(const HashInsArgs& a, hipStream_t s);
+hipError_t launch_hash_clear(int64_t* keys, uint8_t* digests, uint64_t* scores, int64_t capacity,
+                             hipStream_t s);
+
 struct DinArgs {
     TabDev tab[3];
     const float* query;

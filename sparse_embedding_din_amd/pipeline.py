@@ -51,6 +51,16 @@ class DeviceTables:
                 self.tensors.append((vals,))
                 self.desc.append(R.table(R.REC_DIRECT, int(tab["rows"]), vals))
 
+    def to_host(self, i: int) -> dict:
+        """Table i copied back to host numpy arrays (the generator's dict form)."""
+        t = self.tensors[i]
+        out = dict(kind="hash" if len(t) == 4 else "direct", rows=int(self.desc[i].rows),
+                   values=t[0].cpu().numpy())
+        if len(t) == 4:
+            out.update(keys=t[1].cpu().numpy(), digests=t[2].cpu().numpy(),
+                       scores=t[3].cpu().numpy().view(np.uint64))
+        return out
+
     def array(self, idx: Optional[Sequence[int]] = None):
         sel = self.desc if idx is None else [self.desc[i] for i in idx]
         arr = (R.rec_table * len(sel))()

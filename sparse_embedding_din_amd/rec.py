@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "librec.so")
 REC_OK, REC_EINVAL, REC_EUNSUPPORTED, REC_EHIP, REC_EWORKSPACE = 0, -1, -2, -3, -4
 REC_DIRECT, REC_HASH = 0, 1
 REC_F32, REC_BF16, REC_BF16_PACKED = 0, 1, 2
+REC_SCORE_NONE, REC_SCORE_STEP, REC_SCORE_LFU = 0, 1, 2
 REC_DIN_PACKED_BYTES = 131072
 REC_TOWER_PACKED_BYTES = 614400
 REC_DIM = 16
@@ -28,6 +29,7 @@ REC_MAX_B = 16777215
 
 EXPORTS = ["rec_din_pack_mlp", "rec_scan_workspace_bytes", "rec_lengths_to_offsets", "rec_embbag_fwd",
            "rec_kjt_sums_bytes", "rec_kjt_sums", "rec_embbag_fwd_kjt", "rec_hash_lookup",
+           "rec_hash_insert", "rec_hash_clear",
            "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_fwd",
            "rec_sparse_din_fwd_workspace_bytes", "rec_sparse_din_fwd", "rec_towers_fwd",
            "rec_tower_pack_mlp",
@@ -93,6 +95,8 @@ def lib():
         L.rec_embbag_fwd_kjt.argtypes = [C.POINTER(rec_table), i32, i64, vp, vp, vp, sz, vp, vp, vp,
                                          vp]
         L.rec_hash_lookup.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, vp]
+        L.rec_hash_insert.argtypes = [C.POINTER(rec_table), vp, vp, i64, i32, C.c_uint64, vp, vp]
+        L.rec_hash_clear.argtypes = [C.POINTER(rec_table), vp]
         L.rec_din_plan_bytes.argtypes = [i64, i32]
         L.rec_din_plan_bytes.restype = sz
         L.rec_din_plan.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, i64, i32, i32, vp, vp,
@@ -107,7 +111,7 @@ def lib():
         L.rec_towers_fwd.argtypes = [C.POINTER(rec_tower_mlp), i64, vp, i64, vp, vp, vp, vp, vp]
         L.rec_tower_pack_mlp.argtypes = [C.POINTER(rec_tower_mlp), vp, sz, vp]
         for f in ("rec_lengths_to_offsets", "rec_embbag_fwd", "rec_kjt_sums", "rec_embbag_fwd_kjt",
-                  "rec_hash_lookup", "rec_din_plan",
+                  "rec_hash_lookup", "rec_hash_insert", "rec_hash_clear", "rec_din_plan",
                   "rec_din_attn_fwd", "rec_din_pack_mlp", "rec_sparse_din_fwd", "rec_towers_fwd",
                   "rec_tower_pack_mlp"):
             getattr(L, f).restype = C.c_int
@@ -215,6 +219,18 @@ def rec_embbag_fwd_kjt(tables: Sequence[rec_table], T: int, B: int, values, leng
 def rec_hash_lookup(table_: rec_table, keys, n: int, slot_out=None, rows_out=None, stream=None):
     _check(lib().rec_hash_lookup(C.byref(table_), _p(keys), n, _p(slot_out), _p(rows_out),
                                  _stream(stream)), "rec_hash_lookup")
+
+
+def rec_hash_insert(table_: rec_table, keys, values, n: int, score_mode: int = REC_SCORE_NONE,
+                    step: int = 0, slot_out=None, stream=None):
+    _check(lib().rec_hash_insert(C.byref(table_) if table_ is not None else None, _p(keys),
+                                 _p(values), n, score_mode, step, _p(slot_out), _stream(stream)),
+           "rec_hash_insert")
+
+
+def rec_hash_clear(table_: rec_table, stream=None):
+    _check(lib().rec_hash_clear(C.byref(table_) if table_ is not None else None, _stream(stream)),
+           "rec_hash_clear")
 
 
 def rec_din_pack_mlp(mlp: rec_din_mlp, packed, packed_bytes: int, stream=None):

@@ -154,6 +154,50 @@ def test_hash_lookup_errors(lib):
     assert _status(lib.rec_hash_lookup, C.byref(h), FAKE, 0, FAKE, None, None)[0] == R.REC_OK
 
 
+def test_hash_insert_errors(lib):
+    """Every bad argument is refused before any device call; n == 0 is a no-op."""
+    def tab(**kw):
+        t = _table(kind=R.REC_HASH, keys=FAKE, digests=FAKE)
+        for k, v in kw.items():
+            setattr(t, k, v)
+        return t
+    h, hs = tab(), tab(scores=FAKE)
+    ins = lib.rec_hash_insert
+    assert _status(ins, None, FAKE, FAKE, 4, 0, 0, None, None)[0] == R.REC_EINVAL
+    s, msg = _status(ins, C.byref(_table()), FAKE, FAKE, 4, 0, 0, None, None)
+    assert s == R.REC_EINVAL and "REC_HASH" in msg
+    assert _status(ins, C.byref(h), FAKE, FAKE, -1, 0, 0, None, None)[0] == R.REC_EINVAL
+    s, msg = _status(ins, C.byref(hs), FAKE, FAKE, 4, 3, 0, None, None)
+    assert s == R.REC_EINVAL and "score_mode" in msg
+    for mode in (R.REC_SCORE_STEP, R.REC_SCORE_LFU):
+        s, msg = _status(ins, C.byref(h), FAKE, FAKE, 4, mode, 0, None, None)
+        assert s == R.REC_EINVAL and "scores" in msg
+    assert _status(ins, C.byref(tab(scores=FAKE_ODD)), FAKE, FAKE, 4, 1, 0, None, None)[0] == \
+        R.REC_EINVAL
+    assert _status(ins, C.byref(h), None, FAKE, 4, 0, 0, None, None)[0] == R.REC_EINVAL
+    assert _status(ins, C.byref(h), FAKE, None, 4, 0, 0, None, None)[0] == R.REC_EINVAL
+    assert _status(ins, C.byref(h), FAKE, FAKE_ODD, 4, 0, 0, None, None)[0] == R.REC_EINVAL
+    assert _status(ins, C.byref(tab(digests=FAKE_ODD)), FAKE, FAKE, 4, 0, 0, None, None)[0] == \
+        R.REC_EINVAL
+    assert _status(ins, C.byref(tab(rows=0)), FAKE, FAKE, 4, 0, 0, None, None)[0] == R.REC_EINVAL
+    assert _status(ins, C.byref(tab(dim=8)), FAKE, FAKE, 4, 0, 0, None, None)[0] == R.REC_EINVAL
+    assert _status(ins, C.byref(hs), None, None, 0, 2, 5, None, None)[0] == R.REC_OK
+    with pytest.raises(R.RecError):
+        R.rec_hash_insert(_table(), FAKE, FAKE, 4)
+
+
+def test_hash_clear_errors(lib):
+    clr = lib.rec_hash_clear
+    assert _status(clr, None, None)[0] == R.REC_EINVAL
+    s, msg = _status(clr, C.byref(_table()), None)
+    assert s == R.REC_EINVAL and "REC_HASH" in msg
+    t = _table(kind=R.REC_HASH, keys=FAKE, digests=FAKE)
+    t.scores = FAKE_ODD
+    assert _status(clr, C.byref(t), None)[0] == R.REC_EINVAL
+    assert _status(clr, C.byref(_table(kind=R.REC_HASH, keys=None, digests=FAKE)), None)[0] == \
+        R.REC_EINVAL
+
+
 def test_din_pack_errors(lib):
     m = R.din_mlp(R.REC_F32, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0)
     assert _status(lib.rec_din_pack_mlp, C.byref(m), FAKE, R.REC_DIN_PACKED_BYTES, None)[0] == R.REC_EINVAL
