@@ -36,6 +36,8 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 matrix/vector
 
 # algorithmic bytes (what the method must move) and flops per unit
+INSERT_BYTES_PER_KEY = 8 + 64 + 8 + 1 + 64 + 8   # read key + values; write key, digest, values, score
+CLEAR_BYTES_PER_SLOT = 8 + 1 + 8                 # key, digest, score
 EMB_BYTES_PER_ID = 8 + 64                  # raw id + one 64-byte row
 EMB_BYTES_PER_BAG = 4 + 8 + 64             # length + offset + pooled output
 DIN_BYTES_PER_POS = 3 * (8 + 64)           # three ids + three rows
@@ -63,6 +65,8 @@ def parse():
                    help="run the sequence plan on a second stream (pays off when the plan is long, "
                         "e.g. hash-table sequence ids)")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-hash-rebuild", action="store_true",
+                   help="skip timing the rebuild of the hash workload's tables (clear + insert)")
     p.add_argument("--no-towers", action="store_true",
                    help="skip the deep tower + final MLP measurement")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -91,7 +95,7 @@ def src_hash() -> str:
 CAL_BYTES = 64 << 20            # bytes read (and written) by the calibration copy
 KERNELS = {"k_din_attn": "k_din_attn",
            "k_embbag_fwd": "k_embbag_fwd<", "k_fwd_gather": "k_fwd_gather", "k_fwd_sums": "k_fwd_sums",
-           "k_towers_bf16": "k_towers_bf16", "copy": "MulFunctor"}
+           "k_towers_bf16": "k_towers_bf16", "k_hash_insert": "k_hash_insert", "copy": "MulFunctor"}
 
 
 def load_traffic(kernels, shash: str, config: str):
@@ -340,6 +344,64 @@ def main():
                   "full_forward_ms_per_step": None if full_ms is None else round(full_ms, 5),
                   "full_forward_samples_s": None if full_ms is None else round(B / (full_ms * 1e-3), 1)}
 
+    rebuild = None
+    if not a.no_hash_rebuild:
+        # The start-up rebuild of the hash workload's tables ("集成 DynamicEmb"
+        # §6.4: 5 tables, keys and values inserted from storage): clear each
+        # table, then insert its stored pairs with STEP scores.
+        hcfg = synth.CONFIGS[5]
+        hm = model if cfg.hash_keys else synth.make_model(hcfg)
+        htabs = PL.DeviceTables([hm.tables[k] for k in hcfg.hash_keys], dev)
+        hk, hv = [], []
+        for k in hcfg.hash_keys:
+            t = hm.tables[k]
+            occ = np.nonzero(t["keys"] != R.REC_EMPTY_KEY)[0]
+            hk.append(torch.from_numpy(t["keys"][occ]).to(dev))
+            hv.append(torch.from_numpy(np.ascontiguousarray(t["values"][occ])).to(dev))
+        nkeys = sum(x.numel() for x in hk)
+
+        def rebuild_tables(ev=None):
+            for i in range(len(hk)):
+                R.rec_hash_clear(htabs.desc[i], stream=stream)
+                if ev is not None:
+                    ev[i][0].record(stream)
+                R.rec_hash_insert(htabs.desc[i], hk[i], hv[i], hk[i].numel(), R.REC_SCORE_STEP, 1,
+                                  stream=stream)
+                if ev is not None:
+                    ev[i][1].record(stream)
+
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                rebuild_tables()
+            torch.cuda.synchronize()
+            reps_r = 10
+            r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for _ in hk] for _ in range(reps_r)]
+            torch.cuda._sleep(20_000_000)
+            r0.record(stream)
+            for r in range(reps_r):
+                rebuild_tables(evs[r])
+            r1.record(stream)
+            torch.cuda.synchronize()
+        total_us = r0.elapsed_time(r1) * 1e3 / reps_r
+        ins = np.array([[s_.elapsed_time(e_) * 1e3 for s_, e_ in row] for row in evs])
+        ins_us = float(ins.mean())
+        per_table = nkeys / len(hk)
+        ins_gbs = INSERT_BYTES_PER_KEY * per_table / (ins_us * 1e-6) / 1e9
+        rebuild = {"entry": "rec_hash_clear + rec_hash_insert (STEP scores), per table",
+                   "tables": len(hk), "capacity": hcfg.hash_capacity, "keys": int(nkeys),
+                   "us_all_tables": round(total_us, 2),
+                   "keys_per_s": round(nkeys / (total_us * 1e-6), 1),
+                   "insert_avg_launch_us": round(ins_us, 3),
+                   "insert_algorithmic_gb_s": round(ins_gbs, 1),
+                   "insert_hbm_frac": round(ins_gbs / HBM_PEAK_GBS, 4),
+                   "bytes_per_key": INSERT_BYTES_PER_KEY,
+                   "traffic": load_traffic(["k_hash_insert"], shash, cfg.name),
+                   "pages": "about 100-500 ms for 1.5M keys on the GPU (context, another machine)"}
+        print(f"[bench] hash rebuild: {nkeys} keys in {total_us:.1f} us ({ins_us:.2f} us per insert launch)",
+              file=sys.stderr, flush=True)
+
     cpu = None
     if not a.no_cpu:
         import oracle
@@ -384,6 +446,7 @@ def main():
         "din": {"tflops": round(din_tflops, 2), "mfma_frac": round(din_tflops / peak_mfma, 4),
                 "gb_s": round(din_bytes / din_t / 1e9, 1)},
         "towers": towers,
+        "hash_rebuild": rebuild,
         "src_hash": shash,
     }
     if a.calibrate_copy:
