@@ -77,6 +77,8 @@ class Oracle:
         L.orc_hash_insert.restype = None
         L.orc_hash_check.argtypes = [P64, P8, C.c_int64]
         L.orc_hash_check.restype = C.c_int64
+        L.orc_dlrm_interact.argtypes = [PF, C.c_int64, C.c_int32, C.c_int32, PD, PD]
+        L.orc_dlrm_interact.restype = None
         self._keep = []
 
     # -- bookkeeping ---------------------------------------------------------
@@ -125,6 +127,19 @@ class Oracle:
         keys = np.ascontiguousarray(keys, np.int64)
         digests = np.ascontiguousarray(digests, np.uint8)
         return int(self.lib.orc_hash_check(_ptr(keys, P64), _ptr(digests, P8), keys.size))
+
+    # -- DLRM interaction --------------------------------------------------------
+    def dlrm_interact(self, z: np.ndarray, want_scale: bool = False):
+        """z [B][F][d] fp32 -> the upper triangle (with the diagonal) of each
+        sample's Gram matrix, [B][F(F+1)/2] fp64, row by row; with want_scale
+        also sum_k |z_ik z_jk| per entry."""
+        z = np.ascontiguousarray(z, np.float32)
+        B, F, d = z.shape
+        out = np.empty((B, F * (F + 1) // 2), np.float64)
+        sc = np.empty_like(out) if want_scale else None
+        self.lib.orc_dlrm_interact(_ptr(z, PF), B, F, d, _ptr(out, PD),
+                                   None if sc is None else _ptr(sc, PD))
+        return (out, sc) if want_scale else out
 
     # -- tables --------------------------------------------------------------
     def table(self, tab: dict) -> OrcTable:

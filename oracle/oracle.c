@@ -185,6 +185,34 @@ int64_t orc_hash_check(const int64_t* tkeys, const uint8_t* tdig, int64_t capaci
     return bad;
 }
 
+/* ---- DLRM dot-product interaction ([P3] DLRM essay §2.3, §3.1, §4.2: the
+ * interaction layer takes, per sample, the bottom MLP's output and every
+ * pooled embedding, F vectors of width d, and emits the dot product of every
+ * pair i <= j -- the upper triangle with the diagonal, as the essay's loop runs
+ * j from i -- row by row: (0,0), (0,1), ..., (0,F-1), (1,1), ...) ----------
+ * z [B][F][d]; out [B][F(F+1)/2]; scale (or NULL) gets sum_k |z_ik z_jk|,
+ * the size of each dot product's terms.                                    */
+void orc_dlrm_interact(const float* z, int64_t B, int32_t F, int32_t d, double* out, double* scale) {
+    const int64_t npairs = (int64_t)F * (F + 1) / 2;
+    for (int64_t b = 0; b < B; ++b) {
+        const float* zb = z + b * F * d;
+        int64_t o = b * npairs;
+        for (int32_t i = 0; i < F; ++i) {
+            for (int32_t j = i; j < F; ++j) {
+                double acc = 0.0, mag = 0.0;
+                for (int32_t k = 0; k < d; ++k) {
+                    const double t = (double)zb[(int64_t)i * d + k] * (double)zb[(int64_t)j * d + k];
+                    acc += t;
+                    mag += fabs(t);
+                }
+                out[o] = acc;
+                if (scale) scale[o] = mag;
+                ++o;
+            }
+        }
+    }
+}
+
 /* One table as the oracle sees it. */
 typedef struct {
     int32_t kind;                 /* 0 direct, 1 hash */

@@ -502,6 +502,38 @@ def pin_hash_insert(orc):
     assert orc.hash_check(gk3, gd3) == 1
 
 
+def pin_dlrm_interact(orc):
+    """DLRM dot-product interaction (DLRM essay §2.3, §4.2) against torch fp64
+    bmm with triu_indices (row-major, diagonal included), and closed forms:
+    orthonormal rows give the identity's triangle, F copies of one vector give
+    |v|^2 everywhere, a power-of-two scale c scales every entry by c^2 exactly,
+    and F = 1 gives the squared norm."""
+    rng = np.random.default_rng(77)
+    for B, F, d in ((3, 1, 4), (2, 5, 8), (4, 27, 96), (1, 217, 96)):
+        z = rng.standard_normal((B, F, d)).astype(np.float32)
+        got, sc = orc.dlrm_interact(z, want_scale=True)
+        assert got.shape == (B, F * (F + 1) // 2)
+        zt = torch.from_numpy(z).double()
+        gram = torch.bmm(zt, zt.transpose(1, 2).contiguous())
+        iu = torch.triu_indices(F, F)
+        ref = gram[:, iu[0], iu[1]].numpy()
+        assert np.max(np.abs(got - ref) / np.maximum(sc, 1e-300)) < 1e-13
+        absg = torch.bmm(zt.abs(), zt.abs().transpose(1, 2).contiguous())[:, iu[0], iu[1]].numpy()
+        assert np.allclose(sc, absg, rtol=1e-12, atol=0)
+        z4 = (z * 4.0).astype(np.float32)
+        assert np.array_equal(orc.dlrm_interact(z4), 16.0 * got)
+    F, d = 6, 8
+    eye = np.zeros((1, F, d), np.float32)
+    eye[0, np.arange(F), np.arange(F)] = 1.0
+    iu = np.triu_indices(F)
+    assert np.array_equal(orc.dlrm_interact(eye)[0], (iu[0] == iu[1]).astype(np.float64))
+    v = rng.standard_normal(d).astype(np.float32)
+    same = np.tile(v, (1, F, 1))
+    n2 = float(np.dot(v.astype(np.float64), v.astype(np.float64)))
+    assert np.allclose(orc.dlrm_interact(same)[0], n2, rtol=1e-15, atol=0)
+    assert np.allclose(orc.dlrm_interact(v.reshape(1, 1, d))[0], [n2], rtol=1e-15, atol=0)
+
+
 ALL_PINS = [pin_offsets, pin_floor_mod, pin_hash, pin_embbag_direct, pin_embbag_hash,
             pin_din_vs_padded, pin_din_closed_forms, pin_din_hash, pin_towers_closed_forms,
-            pin_towers_library, pin_hash_insert]
+            pin_towers_library, pin_hash_insert, pin_dlrm_interact]

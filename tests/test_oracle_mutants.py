@@ -75,6 +75,13 @@ MUTANTS = [
     ("check ignores duplicates", "bad += seen[i] == seen[i - 1];", "bad += 0;"),
     ("check ignores digests of empty slots", "if (tdig[s] != 0) ++bad;", "if (0) ++bad;"),
     ("check ignores wrong digests", "if (tdig[s] != orc_digest(h)) ++bad;", "if (0) ++bad;"),
+    ("interaction without the diagonal", "for (int32_t j = i; j < F; ++j) {",
+     "for (int32_t j = i + 1; j < F; ++j) {"),
+    ("interaction squares the row", "(double)zb[(int64_t)j * d + k];", "(double)zb[(int64_t)i * d + k];"),
+    ("interaction drops the last component", "for (int32_t k = 0; k < d; ++k) {",
+     "for (int32_t k = 0; k + 1 < d; ++k) {"),
+    ("interaction column-major", "out[o] = acc;",
+     "out[b * npairs + (int64_t)j * (j + 1) / 2 + i] = acc;"),
 ]
 
 
