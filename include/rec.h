@@ -260,6 +260,25 @@ rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const fl
                            void* stream);
 
 /*
+ * DLRM dot-product interaction (DLRM essay, wmrh.cn/news/12459, §2.3: the
+ * interaction layer takes the bottom MLP's output and every pooled embedding
+ * and emits their pairwise dot products; §4.2: its code runs j from i, so the
+ * diagonal is included; §3.1: measured at 217 features of width 96).
+ *   z    fp32 [B][F][d], 16-byte aligned: sample b's F vectors (the bottom
+ *        MLP's output first, then the pooled embeddings, in the caller's order)
+ *   out  fp32 [B][F(F+1)/2]: out[b][p] = <z[b][i], z[b][j]> for the p-th pair
+ *        i <= j in row order (0,0), (0,1), ..., (0,F-1), (1,1), ..., (F-1,F-1)
+ * fp32 products with fp32 accumulation (on the matrix cores); the summation
+ * order is not the sequential one, so results match an fp64 reference to a
+ * few fp32 ulps of sum_k |z_ik z_jk|.
+ * Limits: 1 <= F <= 256; d a multiple of 16, 16 <= d <= 512; the sample must
+ * fit the kernel's LDS stage: 16 * ceil(F / 16) * (d + 4) * 4 bytes <= 144 KiB
+ * (F = 217 allows d up to 160).
+ * Errors: REC_EINVAL, REC_EUNSUPPORTED (shape beyond the limits).
+ */
+rec_status rec_dlrm_interact(const float* z, int64_t B, int32_t F, int32_t d, float* out, void* stream);
+
+/*
  * Empties a hash table: every key becomes REC_EMPTY_KEY, every digest 0 and
  * every score 0 (when table->scores is not NULL); values are left as they
  * are.  The start of a rebuild ("集成 DynamicEmb" §6.4).

@@ -424,6 +424,21 @@ rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const fl
     return hip_status(launch_hash_insert(a, (hipStream_t)stream), "rec_hash_insert");
 }
 
+rec_status rec_dlrm_interact(const float* z, int64_t B, int32_t F, int32_t d, float* out, void* stream) {
+    if (B < 0) return fail(REC_EINVAL, "rec_dlrm_interact: B < 0");
+    if (F < 1) return fail(REC_EINVAL, "rec_dlrm_interact: F < 1");
+    if (d < 16 || d % 16 != 0) return fail(REC_EINVAL, "rec_dlrm_interact: d must be a positive multiple of 16");
+    if (F > 256 || d > 512) return fail(REC_EUNSUPPORTED, "rec_dlrm_interact: F above 256 or d above 512");
+    if ((int64_t)16 * ((F + 15) / 16) * dlrm_stride(d) > kDlrmMaxLdsFloats)
+        return fail(REC_EUNSUPPORTED, "rec_dlrm_interact: F x d does not fit the 144 KiB LDS stage");
+    if (B > 0 && (!z || !out)) return fail(REC_EINVAL, "rec_dlrm_interact: z or out is NULL");
+    if (B > 0 && !aligned16(z)) return fail(REC_EINVAL, "rec_dlrm_interact: z not 16-byte aligned");
+    if (B == 0) return ok();
+    const int cus = num_cus();
+    if (cus < 1) return fail(REC_EHIP, "rec_dlrm_interact: cannot query the device");
+    return hip_status(launch_dlrm_interact(z, B, F, d, out, cus, (hipStream_t)stream), "rec_dlrm_interact");
+}
+
 rec_status rec_hash_clear(const rec_table* table, void* stream) {
     if (!table) return fail(REC_EINVAL, "rec_hash_clear: table is NULL");
     if (table->kind != REC_HASH) return fail(REC_EINVAL, "rec_hash_clear: table kind is not REC_HASH");

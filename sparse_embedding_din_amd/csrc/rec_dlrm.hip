@@ -1,0 +1,97 @@
+// DLRM dot-product interaction: per sample, the dot product of every pair
+// i <= j of its F vectors of width d, row by row.
+//
+// Pages: DLRM essay (wmrh.cn/news/12459) §2.3 (the interaction layer takes
+// the bottom MLP's output and every pooled embedding and emits their pairwise
+// dot products, one triangle only), §4.2 (its code runs j from i, so the
+// diagonal is included), §3.1 (the measured case: 217 features, width 96).
+//
+// On the matrix cores.  A sample's vectors form a small matrix Z [F][d] and
+// the output is the upper triangle of Z Z^T, so each 16 x 16 tile of it is a
+// run of v_mfma_f32_16x16x4f32 over d (fp32 in, fp32 accumulate; the fp32
+// matrix rate is twice the unpacked fp32 vector rate).  One workgroup per
+// sample, persistent over samples: Z is staged in LDS once, rows padded to a
+// multiple of 16 with zeros, with a row stride that puts the 16 rows of an
+// operand read on distinct banks; the T(T+1)/2 tile pairs I <= J of the
+// T = ceil(F / 16) row tiles are dealt to the four waves in turn.  Both
+// operands want row m of their tile in lane (m, g) at lane group g's K
+// positions; giving lane group g the contiguous quarter [g d/4, (g+1) d/4) of
+// d (any K order is right when both operands use it) lets a lane read four K
+// steps with one 16-byte read, and those four steps feed four independent
+// accumulators, summed at the end.
+#include "rec_internal.h"
+#include "rec_mfma.h"
+
+namespace rec {
+namespace {
+
+constexpr int kDlrmWaves = 4;
+
+__global__ __launch_bounds__(64 * kDlrmWaves) void k_dlrm_interact(const float* __restrict__ z, int64_t B,
+                                                                   int F, int d, int stride,
+                                                                   float* __restrict__ out) {
+    __shared__ __attribute__((aligned(16))) float s_z[kDlrmMaxLdsFloats];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 15, g = lane >> 4;
+    const int T = (F + 15) / 16;
+    const int dq = d / 4;                       // a lane group's share of d (a multiple of 4)
+    const int nv = d / 4;                       // float4s per row
+    const int64_t npairs = (int64_t)F * (F + 1) / 2;
+    const int ntile = T * (T + 1) / 2;
+    for (int64_t b = blockIdx.x; b < B; b += gridDim.x) {
+        const float4* src = (const float4*)(z + b * (int64_t)F * d);
+        for (int v = threadIdx.x; v < 16 * T * nv; v += 64 * kDlrmWaves) {
+            const int r = v / nv, c = v - r * nv;
+            const float4 x = r < F ? src[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+            *(float4*)(s_z + r * stride + 4 * c) = x;
+        }
+        __syncthreads();
+        for (int t = wave; t < ntile; t += kDlrmWaves) {
+            int I = 0, rem = t;                     // tile pair t, row by row
+            while (rem >= T - I) {
+                rem -= T - I;
+                ++I;
+            }
+            const int J = I + rem;
+            const float* ra = s_z + (I * 16 + m) * stride + g * dq;
+            const float* rb = s_z + (J * 16 + m) * stride + g * dq;
+            f32x4 acc[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int k = 0; k < dq; k += 4) {
+                const float4 av = *(const float4*)(ra + k);
+                const float4 bv = *(const float4*)(rb + k);
+                acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc[1], 0, 0, 0);
+                acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc[2], 0, 0, 0);
+                acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc[3], 0, 0, 0);
+            }
+            const f32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            // lane (m, g) holds rows 4g..4g+3 of the tile in column m
+            const int j = J * 16 + m;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = I * 16 + 4 * g + r;
+                if (i < F && j < F && i <= j) {
+                    const int64_t row = (int64_t)i * F - (int64_t)i * (i - 1) / 2;   // pairs before row i
+                    out[b * npairs + row + (j - i)] = sum[r];
+                }
+            }
+        }
+        __syncthreads();                        // before the next sample overwrites Z
+    }
+}
+
+}  // namespace
+
+int dlrm_stride(int d) { return (d / 4) % 2 == 0 ? d + 4 : d; }
+
+hipError_t launch_dlrm_interact(const float* z, int64_t B, int F, int d, float* out, int num_cus,
+                                hipStream_t s) {
+    const int64_t grid = B < num_cus ? B : num_cus;
+    hipLaunchKernelGGL(k_dlrm_interact, dim3((unsigned)grid), dim3(64 * kDlrmWaves), 0, s, z, B, F, d,
+                       dlrm_stride(d), out);
+    return hipGetLastError();
+}
+
+}  // namespace rec

@@ -321,6 +321,13 @@ struct HashInsArgs {
     int64_t* slot_out;
 };
 hipError_t launch_hash_insert(const HashInsArgs& a, hipStream_t s);
+
+// DLRM interaction: Z staged in LDS as 16 * ceil(F / 16) rows of dlrm_stride(d)
+// floats, at most kDlrmMaxLdsFloats (144 KiB).
+constexpr int kDlrmMaxLdsFloats = 36864;
+int dlrm_stride(int d);
+hipError_t launch_dlrm_interact(const float* z, int64_t B, int F, int d, float* out, int num_cus,
+                                hipStream_t s);
 hipError_t launch_hash_clear(int64_t* keys, uint8_t* digests, uint64_t* scores, int64_t capacity,
                              hipStream_t s);
 

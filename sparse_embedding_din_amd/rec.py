@@ -29,7 +29,7 @@ REC_MAX_B = 16777215
 
 EXPORTS = ["rec_din_pack_mlp", "rec_scan_workspace_bytes", "rec_lengths_to_offsets", "rec_embbag_fwd",
            "rec_kjt_sums_bytes", "rec_kjt_sums", "rec_embbag_fwd_kjt", "rec_hash_lookup",
-           "rec_hash_insert", "rec_hash_clear",
+           "rec_hash_insert", "rec_hash_clear", "rec_dlrm_interact",
            "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_fwd",
            "rec_sparse_din_fwd_workspace_bytes", "rec_sparse_din_fwd", "rec_towers_fwd",
            "rec_tower_pack_mlp",
@@ -97,6 +97,7 @@ def lib():
         L.rec_hash_lookup.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, vp]
         L.rec_hash_insert.argtypes = [C.POINTER(rec_table), vp, vp, i64, i32, C.c_uint64, vp, vp]
         L.rec_hash_clear.argtypes = [C.POINTER(rec_table), vp]
+        L.rec_dlrm_interact.argtypes = [vp, i64, i32, i32, vp, vp]
         L.rec_din_plan_bytes.argtypes = [i64, i32]
         L.rec_din_plan_bytes.restype = sz
         L.rec_din_plan.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, i64, i32, i32, vp, vp,
@@ -111,7 +112,8 @@ def lib():
         L.rec_towers_fwd.argtypes = [C.POINTER(rec_tower_mlp), i64, vp, i64, vp, vp, vp, vp, vp]
         L.rec_tower_pack_mlp.argtypes = [C.POINTER(rec_tower_mlp), vp, sz, vp]
         for f in ("rec_lengths_to_offsets", "rec_embbag_fwd", "rec_kjt_sums", "rec_embbag_fwd_kjt",
-                  "rec_hash_lookup", "rec_hash_insert", "rec_hash_clear", "rec_din_plan",
+                  "rec_hash_lookup", "rec_hash_insert", "rec_hash_clear", "rec_dlrm_interact",
+                  "rec_din_plan",
                   "rec_din_attn_fwd", "rec_din_pack_mlp", "rec_sparse_din_fwd", "rec_towers_fwd",
                   "rec_tower_pack_mlp"):
             getattr(L, f).restype = C.c_int
@@ -226,6 +228,10 @@ def rec_hash_insert(table_: rec_table, keys, values, n: int, score_mode: int = R
     _check(lib().rec_hash_insert(C.byref(table_) if table_ is not None else None, _p(keys),
                                  _p(values), n, score_mode, step, _p(slot_out), _stream(stream)),
            "rec_hash_insert")
+
+
+def rec_dlrm_interact(z, B: int, F: int, d: int, out, stream=None):
+    _check(lib().rec_dlrm_interact(_p(z), B, F, d, _p(out), _stream(stream)), "rec_dlrm_interact")
 
 
 def rec_hash_clear(table_: rec_table, stream=None):

@@ -198,6 +198,25 @@ def test_hash_clear_errors(lib):
         R.REC_EINVAL
 
 
+def test_dlrm_interact_errors(lib):
+    f = lib.rec_dlrm_interact
+    assert _status(f, FAKE, -1, 5, 16, FAKE, None)[0] == R.REC_EINVAL
+    assert _status(f, FAKE, 4, 0, 16, FAKE, None)[0] == R.REC_EINVAL
+    for d in (0, 8, 24, 100):
+        s, msg = _status(f, FAKE, 4, 5, d, FAKE, None)
+        assert s == R.REC_EINVAL and "multiple of 16" in msg
+    assert _status(f, FAKE, 4, 257, 16, FAKE, None)[0] == R.REC_EUNSUPPORTED
+    assert _status(f, FAKE, 4, 5, 528, FAKE, None)[0] == R.REC_EUNSUPPORTED
+    s, msg = _status(f, FAKE, 4, 217, 176, FAKE, None)              # 224 x 180 floats > 144 KiB
+    assert s == R.REC_EUNSUPPORTED and "LDS" in msg
+    assert _status(f, None, 4, 5, 16, FAKE, None)[0] == R.REC_EINVAL
+    assert _status(f, FAKE, 4, 5, 16, None, None)[0] == R.REC_EINVAL
+    assert _status(f, FAKE_ODD, 4, 5, 16, FAKE, None)[0] == R.REC_EINVAL
+    assert _status(f, None, 0, 217, 160, None, None)[0] == R.REC_OK   # the largest width at F = 217
+    with pytest.raises(R.RecError):
+        R.rec_dlrm_interact(FAKE, 4, 5, 8, FAKE)
+
+
 def test_din_pack_errors(lib):
     m = R.din_mlp(R.REC_F32, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0)
     assert _status(lib.rec_din_pack_mlp, C.byref(m), FAKE, R.REC_DIN_PACKED_BYTES, None)[0] == R.REC_EINVAL
