@@ -79,6 +79,10 @@ class Oracle:
         L.orc_hash_check.restype = C.c_int64
         L.orc_dlrm_interact.argtypes = [PF, C.c_int64, C.c_int32, C.c_int32, PD, PD]
         L.orc_dlrm_interact.restype = None
+        L.orc_embbag_adagrad.argtypes = [C.c_int32, C.c_int64, P64, P64, P64, P32, P64, PF,
+                                         C.c_int64, P32, P64, C.c_int64, PF, C.c_double,
+                                         C.c_double, PD, PD, PD, P8]
+        L.orc_embbag_adagrad.restype = None
         self._keep = []
 
     # -- bookkeeping ---------------------------------------------------------
@@ -127,6 +131,48 @@ class Oracle:
         keys = np.ascontiguousarray(keys, np.int64)
         digests = np.ascontiguousarray(digests, np.uint8)
         return int(self.lib.orc_hash_check(_ptr(keys, P64), _ptr(digests, P8), keys.size))
+
+    # -- backward of the bags + sparse AdaGrad ------------------------------------
+    def embbag_adagrad(self, rows, B: int, values, lengths, offsets, dpooled, weights, accums,
+                       lr: float = 1e-3, eps: float = 1e-10, seq=None):
+        """One sparse AdaGrad step of T direct tables from the gradient of the
+        sum-pooled output, dpooled [B][T*16] (fp32), and optionally of the
+        unpooled sequence rows: seq = (seq_table [3], seq_values [3][>=P],
+        dseq [3][P][16] fp32).  weights / accums: T arrays [rows[t]][16] (not
+        modified).  Returns (new weights, new accums, summed gradient,
+        touched mask), lists of T fp64 arrays (mask: bool)."""
+        T = len(rows)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        base = np.concatenate([[0], np.cumsum(rows)[:-1]]).astype(np.int64)
+        R = int(rows.sum())
+        values = np.ascontiguousarray(values, dtype=np.int64)
+        lengths = np.ascontiguousarray(lengths, dtype=np.int32)
+        offsets = np.ascontiguousarray(offsets, dtype=np.int64)
+        dp = np.ascontiguousarray(dpooled, dtype=np.float32).reshape(B, T * 16)
+        assert lengths.size == T * B and offsets.size >= T * B
+        w = np.concatenate([np.asarray(a, np.float64).reshape(-1, 16) for a in weights])
+        G = np.concatenate([np.asarray(a, np.float64).reshape(-1, 16) for a in accums])
+        assert w.shape == (R, 16) and G.shape == (R, 16)
+        grad = np.zeros((R, 16), np.float64)
+        touched = np.zeros(R, np.uint8)
+        if seq is None:
+            P, st, sv, ds, stride = 0, np.zeros(3, np.int32), np.zeros(1, np.int64), \
+                np.zeros(1, np.float32), 0
+        else:
+            st = np.ascontiguousarray(seq[0], dtype=np.int32)
+            sv = np.ascontiguousarray(seq[1], dtype=np.int64)
+            ds = np.ascontiguousarray(seq[2], dtype=np.float32)
+            P = ds.shape[1]
+            stride = sv.shape[1]
+            assert st.shape == (3,) and ds.shape == (3, P, 16) and sv.shape[0] == 3 and stride >= P
+            assert np.all((st >= 0) & (st < T))
+        self.lib.orc_embbag_adagrad(T, B, _ptr(rows, P64), _ptr(base, P64), _ptr(values, P64),
+                                    _ptr(lengths, P32), _ptr(offsets, P64), _ptr(dp, PF), P,
+                                    _ptr(st, P32), _ptr(sv, P64), stride, _ptr(ds, PF),
+                                    float(lr), float(eps), _ptr(w, PD), _ptr(G, PD),
+                                    _ptr(grad, PD), _ptr(touched, P8))
+        cut = lambda a: [a[base[t]: base[t] + rows[t]] for t in range(T)]  # noqa: E731
+        return cut(w), cut(G), cut(grad), cut(touched.astype(bool))
 
     # -- DLRM interaction --------------------------------------------------------
     def dlrm_interact(self, z: np.ndarray, want_scale: bool = False):

@@ -18,6 +18,8 @@
  *        §4.4 compute graph: pooled deep features; query [B,48]; sequence
  *             [B,100,48]; attn input [B,100,192]; output [B,48]; then the
  *             deep MLP to [B,128], the concat to [B,176] and the final MLP
+ *        run-config table: sparse parameters train with AdaGrad (lr 1e-3);
+ *        §3   the AdaGrad accumulator is as large as the table
  *   [P2] "MultiTowerDIN：集成 DynamicEmb"
  *        §3.2 lookup is an O(1) open-addressing hash table; an unseen id gives
  *             the constant 0 vector
@@ -39,6 +41,10 @@
  *   - no softmax temperature or 1/sqrt(d); max-subtracted for range.
  *   - W1 columns: 0-47 q, 48-95 s, 96-143 q-s, 144-191 q*s; inside each block
  *     the sub-features adgroup, cate, brand, 16 each.
+ *   - the AdaGrad step is the element-wise one (one accumulator per weight,
+ *     starting at 0): G += g^2, w -= lr g / (sqrt(G) + eps), eps 1e-10, no
+ *     decay; g is a row's gradient summed over every read of the row in the
+ *     batch before the step, and rows the batch does not read are untouched.
  *   - hash lookup: the key is the raw id; a key is present iff some slot holds
  *     it.  The oracle finds it by scanning every slot once (sorted index), so
  *     it depends on no hash function or probe order.
@@ -259,6 +265,62 @@ void orc_embbag(int32_t T, int64_t B, const orc_table* tables,
                 for (int d = 0; d < ORC_DIM; ++d) acc[d] += (double)tables[k].values[r * ORC_DIM + d];
             }
             for (int d = 0; d < ORC_DIM; ++d) pooled[s * (int64_t)T * ORC_DIM + k * ORC_DIM + d] = acc[d];
+        }
+    }
+}
+
+/* ---- sparse backward of the bags + AdaGrad step ([P1] run-config table:
+ * sparse parameters train with AdaGrad, lr 1e-3; [P1] §3: the AdaGrad
+ * accumulator is as large as the table, one value per weight; [P2] §3.3:
+ * the gradient is accumulated in fp32 or wider) -------------------------------
+ * All T direct tables sit in one flat row space: table t owns rows
+ * base[t] .. base[t] + rows[t] - 1 of w, G, grad and touched ([R][16] / [R]).
+ * The gradient of a weight row is the sum of the output gradients of every
+ * place that row was read:
+ *   - each id of bag (t, b) adds dpooled[b][16t .. 16t+16) to the row
+ *     floor_mod(id, rows[t]) of table t (the pooled sum reads it once per id,
+ *     so a repeated id adds its bag's gradient once per repetition);
+ *   - each packed sequence position j < P of sub-feature k adds
+ *     dseq[k][j][0..16) to the row of seq_values[k*seq_stride + j] in table
+ *     seq_table[k] (the unpooled sequence rows the attention reads).
+ * grad receives that sum (it must be zero on entry) and touched marks each row
+ * read at least once.  Then every touched row takes one element-wise AdaGrad
+ * step with its summed gradient g:
+ *   G += g * g;   w -= lr * g / (sqrt(G) + eps).
+ * Untouched rows are left as they are.                                      */
+void orc_embbag_adagrad(int32_t T, int64_t B, const int64_t* rows, const int64_t* base,
+                        const int64_t* values, const int32_t* lengths, const int64_t* offsets,
+                        const float* dpooled, int64_t P, const int32_t* seq_table,
+                        const int64_t* seq_values, int64_t seq_stride, const float* dseq,
+                        double lr, double eps, double* w, double* G, double* grad,
+                        uint8_t* touched) {
+    for (int32_t t = 0; t < T; ++t) {
+        for (int64_t b = 0; b < B; ++b) {
+            const int64_t bag = (int64_t)t * B + b;
+            for (int64_t i = 0; i < lengths[bag]; ++i) {
+                const int64_t r = base[t] + orc_floor_mod(values[offsets[bag] + i], rows[t]);
+                touched[r] = 1;
+                for (int d = 0; d < ORC_DIM; ++d)
+                    grad[r * ORC_DIM + d] += (double)dpooled[b * (int64_t)T * ORC_DIM + t * ORC_DIM + d];
+            }
+        }
+    }
+    for (int k = 0; k < 3 && P > 0; ++k) {
+        const int32_t t = seq_table[k];
+        for (int64_t j = 0; j < P; ++j) {
+            const int64_t r = base[t] + orc_floor_mod(seq_values[k * seq_stride + j], rows[t]);
+            touched[r] = 1;
+            for (int d = 0; d < ORC_DIM; ++d)
+                grad[r * ORC_DIM + d] += (double)dseq[(k * P + j) * ORC_DIM + d];
+        }
+    }
+    const int64_t R = base[T - 1] + rows[T - 1];
+    for (int64_t r = 0; r < R; ++r) {
+        if (!touched[r]) continue;
+        for (int d = 0; d < ORC_DIM; ++d) {
+            const double g = grad[r * ORC_DIM + d];
+            G[r * ORC_DIM + d] += g * g;
+            w[r * ORC_DIM + d] -= lr * g / (sqrt(G[r * ORC_DIM + d]) + eps);
         }
     }
 }

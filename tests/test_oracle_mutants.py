@@ -82,6 +82,24 @@ MUTANTS = [
      "for (int32_t k = 0; k + 1 < d; ++k) {"),
     ("interaction column-major", "out[o] = acc;",
      "out[b * npairs + (int64_t)j * (j + 1) / 2 + i] = acc;"),
+    ("AdaGrad accumulates |g| not g^2", "G[r * ORC_DIM + d] += g * g;",
+     "G[r * ORC_DIM + d] += fabs(g);"),
+    ("AdaGrad steps against the old accumulator",
+     "G[r * ORC_DIM + d] += g * g;\n            w[r * ORC_DIM + d] -= lr * g / (sqrt(G[r * ORC_DIM + d]) + eps);",
+     "w[r * ORC_DIM + d] -= lr * g / (sqrt(G[r * ORC_DIM + d]) + eps);\n            G[r * ORC_DIM + d] += g * g;"),
+    ("AdaGrad steps up the gradient", "w[r * ORC_DIM + d] -= lr * g", "w[r * ORC_DIM + d] += lr * g"),
+    ("sequence gradients dropped", "for (int k = 0; k < 3 && P > 0; ++k) {",
+     "for (int k = 0; k < 0 && P > 0; ++k) {"),
+    ("sequence rows from the first sub-feature's table", "const int32_t t = seq_table[k];",
+     "const int32_t t = seq_table[0];"),
+    ("bag gradient from the first table's columns",
+     "(double)dpooled[b * (int64_t)T * ORC_DIM + t * ORC_DIM + d];",
+     "(double)dpooled[b * (int64_t)T * ORC_DIM + d];"),
+    ("a repeated id counted once", "for (int d = 0; d < ORC_DIM; ++d)\n                    grad[r * ORC_DIM + d] +=",
+     "for (int d = 0; d < ORC_DIM; ++d)\n                    grad[r * ORC_DIM + d] = "),
+    ("backward drops the last id of a bag",
+     "for (int64_t i = 0; i < lengths[bag]; ++i) {\n                const int64_t r = base[t]",
+     "for (int64_t i = 0; i + 1 < lengths[bag]; ++i) {\n                const int64_t r = base[t]"),
 ]
 
 
