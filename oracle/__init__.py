@@ -82,7 +82,7 @@ class Oracle:
         L.orc_embbag_adagrad.argtypes = [C.c_int32, C.c_int64, P64, P64, P64, P32, P64, PF,
                                          C.c_int64, P32, P64, C.c_int64, PF, C.c_double,
                                          C.c_double, PD, PD, PD, P8]
-        L.orc_embbag_adagrad.restype = None
+        L.orc_embbag_adagrad.restype = C.c_int64
         self._keep = []
 
     # -- bookkeeping ---------------------------------------------------------
@@ -166,11 +166,12 @@ class Oracle:
             stride = sv.shape[1]
             assert st.shape == (3,) and ds.shape == (3, P, 16) and sv.shape[0] == 3 and stride >= P
             assert np.all((st >= 0) & (st < T))
-        self.lib.orc_embbag_adagrad(T, B, _ptr(rows, P64), _ptr(base, P64), _ptr(values, P64),
+        outside = self.lib.orc_embbag_adagrad(T, B, _ptr(rows, P64), _ptr(base, P64), _ptr(values, P64),
                                     _ptr(lengths, P32), _ptr(offsets, P64), _ptr(dp, PF), P,
                                     _ptr(st, P32), _ptr(sv, P64), stride, _ptr(ds, PF),
                                     float(lr), float(eps), _ptr(w, PD), _ptr(G, PD),
                                     _ptr(grad, PD), _ptr(touched, P8))
+        assert outside == 0, f"{outside} reads resolved to a row outside their table"
         cut = lambda a: [a[base[t]: base[t] + rows[t]] for t in range(T)]  # noqa: E731
         return cut(w), cut(G), cut(grad), cut(touched.astype(bool))
 

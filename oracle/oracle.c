@@ -287,18 +287,23 @@ void orc_embbag(int32_t T, int64_t B, const orc_table* tables,
  * read at least once.  Then every touched row takes one element-wise AdaGrad
  * step with its summed gradient g:
  *   G += g * g;   w -= lr * g / (sqrt(G) + eps).
- * Untouched rows are left as they are.                                      */
-void orc_embbag_adagrad(int32_t T, int64_t B, const int64_t* rows, const int64_t* base,
+ * Untouched rows are left as they are.  Returns the number of reads whose
+ * row fell outside its table (0 unless the row arithmetic is broken); those
+ * are skipped, never written.                                              */
+int64_t orc_embbag_adagrad(int32_t T, int64_t B, const int64_t* rows, const int64_t* base,
                         const int64_t* values, const int32_t* lengths, const int64_t* offsets,
                         const float* dpooled, int64_t P, const int32_t* seq_table,
                         const int64_t* seq_values, int64_t seq_stride, const float* dseq,
                         double lr, double eps, double* w, double* G, double* grad,
                         uint8_t* touched) {
+    int64_t outside = 0;
     for (int32_t t = 0; t < T; ++t) {
         for (int64_t b = 0; b < B; ++b) {
             const int64_t bag = (int64_t)t * B + b;
             for (int64_t i = 0; i < lengths[bag]; ++i) {
-                const int64_t r = base[t] + orc_floor_mod(values[offsets[bag] + i], rows[t]);
+                const int64_t rt = orc_floor_mod(values[offsets[bag] + i], rows[t]);
+                if (rt < 0 || rt >= rows[t]) { ++outside; continue; }
+                const int64_t r = base[t] + rt;
                 touched[r] = 1;
                 for (int d = 0; d < ORC_DIM; ++d)
                     grad[r * ORC_DIM + d] += (double)dpooled[b * (int64_t)T * ORC_DIM + t * ORC_DIM + d];
@@ -308,7 +313,9 @@ void orc_embbag_adagrad(int32_t T, int64_t B, const int64_t* rows, const int64_t
     for (int k = 0; k < 3 && P > 0; ++k) {
         const int32_t t = seq_table[k];
         for (int64_t j = 0; j < P; ++j) {
-            const int64_t r = base[t] + orc_floor_mod(seq_values[k * seq_stride + j], rows[t]);
+            const int64_t rt = orc_floor_mod(seq_values[k * seq_stride + j], rows[t]);
+            if (rt < 0 || rt >= rows[t]) { ++outside; continue; }
+            const int64_t r = base[t] + rt;
             touched[r] = 1;
             for (int d = 0; d < ORC_DIM; ++d)
                 grad[r * ORC_DIM + d] += (double)dseq[(k * P + j) * ORC_DIM + d];
@@ -323,6 +330,7 @@ void orc_embbag_adagrad(int32_t T, int64_t B, const int64_t* rows, const int64_t
             w[r * ORC_DIM + d] -= lr * g / (sqrt(G[r * ORC_DIM + d]) + eps);
         }
     }
+    return outside;
 }
 
 /* ---- DIN target attention ([P1] §4.2, §4.4) -----------------------------

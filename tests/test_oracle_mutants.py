@@ -22,8 +22,9 @@ MUTANTS = [
      "if (r < 0) r = 0;                 /* hash miss"),
     ("pool from the wrong table", "int64_t r = orc_resolve(&tables[k], values[offsets[bag] + i]);",
      "int64_t r = orc_resolve(&tables[0], values[offsets[bag] + i]);"),
-    ("pool drops the last id", "for (int64_t i = 0; i < lengths[bag]; ++i) {",
-     "for (int64_t i = 0; i + 1 < lengths[bag]; ++i) {"),
+    ("pool drops the last id",
+     "for (int64_t i = 0; i < lengths[bag]; ++i) {\n                int64_t r = orc_resolve(",
+     "for (int64_t i = 0; i + 1 < lengths[bag]; ++i) {\n                int64_t r = orc_resolve("),
     ("q - s sign flipped", "x[96 + c] = qc - sc;", "x[96 + c] = sc - qc;"),
     ("q * s replaced by q + s", "x[144 + c] = qc * sc;", "x[144 + c] = qc + sc;"),
     ("q and s blocks swapped", "x[c] = qc;\n                x[48 + c] = sc;",
@@ -98,8 +99,8 @@ MUTANTS = [
     ("a repeated id counted once", "for (int d = 0; d < ORC_DIM; ++d)\n                    grad[r * ORC_DIM + d] +=",
      "for (int d = 0; d < ORC_DIM; ++d)\n                    grad[r * ORC_DIM + d] = "),
     ("backward drops the last id of a bag",
-     "for (int64_t i = 0; i < lengths[bag]; ++i) {\n                const int64_t r = base[t]",
-     "for (int64_t i = 0; i + 1 < lengths[bag]; ++i) {\n                const int64_t r = base[t]"),
+     "for (int64_t i = 0; i < lengths[bag]; ++i) {\n                const int64_t rt = orc_floor_mod(",
+     "for (int64_t i = 0; i + 1 < lengths[bag]; ++i) {\n                const int64_t rt = orc_floor_mod("),
 ]
 
 
