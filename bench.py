@@ -46,6 +46,9 @@ DIN_BYTES_WEIGHTS = 256 * 192 * 2 + 64 * 256 * 2 + (256 + 64 + 64) * 4
 DIN_FLOPS_PER_POS = 2 * (192 * 256 + 256 * 64 + 64)
 TOWER_FLOPS_PER_SAMPLE = 2 * (256 * 512 + 512 * 256 + 256 * 128 + 176 * 64 + 64)
 TOWER_WEIGHT_BYTES = 2 * (256 * 512 + 512 * 256 + 256 * 128 + 176 * 64)
+ADAGRAD_BYTES_PER_READ = 8 + 64            # raw id + the read's 64-byte output gradient
+ADAGRAD_BYTES_PER_BAG = 4 + 8              # length + offset
+ADAGRAD_BYTES_PER_ROW = 2 * (64 + 64)      # weights and accumulator, read and written
 
 
 def parse():
@@ -67,6 +70,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-hash-rebuild", action="store_true",
                    help="skip timing the rebuild of the hash workload's tables (clear + insert)")
+    p.add_argument("--no-adagrad", action="store_true",
+                   help="skip the backward + sparse AdaGrad leg reported beside the step")
     p.add_argument("--no-towers", action="store_true",
                    help="skip the deep tower + final MLP measurement")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -402,6 +407,80 @@ def main():
         print(f"[bench] hash rebuild: {nkeys} keys in {total_us:.1f} us ({ins_us:.2f} us per insert launch)",
               file=sys.stderr, flush=True)
 
+    adagrad = None
+    if not a.no_adagrad and not cfg.hash_keys:
+        # The sparse half of a training step, beside the forward: gradients of
+        # the pooled bags and of the sequence rows (random, as the dense
+        # backward would deliver them) summed per row, then one AdaGrad step
+        # ("当前现状分析" run-config table), on copies of the tables.
+        rng = np.random.default_rng(4242)
+        T = synth.T
+        rows = [int(t["rows"]) for t in model.tables]
+        aw = [torch.from_numpy(np.asarray(t["values"], np.float32)).to(dev) for t in model.tables]
+        aa = [torch.zeros(r, 16, dtype=torch.float32, device=dev) for r in rows]
+        atabs = [R.adagrad_table(aw[t], aa[t], rows[t]) for t in range(T)]
+        legs = []
+        for b_, db in zip(batches, dbs):
+            P_ = int(b_.seq_lengths.sum())
+            off = np.concatenate([[0], np.cumsum(b_.lengths.astype(np.int64))[:-1]])
+            legs.append(dict(
+                db=db, P=P_, off=torch.from_numpy(off).to(dev),
+                gp=torch.from_numpy(rng.standard_normal((B, T * 16)).astype(np.float32)).to(dev),
+                gs=torch.from_numpy(rng.standard_normal((3, P_, 16)).astype(np.float32)).to(dev)))
+        wsb = max(R.rec_embbag_adagrad_workspace_bytes(T, B, L["db"].nnz, L["P"]) for L in legs)
+        aws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        st = list(synth.SEQ_KEYS)
+
+        def adagrad_call(L):
+            db = L["db"]
+            R.rec_embbag_adagrad(atabs, T, B, db.values, db.lengths, L["off"], db.nnz, L["gp"], st,
+                                 db.seq_values, db.seq_stride, L["P"], L["gs"], 1e-3, 1e-10, aws,
+                                 wsb, stream=stream)
+
+        reps_a = 40
+        with torch.cuda.stream(stream):
+            for r in range(4):
+                adagrad_call(legs[r % nb])
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps_a)]
+            torch.cuda._sleep(40_000_000)
+            for r in range(reps_a):
+                evs[r][0].record(stream)
+                adagrad_call(legs[r % nb])
+                evs[r][1].record(stream)
+            torch.cuda.synchronize()
+        d = np.array([s_.elapsed_time(e_) * 1e3 for s_, e_ in evs])
+        # algorithmic work of the average batch: reads, bags and distinct rows
+        reads, touched = [], []
+        for b_ in batches:
+            starts = np.concatenate([[0], np.cumsum(b_.lengths.astype(np.int64))])
+            keys = []
+            for t in range(T):
+                keys.append(np.mod(b_.values[starts[t * B]: starts[(t + 1) * B]], rows[t])
+                            + sum(rows[:t]))
+            Pb = int(b_.seq_lengths.sum())
+            for k, t in enumerate(st):
+                keys.append(np.mod(b_.seq_values[k, :Pb], rows[t]) + sum(rows[:t]))
+            keys = np.concatenate(keys)
+            reads.append(keys.size)
+            touched.append(np.unique(keys).size)
+        n_reads, n_rows = float(np.mean(reads)), float(np.mean(touched))
+        a_bytes = (n_reads * ADAGRAD_BYTES_PER_READ + T * B * ADAGRAD_BYTES_PER_BAG
+                   + n_rows * ADAGRAD_BYTES_PER_ROW)
+        a_us = float(d.mean())
+        adagrad = {"entry": "rec_embbag_adagrad (row keys, radix sort, chunk sums + AdaGrad, "
+                            "cross-chunk runs)",
+                   "avg_call_us": round(a_us, 3), "median_call_us": round(float(np.median(d)), 3),
+                   "reads": n_reads, "distinct_rows": n_rows,
+                   "algorithmic_bytes": a_bytes,
+                   "algorithmic_gb_s": round(a_bytes / (a_us * 1e-6) / 1e9, 1),
+                   "hbm_frac": round(a_bytes / (a_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "traffic": None}
+        print(f"[bench] backward + AdaGrad: {a_us:.2f} us per call ({n_reads:.0f} reads, "
+              f"{n_rows:.0f} rows)", file=sys.stderr, flush=True)
+        del aw, aa, aws, legs
+
     cpu = None
     if not a.no_cpu:
         import oracle
@@ -447,6 +526,7 @@ def main():
                 "gb_s": round(din_bytes / din_t / 1e9, 1)},
         "towers": towers,
         "hash_rebuild": rebuild,
+        "adagrad": adagrad,
         "src_hash": shash,
     }
     if a.calibrate_copy:

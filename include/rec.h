@@ -471,6 +471,72 @@ rec_status rec_towers_fwd(const rec_tower_mlp* mlp, int64_t B, const float* pool
 rec_status rec_tower_pack_mlp(const rec_tower_mlp* mlp, void* packed, size_t packed_bytes,
                               void* stream);
 
+/*
+ * One direct table as the sparse AdaGrad step sees it (host struct; both
+ * arrays are device memory, updated in place).
+ *   weights  fp32 [rows][16], 16-byte aligned (the table rec_embbag_fwd reads)
+ *   accum    fp32 [rows][16], 16-byte aligned: AdaGrad's running sum of
+ *            squared gradients, one value per weight (0 before the first step)
+ *   rows     num_buckets, the floor-mod divisor, >= 1
+ */
+typedef struct {
+    float* weights;
+    float* accum;
+    int64_t rows;
+} rec_adagrad_table;
+
+/* Bytes of workspace rec_embbag_adagrad needs for T tables, B samples, nnz
+ * bag ids and P sequence positions; 0 for invalid arguments or when the
+ * device cannot be queried (the sort's scratch is sized for the device). */
+size_t rec_embbag_adagrad_workspace_bytes(int32_t T, int64_t B, int64_t nnz, int64_t P);
+
+/*
+ * Backward of the sum-pooled embedding bags (and of the unpooled sequence
+ * rows the DIN attention reads) followed by one sparse AdaGrad step
+ * ("当前现状分析": the run-config table trains sparse parameters with
+ * AdaGrad, lr 1e-3, and §3 sizes its accumulator like the table; "集成
+ * DynamicEmb" §3.3: gradients accumulate in fp32).
+ *
+ * Gradient of each row: the sum, over every read of that row in the batch, of
+ * the read's output gradient:
+ *   - id i of bag (t, b) (the KJT of rec_embbag_fwd: key-major, bag t*B + b
+ *     holds values[offsets[t*B+b] .. + lengths[t*B+b])) reads row
+ *     floor_mod(values[i], tables[t].rows) of table t, with output gradient
+ *     grad_pooled[b][16t .. 16t+16);
+ *   - packed sequence position j < P of sub-feature k (0..2) reads row
+ *     floor_mod(seq_values[k*seq_stride + j], rows) of table seq_table[k], with
+ *     output gradient grad_seq[k][j][0..16).
+ * Every row read at least once then takes, element by element, with its
+ * summed gradient g:  accum += g*g;  weights -= lr * g / (sqrt(accum) + eps)
+ * (fp32).  Rows not read are not touched.  A repeated id counts once per
+ * repetition.  The sums run in a fixed order (reads sorted by row, stable), so
+ * results are bit-identical run to run.
+ *
+ *   tables      host array of T rec_adagrad_table (T <= REC_MAX_TABLES);
+ *               direct tables only, sum of rows < 2^32
+ *   values      int64[nnz] raw ids; lengths int32[T*B]; offsets int64[T*B]:
+ *               the exclusive scan of lengths, with offsets[T*B-1] +
+ *               lengths[T*B-1] == nnz (precondition, not checked)
+ *   grad_pooled fp32 [B][T*16], 16-byte aligned
+ *   seq_table   host int32[3] (table index of each sub-feature), or NULL when
+ *               P == 0;  seq_values int64 [3][seq_stride], seq_stride >= P;
+ *   grad_seq    fp32 [3][P][16], 16-byte aligned (NULL when P == 0)
+ *   lr, eps     the step size and the denominator's epsilon (e.g. 1e-3, 1e-10)
+ *   workspace   >= rec_embbag_adagrad_workspace_bytes(T, B, nnz, P) bytes of
+ *               device memory, 256-byte aligned; contents on entry ignored
+ * The tables must not overlap one another or the inputs.
+ * Errors: REC_EINVAL (null or misaligned pointers, T < 1, B < 0, nnz < 0,
+ * P < 0, rows < 1, a seq_table entry outside [0, T)), REC_EUNSUPPORTED
+ * (T > REC_MAX_TABLES, rows summing to 2^32 or more, nnz + 3P or B*T + 3P at
+ * 2^31 or more), REC_EWORKSPACE.  nnz + P == 0 is a no-op.
+ */
+rec_status rec_embbag_adagrad(const rec_adagrad_table* tables, int32_t T, int64_t B,
+                              const int64_t* values, const int32_t* lengths,
+                              const int64_t* offsets, int64_t nnz, const float* grad_pooled,
+                              const int32_t* seq_table, const int64_t* seq_values,
+                              int64_t seq_stride, int64_t P, const float* grad_seq, float lr,
+                              float eps, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* rec_last_error(void);
 

@@ -589,3 +589,120 @@ rec_status rec_towers_fwd(const rec_tower_mlp* mlp, int64_t B, const float* pool
 }
 
 }  // extern "C"
+
+namespace {
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Regions of rec_embbag_adagrad's workspace, in order: keys and sources in,
+// sorted keys and sources, head and tail pieces, the sort's scratch.
+struct BwdLayout {
+    size_t keys_in, src_in, keys_out, src_out, hpart, tpart, sort, sort_bytes, bytes;
+};
+
+bool bwd_layout(int64_t n, BwdLayout* L) {
+    const size_t nb = round256((size_t)n * 4);
+    const size_t nch = (size_t)((n + 15) / 16);
+    const size_t pb = round256(nch * 16 * 4);
+    L->keys_in = 0;
+    L->src_in = L->keys_in + nb;
+    L->keys_out = L->src_in + nb;
+    L->src_out = L->keys_out + nb;
+    L->hpart = L->src_out + nb;
+    L->tpart = L->hpart + pb;
+    L->sort = L->tpart + pb;
+    L->sort_bytes = bwd_sort_bytes(n);
+    L->bytes = L->sort + round256(L->sort_bytes);
+    return L->sort_bytes > 0;
+}
+
+}  // namespace
+
+size_t rec_embbag_adagrad_workspace_bytes(int32_t T, int64_t B, int64_t nnz, int64_t P) {
+    if (T < 1 || T > REC_MAX_TABLES || B < 0 || nnz < 0 || P < 0) return 0;
+    const int64_t n = nnz + 3 * P;
+    if (n >= ((int64_t)1 << 31) || B * T + 3 * P >= ((int64_t)1 << 31)) return 0;
+    if (n == 0) return 0;
+    BwdLayout L;
+    if (!bwd_layout(n, &L)) return 0;
+    return L.bytes;
+}
+
+rec_status rec_embbag_adagrad(const rec_adagrad_table* tables, int32_t T, int64_t B,
+                              const int64_t* values, const int32_t* lengths,
+                              const int64_t* offsets, int64_t nnz, const float* grad_pooled,
+                              const int32_t* seq_table, const int64_t* seq_values,
+                              int64_t seq_stride, int64_t P, const float* grad_seq, float lr,
+                              float eps, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "rec_embbag_adagrad";
+    const std::string f(fn);
+    if (!tables) return fail(REC_EINVAL, f + ": tables is NULL");
+    if (T < 1) return fail(REC_EINVAL, f + ": T < 1");
+    if (T > REC_MAX_TABLES) return fail(REC_EUNSUPPORTED, f + ": T > REC_MAX_TABLES");
+    if (B < 0 || nnz < 0 || P < 0) return fail(REC_EINVAL, f + ": B, nnz and P must be >= 0");
+    const int64_t n = nnz + 3 * P;
+    if (n >= ((int64_t)1 << 31) || B * T + 3 * P >= ((int64_t)1 << 31))
+        return fail(REC_EUNSUPPORTED, f + ": nnz + 3P or B*T + 3P at 2^31 or more");
+    BwdTab tabs[REC_MAX_TABLES];
+    uint64_t total = 0;
+    for (int t = 0; t < T; ++t) {
+        const rec_adagrad_table& a = tables[t];
+        if (a.rows < 1) return fail(REC_EINVAL, f + ": table rows must be >= 1");
+        if (!a.weights || !a.accum) return fail(REC_EINVAL, f + ": table weights or accum is NULL");
+        if (!aligned16(a.weights) || !aligned16(a.accum))
+            return fail(REC_EINVAL, f + ": table weights and accum must be 16-byte aligned");
+        tabs[t].weights = a.weights;
+        tabs[t].accum = a.accum;
+        tabs[t].rows = a.rows;
+        floor_mod_prepare(a.rows, &tabs[t].magic, &tabs[t].shift);
+        tabs[t].base = (uint32_t)total;
+        total += (uint64_t)a.rows;
+        if (total >= ((uint64_t)1 << 32)) return fail(REC_EUNSUPPORTED, f + ": table rows sum to 2^32 or more");
+    }
+    if (nnz > 0 && (!values || !lengths || !offsets || !grad_pooled))
+        return fail(REC_EINVAL, f + ": values, lengths, offsets and grad_pooled are required when nnz > 0");
+    if (nnz > 0 && B == 0) return fail(REC_EINVAL, f + ": nnz > 0 with B == 0");
+    if (grad_pooled && !aligned16(grad_pooled)) return fail(REC_EINVAL, f + ": grad_pooled not 16-byte aligned");
+    BwdArgs a;
+    memset(&a, 0, sizeof(a));
+    if (P > 0) {
+        if (!seq_table || !seq_values || !grad_seq)
+            return fail(REC_EINVAL, f + ": seq_table, seq_values and grad_seq are required when P > 0");
+        if (seq_stride < P) return fail(REC_EINVAL, f + ": seq_stride < P");
+        if (!aligned16(grad_seq)) return fail(REC_EINVAL, f + ": grad_seq not 16-byte aligned");
+        for (int k = 0; k < 3; ++k) {
+            if (seq_table[k] < 0 || seq_table[k] >= T) return fail(REC_EINVAL, f + ": seq_table entry outside [0, T)");
+            a.seq_table[k] = seq_table[k];
+        }
+    }
+    if (n == 0) return ok();
+    BwdLayout L;
+    if (!bwd_layout(n, &L)) return fail(REC_EHIP, f + ": cannot size the sort's scratch on this device");
+    if (!workspace || workspace_bytes < L.bytes) return fail(REC_EWORKSPACE, f + ": workspace missing or too small");
+    if ((uintptr_t)workspace & 255u) return fail(REC_EINVAL, f + ": workspace not 256-byte aligned");
+    char* w = (char*)workspace;
+    a.values = values;
+    a.lengths = lengths;
+    a.offsets = offsets;
+    a.grad_pooled = grad_pooled;
+    a.seq_values = seq_values;
+    a.grad_seq = grad_seq;
+    a.seq_stride = seq_stride;
+    a.B = B;
+    a.nnz = nnz;
+    a.P = P;
+    a.n = n;
+    a.T = T;
+    a.total_rows = (uint32_t)total;
+    a.lr = lr;
+    a.eps = eps;
+    a.keys_in = (uint32_t*)(w + L.keys_in);
+    a.src_in = (uint32_t*)(w + L.src_in);
+    a.hpart = (float*)(w + L.hpart);
+    a.tpart = (float*)(w + L.tpart);
+    int bits = 1;
+    while (bits < 32 && ((uint64_t)1 << bits) < total) ++bits;
+    return hip_status(launch_embbag_adagrad(a, tabs, (uint32_t*)(w + L.keys_out), (uint32_t*)(w + L.src_out),
+                                            w + L.sort, L.sort_bytes, bits, (hipStream_t)stream),
+                      fn);
+}

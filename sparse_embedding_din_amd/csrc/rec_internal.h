@@ -328,6 +328,42 @@ constexpr int kDlrmMaxLdsFloats = 36864;
 int dlrm_stride(int d);
 hipError_t launch_dlrm_interact(const float* z, int64_t B, int F, int d, float* out, int num_cus,
                                 hipStream_t s);
+// Sparse backward + AdaGrad (rec_bwd.hip).  One table: its arrays, its
+// floor-mod constants and its first row in the flat row space of all tables.
+struct BwdTab {
+    float* weights;
+    float* accum;
+    int64_t rows;
+    uint64_t magic;
+    int32_t shift;
+    uint32_t base;
+};
+
+struct BwdArgs {
+    const int64_t* values;
+    const int32_t* lengths;
+    const int64_t* offsets;
+    const float* grad_pooled;     // [B][T*16]
+    const int64_t* seq_values;    // [3][seq_stride]
+    const float* grad_seq;        // [3][P][16]
+    int64_t seq_stride;
+    int64_t B, nnz, P, n;         // n = nnz + 3P contributions
+    int32_t T;
+    int32_t seq_table[3];
+    uint32_t total_rows;
+    float lr, eps;
+    uint32_t* keys_in;            // [n] flat row of each contribution
+    uint32_t* src_in;             // [n] its gradient row
+    const uint32_t* keys;         // sorted (set by the launcher)
+    const uint32_t* src;
+    float* hpart;                 // [chunks][16] head pieces
+    float* tpart;                 // [chunks][16] tail pieces
+};
+
+size_t bwd_sort_bytes(int64_t n);
+hipError_t launch_embbag_adagrad(BwdArgs a, const BwdTab* tabs, uint32_t* keys_out, uint32_t* src_out,
+                                 void* sort_tmp, size_t sort_bytes, int key_bits, hipStream_t s);
+
 hipError_t launch_hash_clear(int64_t* keys, uint8_t* digests, uint64_t* scores, int64_t capacity,
                              hipStream_t s);
 

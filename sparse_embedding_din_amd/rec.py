@@ -32,7 +32,7 @@ EXPORTS = ["rec_din_pack_mlp", "rec_scan_workspace_bytes", "rec_lengths_to_offse
            "rec_hash_insert", "rec_hash_clear", "rec_dlrm_interact",
            "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_fwd",
            "rec_sparse_din_fwd_workspace_bytes", "rec_sparse_din_fwd", "rec_towers_fwd",
-           "rec_tower_pack_mlp",
+           "rec_tower_pack_mlp", "rec_embbag_adagrad_workspace_bytes", "rec_embbag_adagrad",
            "rec_last_error", "rec_version", "rec_host_floor_mod", "rec_host_hash_home",
            "rec_host_hash_probe"]
 
@@ -60,6 +60,10 @@ class rec_tower_mlp(C.Structure):
                 ("wd1", C.c_void_p), ("bd1", C.c_void_p), ("wd2", C.c_void_p), ("bd2", C.c_void_p),
                 ("wd3", C.c_void_p), ("bd3", C.c_void_p), ("wf", C.c_void_p), ("bf", C.c_void_p),
                 ("wo", C.c_void_p), ("bo", C.c_float)]
+
+
+class rec_adagrad_table(C.Structure):
+    _fields_ = [("weights", C.c_void_p), ("accum", C.c_void_p), ("rows", C.c_int64)]
 
 
 class rec_fwd_args(C.Structure):
@@ -111,11 +115,16 @@ def lib():
         L.rec_sparse_din_fwd.argtypes = [C.POINTER(rec_fwd_args), vp]
         L.rec_towers_fwd.argtypes = [C.POINTER(rec_tower_mlp), i64, vp, i64, vp, vp, vp, vp, vp]
         L.rec_tower_pack_mlp.argtypes = [C.POINTER(rec_tower_mlp), vp, sz, vp]
+        L.rec_embbag_adagrad_workspace_bytes.argtypes = [i32, i64, i64, i64]
+        L.rec_embbag_adagrad_workspace_bytes.restype = sz
+        L.rec_embbag_adagrad.argtypes = [C.POINTER(rec_adagrad_table), i32, i64, vp, vp, vp, i64,
+                                         vp, C.POINTER(C.c_int32), vp, i64, i64, vp, C.c_float,
+                                         C.c_float, vp, sz, vp]
         for f in ("rec_lengths_to_offsets", "rec_embbag_fwd", "rec_kjt_sums", "rec_embbag_fwd_kjt",
                   "rec_hash_lookup", "rec_hash_insert", "rec_hash_clear", "rec_dlrm_interact",
                   "rec_din_plan",
                   "rec_din_attn_fwd", "rec_din_pack_mlp", "rec_sparse_din_fwd", "rec_towers_fwd",
-                  "rec_tower_pack_mlp"):
+                  "rec_tower_pack_mlp", "rec_embbag_adagrad"):
             getattr(L, f).restype = C.c_int
         L.rec_last_error.argtypes = []
         L.rec_last_error.restype = C.c_char_p
@@ -176,6 +185,11 @@ def _tables(tabs):
     for i, t in enumerate(tabs):
         arr[i] = t
     return arr
+
+
+def adagrad_table(weights, accum, rows: int) -> rec_adagrad_table:
+    """A host rec_adagrad_table over device tensors (kept alive by the caller)."""
+    return rec_adagrad_table(_p(weights), _p(accum), rows)
 
 
 # -- entry points (same names and arguments as include/rec.h) ----------------
@@ -328,3 +342,23 @@ def rec_host_hash_home(x: int, capacity: int):
     d = C.c_uint8(0)
     home = int(lib().rec_host_hash_home(x, capacity, C.byref(d)))
     return home, int(d.value)
+
+
+def rec_embbag_adagrad_workspace_bytes(T: int, B: int, nnz: int, P: int) -> int:
+    return int(lib().rec_embbag_adagrad_workspace_bytes(T, B, nnz, P))
+
+
+def rec_embbag_adagrad(tables, T: int, B: int, values, lengths, offsets, nnz: int, grad_pooled,
+                       seq_table, seq_values, seq_stride: int, P: int, grad_seq, lr: float,
+                       eps: float, workspace, workspace_bytes: int, stream=None):
+    if isinstance(tables, C.Array):
+        arr = tables
+    else:
+        arr = (rec_adagrad_table * len(tables))()
+        for i, t in enumerate(tables):
+            arr[i] = t
+    st = None if seq_table is None else (C.c_int32 * 3)(*[int(x) for x in seq_table])
+    _check(lib().rec_embbag_adagrad(arr, T, B, _p(values), _p(lengths), _p(offsets), nnz,
+                                    _p(grad_pooled), st, _p(seq_values), seq_stride, P,
+                                    _p(grad_seq), float(lr), float(eps), _p(workspace),
+                                    workspace_bytes, _stream(stream)), "rec_embbag_adagrad")

@@ -465,3 +465,45 @@ def test_host_hash_probe_windowed(lib, cap, nkeys):
         assert R.rec_host_hash_probe(keys, dig, cap, int(k)) == -1
     if cap > 1:
         assert R.rec_host_hash_probe(keys, dig[1:], cap - 1, 0) == -2     # misaligned digests
+
+
+def test_embbag_adagrad_errors(lib):
+    f = lib.rec_embbag_adagrad
+
+    def tabs(n=2, rows=10, w=FAKE, g=FAKE):
+        arr = (R.rec_adagrad_table * n)()
+        for i in range(n):
+            arr[i] = R.rec_adagrad_table(w, g, rows)
+        return arr
+
+    st = (C.c_int32 * 3)(0, 1, 1)
+
+    def call(t=None, T=2, B=4, nnz=8, P=3, seq=st, gp=FAKE, gs=FAKE, ws=FAKE, wsb=1 << 20):
+        t = tabs() if t is None else t
+        return _status(f, t, T, B, FAKE, FAKE, FAKE, nnz, gp, seq, FAKE, max(P, 1), P, gs,
+                       1e-3, 1e-10, ws, wsb, None)
+
+    assert call(t=C.cast(None, C.POINTER(R.rec_adagrad_table)))[0] == R.REC_EINVAL
+    assert call(T=0)[0] == R.REC_EINVAL
+    assert call(t=tabs(33), T=33)[0] == R.REC_EUNSUPPORTED
+    assert call(B=-1)[0] == R.REC_EINVAL
+    assert call(nnz=-1)[0] == R.REC_EINVAL
+    assert call(P=-1)[0] == R.REC_EINVAL
+    assert call(t=tabs(rows=0))[0] == R.REC_EINVAL
+    assert call(t=tabs(w=None))[0] == R.REC_EINVAL
+    assert call(t=tabs(g=FAKE_ODD))[0] == R.REC_EINVAL
+    s, msg = call(t=tabs(rows=1 << 31))
+    assert s == R.REC_EUNSUPPORTED and "2^32" in msg
+    assert call(gp=None)[0] == R.REC_EINVAL
+    assert call(gp=FAKE_ODD)[0] == R.REC_EINVAL
+    assert call(seq=None)[0] == R.REC_EINVAL
+    assert call(gs=FAKE_ODD)[0] == R.REC_EINVAL
+    assert call(seq=(C.c_int32 * 3)(0, 2, 1))[0] == R.REC_EINVAL       # table 2 of T = 2
+    assert call(seq=(C.c_int32 * 3)(-1, 0, 1))[0] == R.REC_EINVAL
+    assert call(nnz=1 << 31)[0] == R.REC_EUNSUPPORTED
+    assert call(nnz=0, P=0, seq=None, gp=None, gs=None, ws=None, wsb=0)[0] == R.REC_OK
+    assert R.rec_embbag_adagrad_workspace_bytes(0, 4, 8, 3) == 0
+    assert R.rec_embbag_adagrad_workspace_bytes(2, 4, 0, 0) == 0
+    with pytest.raises(R.RecError):
+        R.rec_embbag_adagrad([R.adagrad_table(FAKE, FAKE, 10)], 1, 4, FAKE, FAKE, FAKE, 8, None,
+                             None, None, 0, 0, None, 1e-3, 1e-10, FAKE, 1 << 20)
