@@ -486,8 +486,9 @@ typedef struct {
 } rec_adagrad_table;
 
 /* Bytes of workspace rec_embbag_adagrad needs for T tables, B samples, nnz
- * bag ids and P sequence positions; 0 for invalid arguments or when the
- * device cannot be queried (the sort's scratch is sized for the device). */
+ * bag ids and P sequence positions (about 24.5 B per read: 16 B of keys and
+ * sources, 8 B of partial sums, 0.5 B of digit counts); 0 for invalid
+ * arguments or nnz + P == 0. */
 size_t rec_embbag_adagrad_workspace_bytes(int32_t T, int64_t B, int64_t nnz, int64_t P);
 
 /*
@@ -509,8 +510,8 @@ size_t rec_embbag_adagrad_workspace_bytes(int32_t T, int64_t B, int64_t nnz, int
  * Every row read at least once then takes, element by element, with its
  * summed gradient g:  accum += g*g;  weights -= lr * g / (sqrt(accum) + eps)
  * (fp32).  Rows not read are not touched.  A repeated id counts once per
- * repetition.  The sums run in a fixed order (reads sorted by row, stable), so
- * results are bit-identical run to run.
+ * repetition.  The sums run in a fixed order (reads sorted by row with a
+ * stable radix sort, no atomics), so results are bit-identical run to run.
  *
  *   tables      host array of T rec_adagrad_table (T <= REC_MAX_TABLES);
  *               direct tables only, sum of rows < 2^32

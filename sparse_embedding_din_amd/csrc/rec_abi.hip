@@ -595,9 +595,10 @@ namespace {
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Regions of rec_embbag_adagrad's workspace, in order: keys and sources in,
-// sorted keys and sources, head and tail pieces, the sort's scratch.
+// their sort partners, head and tail pieces, the sort's per-tile digit counts
+// and digit totals.
 struct BwdLayout {
-    size_t keys_in, src_in, keys_out, src_out, hpart, tpart, sort, sort_bytes, bytes;
+    size_t keys_in, src_in, keys_out, src_out, hpart, tpart, hist, tot, bytes;
 };
 
 bool bwd_layout(int64_t n, BwdLayout* L) {
@@ -610,10 +611,10 @@ bool bwd_layout(int64_t n, BwdLayout* L) {
     L->src_out = L->keys_out + nb;
     L->hpart = L->src_out + nb;
     L->tpart = L->hpart + pb;
-    L->sort = L->tpart + pb;
-    L->sort_bytes = bwd_sort_bytes(n);
-    L->bytes = L->sort + round256(L->sort_bytes);
-    return L->sort_bytes > 0;
+    L->hist = L->tpart + pb;
+    L->tot = L->hist + round256((size_t)bwd_sort_tiles(n) * 256 * 4);
+    L->bytes = L->tot + round256(256 * 4);
+    return true;
 }
 
 }  // namespace
@@ -677,7 +678,7 @@ rec_status rec_embbag_adagrad(const rec_adagrad_table* tables, int32_t T, int64_
     }
     if (n == 0) return ok();
     BwdLayout L;
-    if (!bwd_layout(n, &L)) return fail(REC_EHIP, f + ": cannot size the sort's scratch on this device");
+    bwd_layout(n, &L);
     if (!workspace || workspace_bytes < L.bytes) return fail(REC_EWORKSPACE, f + ": workspace missing or too small");
     if ((uintptr_t)workspace & 255u) return fail(REC_EINVAL, f + ": workspace not 256-byte aligned");
     char* w = (char*)workspace;
@@ -703,6 +704,7 @@ rec_status rec_embbag_adagrad(const rec_adagrad_table* tables, int32_t T, int64_
     int bits = 1;
     while (bits < 32 && ((uint64_t)1 << bits) < total) ++bits;
     return hip_status(launch_embbag_adagrad(a, tabs, (uint32_t*)(w + L.keys_out), (uint32_t*)(w + L.src_out),
-                                            w + L.sort, L.sort_bytes, bits, (hipStream_t)stream),
+                                            (uint32_t*)(w + L.hist), (uint32_t*)(w + L.tot), bits,
+                                            (hipStream_t)stream),
                       fn);
 }

@@ -15,7 +15,14 @@
 //      position j of sub-feature k (a row of grad_seq).  One wave per table
 //      and 64 bags (or per sub-feature and 64 positions), so the table's
 //      descriptor is wave-uniform.
-//   2. a stable radix sort of (key, source) pairs over the key's bits.
+//   2. a stable LSD radix sort of (key, source) pairs over the key's bits,
+//      8 bits per pass, each pass three launches: k_sort_hist (per tile of
+//      2048 pairs, the count of each digit), k_sort_scan (per digit, the
+//      exclusive scan of its counts over the tiles, and its total), and
+//      k_sort_scatter (each pair to its digit's place, stable: a tile is
+//      ranked in 8 rounds of 256 pairs in order, each wave matching equal
+//      digits by ballots, waves and rounds ordered by counters in LDS).
+//      Every counter is written by a kernel: no memset, no atomics.
 //   3. k_bwd_chunks: the sorted contributions in chunks of 16, one 16-lane
 //      group per chunk, lane d owning component d.  The group loads its 16
 //      gradient rows (64 contiguous bytes each) and sums each run of equal
@@ -33,7 +40,7 @@
 // Hot rows (a 3-row table read once per sample) therefore cost one partial
 // per 16 reads and one walk, not a serial chain of thousands of reads.  No
 // floating-point atomics are used; every sum has one order.
-#include <rocprim/device/device_radix_sort.hpp>
+#include <string.h>
 
 #include "rec_internal.h"
 
@@ -94,28 +101,6 @@ __global__ __launch_bounds__(256) void k_bwd_keys(BwdArgs a, BwdTabArr tabs) {
     a.src_in[c] = (uint32_t)(a.B * a.T + k * a.P + j);
 }
 
-// One element of the AdaGrad step: lane d of a group owns component d.
-__device__ inline void adagrad_apply(const BwdTab* lt, const uint32_t* lbase, int T,
-                                     uint32_t key, float g, int d, float lr, float eps) {
-    const int t = table_of(lbase, T, key);
-    const int64_t r = (int64_t)(key - lbase[t]);
-    if (r >= lt[t].rows) return;                  // unreachable for keys built above
-    float* w = lt[t].weights + r * REC_DIM + d;
-    float* G = lt[t].accum + r * REC_DIM + d;
-    const float gs = *G + g * g;
-    *G = gs;
-    *w = *w - lr * g / (sqrtf(gs) + eps);
-}
-
-// Gradient row of a source index; a source past the end reads nothing.
-__device__ inline float grad_of(const BwdArgs& a, uint32_t src, int d) {
-    const int64_t bt = a.B * a.T;
-    if ((int64_t)src < bt) return a.grad_pooled[(int64_t)src * REC_DIM + d];
-    const int64_t s = (int64_t)src - bt;
-    if (s < 3 * a.P) return a.grad_seq[s * REC_DIM + d];
-    return 0.0f;
-}
-
 __device__ inline void load_tables(const BwdTabArr& tabs, int T, BwdTab* lt, uint32_t* lbase) {
     if (threadIdx.x == 0) {
         for (int t = 0; t < T; ++t) {
@@ -127,120 +112,297 @@ __device__ inline void load_tables(const BwdTabArr& tabs, int T, BwdTab* lt, uin
 }
 
 // ---------------------------------------------------------------------------
-// 3. chunk sums.  256 threads = 16 groups of 16 lanes, one chunk each.
+// 2. radix sort passes.  A tile is 2048 pairs: round r (0..7), thread t holds
+// pair tile*2048 + r*256 + t, so the pairs of a tile are visited in order.
+constexpr int kSortThreads = 256;
+constexpr int kSortRounds = 8;
+constexpr int kSortTile = kSortThreads * kSortRounds;
+
+__global__ __launch_bounds__(256) void k_sort_hist(const uint32_t* keys, int64_t n, int shift,
+                                                   int64_t ntiles, uint32_t* hist) {
+    __shared__ uint32_t h[256];
+    const int t = threadIdx.x;
+    const int64_t tile = blockIdx.x;
+    h[t] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kSortRounds; ++r) {
+        const int64_t idx = tile * kSortTile + r * kSortThreads + t;
+        if (idx < n) atomicAdd(&h[(keys[idx] >> shift) & 255u], 1u);   // counts: order-free
+    }
+    __syncthreads();
+    hist[(int64_t)t * ntiles + tile] = h[t];
+}
+
+// Inclusive scan of one value over the 256 threads (4 waves); returns it and
+// leaves the block total in *total.  Uses red[0..3].
+__device__ inline uint32_t block_scan256(uint32_t v, uint32_t* red, uint32_t* total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_up((int)v, k, 64);
+        if (lane >= k) v += o;
+    }
+    if (lane == 63) red[w] = v;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int j = 0; j < w; ++j) before += red[j];
+    *total = red[0] + red[1] + red[2] + red[3];
+    __syncthreads();
+    return v + before;
+}
+
+// Block d: exclusive scan of digit d's counts over the tiles, in place; its
+// total to tot[d].
+__global__ __launch_bounds__(256) void k_sort_scan(uint32_t* hist, int64_t ntiles, uint32_t* tot) {
+    __shared__ uint32_t red[4];
+    const int t = threadIdx.x;
+    uint32_t* row = hist + (int64_t)blockIdx.x * ntiles;
+    uint32_t carry = 0;
+    for (int64_t j0 = 0; j0 < ntiles; j0 += kSortThreads) {
+        const int64_t j = j0 + t;
+        const uint32_t v = j < ntiles ? row[j] : 0u;
+        uint32_t sum;
+        const uint32_t inc = block_scan256(v, red, &sum);
+        if (j < ntiles) row[j] = carry + inc - v;
+        carry += sum;
+    }
+    if (t == 0) tot[blockIdx.x] = carry;
+}
+
+__global__ __launch_bounds__(256) void k_sort_scatter(const uint32_t* keys, const uint32_t* vals,
+                                                      int64_t n, int shift, int64_t ntiles,
+                                                      const uint32_t* hist, const uint32_t* tot,
+                                                      uint32_t* keys_out, uint32_t* vals_out) {
+    __shared__ uint32_t base[256];        // where digit d's pairs of this tile start
+    __shared__ uint32_t wcnt[4][256];     // this round: pairs of digit d in wave w
+    __shared__ uint32_t red[4];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int64_t tile = blockIdx.x;
+    uint32_t sum;
+    const uint32_t td = tot[t];
+    const uint32_t dstart = block_scan256(td, red, &sum) - td;          // digits below t
+    base[t] = dstart + hist[(int64_t)t * ntiles + tile];
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int r = 0; r < kSortRounds; ++r) {
+        const int64_t idx = tile * kSortTile + r * kSortThreads + t;
+        const bool valid = idx < n;
+        const uint32_t k = valid ? keys[idx] : 0u;
+        const uint32_t v = valid ? vals[idx] : 0u;
+        const uint32_t d = (k >> shift) & 255u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wcnt[j][t] = 0;
+        __syncthreads();
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const uint64_t m = __ballot((d >> b) & 1u);
+            peers &= ((d >> b) & 1u) ? m : ~m;
+        }
+        const uint32_t rank = (uint32_t)__popcll(peers & lt_mask);
+        if (valid && rank == 0) wcnt[w][d] = (uint32_t)__popcll(peers);
+        __syncthreads();
+        if (valid) {
+            uint32_t pos = base[d] + rank;
+            for (int j = 0; j < w; ++j) pos += wcnt[j][d];
+            if ((int64_t)pos < n) {
+                keys_out[pos] = k;
+                vals_out[pos] = v;
+            }
+        }
+        __syncthreads();
+        base[t] += wcnt[0][t] + wcnt[1][t] + wcnt[2][t] + wcnt[3][t];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// A 16-float row held by one lane.
+struct Row16 {
+    float v[16];
+};
+
+__device__ inline void load_row(Row16& r, const float* p) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const float4 x = q[u];
+        r.v[4 * u + 0] = x.x;
+        r.v[4 * u + 1] = x.y;
+        r.v[4 * u + 2] = x.z;
+        r.v[4 * u + 3] = x.w;
+    }
+}
+
+__device__ inline void store_row(float* p, const Row16& r) {
+    float4* q = reinterpret_cast<float4*>(p);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q[u] = make_float4(r.v[4 * u], r.v[4 * u + 1], r.v[4 * u + 2], r.v[4 * u + 3]);
+}
+
+// Gradient row of a source index (a source past the end reads zeros).
+__device__ inline void grad_row(Row16& r, const BwdArgs& a, uint32_t src) {
+    const int64_t bt = a.B * a.T;
+    const int64_t s = (int64_t)src - bt;
+    if ((int64_t)src < bt) {
+        load_row(r, a.grad_pooled + (int64_t)src * REC_DIM);
+    } else if (s < 3 * a.P) {
+        load_row(r, a.grad_seq + s * REC_DIM);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) r.v[e] = 0.0f;
+    }
+}
+
+// The AdaGrad step of one whole row by one lane.
+__device__ inline void adagrad_row(const BwdTab* lt, const uint32_t* lbase, int T, uint32_t key,
+                                   const Row16& g, float lr, float eps) {
+    const int t = table_of(lbase, T, key);
+    const int64_t r = (int64_t)(key - lbase[t]);
+    if (r >= lt[t].rows) return;                  // unreachable for keys built above
+    float* wp = lt[t].weights + r * REC_DIM;
+    float* Gp = lt[t].accum + r * REC_DIM;
+    Row16 w, G;
+    load_row(w, wp);
+    load_row(G, Gp);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        G.v[e] = G.v[e] + g.v[e] * g.v[e];
+        w.v[e] = w.v[e] - lr * g.v[e] / (sqrtf(G.v[e]) + eps);
+    }
+    store_row(Gp, G);
+    store_row(wp, w);
+}
+
+// Value of the lane k places lower in the same 16-lane row (DPP row_shr:k);
+// lanes below k get 0 (never used by the callers).
+template <int k>
+__device__ inline float row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + k, 0xf, 0xf, false));
+}
+
+template <int k>
+__device__ inline void seg_step(Row16& x, bool take) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float t = row_shr<k>(x.v[e]);
+        x.v[e] += take ? t : 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. chunk sums.  256 threads = 16 groups of 16 lanes, one chunk of 16 sorted
+// contributions per group, lane i holding position i's whole gradient row.
+// A segmented inclusive scan across the group (DPP row shifts, a fixed tree)
+// leaves at each run's last lane the sum of the run's part in the chunk.
 __global__ __launch_bounds__(256) void k_bwd_chunks(BwdArgs a, BwdTabArr tabs) {
     __shared__ BwdTab lt[REC_MAX_TABLES];
     __shared__ uint32_t lbase[REC_MAX_TABLES];
     load_tables(tabs, a.T, lt, lbase);
-    const int d = threadIdx.x & 15;
-    const int grp = threadIdx.x >> 4;
+    const int i = threadIdx.x & 15;
     const int gl = (threadIdx.x & 63) & ~15;      // the group's first lane in its wave
-    const int64_t c = (int64_t)blockIdx.x * 16 + grp;
+    const int64_t c = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
     const int64_t n = a.n;
     const int64_t p0 = c * kChunk;
     if (p0 >= n) return;
     const int cnt = (int)((n - p0) < kChunk ? (n - p0) : kChunk);
-    const uint32_t total = a.total_rows;
-
-    // lane d: key and source of position p0 + d, and whether a run starts or
-    // ends there
-    const int64_t p = p0 + d;
-    const bool in = d < cnt;
+    const int64_t p = p0 + i;
+    const bool in = i < cnt;
     const uint32_t key = in ? a.keys[p] : 0xffffffffu;
     const uint32_t src = in ? a.src[p] : 0xffffffffu;
     const bool head = in && (p == 0 || a.keys[p - 1] != key);
     const bool tail = in && (p + 1 >= n || a.keys[p + 1] != key);
-    const uint64_t hm = (__ballot(head) >> gl) & 0xffffu;
-    const uint64_t tm = (__ballot(tail) >> gl) & 0xffffu;
-
-    float g[kChunk];
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-        const uint32_t si = (uint32_t)__shfl((int)src, gl + i, 64);
-        g[i] = i < cnt ? grad_of(a, si, d) : 0.0f;
-    }
-    float acc = 0.0f;
-    bool here = false;                            // the current run began in this chunk
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-        if (i < cnt) {
-            if ((hm >> i) & 1u) { acc = 0.0f; here = true; }
-            acc += g[i];
-            if ((tm >> i) & 1u) {
-                const uint32_t ki = (uint32_t)__shfl((int)key, gl + i, 64);
-                if (here) {
-                    if (ki < total) adagrad_apply(lt, lbase, a.T, ki, acc, d, a.lr, a.eps);
-                } else {
-                    a.hpart[c * REC_DIM + d] = acc;
-                }
-            }
+    const uint32_t hm = (uint32_t)(__ballot(head) >> gl) & 0xffffu;
+    Row16 x;
+    grad_row(x, a, src);
+    // start of lane i's run inside the chunk (0 when it began earlier)
+    const uint32_t upto = hm & ((2u << i) - 1u);
+    const int s0 = upto ? 31 - __builtin_clz(upto) : 0;
+    seg_step<1>(x, i - 1 >= s0);
+    seg_step<2>(x, i - 2 >= s0);
+    seg_step<4>(x, i - 4 >= s0);
+    seg_step<8>(x, i - 8 >= s0);
+    if (tail) {
+        if (upto) {
+            if (key < a.total_rows) adagrad_row(lt, lbase, a.T, key, x, a.lr, a.eps);
+        } else {
+            store_row(a.hpart + c * REC_DIM, x);  // head piece of a run begun earlier
         }
+    } else if (in && i == cnt - 1) {
+        store_row(a.tpart + c * REC_DIM, x);      // tail piece: the run goes on
     }
-    if (!((tm >> (cnt - 1)) & 1u)) a.tpart[c * REC_DIM + d] = acc;
 }
 
 // ---------------------------------------------------------------------------
-// 4. runs that cross chunks.  Each wave examines 64 chunks; a chunk is the
-// END of a crossing run when its first position continues the previous
-// chunk's run and that run ends inside it.
+// 4. runs that cross chunks.  One 16-lane group per chunk; a group whose
+// chunk is the END of a crossing run (its first position continues the
+// previous chunk's run, which ends inside it) walks back 64 chunks per round:
+// lane i looks at chunks cc - i - 16u (u = 0..3), loading the key before each
+// chunk and its tail piece together, so a round is one memory round trip.
 __global__ __launch_bounds__(256) void k_bwd_cross(BwdArgs a, BwdTabArr tabs) {
     __shared__ BwdTab lt[REC_MAX_TABLES];
     __shared__ uint32_t lbase[REC_MAX_TABLES];
     load_tables(tabs, a.T, lt, lbase);
-    const int lane = threadIdx.x & 63;
-    const int d = lane & 15;
-    const int q = lane >> 4;
+    const int i = threadIdx.x & 15;
+    const int gl = (threadIdx.x & 63) & ~15;
     const int64_t n = a.n;
     const int64_t nch = (n + kChunk - 1) / kChunk;
-    const int64_t c0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 64;   // the wave's first chunk
-    const int64_t c = c0 + lane;
-    bool ends = false;
-    if (c > 0 && c < nch) {
-        const int64_t p0 = c * kChunk;
-        const uint32_t k0 = a.keys[p0];
-        if (a.keys[p0 - 1] == k0)
-            ends = p0 + kChunk >= n || a.keys[p0 + kChunk - 1] != k0 || a.keys[p0 + kChunk] != k0;
-    }
-    uint64_t todo = __ballot(ends);
-    while (todo) {
-        const int m1 = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        const int64_t c1 = c0 + m1;
-        const uint32_t K = a.keys[c1 * kChunk];
-        float s = 0.0f;
-        int64_t cc = c1 - 1;                      // newest chunk not yet summed
-        for (;;) {
-            // lane m: does the run also cover the position before chunk cc - m,
-            // i.e. did it begin before that chunk?
-            const int64_t cb = cc - lane;
-            const bool before = cb > 0 && a.keys[cb * kChunk - 1] == K;
-            const uint64_t bm = __ballot(before);
-            const int nb = (~bm) ? __builtin_ctzll(~bm) + 1 : 64;   // chunks cc .. cc-nb+1
-            for (int m = q; m < nb; m += 4) s += a.tpart[(cc - m) * REC_DIM + d];
-            if (nb < 64 || bm != ~0ull) break;
-            cc -= 64;
+    const int64_t c1 = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    if (c1 < 1 || c1 >= nch) return;
+    const int64_t p1 = c1 * kChunk;
+    const uint32_t K = a.keys[p1];
+    if (a.keys[p1 - 1] != K) return;              // no run crosses into this chunk
+    if (p1 + kChunk < n && a.keys[p1 + kChunk - 1] == K && a.keys[p1 + kChunk] == K)
+        return;                                   // the run goes on past this chunk
+    Row16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc.v[e] = 0.0f;
+    int64_t cc = c1 - 1;                          // newest chunk not yet summed
+    for (;;) {
+        Row16 part[4];
+        uint64_t before = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t cb = cc - i - 16 * u;
+            const bool b = cb > 0 && a.keys[cb * kChunk - 1] == K;
+            if (cb >= 0) load_row(part[u], a.tpart + cb * REC_DIM);
+            before |= (uint64_t)((__ballot(b) >> gl) & 0xffffu) << (16 * u);
         }
-        s += __shfl_xor(s, 16, 64);
-        s += __shfl_xor(s, 32, 64);
-        const float gsum = s + a.hpart[c1 * REC_DIM + d];
-        if (q == 0 && K < a.total_rows) adagrad_apply(lt, lbase, a.T, K, gsum, d, a.lr, a.eps);
+        // chunks cc .. cc - nb + 1 belong to the run; the last of them holds its start
+        const int nb = (~before) ? __builtin_ctzll(~before) + 1 : 64;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (i + 16 * u < nb) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc.v[e] += part[u].v[e];
+            }
+        }
+        if (~before) break;
+        cc -= 64;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        float v = acc.v[e];
+        v += __shfl_xor(v, 8, 16);
+        v += __shfl_xor(v, 4, 16);
+        v += __shfl_xor(v, 2, 16);
+        v += __shfl_xor(v, 1, 16);
+        acc.v[e] = v;
+    }
+    if (i == 0 && K < a.total_rows) {
+        Row16 h;
+        load_row(h, a.hpart + c1 * REC_DIM);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc.v[e] += h.v[e];
+        adagrad_row(lt, lbase, a.T, K, acc, a.lr, a.eps);
     }
 }
 
 }  // namespace
 
-size_t bwd_sort_bytes(int64_t n) {
-    size_t bytes = 0;
-    if (n <= 0) return 0;
-    uint32_t* none = nullptr;                     // same iterator types as the launch
-    if (rocprim::radix_sort_pairs(nullptr, bytes, none, none, none, none, (unsigned)n, 0u, 32u,
-                                  (hipStream_t)nullptr) != hipSuccess)
-        return 0;
-    return bytes;
-}
+int64_t bwd_sort_tiles(int64_t n) { return (n + kSortTile - 1) / kSortTile; }
 
 hipError_t launch_embbag_adagrad(BwdArgs a, const BwdTab* tabs, uint32_t* keys_out, uint32_t* src_out,
-                                 void* sort_tmp, size_t sort_bytes, int key_bits, hipStream_t s) {
+                                 uint32_t* sort_hist, uint32_t* sort_tot, int key_bits, hipStream_t s) {
     BwdTabArr ta;
     memset(&ta, 0, sizeof(ta));
     for (int t = 0; t < a.T; ++t) ta.t[t] = tabs[t];
@@ -250,17 +412,32 @@ hipError_t launch_embbag_adagrad(BwdArgs a, const BwdTab* tabs, uint32_t* keys_o
     if (kb > 0) hipLaunchKernelGGL(k_bwd_keys, dim3((unsigned)kb), dim3(256), 0, s, a, ta);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    size_t bytes = sort_bytes;
-    e = rocprim::radix_sort_pairs(sort_tmp, bytes, a.keys_in, keys_out, a.src_in, src_out,
-                                  (unsigned)a.n, 0u, (unsigned)key_bits, s);
-    if (e != hipSuccess) return e;
+    // ping-pong between (keys_in, src_in) and (keys_out, src_out)
+    const int64_t nt = bwd_sort_tiles(a.n);
+    uint32_t* kin = a.keys_in;
+    uint32_t* vin = a.src_in;
+    uint32_t* kout = keys_out;
+    uint32_t* vout = src_out;
+    for (int shift = 0; shift < key_bits; shift += 8) {
+        hipLaunchKernelGGL(k_sort_hist, dim3((unsigned)nt), dim3(kSortThreads), 0, s, kin, a.n, shift, nt,
+                           sort_hist);
+        hipLaunchKernelGGL(k_sort_scan, dim3(256), dim3(kSortThreads), 0, s, sort_hist, nt, sort_tot);
+        hipLaunchKernelGGL(k_sort_scatter, dim3((unsigned)nt), dim3(kSortThreads), 0, s, kin, vin, a.n, shift,
+                           nt, sort_hist, sort_tot, kout, vout);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        uint32_t* tk = kin; kin = kout; kout = tk;
+        uint32_t* tv = vin; vin = vout; vout = tv;
+    }
+    keys_out = kin;                               // the last pass's output
+    src_out = vin;
     a.keys = keys_out;
     a.src = src_out;
     const int64_t nch = (a.n + kChunk - 1) / kChunk;
     hipLaunchKernelGGL(k_bwd_chunks, dim3((unsigned)((nch + 15) / 16)), dim3(256), 0, s, a, ta);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_bwd_cross, dim3((unsigned)((nch + 255) / 256)), dim3(256), 0, s, a, ta);
+    hipLaunchKernelGGL(k_bwd_cross, dim3((unsigned)((nch + 15) / 16)), dim3(256), 0, s, a, ta);
     return hipGetLastError();
 }
 

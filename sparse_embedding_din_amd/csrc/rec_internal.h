@@ -360,9 +360,9 @@ struct BwdArgs {
     float* tpart;                 // [chunks][16] tail pieces
 };
 
-size_t bwd_sort_bytes(int64_t n);
+int64_t bwd_sort_tiles(int64_t n);            // tiles of the radix sort (256 counters each)
 hipError_t launch_embbag_adagrad(BwdArgs a, const BwdTab* tabs, uint32_t* keys_out, uint32_t* src_out,
-                                 void* sort_tmp, size_t sort_bytes, int key_bits, hipStream_t s);
+                                 uint32_t* sort_hist, uint32_t* sort_tot, int key_bits, hipStream_t s);
 
 hipError_t launch_hash_clear(int64_t* keys, uint8_t* digests, uint64_t* scores, int64_t capacity,
                              hipStream_t s);

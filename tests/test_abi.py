@@ -502,6 +502,13 @@ def test_embbag_adagrad_errors(lib):
     assert call(seq=(C.c_int32 * 3)(-1, 0, 1))[0] == R.REC_EINVAL
     assert call(nnz=1 << 31)[0] == R.REC_EUNSUPPORTED
     assert call(nnz=0, P=0, seq=None, gp=None, gs=None, ws=None, wsb=0)[0] == R.REC_OK
+    wsb = R.rec_embbag_adagrad_workspace_bytes(2, 4, 8, 3)
+    assert wsb >= 4 * 4 * 17 and wsb % 256 == 0          # four 4-byte arrays of 17 reads
+    assert call(ws=FAKE, wsb=wsb - 1)[0] == R.REC_EWORKSPACE
+    assert call(ws=None, wsb=wsb)[0] == R.REC_EWORKSPACE
+    assert call(ws=FAKE + 16, wsb=wsb)[0] == R.REC_EINVAL              # not 256-byte aligned
+    big = R.rec_embbag_adagrad_workspace_bytes(16, 8192, 253952, 32768)
+    assert 24 * (253952 + 3 * 32768) <= big <= 26 * (253952 + 3 * 32768)
     assert R.rec_embbag_adagrad_workspace_bytes(0, 4, 8, 3) == 0
     assert R.rec_embbag_adagrad_workspace_bytes(2, 4, 0, 0) == 0
     with pytest.raises(R.RecError):
