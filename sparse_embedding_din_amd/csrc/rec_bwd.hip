@@ -253,17 +253,20 @@ __device__ inline void grad_row(Row16& r, const BwdArgs& a, uint32_t src) {
     }
 }
 
-// The AdaGrad step of one whole row by one lane.
-__device__ inline void adagrad_row(const BwdTab* lt, const uint32_t* lbase, int T, uint32_t key,
-                                   const Row16& g, float lr, float eps) {
+// Weights and accumulator row of a flat row key (null past a table's end,
+// which keys built above never are).
+__device__ inline float* locate(const BwdTab* lt, const uint32_t* lbase, int T, uint32_t key,
+                                float** accum) {
     const int t = table_of(lbase, T, key);
     const int64_t r = (int64_t)(key - lbase[t]);
-    if (r >= lt[t].rows) return;                  // unreachable for keys built above
-    float* wp = lt[t].weights + r * REC_DIM;
-    float* Gp = lt[t].accum + r * REC_DIM;
-    Row16 w, G;
-    load_row(w, wp);
-    load_row(G, Gp);
+    if (r >= lt[t].rows) return nullptr;
+    *accum = lt[t].accum + r * REC_DIM;
+    return lt[t].weights + r * REC_DIM;
+}
+
+// The AdaGrad step of one whole row by one lane, on rows loaded beforehand.
+__device__ inline void adagrad_store(float* wp, float* Gp, Row16& w, Row16& G, const Row16& g,
+                                     float lr, float eps) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         G.v[e] = G.v[e] + g.v[e] * g.v[e];
@@ -317,13 +320,22 @@ __global__ __launch_bounds__(256) void k_bwd_chunks(BwdArgs a, BwdTabArr tabs) {
     // start of lane i's run inside the chunk (0 when it began earlier)
     const uint32_t upto = hm & ((2u << i) - 1u);
     const int s0 = upto ? 31 - __builtin_clz(upto) : 0;
+    // a run that ends here and began in this chunk is complete: its weights
+    // and accumulator are loaded now, beside the gradients
+    float* Gp = nullptr;
+    float* wp = (tail && upto && key < a.total_rows) ? locate(lt, lbase, a.T, key, &Gp) : nullptr;
+    Row16 w, G;
+    if (wp) {
+        load_row(w, wp);
+        load_row(G, Gp);
+    }
     seg_step<1>(x, i - 1 >= s0);
     seg_step<2>(x, i - 2 >= s0);
     seg_step<4>(x, i - 4 >= s0);
     seg_step<8>(x, i - 8 >= s0);
     if (tail) {
         if (upto) {
-            if (key < a.total_rows) adagrad_row(lt, lbase, a.T, key, x, a.lr, a.eps);
+            if (wp) adagrad_store(wp, Gp, w, G, x, a.lr, a.eps);
         } else {
             store_row(a.hpart + c * REC_DIM, x);  // head piece of a run begun earlier
         }
@@ -353,6 +365,15 @@ __global__ __launch_bounds__(256) void k_bwd_cross(BwdArgs a, BwdTabArr tabs) {
     if (a.keys[p1 - 1] != K) return;              // no run crosses into this chunk
     if (p1 + kChunk < n && a.keys[p1 + kChunk - 1] == K && a.keys[p1 + kChunk] == K)
         return;                                   // the run goes on past this chunk
+    // lane 0 owns the step: its rows and the head piece load beside the walk
+    float* Gp = nullptr;
+    float* wp = (i == 0 && K < a.total_rows) ? locate(lt, lbase, a.T, K, &Gp) : nullptr;
+    Row16 w, G, h;
+    if (wp) {
+        load_row(w, wp);
+        load_row(G, Gp);
+        load_row(h, a.hpart + c1 * REC_DIM);
+    }
     Row16 acc;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc.v[e] = 0.0f;
@@ -388,12 +409,10 @@ __global__ __launch_bounds__(256) void k_bwd_cross(BwdArgs a, BwdTabArr tabs) {
         v += __shfl_xor(v, 1, 16);
         acc.v[e] = v;
     }
-    if (i == 0 && K < a.total_rows) {
-        Row16 h;
-        load_row(h, a.hpart + c1 * REC_DIM);
+    if (wp) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc.v[e] += h.v[e];
-        adagrad_row(lt, lbase, a.T, K, acc, a.lr, a.eps);
+        adagrad_store(wp, Gp, w, G, acc, a.lr, a.eps);
     }
 }
 
