@@ -79,7 +79,8 @@ class Oracle:
         L.orc_hash_check.restype = C.c_int64
         L.orc_dlrm_interact.argtypes = [PF, C.c_int64, C.c_int32, C.c_int32, PD, PD]
         L.orc_dlrm_interact.restype = None
-        L.orc_embbag_adagrad.argtypes = [C.c_int32, C.c_int64, P64, P64, P64, P32, P64, PF,
+        L.orc_embbag_adagrad.argtypes = [C.c_int32, C.c_int64, C.POINTER(OrcTable), P64, P64, P32,
+                                         P64, PF,
                                          C.c_int64, P32, P64, C.c_int64, PF, C.c_double,
                                          C.c_double, PD, PD, PD, P8]
         L.orc_embbag_adagrad.restype = C.c_int64
@@ -133,16 +134,21 @@ class Oracle:
         return int(self.lib.orc_hash_check(_ptr(keys, P64), _ptr(digests, P8), keys.size))
 
     # -- backward of the bags + sparse AdaGrad ------------------------------------
-    def embbag_adagrad(self, rows, B: int, values, lengths, offsets, dpooled, weights, accums,
+    def embbag_adagrad(self, tabs, B: int, values, lengths, offsets, dpooled, weights, accums,
                        lr: float = 1e-3, eps: float = 1e-10, seq=None):
-        """One sparse AdaGrad step of T direct tables from the gradient of the
+        """One sparse AdaGrad step of T tables from the gradient of the
         sum-pooled output, dpooled [B][T*16] (fp32), and optionally of the
         unpooled sequence rows: seq = (seq_table [3], seq_values [3][>=P],
-        dseq [3][P][16] fp32).  weights / accums: T arrays [rows[t]][16] (not
-        modified).  Returns (new weights, new accums, summed gradient,
-        touched mask), lists of T fp64 arrays (mask: bool)."""
-        T = len(rows)
-        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        dseq [3][P][16] fp32).  tabs: generator table dicts (direct or hash;
+        a hash table's rows are its slots), or plain row counts for direct
+        tables.  weights / accums: T arrays [rows][16] (not modified).
+        Returns (new weights, new accums, summed gradient, touched mask),
+        lists of T fp64 arrays (mask: bool)."""
+        T = len(tabs)
+        tabs = [dict(kind="direct", rows=int(t), values=np.zeros((1, 16), np.float32))
+                if isinstance(t, (int, np.integer)) else t for t in tabs]
+        wrapped = self.tables(tabs)
+        rows = np.array([int(t["rows"]) for t in tabs], dtype=np.int64)
         base = np.concatenate([[0], np.cumsum(rows)[:-1]]).astype(np.int64)
         R = int(rows.sum())
         values = np.ascontiguousarray(values, dtype=np.int64)
@@ -166,7 +172,7 @@ class Oracle:
             stride = sv.shape[1]
             assert st.shape == (3,) and ds.shape == (3, P, 16) and sv.shape[0] == 3 and stride >= P
             assert np.all((st >= 0) & (st < T))
-        outside = self.lib.orc_embbag_adagrad(T, B, _ptr(rows, P64), _ptr(base, P64), _ptr(values, P64),
+        outside = self.lib.orc_embbag_adagrad(T, B, wrapped, _ptr(base, P64), _ptr(values, P64),
                                     _ptr(lengths, P32), _ptr(offsets, P64), _ptr(dp, PF), P,
                                     _ptr(st, P32), _ptr(sv, P64), stride, _ptr(ds, PF),
                                     float(lr), float(eps), _ptr(w, PD), _ptr(G, PD),

@@ -240,6 +240,75 @@ void orc_resolve_many(const orc_table* t, const int64_t* raw, int64_t n, int64_t
     for (int64_t i = 0; i < n; ++i) rows[i] = orc_resolve(t, raw[i]);
 }
 
+/* ---- sparse backward of the bags + AdaGrad step ([P1] run-config table:
+ * sparse parameters train with AdaGrad, lr 1e-3; [P1] §3: the AdaGrad
+ * accumulator is as large as the table, one value per weight; [P2] §3.3:
+ * the gradient is accumulated in fp32 or wider) -------------------------------
+ * All T tables sit in one flat row space: table t owns rows base[t] ..
+ * base[t] + tables[t].rows - 1 of w, G, grad and touched ([R][16] / [R]); a
+ * hash table's rows are its slots.
+ * The gradient of a weight row is the sum of the output gradients of every
+ * place that row was read:
+ *   - each id of bag (t, b) adds dpooled[b][16t .. 16t+16) to the row of the
+ *     id in table t (direct: floor_mod(id, rows); hash: the slot holding the
+ *     id) -- the pooled sum reads it once per id, so a repeated id adds its
+ *     bag's gradient once per repetition.  A hash miss reads the constant zero
+ *     vector ([P2] §3.2), no row: its gradient goes nowhere;
+ *   - each packed sequence position j < P of sub-feature k adds
+ *     dseq[k][j][0..16) to the row of seq_values[k*seq_stride + j] in table
+ *     seq_table[k] (the unpooled sequence rows the attention reads).
+ * grad receives that sum (it must be zero on entry) and touched marks each row
+ * read at least once.  Then every touched row takes one element-wise AdaGrad
+ * step with its summed gradient g:
+ *   G += g * g;   w -= lr * g / (sqrt(G) + eps).
+ * Untouched rows are left as they are.  Returns the number of reads whose
+ * row fell outside its table (0 unless the row arithmetic is broken); those
+ * are skipped, never written.                                              */
+int64_t orc_embbag_adagrad(int32_t T, int64_t B, const orc_table* tables, const int64_t* base,
+                        const int64_t* values, const int32_t* lengths, const int64_t* offsets,
+                        const float* dpooled, int64_t P, const int32_t* seq_table,
+                        const int64_t* seq_values, int64_t seq_stride, const float* dseq,
+                        double lr, double eps, double* w, double* G, double* grad,
+                        uint8_t* touched) {
+    int64_t outside = 0;
+    for (int32_t t = 0; t < T; ++t) {
+        for (int64_t b = 0; b < B; ++b) {
+            const int64_t bag = (int64_t)t * B + b;
+            for (int64_t i = 0; i < lengths[bag]; ++i) {
+                const int64_t rt = orc_resolve(&tables[t], values[offsets[bag] + i]);
+                if (rt < 0 && tables[t].kind == 1) continue;          /* hash miss */
+                if (rt < 0 || rt >= tables[t].rows) { ++outside; continue; }
+                const int64_t r = base[t] + rt;
+                touched[r] = 1;
+                for (int d = 0; d < ORC_DIM; ++d)
+                    grad[r * ORC_DIM + d] += (double)dpooled[b * (int64_t)T * ORC_DIM + t * ORC_DIM + d];
+            }
+        }
+    }
+    for (int k = 0; k < 3 && P > 0; ++k) {
+        const int32_t t = seq_table[k];
+        for (int64_t j = 0; j < P; ++j) {
+            const int64_t rt = orc_resolve(&tables[t], seq_values[k * seq_stride + j]);
+            if (rt < 0 && tables[t].kind == 1) continue;              /* hash miss */
+            if (rt < 0 || rt >= tables[t].rows) { ++outside; continue; }
+            const int64_t r = base[t] + rt;
+            touched[r] = 1;
+            for (int d = 0; d < ORC_DIM; ++d)
+                grad[r * ORC_DIM + d] += (double)dseq[(k * P + j) * ORC_DIM + d];
+        }
+    }
+    const int64_t R = base[T - 1] + tables[T - 1].rows;
+    for (int64_t r = 0; r < R; ++r) {
+        if (!touched[r]) continue;
+        for (int d = 0; d < ORC_DIM; ++d) {
+            const double g = grad[r * ORC_DIM + d];
+            G[r * ORC_DIM + d] += g * g;
+            w[r * ORC_DIM + d] -= lr * g / (sqrt(G[r * ORC_DIM + d]) + eps);
+        }
+    }
+    return outside;
+}
+
 /* Embedding of a raw id: the table row, or the zero vector on a hash miss. */
 static void orc_emb(const orc_table* t, int64_t raw, double* out16) {
     int64_t r = orc_resolve(t, raw);
@@ -267,70 +336,6 @@ void orc_embbag(int32_t T, int64_t B, const orc_table* tables,
             for (int d = 0; d < ORC_DIM; ++d) pooled[s * (int64_t)T * ORC_DIM + k * ORC_DIM + d] = acc[d];
         }
     }
-}
-
-/* ---- sparse backward of the bags + AdaGrad step ([P1] run-config table:
- * sparse parameters train with AdaGrad, lr 1e-3; [P1] §3: the AdaGrad
- * accumulator is as large as the table, one value per weight; [P2] §3.3:
- * the gradient is accumulated in fp32 or wider) -------------------------------
- * All T direct tables sit in one flat row space: table t owns rows
- * base[t] .. base[t] + rows[t] - 1 of w, G, grad and touched ([R][16] / [R]).
- * The gradient of a weight row is the sum of the output gradients of every
- * place that row was read:
- *   - each id of bag (t, b) adds dpooled[b][16t .. 16t+16) to the row
- *     floor_mod(id, rows[t]) of table t (the pooled sum reads it once per id,
- *     so a repeated id adds its bag's gradient once per repetition);
- *   - each packed sequence position j < P of sub-feature k adds
- *     dseq[k][j][0..16) to the row of seq_values[k*seq_stride + j] in table
- *     seq_table[k] (the unpooled sequence rows the attention reads).
- * grad receives that sum (it must be zero on entry) and touched marks each row
- * read at least once.  Then every touched row takes one element-wise AdaGrad
- * step with its summed gradient g:
- *   G += g * g;   w -= lr * g / (sqrt(G) + eps).
- * Untouched rows are left as they are.  Returns the number of reads whose
- * row fell outside its table (0 unless the row arithmetic is broken); those
- * are skipped, never written.                                              */
-int64_t orc_embbag_adagrad(int32_t T, int64_t B, const int64_t* rows, const int64_t* base,
-                        const int64_t* values, const int32_t* lengths, const int64_t* offsets,
-                        const float* dpooled, int64_t P, const int32_t* seq_table,
-                        const int64_t* seq_values, int64_t seq_stride, const float* dseq,
-                        double lr, double eps, double* w, double* G, double* grad,
-                        uint8_t* touched) {
-    int64_t outside = 0;
-    for (int32_t t = 0; t < T; ++t) {
-        for (int64_t b = 0; b < B; ++b) {
-            const int64_t bag = (int64_t)t * B + b;
-            for (int64_t i = 0; i < lengths[bag]; ++i) {
-                const int64_t rt = orc_floor_mod(values[offsets[bag] + i], rows[t]);
-                if (rt < 0 || rt >= rows[t]) { ++outside; continue; }
-                const int64_t r = base[t] + rt;
-                touched[r] = 1;
-                for (int d = 0; d < ORC_DIM; ++d)
-                    grad[r * ORC_DIM + d] += (double)dpooled[b * (int64_t)T * ORC_DIM + t * ORC_DIM + d];
-            }
-        }
-    }
-    for (int k = 0; k < 3 && P > 0; ++k) {
-        const int32_t t = seq_table[k];
-        for (int64_t j = 0; j < P; ++j) {
-            const int64_t rt = orc_floor_mod(seq_values[k * seq_stride + j], rows[t]);
-            if (rt < 0 || rt >= rows[t]) { ++outside; continue; }
-            const int64_t r = base[t] + rt;
-            touched[r] = 1;
-            for (int d = 0; d < ORC_DIM; ++d)
-                grad[r * ORC_DIM + d] += (double)dseq[(k * P + j) * ORC_DIM + d];
-        }
-    }
-    const int64_t R = base[T - 1] + rows[T - 1];
-    for (int64_t r = 0; r < R; ++r) {
-        if (!touched[r]) continue;
-        for (int d = 0; d < ORC_DIM; ++d) {
-            const double g = grad[r * ORC_DIM + d];
-            G[r * ORC_DIM + d] += g * g;
-            w[r * ORC_DIM + d] -= lr * g / (sqrt(G[r * ORC_DIM + d]) + eps);
-        }
-    }
-    return outside;
 }
 
 /* ---- DIN target attention ([P1] §4.2, §4.4) -----------------------------

@@ -538,35 +538,78 @@ def _torch_sparse_step(m, b, dpooled, seq, weights, opt_state, lr, eps):
     """The pages' training step for the tables ("当前现状分析" run-config table:
     sparse AdaGrad) written with torch library routines in fp64: per-table
     embedding_bag(mode='sum') and embedding, autograd for the table gradients,
-    and torch.optim.Adagrad for the step.  Returns the tensors and optimizer."""
+    and torch.optim.Adagrad for the step.  Every table gets one extra all-zero
+    row that hash misses index (the constant zero vector of "集成 DynamicEmb"
+    §3.2); that row is not part of the table.  Returns the tensors, the
+    optimizer and the gradients of the real rows."""
     B = b.B
     starts = np.concatenate([[0], np.cumsum(b.lengths)])
     L = b.lengths.reshape(synth.T, B)
     if weights is None:
-        weights = [torch.tensor(np.asarray(t["values"], np.float64), requires_grad=True)
+        weights = [torch.tensor(np.concatenate([np.asarray(t["values"], np.float64),
+                                                np.zeros((1, 16))]), requires_grad=True)
                    for t in m.tables]
         opt_state = torch.optim.Adagrad(weights, lr=lr, eps=eps, initial_accumulator_value=0.0,
                                         foreach=False)
+
+    def rows_of(k, raw):
+        r = py_rows(m.tables[k], raw)
+        return torch.from_numpy(np.where(r < 0, int(m.tables[k]["rows"]), r))
+
     opt_state.zero_grad()
     loss = torch.zeros((), dtype=torch.float64)
     for k in range(synth.T):
         lo, hi = starts[k * B], starts[(k + 1) * B]
-        rows = torch.from_numpy(py_rows(m.tables[k], b.values[lo:hi]))
         bag_off = torch.from_numpy(np.concatenate([[0], np.cumsum(L[k])[:-1]]).astype(np.int64))
-        pooled = F.embedding_bag(rows, weights[k], bag_off, mode="sum")
+        pooled = F.embedding_bag(rows_of(k, b.values[lo:hi]), weights[k], bag_off, mode="sum")
         g = torch.from_numpy(dpooled[:, 16 * k:16 * k + 16].astype(np.float64))
         loss = loss + (pooled * g).sum()
     if seq is not None:
         st, sv, ds = seq
         P = ds.shape[1]
         for f in range(3):
-            rows = torch.from_numpy(py_rows(m.tables[st[f]], sv[f, :P]))
-            loss = loss + (F.embedding(rows, weights[st[f]]) *
+            loss = loss + (F.embedding(rows_of(st[f], sv[f, :P]), weights[st[f]]) *
                            torch.from_numpy(ds[f].astype(np.float64))).sum()
     loss.backward()
-    grads = [w.grad.detach().clone().numpy() for w in weights]
+    grads = [w.grad.detach()[:-1].clone().numpy() for w in weights]
     opt_state.step()
     return weights, opt_state, grads
+
+
+def _adagrad_two_steps(orc, m, b, seed):
+    off = orc.lengths_to_offsets(b.lengths)
+    rng = np.random.default_rng(seed)
+    P = int(b.seq_lengths.sum())
+    st = np.array(synth.SEQ_KEYS, np.int32)
+    w = [np.asarray(t["values"], np.float32) for t in m.tables]
+    G = [np.zeros((int(t["rows"]), 16), np.float32) for t in m.tables]
+    tw, topt = None, None
+    for step, lr in ((0, 1e-3), (1, 1e-3)):
+        dp = rng.standard_normal((b.B, 256)).astype(np.float32)
+        ds = rng.standard_normal((3, P, 16)).astype(np.float32)
+        seq = (st, b.seq_values, ds)
+        nw, nG, grad, touched = orc.embbag_adagrad(m.tables, b.B, b.values, b.lengths, off, dp, w,
+                                                   G, lr=lr, eps=1e-10, seq=seq)
+        tw, topt, tgrad = _torch_sparse_step(m, b, dp, seq, tw, topt, lr, 1e-10)
+        for k in range(synth.T):
+            m_ = touched[k]
+            tw_k = tw[k].detach()[:-1].numpy()
+            assert _rel(grad[k], tgrad[k]) < 1e-13, (step, k)
+            assert _rel(nw[k][m_], tw_k[m_]) < 1e-13, (step, k)
+            assert _rel(nG[k], topt.state[tw[k]]["sum"][:-1].numpy()) < 1e-13, (step, k)
+            # rows nobody read (empty hash slots hold NaN) keep their bits
+            w0 = np.asarray(w[k], np.float64)[~m_]
+            assert np.array_equal(nw[k][~m_], w0, equal_nan=True)
+            assert np.array_equal(tw_k[~m_], w0, equal_nan=True)
+            assert np.array_equal(nG[k][~m_], np.asarray(G[k], np.float64)[~m_])
+            assert np.all(np.isfinite(nw[k][m_]))
+            if step == 0:
+                gk = grad[k][touched[k]]
+                assert np.array_equal(nG[k][touched[k]], gk * gk)
+                want = np.asarray(w[k], np.float64)[touched[k]] - lr * gk / (np.abs(gk) + 1e-10)
+                assert _rel(nw[k][touched[k]], want) < 1e-15
+        w = [a.astype(np.float64) for a in nw]
+        G = [a.astype(np.float64) for a in nG]
 
 
 def pin_embbag_adagrad(orc):
@@ -574,9 +617,11 @@ def pin_embbag_adagrad(orc):
     AdaGrad ("当前现状分析" run-config table and §3), against torch fp64
     autograd through embedding_bag / embedding and torch.optim.Adagrad, for two
     steps in a row (the second from the first's accumulators), with empty bags
-    and repeated ids; closed forms: after one step from a zero accumulator
-    G = g^2 exactly and w moves by lr * g / (|g| + eps); untouched rows keep
-    their bits; a repeated id counts once per repetition."""
+    and repeated ids, on direct tables and on hash tables whose misses read
+    the zero vector ("集成 DynamicEmb" §3.2) and so take no gradient; closed
+    forms: after one step from a zero accumulator G = g^2 exactly and w moves
+    by lr * g / (|g| + eps); untouched rows keep their bits; a repeated id
+    counts once per repetition."""
     m, b = _tiny(B=48)
     L = b.lengths.reshape(synth.T, b.B).copy()
     L[2, ::4] = 0
@@ -588,38 +633,24 @@ def pin_embbag_adagrad(orc):
             vals.append(b.values[starts[i]: starts[i] + L[k, bb]])
     b.lengths = L.reshape(-1).astype(np.int32)
     b.values = np.concatenate(vals).astype(np.int64)
-    off = orc.lengths_to_offsets(b.lengths)
+    _adagrad_two_steps(orc, m, b, 91)
+    mh = synth.make_model(TINY_HASH)
+    bh = synth.make_batch(mh, B=40)
+    _adagrad_two_steps(orc, mh, bh, 92)
+    # a hash miss takes no gradient: a bag of misses touches nothing
     rows = [int(t["rows"]) for t in m.tables]
-    rng = np.random.default_rng(91)
-    P = int(b.seq_lengths.sum())
-    st = np.array(synth.SEQ_KEYS, np.int32)
-    w = [np.asarray(t["values"], np.float32) for t in m.tables]
-    G = [np.zeros((r, 16), np.float32) for r in rows]
-    tw, topt = None, None
-    for step, lr in ((0, 1e-3), (1, 1e-3)):
-        dp = rng.standard_normal((b.B, 256)).astype(np.float32)
-        ds = rng.standard_normal((3, P, 16)).astype(np.float32)
-        seq = (st, b.seq_values, ds)
-        nw, nG, grad, touched = orc.embbag_adagrad(rows, b.B, b.values, b.lengths, off, dp, w, G,
-                                                   lr=lr, eps=1e-10, seq=seq)
-        tw, topt, tgrad = _torch_sparse_step(m, b, dp, seq, tw, topt, lr, 1e-10)
-        for k in range(synth.T):
-            assert _rel(grad[k], tgrad[k]) < 1e-13, (step, k)
-            assert _rel(nw[k], tw[k].detach().numpy()) < 1e-13, (step, k)
-            assert _rel(nG[k], topt.state[tw[k]]["sum"].numpy()) < 1e-13, (step, k)
-            # rows nobody read keep their weight and accumulator bit for bit
-            assert np.array_equal(nw[k][~touched[k]], np.asarray(w[k], np.float64)[~touched[k]])
-            assert np.array_equal(nG[k][~touched[k]], np.asarray(G[k], np.float64)[~touched[k]])
-            if step == 0:
-                gk = grad[k][touched[k]]
-                assert np.array_equal(nG[k][touched[k]], gk * gk)
-                want = np.asarray(w[k], np.float64)[touched[k]] - lr * gk / (np.abs(gk) + 1e-10)
-                assert _rel(nw[k][touched[k]], want) < 1e-15
-        w = [a.astype(np.float64) for a in nw]
-        G = [a.astype(np.float64) for a in nG]
+    lens = np.zeros(synth.T, np.int32)
+    lens[0] = 2
+    stored = set(mh.tables[0]["keys"].tolist())
+    miss = [x for x in range(1, 100) if x not in stored][:2]
+    o1 = orc.lengths_to_offsets(lens)
+    dp = np.ones((1, 256), np.float32)
+    zh = [np.zeros((int(t["rows"]), 16)) for t in mh.tables]
+    _, _, grad, touched = orc.embbag_adagrad(mh.tables, 1, np.array(miss, np.int64), lens, o1, dp,
+                                             zh, zh)
+    assert not any(t.any() for t in touched) and all(not g.any() for g in grad)
     # a repeated id adds its bag's gradient once per repetition: one bag of
     # table 8 (3 rows) holding id 4 three times moves row 1 by 3 * dpooled
-    B1 = 1
     lens = np.zeros(synth.T, np.int32)
     lens[8] = 3
     v = np.array([4, 4, 4], np.int64)
@@ -627,7 +658,7 @@ def pin_embbag_adagrad(orc):
     dp = np.zeros((1, 256), np.float32)
     dp[0, 128:144] = np.arange(1, 17, dtype=np.float32) / 8
     z = [np.zeros((r, 16)) for r in rows]
-    _, nG, grad, touched = orc.embbag_adagrad(rows, B1, v, lens, o1, dp, z, z, lr=1e-3)
+    _, nG, grad, touched = orc.embbag_adagrad(rows, 1, v, lens, o1, dp, z, z, lr=1e-3)
     assert [int(t.sum()) for t in touched] == [1 if k == 8 else 0 for k in range(synth.T)]
     assert np.array_equal(grad[8][1], 3.0 * dp[0, 128:144].astype(np.float64))
     assert np.array_equal(nG[8][1], (3.0 * dp[0, 128:144].astype(np.float64)) ** 2)

@@ -98,9 +98,15 @@ MUTANTS = [
      "(double)dpooled[b * (int64_t)T * ORC_DIM + d];"),
     ("a repeated id counted once", "for (int d = 0; d < ORC_DIM; ++d)\n                    grad[r * ORC_DIM + d] +=",
      "for (int d = 0; d < ORC_DIM; ++d)\n                    grad[r * ORC_DIM + d] = "),
+    ("backward hash miss not skipped",
+     "if (rt < 0 && tables[t].kind == 1) continue;          /* hash miss */",
+     "if (0) continue;          /* hash miss */"),
+    ("backward resolves every table by floor mod",
+     "const int64_t rt = orc_resolve(&tables[t], values[offsets[bag] + i]);",
+     "const int64_t rt = orc_floor_mod(values[offsets[bag] + i], tables[t].rows);"),
     ("backward drops the last id of a bag",
-     "for (int64_t i = 0; i < lengths[bag]; ++i) {\n                const int64_t rt = orc_floor_mod(",
-     "for (int64_t i = 0; i + 1 < lengths[bag]; ++i) {\n                const int64_t rt = orc_floor_mod("),
+     "for (int64_t i = 0; i < lengths[bag]; ++i) {\n                const int64_t rt = orc_resolve(",
+     "for (int64_t i = 0; i + 1 < lengths[bag]; ++i) {\n                const int64_t rt = orc_resolve("),
 ]
 
 
