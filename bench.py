@@ -7,7 +7,9 @@ lengths -> offsets, sequence plan, sum-pooled embedding bags (16 tables,
 3.14M rows), padding-free DIN attention (bf16 matrix cores, fp32 accumulate),
 made as one rec_sparse_din_fwd call (three kernel launches).  The rest of the
 MultiTowerDIN forward (deep tower + final MLP, rec_towers_fwd) is timed
-beside it and reported under "towers"; it is not part of the timed step.
+beside it and reported under "towers"; it is not part of the timed step.  So are
+the sparse backward with its AdaGrad step ("adagrad") and the DLRM interaction
+layer at 217 x 96 ("dlrm_interaction").
 Four resident batches rotate (so the L2 does not keep one batch's rows); one
 HIP graph holds a step for each of them and is replayed.  Everything runs on
 one stream: inside a graph, a fork/join to a second stream costs more than
@@ -70,6 +72,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-hash-rebuild", action="store_true",
                    help="skip timing the rebuild of the hash workload's tables (clear + insert)")
+    p.add_argument("--no-interaction", action="store_true",
+                   help="skip the DLRM interaction leg (217 vectors of width 96 per sample)")
     p.add_argument("--no-adagrad", action="store_true",
                    help="skip the backward + sparse AdaGrad leg reported beside the step")
     p.add_argument("--no-towers", action="store_true",
@@ -100,7 +104,10 @@ def src_hash() -> str:
 CAL_BYTES = 64 << 20            # bytes read (and written) by the calibration copy
 KERNELS = {"k_din_attn": "k_din_attn",
            "k_embbag_fwd": "k_embbag_fwd<", "k_fwd_gather": "k_fwd_gather", "k_fwd_sums": "k_fwd_sums",
-           "k_towers_bf16": "k_towers_bf16", "k_hash_insert": "k_hash_insert", "copy": "MulFunctor"}
+           "k_towers_bf16": "k_towers_bf16", "k_hash_insert": "k_hash_insert",
+           "k_bwd_keys": "k_bwd_keys", "k_sort_hist": "k_sort_hist", "k_sort_scan": "k_sort_scan",
+           "k_sort_scatter": "k_sort_scatter", "k_bwd_chunks": "k_bwd_chunks",
+           "k_bwd_cross": "k_bwd_cross", "k_dlrm_interact": "k_dlrm_interact", "copy": "MulFunctor"}
 
 
 def load_traffic(kernels, shash: str, config: str):
@@ -408,7 +415,7 @@ def main():
               file=sys.stderr, flush=True)
 
     adagrad = None
-    if not a.no_adagrad and not cfg.hash_keys:
+    if not a.no_adagrad:
         # The sparse half of a training step, beside the forward: gradients of
         # the pooled bags and of the sequence rows (random, as the dense
         # backward would deliver them) summed per row, then one AdaGrad step
@@ -418,7 +425,22 @@ def main():
         rows = [int(t["rows"]) for t in model.tables]
         aw = [torch.from_numpy(np.asarray(t["values"], np.float32)).to(dev) for t in model.tables]
         aa = [torch.zeros(r, 16, dtype=torch.float32, device=dev) for r in rows]
-        atabs = [R.adagrad_table(aw[t], aa[t], rows[t]) for t in range(T)]
+        akd = [(torch.from_numpy(t["keys"]).to(dev), torch.from_numpy(t["digests"]).to(dev))
+               if t["kind"] == "hash" else (None, None) for t in model.tables]
+        atabs = [R.adagrad_table(aw[t], aa[t], rows[t],
+                                 R.REC_HASH if akd[t][0] is not None else R.REC_DIRECT, *akd[t])
+                 for t in range(T)]
+
+        def flat_rows(t, raw):
+            tab = model.tables[t]
+            if tab["kind"] != "hash":
+                return np.mod(raw, rows[t]) + sum(rows[:t])
+            occ = np.nonzero(tab["keys"] != R.REC_EMPTY_KEY)[0]
+            order = np.argsort(tab["keys"][occ])
+            sk, ss = tab["keys"][occ][order], occ[order]
+            at = np.minimum(np.searchsorted(sk, raw), sk.size - 1)
+            hit = sk[at] == raw
+            return ss[at][hit] + sum(rows[:t])
         legs = []
         for b_, db in zip(batches, dbs):
             P_ = int(b_.seq_lengths.sum())
@@ -457,11 +479,10 @@ def main():
             starts = np.concatenate([[0], np.cumsum(b_.lengths.astype(np.int64))])
             keys = []
             for t in range(T):
-                keys.append(np.mod(b_.values[starts[t * B]: starts[(t + 1) * B]], rows[t])
-                            + sum(rows[:t]))
+                keys.append(flat_rows(t, b_.values[starts[t * B]: starts[(t + 1) * B]]))
             Pb = int(b_.seq_lengths.sum())
             for k, t in enumerate(st):
-                keys.append(np.mod(b_.seq_values[k, :Pb], rows[t]) + sum(rows[:t]))
+                keys.append(flat_rows(t, b_.seq_values[k, :Pb]))
             keys = np.concatenate(keys)
             reads.append(keys.size)
             touched.append(np.unique(keys).size)
@@ -469,6 +490,8 @@ def main():
         a_bytes = (n_reads * ADAGRAD_BYTES_PER_READ + T * B * ADAGRAD_BYTES_PER_BAG
                    + n_rows * ADAGRAD_BYTES_PER_ROW)
         a_us = float(d.mean())
+        total_rows = sum(rows)
+        passes = (int(total_rows).bit_length() + 7) // 8       # the sort covers 0 .. total_rows
         adagrad = {"entry": "rec_embbag_adagrad (row keys, radix sort, chunk sums + AdaGrad, "
                             "cross-chunk runs)",
                    "avg_call_us": round(a_us, 3), "median_call_us": round(float(np.median(d)), 3),
@@ -476,10 +499,53 @@ def main():
                    "algorithmic_bytes": a_bytes,
                    "algorithmic_gb_s": round(a_bytes / (a_us * 1e-6) / 1e9, 1),
                    "hbm_frac": round(a_bytes / (a_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                   "traffic": None}
+                   "traffic": load_traffic(["k_bwd_keys", "k_bwd_chunks", "k_bwd_cross"]
+                                           + ["k_sort_hist", "k_sort_scan", "k_sort_scatter"] * passes,
+                                           shash, cfg.name),
+                   "sort_passes": passes}
         print(f"[bench] backward + AdaGrad: {a_us:.2f} us per call ({n_reads:.0f} reads, "
               f"{n_rows:.0f} rows)", file=sys.stderr, flush=True)
-        del aw, aa, aws, legs
+        del aw, aa, akd, aws, legs
+
+    interaction = None
+    if not a.no_interaction:
+        # The DLRM interaction layer at the pages' measured shape (the DLRM
+        # essay §3.1: 217 vectors of width 96 per sample; 1.8 ms per forward on
+        # a V100 with the batch not given, context only), over 4096 samples.
+        Bi, Fi, di = 4096, 217, 96
+        npairs = Fi * (Fi + 1) // 2
+        zi = torch.randn(Bi, Fi, di, dtype=torch.float32, device=dev)
+        oi = torch.empty(Bi, npairs, dtype=torch.float32, device=dev)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                R.rec_dlrm_interact(zi, Bi, Fi, di, oi, stream=stream)
+            torch.cuda.synchronize()
+            reps_i = 20
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps_i)]
+            torch.cuda._sleep(20_000_000)
+            for r in range(reps_i):
+                evs[r][0].record(stream)
+                R.rec_dlrm_interact(zi, Bi, Fi, di, oi, stream=stream)
+                evs[r][1].record(stream)
+            torch.cuda.synchronize()
+        d = np.array([s_.elapsed_time(e_) * 1e3 for s_, e_ in evs])
+        i_us = float(d.mean())
+        i_flops = 2.0 * di * npairs * Bi
+        i_bytes = 4.0 * (Fi * di + npairs) * Bi
+        interaction = {"entry": "rec_dlrm_interact (upper triangle with the diagonal of Z Z^T)",
+                       "samples": Bi, "vectors": Fi, "width": di, "avg_call_us": round(i_us, 3),
+                       "us_per_sample": round(i_us / Bi, 4),
+                       "achieved_tflops": round(i_flops / (i_us * 1e-6) / 1e12, 2),
+                       "fp32_peak_tflops": FP32_PEAK_TFLOPS,
+                       "mfma_frac": round(i_flops / (i_us * 1e-6) / 1e12 / FP32_PEAK_TFLOPS, 4),
+                       "algorithmic_gb_s": round(i_bytes / (i_us * 1e-6) / 1e9, 1),
+                       "hbm_frac": round(i_bytes / (i_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                       "traffic": load_traffic(["k_dlrm_interact"], shash, cfg.name),
+                       "pages": "1.8 ms per forward on a V100, batch not given (context, another machine)"}
+        print(f"[bench] DLRM interaction: {i_us:.1f} us for {Bi} samples of {Fi} x {di}",
+              file=sys.stderr, flush=True)
+        del zi, oi
 
     cpu = None
     if not a.no_cpu:
@@ -527,6 +593,7 @@ def main():
         "towers": towers,
         "hash_rebuild": rebuild,
         "adagrad": adagrad,
+        "dlrm_interaction": interaction,
         "src_hash": shash,
     }
     if a.calibrate_copy:

@@ -472,17 +472,26 @@ rec_status rec_tower_pack_mlp(const rec_tower_mlp* mlp, void* packed, size_t pac
                               void* stream);
 
 /*
- * One direct table as the sparse AdaGrad step sees it (host struct; both
- * arrays are device memory, updated in place).
- *   weights  fp32 [rows][16], 16-byte aligned (the table rec_embbag_fwd reads)
+ * One table as the sparse AdaGrad step sees it (host struct; the arrays are
+ * device memory; weights and accum are updated in place).
+ *   weights  fp32 [rows][16], 16-byte aligned: the table rec_embbag_fwd reads
+ *            (REC_HASH: the slot values)
  *   accum    fp32 [rows][16], 16-byte aligned: AdaGrad's running sum of
  *            squared gradients, one value per weight (0 before the first step)
- *   rows     num_buckets, the floor-mod divisor, >= 1
+ *   rows     REC_DIRECT: num_buckets, the floor-mod divisor; REC_HASH: the
+ *            capacity
+ *   kind     REC_DIRECT or REC_HASH;  keys, digests: REC_HASH only, laid out
+ *            and aligned as in rec_table (a read of a key no slot holds is a
+ *            miss, which read the zero vector and takes no gradient)
  */
 typedef struct {
     float* weights;
     float* accum;
     int64_t rows;
+    int32_t kind;
+    int32_t reserved;
+    const int64_t* keys;
+    const uint8_t* digests;
 } rec_adagrad_table;
 
 /* Bytes of workspace rec_embbag_adagrad needs for T tables, B samples, nnz
@@ -501,20 +510,21 @@ size_t rec_embbag_adagrad_workspace_bytes(int32_t T, int64_t B, int64_t nnz, int
  * Gradient of each row: the sum, over every read of that row in the batch, of
  * the read's output gradient:
  *   - id i of bag (t, b) (the KJT of rec_embbag_fwd: key-major, bag t*B + b
- *     holds values[offsets[t*B+b] .. + lengths[t*B+b])) reads row
- *     floor_mod(values[i], tables[t].rows) of table t, with output gradient
+ *     holds values[offsets[t*B+b] .. + lengths[t*B+b])) reads the row of
+ *     values[i] in table t (REC_DIRECT: floor_mod(values[i], rows); REC_HASH:
+ *     the slot holding it, none on a miss), with output gradient
  *     grad_pooled[b][16t .. 16t+16);
- *   - packed sequence position j < P of sub-feature k (0..2) reads row
- *     floor_mod(seq_values[k*seq_stride + j], rows) of table seq_table[k], with
- *     output gradient grad_seq[k][j][0..16).
+ *   - packed sequence position j < P of sub-feature k (0..2) reads the row of
+ *     seq_values[k*seq_stride + j] in table seq_table[k], with output gradient
+ *     grad_seq[k][j][0..16).
  * Every row read at least once then takes, element by element, with its
  * summed gradient g:  accum += g*g;  weights -= lr * g / (sqrt(accum) + eps)
  * (fp32).  Rows not read are not touched.  A repeated id counts once per
  * repetition.  The sums run in a fixed order (reads sorted by row with a
  * stable radix sort, no atomics), so results are bit-identical run to run.
  *
- *   tables      host array of T rec_adagrad_table (T <= REC_MAX_TABLES);
- *               direct tables only, sum of rows < 2^32
+ *   tables      host array of T rec_adagrad_table (T <= REC_MAX_TABLES),
+ *               direct or hash; rows summing to less than 2^32 - 1
  *   values      int64[nnz] raw ids; lengths int32[T*B]; offsets int64[T*B]:
  *               the exclusive scan of lengths, with offsets[T*B-1] +
  *               lengths[T*B-1] == nnz (precondition, not checked)
@@ -527,9 +537,10 @@ size_t rec_embbag_adagrad_workspace_bytes(int32_t T, int64_t B, int64_t nnz, int
  *               device memory, 256-byte aligned; contents on entry ignored
  * The tables must not overlap one another or the inputs.
  * Errors: REC_EINVAL (null or misaligned pointers, T < 1, B < 0, nnz < 0,
- * P < 0, rows < 1, a seq_table entry outside [0, T)), REC_EUNSUPPORTED
- * (T > REC_MAX_TABLES, rows summing to 2^32 or more, nnz + 3P or B*T + 3P at
- * 2^31 or more), REC_EWORKSPACE.  nnz + P == 0 is a no-op.
+ * P < 0, rows < 1, unknown kind, a hash table without keys or digests, a
+ * seq_table entry outside [0, T)), REC_EUNSUPPORTED (T > REC_MAX_TABLES, rows
+ * summing to 2^32 - 1 or more, nnz + 3P or B*T + 3P at 2^31 or more),
+ * REC_EWORKSPACE.  nnz + P == 0 is a no-op.
  */
 rec_status rec_embbag_adagrad(const rec_adagrad_table* tables, int32_t T, int64_t B,
                               const int64_t* values, const int32_t* lengths,

@@ -648,17 +648,27 @@ rec_status rec_embbag_adagrad(const rec_adagrad_table* tables, int32_t T, int64_
     uint64_t total = 0;
     for (int t = 0; t < T; ++t) {
         const rec_adagrad_table& a = tables[t];
-        if (a.rows < 1) return fail(REC_EINVAL, f + ": table rows must be >= 1");
         if (!a.weights || !a.accum) return fail(REC_EINVAL, f + ": table weights or accum is NULL");
         if (!aligned16(a.weights) || !aligned16(a.accum))
             return fail(REC_EINVAL, f + ": table weights and accum must be 16-byte aligned");
+        rec_table rt;
+        memset(&rt, 0, sizeof(rt));
+        rt.kind = a.kind;
+        rt.dim = REC_DIM;
+        rt.rows = a.rows;
+        rt.values = a.weights;
+        rt.keys = a.keys;
+        rt.digests = a.digests;
+        rec_status st = prep_table(rt, (f + ": table").c_str(), &tabs[t].tab);
+        if (st != REC_OK) return st;
         tabs[t].weights = a.weights;
         tabs[t].accum = a.accum;
         tabs[t].rows = a.rows;
-        floor_mod_prepare(a.rows, &tabs[t].magic, &tabs[t].shift);
         tabs[t].base = (uint32_t)total;
+        tabs[t].pad_ = 0;
         total += (uint64_t)a.rows;
-        if (total >= ((uint64_t)1 << 32)) return fail(REC_EUNSUPPORTED, f + ": table rows sum to 2^32 or more");
+        if (total >= ((uint64_t)1 << 32) - 1)
+            return fail(REC_EUNSUPPORTED, f + ": table rows sum to 2^32 - 1 or more");
     }
     if (nnz > 0 && (!values || !lengths || !offsets || !grad_pooled))
         return fail(REC_EINVAL, f + ": values, lengths, offsets and grad_pooled are required when nnz > 0");
@@ -701,8 +711,9 @@ rec_status rec_embbag_adagrad(const rec_adagrad_table* tables, int32_t T, int64_
     a.src_in = (uint32_t*)(w + L.src_in);
     a.hpart = (float*)(w + L.hpart);
     a.tpart = (float*)(w + L.tpart);
+    // the sort covers every key up to `total` itself (a hash miss's key)
     int bits = 1;
-    while (bits < 32 && ((uint64_t)1 << bits) < total) ++bits;
+    while (bits < 32 && ((uint64_t)1 << bits) <= total) ++bits;
     return hip_status(launch_embbag_adagrad(a, tabs, (uint32_t*)(w + L.keys_out), (uint32_t*)(w + L.src_out),
                                             (uint32_t*)(w + L.hist), (uint32_t*)(w + L.tot), bits,
                                             (hipStream_t)stream),

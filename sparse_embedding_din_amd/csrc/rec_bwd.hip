@@ -64,6 +64,18 @@ __device__ inline int table_of(const uint32_t* base, int T, uint32_t key) {
     return lo;
 }
 
+// Flat row key of raw id x in table tb: direct, base + floor_mod(x, rows);
+// hash, base + the slot holding x, or `miss` (the total row count, which
+// sorts after every row and is skipped) when no slot holds it -- a miss read
+// the constant zero vector and takes no gradient.
+__device__ inline uint32_t row_key(const BwdTab& tb, int64_t x, uint32_t miss) {
+    if (tb.tab.kind == REC_HASH) {
+        const int64_t slot = hash_probe(tb.tab, x);
+        return slot < 0 ? miss : tb.base + (uint32_t)slot;
+    }
+    return tb.base + (uint32_t)floor_mod_magic(x, tb.tab.rows, tb.tab.magic, tb.tab.shift);
+}
+
 // ---------------------------------------------------------------------------
 // 1. keys and sources.  Blocks of 256 threads; block x covers 4 x 64 bags of
 // one table (x < T * bag_blocks) or 4 x 64 positions of one sub-feature.
@@ -82,8 +94,7 @@ __global__ __launch_bounds__(256) void k_bwd_keys(BwdArgs a, BwdTabArr tabs) {
         const int32_t len = a.lengths[bag];
         const uint32_t src = (uint32_t)(b * a.T + t);
         for (int32_t i = 0; i < len && off + i < a.nnz; ++i) {
-            const int64_t r = floor_mod_magic(a.values[off + i], tb.rows, tb.magic, tb.shift);
-            a.keys_in[off + i] = tb.base + (uint32_t)r;
+            a.keys_in[off + i] = row_key(tb, a.values[off + i], a.total_rows);
             a.src_in[off + i] = src;
         }
         return;
@@ -95,9 +106,8 @@ __global__ __launch_bounds__(256) void k_bwd_keys(BwdArgs a, BwdTabArr tabs) {
     const int64_t j = (y - (int64_t)k * pos_blocks) * 256 + wv * 64 + lane;
     if (j >= a.P) return;
     const BwdTab tb = tabs.t[a.seq_table[k]];
-    const int64_t r = floor_mod_magic(a.seq_values[k * a.seq_stride + j], tb.rows, tb.magic, tb.shift);
     const int64_t c = a.nnz + k * a.P + j;
-    a.keys_in[c] = tb.base + (uint32_t)r;
+    a.keys_in[c] = row_key(tb, a.seq_values[k * a.seq_stride + j], a.total_rows);
     a.src_in[c] = (uint32_t)(a.B * a.T + k * a.P + j);
 }
 

@@ -328,15 +328,16 @@ constexpr int kDlrmMaxLdsFloats = 36864;
 int dlrm_stride(int d);
 hipError_t launch_dlrm_interact(const float* z, int64_t B, int F, int d, float* out, int num_cus,
                                 hipStream_t s);
-// Sparse backward + AdaGrad (rec_bwd.hip).  One table: its arrays, its
-// floor-mod constants and its first row in the flat row space of all tables.
+// Sparse backward + AdaGrad (rec_bwd.hip).  One table: its lookup
+// descriptor (direct floor-mod constants or hash keys/digests), the arrays
+// the step writes, and its first row in the flat row space of all tables.
 struct BwdTab {
+    TabDev tab;
     float* weights;
     float* accum;
     int64_t rows;
-    uint64_t magic;
-    int32_t shift;
     uint32_t base;
+    int32_t pad_;
 };
 
 struct BwdArgs {

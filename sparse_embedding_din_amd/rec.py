@@ -63,7 +63,9 @@ class rec_tower_mlp(C.Structure):
 
 
 class rec_adagrad_table(C.Structure):
-    _fields_ = [("weights", C.c_void_p), ("accum", C.c_void_p), ("rows", C.c_int64)]
+    _fields_ = [("weights", C.c_void_p), ("accum", C.c_void_p), ("rows", C.c_int64),
+                ("kind", C.c_int32), ("reserved", C.c_int32), ("keys", C.c_void_p),
+                ("digests", C.c_void_p)]
 
 
 class rec_fwd_args(C.Structure):
@@ -187,9 +189,10 @@ def _tables(tabs):
     return arr
 
 
-def adagrad_table(weights, accum, rows: int) -> rec_adagrad_table:
+def adagrad_table(weights, accum, rows: int, kind: int = REC_DIRECT, keys=None,
+                  digests=None) -> rec_adagrad_table:
     """A host rec_adagrad_table over device tensors (kept alive by the caller)."""
-    return rec_adagrad_table(_p(weights), _p(accum), rows)
+    return rec_adagrad_table(_p(weights), _p(accum), rows, kind, 0, _p(keys), _p(digests))
 
 
 # -- entry points (same names and arguments as include/rec.h) ----------------

@@ -492,6 +492,15 @@ def test_embbag_adagrad_errors(lib):
     assert call(t=tabs(rows=0))[0] == R.REC_EINVAL
     assert call(t=tabs(w=None))[0] == R.REC_EINVAL
     assert call(t=tabs(g=FAKE_ODD))[0] == R.REC_EINVAL
+    bad_kind = tabs()
+    bad_kind[1].kind = 7
+    assert call(t=bad_kind)[0] == R.REC_EINVAL
+    no_keys = tabs()
+    no_keys[0].kind, no_keys[0].digests = R.REC_HASH, FAKE
+    assert call(t=no_keys)[0] == R.REC_EINVAL
+    odd_dig = tabs()
+    odd_dig[0].kind, odd_dig[0].keys, odd_dig[0].digests = R.REC_HASH, FAKE, FAKE + 4
+    assert call(t=odd_dig)[0] == R.REC_EINVAL
     s, msg = call(t=tabs(rows=1 << 31))
     assert s == R.REC_EUNSUPPORTED and "2^32" in msg
     assert call(gp=None)[0] == R.REC_EINVAL

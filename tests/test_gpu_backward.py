@@ -29,13 +29,27 @@ pytestmark = pytest.mark.gpu
 SEQ_TABLE = np.array(synth.SEQ_KEYS, np.int32)
 
 
-def _gpu_step(rows, B, values, lengths, offsets, dp, weights, accums, lr, eps, seq):
-    """Run rec_embbag_adagrad on copies of weights/accums; returns the new
-    (weights, accums) as numpy fp32 lists."""
-    T = len(rows)
+def _rows(t):
+    return int(t) if isinstance(t, (int, np.integer)) else int(t["rows"])
+
+
+def _gpu_step(tables, B, values, lengths, offsets, dp, weights, accums, lr, eps, seq):
+    """Run rec_embbag_adagrad on copies of weights/accums; `tables` holds row
+    counts (direct tables) or generator table dicts (direct or hash).  Returns
+    the new (weights, accums) as numpy fp32 lists."""
+    T = len(tables)
     tw = [torch.from_numpy(np.ascontiguousarray(w, np.float32)).to(DEV) for w in weights]
     ta = [torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(DEV) for a in accums]
-    tabs = [R.adagrad_table(tw[t], ta[t], int(rows[t])) for t in range(T)]
+    keep, tabs = [], []
+    for t in range(T):
+        tb = tables[t]
+        if isinstance(tb, dict) and tb["kind"] == "hash":
+            k = torch.from_numpy(tb["keys"]).to(DEV)
+            d = torch.from_numpy(tb["digests"]).to(DEV)
+            keep += [k, d]
+            tabs.append(R.adagrad_table(tw[t], ta[t], _rows(tb), R.REC_HASH, k, d))
+        else:
+            tabs.append(R.adagrad_table(tw[t], ta[t], _rows(tb)))
     nnz = int(values.size)
     v = torch.from_numpy(np.ascontiguousarray(values, np.int64)).to(DEV)
     ln = torch.from_numpy(np.ascontiguousarray(lengths, np.int32)).to(DEV)
@@ -65,6 +79,7 @@ def _check(rows, B, values, lengths, offsets, dp, weights, accums, lr, eps, seq,
         m = touched[t]
         w0 = np.asarray(weights[t], np.float32)
         a0 = np.asarray(accums[t], np.float32)
+        # bit for bit, so the NaN of an empty hash slot must stay that NaN
         assert np.array_equal(gw[t][~m].view(np.uint32), w0[~m].view(np.uint32)), (tag, t)
         assert np.array_equal(ga[t][~m].view(np.uint32), a0[~m].view(np.uint32)), (tag, t)
         if not m.any():
@@ -81,15 +96,15 @@ def _offsets(lengths):
     return np.concatenate([[0], np.cumsum(lengths.astype(np.int64))]).astype(np.int64)
 
 
-def _model_case(cfg_i, B, seed, with_seq=True):
-    m = synth.make_model(synth.CONFIGS[cfg_i])
+def _model_case(cfg_i, B, seed, with_seq=True, cfg=None):
+    m = synth.make_model(cfg or synth.CONFIGS[cfg_i])
     b = synth.make_batch(m, B=B)
     rng = np.random.default_rng(seed)
     dp = rng.standard_normal((b.B, 256)).astype(np.float32)
     P = int(b.seq_lengths.sum())
     seq = (SEQ_TABLE, b.seq_values, rng.standard_normal((3, P, 16)).astype(np.float32)) \
         if with_seq else None
-    rows = [int(t["rows"]) for t in m.tables]
+    rows = list(m.tables)
     weights = [np.asarray(t["values"], np.float32) for t in m.tables]
     return m, b, dp, seq, rows, weights
 
@@ -98,11 +113,11 @@ def _model_case(cfg_i, B, seed, with_seq=True):
 def test_adagrad_tiny(with_seq):
     say(f"adagrad tiny B=256 seq={with_seq}")
     m, b, dp, seq, rows, weights = _model_case(1, 256, 5, with_seq)
-    zero = [np.zeros((r, 16), np.float32) for r in rows]
+    zero = [np.zeros((_rows(r), 16), np.float32) for r in rows]
     _check(rows, b.B, b.values, b.lengths, _offsets(b.lengths)[:-1], dp, weights, zero, 1e-3,
            1e-10, seq, "zero accumulator")
     rng = np.random.default_rng(6)
-    acc = [rng.uniform(0.0, 2.0, (r, 16)).astype(np.float32) for r in rows]
+    acc = [rng.uniform(0.0, 2.0, (_rows(r), 16)).astype(np.float32) for r in rows]
     _check(rows, b.B, b.values, b.lengths, _offsets(b.lengths)[:-1], dp, weights, acc, 0.05,
            1e-10, seq, "random accumulator, lr 0.05")
 
@@ -110,7 +125,7 @@ def test_adagrad_tiny(with_seq):
 def test_adagrad_deterministic():
     say("adagrad determinism B=1024")
     m, b, dp, seq, rows, weights = _model_case(1, 1024, 8)
-    acc = [np.zeros((r, 16), np.float32) for r in rows]
+    acc = [np.zeros((_rows(r), 16), np.float32) for r in rows]
     args = (rows, b.B, b.values, b.lengths, _offsets(b.lengths)[:-1], dp, weights, acc, 1e-3,
             1e-10, seq)
     w1, a1 = _gpu_step(*args)
@@ -167,6 +182,23 @@ def test_adagrad_sequence_only_and_bags_only():
 def test_adagrad_full_size(cfg_i, B):
     say(f"adagrad full size cfg={synth.CONFIGS[cfg_i].name} B={B}")
     m, b, dp, seq, rows, weights = _model_case(cfg_i, B, 20 + cfg_i)
-    zero = [np.zeros((r, 16), np.float32) for r in rows]
+    zero = [np.zeros((_rows(r), 16), np.float32) for r in rows]
     _check(rows, b.B, b.values, b.lengths, _offsets(b.lengths)[:-1], dp, weights, zero, 1e-3,
            1e-10, seq, f"{synth.CONFIGS[cfg_i].name}")
+
+
+HASH_TINY = synth.Config(91, "hash_tiny", 64, tuple(synth.TINY_SIZES), "u123", "geom4", "f32",
+                         hash_keys=(0, 1, 2, 3, 4), hash_capacity=3000)
+
+
+@pytest.mark.parametrize("cfg_i,B", [(0, 300), (5, 8192)])
+def test_adagrad_hash(cfg_i, B):
+    """Hash tables ("集成 DynamicEmb" §3.2): a hit updates its slot, a miss
+    (which read the zero vector) updates nothing, and empty slots keep their
+    NaN bits."""
+    cfg = HASH_TINY if cfg_i == 0 else synth.CONFIGS[cfg_i]
+    say(f"adagrad hash cfg={cfg.name} B={B}")
+    m, b, dp, seq, rows, weights = _model_case(cfg_i, B, 40 + cfg_i, cfg=cfg)
+    zero = [np.zeros((_rows(r), 16), np.float32) for r in rows]
+    _check(rows, b.B, b.values, b.lengths, _offsets(b.lengths)[:-1], dp, weights, zero, 1e-3,
+           1e-10, seq, cfg.name)
