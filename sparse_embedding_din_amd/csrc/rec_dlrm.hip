@@ -13,7 +13,7 @@
 // sample, persistent over samples: Z is staged in LDS once, rows padded to a
 // multiple of 16 with zeros, with a row stride that puts the 16 rows of an
 // operand read on distinct banks; the T(T+1)/2 tile pairs I <= J of the
-// T = ceil(F / 16) row tiles are dealt to the four waves in turn.  Both
+// T = ceil(F / 16) row tiles are dealt to the eight waves in turn.  Both
 // operands want row m of their tile in lane (m, g) at lane group g's K
 // positions; giving lane group g the contiguous quarter [g d/4, (g+1) d/4) of
 // d (any K order is right when both operands use it) lets a lane read four K
@@ -25,7 +25,9 @@
 namespace rec {
 namespace {
 
-constexpr int kDlrmWaves = 4;
+constexpr int kDlrmWaves = 8;                  // two per SIMD: one wave's LDS waits hide behind the other's products
+// float4s per thread that hold a whole staged Z (the LDS stage's size)
+constexpr int kDlrmPrefetch = kDlrmMaxLdsFloats / (4 * 64 * kDlrmWaves);
 
 __global__ __launch_bounds__(64 * kDlrmWaves) void k_dlrm_interact(const float* __restrict__ z, int64_t B,
                                                                    int F, int d, int stride,
@@ -38,14 +40,30 @@ __global__ __launch_bounds__(64 * kDlrmWaves) void k_dlrm_interact(const float* 
     const int nv = d / 4;                       // float4s per row
     const int64_t npairs = (int64_t)F * (F + 1) / 2;
     const int ntile = T * (T + 1) / 2;
+    // Z of the next sample travels in registers while the current one is
+    // multiplied: thread t holds float4 t + q*256 of it (zeros past row F)
+    const int nvec = 16 * T * nv;
+    float4 pre[kDlrmPrefetch];
+    auto fetch = [&](int64_t bs) {
+        const float4* src = (const float4*)(z + bs * (int64_t)F * d);
+#pragma unroll
+        for (int q = 0; q < kDlrmPrefetch; ++q) {
+            const int v = threadIdx.x + q * 64 * kDlrmWaves;
+            pre[q] = (v < nvec && v / nv < F) ? src[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    if ((int64_t)blockIdx.x < B) fetch(blockIdx.x);
     for (int64_t b = blockIdx.x; b < B; b += gridDim.x) {
-        const float4* src = (const float4*)(z + b * (int64_t)F * d);
-        for (int v = threadIdx.x; v < 16 * T * nv; v += 64 * kDlrmWaves) {
-            const int r = v / nv, c = v - r * nv;
-            const float4 x = r < F ? src[v] : make_float4(0.f, 0.f, 0.f, 0.f);
-            *(float4*)(s_z + r * stride + 4 * c) = x;
+#pragma unroll
+        for (int q = 0; q < kDlrmPrefetch; ++q) {
+            const int v = threadIdx.x + q * 64 * kDlrmWaves;
+            if (v < nvec) {
+                const int r = v / nv, c = v - r * nv;
+                *(float4*)(s_z + r * stride + 4 * c) = pre[q];
+            }
         }
         __syncthreads();
+        if (b + gridDim.x < B) fetch(b + gridDim.x);
         for (int t = wave; t < ntile; t += kDlrmWaves) {
             int I = 0, rem = t;                     // tile pair t, row by row
             while (rem >= T - I) {
@@ -58,13 +76,19 @@ __global__ __launch_bounds__(64 * kDlrmWaves) void k_dlrm_interact(const float* 
             f32x4 acc[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // the next K step's operands are read before this step's products
+            float4 av = *(const float4*)ra;
+            float4 bv = *(const float4*)rb;
             for (int k = 0; k < dq; k += 4) {
-                const float4 av = *(const float4*)(ra + k);
-                const float4 bv = *(const float4*)(rb + k);
+                const int kn = k + 4 < dq ? k + 4 : k;
+                const float4 an = *(const float4*)(ra + kn);
+                const float4 bn = *(const float4*)(rb + kn);
                 acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc[0], 0, 0, 0);
                 acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc[1], 0, 0, 0);
                 acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc[2], 0, 0, 0);
                 acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc[3], 0, 0, 0);
+                av = an;
+                bv = bn;
             }
             const f32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
             // lane (m, g) holds rows 4g..4g+3 of the tile in column m
