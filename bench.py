@@ -86,12 +86,17 @@ def parse():
     return p.parse_args()
 
 
-def src_hash() -> str:
-    """Hash of the kernel sources with comments and blank space removed:
-    stored traffic figures stay valid across edits of the comments only
-    (the sources hold no string literal with a comment marker in it)."""
+def src_hash(files=None) -> str:
+    """Hash of kernel sources (all of csrc/, or the named files in it) with
+    comments and blank space removed: stored traffic figures stay valid across
+    edits of the comments only (the sources hold no string literal with a
+    comment marker in it)."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "sparse_embedding_din_amd", "csrc", "*"))):
+    if files is None:
+        paths = sorted(glob.glob(os.path.join(ROOT, "sparse_embedding_din_amd", "csrc", "*")))
+    else:
+        paths = [os.path.join(ROOT, "sparse_embedding_din_amd", "csrc", f) for f in sorted(files)]
+    for f in paths:
         with open(f, encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -99,6 +104,21 @@ def src_hash() -> str:
         code = "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
         h.update(os.path.basename(f).encode() + b"\0" + code.encode() + b"\0")
     return h.hexdigest()[:16]
+
+
+# The sources each kernel's traffic depends on: its own file, the headers it
+# includes and the host side that sizes its launch.  A stored figure is used
+# only while these are unchanged.
+_COMMON = ["rec_internal.h", "rec_abi.hip"]
+_FWD = ["rec_din.hip", "rec_fwd.hip", "rec_embbag.hip", "rec_embbag_dev.h", "rec_scan.hip",
+        "rec_scan_dev.h", "rec_mfma.h"] + _COMMON
+_BWD = ["rec_bwd.hip"] + _COMMON
+KERNEL_SOURCES = {"k_din_attn": _FWD, "k_embbag_fwd": _FWD, "k_fwd_gather": _FWD, "k_fwd_sums": _FWD,
+                  "k_towers_bf16": ["rec_tower.hip", "rec_mfma.h"] + _COMMON,
+                  "k_hash_insert": ["rec_hash.hip"] + _COMMON,
+                  "k_bwd_keys": _BWD, "k_sort_hist": _BWD, "k_sort_scan": _BWD, "k_sort_scatter": _BWD,
+                  "k_bwd_chunks": _BWD, "k_bwd_cross": _BWD,
+                  "k_dlrm_interact": ["rec_dlrm.hip", "rec_mfma.h"] + _COMMON}
 
 
 CAL_BYTES = 64 << 20            # bytes read (and written) by the calibration copy
@@ -121,7 +141,7 @@ def load_traffic(kernels, shash: str, config: str):
             return None
         with open(path) as f:
             d = json.load(f)
-        if d.get("src_hash") != shash:
+        if d.get("src_hash") != src_hash(KERNEL_SOURCES[k]):
             return None
         tot += d["bytes_per_launch"]
     return tot
@@ -149,12 +169,13 @@ def traffic_from(fetch_csv: str, write_csv: str, config: str):
     write, nw = per_kernel(write_csv, "WRITE_SIZE")
     f_cal = fetch["copy"] * 1024.0 / CAL_BYTES
     w_cal = write["copy"] * 1024.0 / CAL_BYTES
-    shash = src_hash()
+    only = set(os.environ.get("TRAFFIC_KERNELS", "").split(",")) - {""}
     for k in KERNELS:
-        if k == "copy" or k not in fetch or k not in write:
+        if k == "copy" or k not in fetch or k not in write or (only and k not in only):
             continue
         b = fetch[k] * 1024.0 / f_cal + write[k] * 1024.0 / w_cal
-        d = {"kernel": k, "config": config, "src_hash": shash, "bytes_per_launch": b,
+        d = {"kernel": k, "config": config, "src_hash": src_hash(KERNEL_SOURCES[k]),
+             "sources": KERNEL_SOURCES[k], "bytes_per_launch": b,
              "fetch_kib_raw": fetch[k], "write_kib_raw": write[k], "dispatches": [nf[k], nw[k]],
              "copy_scale": {"fetch": f_cal, "write": w_cal, "bytes": CAL_BYTES}}
         with open(os.path.join(ROOT, "profiles", f"traffic_{k}_{config}.json"), "w") as f:
