@@ -84,6 +84,10 @@ class Oracle:
                                          C.c_int64, P32, P64, C.c_int64, PF, C.c_double,
                                          C.c_double, PD, PD, PD, P8]
         L.orc_embbag_adagrad.restype = C.c_int64
+        L.orc_din_bwd.argtypes = [C.POINTER(OrcTable), P64, C.c_int64, P64, P32, C.c_int32,
+                                  C.c_int64, PD, PD, PD, PD, PD, PD, C.c_double, PD, PD, PD,
+                                  PD, PD, PD, PD, PD, PD]
+        L.orc_din_bwd.restype = None
         self._keep = []
 
     # -- bookkeeping ---------------------------------------------------------
@@ -180,6 +184,32 @@ class Oracle:
         assert outside == 0, f"{outside} reads resolved to a row outside their table"
         cut = lambda a: [a[base[t]: base[t] + rows[t]] for t in range(T)]  # noqa: E731
         return cut(w), cut(G), cut(grad), cut(touched.astype(bool))
+
+    def din_bwd(self, seq_tabs, seq_values, seq_stride, seq_offsets, seq_lengths, max_len, query,
+                w1, b1, w2, b2, w3, b3, gatt, wrapped=None):
+        """Backward of the DIN attention for all B samples given the gradient
+        of its output gatt [B][48].  Returns a dict of fp64 arrays: gq [B][48],
+        gs [seq_stride][48] (by position index), dw1 [256][192], db1 [256],
+        dw2 [64][256], db2 [64], dw3 [64], db3 (a float)."""
+        seq_values = np.ascontiguousarray(seq_values, dtype=np.int64)
+        seq_offsets = np.ascontiguousarray(seq_offsets, dtype=np.int64)
+        seq_lengths = np.ascontiguousarray(seq_lengths, dtype=np.int32)
+        B = seq_lengths.size
+        q = np.ascontiguousarray(query, dtype=np.float64).reshape(B, 48)
+        g = np.ascontiguousarray(gatt, dtype=np.float64).reshape(B, 48)
+        d = [np.ascontiguousarray(a, dtype=np.float64) for a in (w1, b1, w2, b2, w3)]
+        assert d[0].shape == (256, 192) and d[2].shape == (64, 256)
+        arr = wrapped if wrapped is not None else self.tables(seq_tabs)
+        out = dict(gq=np.empty((B, 48)), gs=np.empty((int(seq_stride), 48)),
+                   dw1=np.zeros((256, 192)), db1=np.zeros(256), dw2=np.zeros((64, 256)),
+                   db2=np.zeros(64), dw3=np.zeros(64), db3=np.zeros(1))
+        self.lib.orc_din_bwd(arr, _ptr(seq_values, P64), int(seq_stride), _ptr(seq_offsets, P64),
+                             _ptr(seq_lengths, P32), int(max_len), B, _ptr(q, PD),
+                             *[_ptr(x, PD) for x in d], float(b3), _ptr(g, PD),
+                             *[_ptr(out[k], PD) for k in ("gq", "gs", "dw1", "db1", "dw2", "db2",
+                                                          "dw3", "db3")])
+        out["db3"] = float(out["db3"][0])
+        return out
 
     # -- DLRM interaction --------------------------------------------------------
     def dlrm_interact(self, z: np.ndarray, want_scale: bool = False):

@@ -410,6 +410,129 @@ void orc_din(const orc_table* seq_tables /* 3: adgroup, cate, brand */,
     free(e);
 }
 
+/* ---- DIN attention backward (the training step of [P1]'s run-config table
+ * through the attention of [P1] §4.2 / §4.4) --------------------------------
+ * For every sample b with L = min(seq_lengths[b], max_len) positions and the
+ * gradient g = gatt[b] (48) of its attention output, the forward is
+ * recomputed (s_j, x_j = [q, s_j, q - s_j, q * s_j], z1_j = W1 x_j + b1,
+ * h1_j = relu(z1_j), z2_j = W2 h1_j + b2, h2_j = relu(z2_j),
+ * e_j = w3 . h2_j + b3, p_j = softmax(e)_j) and differentiated by the chain
+ * rule, in the order of that forward read backwards:
+ *   att = sum_j p_j s_j:      dp_j = g . s_j,   ds_j = p_j g
+ *   softmax:                  de_j = p_j (dp_j - sum_k p_k dp_k)
+ *   e_j = w3 . h2_j + b3:     dw3 += de_j h2_j,  db3 += de_j,  dh2_j = de_j w3
+ *   h2_j = relu(z2_j):        dz2_j = dh2_j where z2_j > 0, else 0
+ *   z2_j = W2 h1_j + b2:      dW2 += dz2_j h1_j^T,  db2 += dz2_j,  dh1_j = W2^T dz2_j
+ *   h1_j = relu(z1_j):        dz1_j = dh1_j where z1_j > 0, else 0
+ *   z1_j = W1 x_j + b1:       dW1 += dz1_j x_j^T,  db1 += dz1_j,  dx_j = W1^T dz1_j
+ *   x_j = [q, s, q-s, q*s]:   dq += dx[0:48] + dx[96:144] + s_j * dx[144:192]
+ *                             ds_j += dx[48:96] - dx[96:144] + q * dx[144:192]
+ * A sample with no positions has att = 0 for every q: it contributes nothing.
+ * gq [B][48]; gs [seq_stride][48] by position index seq_offsets[b] + j (zero
+ * for positions past max_len); the weight gradients are sums over all
+ * samples and positions (they must be zero on entry).  Returns nothing. */
+void orc_din_bwd(const orc_table* seq_tables, const int64_t* seq_values, int64_t seq_stride,
+                 const int64_t* seq_offsets, const int32_t* seq_lengths, int32_t max_len,
+                 int64_t B, const double* query, const double* w1, const double* b1,
+                 const double* w2, const double* b2, const double* w3, double b3,
+                 const double* gatt, double* gq, double* gs, double* dw1, double* db1,
+                 double* dw2, double* db2, double* dw3, double* db3) {
+    const int64_t ml = max_len > 0 ? max_len : 1;
+    double* sj = (double*)malloc(sizeof(double) * 48 * (size_t)ml);
+    double* xs = (double*)malloc(sizeof(double) * 192 * (size_t)ml);
+    double* z1 = (double*)malloc(sizeof(double) * 256 * (size_t)ml);
+    double* z2 = (double*)malloc(sizeof(double) * 64 * (size_t)ml);
+    double* e = (double*)malloc(sizeof(double) * (size_t)ml);
+    double* p = (double*)malloc(sizeof(double) * (size_t)ml);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)ml);
+    for (int64_t i = 0; i < seq_stride * 48; ++i) gs[i] = 0.0;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t L = seq_lengths[b] < max_len ? seq_lengths[b] : max_len;
+        const double* q = query + b * 48;
+        const double* g = gatt + b * 48;
+        for (int c = 0; c < 48; ++c) gq[b * 48 + c] = 0.0;
+        if (L <= 0) continue;
+        /* forward, kept per position */
+        for (int64_t j = 0; j < L; ++j) {
+            for (int f = 0; f < 3; ++f)
+                orc_emb(&seq_tables[f], seq_values[f * seq_stride + seq_offsets[b] + j],
+                        sj + j * 48 + f * 16);
+            double* x = xs + j * 192;
+            for (int c = 0; c < 48; ++c) {
+                const double qc = q[c], sc = sj[j * 48 + c];
+                x[c] = qc;
+                x[48 + c] = sc;
+                x[96 + c] = qc - sc;
+                x[144 + c] = qc * sc;
+            }
+            for (int o = 0; o < 256; ++o) {
+                double a = b1[o];
+                for (int i = 0; i < 192; ++i) a += w1[o * 192 + i] * x[i];
+                z1[j * 256 + o] = a;
+            }
+            for (int o = 0; o < 64; ++o) {
+                double a = b2[o];
+                for (int i = 0; i < 256; ++i) a += w2[o * 256 + i] * (z1[j * 256 + i] > 0.0 ? z1[j * 256 + i] : 0.0);
+                z2[j * 64 + o] = a;
+            }
+            double a = b3;
+            for (int i = 0; i < 64; ++i) a += w3[i] * (z2[j * 64 + i] > 0.0 ? z2[j * 64 + i] : 0.0);
+            e[j] = a;
+        }
+        double m = e[0];
+        for (int64_t j = 1; j < L; ++j) if (e[j] > m) m = e[j];
+        double den = 0.0;
+        for (int64_t j = 0; j < L; ++j) den += exp(e[j] - m);
+        for (int64_t j = 0; j < L; ++j) p[j] = exp(e[j] - m) / den;
+        /* att = sum_j p_j s_j */
+        double pdp = 0.0;
+        for (int64_t j = 0; j < L; ++j) {
+            double d = 0.0;
+            for (int c = 0; c < 48; ++c) d += g[c] * sj[j * 48 + c];
+            dp[j] = d;
+            pdp += p[j] * d;
+        }
+        for (int64_t j = 0; j < L; ++j) {
+            double* dsj = gs + (seq_offsets[b] + j) * 48;
+            for (int c = 0; c < 48; ++c) dsj[c] = p[j] * g[c];
+            const double de = p[j] * (dp[j] - pdp);                 /* softmax */
+            double dz2[64], dz1[256], dx[192];
+            *db3 += de;
+            for (int o = 0; o < 64; ++o) {
+                const double h2o = z2[j * 64 + o] > 0.0 ? z2[j * 64 + o] : 0.0;
+                dw3[o] += de * h2o;
+                dz2[o] = z2[j * 64 + o] > 0.0 ? de * w3[o] : 0.0;
+            }
+            for (int o = 0; o < 64; ++o) {
+                db2[o] += dz2[o];
+                for (int i = 0; i < 256; ++i)
+                    dw2[o * 256 + i] += dz2[o] * (z1[j * 256 + i] > 0.0 ? z1[j * 256 + i] : 0.0);
+            }
+            for (int i = 0; i < 256; ++i) {
+                double a = 0.0;
+                for (int o = 0; o < 64; ++o) a += w2[o * 256 + i] * dz2[o];
+                dz1[i] = z1[j * 256 + i] > 0.0 ? a : 0.0;
+            }
+            const double* x = xs + j * 192;
+            for (int o = 0; o < 256; ++o) {
+                db1[o] += dz1[o];
+                for (int i = 0; i < 192; ++i) dw1[o * 192 + i] += dz1[o] * x[i];
+            }
+            for (int i = 0; i < 192; ++i) {
+                double a = 0.0;
+                for (int o = 0; o < 256; ++o) a += w1[o * 192 + i] * dz1[o];
+                dx[i] = a;
+            }
+            for (int c = 0; c < 48; ++c) {
+                const double sc = sj[j * 48 + c];
+                gq[b * 48 + c] += dx[c] + dx[96 + c] + sc * dx[144 + c];
+                dsj[c] += dx[48 + c] - dx[96 + c] + q[c] * dx[144 + c];
+            }
+        }
+    }
+    free(sj); free(xs); free(z1); free(z2); free(e); free(p); free(dp);
+}
+
 /* ------------------------------------------------------------------------
  * Deep tower and final MLP: the rest of the MultiTowerDIN forward
  * ([P1] §4.4 compute graph: the deep MLP 512 -> 256 -> 128 on the pooled deep

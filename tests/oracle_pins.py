@@ -664,6 +664,116 @@ def pin_embbag_adagrad(orc):
     assert np.array_equal(nG[8][1], (3.0 * dp[0, 128:144].astype(np.float64)) ** 2)
 
 
+def _torch_din_grads(model, batch, query, seq_offsets, max_len, gatt, pad_to=100):
+    """Autograd of sum(att * gatt) through the pages' padded DIN, in fp64:
+    gradients of the query, of every real sequence row, and of the MLP."""
+    B = batch.B
+    S = np.zeros((B, pad_to, 48))
+    L = np.minimum(batch.seq_lengths.astype(np.int64), max_len)
+    for i, k in enumerate(synth.SEQ_KEYS):
+        tab = model.tables[k]
+        w = np.asarray(tab["values"], dtype=np.float64)
+        for b in range(B):
+            n = int(L[b])
+            ids = batch.seq_values[i, seq_offsets[b]: seq_offsets[b] + n]
+            r = py_rows(tab, ids)
+            S[b, :n, 16 * i:16 * i + 16] = np.where(r[:, None] < 0, 0.0, w[np.maximum(r, 0)])
+    leaf = lambda a: torch.tensor(np.asarray(a, np.float64), requires_grad=True)  # noqa: E731
+    St, Qt = leaf(S), leaf(query)
+    W1, B1, W2, B2 = leaf(model.w1), leaf(model.b1), leaf(model.w2), leaf(model.b2)
+    W3, B3 = leaf(model.w3), leaf([float(model.b3)])
+    Q = Qt[:, None, :].expand(B, pad_to, 48)
+    X = torch.cat([Q, St, Q - St, Q * St], dim=-1)
+    h1 = torch.relu(F.linear(X, W1, B1))
+    h2 = torch.relu(F.linear(h1, W2, B2))
+    e = F.linear(h2, W3[None, :], B3).squeeze(-1)
+    mask = torch.arange(pad_to)[None, :] < torch.from_numpy(L)[:, None]
+    pw = torch.softmax(e.masked_fill(~mask, float("-inf")), dim=-1)
+    pw = torch.where(mask, pw, torch.zeros_like(pw))
+    att = torch.bmm(pw[:, None, :], St).squeeze(1)
+    (att * torch.from_numpy(np.asarray(gatt, np.float64))).sum().backward()
+    gs = np.zeros((int(seq_offsets[-1] + batch.seq_lengths[-1]) if B else 0, 48))
+    for b in range(B):
+        gs[seq_offsets[b]: seq_offsets[b] + int(L[b])] = St.grad[b, :int(L[b])].numpy()
+    return dict(gq=Qt.grad.numpy(), gs=gs, dw1=W1.grad.numpy(), db1=B1.grad.numpy(),
+                dw2=W2.grad.numpy(), db2=B2.grad.numpy(), dw3=W3.grad.numpy(),
+                db3=float(B3.grad[0]))
+
+
+def pin_din_bwd(orc):
+    """DIN attention backward against torch fp64 autograd through the pages'
+    padded formulation ("当前现状分析" §4.2, §4.4), every gradient; closed
+    forms: one-position sequences take no MLP gradient and pass g straight to
+    their row (p = 1 whatever the score), zero score weights give every row
+    g / L and no gradient to W1, W2 or the query; and central finite
+    differences of the oracle's own forward for entries of W1, b2, w3 and of a
+    query."""
+    for bias, emb_std, w3s in ((True, 0.05, 1.0), (True, 1.0, 20.0)):
+        m, b = _tiny(bias=bias, B=24, emb_std=emb_std, w3_scale=w3s)
+        off = _seq_offsets(b)
+        pooled = orc.embbag(m.tables, b.B, b.values, b.lengths, orc.lengths_to_offsets(b.lengths))
+        q = _query_from(pooled)
+        g = np.random.default_rng(5).standard_normal((b.B, 48))
+        seq_tabs = [m.tables[k] for k in synth.SEQ_KEYS]
+        got = orc.din_bwd(seq_tabs, b.seq_values, b.seq_stride, off, b.seq_lengths, 100, q, m.w1,
+                          m.b1, m.w2, m.b2, m.w3, m.b3, g)
+        ref = _torch_din_grads(m, b, q, off, 100, g)
+        for k in ("gq", "gs", "dw1", "db1", "dw2", "db2", "dw3"):
+            assert _rel(got[k], ref[k]) < 1e-12, (k, _rel(got[k], ref[k]))
+        assert abs(got["db3"] - ref["db3"]) <= 1e-12 * max(1.0, abs(ref["db3"]))
+    # finite differences of the oracle's forward (loss = sum(att * g))
+    m, b = _tiny(bias=True, B=6)
+    off = _seq_offsets(b)
+    seq_tabs = [m.tables[k] for k in synth.SEQ_KEYS]
+    q = np.random.default_rng(6).normal(0, 0.05, (b.B, 48))
+    g = np.random.default_rng(7).standard_normal((b.B, 48))
+
+    def loss(w1, b2, w3, qq):
+        att = orc.din(seq_tabs, b.seq_values, b.seq_stride, off, b.seq_lengths, 100, qq, w1, m.b1,
+                      m.w2, b2, w3, m.b3)
+        return float(np.sum(att * g))
+
+    got = orc.din_bwd(seq_tabs, b.seq_values, b.seq_stride, off, b.seq_lengths, 100, q, m.w1, m.b1,
+                      m.w2, m.b2, m.w3, m.b3, g)
+    base = [np.array(m.w1, np.float64), np.array(m.b2, np.float64), np.array(m.w3, np.float64), q]
+    for which, idx, key in ((0, (7, 100), "dw1"), (0, (200, 5), "dw1"), (1, (3,), "db2"),
+                            (2, (11,), "dw3"), (3, (2, 40), "gq")):
+        h = 1e-6
+        up = [x.copy() for x in base]
+        dn = [x.copy() for x in base]
+        up[which][idx] += h
+        dn[which][idx] -= h
+        fd = (loss(*up) - loss(*dn)) / (2 * h)
+        an = got[key][idx]
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (key, idx, fd, an)
+    # one-position sequences: p = 1, no MLP gradient, ds = g, dq = 0
+    m, b = _tiny(bias=True, B=16)
+    b.seq_lengths = np.ones(b.B, np.int32)
+    b.seq_values = np.ascontiguousarray(b.seq_values[:, :b.B])
+    b.seq_stride = b.B
+    off = _seq_offsets(b)
+    q = np.random.default_rng(8).normal(0, 0.05, (b.B, 48))
+    g = np.random.default_rng(9).standard_normal((b.B, 48))
+    got = orc.din_bwd([m.tables[k] for k in synth.SEQ_KEYS], b.seq_values, b.seq_stride, off,
+                      b.seq_lengths, 100, q, m.w1, m.b1, m.w2, m.b2, m.w3, m.b3, g)
+    assert np.array_equal(got["gs"], g) and not got["gq"].any()
+    for k in ("dw1", "db1", "dw2", "db2", "dw3"):
+        assert not got[k].any(), k
+    assert got["db3"] == 0.0
+    # zero score weights: uniform weights, ds = g / L, nothing reaches W1, W2 or q
+    m, b = _tiny(bias=True, B=16, w3_scale=0.0)
+    off = _seq_offsets(b)
+    got = orc.din_bwd([m.tables[k] for k in synth.SEQ_KEYS], b.seq_values, b.seq_stride, off,
+                      b.seq_lengths, 100, q, m.w1, m.b1, m.w2, m.b2, m.w3, m.b3, g)
+    Ls = np.minimum(b.seq_lengths, 100)
+    for bb in range(b.B):
+        rows = got["gs"][off[bb]: off[bb] + Ls[bb]]
+        assert np.allclose(rows, g[bb] / Ls[bb], rtol=1e-14, atol=1e-16)
+    for k in ("gq", "dw1", "db1", "dw2", "db2"):
+        assert not got[k].any(), k
+
+
 ALL_PINS = [pin_offsets, pin_floor_mod, pin_hash, pin_embbag_direct, pin_embbag_hash,
             pin_din_vs_padded, pin_din_closed_forms, pin_din_hash, pin_towers_closed_forms,
-            pin_towers_library, pin_hash_insert, pin_dlrm_interact, pin_embbag_adagrad]
+            pin_towers_library, pin_hash_insert, pin_dlrm_interact, pin_embbag_adagrad,
+            pin_din_bwd]
