@@ -549,6 +549,49 @@ rec_status rec_embbag_adagrad(const rec_adagrad_table* tables, int32_t T, int64_
                               int64_t seq_stride, int64_t P, const float* grad_seq, float lr,
                               float eps, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace rec_din_attn_bwd needs: 0 without weight gradients,
+ * else about 3.3 KiB per position index (seq_stride) plus 2 MiB. */
+size_t rec_din_attn_bwd_workspace_bytes(int64_t seq_stride, int32_t weight_grads);
+
+/*
+ * Backward of the DIN target attention ("当前现状分析" §4.2, §4.4: the
+ * forward [q, s, q-s, q*s] -> attn MLP (256, 64) -> score -> masked softmax
+ * -> weighted sum of the sequence rows; the run-config table's training step
+ * through it).  Given grad_att = dL/d att [B][48], computes by the chain rule
+ * (the forward is recomputed from the same inputs rec_din_attn_fwd takes):
+ *   grad_query [B][48]        dL/dq (for the pooled columns query_col[k] .. +16
+ *                             of the sample's deep bags; the caller adds it to
+ *                             the pooled gradient)
+ *   grad_seq [3][seq_stride][16] or NULL: dL/ds for every position index
+ *                             seq_offsets[b] + j, j < min(len_b, max_len);
+ *                             every other index gets zeros (rec_embbag_adagrad
+ *                             takes it as its sequence gradient)
+ *   dw1 [256][192], db1 [256], dw2 [64][256], db2 [64], dw3 [64], db3 [1]
+ *                             all six, or all NULL (no weight gradients): the
+ *                             sums over every sample and position
+ * Inputs as rec_din_attn_fwd: seq_tables host [3] (adgroup, cate, brand;
+ * direct or hash, a miss reads the zero vector), seq_values int64
+ * [3][seq_stride], seq_offsets int64 [B] (first position index of sample b),
+ * seq_lengths int32 [B], max_len in [1, REC_MAX_SEQ_LEN], query fp32 with row
+ * stride query_ld and host query_col[3]; mlp host, dtype REC_F32 or REC_BF16
+ * (plain layout; b1 and b2 may be NULL for zero biases).  The arithmetic is
+ * fp32; sums run in one fixed order (bit-identical run to run).
+ *   workspace  >= rec_din_attn_bwd_workspace_bytes(seq_stride, weight grads
+ *              requested) bytes, 256-byte aligned (may be NULL when 0)
+ * Errors: REC_EINVAL (null required pointers, misalignment, B < 0, bad
+ * max_len or query_col, some but not all weight-gradient pointers, bad
+ * table), REC_EUNSUPPORTED (dtype REC_BF16_PACKED), REC_EWORKSPACE.  B == 0 is
+ * a no-op.
+ */
+rec_status rec_din_attn_bwd(const rec_table* seq_tables, const int64_t* seq_values,
+                            int64_t seq_stride, const int64_t* seq_offsets,
+                            const int32_t* seq_lengths, int32_t max_len, int64_t B,
+                            const float* query, int64_t query_ld, const int32_t* query_col,
+                            const rec_din_mlp* mlp, const float* grad_att, float* grad_query,
+                            float* grad_seq, float* dw1, float* db1, float* dw2, float* db2,
+                            float* dw3, float* db3, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* rec_last_error(void);
 

@@ -430,13 +430,16 @@ void orc_din(const orc_table* seq_tables /* 3: adgroup, cate, brand */,
  * A sample with no positions has att = 0 for every q: it contributes nothing.
  * gq [B][48]; gs [seq_stride][48] by position index seq_offsets[b] + j (zero
  * for positions past max_len); the weight gradients are sums over all
- * samples and positions (they must be zero on entry).  Returns nothing. */
+ * samples and positions (they must be zero on entry).  db3 is zero in exact
+ * arithmetic (every score moving by the same amount leaves the softmax
+ * unchanged), so db3_scale receives sum |de_j|, the size of its terms, the
+ * yardstick for its rounding.  Returns nothing. */
 void orc_din_bwd(const orc_table* seq_tables, const int64_t* seq_values, int64_t seq_stride,
                  const int64_t* seq_offsets, const int32_t* seq_lengths, int32_t max_len,
                  int64_t B, const double* query, const double* w1, const double* b1,
                  const double* w2, const double* b2, const double* w3, double b3,
                  const double* gatt, double* gq, double* gs, double* dw1, double* db1,
-                 double* dw2, double* db2, double* dw3, double* db3) {
+                 double* dw2, double* db2, double* dw3, double* db3, double* db3_scale) {
     const int64_t ml = max_len > 0 ? max_len : 1;
     double* sj = (double*)malloc(sizeof(double) * 48 * (size_t)ml);
     double* xs = (double*)malloc(sizeof(double) * 192 * (size_t)ml);
@@ -498,6 +501,7 @@ void orc_din_bwd(const orc_table* seq_tables, const int64_t* seq_values, int64_t
             const double de = p[j] * (dp[j] - pdp);                 /* softmax */
             double dz2[64], dz1[256], dx[192];
             *db3 += de;
+            *db3_scale += fabs(de);
             for (int o = 0; o < 64; ++o) {
                 const double h2o = z2[j * 64 + o] > 0.0 ? z2[j * 64 + o] : 0.0;
                 dw3[o] += de * h2o;

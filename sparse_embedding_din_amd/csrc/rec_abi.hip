@@ -719,3 +719,108 @@ rec_status rec_embbag_adagrad(const rec_adagrad_table* tables, int32_t T, int64_
                                             (hipStream_t)stream),
                       fn);
 }
+
+namespace {
+
+struct DinBwdLayout {
+    size_t valid, X, H1, H2, DZ1, DZ2, DE, part, bytes;
+};
+
+DinBwdLayout din_bwd_layout(int64_t stride) {
+    DinBwdLayout L;
+    const size_t n = (size_t)stride;
+    L.valid = 0;
+    L.X = L.valid + round256(n);
+    L.H1 = L.X + round256(n * 193 * 4);
+    L.H2 = L.H1 + round256(n * 257 * 4);
+    L.DZ1 = L.H2 + round256(n * 65 * 4);
+    L.DZ2 = L.DZ1 + round256(n * 256 * 4);
+    L.DE = L.DZ2 + round256(n * 64 * 4);
+    L.part = L.DE + round256(n * 4);
+    L.bytes = L.part + round256((size_t)din_bwd_splits() * (size_t)din_bwd_part_stride() * 4);
+    return L;
+}
+
+}  // namespace
+
+size_t rec_din_attn_bwd_workspace_bytes(int64_t seq_stride, int32_t weight_grads) {
+    if (seq_stride < 0) return 0;
+    if (!weight_grads) return 0;
+    return din_bwd_layout(seq_stride).bytes;
+}
+
+rec_status rec_din_attn_bwd(const rec_table* seq_tables, const int64_t* seq_values,
+                            int64_t seq_stride, const int64_t* seq_offsets,
+                            const int32_t* seq_lengths, int32_t max_len, int64_t B,
+                            const float* query, int64_t query_ld, const int32_t* query_col,
+                            const rec_din_mlp* mlp, const float* grad_att, float* grad_query,
+                            float* grad_seq, float* dw1, float* db1, float* dw2, float* db2,
+                            float* dw3, float* db3, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+    const std::string f("rec_din_attn_bwd");
+    if (B < 0) return fail(REC_EINVAL, f + ": B < 0");
+    if (max_len < 1 || max_len > REC_MAX_SEQ_LEN) return fail(REC_EINVAL, f + ": max_len outside [1, REC_MAX_SEQ_LEN]");
+    if (seq_stride < 0) return fail(REC_EINVAL, f + ": seq_stride < 0");
+    if (!seq_tables || !mlp || !query_col) return fail(REC_EINVAL, f + ": seq_tables, mlp and query_col are required");
+    if (mlp->dtype == REC_BF16_PACKED) return fail(REC_EUNSUPPORTED, f + ": packed MLP weights are not supported");
+    if (mlp->dtype != REC_F32 && mlp->dtype != REC_BF16) return fail(REC_EINVAL, f + ": unknown dtype");
+    const int nw = (dw1 != nullptr) + (db1 != nullptr) + (dw2 != nullptr) + (db2 != nullptr) +
+                   (dw3 != nullptr) + (db3 != nullptr);
+    if (nw != 0 && nw != 6) return fail(REC_EINVAL, f + ": give all six weight-gradient outputs or none");
+    DinBwdArgs a;
+    memset(&a, 0, sizeof(a));
+    for (int k = 0; k < 3; ++k) {
+        rec_status st = prep_table(seq_tables[k], (f + ": seq table").c_str(), &a.tabs[k]);
+        if (st != REC_OK) return st;
+        if (query_col[k] < 0 || query_col[k] + 16 > query_ld)
+            return fail(REC_EINVAL, f + ": query_col outside the query row");
+        a.qcol[k] = query_col[k];
+    }
+    if (B > 0 && (!seq_values || !seq_offsets || !seq_lengths || !query || !grad_att || !grad_query ||
+                  !mlp->w1 || !mlp->w2 || !mlp->w3))
+        return fail(REC_EINVAL, f + ": a required pointer is NULL");
+    if (grad_seq && !aligned16(grad_seq)) return fail(REC_EINVAL, f + ": grad_seq not 16-byte aligned");
+    const size_t need = rec_din_attn_bwd_workspace_bytes(seq_stride, nw == 6);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(REC_EWORKSPACE, f + ": workspace missing or too small");
+    if (need > 0 && ((uintptr_t)workspace & 255u)) return fail(REC_EINVAL, f + ": workspace not 256-byte aligned");
+    if (B == 0) return ok();
+    a.seq_values = seq_values;
+    a.seq_stride = seq_stride;
+    a.seq_offsets = seq_offsets;
+    a.seq_lengths = seq_lengths;
+    a.max_len = max_len;
+    a.bf16 = mlp->dtype == REC_BF16;
+    a.B = B;
+    a.query = query;
+    a.query_ld = query_ld;
+    a.b3 = mlp->b3;
+    a.w1 = mlp->w1;
+    a.b1 = mlp->b1;
+    a.w2 = mlp->w2;
+    a.b2 = mlp->b2;
+    a.w3 = mlp->w3;
+    a.gatt = grad_att;
+    a.gq = grad_query;
+    a.gs = grad_seq;
+    if (nw == 6) {
+        const DinBwdLayout L = din_bwd_layout(seq_stride);
+        char* w = (char*)workspace;
+        a.valid = (uint8_t*)(w + L.valid);
+        a.X = (float*)(w + L.X);
+        a.H1 = (float*)(w + L.H1);
+        a.H2 = (float*)(w + L.H2);
+        a.DZ1 = (float*)(w + L.DZ1);
+        a.DZ2 = (float*)(w + L.DZ2);
+        a.DE = (float*)(w + L.DE);
+        a.part = (float*)(w + L.part);
+        a.part_stride = din_bwd_part_stride();
+        a.dw1 = dw1;
+        a.db1 = db1;
+        a.dw2 = dw2;
+        a.db2 = db2;
+        a.dw3 = dw3;
+        a.db3 = db3;
+    }
+    return hip_status(launch_din_bwd(a, (hipStream_t)stream), "rec_din_attn_bwd");
+}

@@ -365,6 +365,40 @@ int64_t bwd_sort_tiles(int64_t n);            // tiles of the radix sort (256 co
 hipError_t launch_embbag_adagrad(BwdArgs a, const BwdTab* tabs, uint32_t* keys_out, uint32_t* src_out,
                                  uint32_t* sort_hist, uint32_t* sort_tot, int key_bits, hipStream_t s);
 
+// DIN attention backward (rec_din_bwd.hip).
+struct DinBwdArgs {
+    TabDev tabs[3];
+    const int64_t* seq_values;
+    int64_t seq_stride;
+    const int64_t* seq_offsets;
+    const int32_t* seq_lengths;
+    int32_t max_len;
+    int32_t bf16;                 // w1/w2 are bf16 bit patterns
+    int64_t B;
+    const float* query;
+    int64_t query_ld;
+    int32_t qcol[3];
+    float b3;
+    const void* w1;
+    const float* b1;              // may be NULL (zero)
+    const void* w2;
+    const float* b2;              // may be NULL (zero)
+    const float* w3;
+    const float* gatt;            // [B][48]
+    float* gq;                    // [B][48]
+    float* gs;                    // [3][seq_stride][16] or NULL
+    // weight gradients (valid == NULL: not requested)
+    uint8_t* valid;               // [seq_stride]
+    float *X, *H1, *H2, *DZ1, *DZ2, *DE;
+    float* part;                  // [splits][part_stride]
+    int64_t part_stride;
+    float *dw1, *db1, *dw2, *db2, *dw3, *db3;
+};
+
+int64_t din_bwd_part_stride();
+int din_bwd_splits();
+hipError_t launch_din_bwd(const DinBwdArgs& a, hipStream_t s);
+
 hipError_t launch_hash_clear(int64_t* keys, uint8_t* digests, uint64_t* scores, int64_t capacity,
                              hipStream_t s);
 

@@ -33,6 +33,7 @@ EXPORTS = ["rec_din_pack_mlp", "rec_scan_workspace_bytes", "rec_lengths_to_offse
            "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_fwd",
            "rec_sparse_din_fwd_workspace_bytes", "rec_sparse_din_fwd", "rec_towers_fwd",
            "rec_tower_pack_mlp", "rec_embbag_adagrad_workspace_bytes", "rec_embbag_adagrad",
+           "rec_din_attn_bwd_workspace_bytes", "rec_din_attn_bwd",
            "rec_last_error", "rec_version", "rec_host_floor_mod", "rec_host_hash_home",
            "rec_host_hash_probe"]
 
@@ -117,6 +118,11 @@ def lib():
         L.rec_sparse_din_fwd.argtypes = [C.POINTER(rec_fwd_args), vp]
         L.rec_towers_fwd.argtypes = [C.POINTER(rec_tower_mlp), i64, vp, i64, vp, vp, vp, vp, vp]
         L.rec_tower_pack_mlp.argtypes = [C.POINTER(rec_tower_mlp), vp, sz, vp]
+        L.rec_din_attn_bwd_workspace_bytes.argtypes = [i64, i32]
+        L.rec_din_attn_bwd_workspace_bytes.restype = sz
+        L.rec_din_attn_bwd.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, i32, i64, vp, i64,
+                                       C.POINTER(C.c_int32), C.POINTER(rec_din_mlp), vp, vp, vp,
+                                       vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.rec_embbag_adagrad_workspace_bytes.argtypes = [i32, i64, i64, i64]
         L.rec_embbag_adagrad_workspace_bytes.restype = sz
         L.rec_embbag_adagrad.argtypes = [C.POINTER(rec_adagrad_table), i32, i64, vp, vp, vp, i64,
@@ -126,7 +132,7 @@ def lib():
                   "rec_hash_lookup", "rec_hash_insert", "rec_hash_clear", "rec_dlrm_interact",
                   "rec_din_plan",
                   "rec_din_attn_fwd", "rec_din_pack_mlp", "rec_sparse_din_fwd", "rec_towers_fwd",
-                  "rec_tower_pack_mlp", "rec_embbag_adagrad"):
+                  "rec_tower_pack_mlp", "rec_embbag_adagrad", "rec_din_attn_bwd"):
             getattr(L, f).restype = C.c_int
         L.rec_last_error.argtypes = []
         L.rec_last_error.restype = C.c_char_p
@@ -365,3 +371,21 @@ def rec_embbag_adagrad(tables, T: int, B: int, values, lengths, offsets, nnz: in
                                     _p(grad_pooled), st, _p(seq_values), seq_stride, P,
                                     _p(grad_seq), float(lr), float(eps), _p(workspace),
                                     workspace_bytes, _stream(stream)), "rec_embbag_adagrad")
+
+
+def rec_din_attn_bwd_workspace_bytes(seq_stride: int, weight_grads: bool) -> int:
+    return int(lib().rec_din_attn_bwd_workspace_bytes(seq_stride, int(bool(weight_grads))))
+
+
+def rec_din_attn_bwd(seq_tables: Sequence[rec_table], seq_values, seq_stride: int, seq_offsets,
+                     seq_lengths, max_len: int, B: int, query, query_ld: int, query_col,
+                     mlp: rec_din_mlp, grad_att, grad_query, grad_seq=None, dw1=None, db1=None,
+                     dw2=None, db2=None, dw3=None, db3=None, workspace=None,
+                     workspace_bytes: int = 0, stream=None):
+    qc = (C.c_int32 * 3)(*[int(x) for x in query_col])
+    _check(lib().rec_din_attn_bwd(_tables(seq_tables), _p(seq_values), seq_stride, _p(seq_offsets),
+                                  _p(seq_lengths), max_len, B, _p(query), query_ld, qc,
+                                  C.byref(mlp), _p(grad_att), _p(grad_query), _p(grad_seq),
+                                  _p(dw1), _p(db1), _p(dw2), _p(db2), _p(dw3), _p(db3),
+                                  _p(workspace), workspace_bytes, _stream(stream)),
+           "rec_din_attn_bwd")

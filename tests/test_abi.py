@@ -523,3 +523,33 @@ def test_embbag_adagrad_errors(lib):
     with pytest.raises(R.RecError):
         R.rec_embbag_adagrad([R.adagrad_table(FAKE, FAKE, 10)], 1, 4, FAKE, FAKE, FAKE, 8, None,
                              None, None, 0, 0, None, 1e-3, 1e-10, FAKE, 1 << 20)
+
+
+def test_din_attn_bwd_errors(lib):
+    f = lib.rec_din_attn_bwd
+    seq = R._tables([_table() for _ in range(3)])
+    mlp = R.din_mlp(R.REC_F32, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0)
+    qc = (C.c_int32 * 3)(16, 80, 48)
+    W = [FAKE] * 6
+
+    def call(B=4, max_len=100, stride=64, seq_=seq, mlp_=mlp, qc_=qc, ld=256, gq=FAKE, gs=FAKE,
+             w=W, ws=FAKE, wsb=1 << 30):
+        return _status(f, seq_, FAKE, stride, FAKE, FAKE, max_len, B, FAKE, ld, qc_, C.byref(mlp_),
+                       FAKE, gq, gs, *w, ws, wsb, None)
+
+    assert call(B=-1)[0] == R.REC_EINVAL
+    assert call(max_len=0)[0] == R.REC_EINVAL
+    assert call(max_len=R.REC_MAX_SEQ_LEN + 1)[0] == R.REC_EINVAL
+    assert call(stride=-1)[0] == R.REC_EINVAL
+    assert call(qc_=(C.c_int32 * 3)(16, 250, 48))[0] == R.REC_EINVAL     # 250 + 16 > 256
+    assert call(gq=None)[0] == R.REC_EINVAL
+    assert call(gs=FAKE_ODD)[0] == R.REC_EINVAL
+    s, msg = call(w=[FAKE, FAKE, None, FAKE, FAKE, FAKE])
+    assert s == R.REC_EINVAL and "all six" in msg
+    packed = R.din_mlp(R.REC_BF16_PACKED, FAKE, FAKE, None, FAKE, FAKE, 0.0)
+    assert call(mlp_=packed)[0] == R.REC_EUNSUPPORTED
+    need = R.rec_din_attn_bwd_workspace_bytes(64, True)
+    assert need > 64 * 3300 and R.rec_din_attn_bwd_workspace_bytes(64, False) == 0
+    assert call(wsb=need - 1)[0] == R.REC_EWORKSPACE
+    assert call(ws=FAKE + 16, wsb=need)[0] == R.REC_EINVAL
+    assert call(B=0, ws=None, wsb=0, w=[None] * 6)[0] == R.REC_OK
