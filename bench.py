@@ -8,8 +8,9 @@ lengths -> offsets, sequence plan, sum-pooled embedding bags (16 tables,
 made as one rec_sparse_din_fwd call (three kernel launches).  The rest of the
 MultiTowerDIN forward (deep tower + final MLP, rec_towers_fwd) is timed
 beside it and reported under "towers"; it is not part of the timed step.  So are
-the sparse backward with its AdaGrad step ("adagrad") and the DLRM interaction
-layer at 217 x 96 ("dlrm_interaction").
+the sparse backward with its AdaGrad step ("adagrad"), the DIN attention's
+backward ("din_bwd") and the DLRM interaction layer at 217 x 96
+("dlrm_interaction").
 Four resident batches rotate (so the L2 does not keep one batch's rows); one
 HIP graph holds a step for each of them and is replayed.  Everything runs on
 one stream: inside a graph, a fork/join to a second stream costs more than
@@ -74,6 +75,8 @@ def parse():
                    help="skip timing the rebuild of the hash workload's tables (clear + insert)")
     p.add_argument("--no-interaction", action="store_true",
                    help="skip the DLRM interaction leg (217 vectors of width 96 per sample)")
+    p.add_argument("--no-din-bwd", action="store_true",
+                   help="skip the DIN attention backward leg")
     p.add_argument("--no-adagrad", action="store_true",
                    help="skip the backward + sparse AdaGrad leg reported beside the step")
     p.add_argument("--no-towers", action="store_true",
@@ -528,6 +531,60 @@ def main():
               f"{n_rows:.0f} rows)", file=sys.stderr, flush=True)
         del aw, aa, akd, aws, legs
 
+    din_bwd = None
+    if not a.no_din_bwd:
+        # The attention's backward beside the step: random output gradients
+        # [B,48] through rec_din_attn_bwd (query and sequence-row gradients and
+        # the six MLP weight gradients), plain (unpacked) weights.
+        rng = np.random.default_rng(777)
+        b0, db0, f0 = batches[0], dbs[0], fwds[0]
+        Pb = int(b0.seq_lengths.sum())
+        offs0 = torch.from_numpy(np.concatenate([[0], np.cumsum(b0.seq_lengths.astype(np.int64))[:-1]])).to(dev)
+        mlp_plain = PL.DeviceMLP(model, dev, packed=False)
+        gatt = torch.from_numpy(rng.standard_normal((B, 48)).astype(np.float32)).to(dev)
+        gq = torch.empty(B, 48, dtype=torch.float32, device=dev)
+        gs = torch.empty(3, max(db0.seq_stride, 1), 16, dtype=torch.float32, device=dev)
+        wg = [torch.empty(sh, dtype=torch.float32, device=dev)
+              for sh in ((256, 192), (256,), (64, 256), (64,), (64,), (1,))]
+        wsb_d = R.rec_din_attn_bwd_workspace_bytes(db0.seq_stride, True)
+        ws_d = torch.empty(wsb_d, dtype=torch.uint8, device=dev)
+        seq_arr = tabs.array(list(synth.SEQ_KEYS))
+
+        def din_bwd_call():
+            R.rec_din_attn_bwd(seq_arr, db0.seq_values, db0.seq_stride, offs0, db0.seq_lengths,
+                               cfg.max_len, B, f0.pooled, f0.T * 16, synth.QUERY_COL, mlp_plain.desc,
+                               gatt, gq, gs, *wg, workspace=ws_d, workspace_bytes=wsb_d,
+                               stream=stream)
+
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                din_bwd_call()
+            torch.cuda.synchronize()
+            reps_d = 10
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps_d)]
+            torch.cuda._sleep(20_000_000)
+            for r in range(reps_d):
+                evs[r][0].record(stream)
+                din_bwd_call()
+                evs[r][1].record(stream)
+            torch.cuda.synchronize()
+        d = np.array([s_.elapsed_time(e_) * 1e3 for s_, e_ in evs])
+        d_us = float(d.mean())
+        Pv = float(np.minimum(b0.seq_lengths, cfg.max_len).sum())
+        # per position: the forward again (scores), the forward once more with
+        # the backward's three products, and the two weight-gradient products
+        d_flops = Pv * (2 * DIN_FLOPS_PER_POS + 2 * (64 * 256 + 256 * 192) + 2 * (256 * 193 + 64 * 257 + 65))
+        din_bwd = {"entry": "rec_din_attn_bwd (query, sequence-row and MLP weight gradients)",
+                   "avg_call_us": round(d_us, 2), "positions": Pv, "samples": B,
+                   "flops_per_call": d_flops, "achieved_tflops": round(d_flops / (d_us * 1e-6) / 1e12, 2),
+                   "peak": FP32_PEAK_TFLOPS, "frac": round(d_flops / (d_us * 1e-6) / 1e12 / FP32_PEAK_TFLOPS, 4),
+                   "bound": "fp32 vector arithmetic, one 256-thread workgroup per sample (a first, "
+                            "correctness-first version: the products do not use the matrix cores yet)"}
+        print(f"[bench] DIN attention backward: {d_us:.1f} us per call ({Pv:.0f} positions)",
+              file=sys.stderr, flush=True)
+        del gatt, gq, gs, wg, ws_d
+
     interaction = None
     if not a.no_interaction:
         # The DLRM interaction layer at the pages' measured shape (the DLRM
@@ -614,6 +671,7 @@ def main():
         "towers": towers,
         "hash_rebuild": rebuild,
         "adagrad": adagrad,
+        "din_bwd": din_bwd,
         "dlrm_interaction": interaction,
         "src_hash": shash,
     }

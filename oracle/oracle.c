@@ -433,13 +433,19 @@ void orc_din(const orc_table* seq_tables /* 3: adgroup, cate, brand */,
  * samples and positions (they must be zero on entry).  db3 is zero in exact
  * arithmetic (every score moving by the same amount leaves the softmax
  * unchanged), so db3_scale receives sum |de_j|, the size of its terms, the
- * yardstick for its rounding.  Returns nothing. */
+ * yardstick for its rounding; likewise gq, whose terms of a sample nearly
+ * cancel when its positions look alike (de_j is a difference of nearly equal
+ * terms and the de_j sum to zero), gets gq_scale [B][48]: the chain above run
+ * on the sizes of the terms instead of their values (a running-error bound
+ * of the kind Higham, "Accuracy and Stability of Numerical Algorithms", §3,
+ * uses for sums and products).  Returns nothing. */
 void orc_din_bwd(const orc_table* seq_tables, const int64_t* seq_values, int64_t seq_stride,
                  const int64_t* seq_offsets, const int32_t* seq_lengths, int32_t max_len,
                  int64_t B, const double* query, const double* w1, const double* b1,
                  const double* w2, const double* b2, const double* w3, double b3,
                  const double* gatt, double* gq, double* gs, double* dw1, double* db1,
-                 double* dw2, double* db2, double* dw3, double* db3, double* db3_scale) {
+                 double* dw2, double* db2, double* dw3, double* db3, double* db3_scale,
+                 double* gq_scale) {
     const int64_t ml = max_len > 0 ? max_len : 1;
     double* sj = (double*)malloc(sizeof(double) * 48 * (size_t)ml);
     double* xs = (double*)malloc(sizeof(double) * 192 * (size_t)ml);
@@ -453,7 +459,7 @@ void orc_din_bwd(const orc_table* seq_tables, const int64_t* seq_values, int64_t
         const int64_t L = seq_lengths[b] < max_len ? seq_lengths[b] : max_len;
         const double* q = query + b * 48;
         const double* g = gatt + b * 48;
-        for (int c = 0; c < 48; ++c) gq[b * 48 + c] = 0.0;
+        for (int c = 0; c < 48; ++c) gq[b * 48 + c] = gq_scale[b * 48 + c] = 0.0;
         if (L <= 0) continue;
         /* forward, kept per position */
         for (int64_t j = 0; j < L; ++j) {
@@ -488,12 +494,13 @@ void orc_din_bwd(const orc_table* seq_tables, const int64_t* seq_values, int64_t
         for (int64_t j = 0; j < L; ++j) den += exp(e[j] - m);
         for (int64_t j = 0; j < L; ++j) p[j] = exp(e[j] - m) / den;
         /* att = sum_j p_j s_j */
-        double pdp = 0.0;
+        double pdp = 0.0, pdp_mag = 0.0;
         for (int64_t j = 0; j < L; ++j) {
             double d = 0.0;
             for (int c = 0; c < 48; ++c) d += g[c] * sj[j * 48 + c];
             dp[j] = d;
             pdp += p[j] * d;
+            pdp_mag += p[j] * fabs(d);
         }
         for (int64_t j = 0; j < L; ++j) {
             double* dsj = gs + (seq_offsets[b] + j) * 48;
@@ -527,9 +534,26 @@ void orc_din_bwd(const orc_table* seq_tables, const int64_t* seq_values, int64_t
                 for (int o = 0; o < 256; ++o) a += w1[o * 192 + i] * dz1[o];
                 dx[i] = a;
             }
+            /* the same chain on the sizes of the terms (|de_j|'s terms, then
+             * |w3|, |W2|^T, |W1|^T under the same ReLU gates): the yardstick of
+             * gq, whose terms nearly cancel when a sample's positions look alike */
+            double m2[64], m1[256], mx[192];
+            const double de_mag = p[j] * (fabs(dp[j]) + pdp_mag);
+            for (int o = 0; o < 64; ++o) m2[o] = z2[j * 64 + o] > 0.0 ? de_mag * fabs(w3[o]) : 0.0;
+            for (int i = 0; i < 256; ++i) {
+                double a = 0.0;
+                for (int o = 0; o < 64; ++o) a += fabs(w2[o * 256 + i]) * m2[o];
+                m1[i] = z1[j * 256 + i] > 0.0 ? a : 0.0;
+            }
+            for (int i = 0; i < 192; ++i) {
+                double a = 0.0;
+                for (int o = 0; o < 256; ++o) a += fabs(w1[o * 192 + i]) * m1[o];
+                mx[i] = a;
+            }
             for (int c = 0; c < 48; ++c) {
                 const double sc = sj[j * 48 + c];
                 gq[b * 48 + c] += dx[c] + dx[96 + c] + sc * dx[144 + c];
+                gq_scale[b * 48 + c] += mx[c] + mx[96 + c] + fabs(sc) * mx[144 + c];
                 dsj[c] += dx[48 + c] - dx[96 + c] + q[c] * dx[144 + c];
             }
         }

@@ -721,6 +721,7 @@ def pin_din_bwd(orc):
         for k in ("gq", "gs", "dw1", "db1", "dw2", "db2", "dw3"):
             assert _rel(got[k], ref[k]) < 1e-12, (k, _rel(got[k], ref[k]))
         assert abs(got["db3"] - ref["db3"]) <= 1e-12 * max(1.0, abs(ref["db3"]))
+        assert np.all(got["gq_scale"] >= np.abs(got["gq"]) * (1 - 1e-12))
         # db3 vanishes: the softmax ignores a common shift of the scores
         assert abs(got["db3"]) <= 1e-13 * got["db3_scale"] and got["db3_scale"] > 0
     # finite differences of the oracle's forward (loss = sum(att * g))

@@ -74,7 +74,11 @@ def _check(m, b, seq_values, offs, stride, query, gatt, max_len=100, weights=Tru
     q = np.concatenate([query[:, c:c + 16] for c in synth.QUERY_COL], axis=1).astype(np.float64)
     ref = oracle.get().din_bwd([m.tables[k] for k in synth.SEQ_KEYS], seq_values, stride, offs,
                                b.seq_lengths, max_len, q, m.w1, m.b1, m.w2, m.b2, m.w3, m.b3, gatt)
-    errs = {"gq": row_rel_err(got["gq"], ref["gq"])}
+    # the query gradient sums terms that nearly cancel when a sample's
+    # positions look alike (the score gradients of a sample sum to zero): its
+    # error is measured per row against the size of those terms
+    errs = {"gq": float(np.max(np.abs(got["gq"] - ref["gq"]).max(1) /
+                               np.maximum(ref["gq_scale"].max(1), 1e-30)))}
     gs_ref = ref["gs"].reshape(stride, 3, 16).transpose(1, 0, 2)        # [3][stride][16]
     errs["gs"] = row_rel_err(got["gs"].reshape(-1, 16)[:3 * stride], gs_ref.reshape(-1, 16))
     if weights:
@@ -140,3 +144,10 @@ def test_din_bwd_deterministic():
     c = _gpu(*args, 100)
     for k in a:
         assert np.array_equal(a[k].view(np.uint32), c[k].view(np.uint32)), k
+
+
+def test_din_bwd_full_size():
+    """The Taobao-shaped batch (B = 8192, geometric lengths, full tables, bf16
+    weights), every gradient against the oracle."""
+    say("din bwd full size taobao_B8192")
+    _check(*_case(synth.CONFIGS[2], 8192, 8), tag="taobao_B8192", dtype="bf16")
