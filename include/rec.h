@@ -549,8 +549,9 @@ rec_status rec_embbag_adagrad(const rec_adagrad_table* tables, int32_t T, int64_
                               int64_t seq_stride, int64_t P, const float* grad_seq, float lr,
                               float eps, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace rec_din_attn_bwd needs: 0 without weight gradients,
- * else about 3.3 KiB per position index (seq_stride) plus 2 MiB. */
+/* Bytes of workspace rec_din_attn_bwd needs: 256 KiB (the transposed
+ * weights), plus about 3.3 KiB per position index (seq_stride) and 2 MiB with
+ * weight gradients. */
 size_t rec_din_attn_bwd_workspace_bytes(int64_t seq_stride, int32_t weight_grads);
 
 /*
@@ -577,7 +578,7 @@ size_t rec_din_attn_bwd_workspace_bytes(int64_t seq_stride, int32_t weight_grads
  * (plain layout; b1 and b2 may be NULL for zero biases).  The arithmetic is
  * fp32; sums run in one fixed order (bit-identical run to run).
  *   workspace  >= rec_din_attn_bwd_workspace_bytes(seq_stride, weight grads
- *              requested) bytes, 256-byte aligned (may be NULL when 0)
+ *              requested) bytes, 256-byte aligned
  * Errors: REC_EINVAL (null required pointers, misalignment, B < 0, bad
  * max_len or query_col, some but not all weight-gradient pointers, bad
  * table), REC_EUNSUPPORTED (dtype REC_BF16_PACKED), REC_EWORKSPACE.  B == 0 is

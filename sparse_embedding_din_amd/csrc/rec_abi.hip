@@ -723,13 +723,17 @@ rec_status rec_embbag_adagrad(const rec_adagrad_table* tables, int32_t T, int64_
 namespace {
 
 struct DinBwdLayout {
-    size_t valid, X, H1, H2, DZ1, DZ2, DE, part, bytes;
+    size_t w1t, w2t, valid, X, H1, H2, DZ1, DZ2, DE, part, bytes;
 };
 
-DinBwdLayout din_bwd_layout(int64_t stride) {
+// The transposed weights always; the per-position rows and the split sums
+// only with weight gradients.
+DinBwdLayout din_bwd_layout(int64_t stride, bool weight_grads) {
     DinBwdLayout L;
-    const size_t n = (size_t)stride;
-    L.valid = 0;
+    const size_t n = weight_grads ? (size_t)stride : 0;
+    L.w1t = 0;
+    L.w2t = L.w1t + round256(192 * 256 * 4);
+    L.valid = L.w2t + round256(256 * 64 * 4);
     L.X = L.valid + round256(n);
     L.H1 = L.X + round256(n * 193 * 4);
     L.H2 = L.H1 + round256(n * 257 * 4);
@@ -737,7 +741,7 @@ DinBwdLayout din_bwd_layout(int64_t stride) {
     L.DZ2 = L.DZ1 + round256(n * 256 * 4);
     L.DE = L.DZ2 + round256(n * 64 * 4);
     L.part = L.DE + round256(n * 4);
-    L.bytes = L.part + round256((size_t)din_bwd_splits() * (size_t)din_bwd_part_stride() * 4);
+    L.bytes = L.part + (weight_grads ? round256((size_t)din_bwd_splits() * (size_t)din_bwd_part_stride() * 4) : 0);
     return L;
 }
 
@@ -745,8 +749,7 @@ DinBwdLayout din_bwd_layout(int64_t stride) {
 
 size_t rec_din_attn_bwd_workspace_bytes(int64_t seq_stride, int32_t weight_grads) {
     if (seq_stride < 0) return 0;
-    if (!weight_grads) return 0;
-    return din_bwd_layout(seq_stride).bytes;
+    return din_bwd_layout(seq_stride, weight_grads != 0).bytes;
 }
 
 rec_status rec_din_attn_bwd(const rec_table* seq_tables, const int64_t* seq_values,
@@ -781,9 +784,8 @@ rec_status rec_din_attn_bwd(const rec_table* seq_tables, const int64_t* seq_valu
         return fail(REC_EINVAL, f + ": a required pointer is NULL");
     if (grad_seq && !aligned16(grad_seq)) return fail(REC_EINVAL, f + ": grad_seq not 16-byte aligned");
     const size_t need = rec_din_attn_bwd_workspace_bytes(seq_stride, nw == 6);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(REC_EWORKSPACE, f + ": workspace missing or too small");
-    if (need > 0 && ((uintptr_t)workspace & 255u)) return fail(REC_EINVAL, f + ": workspace not 256-byte aligned");
+    if (!workspace || workspace_bytes < need) return fail(REC_EWORKSPACE, f + ": workspace missing or too small");
+    if ((uintptr_t)workspace & 255u) return fail(REC_EINVAL, f + ": workspace not 256-byte aligned");
     if (B == 0) return ok();
     a.seq_values = seq_values;
     a.seq_stride = seq_stride;
@@ -803,9 +805,11 @@ rec_status rec_din_attn_bwd(const rec_table* seq_tables, const int64_t* seq_valu
     a.gatt = grad_att;
     a.gq = grad_query;
     a.gs = grad_seq;
+    const DinBwdLayout L = din_bwd_layout(seq_stride, nw == 6);
+    char* w = (char*)workspace;
+    a.w1t = (float*)(w + L.w1t);
+    a.w2t = (float*)(w + L.w2t);
     if (nw == 6) {
-        const DinBwdLayout L = din_bwd_layout(seq_stride);
-        char* w = (char*)workspace;
         a.valid = (uint8_t*)(w + L.valid);
         a.X = (float*)(w + L.X);
         a.H1 = (float*)(w + L.H1);

@@ -12,8 +12,10 @@
 //   dW1 = sum_j dz1_j x_j^T, dW2 = sum_j dz2_j h1_j^T, dw3 = sum_j de_j h2_j
 //   (and the biases: the sums of dz1, dz2, de).
 //
-// Three launches, plain fp32 arithmetic (a first, correctness-first version;
-// its matrix products are small per position and run on the vector units):
+// Plain fp32 arithmetic (a first, correctness-first version; its matrix
+// products are small per position and run on the vector units):
+//   k_dinb_transpose  W1^T and W2^T in fp32 into the workspace, so that the
+//                  forward products read weights coalesced as the backward's do;
 //   k_dinb_clear   every position index: its validity flag and its rows of
 //                  grad_seq set to zero (positions past a sample's first
 //                  max_len, and gaps of a padded layout, stay zero);
@@ -67,6 +69,20 @@ __global__ __launch_bounds__(256) void k_dinb_clear(DinBwdArgs a) {
     }
 }
 
+// W1^T [192][256] and W2^T [256][64] in fp32, once per call, so that every
+// product below reads the weights with consecutive threads on consecutive
+// addresses.
+__global__ __launch_bounds__(256) void k_dinb_transpose(DinBwdArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < 256 * 192) {
+        const int64_t o = i / 192, c = i - o * 192;
+        a.w1t[c * 256 + o] = wload(a.w1, i, a.bf16);
+    } else if (i < 256 * 192 + 64 * 256) {
+        const int64_t j = i - 256 * 192, o = j / 256, c = j - o * 256;
+        a.w2t[c * 64 + o] = wload(a.w2, j, a.bf16);
+    }
+}
+
 // x of position j (thread t < 192 forms x[t]) into xs.
 __device__ inline void form_x(const float* q, const float* sj, float* xs, int t) {
     if (t < 192) {
@@ -81,13 +97,15 @@ __device__ inline void form_x(const float* q, const float* sj, float* xs, int t)
 __device__ inline void mlp_fwd(const DinBwdArgs& a, const float* xs, float* h1, float* h2, int t) {
     {
         float acc = a.b1 ? a.b1[t] : 0.0f;
-        for (int i = 0; i < 192; ++i) acc += wload(a.w1, (int64_t)t * 192 + i, a.bf16) * xs[i];
+#pragma unroll 8
+        for (int i = 0; i < 192; ++i) acc += a.w1t[i * 256 + t] * xs[i];
         h1[t] = acc > 0.0f ? acc : 0.0f;
     }
     __syncthreads();
     if (t < 64) {
         float acc = a.b2 ? a.b2[t] : 0.0f;
-        for (int i = 0; i < 256; ++i) acc += wload(a.w2, (int64_t)t * 256 + i, a.bf16) * h1[i];
+#pragma unroll 8
+        for (int i = 0; i < 256; ++i) acc += a.w2t[i * 64 + t] * h1[i];
         h2[t] = acc > 0.0f ? acc : 0.0f;
     }
     __syncthreads();
@@ -170,6 +188,7 @@ __global__ __launch_bounds__(kDinbThreads) void k_dinb_sample(DinBwdArgs a) {
         __syncthreads();
         {
             float acc = 0.0f;
+#pragma unroll 8
             for (int o = 0; o < 64; ++o) acc += wload(a.w2, (int64_t)o * 256 + t, a.bf16) * dz2[o];
             dz1[t] = h1[t] > 0.0f ? acc : 0.0f;
         }
@@ -178,6 +197,7 @@ __global__ __launch_bounds__(kDinbThreads) void k_dinb_sample(DinBwdArgs a) {
         if (a.valid) a.DZ1[pos * 256 + t] = dz1[t];
         if (t < 192) {
             float acc = 0.0f;
+#pragma unroll 8
             for (int o = 0; o < 256; ++o) acc += wload(a.w1, (int64_t)o * 192 + t, a.bf16) * dz1[o];
             dx[t] = acc;
         }
@@ -251,6 +271,7 @@ hipError_t launch_din_bwd(const DinBwdArgs& a, hipStream_t s) {
     if (cgrid > 0) {
         hipLaunchKernelGGL(k_dinb_clear, dim3((unsigned)(cgrid < 65536 ? cgrid : 65536)), dim3(256), 0, s, a);
     }
+    hipLaunchKernelGGL(k_dinb_transpose, dim3((256 * 192 + 64 * 256 + 255) / 256), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_dinb_sample, dim3((unsigned)a.B), dim3(kDinbThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.valid) return e;

@@ -387,6 +387,8 @@ struct DinBwdArgs {
     const float* gatt;            // [B][48]
     float* gq;                    // [B][48]
     float* gs;                    // [3][seq_stride][16] or NULL
+    float* w1t;                   // [192][256] fp32 workspace
+    float* w2t;                   // [256][64] fp32 workspace
     // weight gradients (valid == NULL: not requested)
     uint8_t* valid;               // [seq_stride]
     float *X, *H1, *H2, *DZ1, *DZ2, *DE;

@@ -549,7 +549,9 @@ def test_din_attn_bwd_errors(lib):
     packed = R.din_mlp(R.REC_BF16_PACKED, FAKE, FAKE, None, FAKE, FAKE, 0.0)
     assert call(mlp_=packed)[0] == R.REC_EUNSUPPORTED
     need = R.rec_din_attn_bwd_workspace_bytes(64, True)
-    assert need > 64 * 3300 and R.rec_din_attn_bwd_workspace_bytes(64, False) == 0
+    small = R.rec_din_attn_bwd_workspace_bytes(64, False)
+    assert need > 64 * 3300 + small and small == (192 + 64) * 256 * 4
     assert call(wsb=need - 1)[0] == R.REC_EWORKSPACE
+    assert call(w=[None] * 6, wsb=small - 1)[0] == R.REC_EWORKSPACE
     assert call(ws=FAKE + 16, wsb=need)[0] == R.REC_EINVAL
-    assert call(B=0, ws=None, wsb=0, w=[None] * 6)[0] == R.REC_OK
+    assert call(B=0, wsb=small, w=[None] * 6)[0] == R.REC_OK

@@ -56,7 +56,7 @@ def _gpu(m, b, seq_values, offs, stride, query, gatt, max_len, weights=True, dty
     outs = [torch.full(s, 7.0, dtype=torch.float32, device=DEV)
             for s in ((256, 192), (256,), (64, 256), (64,), (64,), (1,))] if weights else [None] * 6
     wsb = R.rec_din_attn_bwd_workspace_bytes(stride, weights)
-    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV) if wsb else None
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
     R.rec_din_attn_bwd(tabs.array(list(synth.SEQ_KEYS)), to(seq_values), stride, to(offs),
                        to(b.seq_lengths), max_len, B, to(query), 256, synth.QUERY_COL, mlp.desc,
                        to(gatt), gq, gs, *outs, workspace=ws, workspace_bytes=wsb)
