@@ -122,6 +122,8 @@ KERNEL_SOURCES = {"k_din_attn": _FWD, "k_embbag_fwd": _FWD, "k_fwd_gather": _FWD
                   "k_bwd_keys": _BWD, "k_sort_hist": _BWD, "k_sort_scan": _BWD, "k_sort_scatter": _BWD,
                   "k_bwd_chunks": _BWD, "k_bwd_cross": _BWD,
                   "k_dlrm_interact": ["rec_dlrm.hip", "rec_mfma.h"] + _COMMON}
+for _k in ("k_dinb_transpose", "k_dinb_clear", "k_dinb_sample", "k_dinb_wgrad", "k_dinb_reduce"):
+    KERNEL_SOURCES[_k] = ["rec_din_bwd.hip"] + _COMMON
 
 
 CAL_BYTES = 64 << 20            # bytes read (and written) by the calibration copy
@@ -130,7 +132,10 @@ KERNELS = {"k_din_attn": "k_din_attn",
            "k_towers_bf16": "k_towers_bf16", "k_hash_insert": "k_hash_insert",
            "k_bwd_keys": "k_bwd_keys", "k_sort_hist": "k_sort_hist", "k_sort_scan": "k_sort_scan",
            "k_sort_scatter": "k_sort_scatter", "k_bwd_chunks": "k_bwd_chunks",
-           "k_bwd_cross": "k_bwd_cross", "k_dlrm_interact": "k_dlrm_interact", "copy": "MulFunctor"}
+           "k_bwd_cross": "k_bwd_cross", "k_dlrm_interact": "k_dlrm_interact",
+           "k_dinb_transpose": "k_dinb_transpose", "k_dinb_clear": "k_dinb_clear",
+           "k_dinb_sample": "k_dinb_sample", "k_dinb_wgrad": "k_dinb_wgrad",
+           "k_dinb_reduce": "k_dinb_reduce", "copy": "MulFunctor"}
 
 
 def load_traffic(kernels, shash: str, config: str):
@@ -580,7 +585,9 @@ def main():
                    "flops_per_call": d_flops, "achieved_tflops": round(d_flops / (d_us * 1e-6) / 1e12, 2),
                    "peak": FP32_PEAK_TFLOPS, "frac": round(d_flops / (d_us * 1e-6) / 1e12 / FP32_PEAK_TFLOPS, 4),
                    "bound": "fp32 vector arithmetic, one 256-thread workgroup per sample (a first, "
-                            "correctness-first version: the products do not use the matrix cores yet)"}
+                            "correctness-first version: the products do not use the matrix cores yet)",
+                   "traffic": load_traffic(["k_dinb_transpose", "k_dinb_clear", "k_dinb_sample",
+                                            "k_dinb_wgrad", "k_dinb_reduce"], shash, cfg.name)}
         print(f"[bench] DIN attention backward: {d_us:.1f} us per call ({Pv:.0f} positions)",
               file=sys.stderr, flush=True)
         del gatt, gq, gs, wg, ws_d
