@@ -25,9 +25,10 @@
 //                  [x, 1], [h1, 1], [h2, 1], dz1, dz2 and de;
 //   k_dinb_wgrad   the weight gradients as sums over positions of outer
 //                  products, [dz1]^T [x, 1] (dW1 and db1), [dz2]^T [h1, 1]
-//                  (dW2 and db2), [de]^T [h2, 1] (dw3 and db3): 16 x 16
-//                  output tiles, the positions split in kDinbSplits ranges,
-//                  partial sums then added in split order by k_dinb_reduce.
+//                  (dW2 and db2), [de]^T [h2, 1] (dw3 and db3): 64 x 64
+//                  output tiles, blocks of positions staged in LDS, the
+//                  positions split in kDinbSplits ranges, partial sums then
+//                  added in split order by k_dinb_reduce.
 // Every sum has one order: results are bit-identical run to run.
 #include "rec_internal.h"
 
@@ -35,7 +36,7 @@ namespace rec {
 namespace {
 
 constexpr int kDinbThreads = 256;
-constexpr int kDinbSplits = 8;
+constexpr int kDinbSplits = 16;
 constexpr int kLdX = 193, kLdH1 = 257, kLdH2 = 65;       // rows carry a trailing 1
 constexpr int kJobs = 3;
 // job j: C[M][N] = sum_p A[p][m] Bm[p][n]
@@ -216,30 +217,73 @@ __global__ __launch_bounds__(kDinbThreads) void k_dinb_sample(DinBwdArgs a) {
     if (t < 48) a.gq[b * 48 + t] = accq;
 }
 
-// Weight gradients: block (tile, split).  Tiles of 16 x 16 outputs of the
-// three jobs in order; thread (tm, tn) owns output (16 tile_m + tm, 16 tile_n + tn).
+// Weight gradients: block (tile, split).  Tiles of 64 x 64 outputs of the
+// three jobs in order; thread (tm, tn) owns the 4 x 4 outputs (m0 + 4 tm + i,
+// n0 + 4 tn + j).  Blocks of kWB positions of A's and B's tile columns are
+// staged in LDS by coalesced loads (positions without a valid flag, and
+// columns past the edge, staged as zeros), then multiplied from LDS.
+constexpr int kWT = 64;
+constexpr int kWB = 32;
+
+__device__ inline int wgrad_tiles(int job) {
+    return ((kJobM[job] + kWT - 1) / kWT) * ((kJobN[job] + kWT - 1) / kWT);
+}
+
 __global__ __launch_bounds__(256) void k_dinb_wgrad(DinBwdArgs a, int64_t chunk) {
+    __shared__ __attribute__((aligned(16))) float As[kWB][kWT];
+    __shared__ __attribute__((aligned(16))) float Bs[kWB][kWT];
     const int t = threadIdx.x, tm = t >> 4, tn = t & 15;
     int tile = blockIdx.x, job = 0;
     for (; job < kJobs; ++job) {
-        const int nt = ((kJobM[job] + 15) / 16) * ((kJobN[job] + 15) / 16);
+        const int nt = wgrad_tiles(job);
         if (tile < nt) break;
         tile -= nt;
     }
     const int M = kJobM[job], N = kJobN[job];
-    const int ntn = (N + 15) / 16;
-    const int m = (tile / ntn) * 16 + tm, n = (tile % ntn) * 16 + tn;
+    const int ntn = (N + kWT - 1) / kWT;
+    const int m0 = (tile / ntn) * kWT, n0 = (tile % ntn) * kWT;
     const float* A = job == 0 ? a.DZ1 : job == 1 ? a.DZ2 : a.DE;
     const float* Bm = job == 0 ? a.X : job == 1 ? a.H1 : a.H2;
     const int64_t p0 = (int64_t)blockIdx.y * chunk;
     const int64_t p1 = p0 + chunk < a.seq_stride ? p0 + chunk : a.seq_stride;
-    float acc = 0.0f;
-    if (m < M && n < N) {
-        for (int64_t p = p0; p < p1; ++p)
-            if (a.valid[p]) acc += A[p * M + m] * Bm[p * N + n];
-        int64_t base = 0;
-        for (int j = 0; j < job; ++j) base += (int64_t)kJobM[j] * kJobN[j];
-        a.part[(int64_t)blockIdx.y * a.part_stride + base + (int64_t)m * N + n] = acc;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+    for (int64_t pb = p0; pb < p1; pb += kWB) {
+#pragma unroll
+        for (int u = 0; u < kWB * kWT / 256; ++u) {
+            const int e = t + u * 256, r = e / kWT, c = e - r * kWT;
+            const int64_t p = pb + r;
+            const bool ok = p < p1 && a.valid[p];
+            As[r][c] = (ok && m0 + c < M) ? A[p * M + m0 + c] : 0.0f;
+            Bs[r][c] = (ok && n0 + c < N) ? Bm[p * N + n0 + c] : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int r = 0; r < kWB; ++r) {
+            const float4 av = *(const float4*)&As[r][4 * tm];
+            const float4 bv = *(const float4*)&Bs[r][4 * tn];
+            const float ai[4] = {av.x, av.y, av.z, av.w}, bj[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] += ai[i] * bj[j];
+        }
+        __syncthreads();
+    }
+    int64_t base = 0;
+    for (int j = 0; j < job; ++j) base += (int64_t)kJobM[j] * kJobN[j];
+    float* out = a.part + (int64_t)blockIdx.y * a.part_stride + base;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 4 * tm + i;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = n0 + 4 * tn + j;
+            if (m < M && n < N) out[(int64_t)m * N + n] = acc[i][j];
+        }
     }
 }
 
@@ -277,7 +321,7 @@ hipError_t launch_din_bwd(const DinBwdArgs& a, hipStream_t s) {
     if (e != hipSuccess || !a.valid) return e;
     int tiles = 0;
     const int M[kJobs] = {256, 64, 1}, N[kJobs] = {kLdX, kLdH1, kLdH2};
-    for (int j = 0; j < kJobs; ++j) tiles += ((M[j] + 15) / 16) * ((N[j] + 15) / 16);
+    for (int j = 0; j < kJobs; ++j) tiles += ((M[j] + kWT - 1) / kWT) * ((N[j] + kWT - 1) / kWT);
     const int64_t chunk = (a.seq_stride + kDinbSplits - 1) / kDinbSplits;
     hipLaunchKernelGGL(k_dinb_wgrad, dim3((unsigned)tiles, kDinbSplits), dim3(256), 0, s, a, chunk);
     hipLaunchKernelGGL(k_dinb_reduce, dim3((unsigned)((a.part_stride + 255) / 256)), dim3(256), 0, s, a);
