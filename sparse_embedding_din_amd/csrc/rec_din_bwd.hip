@@ -94,19 +94,28 @@ __device__ inline void form_x(const float* q, const float* sj, float* xs, int t)
 }
 
 // h1 = relu(W1 x + b1) (thread t < 256 owns unit t), then h2 = relu(W2 h1 +
-// b2) (t < 64).  Ends with h1 and h2 in LDS, after a barrier.
-__device__ inline void mlp_fwd(const DinBwdArgs& a, const float* xs, float* h1, float* h2, int t) {
+// b2): unit o = t & 63, its 256 inputs split over the four waves (quarter
+// t >> 6), the four partial sums added in quarter order.  Ends with h1 and
+// h2 in LDS, after a barrier.  part holds 256 floats of scratch.
+__device__ inline void mlp_fwd(const DinBwdArgs& a, const float* xs, float* h1, float* h2,
+                               float* part, int t) {
     {
         float acc = a.b1 ? a.b1[t] : 0.0f;
-#pragma unroll 8
+#pragma unroll 16
         for (int i = 0; i < 192; ++i) acc += a.w1t[i * 256 + t] * xs[i];
         h1[t] = acc > 0.0f ? acc : 0.0f;
     }
     __syncthreads();
+    {
+        const int o = t & 63, i0 = (t >> 6) * 64;
+        float acc = 0.0f;
+#pragma unroll 16
+        for (int i = i0; i < i0 + 64; ++i) acc += a.w2t[i * 64 + o] * h1[i];
+        part[t] = acc;
+    }
+    __syncthreads();
     if (t < 64) {
-        float acc = a.b2 ? a.b2[t] : 0.0f;
-#pragma unroll 8
-        for (int i = 0; i < 256; ++i) acc += a.w2t[i * 64 + t] * h1[i];
+        const float acc = (a.b2 ? a.b2[t] : 0.0f) + ((part[t] + part[64 + t]) + (part[128 + t] + part[192 + t]));
         h2[t] = acc > 0.0f ? acc : 0.0f;
     }
     __syncthreads();
@@ -115,7 +124,7 @@ __device__ inline void mlp_fwd(const DinBwdArgs& a, const float* xs, float* h1, 
 __global__ __launch_bounds__(kDinbThreads) void k_dinb_sample(DinBwdArgs a) {
     __shared__ float q[48], g[48];
     __shared__ float sj[REC_MAX_SEQ_LEN][48];
-    __shared__ float xs[192], h1[256], h2[64], dz2[64], dz1[256], dx[192];
+    __shared__ float xs[192], h1[256], h2[64], dz2[64], dz1[256], dx[192], part[256];
     __shared__ float e[REC_MAX_SEQ_LEN], pw[REC_MAX_SEQ_LEN], dp[REC_MAX_SEQ_LEN], de[REC_MAX_SEQ_LEN];
     const int t = threadIdx.x;
     const int64_t b = blockIdx.x;
@@ -139,7 +148,7 @@ __global__ __launch_bounds__(kDinbThreads) void k_dinb_sample(DinBwdArgs a) {
     for (int j = 0; j < L; ++j) {
         form_x(q, sj[j], xs, t);
         __syncthreads();
-        mlp_fwd(a, xs, h1, h2, t);
+        mlp_fwd(a, xs, h1, h2, part, t);
         if (t == 0) {
             float s = a.b3;
             for (int o = 0; o < 64; ++o) s += a.w3[o] * h2[o];
@@ -172,7 +181,7 @@ __global__ __launch_bounds__(kDinbThreads) void k_dinb_sample(DinBwdArgs a) {
         const int64_t pos = off + j;
         form_x(q, sj[j], xs, t);
         __syncthreads();
-        mlp_fwd(a, xs, h1, h2, t);
+        mlp_fwd(a, xs, h1, h2, part, t);
         const float dej = de[j];
         if (t < 64) dz2[t] = h2[t] > 0.0f ? dej * a.w3[t] : 0.0f;
         if (a.valid) {                             // per-position rows for the weight gradients
@@ -189,7 +198,7 @@ __global__ __launch_bounds__(kDinbThreads) void k_dinb_sample(DinBwdArgs a) {
         __syncthreads();
         {
             float acc = 0.0f;
-#pragma unroll 8
+#pragma unroll 16
             for (int o = 0; o < 64; ++o) acc += wload(a.w2, (int64_t)o * 256 + t, a.bf16) * dz2[o];
             dz1[t] = h1[t] > 0.0f ? acc : 0.0f;
         }
@@ -198,7 +207,7 @@ __global__ __launch_bounds__(kDinbThreads) void k_dinb_sample(DinBwdArgs a) {
         if (a.valid) a.DZ1[pos * 256 + t] = dz1[t];
         if (t < 192) {
             float acc = 0.0f;
-#pragma unroll 8
+#pragma unroll 16
             for (int o = 0; o < 256; ++o) acc += wload(a.w1, (int64_t)o * 192 + t, a.bf16) * dz1[o];
             dx[t] = acc;
         }
