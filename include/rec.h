@@ -33,8 +33,10 @@
  *     offsets consistent with lengths; sequence runs in bounds of their
  *     arrays; hash tables laid out as described below.  Violations are
  *     undefined behaviour.
- *   - Results are deterministic: no atomics; the same inputs give bit-identical
- *     outputs run to run.
+ *   - Results are deterministic: the same inputs give bit-identical outputs run
+ *     to run.  No floating-point sum depends on the order of atomics; the one
+ *     entry point that uses atomics, rec_hash_insert (64-bit compare-and-swap
+ *     to claim empty slots), documents what its placement may depend on.
  */
 #ifndef REC_H
 #define REC_H
