@@ -429,7 +429,7 @@ rec_status rec_dlrm_interact(const float* z, int64_t B, int32_t F, int32_t d, fl
     if (F < 1) return fail(REC_EINVAL, "rec_dlrm_interact: F < 1");
     if (d < 16 || d % 16 != 0) return fail(REC_EINVAL, "rec_dlrm_interact: d must be a positive multiple of 16");
     if (F > 256 || d > 512) return fail(REC_EUNSUPPORTED, "rec_dlrm_interact: F above 256 or d above 512");
-    if ((int64_t)16 * ((F + 15) / 16) * dlrm_stride(d) > kDlrmMaxLdsFloats)
+    if ((int64_t)32 * ((F + 31) / 32) * dlrm_stride(d) > kDlrmMaxLdsFloats)
         return fail(REC_EUNSUPPORTED, "rec_dlrm_interact: F x d does not fit the 144 KiB LDS stage");
     if (B > 0 && (!z || !out)) return fail(REC_EINVAL, "rec_dlrm_interact: z or out is NULL");
     if (B > 0 && !aligned16(z)) return fail(REC_EINVAL, "rec_dlrm_interact: z not 16-byte aligned");

@@ -7,23 +7,26 @@
 // diagonal is included), §3.1 (the measured case: 217 features, width 96).
 //
 // On the matrix cores.  A sample's vectors form a small matrix Z [F][d] and
-// the output is the upper triangle of Z Z^T, so each 16 x 16 tile of it is a
-// run of v_mfma_f32_16x16x4f32 over d (fp32 in, fp32 accumulate; the fp32
-// matrix rate is twice the unpacked fp32 vector rate).  One workgroup per
-// sample, persistent over samples: Z is staged in LDS once, rows padded to a
-// multiple of 16 with zeros, with a row stride that puts the 16 rows of an
-// operand read on distinct banks; the T(T+1)/2 tile pairs I <= J of the
-// T = ceil(F / 16) row tiles are dealt to the eight waves in turn.  Both
-// operands want row m of their tile in lane (m, g) at lane group g's K
-// positions; giving lane group g the contiguous quarter [g d/4, (g+1) d/4) of
-// d (any K order is right when both operands use it) lets a lane read four K
-// steps with one 16-byte read, and those four steps feed four independent
-// accumulators, summed at the end.
+// the output is the upper triangle of Z Z^T, so each 32 x 32 tile of it is a
+// run of v_mfma_f32_32x32x2f32 over d (fp32 in, fp32 accumulate; the fp32
+// matrix rate is twice the unpacked fp32 vector rate, and the 32 x 32 shape
+// reads half the LDS operand bytes per flop of the 16 x 16 one).  One
+// workgroup per CU, persistent over samples: Z is staged in LDS, rows padded
+// to a multiple of 32 with zeros, with a row stride that spreads the rows of
+// an operand read over the banks; the next sample's Z rides in registers
+// while the current one is multiplied.  The T(T+1)/2 tile pairs I <= J of the
+// T = ceil(F / 32) row tiles are dealt to the eight waves in turn.  Both
+// operands want row m of their tile in lane (m, h) at lane half h's K
+// positions; giving half h the contiguous half [h d/2, (h+1) d/2) of d (any
+// K order is right when both operands use it) lets a lane read four K steps
+// with one 16-byte read, feeding two independent accumulators.
 #include "rec_internal.h"
 #include "rec_mfma.h"
 
 namespace rec {
 namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kDlrmWaves = 8;                  // two per SIMD: one wave's LDS waits hide behind the other's products
 // float4s per thread that hold a whole staged Z (the LDS stage's size)
@@ -34,15 +37,15 @@ __global__ __launch_bounds__(64 * kDlrmWaves) void k_dlrm_interact(const float* 
                                                                    float* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) float s_z[kDlrmMaxLdsFloats];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int m = lane & 15, g = lane >> 4;
-    const int T = (F + 15) / 16;
-    const int dq = d / 4;                       // a lane group's share of d (a multiple of 4)
+    const int m = lane & 31, h = lane >> 5;
+    const int T = (F + 31) / 32;
+    const int dh = d / 2;                       // a lane half's share of d (a multiple of 8)
     const int nv = d / 4;                       // float4s per row
     const int64_t npairs = (int64_t)F * (F + 1) / 2;
     const int ntile = T * (T + 1) / 2;
     // Z of the next sample travels in registers while the current one is
     // multiplied: thread t holds float4 t + q*256 of it (zeros past row F)
-    const int nvec = 16 * T * nv;
+    const int nvec = 32 * T * nv;
     float4 pre[kDlrmPrefetch];
     auto fetch = [&](int64_t bs) {
         const float4* src = (const float4*)(z + bs * (int64_t)F * d);
@@ -71,31 +74,30 @@ __global__ __launch_bounds__(64 * kDlrmWaves) void k_dlrm_interact(const float* 
                 ++I;
             }
             const int J = I + rem;
-            const float* ra = s_z + (I * 16 + m) * stride + g * dq;
-            const float* rb = s_z + (J * 16 + m) * stride + g * dq;
-            f32x4 acc[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const float* ra = s_z + (I * 32 + m) * stride + h * dh;
+            const float* rb = s_z + (J * 32 + m) * stride + h * dh;
+            f32x16 acc0 = {}, acc1 = {};
             // the next K step's operands are read before this step's products
             float4 av = *(const float4*)ra;
             float4 bv = *(const float4*)rb;
-            for (int k = 0; k < dq; k += 4) {
-                const int kn = k + 4 < dq ? k + 4 : k;
+            for (int k = 0; k < dh; k += 4) {
+                const int kn = k + 4 < dh ? k + 4 : k;
                 const float4 an = *(const float4*)(ra + kn);
                 const float4 bn = *(const float4*)(rb + kn);
-                acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, acc[0], 0, 0, 0);
-                acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, acc[1], 0, 0, 0);
-                acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, acc[2], 0, 0, 0);
-                acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, acc[3], 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.x, bv.x, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.y, bv.y, acc1, 0, 0, 0);
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.z, bv.z, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(av.w, bv.w, acc1, 0, 0, 0);
                 av = an;
                 bv = bn;
             }
-            const f32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-            // lane (m, g) holds rows 4g..4g+3 of the tile in column m
-            const int j = J * 16 + m;
+            const f32x16 sum = acc0 + acc1;
+            // register r of lane (m, h) holds row 8 (r / 4) + 4 h + r % 4 of
+            // the tile, column m
+            const int j = J * 32 + m;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = I * 16 + 4 * g + r;
+            for (int r = 0; r < 16; ++r) {
+                const int i = I * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (i < F && j < F && i <= j) {
                     const int64_t row = (int64_t)i * F - (int64_t)i * (i - 1) / 2;   // pairs before row i
                     out[b * npairs + row + (j - i)] = sum[r];

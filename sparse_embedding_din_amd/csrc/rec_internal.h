@@ -322,7 +322,7 @@ struct HashInsArgs {
 };
 hipError_t launch_hash_insert(const HashInsArgs& a, hipStream_t s);
 
-// DLRM interaction: Z staged in LDS as 16 * ceil(F / 16) rows of dlrm_stride(d)
+// DLRM interaction: Z staged in LDS as 32 * ceil(F / 32) rows of dlrm_stride(d)
 // floats, at most kDlrmMaxLdsFloats (144 KiB).
 constexpr int kDlrmMaxLdsFloats = 36864;
 int dlrm_stride(int d);
