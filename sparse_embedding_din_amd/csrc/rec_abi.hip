@@ -723,24 +723,28 @@ rec_status rec_embbag_adagrad(const rec_adagrad_table* tables, int32_t T, int64_
 namespace {
 
 struct DinBwdLayout {
-    size_t w1t, w2t, valid, X, H1, H2, DZ1, DZ2, DE, part, bytes;
+    size_t w1t, w2t, map, S, X, H1, H2, E, PW, DE, DZ1, DZ2, GQP, part, bytes;
 };
 
-// The transposed weights always; the per-position rows and the split sums
-// only with weight gradients.
+// The transposed weights and the per-position rows always; the split sums of
+// the weight gradients only when they are requested.
 DinBwdLayout din_bwd_layout(int64_t stride, bool weight_grads) {
     DinBwdLayout L;
-    const size_t n = weight_grads ? (size_t)stride : 0;
+    const size_t n = (size_t)stride;
     L.w1t = 0;
     L.w2t = L.w1t + round256(192 * 256 * 4);
-    L.valid = L.w2t + round256(256 * 64 * 4);
-    L.X = L.valid + round256(n);
+    L.map = L.w2t + round256(256 * 64 * 4);
+    L.S = L.map + round256(n * 4);
+    L.X = L.S + round256(n * 48 * 4);
     L.H1 = L.X + round256(n * 193 * 4);
     L.H2 = L.H1 + round256(n * 257 * 4);
-    L.DZ1 = L.H2 + round256(n * 65 * 4);
+    L.E = L.H2 + round256(n * 65 * 4);
+    L.PW = L.E + round256(n * 4);
+    L.DE = L.PW + round256(n * 4);
+    L.DZ1 = L.DE + round256(n * 4);
     L.DZ2 = L.DZ1 + round256(n * 256 * 4);
-    L.DE = L.DZ2 + round256(n * 64 * 4);
-    L.part = L.DE + round256(n * 4);
+    L.GQP = L.DZ2 + round256(n * 64 * 4);
+    L.part = L.GQP + round256(n * 48 * 4);
     L.bytes = L.part + (weight_grads ? round256((size_t)din_bwd_splits() * (size_t)din_bwd_part_stride() * 4) : 0);
     return L;
 }
@@ -809,14 +813,19 @@ rec_status rec_din_attn_bwd(const rec_table* seq_tables, const int64_t* seq_valu
     char* w = (char*)workspace;
     a.w1t = (float*)(w + L.w1t);
     a.w2t = (float*)(w + L.w2t);
+    a.map = (int32_t*)(w + L.map);
+    a.S = (float*)(w + L.S);
+    a.X = (float*)(w + L.X);
+    a.H1 = (float*)(w + L.H1);
+    a.H2 = (float*)(w + L.H2);
+    a.E = (float*)(w + L.E);
+    a.PW = (float*)(w + L.PW);
+    a.DE = (float*)(w + L.DE);
+    a.DZ1 = (float*)(w + L.DZ1);
+    a.DZ2 = (float*)(w + L.DZ2);
+    a.GQP = (float*)(w + L.GQP);
+    a.wgrad = nw == 6;
     if (nw == 6) {
-        a.valid = (uint8_t*)(w + L.valid);
-        a.X = (float*)(w + L.X);
-        a.H1 = (float*)(w + L.H1);
-        a.H2 = (float*)(w + L.H2);
-        a.DZ1 = (float*)(w + L.DZ1);
-        a.DZ2 = (float*)(w + L.DZ2);
-        a.DE = (float*)(w + L.DE);
         a.part = (float*)(w + L.part);
         a.part_stride = din_bwd_part_stride();
         a.dw1 = dw1;

@@ -58,7 +58,7 @@ __device__ inline float seq_elem(const TabDev& t, int64_t x, int d) {
 __global__ __launch_bounds__(256) void k_dinb_clear(DinBwdArgs a) {
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < a.seq_stride;
          p += (int64_t)gridDim.x * blockDim.x) {
-        if (a.valid) a.valid[p] = 0;
+        a.map[p] = -1;
         if (a.gs) {
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
@@ -84,146 +84,321 @@ __global__ __launch_bounds__(256) void k_dinb_transpose(DinBwdArgs a) {
     }
 }
 
-// x of position j (thread t < 192 forms x[t]) into xs.
-__device__ inline void form_x(const float* q, const float* sj, float* xs, int t) {
-    if (t < 192) {
-        const int blk = t / 48, c = t - blk * 48;
-        const float qc = q[c], sc = sj[c];
-        xs[t] = blk == 0 ? qc : blk == 1 ? sc : blk == 2 ? qc - sc : qc * sc;
+// Sample of every position index: map[p] = b for p = off_b + j, j < L_b.
+__global__ __launch_bounds__(256) void k_dinb_map(DinBwdArgs a) {
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < a.B;
+         b += (int64_t)gridDim.x * blockDim.x) {
+        const int32_t len = a.seq_lengths[b];
+        const int L = len < a.max_len ? len : a.max_len;
+        const int64_t off = a.seq_offsets[b];
+        for (int j = 0; j < L; ++j) a.map[off + j] = (int32_t)b;
     }
 }
 
-// h1 = relu(W1 x + b1) (thread t < 256 owns unit t), then h2 = relu(W2 h1 +
-// b2): unit o = t & 63, its 256 inputs split over the four waves (quarter
-// t >> 6), the four partial sums added in quarter order.  Ends with h1 and
-// h2 in LDS, after a barrier.  part holds 256 floats of scratch.
-__device__ inline void mlp_fwd(const DinBwdArgs& a, const float* xs, float* h1, float* h2,
-                               float* part, int t) {
-    {
-        float acc = a.b1 ? a.b1[t] : 0.0f;
-#pragma unroll 16
-        for (int i = 0; i < 192; ++i) acc += a.w1t[i * 256 + t] * xs[i];
-        h1[t] = acc > 0.0f ? acc : 0.0f;
+constexpr int kPT = 64;          // positions per tile
+constexpr int kXS = 196;         // LDS row stride of x / dx rows (192 + 4)
+constexpr int kHS = 260;         // LDS row stride of h1 / dz1 rows (256 + 4)
+constexpr int kWBF = 16 * 260;   // staged weight block (floats)
+
+struct TileLds {
+    float xs[kPT * kXS];         // x rows, later dz2 (stride 65) and dx rows
+    float hs[kPT * kHS];         // h1 rows, later dz1 rows
+    float wb[kWBF];              // a block of weight rows
+};
+
+__device__ inline void unpack16(const float* p, float* v) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const float4 x = *(const float4*)(p + 4 * u);
+        v[4 * u] = x.x; v[4 * u + 1] = x.y; v[4 * u + 2] = x.z; v[4 * u + 3] = x.w;
     }
-    __syncthreads();
-    {
-        const int o = t & 63, i0 = (t >> 6) * 64;
-        float acc = 0.0f;
-#pragma unroll 16
-        for (int i = i0; i < i0 + 64; ++i) acc += a.w2t[i * 64 + o] * h1[i];
-        part[t] = acc;
-    }
-    __syncthreads();
-    if (t < 64) {
-        const float acc = (a.b2 ? a.b2[t] : 0.0f) + ((part[t] + part[64 + t]) + (part[128 + t] + part[192 + t]));
-        h2[t] = acc > 0.0f ? acc : 0.0f;
-    }
-    __syncthreads();
 }
 
-__global__ __launch_bounds__(kDinbThreads) void k_dinb_sample(DinBwdArgs a) {
-    __shared__ float q[48], g[48];
-    __shared__ float sj[REC_MAX_SEQ_LEN][48];
-    __shared__ float xs[192], h1[256], h2[64], dz2[64], dz1[256], dx[192], part[256];
-    __shared__ float e[REC_MAX_SEQ_LEN], pw[REC_MAX_SEQ_LEN], dp[REC_MAX_SEQ_LEN], de[REC_MAX_SEQ_LEN];
-    const int t = threadIdx.x;
-    const int64_t b = blockIdx.x;
+// Forward of 64 positions: x (from the query of the position's sample and its
+// sequence row), h1 = relu(W1 x + b1), h2 = relu(W2 h1 + b2), the score; as
+// LDS-tiled products, each block of weight rows staged once for the tile.
+// Thread (pr, uc) = (t / 16, t % 16) owns positions 4 pr .. 4 pr + 3.
+__global__ __launch_bounds__(256) void k_dinb_fwd(DinBwdArgs a) {
+    __shared__ __attribute__((aligned(16))) TileLds L;
+    const int t = threadIdx.x, pr = t >> 4, uc = t & 15;
+    const int64_t p0 = (int64_t)blockIdx.x * kPT;
+    for (int idx = t; idx < kPT * 48; idx += 256) {
+        const int pi = idx / 48, c = idx - pi * 48, f = c >> 4;
+        const int64_t p = p0 + pi;
+        const int b = p < a.seq_stride ? a.map[p] : -1;
+        float sv = 0.0f, qv = 0.0f;
+        if (b >= 0) {
+            sv = seq_elem(a.tabs[f], a.seq_values[(int64_t)f * a.seq_stride + p], c & 15);
+            qv = a.query[(int64_t)b * a.query_ld + a.qcol[f] + (c & 15)];
+            a.S[p * 48 + c] = sv;
+        }
+        float* x = L.xs + pi * kXS;
+        x[c] = qv;
+        x[48 + c] = sv;
+        x[96 + c] = qv - sv;
+        x[144 + c] = qv * sv;
+    }
+    __syncthreads();
+    // h1: units 16 uc .. 16 uc + 15
+    float acc[4][16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float bj = a.b1 ? a.b1[16 * uc + j] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = bj;
+    }
+    for (int kb = 0; kb < 192; kb += 16) {
+        for (int e = t; e < 16 * 256; e += 256) {
+            const int kk = e >> 8, u = e & 255;
+            L.wb[kk * 260 + u] = a.w1t[(kb + kk) * 256 + u];
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < 16; ++kk) {
+            float xv[4], wv[16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[i] = L.xs[(4 * pr + i) * kXS + kb + kk];
+            unpack16(L.wb + kk * 260 + 16 * uc, wv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) acc[i][j] += xv[i] * wv[j];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) L.hs[(4 * pr + i) * kHS + 16 * uc + j] = acc[i][j] > 0.0f ? acc[i][j] : 0.0f;
+    __syncthreads();
+    // h2: units 4 uc .. 4 uc + 3
+    float a2[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float bj = a.b2 ? a.b2[4 * uc + j] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a2[i][j] = bj;
+    }
+    for (int kb = 0; kb < 256; kb += 64) {
+        for (int e = t; e < 64 * 64; e += 256) {
+            const int kk = e >> 6, u = e & 63;
+            L.wb[kk * 65 + u] = a.w2t[(kb + kk) * 64 + u];
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < 64; ++kk) {
+            float hv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hv[i] = L.hs[(4 * pr + i) * kHS + kb + kk];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float w = L.wb[kk * 65 + 4 * uc + j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a2[i][j] += hv[i] * w;
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float h2[4], part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            h2[j] = a2[i][j] > 0.0f ? a2[i][j] : 0.0f;
+            part += a.w3[4 * uc + j] * h2[j];
+        }
+        // the score's 64 terms: the 16 threads of these positions, a fixed tree
+        part += __shfl_xor(part, 8, 16);
+        part += __shfl_xor(part, 4, 16);
+        part += __shfl_xor(part, 2, 16);
+        part += __shfl_xor(part, 1, 16);
+        const int64_t p = p0 + 4 * pr + i;
+        if (p < a.seq_stride && a.map[p] >= 0) {
+            if (uc == 0) {
+                a.E[p] = a.b3 + part;
+                a.H2[p * kLdH2 + 64] = 1.0f;
+                a.H1[p * kLdH1 + 256] = 1.0f;
+                a.X[p * kLdX + 192] = 1.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a.H2[p * kLdH2 + 4 * uc + j] = h2[j];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) a.H1[p * kLdH1 + 16 * uc + j] = L.hs[(4 * pr + i) * kHS + 16 * uc + j];
+#pragma unroll
+            for (int j = 0; j < 12; ++j) a.X[p * kLdX + 12 * uc + j] = L.xs[(4 * pr + i) * kXS + 12 * uc + j];
+        }
+    }
+}
+
+// Softmax of each sample over its scores, one wave per sample: p_j,
+// dp_j = g . s_j and de_j = p_j (dp_j - sum_k p_k dp_k), reductions as
+// fixed shuffle trees.
+__global__ __launch_bounds__(256) void k_dinb_soft(DinBwdArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (b >= a.B) return;
     const int32_t len = a.seq_lengths[b];
     const int L = len < a.max_len ? len : a.max_len;
-    if (L <= 0) {                                  // att = 0 whatever q: no gradient
-        if (t < 48) a.gq[b * 48 + t] = 0.0f;
-        return;
-    }
+    if (L <= 0) return;
     const int64_t off = a.seq_offsets[b];
-    if (t < 48) {
-        q[t] = a.query[b * a.query_ld + a.qcol[t / 16] + (t & 15)];
-        g[t] = a.gatt[b * 48 + t];
+    const float* g = a.gatt + b * 48;
+    float e[2], dp[2];
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int j = lane + 64 * u;
+        e[u] = -INFINITY;
+        dp[u] = 0.0f;
+        if (j < L) {
+            const int64_t p = off + j;
+            e[u] = a.E[p];
+            float d = 0.0f;
+            for (int c = 0; c < 48; ++c) d += g[c] * a.S[p * 48 + c];
+            dp[u] = d;
+            m = fmaxf(m, e[u]);
+        }
     }
-    for (int idx = t; idx < L * 48; idx += kDinbThreads) {
-        const int j = idx / 48, c = idx - j * 48, f = c / 16;
-        sj[j][c] = seq_elem(a.tabs[f], a.seq_values[(int64_t)f * a.seq_stride + off + j], c & 15);
+    for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
+    float ex[2], den = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        ex[u] = lane + 64 * u < L ? expf(e[u] - m) : 0.0f;
+        den += ex[u];
+    }
+    for (int d = 32; d >= 1; d >>= 1) den += __shfl_xor(den, d, 64);
+    float pw[2], pdp = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        pw[u] = ex[u] / den;
+        pdp += pw[u] * dp[u];
+    }
+    for (int d = 32; d >= 1; d >>= 1) pdp += __shfl_xor(pdp, d, 64);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int j = lane + 64 * u;
+        if (j < L) {
+            a.PW[off + j] = pw[u];
+            a.DE[off + j] = pw[u] * (dp[u] - pdp);
+        }
+    }
+}
+
+// Backward of 64 positions: dz2 = de w3 where h2 > 0, dz1 = W2^T dz2 where
+// h1 > 0, dx = W1^T dz1 (LDS-tiled as the forward), then each position's
+// sequence-row gradient and its terms of the query gradient.
+__global__ __launch_bounds__(256) void k_dinb_bwdt(DinBwdArgs a) {
+    __shared__ __attribute__((aligned(16))) TileLds L;
+    const int t = threadIdx.x, pr = t >> 4, uc = t & 15;
+    const int64_t p0 = (int64_t)blockIdx.x * kPT;
+    float* d2 = L.xs;                               // dz2 rows, stride 65
+    for (int idx = t; idx < kPT * 64; idx += 256) {
+        const int pi = idx >> 6, o = idx & 63;
+        const int64_t p = p0 + pi;
+        const bool ok = p < a.seq_stride && a.map[p] >= 0;
+        const float v = (ok && a.H2[p * kLdH2 + o] > 0.0f) ? a.DE[p] * a.w3[o] : 0.0f;
+        d2[pi * 65 + o] = v;
+        if (ok && a.wgrad) a.DZ2[p * 64 + o] = v;
     }
     __syncthreads();
-    // scores
-    for (int j = 0; j < L; ++j) {
-        form_x(q, sj[j], xs, t);
+    // dz1: units 16 uc .. 16 uc + 15; W2 rows staged 16 at a time
+    float acc[4][16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
+    for (int kb = 0; kb < 64; kb += 16) {
+        for (int e = t; e < 16 * 256; e += 256) {
+            const int kk = e >> 8, u = e & 255;
+            L.wb[kk * 260 + u] = wload(a.w2, (int64_t)(kb + kk) * 256 + u, a.bf16);
+        }
         __syncthreads();
-        mlp_fwd(a, xs, h1, h2, part, t);
-        if (t == 0) {
-            float s = a.b3;
-            for (int o = 0; o < 64; ++o) s += a.w3[o] * h2[o];
-            e[j] = s;
+#pragma unroll 4
+        for (int kk = 0; kk < 16; ++kk) {
+            float dv[4], wv[16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dv[i] = d2[(4 * pr + i) * 65 + kb + kk];
+            unpack16(L.wb + kk * 260 + 16 * uc, wv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) acc[i][j] += dv[i] * wv[j];
         }
         __syncthreads();
     }
-    // softmax, dp_j = g . s_j, de_j (one thread: L <= 128, a fixed order)
-    if (t < L) {
-        float d = 0.0f;
-        for (int c = 0; c < 48; ++c) d += g[c] * sj[t][c];
-        dp[t] = d;
-    }
-    __syncthreads();
-    if (t == 0) {
-        float m = e[0];
-        for (int j = 1; j < L; ++j) m = fmaxf(m, e[j]);
-        float den = 0.0f;
-        for (int j = 0; j < L; ++j) den += expf(e[j] - m);
-        float pdp = 0.0f;
-        for (int j = 0; j < L; ++j) {
-            pw[j] = expf(e[j] - m) / den;
-            pdp += pw[j] * dp[j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t p = p0 + 4 * pr + i;
+        const bool ok = p < a.seq_stride && a.map[p] >= 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int u = 16 * uc + j;
+            const float v = (ok && a.H1[p * kLdH1 + u] > 0.0f) ? acc[i][j] : 0.0f;
+            L.hs[(4 * pr + i) * kHS + u] = v;
+            if (ok && a.wgrad) a.DZ1[p * 256 + u] = v;
         }
-        for (int j = 0; j < L; ++j) de[j] = pw[j] * (dp[j] - pdp);
     }
     __syncthreads();
-    float accq = 0.0f;
-    for (int j = 0; j < L; ++j) {
-        const int64_t pos = off + j;
-        form_x(q, sj[j], xs, t);
+    // dx: columns 12 uc .. 12 uc + 11; W1 rows staged 16 at a time (stride 196)
+    float ax[4][12];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 12; ++j) ax[i][j] = 0.0f;
+    for (int kb = 0; kb < 256; kb += 16) {
+        for (int e = t; e < 16 * 192; e += 256) {
+            const int kk = e / 192, c = e - kk * 192;
+            L.wb[kk * kXS + c] = wload(a.w1, (int64_t)(kb + kk) * 192 + c, a.bf16);
+        }
         __syncthreads();
-        mlp_fwd(a, xs, h1, h2, part, t);
-        const float dej = de[j];
-        if (t < 64) dz2[t] = h2[t] > 0.0f ? dej * a.w3[t] : 0.0f;
-        if (a.valid) {                             // per-position rows for the weight gradients
-            if (t < 192) a.X[pos * kLdX + t] = xs[t];
-            a.H1[pos * kLdH1 + t] = h1[t];
-            if (t < 64) a.H2[pos * kLdH2 + t] = h2[t];
-            if (t == 0) {
-                a.X[pos * kLdX + 192] = 1.0f;
-                a.H1[pos * kLdH1 + 256] = 1.0f;
-                a.H2[pos * kLdH2 + 64] = 1.0f;
-                a.DE[pos] = dej;
+#pragma unroll 4
+        for (int kk = 0; kk < 16; ++kk) {
+            float dv[4], wv[12];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dv[i] = L.hs[(4 * pr + i) * kHS + kb + kk];
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                const float4 x = *(const float4*)(L.wb + kk * kXS + 12 * uc + 4 * u);
+                wv[4 * u] = x.x; wv[4 * u + 1] = x.y; wv[4 * u + 2] = x.z; wv[4 * u + 3] = x.w;
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 12; ++j) ax[i][j] += dv[i] * wv[j];
         }
-        __syncthreads();
-        {
-            float acc = 0.0f;
-#pragma unroll 16
-            for (int o = 0; o < 64; ++o) acc += wload(a.w2, (int64_t)o * 256 + t, a.bf16) * dz2[o];
-            dz1[t] = h1[t] > 0.0f ? acc : 0.0f;
-        }
-        if (a.valid && t < 64) a.DZ2[pos * 64 + t] = dz2[t];
-        __syncthreads();
-        if (a.valid) a.DZ1[pos * 256 + t] = dz1[t];
-        if (t < 192) {
-            float acc = 0.0f;
-#pragma unroll 16
-            for (int o = 0; o < 256; ++o) acc += wload(a.w1, (int64_t)o * 192 + t, a.bf16) * dz1[o];
-            dx[t] = acc;
-        }
-        __syncthreads();
-        if (t < 48) {
-            const float sc = sj[j][t];
-            accq += dx[t] + dx[96 + t] + sc * dx[144 + t];
-            if (a.gs) {
-                const float ds = pw[j] * g[t] + dx[48 + t] - dx[96 + t] + q[t] * dx[144 + t];
-                a.gs[((int64_t)(t / 16) * a.seq_stride + pos) * REC_DIM + (t & 15)] = ds;
-            }
-        }
-        if (a.valid && t == 0) a.valid[pos] = 1;
         __syncthreads();
     }
-    if (t < 48) a.gq[b * 48 + t] = accq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 12; ++j) L.xs[(4 * pr + i) * kXS + 12 * uc + j] = ax[i][j];
+    __syncthreads();
+    for (int idx = t; idx < kPT * 48; idx += 256) {
+        const int pi = idx / 48, c = idx - pi * 48;
+        const int64_t p = p0 + pi;
+        const int b = p < a.seq_stride ? a.map[p] : -1;
+        if (b < 0) continue;
+        const float* dx = L.xs + pi * kXS;
+        const float sv = a.S[p * 48 + c];
+        const float qv = a.query[(int64_t)b * a.query_ld + a.qcol[c >> 4] + (c & 15)];
+        if (a.gs)
+            a.gs[((int64_t)(c >> 4) * a.seq_stride + p) * REC_DIM + (c & 15)] =
+                a.PW[p] * a.gatt[(int64_t)b * 48 + c] + dx[48 + c] - dx[96 + c] + qv * dx[144 + c];
+        a.GQP[p * 48 + c] = dx[c] + dx[96 + c] + sv * dx[144 + c];
+    }
+}
+
+// Query gradient: each sample's position terms added in position order.
+__global__ __launch_bounds__(256) void k_dinb_gq(DinBwdArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= a.B * 48) return;
+    const int64_t b = i / 48;
+    const int c = (int)(i - b * 48);
+    const int32_t len = a.seq_lengths[b];
+    const int L = len < a.max_len ? len : a.max_len;
+    const int64_t off = a.seq_offsets[b];
+    float s = 0.0f;
+    for (int j = 0; j < L; ++j) s += a.GQP[(off + j) * 48 + c];
+    a.gq[i] = s;
 }
 
 // Weight gradients: block (tile, split).  Tiles of 64 x 64 outputs of the
@@ -265,7 +440,7 @@ __global__ __launch_bounds__(256) void k_dinb_wgrad(DinBwdArgs a, int64_t chunk)
         for (int u = 0; u < kWB * kWT / 256; ++u) {
             const int e = t + u * 256, r = e / kWT, c = e - r * kWT;
             const int64_t p = pb + r;
-            const bool ok = p < p1 && a.valid[p];
+            const bool ok = p < p1 && a.map[p] >= 0;
             As[r][c] = (ok && m0 + c < M) ? A[p * M + m0 + c] : 0.0f;
             Bs[r][c] = (ok && n0 + c < N) ? Bm[p * N + n0 + c] : 0.0f;
         }
@@ -325,14 +500,20 @@ hipError_t launch_din_bwd(const DinBwdArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(k_dinb_clear, dim3((unsigned)(cgrid < 65536 ? cgrid : 65536)), dim3(256), 0, s, a);
     }
     hipLaunchKernelGGL(k_dinb_transpose, dim3((256 * 192 + 64 * 256 + 255) / 256), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_dinb_sample, dim3((unsigned)a.B), dim3(kDinbThreads), 0, s, a);
+    const int64_t bgrid = (a.B + 255) / 256;
+    hipLaunchKernelGGL(k_dinb_map, dim3((unsigned)(bgrid < 65536 ? bgrid : 65536)), dim3(256), 0, s, a);
+    const int64_t tiles = (a.seq_stride + kPT - 1) / kPT;
+    if (tiles > 0) hipLaunchKernelGGL(k_dinb_fwd, dim3((unsigned)tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_dinb_soft, dim3((unsigned)((a.B + 3) / 4)), dim3(256), 0, s, a);
+    if (tiles > 0) hipLaunchKernelGGL(k_dinb_bwdt, dim3((unsigned)tiles), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_dinb_gq, dim3((unsigned)((a.B * 48 + 255) / 256)), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !a.valid) return e;
-    int tiles = 0;
+    if (e != hipSuccess || !a.wgrad) return e;
+    int ntiles = 0;
     const int M[kJobs] = {256, 64, 1}, N[kJobs] = {kLdX, kLdH1, kLdH2};
-    for (int j = 0; j < kJobs; ++j) tiles += ((M[j] + kWT - 1) / kWT) * ((N[j] + kWT - 1) / kWT);
+    for (int j = 0; j < kJobs; ++j) ntiles += ((M[j] + kWT - 1) / kWT) * ((N[j] + kWT - 1) / kWT);
     const int64_t chunk = (a.seq_stride + kDinbSplits - 1) / kDinbSplits;
-    hipLaunchKernelGGL(k_dinb_wgrad, dim3((unsigned)tiles, kDinbSplits), dim3(256), 0, s, a, chunk);
+    hipLaunchKernelGGL(k_dinb_wgrad, dim3((unsigned)ntiles, kDinbSplits), dim3(256), 0, s, a, chunk);
     hipLaunchKernelGGL(k_dinb_reduce, dim3((unsigned)((a.part_stride + 255) / 256)), dim3(256), 0, s, a);
     return hipGetLastError();
 }

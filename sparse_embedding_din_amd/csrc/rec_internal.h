@@ -389,9 +389,12 @@ struct DinBwdArgs {
     float* gs;                    // [3][seq_stride][16] or NULL
     float* w1t;                   // [192][256] fp32 workspace
     float* w2t;                   // [256][64] fp32 workspace
-    // weight gradients (valid == NULL: not requested)
-    uint8_t* valid;               // [seq_stride]
-    float *X, *H1, *H2, *DZ1, *DZ2, *DE;
+    // per position index (workspace): its sample (-1: no position), the
+    // sequence row, [x, 1], [h1, 1], [h2, 1], the score, the softmax weight,
+    // de, dz1, dz2 and the query-gradient terms
+    int32_t* map;
+    float *S, *X, *H1, *H2, *E, *PW, *DE, *DZ1, *DZ2, *GQP;
+    int32_t wgrad;                // weight gradients requested
     float* part;                  // [splits][part_stride]
     int64_t part_stride;
     float *dw1, *db1, *dw2, *db2, *dw3, *db3;
