@@ -128,7 +128,8 @@ KERNEL_SOURCES = {"k_din_attn": _FWD, "k_embbag_fwd": _FWD, "k_fwd_gather": _FWD
                   "k_bwd_keys": _BWD, "k_sort_hist": _BWD, "k_sort_scan": _BWD, "k_sort_scatter": _BWD,
                   "k_bwd_chunks": _BWD, "k_bwd_cross": _BWD,
                   "k_dlrm_interact": ["rec_dlrm.hip", "rec_mfma.h"] + _COMMON}
-for _k in ("k_dinb_transpose", "k_dinb_clear", "k_dinb_sample", "k_dinb_wgrad", "k_dinb_reduce"):
+for _k in ("k_dinb_transpose", "k_dinb_clear", "k_dinb_map", "k_dinb_fwd", "k_dinb_soft", "k_dinb_bwdt",
+           "k_dinb_gq", "k_dinb_wgrad", "k_dinb_reduce"):
     KERNEL_SOURCES[_k] = ["rec_din_bwd.hip"] + _COMMON
 
 
@@ -140,7 +141,8 @@ KERNELS = {"k_din_attn": "k_din_attn",
            "k_sort_scatter": "k_sort_scatter", "k_bwd_chunks": "k_bwd_chunks",
            "k_bwd_cross": "k_bwd_cross", "k_dlrm_interact": "k_dlrm_interact",
            "k_dinb_transpose": "k_dinb_transpose", "k_dinb_clear": "k_dinb_clear",
-           "k_dinb_sample": "k_dinb_sample", "k_dinb_wgrad": "k_dinb_wgrad",
+           "k_dinb_map": "k_dinb_map", "k_dinb_fwd": "k_dinb_fwd", "k_dinb_soft": "k_dinb_soft",
+           "k_dinb_bwdt": "k_dinb_bwdt", "k_dinb_gq": "k_dinb_gq", "k_dinb_wgrad": "k_dinb_wgrad",
            "k_dinb_reduce": "k_dinb_reduce", "copy": "MulFunctor"}
 
 
@@ -633,16 +635,17 @@ def main():
         d = np.array([s_.elapsed_time(e_) * 1e3 for s_, e_ in evs])
         d_us = float(d.mean())
         Pv = float(np.minimum(b0.seq_lengths, cfg.max_len).sum())
-        # per position: the forward again (scores), the forward once more with
-        # the backward's three products, and the two weight-gradient products
-        d_flops = Pv * (2 * DIN_FLOPS_PER_POS + 2 * (64 * 256 + 256 * 192) + 2 * (256 * 193 + 64 * 257 + 65))
+        # per position: the forward once (kept for the backward), the
+        # backward's two products, and the weight-gradient products
+        d_flops = Pv * (DIN_FLOPS_PER_POS + 2 * (64 * 256 + 256 * 192) + 2 * (256 * 193 + 64 * 257 + 65))
         din_bwd = {"entry": "rec_din_attn_bwd (query, sequence-row and MLP weight gradients)",
                    "avg_call_us": round(d_us, 2), "positions": Pv, "samples": B,
                    "flops_per_call": d_flops, "achieved_tflops": round(d_flops / (d_us * 1e-6) / 1e12, 2),
                    "peak": FP32_PEAK_TFLOPS, "frac": round(d_flops / (d_us * 1e-6) / 1e12 / FP32_PEAK_TFLOPS, 4),
-                   "bound": "fp32 vector arithmetic, one 256-thread workgroup per sample (a first, "
-                            "correctness-first version: the products do not use the matrix cores yet)",
-                   "traffic": load_traffic(["k_dinb_transpose", "k_dinb_clear", "k_dinb_sample",
+                   "bound": "fp32 vector arithmetic: LDS-tiled products over 64-position tiles "
+                            "(the matrix cores are not used yet)",
+                   "traffic": load_traffic(["k_dinb_transpose", "k_dinb_clear", "k_dinb_map",
+                                            "k_dinb_fwd", "k_dinb_soft", "k_dinb_bwdt", "k_dinb_gq",
                                             "k_dinb_wgrad", "k_dinb_reduce"], shash, cfg.name)}
         print(f"[bench] DIN attention backward: {d_us:.1f} us per call ({Pv:.0f} positions)",
               file=sys.stderr, flush=True)
