@@ -36,7 +36,7 @@ namespace rec {
 namespace {
 
 constexpr int kDinbThreads = 256;
-constexpr int kDinbSplits = 16;
+constexpr int kDinbSplits = 64;
 constexpr int kLdX = 193, kLdH1 = 257, kLdH2 = 65;       // rows carry a trailing 1
 constexpr int kJobs = 3;
 // job j: C[M][N] = sum_p A[p][m] Bm[p][n]
