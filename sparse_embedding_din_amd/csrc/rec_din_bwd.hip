@@ -35,7 +35,6 @@
 namespace rec {
 namespace {
 
-constexpr int kDinbThreads = 256;
 constexpr int kDinbSplits = 64;
 constexpr int kLdX = 193, kLdH1 = 257, kLdH2 = 65;       // rows carry a trailing 1
 constexpr int kJobs = 3;
@@ -95,7 +94,8 @@ __global__ __launch_bounds__(256) void k_dinb_map(DinBwdArgs a) {
     }
 }
 
-constexpr int kPT = 64;          // positions per tile
+constexpr int kPT = 32;          // positions per tile (two tiles' LDS fit a CU)
+constexpr int kPPT = kPT / 16;   // positions per thread
 constexpr int kXS = 196;         // LDS row stride of x / dx rows (192 + 4)
 constexpr int kHS = 260;         // LDS row stride of h1 / dz1 rows (256 + 4)
 constexpr int kWBF = 16 * 260;   // staged weight block (floats)
@@ -114,10 +114,10 @@ __device__ inline void unpack16(const float* p, float* v) {
     }
 }
 
-// Forward of 64 positions: x (from the query of the position's sample and its
+// Forward of kPT positions: x (from the query of the position's sample and its
 // sequence row), h1 = relu(W1 x + b1), h2 = relu(W2 h1 + b2), the score; as
 // LDS-tiled products, each block of weight rows staged once for the tile.
-// Thread (pr, uc) = (t / 16, t % 16) owns positions 4 pr .. 4 pr + 3.
+// Thread (pr, uc) = (t / 16, t % 16) owns positions kPPT pr .. kPPT pr + kPPT - 1.
 __global__ __launch_bounds__(256) void k_dinb_fwd(DinBwdArgs a) {
     __shared__ __attribute__((aligned(16))) TileLds L;
     const int t = threadIdx.x, pr = t >> 4, uc = t & 15;
@@ -140,12 +140,12 @@ __global__ __launch_bounds__(256) void k_dinb_fwd(DinBwdArgs a) {
     }
     __syncthreads();
     // h1: units 16 uc .. 16 uc + 15
-    float acc[4][16];
+    float acc[kPPT][16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const float bj = a.b1 ? a.b1[16 * uc + j] : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][j] = bj;
+        for (int i = 0; i < kPPT; ++i) acc[i][j] = bj;
     }
     for (int kb = 0; kb < 192; kb += 16) {
         for (int e = t; e < 16 * 256; e += 256) {
@@ -155,29 +155,29 @@ __global__ __launch_bounds__(256) void k_dinb_fwd(DinBwdArgs a) {
         __syncthreads();
 #pragma unroll 4
         for (int kk = 0; kk < 16; ++kk) {
-            float xv[4], wv[16];
+            float xv[kPPT], wv[16];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xv[i] = L.xs[(4 * pr + i) * kXS + kb + kk];
+            for (int i = 0; i < kPPT; ++i) xv[i] = L.xs[(kPPT * pr + i) * kXS + kb + kk];
             unpack16(L.wb + kk * 260 + 16 * uc, wv);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kPPT; ++i)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) acc[i][j] += xv[i] * wv[j];
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kPPT; ++i)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) L.hs[(4 * pr + i) * kHS + 16 * uc + j] = acc[i][j] > 0.0f ? acc[i][j] : 0.0f;
+        for (int j = 0; j < 16; ++j) L.hs[(kPPT * pr + i) * kHS + 16 * uc + j] = acc[i][j] > 0.0f ? acc[i][j] : 0.0f;
     __syncthreads();
     // h2: units 4 uc .. 4 uc + 3
-    float a2[4][4];
+    float a2[kPPT][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const float bj = a.b2 ? a.b2[4 * uc + j] : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a2[i][j] = bj;
+        for (int i = 0; i < kPPT; ++i) a2[i][j] = bj;
     }
     for (int kb = 0; kb < 256; kb += 64) {
         for (int e = t; e < 64 * 64; e += 256) {
@@ -187,20 +187,20 @@ __global__ __launch_bounds__(256) void k_dinb_fwd(DinBwdArgs a) {
         __syncthreads();
 #pragma unroll 4
         for (int kk = 0; kk < 64; ++kk) {
-            float hv[4];
+            float hv[kPPT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) hv[i] = L.hs[(4 * pr + i) * kHS + kb + kk];
+            for (int i = 0; i < kPPT; ++i) hv[i] = L.hs[(kPPT * pr + i) * kHS + kb + kk];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float w = L.wb[kk * 65 + 4 * uc + j];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) a2[i][j] += hv[i] * w;
+                for (int i = 0; i < kPPT; ++i) a2[i][j] += hv[i] * w;
             }
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kPPT; ++i) {
         float h2[4], part = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256) void k_dinb_fwd(DinBwdArgs a) {
         part += __shfl_xor(part, 4, 16);
         part += __shfl_xor(part, 2, 16);
         part += __shfl_xor(part, 1, 16);
-        const int64_t p = p0 + 4 * pr + i;
+        const int64_t p = p0 + kPPT * pr + i;
         if (p < a.seq_stride && a.map[p] >= 0) {
             if (uc == 0) {
                 a.E[p] = a.b3 + part;
@@ -223,9 +223,9 @@ __global__ __launch_bounds__(256) void k_dinb_fwd(DinBwdArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) a.H2[p * kLdH2 + 4 * uc + j] = h2[j];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) a.H1[p * kLdH1 + 16 * uc + j] = L.hs[(4 * pr + i) * kHS + 16 * uc + j];
+            for (int j = 0; j < 16; ++j) a.H1[p * kLdH1 + 16 * uc + j] = L.hs[(kPPT * pr + i) * kHS + 16 * uc + j];
 #pragma unroll
-            for (int j = 0; j < 12; ++j) a.X[p * kLdX + 12 * uc + j] = L.xs[(4 * pr + i) * kXS + 12 * uc + j];
+            for (int j = 0; j < 12; ++j) a.X[p * kLdX + 12 * uc + j] = L.xs[(kPPT * pr + i) * kXS + 12 * uc + j];
         }
     }
 }
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void k_dinb_soft(DinBwdArgs a) {
     }
 }
 
-// Backward of 64 positions: dz2 = de w3 where h2 > 0, dz1 = W2^T dz2 where
+// Backward of kPT positions: dz2 = de w3 where h2 > 0, dz1 = W2^T dz2 where
 // h1 > 0, dx = W1^T dz1 (LDS-tiled as the forward), then each position's
 // sequence-row gradient and its terms of the query gradient.
 __global__ __launch_bounds__(256) void k_dinb_bwdt(DinBwdArgs a) {
@@ -301,9 +301,9 @@ __global__ __launch_bounds__(256) void k_dinb_bwdt(DinBwdArgs a) {
     }
     __syncthreads();
     // dz1: units 16 uc .. 16 uc + 15; W2 rows staged 16 at a time
-    float acc[4][16];
+    float acc[kPPT][16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kPPT; ++i)
 #pragma unroll
         for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
     for (int kb = 0; kb < 64; kb += 16) {
@@ -314,34 +314,34 @@ __global__ __launch_bounds__(256) void k_dinb_bwdt(DinBwdArgs a) {
         __syncthreads();
 #pragma unroll 4
         for (int kk = 0; kk < 16; ++kk) {
-            float dv[4], wv[16];
+            float dv[kPPT], wv[16];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dv[i] = d2[(4 * pr + i) * 65 + kb + kk];
+            for (int i = 0; i < kPPT; ++i) dv[i] = d2[(kPPT * pr + i) * 65 + kb + kk];
             unpack16(L.wb + kk * 260 + 16 * uc, wv);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kPPT; ++i)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) acc[i][j] += dv[i] * wv[j];
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t p = p0 + 4 * pr + i;
+    for (int i = 0; i < kPPT; ++i) {
+        const int64_t p = p0 + kPPT * pr + i;
         const bool ok = p < a.seq_stride && a.map[p] >= 0;
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int u = 16 * uc + j;
             const float v = (ok && a.H1[p * kLdH1 + u] > 0.0f) ? acc[i][j] : 0.0f;
-            L.hs[(4 * pr + i) * kHS + u] = v;
+            L.hs[(kPPT * pr + i) * kHS + u] = v;
             if (ok && a.wgrad) a.DZ1[p * 256 + u] = v;
         }
     }
     __syncthreads();
     // dx: columns 12 uc .. 12 uc + 11; W1 rows staged 16 at a time (stride 196)
-    float ax[4][12];
+    float ax[kPPT][12];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kPPT; ++i)
 #pragma unroll
         for (int j = 0; j < 12; ++j) ax[i][j] = 0.0f;
     for (int kb = 0; kb < 256; kb += 16) {
@@ -352,25 +352,25 @@ __global__ __launch_bounds__(256) void k_dinb_bwdt(DinBwdArgs a) {
         __syncthreads();
 #pragma unroll 4
         for (int kk = 0; kk < 16; ++kk) {
-            float dv[4], wv[12];
+            float dv[kPPT], wv[12];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dv[i] = L.hs[(4 * pr + i) * kHS + kb + kk];
+            for (int i = 0; i < kPPT; ++i) dv[i] = L.hs[(kPPT * pr + i) * kHS + kb + kk];
 #pragma unroll
             for (int u = 0; u < 3; ++u) {
                 const float4 x = *(const float4*)(L.wb + kk * kXS + 12 * uc + 4 * u);
                 wv[4 * u] = x.x; wv[4 * u + 1] = x.y; wv[4 * u + 2] = x.z; wv[4 * u + 3] = x.w;
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kPPT; ++i)
 #pragma unroll
                 for (int j = 0; j < 12; ++j) ax[i][j] += dv[i] * wv[j];
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kPPT; ++i)
 #pragma unroll
-        for (int j = 0; j < 12; ++j) L.xs[(4 * pr + i) * kXS + 12 * uc + j] = ax[i][j];
+        for (int j = 0; j < 12; ++j) L.xs[(kPPT * pr + i) * kXS + 12 * uc + j] = ax[i][j];
     __syncthreads();
     for (int idx = t; idx < kPT * 48; idx += 256) {
         const int pi = idx / 48, c = idx - pi * 48;
