@@ -642,7 +642,7 @@ def main():
                    "avg_call_us": round(d_us, 2), "positions": Pv, "samples": B,
                    "flops_per_call": d_flops, "achieved_tflops": round(d_flops / (d_us * 1e-6) / 1e12, 2),
                    "peak": FP32_PEAK_TFLOPS, "frac": round(d_flops / (d_us * 1e-6) / 1e12 / FP32_PEAK_TFLOPS, 4),
-                   "bound": "fp32 vector arithmetic: LDS-tiled products over 64-position tiles "
+                   "bound": "fp32 vector arithmetic: LDS-tiled products over 32-position tiles "
                             "(the matrix cores are not used yet)",
                    "traffic": load_traffic(["k_dinb_transpose", "k_dinb_clear", "k_dinb_map",
                                             "k_dinb_fwd", "k_dinb_soft", "k_dinb_bwdt", "k_dinb_gq",
