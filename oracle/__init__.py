@@ -86,7 +86,7 @@ class Oracle:
         L.orc_embbag_adagrad.restype = C.c_int64
         L.orc_din_bwd.argtypes = [C.POINTER(OrcTable), P64, C.c_int64, P64, P32, C.c_int32,
                                   C.c_int64, PD, PD, PD, PD, PD, PD, C.c_double, PD, PD, PD,
-                                  PD, PD, PD, PD, PD, PD, PD, PD]
+                                  PD, PD, PD, PD, PD, PD, PD, PD, PD]
         L.orc_din_bwd.restype = None
         self._keep = []
 
@@ -186,13 +186,17 @@ class Oracle:
         return cut(w), cut(G), cut(grad), cut(touched.astype(bool))
 
     def din_bwd(self, seq_tabs, seq_values, seq_stride, seq_offsets, seq_lengths, max_len, query,
-                w1, b1, w2, b2, w3, b3, gatt, wrapped=None):
+                w1, b1, w2, b2, w3, b3, gatt, wrapped=None, gates=False):
         """Backward of the DIN attention for all B samples given the gradient
         of its output gatt [B][48].  Returns a dict of fp64 arrays: gq [B][48],
         gs [seq_stride][48] (by position index), dw1 [256][192], db1 [256],
         dw2 [64][256], db2 [64], dw3 [64], db3 (a float), db3_scale (sum |de_j|,
         the size of db3's terms: db3 itself is zero up to rounding), gq_scale
-        [B][48] (the size of each query-gradient entry's terms)."""
+        [B][48] (the size of each query-gradient entry's terms).  With gates,
+        also r1 [seq_stride][256] = z1 / (the size of z1's terms), v1
+        [seq_stride][256] = W2^T dz2 before the first ReLU gate, r2
+        [seq_stride][64] = z2 / (the size of its terms): the ReLU gates within
+        rounding of zero, where either derivative is valid."""
         seq_values = np.ascontiguousarray(seq_values, dtype=np.int64)
         seq_offsets = np.ascontiguousarray(seq_offsets, dtype=np.int64)
         seq_lengths = np.ascontiguousarray(seq_lengths, dtype=np.int32)
@@ -206,11 +210,15 @@ class Oracle:
                    dw1=np.zeros((256, 192)), db1=np.zeros(256), dw2=np.zeros((64, 256)),
                    db2=np.zeros(64), dw3=np.zeros(64), db3=np.zeros(1), db3_scale=np.zeros(1),
                    gq_scale=np.empty((B, 48)))
+        gate = np.empty((int(seq_stride), 576)) if gates else None
         self.lib.orc_din_bwd(arr, _ptr(seq_values, P64), int(seq_stride), _ptr(seq_offsets, P64),
                              _ptr(seq_lengths, P32), int(max_len), B, _ptr(q, PD),
                              *[_ptr(x, PD) for x in d], float(b3), _ptr(g, PD),
                              *[_ptr(out[k], PD) for k in ("gq", "gs", "dw1", "db1", "dw2", "db2",
-                                                          "dw3", "db3", "db3_scale", "gq_scale")])
+                                                          "dw3", "db3", "db3_scale", "gq_scale")],
+                             _ptr(gate, PD) if gates else None)
+        if gates:
+            out["r1"], out["v1"], out["r2"] = gate[:, :256], gate[:, 256:512], gate[:, 512:]
         out["db3"] = float(out["db3"][0])
         out["db3_scale"] = float(out["db3_scale"][0])
         return out

@@ -438,14 +438,21 @@ void orc_din(const orc_table* seq_tables /* 3: adgroup, cate, brand */,
  * terms and the de_j sum to zero), gets gq_scale [B][48]: the chain above run
  * on the sizes of the terms instead of their values (a running-error bound
  * of the kind Higham, "Accuracy and Stability of Numerical Algorithms", §3,
- * uses for sums and products).  Returns nothing. */
+ * uses for sums and products).  The ReLU gates of the chain (z > 0) are
+ * decided in fp64; a z within a few roundings of zero may fall the other way
+ * in a lower precision, and the derivative of ReLU at 0 is not fixed by the
+ * method, so either decision is valid there.  For checking such units, gate
+ * (or NULL) receives per position index [seq_stride][576]: z1_j / a1_j
+ * (256; a1_j = |b1| + sum_i |W1[u][i] x_j[i]|, the size of z1's terms), dh1_j
+ * = W2^T dz2_j before its gate (256), and z2_j / a2_j (64, a2_j likewise).
+ * Returns nothing. */
 void orc_din_bwd(const orc_table* seq_tables, const int64_t* seq_values, int64_t seq_stride,
                  const int64_t* seq_offsets, const int32_t* seq_lengths, int32_t max_len,
                  int64_t B, const double* query, const double* w1, const double* b1,
                  const double* w2, const double* b2, const double* w3, double b3,
                  const double* gatt, double* gq, double* gs, double* dw1, double* db1,
                  double* dw2, double* db2, double* dw3, double* db3, double* db3_scale,
-                 double* gq_scale) {
+                 double* gq_scale, double* gate) {
     const int64_t ml = max_len > 0 ? max_len : 1;
     double* sj = (double*)malloc(sizeof(double) * 48 * (size_t)ml);
     double* xs = (double*)malloc(sizeof(double) * 192 * (size_t)ml);
@@ -455,6 +462,8 @@ void orc_din_bwd(const orc_table* seq_tables, const int64_t* seq_values, int64_t
     double* p = (double*)malloc(sizeof(double) * (size_t)ml);
     double* dp = (double*)malloc(sizeof(double) * (size_t)ml);
     for (int64_t i = 0; i < seq_stride * 48; ++i) gs[i] = 0.0;
+    if (gate)
+        for (int64_t i = 0; i < seq_stride * 576; ++i) gate[i] = 0.0;
     for (int64_t b = 0; b < B; ++b) {
         const int64_t L = seq_lengths[b] < max_len ? seq_lengths[b] : max_len;
         const double* q = query + b * 48;
@@ -519,12 +528,27 @@ void orc_din_bwd(const orc_table* seq_tables, const int64_t* seq_values, int64_t
                 for (int i = 0; i < 256; ++i)
                     dw2[o * 256 + i] += dz2[o] * (z1[j * 256 + i] > 0.0 ? z1[j * 256 + i] : 0.0);
             }
+            double* gt = gate ? gate + (seq_offsets[b] + j) * 576 : NULL;
             for (int i = 0; i < 256; ++i) {
                 double a = 0.0;
                 for (int o = 0; o < 64; ++o) a += w2[o * 256 + i] * dz2[o];
                 dz1[i] = z1[j * 256 + i] > 0.0 ? a : 0.0;
+                if (gt) gt[256 + i] = a;
             }
             const double* x = xs + j * 192;
+            if (gt) {
+                for (int o = 0; o < 256; ++o) {
+                    double a1 = fabs(b1[o]);
+                    for (int i = 0; i < 192; ++i) a1 += fabs(w1[o * 192 + i] * x[i]);
+                    gt[o] = a1 > 0.0 ? z1[j * 256 + o] / a1 : 0.0;
+                }
+                for (int o = 0; o < 64; ++o) {
+                    double a2 = fabs(b2[o]);
+                    for (int i = 0; i < 256; ++i)
+                        a2 += fabs(w2[o * 256 + i] * (z1[j * 256 + i] > 0.0 ? z1[j * 256 + i] : 0.0));
+                    gt[512 + o] = a2 > 0.0 ? z2[j * 64 + o] / a2 : 0.0;
+                }
+            }
             for (int o = 0; o < 256; ++o) {
                 db1[o] += dz1[o];
                 for (int i = 0; i < 192; ++i) dw1[o * 192 + i] += dz1[o] * x[i];

@@ -684,20 +684,33 @@ def _torch_din_grads(model, batch, query, seq_offsets, max_len, gatt, pad_to=100
     W3, B3 = leaf(model.w3), leaf([float(model.b3)])
     Q = Qt[:, None, :].expand(B, pad_to, 48)
     X = torch.cat([Q, St, Q - St, Q * St], dim=-1)
-    h1 = torch.relu(F.linear(X, W1, B1))
-    h2 = torch.relu(F.linear(h1, W2, B2))
+    z1 = F.linear(X, W1, B1)
+    h1 = torch.relu(z1)
+    h1.retain_grad()
+    z2 = F.linear(h1, W2, B2)
+    h2 = torch.relu(z2)
     e = F.linear(h2, W3[None, :], B3).squeeze(-1)
     mask = torch.arange(pad_to)[None, :] < torch.from_numpy(L)[:, None]
     pw = torch.softmax(e.masked_fill(~mask, float("-inf")), dim=-1)
     pw = torch.where(mask, pw, torch.zeros_like(pw))
     att = torch.bmm(pw[:, None, :], St).squeeze(1)
     (att * torch.from_numpy(np.asarray(gatt, np.float64))).sum().backward()
-    gs = np.zeros((int(seq_offsets[-1] + batch.seq_lengths[-1]) if B else 0, 48))
+    P = int(seq_offsets[-1] + batch.seq_lengths[-1]) if B else 0
+    gs = np.zeros((P, 48))
+    # per position index: z1 / (the size of its terms), dL/dh1, z2 / size
+    with torch.no_grad():
+        a1 = X.abs() @ W1.abs().T + B1.abs()
+        a2 = h1.abs() @ W2.abs().T + B2.abs()
+    r1, v1, r2 = np.zeros((P, 256)), np.zeros((P, 256)), np.zeros((P, 64))
     for b in range(B):
-        gs[seq_offsets[b]: seq_offsets[b] + int(L[b])] = St.grad[b, :int(L[b])].numpy()
+        o, n = int(seq_offsets[b]), int(L[b])
+        gs[o: o + n] = St.grad[b, :n].numpy()
+        r1[o: o + n] = (z1[b, :n] / a1[b, :n]).detach().numpy()
+        v1[o: o + n] = h1.grad[b, :n].numpy()
+        r2[o: o + n] = (z2[b, :n] / a2[b, :n]).detach().numpy()
     return dict(gq=Qt.grad.numpy(), gs=gs, dw1=W1.grad.numpy(), db1=B1.grad.numpy(),
                 dw2=W2.grad.numpy(), db2=B2.grad.numpy(), dw3=W3.grad.numpy(),
-                db3=float(B3.grad[0]))
+                db3=float(B3.grad[0]), r1=r1, v1=v1, r2=r2)
 
 
 def pin_din_bwd(orc):
@@ -716,10 +729,17 @@ def pin_din_bwd(orc):
         g = np.random.default_rng(5).standard_normal((b.B, 48))
         seq_tabs = [m.tables[k] for k in synth.SEQ_KEYS]
         got = orc.din_bwd(seq_tabs, b.seq_values, b.seq_stride, off, b.seq_lengths, 100, q, m.w1,
-                          m.b1, m.w2, m.b2, m.w3, m.b3, g)
+                          m.b1, m.w2, m.b2, m.w3, m.b3, g, gates=True)
         ref = _torch_din_grads(m, b, q, off, 100, g)
         for k in ("gq", "gs", "dw1", "db1", "dw2", "db2", "dw3"):
             assert _rel(got[k], ref[k]) < 1e-12, (k, _rel(got[k], ref[k]))
+        # the gate outputs: pre-activations over their terms' sizes (within
+        # [-1, 1]) and the gradient reaching h1 (autograd's dL/dh1)
+        P = ref["r1"].shape[0]
+        for k in ("r1", "v1", "r2"):
+            assert _rel(got[k][:P], ref[k]) < 1e-12, (k, _rel(got[k][:P], ref[k]))
+        assert np.abs(got["r1"]).max() <= 1 and np.abs(got["r2"]).max() <= 1
+        assert (got["v1"] != 0).any() and (got["r1"] > 0).any() and (got["r1"] < 0).any()
         assert abs(got["db3"] - ref["db3"]) <= 1e-12 * max(1.0, abs(ref["db3"]))
         assert np.all(got["gq_scale"] >= np.abs(got["gq"]) * (1 - 1e-12))
         # db3 vanishes: the softmax ignores a common shift of the scores

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import DEV, FP32_TOL, row_rel_err, say
+from gpu_helpers import DEV, FP32_TOL, row_rel_err, say, settle_relu_ties
 from sparse_embedding_din_amd import pipeline as PL
 from sparse_embedding_din_amd import rec as R
 
@@ -73,7 +73,11 @@ def _check(m, b, seq_values, offs, stride, query, gatt, max_len=100, weights=Tru
     got = _gpu(m, b, seq_values, offs, stride, query, gatt, max_len, weights, dtype)
     q = np.concatenate([query[:, c:c + 16] for c in synth.QUERY_COL], axis=1).astype(np.float64)
     ref = oracle.get().din_bwd([m.tables[k] for k in synth.SEQ_KEYS], seq_values, stride, offs,
-                               b.seq_lengths, max_len, q, m.w1, m.b1, m.w2, m.b2, m.w3, m.b3, gatt)
+                               b.seq_lengths, max_len, q, m.w1, m.b1, m.w2, m.b2, m.w3, m.b3, gatt,
+                               gates=True)
+    nties = settle_relu_ties(got, ref, m, seq_values, offs, b.seq_lengths, max_len, q, stride)
+    if nties:
+        say(f"  {tag}: {nties} first-layer gate(s) within rounding of zero")
     # the query gradient sums terms that nearly cancel when a sample's
     # positions look alike (the score gradients of a sample sum to zero): its
     # error is measured per row against the size of those terms

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import DEV, FP32_TOL, row_rel_err, say
+from gpu_helpers import DEV, FP32_TOL, row_rel_err, say, settle_relu_ties
 from sparse_embedding_din_amd import pipeline as PL
 from sparse_embedding_din_amd import rec as R
 
@@ -56,13 +56,18 @@ def test_sparse_train_step(B):
     R.rec_embbag_adagrad(atabs, T, B, db.values, db.lengths, to(off), b.values.size, gp,
                          synth.SEQ_KEYS, db.seq_values, P, P, gs, 1e-3, 1e-10, wa, wsa)
     torch.cuda.synchronize()
+    gs_gpu = gs.cpu().numpy()
 
     # oracle: the same chain in fp64
     orc = oracle.get()
     o = oracle.forward(m, b)
     q = o["query"]
     ob = orc.din_bwd([m.tables[k] for k in synth.SEQ_KEYS], b.seq_values, P, seq_off,
-                     b.seq_lengths, m.cfg.max_len, q, m.w1, m.b1, m.w2, m.b2, m.w3, m.b3, g_att)
+                     b.seq_lengths, m.cfg.max_len, q, m.w1, m.b1, m.w2, m.b2, m.w3, m.b3, g_att,
+                     gates=True)
+    # a first-layer ReLU gate within rounding of zero may go either way
+    settle_relu_ties({"gs": gs_gpu}, ob, m, b.seq_values, seq_off, b.seq_lengths, m.cfg.max_len,
+                     q, P)
     og_pool = g_pool.astype(np.float64)
     for k, c in enumerate(synth.QUERY_COL):
         og_pool[:, c:c + 16] += ob["gq"][:, 16 * k:16 * k + 16]
