@@ -642,8 +642,8 @@ def main():
                    "avg_call_us": round(d_us, 2), "positions": Pv, "samples": B,
                    "flops_per_call": d_flops, "achieved_tflops": round(d_flops / (d_us * 1e-6) / 1e12, 2),
                    "peak": FP32_PEAK_TFLOPS, "frac": round(d_flops / (d_us * 1e-6) / 1e12 / FP32_PEAK_TFLOPS, 4),
-                   "bound": "fp32 vector arithmetic: LDS-tiled products over 32-position tiles "
-                            "(the matrix cores are not used yet)",
+                   "bound": "fp32 matrix cores (v_mfma_f32_16x16x4f32): 32 positions per workgroup, "
+                            "weight gradients as LDS-tiled vector products",
                    "traffic": load_traffic(["k_dinb_transpose", "k_dinb_clear", "k_dinb_map",
                                             "k_dinb_fwd", "k_dinb_soft", "k_dinb_bwdt", "k_dinb_gq",
                                             "k_dinb_wgrad", "k_dinb_reduce"], shash, cfg.name)}

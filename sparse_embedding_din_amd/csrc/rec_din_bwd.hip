@@ -12,17 +12,19 @@
 //   dW1 = sum_j dz1_j x_j^T, dW2 = sum_j dz2_j h1_j^T, dw3 = sum_j de_j h2_j
 //   (and the biases: the sums of dz1, dz2, de).
 //
-// Plain fp32 arithmetic (a first, correctness-first version; its matrix
-// products are small per position and run on the vector units):
-//   k_dinb_transpose  W1^T and W2^T in fp32 into the workspace, so that the
-//                  forward products read weights coalesced as the backward's do;
-//   k_dinb_clear   every position index: its validity flag and its rows of
+// fp32 throughout; the per-position products run on the matrix cores
+// (v_mfma_f32_16x16x4f32, 16 positions per tile):
+//   k_dinb_clear   every position index: no sample yet, and its rows of
 //                  grad_seq set to zero (positions past a sample's first
 //                  max_len, and gaps of a padded layout, stay zero);
-//   k_dinb_sample  one 256-thread workgroup per sample: the scores, the
-//                  softmax, then position by position the backward above;
-//                  with weight gradients requested it stores per position
-//                  [x, 1], [h1, 1], [h2, 1], dz1, dz2 and de;
+//   k_dinb_transpose  W1^T and W2^T in fp32, the A operands of the forward;
+//   k_dinb_map     the sample of every position index;
+//   k_dinb_fwd     the forward of 32 positions per workgroup: S, [x, 1],
+//                  [h1, 1], [h2, 1] and the score of every position;
+//   k_dinb_soft    one wave per sample: the softmax weights p_j and de_j;
+//   k_dinb_bwdt    the backward of 32 positions per workgroup: dz2, dz1, dx,
+//                  each position's sequence-row gradient and query terms;
+//   k_dinb_gq      the query gradient, each sample's terms in position order;
 //   k_dinb_wgrad   the weight gradients as sums over positions of outer
 //                  products, [dz1]^T [x, 1] (dW1 and db1), [dz2]^T [h1, 1]
 //                  (dW2 and db2), [de]^T [h2, 1] (dw3 and db3): 64 x 64
@@ -31,6 +33,7 @@
 //                  added in split order by k_dinb_reduce.
 // Every sum has one order: results are bit-identical run to run.
 #include "rec_internal.h"
+#include "rec_mfma.h"
 
 namespace rec {
 namespace {
@@ -46,12 +49,6 @@ __device__ inline float bf16_bits(uint16_t h) { return __uint_as_float((uint32_t
 
 __device__ inline float wload(const void* w, int64_t i, int bf16) {
     return bf16 ? bf16_bits(((const uint16_t*)w)[i]) : ((const float*)w)[i];
-}
-
-// Component d of the row of raw id x in table t (0 on a hash miss).
-__device__ inline float seq_elem(const TabDev& t, int64_t x, int d) {
-    const int64_t r = t.kind == REC_HASH ? hash_probe(t, x) : floor_mod_magic(x, t.rows, t.magic, t.shift);
-    return r < 0 ? 0.0f : t.values[r * REC_DIM + d];
 }
 
 __global__ __launch_bounds__(256) void k_dinb_clear(DinBwdArgs a) {
@@ -94,139 +91,166 @@ __global__ __launch_bounds__(256) void k_dinb_map(DinBwdArgs a) {
     }
 }
 
-constexpr int kPT = 32;          // positions per tile (two tiles' LDS fit a CU)
-constexpr int kPPT = kPT / 16;   // positions per thread
-constexpr int kXS = 196;         // LDS row stride of x / dx rows (192 + 4)
-constexpr int kHS = 260;         // LDS row stride of h1 / dz1 rows (256 + 4)
-constexpr int kWBF = 16 * 260;   // staged weight block (floats)
+constexpr int kTP = 32;          // positions per workgroup: two 16-position MFMA tiles
+constexpr int kLdS = 260;        // LDS row stride (floats) of the h1 / dz1 rows
 
-struct TileLds {
-    float xs[kPT * kXS];         // x rows, later dz2 (stride 65) and dx rows
-    float hs[kPT * kHS];         // h1 rows, later dz1 rows
-    float wb[kWBF];              // a block of weight rows
-};
+// v_mfma_f32_16x16x4f32, lane l = 16 g + n: A element (row n, K slot g), B
+// element (K slot g, column n); the result holds rows 4g .. 4g+3 of column n.
+// Columns are positions throughout; the K order of a product is free as long
+// as A and B agree.
+__device__ inline f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
-__device__ inline void unpack16(const float* p, float* v) {
+// The lane's 12 features c = 12 g + f of position p's query (q) and
+// sequence row (s); zero where p has no sample, s zero on a hash miss.
+__device__ inline void lane_inputs(const DinBwdArgs& a, int64_t p, int b, int g, float* q, float* s) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const float4 x = *(const float4*)(p + 4 * u);
-        v[4 * u] = x.x; v[4 * u + 1] = x.y; v[4 * u + 2] = x.z; v[4 * u + 3] = x.w;
+    for (int r = 0; r < 3; ++r) {
+        const int c = 12 * g + 4 * r, f = c >> 4, d = c & 15;
+        float4 sv = make_float4(0.f, 0.f, 0.f, 0.f), qv = sv;
+        if (b >= 0) {
+            const TabDev& t = a.tabs[f];
+            const int64_t x = a.seq_values[(int64_t)f * a.seq_stride + p];
+            const int64_t row = t.kind == REC_HASH ? hash_probe(t, x) : floor_mod_magic(x, t.rows, t.magic, t.shift);
+            if (row >= 0) sv = *(const float4*)(t.values + row * REC_DIM + d);
+            const float* qr = a.query + (int64_t)b * a.query_ld + a.qcol[f] + d;
+            qv = make_float4(qr[0], qr[1], qr[2], qr[3]);
+        }
+        s[4 * r] = sv.x; s[4 * r + 1] = sv.y; s[4 * r + 2] = sv.z; s[4 * r + 3] = sv.w;
+        q[4 * r] = qv.x; q[4 * r + 1] = qv.y; q[4 * r + 2] = qv.z; q[4 * r + 3] = qv.w;
     }
 }
 
-// Forward of kPT positions: x (from the query of the position's sample and its
-// sequence row), h1 = relu(W1 x + b1), h2 = relu(W2 h1 + b2), the score; as
-// LDS-tiled products, each block of weight rows staged once for the tile.
-// Thread (pr, uc) = (t / 16, t % 16) owns positions kPPT pr .. kPPT pr + kPPT - 1.
+// Forward of 32 positions on the matrix cores (fp32 operands): each of the
+// four waves builds the inputs x = [q, s, q-s, q*s] of all 32 positions in
+// registers (input i = 12 tau + f of lane g is column 48 tau + 12 g + f of
+// W1), runs h1 = relu(W1 x + b1) for its 64 hidden units and stages them in
+// LDS; then wave w runs h2 = relu(W2 h1 + b2) for units 16 w .. 16 w + 15 and
+// its share of the score, the four shares added in wave order.  Stores S,
+// [h1, 1], [h2, 1], the score and, with weight gradients, [x, 1].
 __global__ __launch_bounds__(256) void k_dinb_fwd(DinBwdArgs a) {
-    __shared__ __attribute__((aligned(16))) TileLds L;
-    const int t = threadIdx.x, pr = t >> 4, uc = t & 15;
-    const int64_t p0 = (int64_t)blockIdx.x * kPT;
-    for (int idx = t; idx < kPT * 48; idx += 256) {
-        const int pi = idx / 48, c = idx - pi * 48, f = c >> 4;
-        const int64_t p = p0 + pi;
-        const int b = p < a.seq_stride ? a.map[p] : -1;
-        float sv = 0.0f, qv = 0.0f;
-        if (b >= 0) {
-            sv = seq_elem(a.tabs[f], a.seq_values[(int64_t)f * a.seq_stride + p], c & 15);
-            qv = a.query[(int64_t)b * a.query_ld + a.qcol[f] + (c & 15)];
-            a.S[p * 48 + c] = sv;
+    __shared__ __attribute__((aligned(16))) float hs[kTP * kLdS];
+    __shared__ float sc[4][kTP];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
+    const int64_t p0 = (int64_t)blockIdx.x * kTP;
+    int64_t p[2];
+    int bs[2];
+    float x[2][48];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        p[s] = p0 + 16 * s + n;
+        bs[s] = p[s] < a.seq_stride ? a.map[p[s]] : -1;
+        float q[12], sv[12];
+        lane_inputs(a, p[s], bs[s], g, q, sv);
+#pragma unroll
+        for (int f = 0; f < 12; ++f) {
+            x[s][f] = q[f];
+            x[s][12 + f] = sv[f];
+            x[s][24 + f] = q[f] - sv[f];
+            x[s][36 + f] = q[f] * sv[f];
         }
-        float* x = L.xs + pi * kXS;
-        x[c] = qv;
-        x[48 + c] = sv;
-        x[96 + c] = qv - sv;
-        x[144 + c] = qv * sv;
-    }
-    __syncthreads();
-    // h1: units 16 uc .. 16 uc + 15
-    float acc[kPPT][16];
+        if (bs[s] >= 0) {
+            if (w == 0) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const float bj = a.b1 ? a.b1[16 * uc + j] : 0.0f;
+                for (int r = 0; r < 3; ++r)
+                    *(float4*)(a.S + p[s] * 48 + 12 * g + 4 * r) =
+                        make_float4(sv[4 * r], sv[4 * r + 1], sv[4 * r + 2], sv[4 * r + 3]);
+            } else if (w == 1 && a.wgrad) {
 #pragma unroll
-        for (int i = 0; i < kPPT; ++i) acc[i][j] = bj;
-    }
-    for (int kb = 0; kb < 192; kb += 16) {
-        for (int e = t; e < 16 * 256; e += 256) {
-            const int kk = e >> 8, u = e & 255;
-            L.wb[kk * 260 + u] = a.w1t[(kb + kk) * 256 + u];
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < 16; ++kk) {
-            float xv[kPPT], wv[16];
-#pragma unroll
-            for (int i = 0; i < kPPT; ++i) xv[i] = L.xs[(kPPT * pr + i) * kXS + kb + kk];
-            unpack16(L.wb + kk * 260 + 16 * uc, wv);
-#pragma unroll
-            for (int i = 0; i < kPPT; ++i)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) acc[i][j] += xv[i] * wv[j];
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < kPPT; ++i)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) L.hs[(kPPT * pr + i) * kHS + 16 * uc + j] = acc[i][j] > 0.0f ? acc[i][j] : 0.0f;
-    __syncthreads();
-    // h2: units 4 uc .. 4 uc + 3
-    float a2[kPPT][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const float bj = a.b2 ? a.b2[4 * uc + j] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < kPPT; ++i) a2[i][j] = bj;
-    }
-    for (int kb = 0; kb < 256; kb += 64) {
-        for (int e = t; e < 64 * 64; e += 256) {
-            const int kk = e >> 6, u = e & 63;
-            L.wb[kk * 65 + u] = a.w2t[(kb + kk) * 64 + u];
-        }
-        __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < 64; ++kk) {
-            float hv[kPPT];
-#pragma unroll
-            for (int i = 0; i < kPPT; ++i) hv[i] = L.hs[(kPPT * pr + i) * kHS + kb + kk];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float w = L.wb[kk * 65 + 4 * uc + j];
-#pragma unroll
-                for (int i = 0; i < kPPT; ++i) a2[i][j] += hv[i] * w;
+                for (int i = 0; i < 48; ++i) a.X[p[s] * kLdX + 48 * (i / 12) + 12 * g + (i % 12)] = x[s][i];
+                if (g == 0) a.X[p[s] * kLdX + 192] = 1.0f;
+            } else if (w == 2 && g == 0) {
+                a.H1[p[s] * kLdH1 + 256] = 1.0f;
+                a.H2[p[s] * kLdH2 + 64] = 1.0f;
             }
         }
-        __syncthreads();
+    }
+    // layer 1: hidden blocks 2w and 2w + 1 (32 units each, two row tiles)
+#pragma unroll 1
+    for (int hh = 0; hh < 2; ++hh) {
+        const int hb = 2 * w + hh;
+        f32x4 acc[2][2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            f32x4 bv = {0.f, 0.f, 0.f, 0.f};
+            if (a.b1) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) bv[i] = a.b1[hb * 32 + rt * 16 + 4 * g + i];
+            }
+            acc[0][rt] = bv;
+            acc[1][rt] = bv;
+        }
+        const float* wr = a.w1t + (int64_t)(12 * g) * 256 + hb * 32 + n;
+#pragma unroll
+        for (int i = 0; i < 48; ++i) {
+            const int k = 48 * (i / 12) + (i % 12);          // + 12 g, in wr
+            const float a0 = wr[k * 256], a1 = wr[k * 256 + 16];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                acc[s][0] = mfma4(a0, x[s][i], acc[s][0]);
+                acc[s][1] = mfma4(a1, x[s][i], acc[s][1]);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int u = hb * 32 + rt * 16 + 4 * g + i;
+                    const float h = fmaxf(acc[s][rt][i], 0.0f);
+                    hs[(16 * s + n) * kLdS + u] = h;
+                    if (bs[s] >= 0) a.H1[p[s] * kLdH1 + u] = h;
+                }
+    }
+    __syncthreads();
+    // layer 2: outputs 16 w .. 16 w + 15, K = the 256 units as 64 steps of 4
+    // (unit 4 k4 + g), two accumulators per tile for independent chains
+    f32x4 acc2[2][2];
+    {
+        f32x4 bv = {0.f, 0.f, 0.f, 0.f};
+        if (a.b2) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bv[i] = a.b2[16 * w + 4 * g + i];
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            acc2[s][0] = bv;
+            acc2[s][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    const float* w2r = a.w2t + (int64_t)g * 64 + 16 * w + n;
+#pragma unroll 8
+    for (int k4 = 0; k4 < 64; k4 += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int u = 4 * (k4 + h);                      // + g
+            const float av = w2r[u * 64];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                acc2[s][h] = mfma4(av, hs[(16 * s + n) * kLdS + u + g], acc2[s][h]);
+        }
     }
 #pragma unroll
-    for (int i = 0; i < kPPT; ++i) {
-        float h2[4], part = 0.0f;
+    for (int s = 0; s < 2; ++s) {
+        float part = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            h2[j] = a2[i][j] > 0.0f ? a2[i][j] : 0.0f;
-            part += a.w3[4 * uc + j] * h2[j];
+        for (int i = 0; i < 4; ++i) {
+            const int o = 16 * w + 4 * g + i;
+            const float h2 = fmaxf(acc2[s][0][i] + acc2[s][1][i], 0.0f);
+            if (bs[s] >= 0) a.H2[p[s] * kLdH2 + o] = h2;
+            part += a.w3[o] * h2;
         }
-        // the score's 64 terms: the 16 threads of these positions, a fixed tree
-        part += __shfl_xor(part, 8, 16);
-        part += __shfl_xor(part, 4, 16);
-        part += __shfl_xor(part, 2, 16);
-        part += __shfl_xor(part, 1, 16);
-        const int64_t p = p0 + kPPT * pr + i;
-        if (p < a.seq_stride && a.map[p] >= 0) {
-            if (uc == 0) {
-                a.E[p] = a.b3 + part;
-                a.H2[p * kLdH2 + 64] = 1.0f;
-                a.H1[p * kLdH1 + 256] = 1.0f;
-                a.X[p * kLdX + 192] = 1.0f;
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) a.H2[p * kLdH2 + 4 * uc + j] = h2[j];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) a.H1[p * kLdH1 + 16 * uc + j] = L.hs[(kPPT * pr + i) * kHS + 16 * uc + j];
-#pragma unroll
-            for (int j = 0; j < 12; ++j) a.X[p * kLdX + 12 * uc + j] = L.xs[(kPPT * pr + i) * kXS + 12 * uc + j];
-        }
+        part += __shfl_xor(part, 16, 64);
+        part += __shfl_xor(part, 32, 64);
+        if (g == 0) sc[w][16 * s + n] = part;
+    }
+    __syncthreads();
+    if (threadIdx.x < kTP) {
+        const int64_t pp = p0 + threadIdx.x;
+        if (pp < a.seq_stride && a.map[pp] >= 0)
+            a.E[pp] = a.b3 + (((sc[0][threadIdx.x] + sc[1][threadIdx.x]) + sc[2][threadIdx.x]) + sc[3][threadIdx.x]);
     }
 }
 
@@ -283,107 +307,120 @@ __global__ __launch_bounds__(256) void k_dinb_soft(DinBwdArgs a) {
     }
 }
 
-// Backward of kPT positions: dz2 = de w3 where h2 > 0, dz1 = W2^T dz2 where
-// h1 > 0, dx = W1^T dz1 (LDS-tiled as the forward), then each position's
-// sequence-row gradient and its terms of the query gradient.
+template <bool BF>
+__device__ inline float wld(const void* w, int64_t i) {
+    if constexpr (BF) return bf16_bits(((const uint16_t*)w)[i]);
+    else return ((const float*)w)[i];
+}
+
+// Backward of 32 positions on the matrix cores (fp32 operands):
+// dz2 = de w3 where h2 > 0 (every wave, all 64 units, from [h2, 1] and de);
+// wave w: dz1 = W2^T dz2 where h1 > 0 for units 64 w .. 64 w + 63, staged in
+// LDS; then dx = W1^T dz1 for inputs 48 w .. 48 w + 47, i.e. the block
+// tau = w of [q, s, q-s, q*s]; the four blocks meet in LDS for each
+// position's sequence-row gradient and its terms of the query gradient.
+// Weights are read in their own layout and type.
+template <bool BF>
 __global__ __launch_bounds__(256) void k_dinb_bwdt(DinBwdArgs a) {
-    __shared__ __attribute__((aligned(16))) TileLds L;
-    const int t = threadIdx.x, pr = t >> 4, uc = t & 15;
-    const int64_t p0 = (int64_t)blockIdx.x * kPT;
-    float* d2 = L.xs;                               // dz2 rows, stride 65
-    for (int idx = t; idx < kPT * 64; idx += 256) {
-        const int pi = idx >> 6, o = idx & 63;
-        const int64_t p = p0 + pi;
-        const bool ok = p < a.seq_stride && a.map[p] >= 0;
-        const float v = (ok && a.H2[p * kLdH2 + o] > 0.0f) ? a.DE[p] * a.w3[o] : 0.0f;
-        d2[pi * 65 + o] = v;
-        if (ok && a.wgrad) a.DZ2[p * 64 + o] = v;
-    }
-    __syncthreads();
-    // dz1: units 16 uc .. 16 uc + 15; W2 rows staged 16 at a time
-    float acc[kPPT][16];
+    __shared__ __attribute__((aligned(16))) float ds[kTP * kLdS];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
+    const int64_t p0 = (int64_t)blockIdx.x * kTP;
+    int64_t p[2];
+    int bs[2];
+    float dz2[2][16];                  // step st: unit 16 (st / 4) + 4 g + st % 4
 #pragma unroll
-    for (int i = 0; i < kPPT; ++i)
+    for (int s = 0; s < 2; ++s) {
+        p[s] = p0 + 16 * s + n;
+        bs[s] = p[s] < a.seq_stride ? a.map[p[s]] : -1;
+        const float de = bs[s] >= 0 ? a.DE[p[s]] : 0.0f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[i][j] = 0.0f;
-    for (int kb = 0; kb < 64; kb += 16) {
-        for (int e = t; e < 16 * 256; e += 256) {
-            const int kk = e >> 8, u = e & 255;
-            L.wb[kk * 260 + u] = wload(a.w2, (int64_t)(kb + kk) * 256 + u, a.bf16);
+        for (int st = 0; st < 16; ++st) {
+            const int o = 16 * (st >> 2) + 4 * g + (st & 3);
+            const float h2 = bs[s] >= 0 ? a.H2[p[s] * kLdH2 + o] : 0.0f;
+            dz2[s][st] = h2 > 0.0f ? de * a.w3[o] : 0.0f;
         }
-        __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < 16; ++kk) {
-            float dv[kPPT], wv[16];
+        if (w == 0 && a.wgrad && bs[s] >= 0) {
 #pragma unroll
-            for (int i = 0; i < kPPT; ++i) dv[i] = d2[(kPPT * pr + i) * 65 + kb + kk];
-            unpack16(L.wb + kk * 260 + 16 * uc, wv);
-#pragma unroll
-            for (int i = 0; i < kPPT; ++i)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) acc[i][j] += dv[i] * wv[j];
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < kPPT; ++i) {
-        const int64_t p = p0 + kPPT * pr + i;
-        const bool ok = p < a.seq_stride && a.map[p] >= 0;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int u = 16 * uc + j;
-            const float v = (ok && a.H1[p * kLdH1 + u] > 0.0f) ? acc[i][j] : 0.0f;
-            L.hs[(kPPT * pr + i) * kHS + u] = v;
-            if (ok && a.wgrad) a.DZ1[p * 256 + u] = v;
+            for (int mt = 0; mt < 4; ++mt)
+                *(float4*)(a.DZ2 + p[s] * 64 + 16 * mt + 4 * g) =
+                    make_float4(dz2[s][4 * mt], dz2[s][4 * mt + 1], dz2[s][4 * mt + 2], dz2[s][4 * mt + 3]);
         }
     }
-    __syncthreads();
-    // dx: columns 12 uc .. 12 uc + 11; W1 rows staged 16 at a time (stride 196)
-    float ax[kPPT][12];
+    // dz1 for the row tiles ut = 4w .. 4w + 3: A = W2[o][16 ut + n]
+    f32x4 acc[2][4];
 #pragma unroll
-    for (int i = 0; i < kPPT; ++i)
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int j = 0; j < 12; ++j) ax[i][j] = 0.0f;
-    for (int kb = 0; kb < 256; kb += 16) {
-        for (int e = t; e < 16 * 192; e += 256) {
-            const int kk = e / 192, c = e - kk * 192;
-            L.wb[kk * kXS + c] = wload(a.w1, (int64_t)(kb + kk) * 192 + c, a.bf16);
+        for (int j = 0; j < 4; ++j) acc[s][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+        const int o = 16 * (st >> 2) + 4 * g + (st & 3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float av = wld<BF>(a.w2, (int64_t)o * 256 + (4 * w + j) * 16 + n);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) acc[s][j] = mfma4(av, dz2[s][st], acc[s][j]);
         }
-        __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < 16; ++kk) {
-            float dv[kPPT], wv[12];
+    }
 #pragma unroll
-            for (int i = 0; i < kPPT; ++i) dv[i] = L.hs[(kPPT * pr + i) * kHS + kb + kk];
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int u = 0; u < 3; ++u) {
-                const float4 x = *(const float4*)(L.wb + kk * kXS + 12 * uc + 4 * u);
-                wv[4 * u] = x.x; wv[4 * u + 1] = x.y; wv[4 * u + 2] = x.z; wv[4 * u + 3] = x.w;
+        for (int j = 0; j < 4; ++j) {
+            const int u0 = (4 * w + j) * 16 + 4 * g;
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float h1 = bs[s] >= 0 ? a.H1[p[s] * kLdH1 + u0 + i] : 0.0f;
+                v[i] = h1 > 0.0f ? acc[s][j][i] : 0.0f;
+                ds[(16 * s + n) * kLdS + u0 + i] = v[i];
             }
-#pragma unroll
-            for (int i = 0; i < kPPT; ++i)
-#pragma unroll
-                for (int j = 0; j < 12; ++j) ax[i][j] += dv[i] * wv[j];
+            if (a.wgrad && bs[s] >= 0)
+                *(float4*)(a.DZ1 + p[s] * 256 + u0) = make_float4(v[0], v[1], v[2], v[3]);
         }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int i = 0; i < kPPT; ++i)
-#pragma unroll
-        for (int j = 0; j < 12; ++j) L.xs[(kPPT * pr + i) * kXS + 12 * uc + j] = ax[i][j];
     __syncthreads();
-    for (int idx = t; idx < kPT * 48; idx += 256) {
+    // dx for the row tiles 3w .. 3w + 2, K = the 256 units as 64 steps of 4
+    // (unit 4 k4 + g): A = W1[unit][16 (3w + c1) + n]
+    f32x4 dx[2][3];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int c1 = 0; c1 < 3; ++c1) dx[s][c1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int k4 = 0; k4 < 64; ++k4) {
+        const int u = 4 * k4 + g;
+        float bv[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) bv[s] = ds[(16 * s + n) * kLdS + u];
+#pragma unroll
+        for (int c1 = 0; c1 < 3; ++c1) {
+            const float av = wld<BF>(a.w1, (int64_t)u * 192 + (3 * w + c1) * 16 + n);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) dx[s][c1] = mfma4(av, bv[s], dx[s][c1]);
+        }
+    }
+    __syncthreads();                   // every wave is done reading dz1
+    // block tau = w of dx, element c = 16 c1 + 4 g + i, into dxs[tau][position][48]
+    float* dxs = ds;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int c1 = 0; c1 < 3; ++c1)
+            *(float4*)(dxs + (w * kTP + 16 * s + n) * 48 + 16 * c1 + 4 * g) =
+                make_float4(dx[s][c1][0], dx[s][c1][1], dx[s][c1][2], dx[s][c1][3]);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kTP * 48; idx += 256) {
         const int pi = idx / 48, c = idx - pi * 48;
-        const int64_t p = p0 + pi;
-        const int b = p < a.seq_stride ? a.map[p] : -1;
+        const int64_t pp = p0 + pi;
+        const int b = pp < a.seq_stride ? a.map[pp] : -1;
         if (b < 0) continue;
-        const float* dx = L.xs + pi * kXS;
-        const float sv = a.S[p * 48 + c];
+        const float d0 = dxs[(0 * kTP + pi) * 48 + c], d1 = dxs[(1 * kTP + pi) * 48 + c];
+        const float d2 = dxs[(2 * kTP + pi) * 48 + c], d3 = dxs[(3 * kTP + pi) * 48 + c];
+        const float sv = a.S[pp * 48 + c];
         const float qv = a.query[(int64_t)b * a.query_ld + a.qcol[c >> 4] + (c & 15)];
         if (a.gs)
-            a.gs[((int64_t)(c >> 4) * a.seq_stride + p) * REC_DIM + (c & 15)] =
-                a.PW[p] * a.gatt[(int64_t)b * 48 + c] + dx[48 + c] - dx[96 + c] + qv * dx[144 + c];
-        a.GQP[p * 48 + c] = dx[c] + dx[96 + c] + sv * dx[144 + c];
+            a.gs[((int64_t)(c >> 4) * a.seq_stride + pp) * REC_DIM + (c & 15)] =
+                a.PW[pp] * a.gatt[(int64_t)b * 48 + c] + d1 - d2 + qv * d3;
+        a.GQP[pp * 48 + c] = d0 + d2 + sv * d3;
     }
 }
 
@@ -502,10 +539,13 @@ hipError_t launch_din_bwd(const DinBwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_dinb_transpose, dim3((256 * 192 + 64 * 256 + 255) / 256), dim3(256), 0, s, a);
     const int64_t bgrid = (a.B + 255) / 256;
     hipLaunchKernelGGL(k_dinb_map, dim3((unsigned)(bgrid < 65536 ? bgrid : 65536)), dim3(256), 0, s, a);
-    const int64_t tiles = (a.seq_stride + kPT - 1) / kPT;
+    const int64_t tiles = (a.seq_stride + kTP - 1) / kTP;
     if (tiles > 0) hipLaunchKernelGGL(k_dinb_fwd, dim3((unsigned)tiles), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_dinb_soft, dim3((unsigned)((a.B + 3) / 4)), dim3(256), 0, s, a);
-    if (tiles > 0) hipLaunchKernelGGL(k_dinb_bwdt, dim3((unsigned)tiles), dim3(256), 0, s, a);
+    if (tiles > 0) {
+        if (a.bf16) hipLaunchKernelGGL(k_dinb_bwdt<true>, dim3((unsigned)tiles), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(k_dinb_bwdt<false>, dim3((unsigned)tiles), dim3(256), 0, s, a);
+    }
     hipLaunchKernelGGL(k_dinb_gq, dim3((unsigned)((a.B * 48 + 255) / 256)), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.wgrad) return e;
