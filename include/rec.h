@@ -552,7 +552,7 @@ rec_status rec_embbag_adagrad(const rec_adagrad_table* tables, int32_t T, int64_
                               float eps, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace rec_din_attn_bwd needs: 256 KiB (the transposed
- * weights) plus about 3.7 KiB per position index (seq_stride), and 16 MiB more
+ * weights) plus about 3.7 KiB per position index (seq_stride), and 64 MiB more
  * with weight gradients. */
 size_t rec_din_attn_bwd_workspace_bytes(int64_t seq_stride, int32_t weight_grads);
 

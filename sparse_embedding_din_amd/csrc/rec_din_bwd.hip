@@ -27,10 +27,10 @@
 //   k_dinb_gq      the query gradient, each sample's terms in position order;
 //   k_dinb_wgrad   the weight gradients as sums over positions of outer
 //                  products, [dz1]^T [x, 1] (dW1 and db1), [dz2]^T [h1, 1]
-//                  (dW2 and db2), [de]^T [h2, 1] (dw3 and db3): 64 x 64
-//                  output tiles, blocks of positions staged in LDS, the
-//                  positions split in kDinbSplits ranges, partial sums then
-//                  added in split order by k_dinb_reduce.
+//                  (dW2 and db2), [de]^T [h2, 1] (dw3 and db3), on the
+//                  matrix cores with positions as K: one workgroup per range
+//                  of positions (kDinbSplits ranges), whose sums
+//                  k_dinb_reduce adds in range order.
 // Every sum has one order: results are bit-identical run to run.
 #include "rec_internal.h"
 #include "rec_mfma.h"
@@ -38,12 +38,8 @@
 namespace rec {
 namespace {
 
-constexpr int kDinbSplits = 64;
+constexpr int kDinbSplits = 256;      // position ranges of the weight gradients
 constexpr int kLdX = 193, kLdH1 = 257, kLdH2 = 65;       // rows carry a trailing 1
-constexpr int kJobs = 3;
-// job j: C[M][N] = sum_p A[p][m] Bm[p][n]
-__constant__ int kJobM[kJobs] = {256, 64, 1};
-__constant__ int kJobN[kJobs] = {kLdX, kLdH1, kLdH2};
 
 __device__ inline float bf16_bits(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -438,72 +434,108 @@ __global__ __launch_bounds__(256) void k_dinb_gq(DinBwdArgs a) {
     a.gq[i] = s;
 }
 
-// Weight gradients: block (tile, split).  Tiles of 64 x 64 outputs of the
-// three jobs in order; thread (tm, tn) owns the 4 x 4 outputs (m0 + 4 tm + i,
-// n0 + 4 tn + j).  Blocks of kWB positions of A's and B's tile columns are
-// staged in LDS by coalesced loads (positions without a valid flag, and
-// columns past the edge, staged as zeros), then multiplied from LDS.
-constexpr int kWT = 64;
-constexpr int kWB = 32;
+// Weight gradients of one range of positions per workgroup, on the matrix
+// cores with the positions as the K index (4 per step, lane group g takes
+// position 4 k + g): C[m][n] += A[p][m] B[p][n] for dW1 (A = dz1, B = [x, 1],
+// 16 x 13 tiles of 16 x 16), dW2 (A = dz2, B = [h1, 1], 4 x 17 tiles) and dw3
+// (A = de, one row, B = [h2, 1], 5 tiles).  Wave w owns dW1's row tiles 2w and
+// 2w + 1, dW2's row tile w / 2 with nine of its column tiles (the ninth of the
+// odd waves lies past the edge and is dropped), and wave 7 the dw3 tiles; so
+// each position's rows are read once per workgroup, and the waves' reads of
+// the same [x, 1] and [h1, 1] rows meet in the cache.  Positions without a
+// sample, and columns past an edge, enter as zeros.  The range's sums go to
+// its slot of the split sums, which k_dinb_reduce adds in range order.
+constexpr int kWgWaves = 8;
 
-__device__ inline int wgrad_tiles(int job) {
-    return ((kJobM[job] + kWT - 1) / kWT) * ((kJobN[job] + kWT - 1) / kWT);
+// One step's operands of a lane: position pb + g of the range ending at p1.
+struct WgOps {
+    float A1[2], B1[13], A2, B2[9], A3, B3[5];
+};
+
+__device__ inline void wg_load(const DinBwdArgs& a, int64_t pb, int64_t p1, int w, int n, int g,
+                               WgOps& o) {
+    const int64_t p = pb + g;
+    const bool ok = p < p1 && a.map[p] >= 0;
+    const int c2lo = (w & 1) ? 9 : 0, r2 = w >> 1;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) o.A1[t] = ok ? a.DZ1[p * 256 + 16 * (2 * w + t) + n] : 0.0f;
+#pragma unroll
+    for (int c = 0; c < 13; ++c) o.B1[c] = (ok && 16 * c + n < kLdX) ? a.X[p * kLdX + 16 * c + n] : 0.0f;
+    o.A2 = ok ? a.DZ2[p * 64 + 16 * r2 + n] : 0.0f;
+#pragma unroll
+    for (int c = 0; c < 9; ++c) {
+        const int col = 16 * (c2lo + c) + n;
+        o.B2[c] = (ok && col < kLdH1) ? a.H1[p * kLdH1 + col] : 0.0f;
+    }
+    o.A3 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 5; ++c) o.B3[c] = 0.0f;
+    if (w == kWgWaves - 1) {
+        o.A3 = (ok && n == 0) ? a.DE[p] : 0.0f;
+#pragma unroll
+        for (int c = 0; c < 5; ++c) {
+            const int col = 16 * c + n;
+            o.B3[c] = (ok && col < kLdH2) ? a.H2[p * kLdH2 + col] : 0.0f;
+        }
+    }
 }
 
-__global__ __launch_bounds__(256) void k_dinb_wgrad(DinBwdArgs a, int64_t chunk) {
-    __shared__ __attribute__((aligned(16))) float As[kWB][kWT];
-    __shared__ __attribute__((aligned(16))) float Bs[kWB][kWT];
-    const int t = threadIdx.x, tm = t >> 4, tn = t & 15;
-    int tile = blockIdx.x, job = 0;
-    for (; job < kJobs; ++job) {
-        const int nt = wgrad_tiles(job);
-        if (tile < nt) break;
-        tile -= nt;
-    }
-    const int M = kJobM[job], N = kJobN[job];
-    const int ntn = (N + kWT - 1) / kWT;
-    const int m0 = (tile / ntn) * kWT, n0 = (tile % ntn) * kWT;
-    const float* A = job == 0 ? a.DZ1 : job == 1 ? a.DZ2 : a.DE;
-    const float* Bm = job == 0 ? a.X : job == 1 ? a.H1 : a.H2;
-    const int64_t p0 = (int64_t)blockIdx.y * chunk;
+__global__ __launch_bounds__(64 * kWgWaves) void k_dinb_wgrad(DinBwdArgs a, int64_t chunk) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
+    const int64_t p0 = (int64_t)blockIdx.x * chunk;
     const int64_t p1 = p0 + chunk < a.seq_stride ? p0 + chunk : a.seq_stride;
-    float acc[4][4];
+    const int c2lo = (w & 1) ? 9 : 0, r2 = w >> 1;
+    f32x4 acc1[2][13], acc2[9], acc3[5];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int c = 0; c < 13; ++c) acc1[0][c] = acc1[1][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-    for (int64_t pb = p0; pb < p1; pb += kWB) {
+    for (int c = 0; c < 9; ++c) acc2[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < kWB * kWT / 256; ++u) {
-            const int e = t + u * 256, r = e / kWT, c = e - r * kWT;
-            const int64_t p = pb + r;
-            const bool ok = p < p1 && a.map[p] >= 0;
-            As[r][c] = (ok && m0 + c < M) ? A[p * M + m0 + c] : 0.0f;
-            Bs[r][c] = (ok && n0 + c < N) ? Bm[p * N + n0 + c] : 0.0f;
+    for (int c = 0; c < 5; ++c) acc3[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    WgOps cur;
+    if (p0 < p1) wg_load(a, p0, p1, w, n, g, cur);
+    // the next step's operands are in flight while this step's products run
+    for (int64_t pb = p0; pb < p1; pb += 4) {
+        WgOps nxt = cur;
+        if (pb + 4 < p1) wg_load(a, pb + 4, p1, w, n, g, nxt);
+#pragma unroll
+        for (int c = 0; c < 13; ++c) {
+            acc1[0][c] = mfma4(cur.A1[0], cur.B1[c], acc1[0][c]);
+            acc1[1][c] = mfma4(cur.A1[1], cur.B1[c], acc1[1][c]);
         }
-        __syncthreads();
-#pragma unroll 4
-        for (int r = 0; r < kWB; ++r) {
-            const float4 av = *(const float4*)&As[r][4 * tm];
-            const float4 bv = *(const float4*)&Bs[r][4 * tn];
-            const float ai[4] = {av.x, av.y, av.z, av.w}, bj[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int c = 0; c < 9; ++c) acc2[c] = mfma4(cur.A2, cur.B2[c], acc2[c]);
+        if (w == kWgWaves - 1) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] += ai[i] * bj[j];
+            for (int c = 0; c < 5; ++c) acc3[c] = mfma4(cur.A3, cur.B3[c], acc3[c]);
         }
-        __syncthreads();
+        cur = nxt;
     }
-    int64_t base = 0;
-    for (int j = 0; j < job; ++j) base += (int64_t)kJobM[j] * kJobN[j];
-    float* out = a.part + (int64_t)blockIdx.y * a.part_stride + base;
+    // result element i of a tile: row 4 g + i, column n
+    float* out = a.part + (int64_t)blockIdx.x * a.part_stride;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = m0 + 4 * tm + i;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int n = n0 + 4 * tn + j;
-            if (m < M && n < N) out[(int64_t)m * N + n] = acc[i][j];
+        for (int c = 0; c < 13; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * (2 * w + t) + 4 * g + i, col = 16 * c + n;
+                if (col < kLdX) out[(int64_t)m * kLdX + col] = acc1[t][c][i];
+            }
+    float* out2 = out + 256 * kLdX;
+#pragma unroll
+    for (int c = 0; c < 9; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 16 * r2 + 4 * g + i, col = 16 * (c2lo + c) + n;
+            if (col < kLdH1) out2[(int64_t)m * kLdH1 + col] = acc2[c][i];
+        }
+    if (w == kWgWaves - 1 && g == 0) {
+        float* out3 = out2 + 64 * kLdH1;
+#pragma unroll
+        for (int c = 0; c < 5; ++c) {
+            const int col = 16 * c + n;
+            if (col < kLdH2) out3[col] = acc3[c][0];
         }
     }
 }
@@ -549,11 +581,8 @@ hipError_t launch_din_bwd(const DinBwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_dinb_gq, dim3((unsigned)((a.B * 48 + 255) / 256)), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.wgrad) return e;
-    int ntiles = 0;
-    const int M[kJobs] = {256, 64, 1}, N[kJobs] = {kLdX, kLdH1, kLdH2};
-    for (int j = 0; j < kJobs; ++j) ntiles += ((M[j] + kWT - 1) / kWT) * ((N[j] + kWT - 1) / kWT);
-    const int64_t chunk = (a.seq_stride + kDinbSplits - 1) / kDinbSplits;
-    hipLaunchKernelGGL(k_dinb_wgrad, dim3((unsigned)ntiles, kDinbSplits), dim3(256), 0, s, a, chunk);
+    const int64_t chunk = ((a.seq_stride + kDinbSplits - 1) / kDinbSplits + 3) & ~(int64_t)3;
+    hipLaunchKernelGGL(k_dinb_wgrad, dim3((unsigned)kDinbSplits), dim3(64 * kWgWaves), 0, s, a, chunk);
     hipLaunchKernelGGL(k_dinb_reduce, dim3((unsigned)((a.part_stride + 255) / 256)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
