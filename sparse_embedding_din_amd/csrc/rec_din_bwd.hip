@@ -217,16 +217,24 @@ __global__ __launch_bounds__(256) void k_dinb_fwd(DinBwdArgs a) {
         }
     }
     const float* w2r = a.w2t + (int64_t)g * 64 + 16 * w + n;
-#pragma unroll 8
-    for (int k4 = 0; k4 < 64; k4 += 2) {
+    // eight chunks of eight steps, the next chunk's weights in flight
+    float aw[2][8];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int u = 4 * (k4 + h);                      // + g
-            const float av = w2r[u * 64];
+    for (int j = 0; j < 8; ++j) aw[0][j] = w2r[4 * j * 64];
+#pragma unroll
+    for (int ch = 0; ch < 8; ++ch) {
+        if (ch + 1 < 8) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) aw[(ch + 1) & 1][j] = w2r[4 * (8 * (ch + 1) + j) * 64];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int u = 4 * (8 * ch + j);                  // + g
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                acc2[s][h] = mfma4(av, hs[(16 * s + n) * kLdS + u + g], acc2[s][h]);
+                acc2[s][j & 1] = mfma4(aw[ch & 1][j], hs[(16 * s + n) * kLdS + u + g], acc2[s][j & 1]);
         }
+        __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -381,18 +389,36 @@ __global__ __launch_bounds__(256) void k_dinb_bwdt(DinBwdArgs a) {
     for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int c1 = 0; c1 < 3; ++c1) dx[s][c1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int k4 = 0; k4 < 64; ++k4) {
-        const int u = 4 * k4 + g;
-        float bv[2];
+    // K in eight chunks of eight steps, the next chunk's weights in flight
+    // while this chunk's products run
+    float aw[2][8][3];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) bv[s] = ds[(16 * s + n) * kLdS + u];
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int c1 = 0; c1 < 3; ++c1) {
-            const float av = wld<BF>(a.w1, (int64_t)u * 192 + (3 * w + c1) * 16 + n);
+        for (int c1 = 0; c1 < 3; ++c1)
+            aw[0][j][c1] = wld<BF>(a.w1, (int64_t)(4 * j + g) * 192 + (3 * w + c1) * 16 + n);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) dx[s][c1] = mfma4(av, bv[s], dx[s][c1]);
+    for (int ch = 0; ch < 8; ++ch) {
+        if (ch + 1 < 8) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int c1 = 0; c1 < 3; ++c1)
+                    aw[(ch + 1) & 1][j][c1] =
+                        wld<BF>(a.w1, (int64_t)(4 * (8 * (ch + 1) + j) + g) * 192 + (3 * w + c1) * 16 + n);
         }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int u = 4 * (8 * ch + j) + g;
+            float bv[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) bv[s] = ds[(16 * s + n) * kLdS + u];
+#pragma unroll
+            for (int c1 = 0; c1 < 3; ++c1)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) dx[s][c1] = mfma4(aw[ch & 1][j][c1], bv[s], dx[s][c1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();                   // every wave is done reading dz1
     // block tau = w of dx, element c = 16 c1 + 4 g + i, into dxs[tau][position][48]
