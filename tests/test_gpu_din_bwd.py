@@ -127,6 +127,15 @@ def test_din_bwd_edges():
         assert not got["gs"][k, offs[4] + 10: offs[4] + 40].any()
 
 
+def test_din_bwd_long_sequences():
+    """Sequences up to and past the largest max_len (128): a sample's
+    positions span several workgroups of the position tiles, and the softmax
+    wave holds two positions per lane."""
+    say("din bwd long sequences, max_len 128")
+    lengths = [0, 1, 63, 64, 65, 100, 127, 128, 129, 200, 5, 128, 96, 17, 250, 2]
+    _check(*_case(synth.CONFIGS[1], len(lengths), 10, lengths=lengths), max_len=128, tag="long")
+
+
 def test_din_bwd_padded_layout_and_inputs_only():
     say("din bwd padded layout, no weight gradients")
     m, b, sv, offs, stride, q, g = _case(synth.CONFIGS[1], 32, 5, pad_to=100)
