@@ -128,7 +128,7 @@ KERNEL_SOURCES = {"k_din_attn": _FWD, "k_embbag_fwd": _FWD, "k_fwd_gather": _FWD
                   "k_bwd_keys": _BWD, "k_sort_hist": _BWD, "k_sort_scan": _BWD, "k_sort_scatter": _BWD,
                   "k_bwd_chunks": _BWD, "k_bwd_cross": _BWD,
                   "k_dlrm_interact": ["rec_dlrm.hip", "rec_mfma.h"] + _COMMON}
-for _k in ("k_dinb_transpose", "k_dinb_clear", "k_dinb_map", "k_dinb_fwd", "k_dinb_soft", "k_dinb_bwdt",
+for _k in ("k_dinb_prep", "k_dinb_map", "k_dinb_fwd", "k_dinb_soft", "k_dinb_bwdt",
            "k_dinb_gq", "k_dinb_wgrad", "k_dinb_reduce"):
     KERNEL_SOURCES[_k] = ["rec_din_bwd.hip"] + _COMMON
 
@@ -140,7 +140,7 @@ KERNELS = {"k_din_attn": "k_din_attn",
            "k_bwd_keys": "k_bwd_keys", "k_sort_hist": "k_sort_hist", "k_sort_scan": "k_sort_scan",
            "k_sort_scatter": "k_sort_scatter", "k_bwd_chunks": "k_bwd_chunks",
            "k_bwd_cross": "k_bwd_cross", "k_dlrm_interact": "k_dlrm_interact",
-           "k_dinb_transpose": "k_dinb_transpose", "k_dinb_clear": "k_dinb_clear",
+           "k_dinb_prep": "k_dinb_prep",
            "k_dinb_map": "k_dinb_map", "k_dinb_fwd": "k_dinb_fwd", "k_dinb_soft": "k_dinb_soft",
            "k_dinb_bwdt": "k_dinb_bwdt", "k_dinb_gq": "k_dinb_gq", "k_dinb_wgrad": "k_dinb_wgrad",
            "k_dinb_reduce": "k_dinb_reduce", "copy": "MulFunctor"}
@@ -644,7 +644,7 @@ def main():
                    "peak": FP32_PEAK_TFLOPS, "frac": round(d_flops / (d_us * 1e-6) / 1e12 / FP32_PEAK_TFLOPS, 4),
                    "bound": "fp32 matrix cores (v_mfma_f32_16x16x4f32): 32 positions per workgroup, "
                             "weight gradients as LDS-tiled vector products",
-                   "traffic": load_traffic(["k_dinb_transpose", "k_dinb_clear", "k_dinb_map",
+                   "traffic": load_traffic(["k_dinb_prep", "k_dinb_map",
                                             "k_dinb_fwd", "k_dinb_soft", "k_dinb_bwdt", "k_dinb_gq",
                                             "k_dinb_wgrad", "k_dinb_reduce"], shash, cfg.name)}
         print(f"[bench] DIN attention backward: {d_us:.1f} us per call ({Pv:.0f} positions)",

@@ -14,16 +14,16 @@
 //
 // fp32 throughout; the per-position products run on the matrix cores
 // (v_mfma_f32_16x16x4f32, 16 positions per tile):
-//   k_dinb_clear   every position index: no sample yet, and its rows of
-//                  grad_seq set to zero (positions past a sample's first
-//                  max_len, and gaps of a padded layout, stay zero);
-//   k_dinb_transpose  W1^T and W2^T in fp32, the A operands of the forward;
+//   k_dinb_prep    every position index marked as having no sample yet;
+//                  W1^T and W2^T in fp32, the A operands of the forward;
 //   k_dinb_map     the sample of every position index;
 //   k_dinb_fwd     the forward of 32 positions per workgroup: S, [x, 1],
 //                  [h1, 1], [h2, 1] and the score of every position;
 //   k_dinb_soft    one wave per sample: the softmax weights p_j and de_j;
 //   k_dinb_bwdt    the backward of 32 positions per workgroup: dz2, dz1, dx,
-//                  each position's sequence-row gradient and query terms;
+//                  each position's sequence-row gradient and query terms
+//                  (zero rows where no position reads: past a sample's
+//                  first max_len, gaps of a padded layout);
 //   k_dinb_gq      the query gradient, each sample's terms in position order;
 //   k_dinb_wgrad   the weight gradients as sums over positions of outer
 //                  products, [dz1]^T [x, 1] (dW1 and db1), [dz2]^T [h1, 1]
@@ -47,26 +47,12 @@ __device__ inline float wload(const void* w, int64_t i, int bf16) {
     return bf16 ? bf16_bits(((const uint16_t*)w)[i]) : ((const float*)w)[i];
 }
 
-__global__ __launch_bounds__(256) void k_dinb_clear(DinBwdArgs a) {
-    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < a.seq_stride;
-         p += (int64_t)gridDim.x * blockDim.x) {
-        a.map[p] = -1;
-        if (a.gs) {
-#pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                float4* r = (float4*)(a.gs + ((int64_t)k * a.seq_stride + p) * REC_DIM);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) r[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-        }
-    }
-}
-
-// W1^T [192][256] and W2^T [256][64] in fp32, once per call, so that every
-// product below reads the weights with consecutive threads on consecutive
-// addresses.
-__global__ __launch_bounds__(256) void k_dinb_transpose(DinBwdArgs a) {
+// Every position index marked as having no sample yet (k_dinb_map then marks
+// the real ones), and W1^T [192][256] and W2^T [256][64] in fp32, the
+// forward tile's A operands (so that its weight reads are coalesced).
+__global__ __launch_bounds__(256) void k_dinb_prep(DinBwdArgs a) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t p = i; p < a.seq_stride; p += (int64_t)gridDim.x * blockDim.x) a.map[p] = -1;
     if (i < 256 * 192) {
         const int64_t o = i / 192, c = i - o * 192;
         a.w1t[c * 256 + o] = wload(a.w1, i, a.bf16);
@@ -433,8 +419,12 @@ __global__ __launch_bounds__(256) void k_dinb_bwdt(DinBwdArgs a) {
     for (int idx = threadIdx.x; idx < kTP * 48; idx += 256) {
         const int pi = idx / 48, c = idx - pi * 48;
         const int64_t pp = p0 + pi;
-        const int b = pp < a.seq_stride ? a.map[pp] : -1;
-        if (b < 0) continue;
+        if (pp >= a.seq_stride) continue;
+        const int b = a.map[pp];
+        if (b < 0) {                   // no position here: a zero row
+            if (a.gs) a.gs[((int64_t)(c >> 4) * a.seq_stride + pp) * REC_DIM + (c & 15)] = 0.0f;
+            continue;
+        }
         const float d0 = dxs[(0 * kTP + pi) * 48 + c], d1 = dxs[(1 * kTP + pi) * 48 + c];
         const float d2 = dxs[(2 * kTP + pi) * 48 + c], d3 = dxs[(3 * kTP + pi) * 48 + c];
         const float sv = a.S[pp * 48 + c];
@@ -590,11 +580,10 @@ int64_t din_bwd_part_stride() { return 256 * kLdX + 64 * kLdH1 + kLdH2; }
 int din_bwd_splits() { return kDinbSplits; }
 
 hipError_t launch_din_bwd(const DinBwdArgs& a, hipStream_t s) {
-    const int64_t cgrid = (a.seq_stride + 255) / 256;
-    if (cgrid > 0) {
-        hipLaunchKernelGGL(k_dinb_clear, dim3((unsigned)(cgrid < 65536 ? cgrid : 65536)), dim3(256), 0, s, a);
-    }
-    hipLaunchKernelGGL(k_dinb_transpose, dim3((256 * 192 + 64 * 256 + 255) / 256), dim3(256), 0, s, a);
+    int64_t pgrid = (a.seq_stride + 255) / 256;
+    const int64_t tgrid = (256 * 192 + 64 * 256 + 255) / 256;
+    pgrid = pgrid < tgrid ? tgrid : (pgrid < 65536 ? pgrid : 65536);
+    hipLaunchKernelGGL(k_dinb_prep, dim3((unsigned)pgrid), dim3(256), 0, s, a);
     const int64_t bgrid = (a.B + 255) / 256;
     hipLaunchKernelGGL(k_dinb_map, dim3((unsigned)(bgrid < 65536 ? bgrid : 65536)), dim3(256), 0, s, a);
     const int64_t tiles = (a.seq_stride + kTP - 1) / kTP;
