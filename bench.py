@@ -204,7 +204,7 @@ def main():
     a = parse()
     if a.traffic_from:
         import synth
-        traffic_from(a.traffic_from[0], a.traffic_from[1], synth.CONFIGS[a.config].name)
+        traffic_from(a.traffic_from[0], a.traffic_from[1], synth.WORKLOADS[a.config].name)
         return
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not supported "
@@ -222,7 +222,7 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     R.lib()
     dev = torch.device("cuda")
-    cfg = synth.CONFIGS[a.config]
+    cfg = synth.WORKLOADS[a.config]
     B = cfg.B
     t_gen = time.perf_counter()
     model = synth.make_model(cfg)
@@ -448,7 +448,7 @@ def main():
         # The start-up rebuild of the hash workload's tables ("集成 DynamicEmb"
         # §6.4: 5 tables, keys and values inserted from storage): clear each
         # table, then insert its stored pairs with STEP scores.
-        hcfg = synth.CONFIGS[5]
+        hcfg = synth.WORKLOADS[5]
         hm = model if cfg.hash_keys else synth.make_model(hcfg)
         htabs = PL.DeviceTables([hm.tables[k] for k in hcfg.hash_keys], dev)
         hk, hv = [], []

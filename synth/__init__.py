@@ -75,7 +75,7 @@ class Config:
     max_len: int = MAX_LEN
 
 
-CONFIGS: Dict[int, Config] = {
+WORKLOADS: Dict[int, Config] = {
     1: Config(1, "tiny_fp32_B256", 256, tuple(TINY_SIZES), "u123", "geom4", "f32"),
     2: Config(2, "taobao_B8192", 8192, tuple(FULL_SIZES), "u123", "geom4", "bf16"),
     3: Config(3, "long_seq_B8192", 8192, tuple(FULL_SIZES), "u123", "unif100", "bf16"),

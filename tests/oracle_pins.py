@@ -114,7 +114,7 @@ def _query_from(pooled):
 
 
 def _tiny(bias=True, B=64, emb_std=0.05, w3_scale=1.0):
-    m = synth.make_model(synth.CONFIGS[1], bias=bias, emb_std=emb_std, w3_scale=w3_scale)
+    m = synth.make_model(synth.WORKLOADS[1], bias=bias, emb_std=emb_std, w3_scale=w3_scale)
     b = synth.make_batch(m, B=B)
     return m, b
 

@@ -97,7 +97,7 @@ def _offsets(lengths):
 
 
 def _model_case(cfg_i, B, seed, with_seq=True, cfg=None):
-    m = synth.make_model(cfg or synth.CONFIGS[cfg_i])
+    m = synth.make_model(cfg or synth.WORKLOADS[cfg_i])
     b = synth.make_batch(m, B=B)
     rng = np.random.default_rng(seed)
     dp = rng.standard_normal((b.B, 256)).astype(np.float32)
@@ -180,11 +180,11 @@ def test_adagrad_sequence_only_and_bags_only():
 
 @pytest.mark.parametrize("cfg_i,B", [(2, 8192), (4, 65536)])
 def test_adagrad_full_size(cfg_i, B):
-    say(f"adagrad full size cfg={synth.CONFIGS[cfg_i].name} B={B}")
+    say(f"adagrad full size cfg={synth.WORKLOADS[cfg_i].name} B={B}")
     m, b, dp, seq, rows, weights = _model_case(cfg_i, B, 20 + cfg_i)
     zero = [np.zeros((_rows(r), 16), np.float32) for r in rows]
     _check(rows, b.B, b.values, b.lengths, _offsets(b.lengths)[:-1], dp, weights, zero, 1e-3,
-           1e-10, seq, f"{synth.CONFIGS[cfg_i].name}")
+           1e-10, seq, f"{synth.WORKLOADS[cfg_i].name}")
 
 
 HASH_TINY = synth.Config(91, "hash_tiny", 64, tuple(synth.TINY_SIZES), "u123", "geom4", "f32",
@@ -196,7 +196,7 @@ def test_adagrad_hash(cfg_i, B):
     """Hash tables ("集成 DynamicEmb" §3.2): a hit updates its slot, a miss
     (which read the zero vector) updates nothing, and empty slots keep their
     NaN bits."""
-    cfg = HASH_TINY if cfg_i == 0 else synth.CONFIGS[cfg_i]
+    cfg = HASH_TINY if cfg_i == 0 else synth.WORKLOADS[cfg_i]
     say(f"adagrad hash cfg={cfg.name} B={B}")
     m, b, dp, seq, rows, weights = _model_case(cfg_i, B, 40 + cfg_i, cfg=cfg)
     zero = [np.zeros((_rows(r), 16), np.float32) for r in rows]

@@ -100,17 +100,17 @@ def _check(m, b, seq_values, offs, stride, query, gatt, max_len=100, weights=Tru
 
 def test_din_bwd_tiny_fp32():
     say("din bwd tiny fp32 B=64")
-    _check(*_case(synth.CONFIGS[1], 64, 1), tag="fp32")
+    _check(*_case(synth.WORKLOADS[1], 64, 1), tag="fp32")
 
 
 def test_din_bwd_sharp():
     say("din bwd sharp (embeddings std 1) B=48")
-    _check(*_case(synth.CONFIGS[1], 48, 2, emb_std=1.0), tag="sharp")
+    _check(*_case(synth.WORKLOADS[1], 48, 2, emb_std=1.0), tag="sharp")
 
 
 def test_din_bwd_bf16_weights():
     say("din bwd bf16 weights B=64")
-    cfg = synth.CONFIGS[2]
+    cfg = synth.WORKLOADS[2]
     small = synth.Config(cfg.index, cfg.name, 64, tuple(synth.TINY_SIZES), cfg.bag_law, cfg.seq_law,
                          cfg.mlp_dtype)
     _check(*_case(small, 64, 3), tag="bf16", dtype="bf16")
@@ -119,7 +119,7 @@ def test_din_bwd_bf16_weights():
 def test_din_bwd_edges():
     say("din bwd edges: empty, one position, past max_len")
     lengths = [0, 1, 3, 0, 40, 1, 7, 12]
-    m, b, sv, offs, stride, q, g = _case(synth.CONFIGS[1], 8, 4, lengths=lengths)
+    m, b, sv, offs, stride, q, g = _case(synth.WORKLOADS[1], 8, 4, lengths=lengths)
     got = _check(m, b, sv, offs, stride, q, g, max_len=10, tag="max_len 10")
     assert not got["gq"][0].any() and not got["gq"][3].any()
     # positions 10..39 of sample 4 are past max_len: their rows are zero
@@ -133,12 +133,12 @@ def test_din_bwd_long_sequences():
     wave holds two positions per lane."""
     say("din bwd long sequences, max_len 128")
     lengths = [0, 1, 63, 64, 65, 100, 127, 128, 129, 200, 5, 128, 96, 17, 250, 2]
-    _check(*_case(synth.CONFIGS[1], len(lengths), 10, lengths=lengths), max_len=128, tag="long")
+    _check(*_case(synth.WORKLOADS[1], len(lengths), 10, lengths=lengths), max_len=128, tag="long")
 
 
 def test_din_bwd_padded_layout_and_inputs_only():
     say("din bwd padded layout, no weight gradients")
-    m, b, sv, offs, stride, q, g = _case(synth.CONFIGS[1], 32, 5, pad_to=100)
+    m, b, sv, offs, stride, q, g = _case(synth.WORKLOADS[1], 32, 5, pad_to=100)
     got = _check(m, b, sv, offs, stride, q, g, weights=False, tag="padded")
     L = b.seq_lengths
     for bb in range(b.B):                          # the gaps get zero rows
@@ -152,7 +152,7 @@ def test_din_bwd_hash():
 
 def test_din_bwd_deterministic():
     say("din bwd twice, bit-identical")
-    args = _case(synth.CONFIGS[1], 96, 7)
+    args = _case(synth.WORKLOADS[1], 96, 7)
     a = _gpu(*args, 100)
     c = _gpu(*args, 100)
     for k in a:
@@ -163,4 +163,4 @@ def test_din_bwd_full_size():
     """The Taobao-shaped batch (B = 8192, geometric lengths, full tables, bf16
     weights), every gradient against the oracle."""
     say("din bwd full size taobao_B8192")
-    _check(*_case(synth.CONFIGS[2], 8192, 8), tag="taobao_B8192", dtype="bf16")
+    _check(*_case(synth.WORKLOADS[2], 8192, 8), tag="taobao_B8192", dtype="bf16")

@@ -195,12 +195,12 @@ def test_clear_then_rebuild_gives_same_forward():
     bit-identical pooled and attention outputs to the generator's tables
     (slots may differ, every lookup does not)."""
     orc = oracle.get()
-    m = synth.make_model(synth.CONFIGS[5])
+    m = synth.make_model(synth.WORKLOADS[5])
     b = synth.make_batch(m, B=4096)
     say("rebuild hash workload B=4096")
     ref_tabs = PL.DeviceTables(m.tables, DEV)
     gpu_tabs = PL.DeviceTables(m.tables, DEV)
-    for k in synth.CONFIGS[5].hash_keys:
+    for k in synth.WORKLOADS[5].hash_keys:
         R.rec_hash_clear(gpu_tabs.desc[k])
         torch.cuda.synchronize()
         cleared = gpu_tabs.to_host(k)

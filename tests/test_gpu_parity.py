@@ -23,7 +23,7 @@ def models():
     def get(i, **kw):
         key = (i, tuple(sorted(kw.items())))
         if key not in cache:
-            cache[key] = synth.make_model(synth.CONFIGS[i], **kw)
+            cache[key] = synth.make_model(synth.WORKLOADS[i], **kw)
         return cache[key]
     return get
 
@@ -316,7 +316,7 @@ def test_din_sharp_fp32(models):
     to the fp32 tolerance; the output bound is the one that score tolerance
     implies: with p = softmax(e), |d att| <= 2 max|de| max_j |s_j| per
     feature, so rows may deviate by 2 * (1e-5 * max|e|) * max|s| / |att|."""
-    m = synth.make_model(synth.CONFIGS[1], bias=True, emb_std=1.0, w3_scale=20.0)
+    m = synth.make_model(synth.WORKLOADS[1], bias=True, emb_std=1.0, w3_scale=20.0)
     b = synth.make_batch(m, B=200)
     r = Run(m, b)
     o = oracle_forward(m, b)
@@ -337,7 +337,7 @@ def test_din_sharp_fp32(models):
 
 def test_din_sharp_bf16_scores(models):
     """Peaky case through the bf16 matrix cores: score-level parity."""
-    m = synth.make_model(synth.CONFIGS[2], bias=True, emb_std=1.0, w3_scale=20.0)
+    m = synth.make_model(synth.WORKLOADS[2], bias=True, emb_std=1.0, w3_scale=20.0)
     b = synth.make_batch(m, B=512)
     r = Run(m, b)
     o = oracle_forward(m, b)

@@ -71,7 +71,7 @@ CASES = [  # cfg, B, pooled_ld, input std, rows checked (None = all), packed bf1
 @pytest.mark.parametrize("cfg,B,ld,std,nsample,packed", CASES)
 def test_towers_parity(cfg, B, ld, std, nsample, packed):
     say(f"towers cfg={cfg} B={B} ld={ld} std={std} packed={packed}")
-    m = synth.make_model(synth.CONFIGS[cfg], bias=True)
+    m = synth.make_model(synth.WORKLOADS[cfg], bias=True)
     tw = PL.DeviceTowers(m.towers, DEV, dtype=m.mlp_dtype, packed=packed)
     tol = FP32_TOL if m.mlp_dtype == "f32" else BF16_TOL
     pooled, att = _inputs(B, ld, std, seed=100 + cfg)
@@ -92,7 +92,7 @@ def test_towers_optional_outputs_and_determinism():
     """Same inputs -> same bits; the outputs do not depend on which optional
     outputs are asked for, nor on whether the weights are packed (the packed
     image only moves the same operands)."""
-    m = synth.make_model(synth.CONFIGS[2], bias=True)
+    m = synth.make_model(synth.WORKLOADS[2], bias=True)
     tw = PL.DeviceTowers(m.towers, DEV)
     plain = PL.DeviceTowers(m.towers, DEV, packed=False)
     assert tw.dtype == R.REC_BF16_PACKED and plain.dtype == R.REC_BF16
@@ -110,7 +110,7 @@ def test_towers_optional_outputs_and_determinism():
 def test_tower_pack_image():
     """The packed image holds every weight exactly once (plus the zero
     padding of wf's columns 176..191), bit for bit."""
-    m = synth.make_model(synth.CONFIGS[2], bias=True)
+    m = synth.make_model(synth.WORKLOADS[2], bias=True)
     tw = PL.DeviceTowers(m.towers, DEV)
     torch.cuda.synchronize()
     img = tw.packed.cpu().numpy().view(np.uint16)
@@ -126,7 +126,7 @@ def test_towers_sample_independence():
     """A sample's outputs depend on its own row only: a permuted batch gives
     the permuted outputs, bit for bit (each workgroup holds 32 samples, so
     this also moves samples across workgroups and ragged tails)."""
-    m = synth.make_model(synth.CONFIGS[2], bias=True)
+    m = synth.make_model(synth.WORKLOADS[2], bias=True)
     tw = PL.DeviceTowers(m.towers, DEV)
     pooled, att = _inputs(1500, 256, 0.05, seed=4)
     perm = np.random.default_rng(2).permutation(1500)
@@ -137,7 +137,7 @@ def test_towers_sample_independence():
 
 
 def test_towers_zero_batch():
-    m = synth.make_model(synth.CONFIGS[2], bias=True)
+    m = synth.make_model(synth.WORKLOADS[2], bias=True)
     tw = PL.DeviceTowers(m.towers, DEV)
     logit = torch.full((4,), 7.0, device=DEV)
     p = torch.zeros(1, 256, device=DEV)
@@ -151,7 +151,7 @@ def test_towers_zero_batch():
 def test_forward_with_towers(cfg, B, whole):
     """Sparse forward + towers against the oracle's whole forward (pooled and
     attention in fp64 feed the oracle's towers)."""
-    m = synth.make_model(synth.CONFIGS[cfg], bias=True)
+    m = synth.make_model(synth.WORKLOADS[cfg], bias=True)
     b = synth.make_batch(m, B=B)
     say(f"forward+towers cfg={cfg} B={B} whole={whole}")
     tabs = PL.DeviceTables(m.tables, DEV)

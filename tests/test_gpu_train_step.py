@@ -22,7 +22,7 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("B", [256, 2048])
 def test_sparse_train_step(B):
     say(f"train step tiny fp32 B={B}")
-    m = synth.make_model(synth.CONFIGS[1], bias=True)
+    m = synth.make_model(synth.WORKLOADS[1], bias=True)
     b = synth.make_batch(m, B=B)
     rng = np.random.default_rng(B)
     T, P = synth.T, int(b.seq_lengths.sum())

@@ -30,7 +30,7 @@ def test_pages_figures():
     assert synth.DIM == F["embedding_dim"]["value"]
     assert synth.MAX_LEN == F["seq_cap"]["value"]
     B = F["batch_size"]["value"]
-    assert synth.CONFIGS[2].B == B
+    assert synth.WORKLOADS[2].B == B
     _close(B * 5 * 3 * synth.DIM, F["real_seq_elements"])
     _close(B * synth.MAX_LEN * 3 * synth.DIM, F["padded_seq_elements"])
     assert 3 * synth.DIM == F["query_width"]["value"] == F["din_output_width"]["value"]
@@ -56,7 +56,7 @@ def test_hash_generator_sanity():
     """Generator checks: the layout invariant (every stored key reachable by
     linear probing from its home with no empty slot in between), digests
     marking exactly the occupied slots, and the 80% hit rate of queries."""
-    cfg = synth.CONFIGS[5]
+    cfg = synth.WORKLOADS[5]
     small = synth.Config(93, "hs", 4096, tuple(synth.TINY_SIZES), "u123", "geom4", "f32",
                          hash_keys=(0, 1), hash_capacity=20000)
     m = synth.make_model(small)
