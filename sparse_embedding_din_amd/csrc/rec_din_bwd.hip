@@ -446,7 +446,16 @@ __global__ __launch_bounds__(256) void k_dinb_gq(DinBwdArgs a) {
     const int L = len < a.max_len ? len : a.max_len;
     const int64_t off = a.seq_offsets[b];
     float s = 0.0f;
-    for (int j = 0; j < L; ++j) s += a.GQP[(off + j) * 48 + c];
+    int j = 0;
+    // four loads in flight per round, added in position order
+    for (; j + 4 <= L; j += 4) {
+        float v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = a.GQP[(off + j + k) * 48 + c];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) s += v[k];
+    }
+    for (; j < L; ++j) s += a.GQP[(off + j) * 48 + c];
     a.gq[i] = s;
 }
 
