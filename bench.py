@@ -458,6 +458,8 @@ def main():
             hk.append(torch.from_numpy(t["keys"][occ]).to(dev))
             hv.append(torch.from_numpy(np.ascontiguousarray(t["values"][occ])).to(dev))
         nkeys = sum(x.numel() for x in hk)
+        ins_wsb = max(R.rec_hash_insert_workspace_bytes(x.numel()) for x in hk)
+        ins_ws = torch.empty(ins_wsb, dtype=torch.uint8, device=dev)
 
         def rebuild_tables(ev=None):
             for i in range(len(hk)):
@@ -465,7 +467,7 @@ def main():
                 if ev is not None:
                     ev[i][0].record(stream)
                 R.rec_hash_insert(htabs.desc[i], hk[i], hv[i], hk[i].numel(), R.REC_SCORE_STEP, 1,
-                                  stream=stream)
+                                  None, ins_ws, ins_wsb, stream=stream)
                 if ev is not None:
                     ev[i][1].record(stream)
 

@@ -21,7 +21,10 @@
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless marked "host".  The caller owns and
  *     allocates every buffer, including workspaces; the library allocates
- *     nothing and keeps no state besides a thread-local error message.
+ *     nothing.  Its only state is a thread-local error message, a cache of
+ *     each device's compute-unit count (read once per device, used to size
+ *     persistent grids), and the thread-local timing events of
+ *     rec_time_next_launch.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *     null stream).  Device buffers must stay alive until that work is done.
  *     Host structs and host arrays are read during the call only.
@@ -34,9 +37,13 @@
  *     arrays; hash tables laid out as described below.  Violations are
  *     undefined behaviour.
  *   - Results are deterministic: the same inputs give bit-identical outputs run
- *     to run.  No floating-point sum depends on the order of atomics; the one
- *     entry point that uses atomics, rec_hash_insert (64-bit compare-and-swap
- *     to claim empty slots), documents what its placement may depend on.
+ *     to run.  No floating-point sum depends on the order of atomics.  Two
+ *     places use atomics: rec_hash_insert (64-bit compare-and-swap to claim
+ *     empty slots; it documents what its placement may depend on), and the
+ *     DIN plan (rec_din_plan, rec_din_attn_fwd, rec_sparse_din_fwd), which
+ *     appends the samples without positions to a list with one atomic add per
+ *     16 samples: the list's order may vary, but each of its samples only gets
+ *     its zero output row, so no output depends on that order.
  */
 #ifndef REC_H
 #define REC_H
@@ -59,11 +66,13 @@ typedef enum {
 enum { REC_DIRECT = 0, REC_HASH = 1 };   /* rec_table.kind */
 enum { REC_F32 = 0, REC_BF16 = 1, REC_BF16_PACKED = 2 };   /* rec_din_mlp.dtype */
 enum { REC_SCORE_NONE = 0, REC_SCORE_STEP = 1, REC_SCORE_LFU = 2 };   /* rec_hash_insert */
+enum { REC_TIME_DIN_ATTN = 0, REC_TIME_GATHER = 1, REC_TIME_SUMS = 2, REC_TIME_TOWERS = 3,
+       REC_TIME_DLRM_INTERACT = 4, REC_TIME_KINDS = 5 };           /* rec_time_next_launch */
 
 #define REC_DIM 16                        /* embedding width of every table */
 #define REC_EMPTY_KEY ((int64_t)-1)       /* empty hash slot; never a valid key */
 #define REC_MAX_TABLES 32                 /* tables per rec_embbag_fwd call */
-#define REC_MAX_SEQ_LEN 128               /* largest max_len for the DIN call */
+#define REC_MAX_SEQ_LEN 1024              /* largest max_len for the DIN calls */
 #define REC_MAX_B 16777215                /* largest batch for the DIN plan */
 #define REC_DIN_PACKED_BYTES 131072       /* packed bf16 W1+W2 (rec_din_pack_mlp) */
 #define REC_TOWER_PACKED_BYTES 614400     /* packed bf16 tower weights (rec_tower_pack_mlp) */
@@ -148,21 +157,18 @@ typedef struct {
  */
 rec_status rec_din_pack_mlp(const rec_din_mlp* mlp, void* packed, size_t packed_bytes, void* stream);
 
-/* Bytes of workspace rec_lengths_to_offsets needs for n lengths. */
-size_t rec_scan_workspace_bytes(int64_t n);
-
 /*
  * offsets = exclusive prefix sum of lengths ("当前现状分析" §2: a jagged
  * feature is values + lengths; offsets locate each bag/sequence).
  *   lengths  int32[n], each >= 0
- *   offsets  int64[n+1]: offsets[0] = 0, offsets[i+1] = offsets[i] + lengths[i]
- *   workspace >= rec_scan_workspace_bytes(n) bytes of device memory (scratch,
- *            contents on entry ignored), 8-byte aligned
- * Errors: REC_EINVAL (null lengths/offsets, n < 0), REC_EWORKSPACE.
+ *   offsets  int64[n+1], 8-byte aligned: offsets[0] = 0, offsets[i+1] =
+ *            offsets[i] + lengths[i]
+ * No workspace: the per-block sums of the scan live in `offsets` itself until
+ * the last of the call's three launches overwrites them.
+ * Errors: REC_EINVAL (null lengths/offsets, n < 0, misaligned offsets).
  * n == 0 writes offsets[0] = 0 (one tiny kernel).
  */
-rec_status rec_lengths_to_offsets(const int32_t* lengths, int64_t n, int64_t* offsets,
-                                  void* workspace, size_t workspace_bytes, void* stream);
+rec_status rec_lengths_to_offsets(const int32_t* lengths, int64_t n, int64_t* offsets, void* stream);
 
 /*
  * Sum-pooled embedding bags over T tables ("当前现状分析" §3, §4.4; DLRM
@@ -230,6 +236,11 @@ rec_status rec_embbag_fwd_kjt(const rec_table* tables, int32_t T, int64_t B,
 rec_status rec_hash_lookup(const rec_table* table, const int64_t* keys, int64_t n,
                            int64_t* slot_out, float* rows_out, void* stream);
 
+/* Bytes of workspace rec_hash_insert needs for n pairs (4 B per pair and a
+ * winner table of 8 B per entry, at least 2n entries); 0 for n < 0 or
+ * n > 2^30. */
+size_t rec_hash_insert_workspace_bytes(int64_t n);
+
 /*
  * Insert-or-assign n (key, values) pairs into a hash table ("集成 DynamicEmb"
  * §6.4: a service rebuilds its tables at start-up by inserting the stored
@@ -246,20 +257,23 @@ rec_status rec_hash_lookup(const rec_table* table, const int64_t* keys, int64_t 
  *              table had no empty slot on the key's probe sequence (the pair
  *              is not stored: no eviction, the NO_EVICTION behaviour), -2 for
  *              REC_EMPTY_KEY (never stored)
- * A key already stored keeps its slot and gets the new values and score; a
- * new key takes the first empty slot of its probe sequence, so the table
- * keeps the placement convention above.  Which empty slot a new key takes
- * can depend on the order in which concurrent lanes claim slots; every
- * lookup result (found or not, and the values) does not.  A key given more
- * than once in one call is stored once; its values are those of one of its
- * occurrences (unspecified which) and LFU counts every occurrence.  Nothing
- * else may read or write the table while the call runs.  Eviction and
- * frequency admission are not performed.
- * Errors: REC_EINVAL.
+ *   workspace  >= rec_hash_insert_workspace_bytes(n) bytes of device memory,
+ *              256-byte aligned, contents on entry ignored
+ * The result is that of inserting the pairs one after another in index
+ * order: a key already stored keeps its slot and gets the new values and
+ * score; a new key takes an empty slot of its probe sequence, so the table
+ * keeps the placement convention above; a key given several times in one
+ * call is stored once, with the values of its last occurrence, and LFU counts
+ * every occurrence.  Which empty slot a new key takes can depend on the order
+ * in which concurrent lanes claim slots; every lookup result (found or not,
+ * and the values) does not.  Nothing else may read or write the table while
+ * the call runs.  Three launches.  Eviction and frequency admission are
+ * rec_hash_admit's.
+ * Errors: REC_EINVAL, REC_EUNSUPPORTED (n > 2^30), REC_EWORKSPACE.
  */
 rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const float* values,
                            int64_t n, int32_t score_mode, uint64_t step, int64_t* slot_out,
-                           void* stream);
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * DLRM dot-product interaction (DLRM essay, wmrh.cn/news/12459, §2.3: the
@@ -300,7 +314,7 @@ size_t rec_din_plan_bytes(int64_t B, int32_t max_len);
  *   - packs the positions: sample b, step j < L_b = min(seq_lengths[b],
  *     max_len) becomes packed position pos_start(b) + j, where pos_start is
  *     the exclusive prefix sum of the L_b;
- *   - records how rec_din_attn_fwd splits the P = sum L_b packed positions
+ *   - records how rec_din_attn_fwd_plan splits the P = sum L_b packed positions
  *     over its waves: ranges of `range_positions` positions (0 = P split
  *     evenly over every wave the device runs at once, rounded up to 16);
  *   - resolves the three sub-feature ids of every packed position to its row
@@ -316,7 +330,7 @@ size_t rec_din_plan_bytes(int64_t B, int32_t max_len);
  *   seq_lengths int32[B], each >= 0
  * Outputs:
  *   plan            >= rec_din_plan_bytes(B, max_len) bytes, 16-byte aligned,
- *                   opaque; used by rec_din_attn_fwd
+ *                   opaque; used by rec_din_attn_fwd_plan
  *   seq_offsets_out int64[B+1] or NULL: exclusive prefix sum of the unclamped
  *                   seq_lengths (the jagged offsets)
  *   rows_out        int64 [3][seq_stride] or NULL: the row/slot of every id
@@ -332,41 +346,86 @@ rec_status rec_din_plan(const rec_table* seq_tables, const int64_t* seq_values,
                         int32_t range_positions, int64_t* seq_offsets_out, int64_t* rows_out,
                         void* plan, size_t plan_bytes, void* stream);
 
+/* Bytes of workspace rec_din_attn_fwd needs for B samples capped at max_len
+ * positions (the plan it builds: about 20 bytes per possible position,
+ * B * max_len, plus per-sample data); 0 for invalid arguments. */
+size_t rec_din_attn_workspace_bytes(int64_t B, int32_t max_len);
+
 /*
- * DIN target attention, padding-free ("当前现状分析" §4.2, §4.4), over a plan
- * from rec_din_plan (same seq_tables, B and max_len).  For sample b with L_b
- * positions (rows resolved by the plan):
- *   s_j = [adgroup row | cate row | brand row] (48 floats; a miss is zeros)
+ * DIN target attention, padding-free, in one call ("当前现状分析" §4.2: the
+ * attention input [q, s, q-s, q*s], attn MLP (256, 64), one score per
+ * position, masked softmax, weighted sum; §4.4: query [B,48], output [B,48];
+ * §4.1: real lengths are ~3-5 of a cap of 100, so positions are packed, never
+ * padded; §6.4 of the same page: the sparse model hands over the query, the
+ * sequence and its lengths).  For sample b with L_b = min(seq_lengths[b],
+ * max_len) positions j < L_b:
+ *   s_j = [adgroup row | cate row | brand row] of the ids
+ *         seq_values[f*seq_stride + off_b + j], f = 0..2, in seq_tables[f]
+ *         (direct: floor-mod row; hash: the slot, a miss reads 16 x +0.0)
  *   q   = query[b*query_ld + query_col[f] + d] (f = 0..2, d < 16), the pooled
  *         target features (for rec_embbag_fwd's output with the 16 deep
  *         features in page order: query_ld 256, query_col {16, 80, 48})
  *   e_j = w3 . relu(W2 relu(W1 [q, s_j, q - s_j, q*s_j] + b1) + b2) + b3
  *   p_j = softmax over j < L_b of e_j (max-subtracted, no temperature)
  *   out[b][0..48) = sum_j p_j s_j;  L_b == 0 gives 48 x +0.0
- * Positions past L_b are never read, so any sequence layout with the same
- * lengths gives bit-identical output.  A sample whose positions the kernel
- * splits between two waves is merged from their partial sums, so a different
- * range_positions (or a device with another number of CUs) may change the
- * last bits of its output (not of scores_out).  The plan is only read.
- *   seq_tables  host array of 3 descriptors (the same as for the plan)
+ * Positions j >= L_b are never read, so any sequence layout with the same
+ * lengths gives bit-identical output.  P = sum_b L_b is the number of packed
+ * positions; packed position pos_start(b) + j (pos_start = exclusive prefix
+ * sum of the L_b) indexes scores_out and weights_out.
+ *   seq_tables  host array of 3 descriptors (adgroup, cate, brand), each at
+ *               most 2^31 - 1 rows
+ *   seq_values  int64 [3][seq_stride] raw ids
+ *   seq_offsets int64[B] giving off_b (any layout, e.g. padded off_b = 100 b),
+ *               or NULL for the packed jagged layout (off_b = exclusive prefix
+ *               sum of the unclamped seq_lengths)
+ *   seq_lengths int32[B], each >= 0;  max_len in [1, REC_MAX_SEQ_LEN]
+ *   query       fp32, rows 16-byte aligned (query_ld and query_col[f]
+ *               multiples of 4);  query_col host int32[3]
  *   mlp         host struct (device arrays inside)
  *   out         fp32 [B][48], 16-byte aligned
- *   scores_out  fp32 [P] or NULL: e at each packed position (P = sum L_b)
+ *   scores_out  fp32 [P] or NULL: e at each packed position
  *   weights_out fp32 [P] or NULL: p at each packed position (needs scores_out)
- * query and query_ld/query_col must give 16-byte aligned rows (query_ld and
- * query_col[f] multiples of 4).
- * Errors: REC_EINVAL (null pointers, bad table/mlp, misalignment, B < 0,
- * max_len out of range, weights_out without scores_out), REC_EWORKSPACE
- * (plan too small for B, max_len).
+ *   rows_out    int64 [3][seq_stride] or NULL: the row/slot (-1: hash miss) of
+ *               every id read (positions past L_b are not written)
+ *   workspace   >= rec_din_attn_workspace_bytes(B, max_len) bytes of device
+ *               memory, 16-byte aligned, contents on entry ignored; it holds
+ *               the plan (packed positions, resolved rows, work split)
+ * Three launches: plan sums, plan build, attention.  A sample whose positions
+ * the attention splits between two waves is merged from their partial sums,
+ * so a device with another number of compute units may change the last bits
+ * of its output (not of scores_out).
+ * Errors: REC_EINVAL (null seq_tables/seq_values/seq_lengths/query/query_col/
+ * mlp/out, bad table or mlp, misalignment, B < 0, max_len outside
+ * [1, REC_MAX_SEQ_LEN], weights_out without scores_out), REC_EUNSUPPORTED
+ * (B > REC_MAX_B, a sequence table above 2^31 - 1 rows), REC_EWORKSPACE
+ * (workspace NULL or smaller than required).  B == 0 is a no-op.
  */
-rec_status rec_din_attn_fwd(const rec_table* seq_tables, const void* plan, size_t plan_bytes,
-                            int64_t B, int32_t max_len, const float* query, int64_t query_ld,
-                            const int32_t* query_col, const rec_din_mlp* mlp, float* out,
-                            float* scores_out, float* weights_out, void* stream);
+rec_status rec_din_attn_fwd(const rec_table* seq_tables, const int64_t* seq_values,
+                            int64_t seq_stride, const int64_t* seq_offsets,
+                            const int32_t* seq_lengths, int32_t max_len, int64_t B,
+                            const float* query, int64_t query_ld, const int32_t* query_col,
+                            const rec_din_mlp* mlp, float* out, float* scores_out,
+                            float* weights_out, int64_t* rows_out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
+ * The attention of rec_din_attn_fwd over a plan built earlier by
+ * rec_din_plan (same seq_tables, B and max_len), for callers that build the
+ * plan on another stream or reuse it: out, scores_out and weights_out are
+ * those of rec_din_attn_fwd; a plan with range_positions != 0 splits the
+ * positions differently, which may change the last bits of a sample cut
+ * between waves.  The plan is only read.  One launch.
+ * Errors: as rec_din_attn_fwd, with REC_EWORKSPACE for a missing plan or one
+ * smaller than rec_din_plan_bytes(B, max_len).
+ */
+rec_status rec_din_attn_fwd_plan(const rec_table* seq_tables, const void* plan, size_t plan_bytes,
+                                 int64_t B, int32_t max_len, const float* query, int64_t query_ld,
+                                 const int32_t* query_col, const rec_din_mlp* mlp, float* out,
+                                 float* scores_out, float* weights_out, void* stream);
 
 /*
  * The whole sparse forward in one call: rec_kjt_sums + rec_din_plan +
- * rec_embbag_fwd_kjt + rec_din_attn_fwd, with the query read from the pooled
+ * rec_embbag_fwd_kjt + rec_din_attn_fwd_plan, with the query read from the pooled
  * output.  The deep and sequence sides share launches (three in all instead
  * of five).  Results are bit-identical to the four calls made one by one.
  * Every pointer is a device pointer except `tables`, `seq_tables` and `mlp`
@@ -574,7 +633,11 @@ size_t rec_din_attn_bwd_workspace_bytes(int64_t seq_stride, int32_t weight_grads
  *                             sums over every sample and position
  * Inputs as rec_din_attn_fwd: seq_tables host [3] (adgroup, cate, brand;
  * direct or hash, a miss reads the zero vector), seq_values int64
- * [3][seq_stride], seq_offsets int64 [B] (first position index of sample b),
+ * [3][seq_stride], seq_offsets int64 [B] (first position index of sample b;
+ * required, and the samples' position ranges [off_b, off_b + L_b) must not
+ * overlap: per-position data lives at the position index, so two samples
+ * sharing one would overwrite each other's terms -- precondition, not
+ * checked),
  * seq_lengths int32 [B], max_len in [1, REC_MAX_SEQ_LEN], query fp32 with row
  * stride query_ld and host query_col[3]; mlp host, dtype REC_F32 or REC_BF16
  * (plain layout; b1 and b2 may be NULL for zero biases).  The arithmetic is
@@ -594,6 +657,30 @@ rec_status rec_din_attn_bwd(const rec_table* seq_tables, const int64_t* seq_valu
                             float* grad_seq, float* dw1, float* db1, float* dw2, float* db2,
                             float* dw3, float* db3, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/*
+ * Measurement hook: the next launch, made by this thread through any entry
+ * point, of the kernel named by `kernel` records hipEvent_t `start` when that
+ * kernel begins and `stop` when it ends (the events are bound to the kernel's
+ * dispatch, hipExtLaunchKernelGGL), so hipEventElapsedTime(start, stop) is the
+ * kernel's own execution time, as a kernel trace measures it, without the
+ * launch's dispatch gap.  Kernels:
+ *   REC_TIME_DIN_ATTN       the DIN attention (rec_din_attn_fwd,
+ *                           rec_din_attn_fwd_plan, rec_sparse_din_fwd)
+ *   REC_TIME_GATHER         the embedding bags (rec_embbag_fwd,
+ *                           rec_embbag_fwd_kjt) or, in rec_sparse_din_fwd, the
+ *                           launch that builds the plan and pools the bags
+ *   REC_TIME_SUMS           the KJT sums (rec_kjt_sums; with the plan sums in
+ *                           rec_sparse_din_fwd)
+ *   REC_TIME_TOWERS         the bf16 towers (rec_towers_fwd)
+ *   REC_TIME_DLRM_INTERACT  the interaction (rec_dlrm_interact)
+ * The events (created by the caller with timing enabled, on the device of
+ * the launch) are used by one launch and then forgotten; start == stop ==
+ * NULL forgets them without a launch.  The setting is thread-local state of
+ * the library.  Not for use while a stream is being captured into a graph.
+ * Errors: REC_EINVAL (unknown kernel, one event NULL and not the other).
+ */
+rec_status rec_time_next_launch(int32_t kernel, void* start, void* stop);
 
 /* Message for the last non-OK status on this thread ("" if none). */
 const char* rec_last_error(void);

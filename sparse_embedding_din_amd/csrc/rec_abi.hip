@@ -12,6 +12,7 @@ using namespace rec;
 namespace {
 
 thread_local std::string g_err;
+thread_local hipEvent_t g_time[REC_TIME_KINDS][2];
 
 rec_status fail(rec_status s, const std::string& msg) {
     g_err = msg;
@@ -73,7 +74,8 @@ int num_cus() {
 rec_status prep_plan(const char* fn, const rec_table* seq_tables, const int64_t* seq_values,
                      int64_t seq_stride, const int64_t* seq_offsets, const int32_t* seq_lengths,
                      int64_t B, int32_t max_len, int32_t range_positions, int64_t* seq_offsets_out,
-                     int64_t* rows_out, void* plan, size_t plan_bytes, PlanArgs* a, bool* work) {
+                     int64_t* rows_out, void* plan, size_t plan_bytes, PlanArgs* a, bool* work,
+                     const char* buf = "plan", const char* need_fn = "rec_din_plan_bytes") {
     const std::string f(fn);
     *work = false;
     if (B < 0) return fail(REC_EINVAL, f + ": B < 0");
@@ -87,10 +89,10 @@ rec_status prep_plan(const char* fn, const rec_table* seq_tables, const int64_t*
     if (B > 0 && (!seq_lengths || !seq_values))
         return fail(REC_EINVAL, f + ": seq_lengths and seq_values are required");
     if (seq_stride < 0) return fail(REC_EINVAL, f + ": seq_stride < 0");
-    if (!plan) return fail(REC_EINVAL, f + ": plan is NULL");
-    if (!aligned16(plan)) return fail(REC_EINVAL, f + ": plan not 16-byte aligned");
+    if (!plan) return fail(REC_EWORKSPACE, f + ": " + buf + " is NULL");
+    if (!aligned16(plan)) return fail(REC_EINVAL, f + ": " + buf + " not 16-byte aligned");
     if (plan_bytes < rec_din_plan_bytes(B, max_len))
-        return fail(REC_EWORKSPACE, f + ": plan smaller than rec_din_plan_bytes(B, max_len)");
+        return fail(REC_EWORKSPACE, f + ": " + buf + " smaller than " + need_fn + "(B, max_len)");
     memset(a, 0, sizeof(*a));
     for (int t = 0; t < 3; ++t) {
         rec_status st = prep_table(seq_tables[t], (f + ": seq table").c_str(), &a->tab[t]);
@@ -117,7 +119,8 @@ rec_status prep_plan(const char* fn, const rec_table* seq_tables, const int64_t*
 rec_status prep_attn(const char* fn, const rec_table* seq_tables, const void* plan, size_t plan_bytes,
                      int64_t B, int32_t max_len, const float* query, int64_t query_ld,
                      const int32_t* query_col, const rec_din_mlp* mlp, float* out,
-                     float* scores_out, float* weights_out, DinArgs* a, bool* work) {
+                     float* scores_out, float* weights_out, DinArgs* a, bool* work,
+                     const char* buf = "plan", const char* need_fn = "rec_din_plan_bytes") {
     const std::string f(fn);
     *work = false;
     if (B < 0) return fail(REC_EINVAL, f + ": B < 0");
@@ -143,9 +146,9 @@ rec_status prep_attn(const char* fn, const rec_table* seq_tables, const void* pl
     if (!aligned16(out)) return fail(REC_EINVAL, f + ": out not 16-byte aligned");
     if (weights_out && !scores_out)
         return fail(REC_EINVAL, f + ": weights_out requires scores_out");
-    if (!plan) return fail(REC_EINVAL, f + ": plan is NULL");
+    if (!plan) return fail(REC_EWORKSPACE, f + ": " + buf + " is NULL");
     if (plan_bytes < rec_din_plan_bytes(B, max_len))
-        return fail(REC_EWORKSPACE, f + ": plan smaller than rec_din_plan_bytes(B, max_len)");
+        return fail(REC_EWORKSPACE, f + ": " + buf + " smaller than " + need_fn + "(B, max_len)");
     memset(a, 0, sizeof(*a));
     for (int t = 0; t < 3; ++t) {
         rec_status s = prep_table(seq_tables[t], (f + ": seq table").c_str(), &a->tab[t]);
@@ -273,7 +276,24 @@ rec_status prep_towers(const char* fn, const rec_tower_mlp* mlp, int64_t B, cons
 
 }  // namespace
 
+bool rec::take_timing(int which, hipEvent_t* start, hipEvent_t* stop) {
+    if (which < 0 || which >= REC_TIME_KINDS || !g_time[which][0]) return false;
+    *start = g_time[which][0];
+    *stop = g_time[which][1];
+    g_time[which][0] = g_time[which][1] = nullptr;
+    return true;
+}
+
 extern "C" {
+
+rec_status rec_time_next_launch(int32_t kernel, void* start, void* stop) {
+    if (kernel < 0 || kernel >= REC_TIME_KINDS) return fail(REC_EINVAL, "rec_time_next_launch: unknown kernel");
+    if ((start == nullptr) != (stop == nullptr))
+        return fail(REC_EINVAL, "rec_time_next_launch: give both events or neither");
+    g_time[kernel][0] = (hipEvent_t)start;
+    g_time[kernel][1] = (hipEvent_t)stop;
+    return ok();
+}
 
 const char* rec_last_error(void) { return g_err.c_str(); }
 
@@ -305,22 +325,12 @@ int64_t rec_host_hash_home(int64_t x, int64_t capacity, uint8_t* digest) {
     return capacity >= 1 ? hash_home(h, capacity) : -1;
 }
 
-size_t rec_scan_workspace_bytes(int64_t n) {
-    return n > 0 ? (size_t)scan_blocks(n) * sizeof(int64_t) : 0;
-}
-
-rec_status rec_lengths_to_offsets(const int32_t* lengths, int64_t n, int64_t* offsets,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+rec_status rec_lengths_to_offsets(const int32_t* lengths, int64_t n, int64_t* offsets, void* stream) {
     if (n < 0) return fail(REC_EINVAL, "rec_lengths_to_offsets: n < 0");
     if (!offsets) return fail(REC_EINVAL, "rec_lengths_to_offsets: offsets is NULL");
     if (n > 0 && !lengths) return fail(REC_EINVAL, "rec_lengths_to_offsets: lengths is NULL");
-    const size_t need = rec_scan_workspace_bytes(n);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(REC_EWORKSPACE, "rec_lengths_to_offsets: workspace smaller than rec_scan_workspace_bytes(n)");
-    if (need > 0 && ((uintptr_t)workspace & 7u))
-        return fail(REC_EINVAL, "rec_lengths_to_offsets: workspace not 8-byte aligned");
-    return hip_status(launch_lengths_to_offsets(lengths, n, offsets, (int64_t*)workspace,
-                                                (hipStream_t)stream),
+    if ((uintptr_t)offsets & 7u) return fail(REC_EINVAL, "rec_lengths_to_offsets: offsets not 8-byte aligned");
+    return hip_status(launch_lengths_to_offsets(lengths, n, offsets, (hipStream_t)stream),
                       "rec_lengths_to_offsets");
 }
 
@@ -390,12 +400,18 @@ rec_status rec_hash_lookup(const rec_table* table, const int64_t* keys, int64_t 
     return hip_status(launch_hash_lookup(a, (hipStream_t)stream), "rec_hash_lookup");
 }
 
+size_t rec_hash_insert_workspace_bytes(int64_t n) {
+    if (n < 0 || n > ((int64_t)1 << 30)) return 0;
+    return align256(4 * (size_t)n) + 8 * (size_t)hash_insert_tag_entries(n);
+}
+
 rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const float* values,
                            int64_t n, int32_t score_mode, uint64_t step, int64_t* slot_out,
-                           void* stream) {
+                           void* workspace, size_t workspace_bytes, void* stream) {
     if (!table) return fail(REC_EINVAL, "rec_hash_insert: table is NULL");
     if (table->kind != REC_HASH) return fail(REC_EINVAL, "rec_hash_insert: table kind is not REC_HASH");
     if (n < 0) return fail(REC_EINVAL, "rec_hash_insert: n < 0");
+    if (n > ((int64_t)1 << 30)) return fail(REC_EUNSUPPORTED, "rec_hash_insert: n above 2^30");
     if (score_mode != REC_SCORE_NONE && score_mode != REC_SCORE_STEP && score_mode != REC_SCORE_LFU)
         return fail(REC_EINVAL, "rec_hash_insert: unknown score_mode");
     if (score_mode != REC_SCORE_NONE && !table->scores)
@@ -409,6 +425,9 @@ rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const fl
     rec_status s = prep_table(*table, "rec_hash_insert: table", &t.tab);
     if (s != REC_OK) return s;
     if (n == 0) return ok();
+    if (!workspace || workspace_bytes < rec_hash_insert_workspace_bytes(n))
+        return fail(REC_EWORKSPACE, "rec_hash_insert: workspace missing or smaller than rec_hash_insert_workspace_bytes(n)");
+    if ((uintptr_t)workspace & 255u) return fail(REC_EINVAL, "rec_hash_insert: workspace not 256-byte aligned");
     HashInsArgs a;
     a.keys = const_cast<int64_t*>(table->keys);
     a.digests = const_cast<uint8_t*>(table->digests);
@@ -421,6 +440,9 @@ rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const fl
     a.mode = score_mode;
     a.step = step;
     a.slot_out = slot_out;
+    a.pair_slot = (int32_t*)workspace;
+    a.tag = (uint64_t*)((char*)workspace + align256(4 * (size_t)n));
+    a.ntag = hash_insert_tag_entries(n);
     return hip_status(launch_hash_insert(a, (hipStream_t)stream), "rec_hash_insert");
 }
 
@@ -488,20 +510,47 @@ rec_status rec_din_plan(const rec_table* seq_tables, const int64_t* seq_values,
     return hip_status(launch_din_plan(a, (hipStream_t)stream), "rec_din_plan");
 }
 
-rec_status rec_din_attn_fwd(const rec_table* seq_tables, const void* plan, size_t plan_bytes,
-                            int64_t B, int32_t max_len, const float* query, int64_t query_ld,
-                            const int32_t* query_col, const rec_din_mlp* mlp, float* out,
-                            float* scores_out, float* weights_out, void* stream) {
+rec_status rec_din_attn_fwd_plan(const rec_table* seq_tables, const void* plan, size_t plan_bytes,
+                                 int64_t B, int32_t max_len, const float* query, int64_t query_ld,
+                                 const int32_t* query_col, const rec_din_mlp* mlp, float* out,
+                                 float* scores_out, float* weights_out, void* stream) {
     DinArgs a;
     bool work;
-    rec_status s = prep_attn("rec_din_attn_fwd", seq_tables, plan, plan_bytes, B, max_len, query,
+    rec_status s = prep_attn("rec_din_attn_fwd_plan", seq_tables, plan, plan_bytes, B, max_len, query,
                              query_ld, query_col, mlp, out, scores_out, weights_out, &a, &work);
     if (s != REC_OK) return s;
     if (!work) return ok();
     const int cus = num_cus();
-    if (cus < 1) return fail(REC_EHIP, "rec_din_attn_fwd: cannot query the device");
+    if (cus < 1) return fail(REC_EHIP, "rec_din_attn_fwd_plan: cannot query the device");
     a.waves = din_waves(cus);
-    return hip_status(launch_din(a, (hipStream_t)stream), "rec_din_attn_fwd");
+    return hip_status(launch_din(a, (hipStream_t)stream), "rec_din_attn_fwd_plan");
+}
+
+size_t rec_din_attn_workspace_bytes(int64_t B, int32_t max_len) { return rec_din_plan_bytes(B, max_len); }
+
+rec_status rec_din_attn_fwd(const rec_table* seq_tables, const int64_t* seq_values, int64_t seq_stride,
+                            const int64_t* seq_offsets, const int32_t* seq_lengths, int32_t max_len,
+                            int64_t B, const float* query, int64_t query_ld, const int32_t* query_col,
+                            const rec_din_mlp* mlp, float* out, float* scores_out, float* weights_out,
+                            int64_t* rows_out, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* fn = "rec_din_attn_fwd";
+    PlanArgs p;
+    DinArgs d;
+    bool wp, wd;
+    rec_status s = prep_plan(fn, seq_tables, seq_values, seq_stride, seq_offsets, seq_lengths, B,
+                             max_len, 0, nullptr, rows_out, workspace, workspace_bytes, &p, &wp,
+                             "workspace", "rec_din_attn_workspace_bytes");
+    if (s != REC_OK) return s;
+    s = prep_attn(fn, seq_tables, workspace, workspace_bytes, B, max_len, query, query_ld, query_col,
+                  mlp, out, scores_out, weights_out, &d, &wd, "workspace", "rec_din_attn_workspace_bytes");
+    if (s != REC_OK) return s;
+    if (!wp || !wd) return ok();
+    const int cus = num_cus();
+    if (cus < 1) return fail(REC_EHIP, "rec_din_attn_fwd: cannot query the device");
+    p.waves = d.waves = din_waves(cus);
+    hipError_t h = launch_din_plan(p, (hipStream_t)stream);
+    if (h == hipSuccess) h = launch_din(d, (hipStream_t)stream);
+    return hip_status(h, fn);
 }
 
 rec_status rec_embbag_fwd_kjt(const rec_table* tables, int32_t T, int64_t B,

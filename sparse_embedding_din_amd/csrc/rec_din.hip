@@ -782,11 +782,11 @@ hipError_t launch_din(const DinArgs& a, hipStream_t s) {
     // kMaxDinGroups workgroups (more groups are looped over)
     const dim3 grid((unsigned)din_groups(a.waves)), block(64 * kDinWaves);
     if (a.dtype == REC_BF16_PACKED)
-        hipLaunchKernelGGL(k_din_attn<REC_BF16_PACKED>, grid, block, 0, s, a);
+        REC_LAUNCH(REC_TIME_DIN_ATTN, k_din_attn<REC_BF16_PACKED>, grid, block, 0, s, a);
     else if (a.dtype == REC_BF16)
-        hipLaunchKernelGGL(k_din_attn<REC_BF16>, grid, block, 0, s, a);
+        REC_LAUNCH(REC_TIME_DIN_ATTN, k_din_attn<REC_BF16>, grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL(k_din_attn<REC_F32>, grid, block, 0, s, a);
+        REC_LAUNCH(REC_TIME_DIN_ATTN, k_din_attn<REC_F32>, grid, block, 0, s, a);
     return hipGetLastError();
 }
 

@@ -245,8 +245,11 @@ __global__ __launch_bounds__(256) void k_dinb_fwd(DinBwdArgs a) {
 }
 
 // Softmax of each sample over its scores, one wave per sample: p_j,
-// dp_j = g . s_j and de_j = p_j (dp_j - sum_k p_k dp_k), reductions as
-// fixed shuffle trees.
+// dp_j = g . s_j and de_j = p_j (dp_j - sum_k p_k dp_k).  Lane l takes the
+// positions j = l, l + 64, ... (any length up to max_len); the max, the
+// denominator and sum_k exp(e_k - m) dp_k are reduced by fixed shuffle
+// trees.  The second pass parks exp(e_j - m) in PW and dp_j in DE, which the
+// same lane rewrites in the third.
 __global__ __launch_bounds__(256) void k_dinb_soft(DinBwdArgs a) {
     const int lane = threadIdx.x & 63;
     const int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -256,44 +259,30 @@ __global__ __launch_bounds__(256) void k_dinb_soft(DinBwdArgs a) {
     if (L <= 0) return;
     const int64_t off = a.seq_offsets[b];
     const float* g = a.gatt + b * 48;
-    float e[2], dp[2];
     float m = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int j = lane + 64 * u;
-        e[u] = -INFINITY;
-        dp[u] = 0.0f;
-        if (j < L) {
-            const int64_t p = off + j;
-            e[u] = a.E[p];
-            float d = 0.0f;
-            for (int c = 0; c < 48; ++c) d += g[c] * a.S[p * 48 + c];
-            dp[u] = d;
-            m = fmaxf(m, e[u]);
-        }
-    }
+    for (int j = lane; j < L; j += 64) m = fmaxf(m, a.E[off + j]);
     for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 64));
-    float ex[2], den = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        ex[u] = lane + 64 * u < L ? expf(e[u] - m) : 0.0f;
-        den += ex[u];
+    float den = 0.0f, edp = 0.0f;
+    for (int j = lane; j < L; j += 64) {
+        const int64_t p = off + j;
+        float dp = 0.0f;
+        for (int c = 0; c < 48; ++c) dp += g[c] * a.S[p * 48 + c];
+        const float ex = expf(a.E[p] - m);
+        den += ex;
+        edp += ex * dp;
+        a.PW[p] = ex;
+        a.DE[p] = dp;
     }
-    for (int d = 32; d >= 1; d >>= 1) den += __shfl_xor(den, d, 64);
-    float pw[2], pdp = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        pw[u] = ex[u] / den;
-        pdp += pw[u] * dp[u];
+    for (int d = 32; d >= 1; d >>= 1) {
+        den += __shfl_xor(den, d, 64);
+        edp += __shfl_xor(edp, d, 64);
     }
-    for (int d = 32; d >= 1; d >>= 1) pdp += __shfl_xor(pdp, d, 64);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int j = lane + 64 * u;
-        if (j < L) {
-            a.PW[off + j] = pw[u];
-            a.DE[off + j] = pw[u] * (dp[u] - pdp);
-        }
+    const float pdp = edp / den;
+    for (int j = lane; j < L; j += 64) {
+        const int64_t p = off + j;
+        const float pw = a.PW[p] / den;
+        a.PW[p] = pw;
+        a.DE[p] = pw * (a.DE[p] - pdp);
     }
 }
 

@@ -115,8 +115,8 @@ int dlrm_stride(int d) { return (d / 4) % 2 == 0 ? d + 4 : d; }
 hipError_t launch_dlrm_interact(const float* z, int64_t B, int F, int d, float* out, int num_cus,
                                 hipStream_t s) {
     const int64_t grid = B < num_cus ? B : num_cus;
-    hipLaunchKernelGGL(k_dlrm_interact, dim3((unsigned)grid), dim3(64 * kDlrmWaves), 0, s, z, B, F, d,
-                       dlrm_stride(d), out);
+    REC_LAUNCH(REC_TIME_DLRM_INTERACT, k_dlrm_interact, dim3((unsigned)grid), dim3(64 * kDlrmWaves), 0, s, z,
+               B, F, d, dlrm_stride(d), out);
     return hipGetLastError();
 }
 

@@ -53,11 +53,11 @@ hipError_t launch_embbag(const EmbArgs& a, hipStream_t s) {
     for (int t = 0; t < a.T; ++t) hash = hash || a.tab[t].kind == REC_HASH;
     const dim3 grid((unsigned)blocks), block(64 * kWaves);
     if (a.offsets) {
-        if (hash) hipLaunchKernelGGL((k_embbag_fwd<true, false>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_embbag_fwd<false, false>), grid, block, 0, s, a);
+        if (hash) REC_LAUNCH(REC_TIME_GATHER, (k_embbag_fwd<true, false>), grid, block, 0, s, a);
+        else REC_LAUNCH(REC_TIME_GATHER, (k_embbag_fwd<false, false>), grid, block, 0, s, a);
     } else {
-        if (hash) hipLaunchKernelGGL((k_embbag_fwd<true, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_embbag_fwd<false, true>), grid, block, 0, s, a);
+        if (hash) REC_LAUNCH(REC_TIME_GATHER, (k_embbag_fwd<true, true>), grid, block, 0, s, a);
+        else REC_LAUNCH(REC_TIME_GATHER, (k_embbag_fwd<false, true>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }

@@ -61,7 +61,7 @@ hipError_t launch_fwd_front(const PlanArgs& p, const EmbArgs& e, hipStream_t s) 
     a.hdr = (int32_t*)pl;
     a.nkjt = (int64_t)e.T * k.nK;
     a.max_len = p.max_len;
-    hipLaunchKernelGGL(k_fwd_sums, dim3((unsigned)(a.nkjt + L.nblocks)), dim3(kScanThreads), 0, s, a);
+    REC_LAUNCH(REC_TIME_SUMS, k_fwd_sums, dim3((unsigned)(a.nkjt + L.nblocks)), dim3(kScanThreads), 0, s, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t nbuild = (p.B + kPlanChunk - 1) / kPlanChunk;
@@ -70,10 +70,10 @@ hipError_t launch_fwd_front(const PlanArgs& p, const EmbArgs& e, hipStream_t s) 
     bool he = false;
     for (int t = 0; t < e.T; ++t) he = he || e.tab[t].kind == REC_HASH;
     const dim3 grid((unsigned)(nbuild + emb_blocks)), block(256);
-    if (hs && he) hipLaunchKernelGGL((k_fwd_gather<true, true>), grid, block, 0, s, p, e, nbuild);
-    else if (hs) hipLaunchKernelGGL((k_fwd_gather<true, false>), grid, block, 0, s, p, e, nbuild);
-    else if (he) hipLaunchKernelGGL((k_fwd_gather<false, true>), grid, block, 0, s, p, e, nbuild);
-    else hipLaunchKernelGGL((k_fwd_gather<false, false>), grid, block, 0, s, p, e, nbuild);
+    if (hs && he) REC_LAUNCH(REC_TIME_GATHER, (k_fwd_gather<true, true>), grid, block, 0, s, p, e, nbuild);
+    else if (hs) REC_LAUNCH(REC_TIME_GATHER, (k_fwd_gather<true, false>), grid, block, 0, s, p, e, nbuild);
+    else if (he) REC_LAUNCH(REC_TIME_GATHER, (k_fwd_gather<false, true>), grid, block, 0, s, p, e, nbuild);
+    else REC_LAUNCH(REC_TIME_GATHER, (k_fwd_gather<false, false>), grid, block, 0, s, p, e, nbuild);
     return hipGetLastError();
 }
 

@@ -3,12 +3,28 @@
 // device), and the kernel launchers each .hip file provides.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "rec.h"
 
 namespace rec {
+
+// Kernel timing (rec_time_next_launch): takes, and clears, the events this
+// thread set for the next launch of kernel class `which`.
+bool take_timing(int which, hipEvent_t* start, hipEvent_t* stop);
+
+// A launch that records the caller's timing events, when set, at the
+// kernel's own start and end (hipExtLaunchKernelGGL), else a plain launch.
+#define REC_LAUNCH(which, kernel, grid, block, shmem, stream, ...)                              \
+    do {                                                                                         \
+        hipEvent_t ev0_, ev1_;                                                                   \
+        if (take_timing(which, &ev0_, &ev1_))                                                    \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, ev0_, ev1_, 0, __VA_ARGS__); \
+        else                                                                                     \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                   \
+    } while (0)
 
 // ---------------------------------------------------------------------------
 // A table as the kernels see it (48 bytes, passed in kernel arguments).
@@ -260,7 +276,7 @@ __host__ __device__ inline int64_t din_span(int64_t P, int32_t req, int64_t wave
 // ---------------------------------------------------------------------------
 // Launchers (return the hipError_t of the launch)
 hipError_t launch_lengths_to_offsets(const int32_t* lengths, int64_t n, int64_t* offsets,
-                                     int64_t* block_sums, hipStream_t s);
+                                     hipStream_t s);
 struct PlanArgs {
     TabDev tab[3];
     const int64_t* seq_values;
@@ -319,7 +335,11 @@ struct HashInsArgs {
     int32_t mode;
     uint64_t step;
     int64_t* slot_out;
+    int32_t* pair_slot;         // workspace: [n] slot of each pair (-1 not stored, -2 empty marker)
+    uint64_t* tag;              // workspace: [ntag] winner table, (slot + 1) << 32 | pair index
+    int64_t ntag;               // a power of two >= 2n
 };
+int64_t hash_insert_tag_entries(int64_t n);
 hipError_t launch_hash_insert(const HashInsArgs& a, hipStream_t s);
 
 // DLRM interaction: Z staged in LDS as 32 * ceil(F / 32) rows of dlrm_stride(d)

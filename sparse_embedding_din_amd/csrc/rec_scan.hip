@@ -6,12 +6,17 @@
 // lengths) and §4.1 (click sequences are short, ~3-5 of a cap of 100, so the
 // attention works on packed positions instead of a [B,100] padding).
 //
-// Two launches, no inter-block waiting: a reduce pass writes one sum per
-// 1024-length block (and per smaller chunk where a consumer wants them); the
-// consumer adds up the sums before its own piece and scans the piece itself.
-// For plain offsets the consumer is an apply pass; for the KJT it is the
-// embedding-bag kernel; for the DIN plan it is the pass that also writes the
-// per-position entries.
+// Plain offsets take three launches and no workspace: a reduce pass writes
+// each 1024-length block's sum into the offsets array itself, at the first
+// slot the block will later own (offsets[1024 k + 1]); one workgroup turns
+// those sums into exclusive block prefixes in place; the apply pass then
+// reads its block's prefix from that slot before writing its offsets over
+// it (no other block reads or writes the slot).  The KJT and the DIN plan
+// use two launches: a reduce pass writes one sum per block (and per smaller
+// chunk where a consumer wants them) into their own buffers, and the
+// consumer adds up the sums before its own piece and scans the piece itself
+// (for the KJT the consumer is the embedding-bag kernel; for the plan, the
+// pass that also writes the per-position entries).
 #include "rec_scan_dev.h"
 
 namespace rec {
@@ -19,7 +24,7 @@ namespace {
 
 __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const int32_t* __restrict__ len,
                                                              int64_t n,
-                                                             int64_t* __restrict__ sums) {
+                                                             int64_t* __restrict__ offsets) {
     __shared__ int64_t red[kScanThreads / 64];
     const int64_t base = (int64_t)blockIdx.x * kScanChunk;
     int64_t raw = 0;
@@ -29,20 +34,35 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const int32_t* __r
         if (idx < n) raw += len[idx];
     }
     raw = block_sum(raw, red);
-    if (threadIdx.x == 0) sums[blockIdx.x] = raw;
+    if (threadIdx.x == 0) offsets[base + 1] = raw;
+}
+
+// One workgroup: the block sums at offsets[1024 k + 1] become the sums of
+// the blocks before k, in block order.
+__global__ __launch_bounds__(kScanThreads) void k_scan_blocks(int64_t nb,
+                                                             int64_t* __restrict__ offsets) {
+    __shared__ int64_t red[kScanThreads / 64];
+    int64_t run = 0;
+    for (int64_t c = 0; c < nb; c += kScanThreads) {
+        const int64_t k = c + threadIdx.x;
+        const int64_t v = k < nb ? offsets[k * kScanChunk + 1] : 0;
+        const int64_t ex = block_excl_scan(v, red);
+        const int64_t tot = block_sum(v, red);
+        if (k < nb) offsets[k * kScanChunk + 1] = run + ex;
+        run += tot;
+    }
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_offsets_apply(const int32_t* __restrict__ len,
                                                                int64_t n,
-                                                               const int64_t* __restrict__ sums,
                                                                int64_t* __restrict__ offsets) {
     __shared__ int32_t sl[kScanChunk + kScanChunk / kScanItems];
     __shared__ int64_t red[kScanThreads / 64];
+    __shared__ int64_t s_before;
     const int64_t base = (int64_t)blockIdx.x * kScanChunk;
-    int64_t before = 0;
-    for (int64_t j = threadIdx.x; j < (int64_t)blockIdx.x; j += kScanThreads) before += sums[j];
-    before = block_sum(before, red);
-    stage_chunk(len, n, base, sl);
+    if (threadIdx.x == 0) s_before = n > 0 ? offsets[base + 1] : 0;
+    stage_chunk(len, n, base, sl);          // its barrier also publishes s_before
+    const int64_t before = s_before;
     const int t = threadIdx.x;
     int64_t loc[kScanItems];
     int64_t run = 0;
@@ -83,21 +103,22 @@ __global__ __launch_bounds__(256) void k_plan_build(const PlanArgs a) {
 }  // namespace
 
 hipError_t launch_lengths_to_offsets(const int32_t* lengths, int64_t n, int64_t* offsets,
-                                     int64_t* block_sums, hipStream_t s) {
+                                     hipStream_t s) {
     const int64_t nb = scan_blocks(n);
     if (nb > 0) {
         hipLaunchKernelGGL(k_scan_reduce, dim3((unsigned)nb), dim3(kScanThreads), 0, s, lengths, n,
-                           block_sums);
+                           offsets);
+        hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(kScanThreads), 0, s, nb, offsets);
     }
     hipLaunchKernelGGL(k_offsets_apply, dim3((unsigned)(nb > 0 ? nb : 1)), dim3(kScanThreads), 0,
-                       s, lengths, n, block_sums, offsets);
+                       s, lengths, n, offsets);
     return hipGetLastError();
 }
 
 hipError_t launch_kjt_sums(const int32_t* lengths, int32_t T, int64_t B, void* sums, hipStream_t s) {
     const KjtLayout k = kjt_layout(T, B);
     char* p = (char*)sums;
-    hipLaunchKernelGGL(k_kjt_sums, dim3((unsigned)(T * k.nK)), dim3(kScanThreads), 0, s, lengths, B,
+    REC_LAUNCH(REC_TIME_SUMS, k_kjt_sums, dim3((unsigned)(T * k.nK)), dim3(kScanThreads), 0, s, lengths, B,
                        k.nK, k.G, (int64_t*)p, (int64_t*)(p + k.off_segp), (int64_t*)(p + k.off_chp));
     return hipGetLastError();
 }

@@ -442,11 +442,11 @@ template <int G>
 hipError_t launch_bf16(const TowerArgs& a, hipStream_t s) {
     const int64_t blocks = (a.B + 16 * G - 1) / (16 * G);
     if (a.dtype == REC_BF16_PACKED)
-        hipLaunchKernelGGL((k_towers_bf16<true, kStream, G>), dim3((unsigned)blocks),
-                           dim3(64 * kWaves), 0, s, a);
+        REC_LAUNCH(REC_TIME_TOWERS, (k_towers_bf16<true, kStream, G>), dim3((unsigned)blocks),
+                   dim3(64 * kWaves), 0, s, a);
     else
-        hipLaunchKernelGGL((k_towers_bf16<false, kStream, G>), dim3((unsigned)blocks),
-                           dim3(64 * kWaves), 0, s, a);
+        REC_LAUNCH(REC_TIME_TOWERS, (k_towers_bf16<false, kStream, G>), dim3((unsigned)blocks),
+                   dim3(64 * kWaves), 0, s, a);
     return hipGetLastError();
 }
 

@@ -4,11 +4,12 @@ four C-ABI calls:
     rec_kjt_sums            (deep KJT lengths -> block and chunk sums)
     rec_din_plan            (sequence lengths/ids -> packed positions, rows)
     rec_embbag_fwd_kjt      (offsets and pooled [B, 256])
-    rec_din_attn_fwd        (attention [B, 48], query read from the pooled output)
+    rec_din_attn_fwd_plan   (attention [B, 48], query read from the pooled output)
 
 With fused=False the deep side is rec_lengths_to_offsets + rec_embbag_fwd.
-run_whole() makes the same forward one rec_sparse_din_fwd call (four
-launches instead of six, bit-identical results).
+run_whole() makes the same forward one rec_sparse_din_fwd call (three
+launches, bit-identical results); din_one_call() is the attention as one
+rec_din_attn_fwd call (plan and attention).
 
 torch provides device memory and the stream; every step runs in librec.
 Inputs are plain numpy arrays / dicts (as the seeded generator produces).
@@ -156,8 +157,6 @@ class SparseDinForward:
         self.seq_arr = tables.array(list(SEQ_KEYS))
         self.query_col = (C.c_int32 * 3)(*[16 * k for k in SEQ_KEYS])
         self.offsets = torch.empty(T * B_max + 1, dtype=torch.int64, device=device)
-        self.ws_bytes = max(R.rec_scan_workspace_bytes(T * B_max), 8)
-        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         self.kjt_bytes = R.rec_kjt_sums_bytes(T, B_max)
         self.kjt = torch.empty(max(self.kjt_bytes, 8), dtype=torch.uint8, device=device)
         self.plan_bytes = R.rec_din_plan_bytes(B_max, max_len)
@@ -177,8 +176,7 @@ class SparseDinForward:
         if self.fused:
             R.rec_kjt_sums(b.lengths, self.T, b.B, self.kjt, self.kjt_bytes, stream)
         else:
-            R.rec_lengths_to_offsets(b.lengths, self.T * b.B, self.offsets, self.ws, self.ws_bytes,
-                                     stream)
+            R.rec_lengths_to_offsets(b.lengths, self.T * b.B, self.offsets, stream)
 
     def plan_step(self, b: DeviceBatch, rows_out=None, stream=None):
         R.rec_din_plan(self.seq_arr, b.seq_values, b.seq_stride, b.seq_offsets, b.seq_lengths,
@@ -194,9 +192,17 @@ class SparseDinForward:
                              self.pooled, rows_out, stream)
 
     def din_step(self, b: DeviceBatch, scores=None, weights=None, stream=None):
-        R.rec_din_attn_fwd(self.seq_arr, self.plan, self.plan_bytes, b.B, self.max_len,
-                           self.pooled, self.T * 16, self.query_col, self.mlp.desc, self.att,
-                           scores, weights, stream)
+        R.rec_din_attn_fwd_plan(self.seq_arr, self.plan, self.plan_bytes, b.B, self.max_len,
+                                self.pooled, self.T * 16, self.query_col, self.mlp.desc, self.att,
+                                scores, weights, stream)
+
+    def din_one_call(self, b: DeviceBatch, scores=None, weights=None, rows_out=None, stream=None):
+        """The attention as one rec_din_attn_fwd call (plan built inside, in
+        the plan buffer), query read from the pooled output."""
+        R.rec_din_attn_fwd(self.seq_arr, b.seq_values, b.seq_stride, b.seq_offsets, b.seq_lengths,
+                           self.max_len, b.B, self.pooled, self.T * 16, self.query_col,
+                           self.mlp.desc, self.att, scores, weights, rows_out, self.plan,
+                           self.plan_bytes, stream)
 
     def tower_step(self, b: DeviceBatch, stream=None):
         R.rec_towers_fwd(self.towers.desc, b.B, self.pooled, self.T * 16, self.att, self.logit,

@@ -19,22 +19,26 @@ REC_OK, REC_EINVAL, REC_EUNSUPPORTED, REC_EHIP, REC_EWORKSPACE = 0, -1, -2, -3, 
 REC_DIRECT, REC_HASH = 0, 1
 REC_F32, REC_BF16, REC_BF16_PACKED = 0, 1, 2
 REC_SCORE_NONE, REC_SCORE_STEP, REC_SCORE_LFU = 0, 1, 2
+(REC_TIME_DIN_ATTN, REC_TIME_GATHER, REC_TIME_SUMS, REC_TIME_TOWERS,
+ REC_TIME_DLRM_INTERACT, REC_TIME_KINDS) = 0, 1, 2, 3, 4, 5
 REC_DIN_PACKED_BYTES = 131072
 REC_TOWER_PACKED_BYTES = 614400
 REC_DIM = 16
 REC_EMPTY_KEY = -1
 REC_MAX_TABLES = 32
-REC_MAX_SEQ_LEN = 128
+REC_MAX_SEQ_LEN = 1024
 REC_MAX_B = 16777215
 
-EXPORTS = ["rec_din_pack_mlp", "rec_scan_workspace_bytes", "rec_lengths_to_offsets", "rec_embbag_fwd",
+EXPORTS = ["rec_din_pack_mlp", "rec_lengths_to_offsets", "rec_embbag_fwd",
            "rec_kjt_sums_bytes", "rec_kjt_sums", "rec_embbag_fwd_kjt", "rec_hash_lookup",
-           "rec_hash_insert", "rec_hash_clear", "rec_dlrm_interact",
-           "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_fwd",
+           "rec_hash_insert_workspace_bytes", "rec_hash_insert", "rec_hash_clear",
+           "rec_dlrm_interact",
+           "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_workspace_bytes", "rec_din_attn_fwd",
+           "rec_din_attn_fwd_plan",
            "rec_sparse_din_fwd_workspace_bytes", "rec_sparse_din_fwd", "rec_towers_fwd",
            "rec_tower_pack_mlp", "rec_embbag_adagrad_workspace_bytes", "rec_embbag_adagrad",
            "rec_din_attn_bwd_workspace_bytes", "rec_din_attn_bwd",
-           "rec_last_error", "rec_version", "rec_host_floor_mod", "rec_host_hash_home",
+           "rec_time_next_launch", "rec_last_error", "rec_version", "rec_host_floor_mod", "rec_host_hash_home",
            "rec_host_hash_probe"]
 
 
@@ -92,9 +96,7 @@ def lib():
             raise RuntimeError(f"{LIB_PATH} is not built: run `python -m sparse_embedding_din_amd.build`")
         L = C.CDLL(LIB_PATH)
         vp, i64, i32, sz = C.c_void_p, C.c_int64, C.c_int32, C.c_size_t
-        L.rec_scan_workspace_bytes.argtypes = [i64]
-        L.rec_scan_workspace_bytes.restype = sz
-        L.rec_lengths_to_offsets.argtypes = [vp, i64, vp, vp, sz, vp]
+        L.rec_lengths_to_offsets.argtypes = [vp, i64, vp, vp]
         L.rec_embbag_fwd.argtypes = [C.POINTER(rec_table), i32, i64, vp, vp, vp, vp, vp, vp]
         L.rec_kjt_sums_bytes.argtypes = [i32, i64]
         L.rec_kjt_sums_bytes.restype = sz
@@ -102,16 +104,24 @@ def lib():
         L.rec_embbag_fwd_kjt.argtypes = [C.POINTER(rec_table), i32, i64, vp, vp, vp, sz, vp, vp, vp,
                                          vp]
         L.rec_hash_lookup.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, vp]
-        L.rec_hash_insert.argtypes = [C.POINTER(rec_table), vp, vp, i64, i32, C.c_uint64, vp, vp]
+        L.rec_hash_insert_workspace_bytes.argtypes = [i64]
+        L.rec_hash_insert_workspace_bytes.restype = sz
+        L.rec_hash_insert.argtypes = [C.POINTER(rec_table), vp, vp, i64, i32, C.c_uint64, vp, vp,
+                                      sz, vp]
         L.rec_hash_clear.argtypes = [C.POINTER(rec_table), vp]
         L.rec_dlrm_interact.argtypes = [vp, i64, i32, i32, vp, vp]
         L.rec_din_plan_bytes.argtypes = [i64, i32]
         L.rec_din_plan_bytes.restype = sz
         L.rec_din_plan.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, i64, i32, i32, vp, vp,
                                    vp, sz, vp]
-        L.rec_din_attn_fwd.argtypes = [C.POINTER(rec_table), vp, sz, i64, i32, vp, i64,
+        L.rec_din_attn_fwd_plan.argtypes = [C.POINTER(rec_table), vp, sz, i64, i32, vp, i64,
+                                            C.POINTER(C.c_int32), C.POINTER(rec_din_mlp), vp, vp,
+                                            vp, vp]
+        L.rec_din_attn_workspace_bytes.argtypes = [i64, i32]
+        L.rec_din_attn_workspace_bytes.restype = sz
+        L.rec_din_attn_fwd.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, i32, i64, vp, i64,
                                        C.POINTER(C.c_int32), C.POINTER(rec_din_mlp), vp, vp, vp,
-                                       vp]
+                                       vp, vp, sz, vp]
         L.rec_din_pack_mlp.argtypes = [C.POINTER(rec_din_mlp), vp, sz, vp]
         L.rec_sparse_din_fwd_workspace_bytes.argtypes = [i32, i64, i32]
         L.rec_sparse_din_fwd_workspace_bytes.restype = sz
@@ -131,9 +141,11 @@ def lib():
         for f in ("rec_lengths_to_offsets", "rec_embbag_fwd", "rec_kjt_sums", "rec_embbag_fwd_kjt",
                   "rec_hash_lookup", "rec_hash_insert", "rec_hash_clear", "rec_dlrm_interact",
                   "rec_din_plan",
-                  "rec_din_attn_fwd", "rec_din_pack_mlp", "rec_sparse_din_fwd", "rec_towers_fwd",
+                  "rec_din_attn_fwd", "rec_din_attn_fwd_plan", "rec_din_pack_mlp", "rec_sparse_din_fwd", "rec_towers_fwd",
                   "rec_tower_pack_mlp", "rec_embbag_adagrad", "rec_din_attn_bwd"):
             getattr(L, f).restype = C.c_int
+        L.rec_time_next_launch.argtypes = [i32, vp, vp]
+        L.rec_time_next_launch.restype = C.c_int
         L.rec_last_error.argtypes = []
         L.rec_last_error.restype = C.c_char_p
         L.rec_version.restype = C.c_int32
@@ -206,17 +218,20 @@ def rec_version() -> int:
     return int(lib().rec_version())
 
 
+def rec_time_next_launch(kernel: int, start=None, stop=None):
+    """start/stop: torch.cuda.Event(enable_timing=True) already recorded once
+    (so that the HIP event exists), or raw event handles."""
+    h = [None if e is None else (e if isinstance(e, int) else e.cuda_event) for e in (start, stop)]
+    _check(lib().rec_time_next_launch(kernel, h[0], h[1]), "rec_time_next_launch")
+
+
 def rec_last_error() -> str:
     return lib().rec_last_error().decode()
 
 
-def rec_scan_workspace_bytes(n: int) -> int:
-    return int(lib().rec_scan_workspace_bytes(n))
-
-
-def rec_lengths_to_offsets(lengths, n: int, offsets, workspace, workspace_bytes: int, stream=None):
-    _check(lib().rec_lengths_to_offsets(_p(lengths), n, _p(offsets), _p(workspace),
-                                        workspace_bytes, _stream(stream)), "rec_lengths_to_offsets")
+def rec_lengths_to_offsets(lengths, n: int, offsets, stream=None):
+    _check(lib().rec_lengths_to_offsets(_p(lengths), n, _p(offsets), _stream(stream)),
+           "rec_lengths_to_offsets")
 
 
 def rec_embbag_fwd(tables: Sequence[rec_table], T: int, B: int, values, lengths, offsets, out,
@@ -246,10 +261,16 @@ def rec_hash_lookup(table_: rec_table, keys, n: int, slot_out=None, rows_out=Non
                                  _stream(stream)), "rec_hash_lookup")
 
 
+def rec_hash_insert_workspace_bytes(n: int) -> int:
+    return int(lib().rec_hash_insert_workspace_bytes(n))
+
+
 def rec_hash_insert(table_: rec_table, keys, values, n: int, score_mode: int = REC_SCORE_NONE,
-                    step: int = 0, slot_out=None, stream=None):
+                    step: int = 0, slot_out=None, workspace=None, workspace_bytes: int = 0,
+                    stream=None):
     _check(lib().rec_hash_insert(C.byref(table_) if table_ is not None else None, _p(keys),
-                                 _p(values), n, score_mode, step, _p(slot_out), _stream(stream)),
+                                 _p(values), n, score_mode, step, _p(slot_out), _p(workspace),
+                                 workspace_bytes, _stream(stream)),
            "rec_hash_insert")
 
 
@@ -280,15 +301,34 @@ def rec_din_plan(seq_tables: Sequence[rec_table], seq_values, seq_stride: int, s
            "rec_din_plan")
 
 
-def rec_din_attn_fwd(seq_tables: Sequence[rec_table], plan, plan_bytes: int, B: int,
-                     max_len: int, query, query_ld: int, query_col: Sequence[int],
-                     mlp: rec_din_mlp, out, scores_out=None, weights_out=None, stream=None):
+def rec_din_attn_workspace_bytes(B: int, max_len: int) -> int:
+    return int(lib().rec_din_attn_workspace_bytes(B, max_len))
+
+
+def rec_din_attn_fwd(seq_tables: Sequence[rec_table], seq_values, seq_stride: int, seq_offsets,
+                     seq_lengths, max_len: int, B: int, query, query_ld: int,
+                     query_col: Sequence[int], mlp: rec_din_mlp, out, scores_out=None,
+                     weights_out=None, rows_out=None, workspace=None, workspace_bytes: int = 0,
+                     stream=None):
     qc = None if query_col is None else (C.c_int32 * 3)(*query_col)
-    _check(lib().rec_din_attn_fwd(_tables(seq_tables), _p(plan), plan_bytes, B, max_len,
-                                  _p(query), query_ld, qc,
+    _check(lib().rec_din_attn_fwd(_tables(seq_tables) if seq_tables is not None else None,
+                                  _p(seq_values), seq_stride, _p(seq_offsets), _p(seq_lengths),
+                                  max_len, B, _p(query), query_ld, qc,
                                   C.byref(mlp) if mlp is not None else None, _p(out),
-                                  _p(scores_out), _p(weights_out), _stream(stream)),
+                                  _p(scores_out), _p(weights_out), _p(rows_out), _p(workspace),
+                                  workspace_bytes, _stream(stream)),
            "rec_din_attn_fwd")
+
+
+def rec_din_attn_fwd_plan(seq_tables: Sequence[rec_table], plan, plan_bytes: int, B: int,
+                          max_len: int, query, query_ld: int, query_col: Sequence[int],
+                          mlp: rec_din_mlp, out, scores_out=None, weights_out=None, stream=None):
+    qc = None if query_col is None else (C.c_int32 * 3)(*query_col)
+    _check(lib().rec_din_attn_fwd_plan(_tables(seq_tables), _p(plan), plan_bytes, B, max_len,
+                                       _p(query), query_ld, qc,
+                                       C.byref(mlp) if mlp is not None else None, _p(out),
+                                       _p(scores_out), _p(weights_out), _stream(stream)),
+           "rec_din_attn_fwd_plan")
 
 
 def rec_towers_fwd(mlp: rec_tower_mlp, B: int, pooled, pooled_ld: int, att, logit,

@@ -66,18 +66,14 @@ def _table(kind=R.REC_DIRECT, rows=100, dim=16, values=FAKE, keys=None, digests=
 
 
 def test_scan_errors(lib):
-    s, msg = _status(lib.rec_lengths_to_offsets, FAKE, -1, FAKE, FAKE, 64, None)
+    s, msg = _status(lib.rec_lengths_to_offsets, FAKE, -1, FAKE, None)
     assert s == R.REC_EINVAL and "n < 0" in msg
-    s, msg = _status(lib.rec_lengths_to_offsets, FAKE, 10, None, FAKE, 64, None)
+    s, msg = _status(lib.rec_lengths_to_offsets, FAKE, 10, None, None)
     assert s == R.REC_EINVAL and "offsets" in msg
-    s, msg = _status(lib.rec_lengths_to_offsets, None, 10, FAKE, FAKE, 64, None)
+    s, msg = _status(lib.rec_lengths_to_offsets, None, 10, FAKE, None)
     assert s == R.REC_EINVAL and "lengths" in msg
-    need = R.rec_scan_workspace_bytes(5000)
-    assert need > 0 and R.rec_scan_workspace_bytes(0) == 0
-    s, msg = _status(lib.rec_lengths_to_offsets, FAKE, 5000, FAKE, FAKE, need - 1, None)
-    assert s == R.REC_EWORKSPACE
-    s, msg = _status(lib.rec_lengths_to_offsets, FAKE, 5000, FAKE, None, need, None)
-    assert s == R.REC_EWORKSPACE
+    s, msg = _status(lib.rec_lengths_to_offsets, FAKE, 10, FAKE + 4, None)
+    assert s == R.REC_EINVAL and "aligned" in msg
 
 
 def test_embbag_errors(lib):
@@ -163,25 +159,34 @@ def test_hash_insert_errors(lib):
         return t
     h, hs = tab(), tab(scores=FAKE)
     ins = lib.rec_hash_insert
-    assert _status(ins, None, FAKE, FAKE, 4, 0, 0, None, None)[0] == R.REC_EINVAL
-    s, msg = _status(ins, C.byref(_table()), FAKE, FAKE, 4, 0, 0, None, None)
+    assert _status(ins, None, FAKE, FAKE, 4, 0, 0, None, None, 0, None)[0] == R.REC_EINVAL
+    s, msg = _status(ins, C.byref(_table()), FAKE, FAKE, 4, 0, 0, None, None, 0, None)
     assert s == R.REC_EINVAL and "REC_HASH" in msg
-    assert _status(ins, C.byref(h), FAKE, FAKE, -1, 0, 0, None, None)[0] == R.REC_EINVAL
-    s, msg = _status(ins, C.byref(hs), FAKE, FAKE, 4, 3, 0, None, None)
+    assert _status(ins, C.byref(h), FAKE, FAKE, -1, 0, 0, None, None, 0, None)[0] == R.REC_EINVAL
+    s, msg = _status(ins, C.byref(hs), FAKE, FAKE, 4, 3, 0, None, None, 0, None)
     assert s == R.REC_EINVAL and "score_mode" in msg
     for mode in (R.REC_SCORE_STEP, R.REC_SCORE_LFU):
-        s, msg = _status(ins, C.byref(h), FAKE, FAKE, 4, mode, 0, None, None)
+        s, msg = _status(ins, C.byref(h), FAKE, FAKE, 4, mode, 0, None, None, 0, None)
         assert s == R.REC_EINVAL and "scores" in msg
-    assert _status(ins, C.byref(tab(scores=FAKE_ODD)), FAKE, FAKE, 4, 1, 0, None, None)[0] == \
+    assert _status(ins, C.byref(tab(scores=FAKE_ODD)), FAKE, FAKE, 4, 1, 0, None, None, 0, None)[0] == \
         R.REC_EINVAL
-    assert _status(ins, C.byref(h), None, FAKE, 4, 0, 0, None, None)[0] == R.REC_EINVAL
-    assert _status(ins, C.byref(h), FAKE, None, 4, 0, 0, None, None)[0] == R.REC_EINVAL
-    assert _status(ins, C.byref(h), FAKE, FAKE_ODD, 4, 0, 0, None, None)[0] == R.REC_EINVAL
-    assert _status(ins, C.byref(tab(digests=FAKE_ODD)), FAKE, FAKE, 4, 0, 0, None, None)[0] == \
+    assert _status(ins, C.byref(h), None, FAKE, 4, 0, 0, None, None, 0, None)[0] == R.REC_EINVAL
+    assert _status(ins, C.byref(h), FAKE, None, 4, 0, 0, None, None, 0, None)[0] == R.REC_EINVAL
+    assert _status(ins, C.byref(h), FAKE, FAKE_ODD, 4, 0, 0, None, None, 0, None)[0] == R.REC_EINVAL
+    assert _status(ins, C.byref(tab(digests=FAKE_ODD)), FAKE, FAKE, 4, 0, 0, None, None, 0, None)[0] == \
         R.REC_EINVAL
-    assert _status(ins, C.byref(tab(rows=0)), FAKE, FAKE, 4, 0, 0, None, None)[0] == R.REC_EINVAL
-    assert _status(ins, C.byref(tab(dim=8)), FAKE, FAKE, 4, 0, 0, None, None)[0] == R.REC_EINVAL
-    assert _status(ins, C.byref(hs), None, None, 0, 2, 5, None, None)[0] == R.REC_OK
+    assert _status(ins, C.byref(tab(rows=0)), FAKE, FAKE, 4, 0, 0, None, None, 0, None)[0] == R.REC_EINVAL
+    assert _status(ins, C.byref(tab(dim=8)), FAKE, FAKE, 4, 0, 0, None, None, 0, None)[0] == R.REC_EINVAL
+    assert _status(ins, C.byref(hs), None, None, 0, 2, 5, None, None, 0, None)[0] == R.REC_OK
+    need = R.rec_hash_insert_workspace_bytes(4)
+    assert need >= 4 * 4 + 8 * 8 and R.rec_hash_insert_workspace_bytes(-1) == 0
+    assert R.rec_hash_insert_workspace_bytes((1 << 30) + 1) == 0
+    s, msg = _status(ins, C.byref(h), FAKE, FAKE, 4, 0, 0, None, None, 0, None)
+    assert s == R.REC_EWORKSPACE and "workspace" in msg
+    assert _status(ins, C.byref(h), FAKE, FAKE, 4, 0, 0, None, FAKE, need - 1, None)[0] == R.REC_EWORKSPACE
+    assert _status(ins, C.byref(h), FAKE, FAKE, 4, 0, 0, None, FAKE + 16, need, None)[0] == R.REC_EINVAL
+    assert _status(ins, C.byref(h), FAKE, FAKE, (1 << 30) + 1, 0, 0, None, FAKE, need, None)[0] == \
+        R.REC_EUNSUPPORTED
     with pytest.raises(R.RecError):
         R.rec_hash_insert(_table(), FAKE, FAKE, 4)
 
@@ -254,7 +259,7 @@ def test_din_plan_errors(lib):
     assert call(lengths=None)[0] == R.REC_EINVAL
     assert call(values=None)[0] == R.REC_EINVAL
     assert call(stride=-1)[0] == R.REC_EINVAL
-    assert call(plan=None)[0] == R.REC_EINVAL
+    assert call(plan=None)[0] == R.REC_EWORKSPACE
     assert call(plan=FAKE_ODD)[0] == R.REC_EINVAL
     assert call(pb=pb - 1)[0] == R.REC_EWORKSPACE
     bad = R._tables([_table(), _table(dim=4), _table()])
@@ -274,7 +279,7 @@ def test_din_attn_errors(lib):
         a.update(kw)
         qc = None if a["qcol"] is None else (C.c_int32 * 3)(*a["qcol"])
         mlp = None if a["mlp"] is None else C.byref(a["mlp"])
-        return _status(lib.rec_din_attn_fwd, a["tables"], a["plan"], a["pb"], a["B"], a["ml"],
+        return _status(lib.rec_din_attn_fwd_plan, a["tables"], a["plan"], a["pb"], a["B"], a["ml"],
                        a["q"], a["qld"], qc, mlp, a["out"], a["scores"], a["weights"], None)
     assert call(B=-1)[0] == R.REC_EINVAL
     assert call(B=R.REC_MAX_B + 1)[0] == R.REC_EUNSUPPORTED
@@ -293,9 +298,58 @@ def test_din_attn_errors(lib):
     assert call(out=FAKE_ODD)[0] == R.REC_EINVAL
     s, msg = call(weights=FAKE)
     assert s == R.REC_EINVAL and "scores_out" in msg
-    assert call(plan=None)[0] == R.REC_EINVAL
+    assert call(plan=None)[0] == R.REC_EWORKSPACE
     assert call(pb=pb - 1)[0] == R.REC_EWORKSPACE
     assert call(B=0, pb=R.rec_din_plan_bytes(0, ml))[0] == R.REC_OK
+
+
+def test_din_attn_one_call_errors(lib):
+    """rec_din_attn_fwd (plan built inside the caller's workspace): every
+    argument error is caught on the host before any launch."""
+    seq = R._tables([_table() for _ in range(3)])
+    B, ml = 64, 100
+    wb = R.rec_din_attn_workspace_bytes(B, ml)
+    assert wb == R.rec_din_plan_bytes(B, ml) and wb > 20 * B * ml
+    assert R.rec_din_attn_workspace_bytes(4, R.REC_MAX_SEQ_LEN) > 20 * 4 * R.REC_MAX_SEQ_LEN
+    assert R.rec_din_attn_workspace_bytes(4, R.REC_MAX_SEQ_LEN + 1) == 0
+    assert R.rec_din_attn_workspace_bytes(-1, ml) == 0 and R.rec_din_attn_workspace_bytes(4, 0) == 0
+    good = R.din_mlp(R.REC_BF16_PACKED, FAKE, FAKE, None, FAKE, FAKE, 0.0)
+
+    def call(**kw):
+        a = dict(tables=seq, values=FAKE, stride=B * 4, offsets=None, lengths=FAKE, ml=ml, B=B,
+                 q=FAKE, qld=256, qcol=(16, 80, 48), mlp=good, out=FAKE, scores=None,
+                 weights=None, rows=None, ws=FAKE, wb=wb)
+        a.update(kw)
+        qc = None if a["qcol"] is None else (C.c_int32 * 3)(*a["qcol"])
+        mlp = None if a["mlp"] is None else C.byref(a["mlp"])
+        return _status(lib.rec_din_attn_fwd, a["tables"], a["values"], a["stride"], a["offsets"],
+                       a["lengths"], a["ml"], a["B"], a["q"], a["qld"], qc, mlp, a["out"],
+                       a["scores"], a["weights"], a["rows"], a["ws"], a["wb"], None)
+    assert call(B=-1)[0] == R.REC_EINVAL
+    assert call(B=R.REC_MAX_B + 1)[0] == R.REC_EUNSUPPORTED
+    for bad_ml in (0, R.REC_MAX_SEQ_LEN + 1):
+        s, msg = call(ml=bad_ml, wb=R.rec_din_attn_workspace_bytes(B, R.REC_MAX_SEQ_LEN))
+        assert s == R.REC_EINVAL and "max_len" in msg
+    assert call(tables=None)[0] == R.REC_EINVAL
+    assert call(values=None)[0] == R.REC_EINVAL
+    assert call(lengths=None)[0] == R.REC_EINVAL
+    assert call(stride=-1)[0] == R.REC_EINVAL
+    assert call(q=None)[0] == R.REC_EINVAL
+    assert call(qcol=None)[0] == R.REC_EINVAL
+    assert call(q=FAKE_ODD)[0] == R.REC_EINVAL
+    assert call(qcol=(16, 82, 48))[0] == R.REC_EINVAL
+    assert call(mlp=None)[0] == R.REC_EINVAL
+    assert call(out=None)[0] == R.REC_EINVAL
+    s, msg = call(weights=FAKE)
+    assert s == R.REC_EINVAL and "scores_out" in msg
+    s, msg = call(ws=None)
+    assert s == R.REC_EWORKSPACE and "workspace" in msg
+    s, msg = call(wb=wb - 1)
+    assert s == R.REC_EWORKSPACE and "rec_din_attn_workspace_bytes" in msg
+    assert call(ws=FAKE_ODD)[0] == R.REC_EINVAL
+    bad = R._tables([_table(), _table(kind=7), _table()])
+    assert call(tables=bad)[0] == R.REC_EINVAL
+    assert call(B=0, wb=R.rec_din_attn_workspace_bytes(0, ml))[0] == R.REC_OK
 
 
 def test_whole_forward_errors(lib):

@@ -136,6 +136,15 @@ def test_din_bwd_long_sequences():
     _check(*_case(synth.WORKLOADS[1], len(lengths), 10, lengths=lengths), max_len=128, tag="long")
 
 
+def test_din_bwd_max_len_1024():
+    """max_len at its largest (1024): sequences of several hundred positions
+    and one past the cap; the softmax wave walks 64 positions per lane step."""
+    say("din bwd sequences up to 1100, max_len 1024")
+    lengths = [700, 0, 1024, 1, 1100, 129, 300, 64, 1023, 5]
+    _check(*_case(synth.WORKLOADS[1], len(lengths), 11, lengths=lengths), max_len=1024,
+           tag="max_len 1024")
+
+
 def test_din_bwd_padded_layout_and_inputs_only():
     say("din bwd padded layout, no weight gradients")
     m, b, sv, offs, stride, q, g = _case(synth.WORKLOADS[1], 32, 5, pad_to=100)

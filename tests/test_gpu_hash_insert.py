@@ -41,7 +41,9 @@ def _insert(dt, keys, vals, mode=R.REC_SCORE_NONE, step=0):
     k = torch.from_numpy(np.ascontiguousarray(keys, np.int64)).to(DEV)
     v = torch.from_numpy(np.ascontiguousarray(vals, np.float32).reshape(-1, 16)).to(DEV)
     slot = torch.full((max(keys.size, 1),), -9, dtype=torch.int64, device=DEV)
-    R.rec_hash_insert(dt.desc[0], k, v, keys.size, mode, step, slot)
+    wsb = R.rec_hash_insert_workspace_bytes(keys.size)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV)
+    R.rec_hash_insert(dt.desc[0], k, v, keys.size, mode, step, slot, ws, wsb)
     torch.cuda.synchronize()
     return slot.cpu().numpy()[: keys.size]
 
@@ -170,7 +172,8 @@ def test_full_table_stores_no_more():
 
 def test_empty_marker_and_duplicates():
     """The empty marker is refused (-2); a key given twice in one call is
-    stored once with the values of one occurrence, and LFU counts both."""
+    stored once with the values of its last occurrence (as inserting the
+    pairs in order leaves it: the oracle's map), and LFU counts both."""
     orc = oracle.get()
     rng = np.random.default_rng(13)
     base = _keys(rng, 300)
@@ -178,15 +181,44 @@ def test_empty_marker_and_duplicates():
     vals = _vals(rng, keys.size)
     dt = _dev_empty(1021)
     slot = _insert(dt, keys, vals, R.REC_SCORE_LFU)
+    ref = orc.empty_hash_table(1021)
+    orc.hash_insert(ref, keys, vals, R.REC_SCORE_LFU)
     g = dt.to_host(0)
     assert slot[-1] == -2 and orc.hash_check(g["keys"], g["digests"]) == 0
     assert np.array_equal(slot[300:400], slot[:100])
     assert np.sum(g["keys"] != synth.EMPTY_KEY) == 300
     for i in range(100):
-        got = g["values"][slot[i]]
-        assert np.array_equal(got, vals[i]) or np.array_equal(got, vals[300 + i])
+        assert np.array_equal(g["values"][slot[i]], vals[300 + i])
         assert g["scores"][slot[i]] == 2
     assert np.all(g["scores"][slot[100:300]] == 1)
+    assert _stored(g) == _stored(ref)
+
+
+@pytest.mark.parametrize("reps", [2, 5])
+def test_duplicates_across_workgroups_last_wins(reps):
+    """Each key appears `reps` times, its occurrences thousands of pairs
+    apart (so in different workgroups) with values that differ in every
+    16-byte piece: the stored row is exactly that of the last occurrence,
+    never a mix, and the map equals the oracle's sequential insert."""
+    orc = oracle.get()
+    rng = np.random.default_rng(100 + reps)
+    base = _keys(rng, 3000)
+    keys = np.concatenate([rng.permutation(base) for _ in range(reps)])
+    vals = np.repeat(np.arange(keys.size, dtype=np.float32)[:, None], 16, axis=1)
+    vals += np.arange(16, dtype=np.float32)[None, :] * 1e-3          # every float4 differs
+    cap = 4099
+    dt = _dev_empty(cap)
+    say(f"duplicates x{reps} across workgroups n={keys.size}")
+    slot = _insert(dt, keys, vals, R.REC_SCORE_LFU)
+    ref = orc.empty_hash_table(cap)
+    orc.hash_insert(ref, keys, vals, R.REC_SCORE_LFU)
+    g = dt.to_host(0)
+    assert orc.hash_check(g["keys"], g["digests"]) == 0
+    assert _stored(g) == _stored(ref)
+    last = {int(k): i for i, k in enumerate(keys)}
+    for k, i in list(last.items())[:500]:
+        assert np.array_equal(g["values"][slot[i]], vals[i])
+    assert np.all(g["scores"][slot[:3000]] == reps)
 
 
 def test_clear_then_rebuild_gives_same_forward():
@@ -210,7 +242,9 @@ def test_clear_then_rebuild_gives_same_forward():
         occ = np.nonzero(t["keys"] != synth.EMPTY_KEY)[0]
         kk = torch.from_numpy(t["keys"][occ]).to(DEV)
         vv = torch.from_numpy(np.ascontiguousarray(t["values"][occ])).to(DEV)
-        R.rec_hash_insert(gpu_tabs.desc[k], kk, vv, occ.size, R.REC_SCORE_STEP, 1)
+        wsb = R.rec_hash_insert_workspace_bytes(occ.size)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+        R.rec_hash_insert(gpu_tabs.desc[k], kk, vv, occ.size, R.REC_SCORE_STEP, 1, None, ws, wsb)
         torch.cuda.synchronize()
         g = gpu_tabs.to_host(k)
         assert orc.hash_check(g["keys"], g["digests"]) == 0

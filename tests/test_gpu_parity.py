@@ -33,16 +33,14 @@ def _tol(model):
 
 
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("n", [0, 1, 5, 4095, 4096, 4097, 131089])
+@pytest.mark.parametrize("n", [0, 1, 5, 1024, 1025, 4095, 4096, 4097, 131089, 300000])
 def test_lengths_to_offsets(n):
     rng = np.random.default_rng(n)
     L = rng.integers(0, 4, size=n).astype(np.int32)
     say(f"scan n={n}")
     lt = torch.from_numpy(L).to(DEV)
     off = torch.full((n + 1,), -5, dtype=torch.int64, device=DEV)
-    wsb = max(R.rec_scan_workspace_bytes(n), 8)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
-    R.rec_lengths_to_offsets(lt, n, off, ws, wsb)
+    R.rec_lengths_to_offsets(lt, n, off)
     torch.cuda.synchronize()
     assert np.array_equal(off.cpu().numpy(), oracle.get().lengths_to_offsets(L))
 
