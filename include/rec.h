@@ -76,6 +76,7 @@ enum { REC_TIME_DIN_ATTN = 0, REC_TIME_GATHER = 1, REC_TIME_SUMS = 2, REC_TIME_T
 #define REC_MAX_B 16777215                /* largest batch for the DIN plan */
 #define REC_DIN_PACKED_BYTES 131072       /* packed bf16 W1+W2 (rec_din_pack_mlp) */
 #define REC_TOWER_PACKED_BYTES 614400     /* packed bf16 tower weights (rec_tower_pack_mlp) */
+#define REC_NOALLOC_SCRATCH_BYTES 33554432 /* static scratch of rec_sparse_din_fwd_noalloc (32 MiB) */
 
 /*
  * One embedding table (host struct; the arrays inside are device memory).
@@ -466,6 +467,29 @@ size_t rec_sparse_din_fwd_workspace_bytes(int32_t T, int64_t B, int32_t max_len)
  * REC_EINVAL (args or workspace NULL or misaligned) and REC_EWORKSPACE.
  * B == 0 is a no-op. */
 rec_status rec_sparse_din_fwd(const rec_fwd_args* args, void* stream);
+
+/*
+ * rec_sparse_din_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same forward, kernels and results, with the workspace
+ * (KJT sums and plan) in a static device array of REC_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) that the library holds on each device it runs on, from load until
+ * the process ends.  args->workspace and args->workspace_bytes are ignored;
+ * the caller still passes every input and output.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * call on a device looks up the array's address there.
+ * Every call on one device shares that device's array and leaves its
+ * contents behind: calls that overlap on one device (on two streams, or from
+ * two threads without ordering) race and give undefined results.  Nothing in
+ * the array needs to start at zero.
+ * Limit: rec_sparse_din_fwd_workspace_bytes(T, B, max_len) must not exceed
+ * REC_NOALLOC_SCRATCH_BYTES (at T = 16, max_len = 100: B up to about 16,000;
+ * the Taobao batch, B = 8192, needs about 16.6 MB).
+ * Errors: those of rec_sparse_din_fwd (messages name
+ * rec_sparse_din_fwd_noalloc), with REC_EWORKSPACE for a batch beyond the
+ * limit (checked before anything else; no device is touched).
+ */
+rec_status rec_sparse_din_fwd_noalloc(const rec_fwd_args* args, void* stream);
 
 /*
  * The rest of the MultiTowerDIN forward after the sparse part: the deep tower

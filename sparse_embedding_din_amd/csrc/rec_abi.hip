@@ -3,6 +3,7 @@
 // check runs before the first HIP call, so a rejected call touches no device.
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "rec_internal.h"
@@ -572,40 +573,63 @@ size_t rec_sparse_din_fwd_workspace_bytes(int32_t T, int64_t B, int32_t max_len)
     return align256(k) + p;
 }
 
-rec_status rec_sparse_din_fwd(const rec_fwd_args* x, void* stream) {
-    if (!x) return fail(REC_EINVAL, "rec_sparse_din_fwd: args is NULL");
-    const char* fn = "rec_sparse_din_fwd";
-    if (!x->workspace) return fail(REC_EINVAL, "rec_sparse_din_fwd: workspace is NULL");
-    if (!aligned16(x->workspace)) return fail(REC_EINVAL, "rec_sparse_din_fwd: workspace not 16-byte aligned");
+}  // extern "C"
+
+namespace {
+
+// rec_sparse_din_fwd's checks and kernel arguments for a given workspace;
+// *work is false when there is nothing to launch.  No HIP call.
+rec_status prep_whole(const char* fn, const rec_fwd_args* x, char* ws, size_t wsb, EmbArgs* e,
+                      PlanArgs* p, DinArgs* d, bool* work) {
+    *work = false;
     const size_t need = rec_sparse_din_fwd_workspace_bytes(x->T, x->B, x->max_len);
     if (need == 0 && (x->T < 1 || x->T > REC_MAX_TABLES || x->B < 0))
-        return fail(REC_EINVAL, "rec_sparse_din_fwd: T or B out of range");
-    if (x->workspace_bytes < need)
-        return fail(REC_EWORKSPACE, "rec_sparse_din_fwd: workspace smaller than rec_sparse_din_fwd_workspace_bytes");
-    char* ws = (char*)x->workspace;
+        return fail(REC_EINVAL, std::string(fn) + ": T or B out of range");
+    if (wsb < need)
+        return fail(REC_EWORKSPACE, std::string(fn) + ": workspace smaller than rec_sparse_din_fwd_workspace_bytes");
     const size_t kb = align256(rec_kjt_sums_bytes(x->T, x->B));
-    EmbArgs e;
-    PlanArgs p;
-    DinArgs d;
     bool we, wp, wd;
     rec_status s = prep_embbag_kjt(fn, x->tables, x->T, x->B, x->values, x->lengths, ws, kb,
-                                   x->offsets_out, x->pooled, x->rows_out, &e, &we);
+                                   x->offsets_out, x->pooled, x->rows_out, e, &we);
     if (s != REC_OK) return s;
     s = prep_plan(fn, x->seq_tables, x->seq_values, x->seq_stride, x->seq_offsets, x->seq_lengths,
                   x->B, x->max_len, x->range_positions, x->seq_offsets_out, x->seq_rows_out,
-                  ws + kb, x->workspace_bytes - kb, &p, &wp);
+                  ws + kb, wsb - kb, p, &wp);
     if (s != REC_OK) return s;
-    s = prep_attn(fn, x->seq_tables, ws + kb, x->workspace_bytes - kb, x->B, x->max_len, x->pooled,
+    s = prep_attn(fn, x->seq_tables, ws + kb, wsb - kb, x->B, x->max_len, x->pooled,
                   (int64_t)x->T * 16, x->query_col, x->mlp, x->att, x->scores_out, x->weights_out,
-                  &d, &wd);
+                  d, &wd);
     if (s != REC_OK) return s;
-    if (!we || !wp || !wd) return ok();
+    *work = we && wp && wd;
+    return REC_OK;
+}
+
+rec_status launch_whole(const char* fn, EmbArgs& e, PlanArgs& p, DinArgs& d, void* stream) {
     const int cus = num_cus();
-    if (cus < 1) return fail(REC_EHIP, "rec_sparse_din_fwd: cannot query the device");
+    if (cus < 1) return fail(REC_EHIP, std::string(fn) + ": cannot query the device");
     p.waves = d.waves = din_waves(cus);
     hipError_t h = launch_fwd_front(p, e, (hipStream_t)stream);
     if (h == hipSuccess) h = launch_din(d, (hipStream_t)stream);
     return hip_status(h, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+rec_status rec_sparse_din_fwd(const rec_fwd_args* x, void* stream) {
+    const char* fn = "rec_sparse_din_fwd";
+    if (!x) return fail(REC_EINVAL, "rec_sparse_din_fwd: args is NULL");
+    if (!x->workspace) return fail(REC_EINVAL, "rec_sparse_din_fwd: workspace is NULL");
+    if (!aligned16(x->workspace)) return fail(REC_EINVAL, "rec_sparse_din_fwd: workspace not 16-byte aligned");
+    EmbArgs e;
+    PlanArgs p;
+    DinArgs d;
+    bool work;
+    rec_status s = prep_whole(fn, x, (char*)x->workspace, x->workspace_bytes, &e, &p, &d, &work);
+    if (s != REC_OK) return s;
+    if (!work) return ok();
+    return launch_whole(fn, e, p, d, stream);
 }
 
 rec_status rec_tower_pack_mlp(const rec_tower_mlp* mlp, void* packed, size_t packed_bytes,
@@ -885,4 +909,65 @@ rec_status rec_din_attn_bwd(const rec_table* seq_tables, const int64_t* seq_valu
         a.db3 = db3;
     }
     return hip_status(launch_din_bwd(a, (hipStream_t)stream), "rec_din_attn_bwd");
+}
+
+// ---------------------------------------------------------------------------
+// rec_sparse_din_fwd_noalloc: the whole forward with its workspace (the KJT
+// sums and the plan) in a static device array instead of a caller's buffer.
+// Each device holds its own copy of the array, from the library's load until
+// the process ends; the host side takes the array's device address once per
+// device (hipGetSymbolAddress, under a lock) and passes that address to the
+// kernels, never the array's name.
+static __device__ __align__(256) unsigned char scratch[REC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+rec_status scratch_of_current_device(const char* fn, void** out) {
+    int dev = -1;
+    hipError_t h = hipGetDevice(&dev);
+    if (h != hipSuccess) return hip_status(h, fn);
+    if (dev < 0 || dev >= kMaxDevices) return fail(REC_EUNSUPPORTED, std::string(fn) + ": device index above 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        h = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (h != hipSuccess) return hip_status(h, fn);
+        if (!p) return fail(REC_EHIP, std::string(fn) + ": no device address for the static scratch");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return REC_OK;
+}
+
+}  // namespace
+
+rec_status rec_sparse_din_fwd_noalloc(const rec_fwd_args* x, void* stream) {
+    const char* fn = "rec_sparse_din_fwd_noalloc";
+    if (!x) return fail(REC_EINVAL, "rec_sparse_din_fwd_noalloc: args is NULL");
+    const size_t need = rec_sparse_din_fwd_workspace_bytes(x->T, x->B, x->max_len);
+    if (need > REC_NOALLOC_SCRATCH_BYTES)
+        return fail(REC_EWORKSPACE, "rec_sparse_din_fwd_noalloc: this batch needs " + std::to_string(need) +
+                                        " bytes of workspace; the static scratch holds REC_NOALLOC_SCRATCH_BYTES = " +
+                                        std::to_string((size_t)REC_NOALLOC_SCRATCH_BYTES));
+    EmbArgs e;
+    PlanArgs p;
+    DinArgs d;
+    bool work;
+    // every check first, against a stand-in address with the scratch's
+    // alignment (nothing is dereferenced on the host), so a rejected call
+    // touches no device
+    char* const stand_in = (char*)(uintptr_t)256;
+    rec_status s = prep_whole(fn, x, stand_in, REC_NOALLOC_SCRATCH_BYTES, &e, &p, &d, &work);
+    if (s != REC_OK) return s;
+    if (!work) return ok();
+    void* ws = nullptr;
+    s = scratch_of_current_device(fn, &ws);
+    if (s != REC_OK) return s;
+    s = prep_whole(fn, x, (char*)ws, REC_NOALLOC_SCRATCH_BYTES, &e, &p, &d, &work);
+    if (s != REC_OK) return s;
+    return launch_whole(fn, e, p, d, stream);
 }

@@ -23,6 +23,7 @@ REC_SCORE_NONE, REC_SCORE_STEP, REC_SCORE_LFU = 0, 1, 2
  REC_TIME_DLRM_INTERACT, REC_TIME_KINDS) = 0, 1, 2, 3, 4, 5
 REC_DIN_PACKED_BYTES = 131072
 REC_TOWER_PACKED_BYTES = 614400
+REC_NOALLOC_SCRATCH_BYTES = 33554432
 REC_DIM = 16
 REC_EMPTY_KEY = -1
 REC_MAX_TABLES = 32
@@ -35,7 +36,8 @@ EXPORTS = ["rec_din_pack_mlp", "rec_lengths_to_offsets", "rec_embbag_fwd",
            "rec_dlrm_interact",
            "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_workspace_bytes", "rec_din_attn_fwd",
            "rec_din_attn_fwd_plan",
-           "rec_sparse_din_fwd_workspace_bytes", "rec_sparse_din_fwd", "rec_towers_fwd",
+           "rec_sparse_din_fwd_workspace_bytes", "rec_sparse_din_fwd", "rec_sparse_din_fwd_noalloc",
+           "rec_towers_fwd",
            "rec_tower_pack_mlp", "rec_embbag_adagrad_workspace_bytes", "rec_embbag_adagrad",
            "rec_din_attn_bwd_workspace_bytes", "rec_din_attn_bwd",
            "rec_time_next_launch", "rec_last_error", "rec_version", "rec_host_floor_mod", "rec_host_hash_home",
@@ -126,6 +128,7 @@ def lib():
         L.rec_sparse_din_fwd_workspace_bytes.argtypes = [i32, i64, i32]
         L.rec_sparse_din_fwd_workspace_bytes.restype = sz
         L.rec_sparse_din_fwd.argtypes = [C.POINTER(rec_fwd_args), vp]
+        L.rec_sparse_din_fwd_noalloc.argtypes = [C.POINTER(rec_fwd_args), vp]
         L.rec_towers_fwd.argtypes = [C.POINTER(rec_tower_mlp), i64, vp, i64, vp, vp, vp, vp, vp]
         L.rec_tower_pack_mlp.argtypes = [C.POINTER(rec_tower_mlp), vp, sz, vp]
         L.rec_din_attn_bwd_workspace_bytes.argtypes = [i64, i32]
@@ -141,7 +144,8 @@ def lib():
         for f in ("rec_lengths_to_offsets", "rec_embbag_fwd", "rec_kjt_sums", "rec_embbag_fwd_kjt",
                   "rec_hash_lookup", "rec_hash_insert", "rec_hash_clear", "rec_dlrm_interact",
                   "rec_din_plan",
-                  "rec_din_attn_fwd", "rec_din_attn_fwd_plan", "rec_din_pack_mlp", "rec_sparse_din_fwd", "rec_towers_fwd",
+                  "rec_din_attn_fwd", "rec_din_attn_fwd_plan", "rec_din_pack_mlp", "rec_sparse_din_fwd",
+                  "rec_sparse_din_fwd_noalloc", "rec_towers_fwd",
                   "rec_tower_pack_mlp", "rec_embbag_adagrad", "rec_din_attn_bwd"):
             getattr(L, f).restype = C.c_int
         L.rec_time_next_launch.argtypes = [i32, vp, vp]
@@ -376,6 +380,12 @@ def fwd_args(T: int, B: int, max_len: int, tables, values, lengths, seq_tables, 
 def rec_sparse_din_fwd(args: Optional[rec_fwd_args], stream=None):
     _check(lib().rec_sparse_din_fwd(C.byref(args) if args is not None else None, _stream(stream)),
            "rec_sparse_din_fwd")
+
+
+def rec_sparse_din_fwd_noalloc(args: Optional[rec_fwd_args], stream=None):
+    _check(lib().rec_sparse_din_fwd_noalloc(C.byref(args) if args is not None else None,
+                                            _stream(stream)),
+           "rec_sparse_din_fwd_noalloc")
 
 
 def rec_host_floor_mod(x: int, n: int) -> int:

@@ -47,7 +47,8 @@ def test_exports_every_declared_function(lib):
 def test_header_constants_match_binding(lib):
     text = open(HEADER).read()
     defs = dict(re.findall(r"#define\s+(REC_\w+)\s+\(?(-?\w+)", text))
-    for name in ("REC_DIM", "REC_MAX_TABLES", "REC_MAX_SEQ_LEN", "REC_MAX_B", "REC_DIN_PACKED_BYTES"):
+    for name in ("REC_DIM", "REC_MAX_TABLES", "REC_MAX_SEQ_LEN", "REC_MAX_B", "REC_DIN_PACKED_BYTES",
+                 "REC_TOWER_PACKED_BYTES", "REC_NOALLOC_SCRATCH_BYTES"):
         assert int(defs[name], 0) == getattr(R, name), name
     enums = dict((k, int(v)) for k, v in re.findall(r"\b(REC_[A-Z0-9_]+)\s*=\s*(-?\d+)", text))
     for name in ("REC_OK", "REC_EINVAL", "REC_EUNSUPPORTED", "REC_EHIP", "REC_EWORKSPACE",
@@ -609,3 +610,18 @@ def test_din_attn_bwd_errors(lib):
     assert call(w=[None] * 6, wsb=small - 1)[0] == R.REC_EWORKSPACE
     assert call(ws=FAKE + 16, wsb=need)[0] == R.REC_EINVAL
     assert call(B=0, wsb=small, w=[None] * 6)[0] == R.REC_OK
+
+
+def test_noalloc_limit_checked_before_the_device(lib):
+    """rec_sparse_din_fwd_noalloc refuses a batch beyond its static scratch
+    with REC_EWORKSPACE before any HIP call (this runs without a GPU)."""
+    assert _status(lib.rec_sparse_din_fwd_noalloc, None, None)[0] == R.REC_EINVAL
+    a = R.rec_fwd_args()
+    a.T, a.max_len, a.B = 16, 100, 1 << 20
+    assert R.rec_sparse_din_fwd_workspace_bytes(16, 1 << 20, 100) > R.REC_NOALLOC_SCRATCH_BYTES
+    s, msg = _status(lib.rec_sparse_din_fwd_noalloc, C.byref(a), None)
+    assert s == R.REC_EWORKSPACE and "REC_NOALLOC_SCRATCH_BYTES" in msg
+    assert R.rec_sparse_din_fwd_workspace_bytes(16, 8192, 100) <= R.REC_NOALLOC_SCRATCH_BYTES
+    a.B = 8192                    # fits: the argument checks come next (no tables given)
+    s, msg = _status(lib.rec_sparse_din_fwd_noalloc, C.byref(a), None)
+    assert s == R.REC_EINVAL and "rec_sparse_din_fwd_noalloc" in msg
