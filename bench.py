@@ -48,6 +48,8 @@ CLEAR_BYTES_PER_SLOT = 8 + 1 + 8                 # key, digest, score
 EMB_BYTES_PER_ID = 8 + 64                  # raw id + one 64-byte row
 EMB_BYTES_PER_BAG = 4 + 8 + 64             # length + offset + pooled output
 DIN_BYTES_PER_POS = 3 * (8 + 64)           # three ids + three rows
+PLAN_BYTES_PER_POS = 3 * 8 + 20            # the plan build: three ids in, 20 B of entries out
+PLAN_BYTES_PER_SAMPLE = 4 + 4 + 8          # length in; packed start, sequence base out
 DIN_BYTES_PER_SAMPLE = 4 + 8 + 4 + 192 + 192   # length, offset, packed start, query, output
 DIN_BYTES_WEIGHTS = 256 * 192 * 2 + 64 * 256 * 2 + (256 + 64 + 64) * 4
 DIN_FLOPS_PER_POS = 2 * (192 * 256 + 256 * 64 + 64)
@@ -67,7 +69,7 @@ def parse():
     p.add_argument("--batches", type=int, default=4)
     p.add_argument("--range-positions", type=int, default=0)
     p.add_argument("--kernel-reps", type=int, default=100)
-    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--cpu-seconds", type=float, default=8.0)
     p.add_argument("--no-graph", action="store_true")
     p.add_argument("--calls", action="store_true",
                    help="run a step as the four separate calls instead of one rec_sparse_din_fwd")
@@ -134,6 +136,8 @@ for _k in ("k_dinb_prep", "k_dinb_map", "k_dinb_fwd", "k_dinb_soft", "k_dinb_bwd
 
 
 CAL_BYTES = 64 << 20            # bytes read (and written) by the calibration copy
+CAL_ROWS = 1 << 20              # random 64-byte rows read (and written) by the calibration gather
+CAL_TABLE_ROWS = 3 << 20        # rows of its table (192 MiB, like the embedding tables)
 KERNELS = {"k_din_attn": "k_din_attn",
            "k_embbag_fwd": "k_embbag_fwd<", "k_fwd_gather": "k_fwd_gather", "k_fwd_sums": "k_fwd_sums",
            "k_towers_bf16": "k_towers_bf16", "k_hash_insert": "k_hash_insert",
@@ -143,7 +147,11 @@ KERNELS = {"k_din_attn": "k_din_attn",
            "k_dinb_prep": "k_dinb_prep",
            "k_dinb_map": "k_dinb_map", "k_dinb_fwd": "k_dinb_fwd", "k_dinb_soft": "k_dinb_soft",
            "k_dinb_bwdt": "k_dinb_bwdt", "k_dinb_gq": "k_dinb_gq", "k_dinb_wgrad": "k_dinb_wgrad",
-           "k_dinb_reduce": "k_dinb_reduce", "copy": "MulFunctor"}
+           "k_dinb_reduce": "k_dinb_reduce", "copy": "MulFunctor", "gather_cal": "ndexSelect"}
+# kernels whose reads are mostly random 64-byte rows: their FETCH_SIZE is scaled
+# by the calibration gather's reading (random 64-byte rows), the others' by
+# the calibration copy's (streaming)
+RANDOM_ROW_KERNELS = {"k_din_attn", "k_embbag_fwd", "k_fwd_gather", "k_bwd_chunks", "k_bwd_cross"}
 
 
 def load_traffic(kernels, shash: str, config: str):
@@ -185,19 +193,105 @@ def traffic_from(fetch_csv: str, write_csv: str, config: str):
     write, nw = per_kernel(write_csv, "WRITE_SIZE")
     f_cal = fetch["copy"] * 1024.0 / CAL_BYTES
     w_cal = write["copy"] * 1024.0 / CAL_BYTES
+    g_cal = fetch["gather_cal"] * 1024.0 / (CAL_ROWS * 64) if "gather_cal" in fetch else None
+    gw_cal = write["gather_cal"] * 1024.0 / (CAL_ROWS * 64) if "gather_cal" in write else None
     only = set(os.environ.get("TRAFFIC_KERNELS", "").split(",")) - {""}
     for k in KERNELS:
-        if k == "copy" or k not in fetch or k not in write or (only and k not in only):
+        if k in ("copy", "gather_cal") or k not in fetch or k not in write or (only and k not in only):
             continue
-        b = fetch[k] * 1024.0 / f_cal + write[k] * 1024.0 / w_cal
+        raw = (fetch[k] + write[k]) * 1024.0
+        by_copy = fetch[k] * 1024.0 / f_cal + write[k] * 1024.0 / w_cal
+        by_gather = None if g_cal is None else fetch[k] * 1024.0 / g_cal + write[k] * 1024.0 / w_cal
+        use_gather = k in RANDOM_ROW_KERNELS and by_gather is not None
+        b = by_gather if use_gather else by_copy
         d = {"kernel": k, "config": config, "src_hash": src_hash(KERNEL_SOURCES[k]),
              "sources": KERNEL_SOURCES[k], "bytes_per_launch": b,
+             "scaled_by": "calibration gather (random 64-byte rows)" if use_gather else "calibration copy",
+             "bytes_raw": raw, "bytes_copy_scaled": by_copy, "bytes_gather_scaled": by_gather,
              "fetch_kib_raw": fetch[k], "write_kib_raw": write[k], "dispatches": [nf[k], nw[k]],
-             "copy_scale": {"fetch": f_cal, "write": w_cal, "bytes": CAL_BYTES}}
+             "copy_scale": {"fetch": f_cal, "write": w_cal, "bytes": CAL_BYTES},
+             "gather_scale": {"fetch": g_cal, "write": gw_cal, "rows": CAL_ROWS, "bytes": CAL_ROWS * 64}}
         with open(os.path.join(ROOT, "profiles", f"traffic_{k}_{config}.json"), "w") as f:
             json.dump(d, f, indent=1)
-        print(f"{k}: {b / 1e6:.3f} MB per launch (fetch {fetch[k]:.0f} KiB, write {write[k]:.0f} KiB)")
-    print(f"copy scale: fetch {f_cal:.3f}, write {w_cal:.3f}")
+        print(f"{k}: {b / 1e6:.3f} MB per launch ({d['scaled_by']}; raw {raw / 1e6:.3f} MB: fetch "
+              f"{fetch[k]:.0f} KiB, write {write[k]:.0f} KiB)")
+    print(f"copy scale: fetch {f_cal:.3f}, write {w_cal:.3f}; gather scale: fetch {g_cal}, write {gw_cal}")
+
+
+_CPU = {}
+
+
+def _cpu_worker(args):
+    """One CPU worker: the oracle forward over its share of batch 0's samples,
+    repeated for `seconds`; returns (samples done, seconds)."""
+    i, workers, seconds = args
+    import numpy as np
+
+    import oracle
+    model, batch = _CPU["model"], _CPU["batch"]
+    shard = np.arange(i, batch.B, workers, dtype=np.int64)
+    orc = oracle.get()
+    t0 = time.perf_counter()
+    done = 0
+    while True:
+        oracle.forward(model, batch, samples=shard, orc=orc)
+        done += shard.size
+        if time.perf_counter() - t0 >= seconds:
+            break
+    return done, time.perf_counter() - t0
+
+
+def cpu_model_name() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_leg(cfg, model, batch, seconds: float, max_workers: int = 16):
+    """The oracle as it stands (fp64 C) timed on this host, before the GPU is
+    touched (the worker pool forks): on one thread over batch 0's samples,
+    then on min(usable cores, max_workers) processes, each over its share of
+    the samples (the oracle's work is independent per sample)."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    import oracle
+    _CPU["model"], _CPU["batch"] = model, batch
+    nproc = os.cpu_count() or 1
+    usable = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else nproc
+    workers = max(1, min(usable, max_workers))
+    orc = oracle.get()
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.forward(model, batch, orc=orc)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 20:
+            break
+    one = reps * batch.B / el
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        t1 = time.perf_counter()
+        res = pool.map(_cpu_worker, [(i, workers, seconds) for i in range(workers)])
+        wall = time.perf_counter() - t1
+    done = sum(r[0] for r in res)
+    many = done / max(r[1] for r in res)
+    print(f"[bench] oracle: {one:.0f} samples/s on 1 thread, {many:.0f} on {workers} processes",
+          file=sys.stderr, flush=True)
+    return {"value": round(many, 1), "unit": "samples/s", "cores": workers, "kind": "oracle",
+            "single_thread": round(one, 1), "nproc": nproc, "usable_cores": usable,
+            "cpu_model": cpu_model_name(),
+            "sample": f"the oracle forward (fp64 C: offsets, embedding bags, DIN attention) of "
+                      f"batch 0 ({batch.B} samples) of {cfg.name}: {reps} passes on one thread "
+                      f"in {el:.1f} s; then {workers} processes, each over every {workers}-th "
+                      f"sample for about {seconds:.0f} s ({done} samples, {wall:.1f} s wall)"}
 
 
 def main():
@@ -212,9 +306,20 @@ def main():
               "collective; multi-GPU runs are not part of it)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
-    import torch
 
     import synth
+    cfg = synth.WORKLOADS[a.config]
+    B = cfg.B
+    t_gen = time.perf_counter()
+    model = synth.make_model(cfg)
+    batches = [synth.make_batch(model, batch_index=i) for i in range(a.batches)]
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
+    # the CPU leg runs first: its worker pool forks, which must happen before
+    # this process touches the GPU
+    cpu = None if a.no_cpu else cpu_leg(cfg, model, batches[0], a.cpu_seconds)
+
+    import torch
+
     from sparse_embedding_din_amd import pipeline as PL
     from sparse_embedding_din_amd import rec as R
 
@@ -222,12 +327,6 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     R.lib()
     dev = torch.device("cuda")
-    cfg = synth.WORKLOADS[a.config]
-    B = cfg.B
-    t_gen = time.perf_counter()
-    model = synth.make_model(cfg)
-    batches = [synth.make_batch(model, batch_index=i) for i in range(a.batches)]
-    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
     tabs = PL.DeviceTables(model.tables, dev)
     mlp = PL.DeviceMLP(model, dev)
     # one set of buffers (offsets, plan, outputs) per resident batch, so any
@@ -269,16 +368,18 @@ def main():
             for f, db in zip(fwds, dbs):
                 step(f, db)
         torch.cuda.synchronize()
-        a.steps = (a.steps + nb - 1) // nb * nb
-        a.warmup = (a.warmup + nb - 1) // nb * nb
+        a.steps = (a.steps + nb - 1) // nb * nb      # whole replays in the timed region
 
     def run_steps(n):
+        """n steps: whole replays of the graph (nb steps each), then any
+        remainder as single steps."""
+        k0 = 0
         if graph is not None:
             for _ in range(n // nb):
                 graph.replay()
-        else:
-            for k in range(n):
-                step(fwds[k % nb], dbs[k % nb])
+            k0 = n // nb * nb
+        for k in range(k0, n):
+            step(fwds[k % nb], dbs[k % nb])
 
     with torch.cuda.stream(stream):
         run_steps(a.warmup)
@@ -347,62 +448,114 @@ def main():
     if in_flight:
         two_stream = min(in_flight.values(), key=lambda r: r["ms_per_step"])
 
-    # Per-call kernel durations, from HIP events recorded on the launch stream
-    # around each call; a spin kernel holds the GPU while the calls are
-    # enqueued so that host enqueue time does not show up between the events.
-    calls = {
-        "offsets": lambda f, db: f.offsets_step(db),
-        "plan": lambda f, db: f.plan_step(db),
-        "embbag": lambda f, db: f.embbag_step(db),
-        "din": lambda f, db: f.din_step(db),
-    }
-    if tw is not None:
-        calls["towers"] = towers_call
-    reps = a.kernel_reps
-    kern_us = {}
-    with torch.cuda.stream(stream):
-        for name, fn in calls.items():
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(reps)]
+    # Kernel durations: HIP events bound to the kernel's own dispatch
+    # (rec_time_next_launch -> hipExtLaunchKernelGGL), so each is the
+    # kernel's execution time alone, as a kernel trace measures it.  The
+    # steps are enqueued one by one (events cannot be bound inside a graph)
+    # on the same launch stream and resident batches as the timed region.
+    # Warm: back to back.  Cold: a 1 GiB read before each step evicts the
+    # L2s and the 256 MB MALL, so the tables (192 MB) come from HBM.
+    def stats(v):
+        v = np.asarray(v, np.float64)
+        return dict(mean=float(v.mean()), median=float(np.median(v)),
+                    p10=float(np.percentile(v, 10)), p90=float(np.percentile(v, 90)), n=int(v.size))
+
+    def timed(enqueue, kinds, reps, flush=None):
+        """enqueue(r) enqueues rep r; kinds: name -> REC_TIME_* (each kernel
+        must launch once per rep).  Returns per-kernel stats (us) and the
+        stats of events around each rep (us)."""
+        evs = [{k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for k in list(kinds) + ["_rep"]} for _ in range(reps)]
+        with torch.cuda.stream(stream):
+            for e in evs:                          # create the HIP events
+                for x, y in e.values():
+                    x.record(stream)
+                    y.record(stream)
             torch.cuda.synchronize()
-            torch.cuda._sleep(20_000_000)
             for r in range(reps):
-                evs[r][0].record(stream)
-                fn(fwds[r % nb], dbs[r % nb])
-                evs[r][1].record(stream)
+                if flush is not None:
+                    flush()
+                for k, w in kinds.items():
+                    R.rec_time_next_launch(w, *evs[r][k])
+                evs[r]["_rep"][0].record(stream)
+                enqueue(r)
+                evs[r]["_rep"][1].record(stream)
             torch.cuda.synchronize()
-            d = np.array([s.elapsed_time(e) * 1e3 for s, e in evs])
-            kern_us[name] = dict(mean=float(d.mean()), median=float(np.median(d)),
-                                 p10=float(np.percentile(d, 10)), p90=float(np.percentile(d, 90)))
-    print(f"[bench] per-call us: " + ", ".join(f"{k}={v['median']:.2f}" for k, v in kern_us.items()),
-          file=sys.stderr, flush=True)
+        out = {k: stats([e[k][0].elapsed_time(e[k][1]) * 1e3 for e in evs]) for k in kinds}
+        return out, stats([e["_rep"][0].elapsed_time(e["_rep"][1]) * 1e3 for e in evs])
+
+    reps = a.kernel_reps
+    step_kinds = {"sums": R.REC_TIME_SUMS, "gather": R.REC_TIME_GATHER, "din": R.REC_TIME_DIN_ATTN}
+    kern_us, _ = timed(lambda r: fwds[r % nb].run_whole(dbs[r % nb]), step_kinds, reps)
+
+    def calls_rep(r):
+        f, db = fwds[r % nb], dbs[r % nb]
+        f.offsets_step(db)
+        f.plan_step(db)
+        f.embbag_step(db)
+        f.din_step(db)
+    call_us, _ = timed(calls_rep, {"embbag": R.REC_TIME_GATHER, "din_plan": R.REC_TIME_DIN_ATTN}, reps)
+    if tw is not None:
+        kern_us["towers"] = timed(lambda r: towers_call(fwds[r % nb], dbs[r % nb]),
+                                  {"towers": R.REC_TIME_TOWERS}, reps)[0]["towers"]
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)     # 1 GiB
+    flush_buf.fill_(1.0)
+    flush_out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush():
+        torch.sum(flush_buf, dim=0, out=flush_out)
+    cold_reps = max(10, reps // 4)
+    cold_us, _ = timed(lambda r: fwds[r % nb].run_whole(dbs[r % nb]), step_kinds, cold_reps, flush)
+    # the step's wall time, warm and cold, one graph replay per step (a graph
+    # per resident batch), events around each replay
+    step_graphs = []
+    for f, db in zip(fwds, dbs):
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1, stream=stream):
+            step(f, db)
+        step_graphs.append(g1)
+    torch.cuda.synchronize()
+    _, warm_step = timed(lambda r: step_graphs[r % nb].replay(), {}, reps)
+    _, cold_step = timed(lambda r: step_graphs[r % nb].replay(), {}, cold_reps, flush)
+    del step_graphs
+    cold_calls, _ = timed(calls_rep, {"embbag": R.REC_TIME_GATHER, "din_plan": R.REC_TIME_DIN_ATTN},
+                          cold_reps, flush)
+    del flush_buf
+    print(f"[bench] kernel us (warm): " + ", ".join(f"{k}={v['mean']:.2f}" for k, v in kern_us.items())
+          + f"; calls: embbag={call_us['embbag']['mean']:.2f} din={call_us['din_plan']['mean']:.2f}"
+          + f"; cold: " + ", ".join(f"{k}={v['mean']:.2f}" for k, v in cold_us.items())
+          + f", step {cold_step['mean']:.2f} (warm {warm_step['mean']:.2f})", file=sys.stderr, flush=True)
 
     # algorithmic work of the average batch
     nnz = float(np.mean([b.values.size for b in batches]))
     P = float(np.mean([np.minimum(b.seq_lengths, cfg.max_len).sum() for b in batches]))
     emb_bytes = nnz * EMB_BYTES_PER_ID + synth.T * B * EMB_BYTES_PER_BAG
+    plan_bytes = P * PLAN_BYTES_PER_POS + B * PLAN_BYTES_PER_SAMPLE
     din_bytes = P * DIN_BYTES_PER_POS + B * DIN_BYTES_PER_SAMPLE + DIN_BYTES_WEIGHTS
     din_flops = P * DIN_FLOPS_PER_POS
-    emb_t = kern_us["embbag"]["mean"] * 1e-6
-    din_t = kern_us["din"]["mean"] * 1e-6
     bf16 = mlp.dtype in (R.REC_BF16, R.REC_BF16_PACKED)
     peak_mfma = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
-    emb_gbs = emb_bytes / emb_t / 1e9
-    din_tflops = din_flops / din_t / 1e12
     shash = src_hash()
-    if din_t >= emb_t:
-        roof = {"kernel": "rec_din_attn_fwd (k_din_attn)", "bound": "mfma",
-                "achieved": round(din_tflops, 2),
-                "peak": peak_mfma, "unit": "TFLOP/s", "frac": round(din_tflops / peak_mfma, 4),
-                "traffic": load_traffic(["k_din_attn"], shash, cfg.name),
-                "per_launch": {"flops": din_flops, "bytes": din_bytes, "positions": P, "samples": B},
-                "avg_launch_us": round(kern_us["din"]["mean"], 3)}
-    else:
-        roof = {"kernel": "k_embbag_fwd", "bound": "hbm", "achieved": round(emb_gbs, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(emb_gbs / HBM_PEAK_GBS, 4),
-                "traffic": load_traffic(["k_embbag_fwd"], shash, cfg.name),
-                "per_launch": {"bytes": emb_bytes, "ids": nnz, "bags": synth.T * B},
-                "avg_launch_us": round(kern_us["embbag"]["mean"], 3)}
+
+    def rates(ku, cu):
+        din_t = ku["din"]["mean"] * 1e-6
+        return {"din_tflops": round(din_flops / din_t / 1e12, 2),
+                "din_mfma_frac": round(din_flops / din_t / 1e12 / peak_mfma, 4),
+                "gather_gb_s": round((emb_bytes + plan_bytes) / (ku["gather"]["mean"] * 1e-6) / 1e9, 1),
+                "gather_hbm_frac": round((emb_bytes + plan_bytes) / (ku["gather"]["mean"] * 1e-6)
+                                         / 1e9 / HBM_PEAK_GBS, 4),
+                "embbag_gb_s": round(emb_bytes / (cu["embbag"]["mean"] * 1e-6) / 1e9, 1),
+                "embbag_hbm_frac": round(emb_bytes / (cu["embbag"]["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    warm_rates, cold_rates = rates(kern_us, call_us), rates(cold_us, cold_calls)
+    din_tflops = warm_rates["din_tflops"]
+    roof = {"kernel": "k_din_attn (the attention launch of rec_sparse_din_fwd)", "bound": "mfma",
+            "achieved": din_tflops, "peak": peak_mfma, "unit": "TFLOP/s",
+            "frac": round(din_tflops / peak_mfma, 4),
+            "traffic": load_traffic(["k_din_attn"], shash, cfg.name),
+            "per_launch": {"flops": din_flops, "bytes": din_bytes, "positions": P, "samples": B},
+            "avg_launch_us": round(kern_us["din"]["mean"], 3),
+            "timing": "mean kernel execution time of the attention launch over "
+                      f"{kern_us['din']['n']} warm steps (HIP events bound to the dispatch)"}
 
     # The whole MultiTowerDIN forward (sparse step + towers), graph-replayed
     # the same way, for the record; `value` stays the sparse step.
@@ -458,7 +611,7 @@ def main():
             hk.append(torch.from_numpy(t["keys"][occ]).to(dev))
             hv.append(torch.from_numpy(np.ascontiguousarray(t["values"][occ])).to(dev))
         nkeys = sum(x.numel() for x in hk)
-        ins_wsb = max(R.rec_hash_insert_workspace_bytes(x.numel()) for x in hk)
+        ins_wsb = max(R.rec_hash_insert_workspace_bytes(x.numel(), hcfg.hash_capacity) for x in hk)
         ins_ws = torch.empty(ins_wsb, dtype=torch.uint8, device=dev)
 
         def rebuild_tables(ev=None):
@@ -666,17 +819,8 @@ def main():
             for _ in range(3):
                 R.rec_dlrm_interact(zi, Bi, Fi, di, oi, stream=stream)
             torch.cuda.synchronize()
-            reps_i = 20
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(reps_i)]
-            torch.cuda._sleep(20_000_000)
-            for r in range(reps_i):
-                evs[r][0].record(stream)
-                R.rec_dlrm_interact(zi, Bi, Fi, di, oi, stream=stream)
-                evs[r][1].record(stream)
-            torch.cuda.synchronize()
-        d = np.array([s_.elapsed_time(e_) * 1e3 for s_, e_ in evs])
-        i_us = float(d.mean())
+        i_us = timed(lambda r: R.rec_dlrm_interact(zi, Bi, Fi, di, oi, stream=stream),
+                     {"interact": R.REC_TIME_DLRM_INTERACT}, 20)[0]["interact"]["mean"]
         i_flops = 2.0 * di * npairs * Bi
         i_bytes = 4.0 * (Fi * di + npairs) * Bi
         interaction = {"entry": "rec_dlrm_interact (upper triangle with the diagonal of Z Z^T)",
@@ -692,23 +836,6 @@ def main():
         print(f"[bench] DLRM interaction: {i_us:.1f} us for {Bi} samples of {Fi} x {di}",
               file=sys.stderr, flush=True)
         del zi, oi
-
-    cpu = None
-    if not a.no_cpu:
-        import oracle
-        orc = oracle.get()
-        t0 = time.perf_counter()
-        reps_cpu = 0
-        while True:
-            oracle.forward(model, batches[0], orc=orc)
-            reps_cpu += 1
-            el = time.perf_counter() - t0
-            if el >= a.cpu_seconds or reps_cpu >= 20:
-                break
-        cpu = {"value": round(reps_cpu * B / el, 1), "unit": "samples/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"{reps_cpu} oracle forwards (fp64 C, single thread: offsets, embedding "
-                         f"bags, DIN attention) of batch 0 ({B} samples) of {cfg.name}, {el:.1f} s"}
 
     # `value` is whole-job throughput: with two batches in flight when that is
     # faster (every step is still one whole pass over one resident batch).
@@ -745,9 +872,12 @@ def main():
         "single_stream": single,
         "batches_in_flight": list(in_flight.values()),
         "kernels_us": kern_us,
-        "embbag": {"gb_s": round(emb_gbs, 1), "hbm_frac": round(emb_gbs / HBM_PEAK_GBS, 4)},
-        "din": {"tflops": round(din_tflops, 2), "mfma_frac": round(din_tflops / peak_mfma, 4),
-                "gb_s": round(din_bytes / din_t / 1e9, 1)},
+        "calls_us": call_us,
+        "warm": {"step_us": warm_step, **warm_rates},
+        "cold": {"step_us": cold_step, "kernels_us": cold_us, "calls_us": cold_calls, **cold_rates,
+                 "flush": "1 GiB read before each step (L2s and the 256 MB MALL evicted)"},
+        "algorithmic": {"gather_bytes": emb_bytes + plan_bytes, "embbag_bytes": emb_bytes,
+                        "plan_bytes": plan_bytes, "din_bytes": din_bytes, "din_flops": din_flops},
         "towers": towers,
         "hash_rebuild": rebuild,
         "adagrad": adagrad,
@@ -756,10 +886,19 @@ def main():
         "src_hash": shash,
     }
     if a.calibrate_copy:
+        # counter calibration: a streaming copy (CAL_BYTES read, CAL_BYTES
+        # written) and a gather of CAL_ROWS random 64-byte rows of a 192 MB
+        # table (CAL_ROWS * 64 bytes read, as many written)
         src = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             torch.mul(src, 1.0, out=dst)
+        g = torch.Generator(device="cpu").manual_seed(5)
+        table = torch.rand(CAL_TABLE_ROWS, 16, generator=g).to(dev)
+        idx = torch.randint(0, CAL_TABLE_ROWS, (CAL_ROWS,), generator=g).to(dev)
+        rows_out = torch.empty(CAL_ROWS, 16, dtype=torch.float32, device=dev)
+        for _ in range(3):
+            torch.index_select(table, 0, idx, out=rows_out)
         torch.cuda.synchronize()
     print(json.dumps(out), flush=True)
 

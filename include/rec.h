@@ -237,10 +237,10 @@ rec_status rec_embbag_fwd_kjt(const rec_table* tables, int32_t T, int64_t B,
 rec_status rec_hash_lookup(const rec_table* table, const int64_t* keys, int64_t n,
                            int64_t* slot_out, float* rows_out, void* stream);
 
-/* Bytes of workspace rec_hash_insert needs for n pairs (4 B per pair and a
- * winner table of 8 B per entry, at least 2n entries); 0 for n < 0 or
- * n > 2^30. */
-size_t rec_hash_insert_workspace_bytes(int64_t n);
+/* Bytes of workspace rec_hash_insert needs for n pairs into a table of
+ * `capacity` slots (4 B per pair and 4 B per slot); 0 for n < 0, n > 2^30 or
+ * a capacity outside [1, 2^31 - 1]. */
+size_t rec_hash_insert_workspace_bytes(int64_t n, int64_t capacity);
 
 /*
  * Insert-or-assign n (key, values) pairs into a hash table ("集成 DynamicEmb"
@@ -258,8 +258,8 @@ size_t rec_hash_insert_workspace_bytes(int64_t n);
  *              table had no empty slot on the key's probe sequence (the pair
  *              is not stored: no eviction, the NO_EVICTION behaviour), -2 for
  *              REC_EMPTY_KEY (never stored)
- *   workspace  >= rec_hash_insert_workspace_bytes(n) bytes of device memory,
- *              256-byte aligned, contents on entry ignored
+ *   workspace  >= rec_hash_insert_workspace_bytes(n, table->rows) bytes of
+ *              device memory, 256-byte aligned, contents on entry ignored
  * The result is that of inserting the pairs one after another in index
  * order: a key already stored keeps its slot and gets the new values and
  * score; a new key takes an empty slot of its probe sequence, so the table

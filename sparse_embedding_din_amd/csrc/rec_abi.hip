@@ -401,9 +401,9 @@ rec_status rec_hash_lookup(const rec_table* table, const int64_t* keys, int64_t 
     return hip_status(launch_hash_lookup(a, (hipStream_t)stream), "rec_hash_lookup");
 }
 
-size_t rec_hash_insert_workspace_bytes(int64_t n) {
-    if (n < 0 || n > ((int64_t)1 << 30)) return 0;
-    return align256(4 * (size_t)n) + 8 * (size_t)hash_insert_tag_entries(n);
+size_t rec_hash_insert_workspace_bytes(int64_t n, int64_t capacity) {
+    if (n < 0 || n > ((int64_t)1 << 30) || capacity < 1 || capacity > 2147483647LL) return 0;
+    return align256(4 * (size_t)n) + 4 * (size_t)capacity;
 }
 
 rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const float* values,
@@ -426,8 +426,8 @@ rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const fl
     rec_status s = prep_table(*table, "rec_hash_insert: table", &t.tab);
     if (s != REC_OK) return s;
     if (n == 0) return ok();
-    if (!workspace || workspace_bytes < rec_hash_insert_workspace_bytes(n))
-        return fail(REC_EWORKSPACE, "rec_hash_insert: workspace missing or smaller than rec_hash_insert_workspace_bytes(n)");
+    if (!workspace || workspace_bytes < rec_hash_insert_workspace_bytes(n, table->rows))
+        return fail(REC_EWORKSPACE, "rec_hash_insert: workspace missing or smaller than rec_hash_insert_workspace_bytes(n, capacity)");
     if ((uintptr_t)workspace & 255u) return fail(REC_EINVAL, "rec_hash_insert: workspace not 256-byte aligned");
     HashInsArgs a;
     a.keys = const_cast<int64_t*>(table->keys);
@@ -442,8 +442,7 @@ rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const fl
     a.step = step;
     a.slot_out = slot_out;
     a.pair_slot = (int32_t*)workspace;
-    a.tag = (uint64_t*)((char*)workspace + align256(4 * (size_t)n));
-    a.ntag = hash_insert_tag_entries(n);
+    a.winner = (int32_t*)((char*)workspace + align256(4 * (size_t)n));
     return hip_status(launch_hash_insert(a, (hipStream_t)stream), "rec_hash_insert");
 }
 

@@ -16,10 +16,10 @@
 //      digest; scores are updated (STEP: every lane writes the same step;
 //      LFU: one atomic add per pair).  With no empty slot on the whole
 //      sequence the pair is not stored (no eviction).  The same launch
-//      clears the workspace's winner table.
+//      clears the workspace's winner words (one per slot).
 //   2. winner: every pair that placed its key records its index in the
-//      winner table under its slot with a 64-bit atomic max of
-//      (slot + 1) << 32 | index, so each slot ends with its last pair.
+//      workspace's winner word of its slot with an atomic max, so each slot
+//      ends with its last pair.
 //   3. values: the pair whose index won copies its 16 values into the slot;
 //      so a key given several times gets the values of its last occurrence,
 //      as inserting the pairs one after another would leave them.
@@ -30,7 +30,7 @@ namespace {
 
 __global__ __launch_bounds__(256) void k_hash_insert(const HashInsArgs a) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < a.ntag) a.tag[i] = 0;
+    if (i < a.capacity) a.winner[i] = -1;
     if (i >= a.n) return;
     const int64_t key = a.in_keys[i];
     int64_t slot = -2;                        // the empty marker is never stored
@@ -70,45 +70,21 @@ __global__ __launch_bounds__(256) void k_hash_insert(const HashInsArgs a) {
     a.pair_slot[i] = (int32_t)slot;
 }
 
-// Entry of the winner table for slot s: linear probing from a mix of s over
-// ntag (a power of two, at least twice the pairs, so never full).
-__device__ inline uint64_t* winner_entry(const HashInsArgs& a, int64_t s, bool claim, uint64_t mine) {
-    const uint64_t want = (uint64_t)(s + 1) << 32;
-    uint64_t e = mix64((uint64_t)s) & (uint64_t)(a.ntag - 1);
-    for (;;) {
-        uint64_t cur = __hip_atomic_load(a.tag + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (cur == 0 && claim) {
-            uint64_t seen = 0;
-            if (__hip_atomic_compare_exchange_strong(a.tag + e, &seen, mine, __ATOMIC_RELAXED,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-                return a.tag + e;
-            cur = seen;
-        }
-        if ((cur & 0xffffffff00000000ull) == want) return a.tag + e;
-        e = (e + 1) & (uint64_t)(a.ntag - 1);
-    }
-}
-
 __global__ __launch_bounds__(256) void k_hash_insert_winner(const HashInsArgs a) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= a.n) return;
-    const int64_t s = a.pair_slot[i];
-    if (s < 0) return;
-    const uint64_t mine = ((uint64_t)(s + 1) << 32) | (uint64_t)i;
-    uint64_t* e = winner_entry(a, s, true, mine);
-    __hip_atomic_fetch_max(e, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int32_t s = a.pair_slot[i];
+    if (s >= 0) atomicMax(a.winner + s, (int32_t)i);
 }
 
 __global__ __launch_bounds__(256) void k_hash_insert_values(const HashInsArgs a) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= a.n) return;
-    const int64_t s = a.pair_slot[i];
+    const int32_t s = a.pair_slot[i];
     if (a.slot_out) a.slot_out[i] = s;
-    if (s < 0) return;
-    const uint64_t w = *winner_entry(a, s, false, 0);
-    if ((int64_t)(w & 0xffffffffull) != i) return;
+    if (s < 0 || a.winner[s] != (int32_t)i) return;
     const float4* src = (const float4*)(a.in_values + i * 16);
-    float4* dst = (float4*)(a.values + s * 16);
+    float4* dst = (float4*)(a.values + (int64_t)s * 16);
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[r] = src[r];
 }
@@ -124,15 +100,9 @@ __global__ __launch_bounds__(256) void k_hash_clear(int64_t* keys, uint8_t* dige
 
 }  // namespace
 
-int64_t hash_insert_tag_entries(int64_t n) {
-    int64_t t = 64;
-    while (t < 2 * n) t <<= 1;
-    return t;
-}
-
 hipError_t launch_hash_insert(const HashInsArgs& a, hipStream_t s) {
     const int64_t blocks = (a.n + 255) / 256;
-    const int64_t blocks0 = (max(a.n, a.ntag) + 255) / 256;
+    const int64_t blocks0 = (max(a.n, a.capacity) + 255) / 256;
     hipLaunchKernelGGL(k_hash_insert, dim3((unsigned)blocks0), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_hash_insert_winner, dim3((unsigned)blocks), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_hash_insert_values, dim3((unsigned)blocks), dim3(256), 0, s, a);

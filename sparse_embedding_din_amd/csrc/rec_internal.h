@@ -336,10 +336,8 @@ struct HashInsArgs {
     uint64_t step;
     int64_t* slot_out;
     int32_t* pair_slot;         // workspace: [n] slot of each pair (-1 not stored, -2 empty marker)
-    uint64_t* tag;              // workspace: [ntag] winner table, (slot + 1) << 32 | pair index
-    int64_t ntag;               // a power of two >= 2n
+    int32_t* winner;            // workspace: [capacity] last pair index stored in each slot
 };
-int64_t hash_insert_tag_entries(int64_t n);
 hipError_t launch_hash_insert(const HashInsArgs& a, hipStream_t s);
 
 // DLRM interaction: Z staged in LDS as 32 * ceil(F / 32) rows of dlrm_stride(d)

@@ -106,7 +106,7 @@ def lib():
         L.rec_embbag_fwd_kjt.argtypes = [C.POINTER(rec_table), i32, i64, vp, vp, vp, sz, vp, vp, vp,
                                          vp]
         L.rec_hash_lookup.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, vp]
-        L.rec_hash_insert_workspace_bytes.argtypes = [i64]
+        L.rec_hash_insert_workspace_bytes.argtypes = [i64, i64]
         L.rec_hash_insert_workspace_bytes.restype = sz
         L.rec_hash_insert.argtypes = [C.POINTER(rec_table), vp, vp, i64, i32, C.c_uint64, vp, vp,
                                       sz, vp]
@@ -265,8 +265,8 @@ def rec_hash_lookup(table_: rec_table, keys, n: int, slot_out=None, rows_out=Non
                                  _stream(stream)), "rec_hash_lookup")
 
 
-def rec_hash_insert_workspace_bytes(n: int) -> int:
-    return int(lib().rec_hash_insert_workspace_bytes(n))
+def rec_hash_insert_workspace_bytes(n: int, capacity: int) -> int:
+    return int(lib().rec_hash_insert_workspace_bytes(n, capacity))
 
 
 def rec_hash_insert(table_: rec_table, keys, values, n: int, score_mode: int = REC_SCORE_NONE,

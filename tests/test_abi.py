@@ -179,9 +179,10 @@ def test_hash_insert_errors(lib):
     assert _status(ins, C.byref(tab(rows=0)), FAKE, FAKE, 4, 0, 0, None, None, 0, None)[0] == R.REC_EINVAL
     assert _status(ins, C.byref(tab(dim=8)), FAKE, FAKE, 4, 0, 0, None, None, 0, None)[0] == R.REC_EINVAL
     assert _status(ins, C.byref(hs), None, None, 0, 2, 5, None, None, 0, None)[0] == R.REC_OK
-    need = R.rec_hash_insert_workspace_bytes(4)
-    assert need >= 4 * 4 + 8 * 8 and R.rec_hash_insert_workspace_bytes(-1) == 0
-    assert R.rec_hash_insert_workspace_bytes((1 << 30) + 1) == 0
+    need = R.rec_hash_insert_workspace_bytes(4, 100)
+    assert need >= 4 * 4 + 4 * 100 and R.rec_hash_insert_workspace_bytes(-1, 100) == 0
+    assert R.rec_hash_insert_workspace_bytes((1 << 30) + 1, 100) == 0
+    assert R.rec_hash_insert_workspace_bytes(4, 0) == 0
     s, msg = _status(ins, C.byref(h), FAKE, FAKE, 4, 0, 0, None, None, 0, None)
     assert s == R.REC_EWORKSPACE and "workspace" in msg
     assert _status(ins, C.byref(h), FAKE, FAKE, 4, 0, 0, None, FAKE, need - 1, None)[0] == R.REC_EWORKSPACE

@@ -41,7 +41,7 @@ def _insert(dt, keys, vals, mode=R.REC_SCORE_NONE, step=0):
     k = torch.from_numpy(np.ascontiguousarray(keys, np.int64)).to(DEV)
     v = torch.from_numpy(np.ascontiguousarray(vals, np.float32).reshape(-1, 16)).to(DEV)
     slot = torch.full((max(keys.size, 1),), -9, dtype=torch.int64, device=DEV)
-    wsb = R.rec_hash_insert_workspace_bytes(keys.size)
+    wsb = R.rec_hash_insert_workspace_bytes(keys.size, int(dt.desc[0].rows))
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=DEV)
     R.rec_hash_insert(dt.desc[0], k, v, keys.size, mode, step, slot, ws, wsb)
     torch.cuda.synchronize()
@@ -242,7 +242,7 @@ def test_clear_then_rebuild_gives_same_forward():
         occ = np.nonzero(t["keys"] != synth.EMPTY_KEY)[0]
         kk = torch.from_numpy(t["keys"][occ]).to(DEV)
         vv = torch.from_numpy(np.ascontiguousarray(t["values"][occ])).to(DEV)
-        wsb = R.rec_hash_insert_workspace_bytes(occ.size)
+        wsb = R.rec_hash_insert_workspace_bytes(occ.size, int(gpu_tabs.desc[k].rows))
         ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
         R.rec_hash_insert(gpu_tabs.desc[k], kk, vv, occ.size, R.REC_SCORE_STEP, 1, None, ws, wsb)
         torch.cuda.synchronize()
