@@ -88,6 +88,10 @@ class Oracle:
                                   C.c_int64, PD, PD, PD, PD, PD, PD, C.c_double, PD, PD, PD,
                                   PD, PD, PD, PD, PD, PD, PD, PD, PD]
         L.orc_din_bwd.restype = None
+        L.orc_dlrm_fwd.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32, PD, PD, PD, PD, PD,
+                                   P64, C.POINTER(PF), P32, P64, P32, P64, PD, PD, PD, PD, PD,
+                                   C.c_double, PD, PD, PD, PD, PD, PD]
+        L.orc_dlrm_fwd.restype = None
         self._keep = []
 
     # -- bookkeeping ---------------------------------------------------------
@@ -235,6 +239,46 @@ class Oracle:
         self.lib.orc_dlrm_interact(_ptr(z, PF), B, F, d, _ptr(out, PD),
                                    None if sc is None else _ptr(sc, PD))
         return (out, sc) if want_scale else out
+
+    # -- DLRM forward ------------------------------------------------------------
+    def dlrm_fwd(self, m, dense, values, lengths, offsets=None):
+        """The DLRM forward of a model m (attributes wb1, bb1, wb2, bb2, tables
+        (S arrays [rows][d] fp32), modes (S ints: 0 sum, 1 mean), wt1, bt1,
+        wt2, bt2, wt3, bt3; weights as the GPU receives them) on dense [B][nd]
+        and the key-major KJT (values, lengths [S*B], offsets [S*B] or None
+        for the exclusive scan of lengths).  Returns a dict of fp64 arrays:
+        z [B][S+1][d], inter [B][npairs], logit [B], prob [B], lscale [B]
+        (|bt3| + sum |wt3_i t2_i|) and iscale [B][npairs] (sum_k |z_ik z_jk|)."""
+        dense = np.ascontiguousarray(dense, np.float64)
+        B, nd = dense.shape
+        S = len(m.tables)
+        d = int(m.tables[0].shape[1])
+        F = S + 1
+        npairs = F * (F + 1) // 2
+        values = np.ascontiguousarray(values, np.int64)
+        lengths = np.ascontiguousarray(lengths, np.int32)
+        assert lengths.size == S * B
+        if offsets is None:
+            offsets = self.lengths_to_offsets(lengths)[:-1]
+        offsets = np.ascontiguousarray(offsets, np.int64)
+        tabs = [np.ascontiguousarray(t, np.float32) for t in m.tables]
+        assert all(t.ndim == 2 and t.shape[1] == d for t in tabs)
+        rows = np.array([t.shape[0] for t in tabs], np.int64)
+        ptrs = (PF * S)(*[_ptr(t, PF) for t in tabs])
+        modes = np.ascontiguousarray(m.modes, np.int32)
+        w = [np.ascontiguousarray(getattr(m, k), np.float64)
+             for k in ("wb1", "bb1", "wb2", "bb2", "wt1", "bt1", "wt2", "bt2", "wt3")]
+        assert w[0].shape == (128, nd) and w[2].shape == (d, 128)
+        assert w[4].shape == (128, npairs) and w[6].shape == (64, 128) and w[8].shape == (64,)
+        out = dict(z=np.empty((B, F, d)), inter=np.empty((B, npairs)), logit=np.empty(B),
+                   prob=np.empty(B), lscale=np.empty(B), iscale=np.empty((B, npairs)))
+        self.lib.orc_dlrm_fwd(B, nd, d, S, _ptr(dense, PD), *[_ptr(x, PD) for x in w[:4]],
+                              _ptr(rows, P64), ptrs, _ptr(modes, P32), _ptr(values, P64),
+                              _ptr(lengths, P32), _ptr(offsets, P64),
+                              *[_ptr(x, PD) for x in w[4:]], float(m.bt3),
+                              *[_ptr(out[k], PD) for k in ("z", "inter", "logit", "prob", "lscale",
+                                                           "iscale")])
+        return out
 
     # -- tables --------------------------------------------------------------
     def table(self, tab: dict) -> OrcTable:

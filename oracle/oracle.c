@@ -636,3 +636,88 @@ void orc_towers(int64_t ns, const double* pooled, int64_t ld, const double* att,
         if (prob) prob[s] = 1.0 / (1.0 + exp(-lg));
     }
 }
+
+/* ------------------------------------------------------------------------
+ * DLRM forward ([P3] §2.3: four layers with separate duties -- a bottom MLP
+ * maps the dense features to a vector of the embedding width, per-table
+ * EmbeddingBags pool the sparse ids, the interaction layer takes the dot
+ * product of every pair of those vectors (upper triangle only), a top MLP
+ * turns the dot products into the prediction; §3.2: a bag pools by sum or by
+ * mean; §3.3 and §4.2: with S sparse features and one dense vector the
+ * interaction has (S+1)(S+2)/2 outputs, the pairs (i, j) with j running from
+ * i, and the top MLP takes exactly those; §4.2's layer widths: bottom
+ * n_dense -> 128 -> d with ReLU after both layers, top -> 128 -> 64 -> 1 with
+ * ReLU, ReLU, sigmoid).
+ *   h   = relu(Wb2 relu(Wb1 x + bb1) + bb2)            x = dense row (n_dense)
+ *   e_t = sum (or mean) over bag (t, b) of table t's rows (d each); an
+ *         empty bag gives 0 in both modes
+ *   z   = [h, e_0, ..., e_{S-1}]                       (S+1 vectors of width d)
+ *   I   = <z_i, z_j> for i <= j, row order (0,0), (0,1), ..., (S,S)
+ *   t1  = relu(Wt1 I + bt1);  t2 = relu(Wt2 t1 + bt2)
+ *   logit = wt3 . t2 + bt3;   prob = 1 / (1 + exp(-logit))
+ * Readings: the tables are direct (row = floor_mod(id, rows)); the bags are
+ * the key-major KJT (bag t*B + b holds values[offsets[bag] .. + lengths[bag]));
+ * biases on every layer.  tables[t] points at table t's [rows[t]][d] fp32
+ * rows; modes[t] is 0 for sum, 1 for mean.  Outputs: z [B][S+1][d], inter
+ * [B][npairs], logit [B], prob [B]; lscale [B] (or NULL) receives |bt3| +
+ * sum_i |wt3_i t2_i|, the size of the logit's terms; iscale [B][npairs] (or
+ * NULL) receives sum_k |z_ik z_jk|.                                        */
+static void orc_dense(const double* W, const double* bias, const double* in, int nin, int nout,
+                      double* out) {
+    for (int o = 0; o < nout; ++o) {
+        double acc = bias[o];
+        for (int i = 0; i < nin; ++i) acc += W[(int64_t)o * nin + i] * in[i];
+        out[o] = acc > 0.0 ? acc : 0.0;
+    }
+}
+
+void orc_dlrm_fwd(int64_t B, int32_t nd, int32_t d, int32_t S, const double* dense,
+                  const double* wb1, const double* bb1, const double* wb2, const double* bb2,
+                  const int64_t* rows, const float* const* tables, const int32_t* modes,
+                  const int64_t* values, const int32_t* lengths, const int64_t* offsets,
+                  const double* wt1, const double* bt1, const double* wt2, const double* bt2,
+                  const double* wt3, double bt3, double* z, double* inter, double* logit,
+                  double* prob, double* lscale, double* iscale) {
+    const int32_t F = S + 1;
+    const int64_t npairs = (int64_t)F * (F + 1) / 2;
+    double h1[128], t1[128], t2[64];
+    for (int64_t b = 0; b < B; ++b) {
+        double* zb = z + b * F * d;
+        orc_dense(wb1, bb1, dense + b * nd, nd, 128, h1);
+        orc_dense(wb2, bb2, h1, 128, d, zb);
+        for (int32_t t = 0; t < S; ++t) {
+            double* e = zb + (int64_t)(1 + t) * d;
+            for (int32_t c = 0; c < d; ++c) e[c] = 0.0;
+            const int64_t bag = (int64_t)t * B + b;
+            for (int64_t i = 0; i < lengths[bag]; ++i) {
+                const int64_t r = orc_floor_mod(values[offsets[bag] + i], rows[t]);
+                for (int32_t c = 0; c < d; ++c) e[c] += (double)tables[t][r * d + c];
+            }
+            if (modes[t] == 1 && lengths[bag] > 0)
+                for (int32_t c = 0; c < d; ++c) e[c] /= (double)lengths[bag];
+        }
+        double* ib = inter + b * npairs;
+        int64_t o = 0;
+        for (int32_t i = 0; i < F; ++i)
+            for (int32_t j = i; j < F; ++j) {
+                double acc = 0.0, mag = 0.0;
+                for (int32_t k = 0; k < d; ++k) {
+                    acc += zb[(int64_t)i * d + k] * zb[(int64_t)j * d + k];
+                    mag += fabs(zb[(int64_t)i * d + k] * zb[(int64_t)j * d + k]);
+                }
+                ib[o] = acc;
+                if (iscale) iscale[b * npairs + o] = mag;
+                ++o;
+            }
+        orc_dense(wt1, bt1, ib, (int)npairs, 128, t1);
+        orc_dense(wt2, bt2, t1, 128, 64, t2);
+        double lg = bt3, mag = fabs(bt3);
+        for (int i = 0; i < 64; ++i) {
+            lg += wt3[i] * t2[i];
+            mag += fabs(wt3[i] * t2[i]);
+        }
+        logit[b] = lg;
+        prob[b] = 1.0 / (1.0 + exp(-lg));
+        if (lscale) lscale[b] = mag;
+    }
+}

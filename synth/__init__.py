@@ -412,3 +412,92 @@ def padded_seq_layout(batch: Batch, pad_to: int, rng_seed: int = 7):
         n = int(batch.seq_lengths[b])
         out[:, b * pad_to: b * pad_to + n] = batch.seq_values[:, starts[b]:starts[b] + n]
     return out, (np.arange(B, dtype=np.int64) * pad_to), B * pad_to
+
+
+# ----------------------------------------------------------------------------
+# DLRM workload (DLRM essay, wmrh.cn/news/12459): §4.2's minimal model -- 13
+# dense features (the Criteo layout it names), 8 sparse features with tables
+# of 100000, 50000, 20000, 10000, 5000, 2000, 1000 and 500 rows, embedding
+# width 96, bottom MLP 13 -> 128 -> 96, top MLP (S+1)(S+2)/2 -> 128 -> 64 -> 1;
+# §3.2: each bag pools several ids (e.g. the last five clicked items) by sum
+# or mean; §4.3: dense features are log-transformed and standardised (so
+# N(0, 1) here) and ids are remapped to 0 .. rows-1; §5.1: Xavier-uniform
+# weights, gain 1, for the tables too.
+DLRM_SIZES = (100000, 50000, 20000, 10000, 5000, 2000, 1000, 500)
+DLRM_DENSE = 13
+DLRM_DIM = 96
+
+
+@dataclasses.dataclass(frozen=True)
+class DlrmConfig:
+    index: int
+    name: str
+    B: int
+    sizes: tuple = DLRM_SIZES
+    n_dense: int = DLRM_DENSE
+    dim: int = DLRM_DIM
+    modes: tuple = (0,) * len(DLRM_SIZES)     # 0 sum, 1 mean, per table
+    bag_max: int = 5                           # bags hold 1 .. bag_max ids (uniform)
+
+
+DLRM_WORKLOADS: Dict[int, DlrmConfig] = {
+    1: DlrmConfig(101, "dlrm_sum_B8192", 8192),
+    2: DlrmConfig(102, "dlrm_mixed_B8192", 8192, modes=(0, 1, 0, 1, 0, 1, 0, 1)),
+}
+
+
+@dataclasses.dataclass
+class DlrmModel:
+    cfg: DlrmConfig
+    tables: List[np.ndarray]     # S arrays [rows][d] fp32
+    modes: tuple
+    wb1: np.ndarray
+    bb1: np.ndarray
+    wb2: np.ndarray
+    bb2: np.ndarray
+    wt1: np.ndarray
+    bt1: np.ndarray
+    wt2: np.ndarray
+    bt2: np.ndarray
+    wt3: np.ndarray
+    bt3: float
+
+
+@dataclasses.dataclass
+class DlrmBatch:
+    B: int
+    dense: np.ndarray            # fp32 [B][n_dense]
+    lengths: np.ndarray          # int32 [S*B], key-major
+    values: np.ndarray           # int64 [nnz], key-major, ids in [0, rows)
+
+
+def make_dlrm(cfg: DlrmConfig, *, bias: bool = False, emb_scale: float = 1.0) -> DlrmModel:
+    """Xavier-uniform tables and layers; bias=True draws U(-0.1, 0.1) biases
+    (parity tests), else zeros."""
+    rng = np.random.default_rng(np.random.SeedSequence([SEED_BASE, cfg.index]))
+    S = len(cfg.sizes)
+    npairs = (S + 1) * (S + 2) // 2
+    tables = [_xavier(rng, n, cfg.dim) * np.float32(emb_scale) for n in cfg.sizes]
+    wb1 = _xavier(rng, 128, cfg.n_dense)
+    wb2 = _xavier(rng, cfg.dim, 128)
+    wt1 = _xavier(rng, 128, npairs)
+    wt2 = _xavier(rng, 64, 128)
+    wt3 = _xavier(rng, 1, 64).reshape(64)
+
+    def b(n):
+        return (rng.uniform(-0.1, 0.1, n).astype(np.float32) if bias else np.zeros(n, np.float32))
+    bb1, bb2, bt1, bt2 = b(128), b(cfg.dim), b(128), b(64)
+    bt3 = float(np.float32(rng.uniform(-0.1, 0.1))) if bias else 0.0
+    return DlrmModel(cfg, tables, tuple(cfg.modes), wb1, bb1, wb2, bb2, wt1, bt1, wt2, bt2, wt3, bt3)
+
+
+def make_dlrm_batch(model: DlrmModel, batch_index: int = 0, B: Optional[int] = None) -> DlrmBatch:
+    cfg = model.cfg
+    B = cfg.B if B is None else B
+    rng = np.random.default_rng(np.random.SeedSequence([SEED_BASE, cfg.index, 1 + batch_index, B]))
+    S = len(cfg.sizes)
+    dense = rng.standard_normal((B, cfg.n_dense)).astype(np.float32)
+    lengths = rng.integers(1, cfg.bag_max + 1, size=(S, B)).astype(np.int32)
+    vals = [rng.integers(0, cfg.sizes[t], size=int(lengths[t].sum()), dtype=np.int64)
+            for t in range(S)]
+    return DlrmBatch(B, dense, lengths.reshape(-1).copy(), np.concatenate(vals))

@@ -796,7 +796,95 @@ def pin_din_bwd(orc):
         assert not got[k].any(), k
 
 
+def _torch_dlrm(m, dense, values, lengths):
+    """The DLRM essay's forward (§2.3, §4.2) written with torch library
+    routines in fp64: F.embedding_bag per table (mode 'sum' or 'mean', offsets
+    from a cumulative sum of the lengths), F.linear + relu for the bottom and
+    top MLPs, bmm with triu_indices for the interaction, sigmoid."""
+    import torch.nn.functional as Fn
+    S = len(m.tables)
+    B = dense.shape[0]
+    D = lambda a: torch.from_numpy(np.asarray(a, np.float64))  # noqa: E731
+    x = D(dense)
+    h = torch.relu(Fn.linear(torch.relu(Fn.linear(x, D(m.wb1), D(m.bb1))), D(m.wb2), D(m.bb2)))
+    L = np.asarray(lengths, np.int64).reshape(S, B)
+    starts = np.concatenate([[0], np.cumsum(L.reshape(-1))])
+    vecs = [h]
+    for t in range(S):
+        ids = torch.from_numpy(np.asarray(values[starts[t * B]: starts[(t + 1) * B]], np.int64))
+        off = torch.from_numpy(starts[t * B: (t + 1) * B] - starts[t * B])
+        mode = "mean" if m.modes[t] == 1 else "sum"
+        vecs.append(Fn.embedding_bag(ids, D(m.tables[t]), off, mode=mode))
+    z = torch.stack(vecs, dim=1)                                   # [B][S+1][d]
+    gram = torch.bmm(z, z.transpose(1, 2).contiguous())
+    iu = torch.triu_indices(S + 1, S + 1)
+    inter = gram[:, iu[0], iu[1]]
+    t2 = torch.relu(Fn.linear(torch.relu(Fn.linear(inter, D(m.wt1), D(m.bt1))), D(m.wt2), D(m.bt2)))
+    logit = t2 @ D(m.wt3) + m.bt3
+    return z.numpy(), inter.numpy(), logit.numpy(), torch.sigmoid(logit).numpy()
+
+
+def pin_dlrm_fwd(orc):
+    """The DLRM forward (DLRM essay §2.3 four layers, §3.2 sum / mean bags,
+    §4.2 widths) against torch fp64 library routines (F.embedding_bag in sum
+    and mean mode, F.linear, bmm + triu_indices, sigmoid), on a small model
+    with mixed modes and empty bags; and closed forms: a one-id bag equals its
+    row in both modes, a bag of one id repeated k times equals the row in mean
+    mode and k times it in sum mode, an empty bag is 0 in both modes, zero
+    top weights give logit = bt3, and a zero bottom MLP zeroes every pair with
+    the dense vector."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.DLRM_WORKLOADS[2], sizes=(50, 40, 30, 20, 9), n_dense=5,
+                              dim=32, modes=(0, 1, 1, 0, 1), bag_max=4)
+    m = synth.make_dlrm(cfg, bias=True, emb_scale=4.0)
+    b = synth.make_dlrm_batch(m, B=24)
+    L = b.lengths.reshape(5, 24).copy()
+    L[1, 3] = 0
+    L[0, 7] = 0
+    vals = []
+    starts = np.concatenate([[0], np.cumsum(b.lengths)])
+    rng = np.random.default_rng(5)
+    for t in range(5):
+        for bb in range(24):
+            vals.append(rng.integers(0, cfg.sizes[t], size=int(L[t, bb])))
+    values = np.concatenate(vals).astype(np.int64)
+    got = orc.dlrm_fwd(m, b.dense, values, L.reshape(-1))
+    z, inter, logit, prob = _torch_dlrm(m, b.dense, values, L.reshape(-1))
+    assert _rel(got["z"], z) < 1e-13
+    assert np.max(np.abs(got["inter"] - inter) / np.maximum(got["iscale"], 1e-300)) < 1e-13
+    assert np.max(np.abs(got["logit"] - logit) / np.maximum(got["lscale"], 1e-300)) < 1e-13
+    assert np.max(np.abs(got["prob"] - prob)) < 1e-13
+    assert not got["z"][3, 2].any() and not got["z"][7, 1].any()        # empty bags
+    # closed forms on hand-made bags: table t, sample 0
+    B = 4
+    dense = np.zeros((B, 5), np.float32)
+    Lc = np.ones((5, B), np.int32)
+    row = 7
+    Lc[1, 0], Lc[0, 0], Lc[3, 1] = 3, 3, 0
+    vals = []
+    for t in range(5):
+        for bb in range(B):
+            vals.append(np.full(int(Lc[t, bb]), row + 0 * bb, np.int64))
+    values = np.concatenate(vals)
+    mz = dataclasses.replace(m, bb1=np.zeros_like(m.bb1), bb2=np.zeros_like(m.bb2))
+    g = orc.dlrm_fwd(mz, dense, values, Lc.reshape(-1))
+    for t in range(5):
+        r = m.tables[t][row].astype(np.float64)
+        k = int(Lc[t, 0])
+        want = r if (m.modes[t] == 1 or k == 1) else k * r
+        assert np.array_equal(g["z"][0, 1 + t], want), t
+    assert not g["z"][1, 4].any()                                   # empty bag, table 3
+    assert not g["z"][:, 0].any()                                   # zero dense, zero biases
+    F = 6
+    iu = np.triu_indices(F)
+    assert not g["inter"][:, iu[0] == 0].any()                      # pairs with the dense vector
+    m0 = dataclasses.replace(m, wt3=np.zeros_like(m.wt3))
+    g0 = orc.dlrm_fwd(m0, b.dense, b.values, b.lengths)
+    assert np.all(g0["logit"] == m.bt3) and np.allclose(g0["prob"], 1 / (1 + np.exp(-m.bt3)),
+                                                        rtol=1e-15, atol=0)
+
+
 ALL_PINS = [pin_offsets, pin_floor_mod, pin_hash, pin_embbag_direct, pin_embbag_hash,
             pin_din_vs_padded, pin_din_closed_forms, pin_din_hash, pin_towers_closed_forms,
             pin_towers_library, pin_hash_insert, pin_dlrm_interact, pin_embbag_adagrad,
-            pin_din_bwd]
+            pin_din_bwd, pin_dlrm_fwd]

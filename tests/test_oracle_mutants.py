@@ -121,6 +121,21 @@ MUTANTS = [
     ("backward drops the last id of a bag",
      "for (int64_t i = 0; i < lengths[bag]; ++i) {\n                const int64_t rt = orc_resolve(",
      "for (int64_t i = 0; i + 1 < lengths[bag]; ++i) {\n                const int64_t rt = orc_resolve("),
+    ("DLRM mean divides by the length + 1", "e[c] /= (double)lengths[bag];",
+     "e[c] /= (double)(lengths[bag] + 1);"),
+    ("DLRM mean bags summed", "if (modes[t] == 1 && lengths[bag] > 0)", "if (0)"),
+    ("DLRM bag drops the last id", "for (int64_t i = 0; i < lengths[bag]; ++i) {\n                const int64_t r = orc_floor_mod(",
+     "for (int64_t i = 0; i + 1 < lengths[bag]; ++i) {\n                const int64_t r = orc_floor_mod("),
+    ("DLRM bottom reads the first dense row", "orc_dense(wb1, bb1, dense + b * nd, nd, 128, h1);",
+     "orc_dense(wb1, bb1, dense, nd, 128, h1);"),
+    ("DLRM bottom skips its second layer", "orc_dense(wb2, bb2, h1, 128, d, zb);",
+     "for (int32_t c = 0; c < d; ++c) zb[c] = h1[c];"),
+    ("DLRM top skips its second layer", "orc_dense(wt2, bt2, t1, 128, 64, t2);",
+     "for (int i = 0; i < 64; ++i) t2[i] = t1[i];"),
+    ("DLRM logit bias dropped", "double lg = bt3, mag = fabs(bt3);", "double lg = 0.0, mag = fabs(bt3);"),
+    ("DLRM sigmoid sign flipped", "prob[b] = 1.0 / (1.0 + exp(-lg));", "prob[b] = 1.0 / (1.0 + exp(lg));"),
+    ("DLRM interaction squares the row", "acc += zb[(int64_t)i * d + k] * zb[(int64_t)j * d + k];",
+     "acc += zb[(int64_t)i * d + k] * zb[(int64_t)i * d + k];"),
 ]
 
 
