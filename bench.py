@@ -79,6 +79,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-hash-rebuild", action="store_true",
                    help="skip timing the rebuild of the hash workload's tables (clear + insert)")
+    p.add_argument("--no-dlrm", action="store_true",
+                   help="skip the DLRM forward leg (the essay's example model, B=8192)")
     p.add_argument("--no-interaction", action="store_true",
                    help="skip the DLRM interaction leg (217 vectors of width 96 per sample)")
     p.add_argument("--no-two-streams", action="store_true",
@@ -129,7 +131,8 @@ KERNEL_SOURCES = {"k_din_attn": _FWD, "k_embbag_fwd": _FWD, "k_fwd_gather": _FWD
                   "k_hash_insert": ["rec_hash.hip"] + _COMMON,
                   "k_bwd_keys": _BWD, "k_sort_hist": _BWD, "k_sort_scan": _BWD, "k_sort_scatter": _BWD,
                   "k_bwd_chunks": _BWD, "k_bwd_cross": _BWD,
-                  "k_dlrm_interact": ["rec_dlrm.hip", "rec_mfma.h"] + _COMMON}
+                  "k_dlrm_interact": ["rec_dlrm.hip", "rec_mfma.h"] + _COMMON,
+                  "k_dlrm_embed": ["rec_dlrm_fwd.hip"] + _COMMON, "k_dlrm_top": ["rec_dlrm_fwd.hip"] + _COMMON}
 for _k in ("k_dinb_prep", "k_dinb_map", "k_dinb_fwd", "k_dinb_soft", "k_dinb_bwdt",
            "k_dinb_gq", "k_dinb_wgrad", "k_dinb_reduce"):
     KERNEL_SOURCES[_k] = ["rec_din_bwd.hip"] + _COMMON
@@ -147,11 +150,13 @@ KERNELS = {"k_din_attn": "k_din_attn",
            "k_dinb_prep": "k_dinb_prep",
            "k_dinb_map": "k_dinb_map", "k_dinb_fwd": "k_dinb_fwd", "k_dinb_soft": "k_dinb_soft",
            "k_dinb_bwdt": "k_dinb_bwdt", "k_dinb_gq": "k_dinb_gq", "k_dinb_wgrad": "k_dinb_wgrad",
-           "k_dinb_reduce": "k_dinb_reduce", "copy": "MulFunctor", "gather_cal": "ndexSelect"}
+           "k_dinb_reduce": "k_dinb_reduce", "copy": "MulFunctor", "gather_cal": "ndexSelect",
+           "k_dlrm_embed": "k_dlrm_embed", "k_dlrm_top": "k_dlrm_top"}
 # kernels whose reads are mostly random 64-byte rows: their FETCH_SIZE is scaled
 # by the calibration gather's reading (random 64-byte rows), the others' by
 # the calibration copy's (streaming)
-RANDOM_ROW_KERNELS = {"k_din_attn", "k_embbag_fwd", "k_fwd_gather", "k_bwd_chunks", "k_bwd_cross"}
+RANDOM_ROW_KERNELS = {"k_din_attn", "k_embbag_fwd", "k_fwd_gather", "k_bwd_chunks", "k_bwd_cross",
+                      "k_dlrm_embed"}
 
 
 def load_traffic(kernels, shash: str, config: str):
@@ -837,6 +842,55 @@ def main():
               file=sys.stderr, flush=True)
         del zi, oi
 
+    dlrm = None
+    if not a.no_dlrm:
+        # The DLRM essay's example model (§4.2: 13 dense features, 8 tables of
+        # 100000 .. 500 rows, width 96, bottom 13-128-96, top 45-128-64-1) over
+        # B = 8192 samples with bags of 1-5 ids, by rec_dlrm_fwd.
+        dcfg = synth.DLRM_WORKLOADS[1]
+        dm = synth.make_dlrm(dcfg)
+        dbt = synth.make_dlrm_batch(dm)
+        to = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
+        keep = [to(t) for t in dm.tables] + [to(getattr(dm, k)) for k in
+                                            ("wb1", "bb1", "wb2", "bb2", "wt1", "bt1", "wt2", "bt2", "wt3")]
+        S_, d_ = len(dm.tables), dcfg.dim
+        dmlp = R.dlrm_mlp(dcfg.n_dense, d_, S_, *keep[S_:], dm.bt3)
+        dtabs = [R.table(R.REC_DIRECT, t.shape[0], keep[i], dim=d_) for i, t in enumerate(dm.tables)]
+        Bd = dbt.B
+        doff = to(np.concatenate([[0], np.cumsum(dbt.lengths.astype(np.int64))[:-1]]))
+        dd, dv, dl = to(dbt.dense), to(dbt.values), to(dbt.lengths)
+        zbuf = torch.empty(Bd, S_ + 1, d_, dtype=torch.float32, device=dev)
+        lg, pr = torch.empty(Bd, dtype=torch.float32, device=dev), torch.empty(Bd, dtype=torch.float32, device=dev)
+
+        def dlrm_call(r=0):
+            R.rec_dlrm_fwd(dmlp, dtabs, list(dm.modes), Bd, dd, dv, dl, doff, zbuf, None, lg, pr,
+                           stream=stream)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                dlrm_call()
+            torch.cuda.synchronize()
+        dk, dcall = timed(dlrm_call, {"embed": R.REC_TIME_DLRM_EMBED, "top": R.REC_TIME_DLRM_TOP}, 40)
+        nnz_d = float(dbt.values.size)
+        F_ = S_ + 1
+        embed_bytes = (nnz_d * (8 + 4 * d_) + S_ * Bd * (4 + 8) + Bd * dcfg.n_dense * 4
+                       + Bd * F_ * d_ * 4)
+        top_bytes = Bd * F_ * d_ * 4 + Bd * 8
+        np_ = F_ * (F_ + 1) // 2
+        top_flops = Bd * 2.0 * (np_ * d_ + np_ * 128 + 128 * 64 + 64)
+        dlrm = {"entry": "rec_dlrm_fwd (bags of width 96 + bottom MLP; interaction + top MLP)",
+                "workload": f"{dcfg.name}: B={Bd}, 13 dense, tables {list(dcfg.sizes)} of width {d_}, "
+                            f"bags 1-{dcfg.bag_max} ids, sum pooling",
+                "call_us": dcall, "kernels_us": dk,
+                "samples_s": round(Bd / (dcall["mean"] * 1e-6), 1),
+                "embed_algorithmic_bytes": embed_bytes,
+                "embed_gb_s": round(embed_bytes / (dk["embed"]["mean"] * 1e-6) / 1e9, 1),
+                "embed_hbm_frac": round(embed_bytes / (dk["embed"]["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "top_bytes": top_bytes, "top_flops": top_flops,
+                "top_tflops": round(top_flops / (dk["top"]["mean"] * 1e-6) / 1e12, 2)}
+        print(f"[bench] DLRM forward: {dcall['mean']:.1f} us per call (embed {dk['embed']['mean']:.1f}, "
+              f"top {dk['top']['mean']:.1f})", file=sys.stderr, flush=True)
+        del keep, zbuf
+
     # `value` is whole-job throughput: with two batches in flight when that is
     # faster (every step is still one whole pass over one resident batch).
     single = {"ms_per_step": round(ms_per_step, 5), "gpu_ms_per_step": round(gpu_ms, 5),
@@ -883,6 +937,7 @@ def main():
         "adagrad": adagrad,
         "din_bwd": din_bwd,
         "dlrm_interaction": interaction,
+        "dlrm_forward": dlrm,
         "src_hash": shash,
     }
     if a.calibrate_copy:

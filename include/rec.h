@@ -67,7 +67,9 @@ enum { REC_DIRECT = 0, REC_HASH = 1 };   /* rec_table.kind */
 enum { REC_F32 = 0, REC_BF16 = 1, REC_BF16_PACKED = 2 };   /* rec_din_mlp.dtype */
 enum { REC_SCORE_NONE = 0, REC_SCORE_STEP = 1, REC_SCORE_LFU = 2 };   /* rec_hash_insert */
 enum { REC_TIME_DIN_ATTN = 0, REC_TIME_GATHER = 1, REC_TIME_SUMS = 2, REC_TIME_TOWERS = 3,
-       REC_TIME_DLRM_INTERACT = 4, REC_TIME_KINDS = 5 };           /* rec_time_next_launch */
+       REC_TIME_DLRM_INTERACT = 4, REC_TIME_DLRM_EMBED = 5, REC_TIME_DLRM_TOP = 6,
+       REC_TIME_KINDS = 7 };                                        /* rec_time_next_launch */
+enum { REC_POOL_SUM = 0, REC_POOL_MEAN = 1 };                    /* rec_dlrm_fwd bag modes */
 
 #define REC_DIM 16                        /* embedding width of every table */
 #define REC_EMPTY_KEY ((int64_t)-1)       /* empty hash slot; never a valid key */
@@ -294,6 +296,63 @@ rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const fl
  * Errors: REC_EINVAL, REC_EUNSUPPORTED (shape beyond the limits).
  */
 rec_status rec_dlrm_interact(const float* z, int64_t B, int32_t F, int32_t d, float* out, void* stream);
+
+/*
+ * The DLRM forward around the interaction (DLRM essay, wmrh.cn/news/12459:
+ * §2.3 four layers -- a bottom MLP brings the dense features to the
+ * embedding width, per-feature EmbeddingBags pool the sparse ids, the
+ * interaction layer takes the dot product of every pair (one triangle only),
+ * a top MLP turns the dot products into the prediction; §3.2 a bag pools by
+ * sum or by mean; §3.3, §4.2 the widths and the pair order, j running from i).
+ * For sample b:
+ *   h     = relu(wb2 relu(wb1 dense[b] + bb1) + bb2)        (d)
+ *   e_t   = sum over bag (t, b) of table t's rows (REC_POOL_SUM), or that sum
+ *           divided by the bag's length (REC_POOL_MEAN); an empty bag gives 0
+ *   z[b]  = [h, e_0, ..., e_{S-1}]                         ([S+1][d])
+ *   I     = <z_i, z_j> for i <= j in row order (0,0), (0,1), ..., (S,S)
+ *   logit = wt3 . relu(wt2 relu(wt1 I + bt1) + bt2) + bt3;  prob = sigmoid
+ * All fp32; each dot product and layer sums in a fixed order (results are
+ * bit-identical run to run).
+ */
+typedef struct {
+    int32_t n_dense;              /* dense features, 1..128 */
+    int32_t dim;                  /* d: table width = bottom output, 32..256, multiple of 32 */
+    int32_t S;                    /* sparse features (tables), 1..31; (S+1)*dim <= 1024 */
+    int32_t reserved;
+    const float* wb1;             /* [128][n_dense] (torch.nn.Linear.weight layout) */
+    const float* bb1;             /* [128] */
+    const float* wb2;             /* [dim][128] */
+    const float* bb2;             /* [dim] */
+    const float* wt1;             /* [128][(S+1)(S+2)/2] */
+    const float* bt1;             /* [128] */
+    const float* wt2;             /* [64][128] */
+    const float* bt2;             /* [64] */
+    const float* wt3;             /* [64] */
+    float bt3;
+} rec_dlrm_mlp;
+
+/*
+ *   mlp      host struct; every array 16-byte aligned device memory
+ *   tables   host array of S descriptors, kind REC_DIRECT, dim == mlp->dim
+ *            (values [rows][dim] fp32, 16-byte aligned); row = floor_mod(id, rows)
+ *   modes    host int32[S]: REC_POOL_SUM or REC_POOL_MEAN per table
+ *   dense    fp32 [B][n_dense]
+ *   values   int64[nnz] ids;  lengths int32[S*B];  offsets int64[S*B]: the
+ *            key-major KJT (bag t*B + b holds values[offsets[t*B+b] .. +
+ *            lengths[t*B+b])), e.g. from rec_lengths_to_offsets
+ *   z        fp32 [B][S+1][dim], 16-byte aligned: written (the interaction
+ *            input: bottom output first, then the bags in table order)
+ *   inter    fp32 [B][(S+1)(S+2)/2] or NULL: the interaction output
+ *   logit    fp32 [B];  prob fp32 [B] or NULL
+ * Two launches (bags and bottom MLP; interaction and top MLP).
+ * Errors: REC_EINVAL (null required pointers, misalignment, B < 0, a table
+ * that is not direct or whose dim differs, unknown mode, sizes outside the
+ * limits above).  B == 0 is a no-op.
+ */
+rec_status rec_dlrm_fwd(const rec_dlrm_mlp* mlp, const rec_table* tables, const int32_t* modes,
+                        int64_t B, const float* dense, const int64_t* values,
+                        const int32_t* lengths, const int64_t* offsets, float* z, float* inter,
+                        float* logit, float* prob, void* stream);
 
 /*
  * Empties a hash table: every key becomes REC_EMPTY_KEY, every digest 0 and
@@ -698,6 +757,8 @@ rec_status rec_din_attn_bwd(const rec_table* seq_tables, const int64_t* seq_valu
  *                           rec_sparse_din_fwd)
  *   REC_TIME_TOWERS         the bf16 towers (rec_towers_fwd)
  *   REC_TIME_DLRM_INTERACT  the interaction (rec_dlrm_interact)
+ *   REC_TIME_DLRM_EMBED     rec_dlrm_fwd's bags and bottom MLP
+ *   REC_TIME_DLRM_TOP       rec_dlrm_fwd's interaction and top MLP
  * The events (created by the caller with timing enabled, on the device of
  * the launch) are used by one launch and then forgotten; start == stop ==
  * NULL forgets them without a launch.  The setting is thread-local state of

@@ -461,6 +461,68 @@ rec_status rec_dlrm_interact(const float* z, int64_t B, int32_t F, int32_t d, fl
     return hip_status(launch_dlrm_interact(z, B, F, d, out, cus, (hipStream_t)stream), "rec_dlrm_interact");
 }
 
+rec_status rec_dlrm_fwd(const rec_dlrm_mlp* mlp, const rec_table* tables, const int32_t* modes,
+                        int64_t B, const float* dense, const int64_t* values,
+                        const int32_t* lengths, const int64_t* offsets, float* z, float* inter,
+                        float* logit, float* prob, void* stream) {
+    const std::string f("rec_dlrm_fwd");
+    if (!mlp || !tables || !modes) return fail(REC_EINVAL, f + ": mlp, tables and modes are required");
+    if (B < 0) return fail(REC_EINVAL, f + ": B < 0");
+    const int32_t S = mlp->S, d = mlp->dim, nd = mlp->n_dense;
+    if (S < 1 || S > 31) return fail(REC_EINVAL, f + ": S outside [1, 31]");
+    if (d < 32 || d > 256 || d % 32) return fail(REC_EINVAL, f + ": dim must be a multiple of 32 in [32, 256]");
+    if (nd < 1 || nd > kDlrmMaxDense) return fail(REC_EINVAL, f + ": n_dense outside [1, 128]");
+    if ((S + 1) * d > kDlrmMaxZ) return fail(REC_EINVAL, f + ": (S + 1) * dim above 1024");
+    const void* arrays[] = {mlp->wb1, mlp->bb1, mlp->wb2, mlp->bb2, mlp->wt1, mlp->bt1, mlp->wt2,
+                            mlp->bt2, mlp->wt3};
+    for (const void* p : arrays) {
+        if (!p) return fail(REC_EINVAL, f + ": mlp weights and biases are required");
+        if (!aligned16(p)) return fail(REC_EINVAL, f + ": mlp arrays must be 16-byte aligned");
+    }
+    DlrmArgs a;
+    memset(&a, 0, sizeof(a));
+    for (int t = 0; t < S; ++t) {
+        const rec_table& tb = tables[t];
+        if (tb.kind != REC_DIRECT) return fail(REC_EINVAL, f + ": tables must be REC_DIRECT");
+        if (tb.dim != d) return fail(REC_EINVAL, f + ": a table's dim differs from mlp->dim");
+        if (tb.rows < 1) return fail(REC_EINVAL, f + ": rows must be >= 1");
+        if (!tb.values || !aligned16(tb.values)) return fail(REC_EINVAL, f + ": table values NULL or misaligned");
+        if (modes[t] != REC_POOL_SUM && modes[t] != REC_POOL_MEAN) return fail(REC_EINVAL, f + ": unknown mode");
+        a.tab[t].values = tb.values;
+        a.tab[t].rows = tb.rows;
+        a.tab[t].kind = REC_DIRECT;
+        floor_mod_prepare(tb.rows, &a.tab[t].magic, &a.tab[t].shift);
+        a.mode[t] = modes[t];
+    }
+    if (B == 0) return ok();
+    if (!dense || !values || !lengths || !offsets || !z || !logit)
+        return fail(REC_EINVAL, f + ": dense, values, lengths, offsets, z and logit are required");
+    if (!aligned16(z)) return fail(REC_EINVAL, f + ": z not 16-byte aligned");
+    a.B = B;
+    a.S = S;
+    a.dim = d;
+    a.n_dense = nd;
+    a.dense = dense;
+    a.values = values;
+    a.lengths = lengths;
+    a.offsets = offsets;
+    a.wb1 = mlp->wb1;
+    a.bb1 = mlp->bb1;
+    a.wb2 = mlp->wb2;
+    a.bb2 = mlp->bb2;
+    a.wt1 = mlp->wt1;
+    a.bt1 = mlp->bt1;
+    a.wt2 = mlp->wt2;
+    a.bt2 = mlp->bt2;
+    a.wt3 = mlp->wt3;
+    a.bt3 = mlp->bt3;
+    a.z = z;
+    a.inter = inter;
+    a.logit = logit;
+    a.prob = prob;
+    return hip_status(launch_dlrm_fwd(a, (hipStream_t)stream), "rec_dlrm_fwd");
+}
+
 rec_status rec_hash_clear(const rec_table* table, void* stream) {
     if (!table) return fail(REC_EINVAL, "rec_hash_clear: table is NULL");
     if (table->kind != REC_HASH) return fail(REC_EINVAL, "rec_hash_clear: table kind is not REC_HASH");

@@ -346,6 +346,27 @@ constexpr int kDlrmMaxLdsFloats = 36864;
 int dlrm_stride(int d);
 hipError_t launch_dlrm_interact(const float* z, int64_t B, int F, int d, float* out, int num_cus,
                                 hipStream_t s);
+// The DLRM forward around the interaction (rec_dlrm_fwd.hip).
+constexpr int kDlrmMaxDense = 128;           // dense features
+constexpr int kDlrmMaxZ = 1024;              // (S + 1) * d floats per sample
+constexpr int kDlrmMaxPairs = 528;           // (S + 1)(S + 2) / 2 at S = 31
+struct DlrmArgs {
+    TabDev tab[32];
+    int32_t mode[32];
+    int64_t B;
+    int32_t S, dim, n_dense;
+    const float* dense;
+    const int64_t* values;
+    const int32_t* lengths;
+    const int64_t* offsets;
+    const float *wb1, *bb1, *wb2, *bb2, *wt1, *bt1, *wt2, *bt2, *wt3;
+    float bt3;
+    float* z;
+    float* inter;
+    float* logit;
+    float* prob;
+};
+hipError_t launch_dlrm_fwd(const DlrmArgs& a, hipStream_t s);
 // Sparse backward + AdaGrad (rec_bwd.hip).  One table: its lookup
 // descriptor (direct floor-mod constants or hash keys/digests), the arrays
 // the step writes, and its first row in the flat row space of all tables.

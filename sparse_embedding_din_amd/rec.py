@@ -20,7 +20,8 @@ REC_DIRECT, REC_HASH = 0, 1
 REC_F32, REC_BF16, REC_BF16_PACKED = 0, 1, 2
 REC_SCORE_NONE, REC_SCORE_STEP, REC_SCORE_LFU = 0, 1, 2
 (REC_TIME_DIN_ATTN, REC_TIME_GATHER, REC_TIME_SUMS, REC_TIME_TOWERS,
- REC_TIME_DLRM_INTERACT, REC_TIME_KINDS) = 0, 1, 2, 3, 4, 5
+ REC_TIME_DLRM_INTERACT, REC_TIME_DLRM_EMBED, REC_TIME_DLRM_TOP, REC_TIME_KINDS) = range(8)
+REC_POOL_SUM, REC_POOL_MEAN = 0, 1
 REC_DIN_PACKED_BYTES = 131072
 REC_TOWER_PACKED_BYTES = 614400
 REC_NOALLOC_SCRATCH_BYTES = 33554432
@@ -33,7 +34,7 @@ REC_MAX_B = 16777215
 EXPORTS = ["rec_din_pack_mlp", "rec_lengths_to_offsets", "rec_embbag_fwd",
            "rec_kjt_sums_bytes", "rec_kjt_sums", "rec_embbag_fwd_kjt", "rec_hash_lookup",
            "rec_hash_insert_workspace_bytes", "rec_hash_insert", "rec_hash_clear",
-           "rec_dlrm_interact",
+           "rec_dlrm_interact", "rec_dlrm_fwd",
            "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_workspace_bytes", "rec_din_attn_fwd",
            "rec_din_attn_fwd_plan",
            "rec_sparse_din_fwd_workspace_bytes", "rec_sparse_din_fwd", "rec_sparse_din_fwd_noalloc",
@@ -67,6 +68,13 @@ class rec_tower_mlp(C.Structure):
                 ("wd1", C.c_void_p), ("bd1", C.c_void_p), ("wd2", C.c_void_p), ("bd2", C.c_void_p),
                 ("wd3", C.c_void_p), ("bd3", C.c_void_p), ("wf", C.c_void_p), ("bf", C.c_void_p),
                 ("wo", C.c_void_p), ("bo", C.c_float)]
+
+
+class rec_dlrm_mlp(C.Structure):
+    _fields_ = [("n_dense", C.c_int32), ("dim", C.c_int32), ("S", C.c_int32), ("reserved", C.c_int32),
+                ("wb1", C.c_void_p), ("bb1", C.c_void_p), ("wb2", C.c_void_p), ("bb2", C.c_void_p),
+                ("wt1", C.c_void_p), ("bt1", C.c_void_p), ("wt2", C.c_void_p), ("bt2", C.c_void_p),
+                ("wt3", C.c_void_p), ("bt3", C.c_float)]
 
 
 class rec_adagrad_table(C.Structure):
@@ -112,6 +120,8 @@ def lib():
                                       sz, vp]
         L.rec_hash_clear.argtypes = [C.POINTER(rec_table), vp]
         L.rec_dlrm_interact.argtypes = [vp, i64, i32, i32, vp, vp]
+        L.rec_dlrm_fwd.argtypes = [C.POINTER(rec_dlrm_mlp), C.POINTER(rec_table),
+                                   C.POINTER(C.c_int32), i64, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.rec_din_plan_bytes.argtypes = [i64, i32]
         L.rec_din_plan_bytes.restype = sz
         L.rec_din_plan.argtypes = [C.POINTER(rec_table), vp, i64, vp, vp, i64, i32, i32, vp, vp,
@@ -143,6 +153,7 @@ def lib():
                                          C.c_float, vp, sz, vp]
         for f in ("rec_lengths_to_offsets", "rec_embbag_fwd", "rec_kjt_sums", "rec_embbag_fwd_kjt",
                   "rec_hash_lookup", "rec_hash_insert", "rec_hash_clear", "rec_dlrm_interact",
+                  "rec_dlrm_fwd",
                   "rec_din_plan",
                   "rec_din_attn_fwd", "rec_din_attn_fwd_plan", "rec_din_pack_mlp", "rec_sparse_din_fwd",
                   "rec_sparse_din_fwd_noalloc", "rec_towers_fwd",
@@ -280,6 +291,22 @@ def rec_hash_insert(table_: rec_table, keys, values, n: int, score_mode: int = R
 
 def rec_dlrm_interact(z, B: int, F: int, d: int, out, stream=None):
     _check(lib().rec_dlrm_interact(_p(z), B, F, d, _p(out), _stream(stream)), "rec_dlrm_interact")
+
+
+def dlrm_mlp(n_dense: int, dim: int, S: int, wb1, bb1, wb2, bb2, wt1, bt1, wt2, bt2, wt3,
+             bt3: float) -> rec_dlrm_mlp:
+    return rec_dlrm_mlp(n_dense, dim, S, 0, _p(wb1), _p(bb1), _p(wb2), _p(bb2), _p(wt1), _p(bt1),
+                        _p(wt2), _p(bt2), _p(wt3), float(bt3))
+
+
+def rec_dlrm_fwd(mlp: rec_dlrm_mlp, tables: Sequence[rec_table], modes: Sequence[int], B: int,
+                 dense, values, lengths, offsets, z, inter, logit, prob=None, stream=None):
+    md = None if modes is None else (C.c_int32 * len(modes))(*[int(x) for x in modes])
+    _check(lib().rec_dlrm_fwd(C.byref(mlp) if mlp is not None else None,
+                              _tables(tables) if tables is not None else None, md, B, _p(dense),
+                              _p(values), _p(lengths), _p(offsets), _p(z), _p(inter), _p(logit),
+                              _p(prob), _stream(stream)),
+           "rec_dlrm_fwd")
 
 
 def rec_hash_clear(table_: rec_table, stream=None):

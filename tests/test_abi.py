@@ -626,3 +626,47 @@ def test_noalloc_limit_checked_before_the_device(lib):
     a.B = 8192                    # fits: the argument checks come next (no tables given)
     s, msg = _status(lib.rec_sparse_din_fwd_noalloc, C.byref(a), None)
     assert s == R.REC_EINVAL and "rec_sparse_din_fwd_noalloc" in msg
+
+
+def test_dlrm_fwd_errors(lib):
+    """rec_dlrm_fwd: every bad argument is refused on the host."""
+    S, d, nd = 8, 96, 13
+    good = R.dlrm_mlp(nd, d, S, *([FAKE] * 9), 0.0)
+    tabs = [_table(rows=100, dim=d) for _ in range(S)]
+    modes = [R.REC_POOL_SUM] * S
+
+    def call(mlp=good, tables=tabs, md=modes, B=4, dense=FAKE, values=FAKE, lengths=FAKE,
+             offsets=FAKE, z=FAKE, inter=None, logit=FAKE, prob=None):
+        m = None if mlp is None else C.byref(mlp)
+        t = None if tables is None else R._tables(tables)
+        mm = None if md is None else (C.c_int32 * len(md))(*md)
+        return _status(lib.rec_dlrm_fwd, m, t, mm, B, dense, values, lengths, offsets, z, inter,
+                       logit, prob, None)
+    assert call(mlp=None)[0] == R.REC_EINVAL
+    assert call(tables=None)[0] == R.REC_EINVAL
+    assert call(md=None)[0] == R.REC_EINVAL
+    assert call(B=-1)[0] == R.REC_EINVAL
+    for kw in (dict(S=0), dict(S=32), dict(dim=48), dict(dim=16), dict(dim=288), dict(n_dense=0),
+               dict(n_dense=129)):
+        m = R.dlrm_mlp(kw.get("n_dense", nd), kw.get("dim", d), kw.get("S", S), *([FAKE] * 9), 0.0)
+        s, msg = call(mlp=m, tables=[_table(rows=100, dim=kw.get("dim", d))] * max(kw.get("S", S), 1),
+                      md=[0] * max(kw.get("S", S), 1))
+        assert s == R.REC_EINVAL, kw
+    m = R.dlrm_mlp(nd, 128, 8, *([FAKE] * 9), 0.0)               # (S+1) * dim = 1152 > 1024
+    assert call(mlp=m, tables=[_table(rows=100, dim=128)] * 8)[0] == R.REC_EINVAL
+    m = R.dlrm_mlp(nd, d, S, *([FAKE] * 8), None, 0.0)
+    assert call(mlp=m)[0] == R.REC_EINVAL
+    m = R.dlrm_mlp(nd, d, S, FAKE_ODD, *([FAKE] * 8), 0.0)
+    assert call(mlp=m)[0] == R.REC_EINVAL
+    bad = list(tabs)
+    bad[3] = _table(rows=100, dim=16)
+    assert call(tables=bad)[0] == R.REC_EINVAL
+    bad[3] = _table(kind=R.REC_HASH, rows=100, dim=d, keys=FAKE, digests=FAKE)
+    assert call(tables=bad)[0] == R.REC_EINVAL
+    bad[3] = _table(rows=0, dim=d)
+    assert call(tables=bad)[0] == R.REC_EINVAL
+    assert call(md=[0] * 7 + [2])[0] == R.REC_EINVAL
+    for k in ("dense", "values", "lengths", "offsets", "z", "logit"):
+        assert call(**{k: None})[0] == R.REC_EINVAL, k
+    assert call(z=FAKE_ODD)[0] == R.REC_EINVAL
+    assert call(B=0, dense=None, values=None, lengths=None, offsets=None, z=None, logit=None)[0] == R.REC_OK
