@@ -92,6 +92,9 @@ class Oracle:
                                    P64, C.POINTER(PF), P32, P64, P32, P64, PD, PD, PD, PD, PD,
                                    C.c_double, PD, PD, PD, PD, PD, PD]
         L.orc_dlrm_fwd.restype = None
+        L.orc_hash_admit.argtypes = [P64, P8, PU, PF, C.c_int64, C.c_int64, P64, PU, C.c_int64, P64,
+                                     PF, C.c_int64, C.c_uint64, C.c_int32, C.c_uint64, P64, P64]
+        L.orc_hash_admit.restype = None
         self._keep = []
 
     # -- bookkeeping ---------------------------------------------------------
@@ -134,6 +137,43 @@ class Oracle:
                                  _ptr(keys, P64), _ptr(vals, PF), keys.size, int(mode),
                                  int(step), _ptr(out, P64))
         return out
+
+    @staticmethod
+    def empty_counter_table(capacity: int) -> dict:
+        """An empty admission counter table: keys -1, counts 0."""
+        return dict(rows=capacity, keys=np.full(capacity, -1, np.int64),
+                    counts=np.zeros(capacity, np.uint64))
+
+    def hash_admit(self, tab: dict, counter: dict, keys: np.ndarray, init_vals: np.ndarray,
+                   threshold: int, mode: int, step: int = 0, max_keys: Optional[int] = None):
+        """One admission step ("集成 DynamicEmb" §4.1, §4.2) in place on `tab`
+        (keys, digests, scores, values) and `counter` (keys, counts).
+        Returns (slot of every key after the call, [admitted, evicted,
+        candidates left out])."""
+        keys = np.ascontiguousarray(keys, np.int64)
+        init_vals = np.ascontiguousarray(init_vals, np.float32).reshape(-1, 16)
+        assert init_vals.shape[0] == keys.size
+        for k, t in (("keys", np.int64), ("digests", np.uint8), ("scores", np.uint64),
+                     ("values", np.float32)):
+            assert tab[k].dtype == t and tab[k].flags.c_contiguous, k
+        assert counter["keys"].dtype == np.int64 and counter["counts"].dtype == np.uint64
+        cap = int(tab["rows"])
+        mk = cap if max_keys is None else int(max_keys)
+        out = np.empty(keys.size, np.int64)
+        counts = np.zeros(3, np.int64)
+        self.lib.orc_hash_admit(_ptr(tab["keys"], P64), _ptr(tab["digests"], P8),
+                                _ptr(tab["scores"], PU), _ptr(tab["values"], PF), cap, mk,
+                                _ptr(counter["keys"], P64), _ptr(counter["counts"], PU),
+                                int(counter["rows"]), _ptr(keys, P64), _ptr(init_vals, PF),
+                                keys.size, int(threshold), int(mode), int(step), _ptr(out, P64),
+                                _ptr(counts, P64))
+        return out, counts
+
+    @staticmethod
+    def hash_find_slow(tab: dict, key: int) -> int:
+        """The slot holding `key`, by a scan of every slot (-1 if none)."""
+        hit = np.nonzero(tab["keys"] == key)[0]
+        return int(hit[0]) if hit.size else -1
 
     def hash_check(self, keys: np.ndarray, digests: np.ndarray) -> int:
         """Number of slots that break the table convention (0 for a valid table)."""

@@ -56,6 +56,7 @@
 
 #define ORC_DIM 16
 #define ORC_EMPTY_KEY ((int64_t)-1)
+#define ORC_TOMBSTONE ((int64_t)-2)      /* a slot whose key was evicted */
 
 /* ---- jagged bookkeeping ([P1] §2: values + lengths -> offsets) ---------- */
 void orc_lengths_to_offsets(const int32_t* lengths, int64_t n, int64_t* offsets) {
@@ -142,7 +143,7 @@ void orc_hash_insert(int64_t* tkeys, uint8_t* tdig, uint64_t* tscores, float* tv
                      int32_t mode, uint64_t step, int64_t* slot_out) {
     for (int64_t i = 0; i < n; ++i) {
         const int64_t key = keys[i];
-        if (key == ORC_EMPTY_KEY) { slot_out[i] = -2; continue; }
+        if (key == ORC_EMPTY_KEY || key == ORC_TOMBSTONE) { slot_out[i] = -2; continue; }
         const uint64_t h = orc_mix64((uint64_t)key);
         int64_t at = orc_home(h, capacity), slot = -1;
         int is_new = 0;
@@ -177,6 +178,10 @@ int64_t orc_hash_check(const int64_t* tkeys, const uint8_t* tdig, int64_t capaci
     for (int64_t s = 0; s < capacity; ++s) {
         if (tkeys[s] == ORC_EMPTY_KEY) {
             if (tdig[s] != 0) ++bad;
+            continue;
+        }
+        if (tkeys[s] == ORC_TOMBSTONE) {        /* a deleted key: probes pass it */
+            if (tdig[s] == 0) ++bad;
             continue;
         }
         seen[n++] = tkeys[s];
@@ -720,4 +725,147 @@ void orc_dlrm_fwd(int64_t B, int32_t nd, int32_t d, int32_t S, const double* den
         prob[b] = 1.0 / (1.0 + exp(-lg));
         if (lscale) lscale[b] = mag;
     }
+}
+
+/* ------------------------------------------------------------------------
+ * Frequency admission and score-driven eviction, one batch of ids at a time
+ * ([P2] §4.1: an id enters its table only once it has been seen at least
+ * `threshold` times, and until then reads the constant 0 vector; §4.2: the
+ * score strategy picks what leaves a full table -- STEP the entry inserted
+ * earliest, LFU the one used least, NO_EVICTION none, so a full table stops
+ * taking ids; §2 and §7: an initializer gives a new row its values).
+ * Readings (the pages give no algorithm):
+ *   - the ids of a call are taken together: each distinct id counts once per
+ *     occurrence; the distinct ids are processed in the order of their first
+ *     occurrence;
+ *   - an id already stored is "used": STEP sets its score to `step`, LFU
+ *     adds its number of occurrences, NO_EVICTION leaves scores alone;
+ *   - an id not stored adds its occurrences to its count in the counter
+ *     table (a second key -> count table, 0 when absent); it becomes a
+ *     candidate when the count reaches `threshold`, else the count is kept;
+ *   - the table holds at most max_keys ids.  Candidates are admitted in
+ *     first-occurrence order while there is room; for the rest, STEP and LFU
+ *     first evict as many entries stored before the call as there are
+ *     candidates left, the smallest scores first (scores compared after
+ *     saturating at 2^32 - 1; equal scores: the lower slot first), and then
+ *     admit that many more; candidates still left keep their counts;
+ *   - an evicted slot becomes a tombstone (key -2, digest kept, score 0):
+ *     lookups pass it, inserts may reuse it; -1 and -2 are never stored;
+ *   - an admitted id takes the first empty or tombstone slot of its probe
+ *     sequence, its digest, init_vals of its first occurrence, the score
+ *     `step` (STEP), its count (LFU) or none (NO_EVICTION); its count in the
+ *     counter table becomes 0;
+ *   - a new id whose count has no room in a full counter table is not
+ *     counted (its count stays 0 before this call's occurrences).
+ * slot_out[i] is the slot holding keys[i] after the call, -1 if absent, -2
+ * for the reserved keys.  counts_out (3): ids admitted, entries evicted,
+ * candidates left out.  The tables are searched by scanning their slots, so
+ * nothing here depends on probe order except where a new id is placed.     */
+static int64_t orc_scan_find(const int64_t* k, int64_t cap, int64_t key) {
+    for (int64_t s = 0; s < cap; ++s)
+        if (k[s] == key) return s;
+    return -1;
+}
+
+typedef struct { uint64_t score; int64_t slot; } orc_victim;
+
+static int orc_victim_cmp(const void* a, const void* b) {
+    const orc_victim* x = (const orc_victim*)a;
+    const orc_victim* y = (const orc_victim*)b;
+    if (x->score != y->score) return x->score < y->score ? -1 : 1;
+    return (x->slot > y->slot) - (x->slot < y->slot);
+}
+
+void orc_hash_admit(int64_t* tkeys, uint8_t* tdig, uint64_t* tscores, float* tvals,
+                    int64_t capacity, int64_t max_keys, int64_t* ckeys, uint64_t* ccounts,
+                    int64_t ccap, const int64_t* keys, const float* init_vals, int64_t n,
+                    uint64_t threshold, int32_t mode, uint64_t step, int64_t* slot_out,
+                    int64_t* counts_out) {
+    int64_t* dk = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));   /* distinct ids */
+    int64_t* df = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));   /* first index */
+    uint64_t* dc = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)(n > 0 ? n : 1)); /* occurrences */
+    int64_t nd = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if (keys[i] == ORC_EMPTY_KEY || keys[i] == ORC_TOMBSTONE) continue;
+        int64_t j = 0;
+        while (j < nd && dk[j] != keys[i]) ++j;
+        if (j == nd) { dk[nd] = keys[i]; df[nd] = i; dc[nd] = 0; ++nd; }
+        dc[j] += 1;
+    }
+    int64_t stored = 0;
+    for (int64_t s = 0; s < capacity; ++s)
+        stored += tkeys[s] != ORC_EMPTY_KEY && tkeys[s] != ORC_TOMBSTONE;
+    int64_t* cand = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nd > 0 ? nd : 1));
+    uint64_t* ctot = (uint64_t*)malloc(sizeof(uint64_t) * (size_t)(nd > 0 ? nd : 1));
+    int64_t ncand = 0;
+    for (int64_t j = 0; j < nd; ++j) {
+        const int64_t s = orc_scan_find(tkeys, capacity, dk[j]);
+        if (s >= 0) {
+            if (mode == ORC_SCORE_STEP) tscores[s] = step;
+            if (mode == ORC_SCORE_LFU) tscores[s] += dc[j];
+            continue;
+        }
+        const int64_t c = orc_scan_find(ckeys, ccap, dk[j]);
+        const uint64_t total = (c >= 0 ? ccounts[c] : 0) + dc[j];
+        if (total >= threshold) {
+            cand[ncand] = j;
+            ctot[ncand] = total;
+            ++ncand;
+        } else if (c >= 0) {
+            ccounts[c] = total;
+        } else {
+            const int64_t e = orc_scan_find(ckeys, ccap, ORC_EMPTY_KEY);
+            if (e >= 0) { ckeys[e] = dk[j]; ccounts[e] = total; }
+        }
+    }
+    int64_t room = max_keys - stored;
+    if (room < 0) room = 0;
+    int64_t nvict = 0;
+    if (mode != ORC_SCORE_NONE && ncand > room) {
+        orc_victim* v = (orc_victim*)malloc(sizeof(orc_victim) * (size_t)(stored > 0 ? stored : 1));
+        int64_t nv = 0;
+        for (int64_t s = 0; s < capacity; ++s) {
+            if (tkeys[s] == ORC_EMPTY_KEY || tkeys[s] == ORC_TOMBSTONE) continue;
+            v[nv].score = tscores[s] < 0xffffffffull ? tscores[s] : 0xffffffffull;
+            v[nv].slot = s;
+            ++nv;
+        }
+        qsort(v, (size_t)nv, sizeof(orc_victim), orc_victim_cmp);
+        nvict = ncand - room < nv ? ncand - room : nv;
+        for (int64_t i = 0; i < nvict; ++i) {
+            tkeys[v[i].slot] = ORC_TOMBSTONE;
+            tscores[v[i].slot] = 0;
+        }
+        free(v);
+    }
+    int64_t admit = room + nvict < ncand ? room + nvict : ncand;
+    for (int64_t q = 0; q < ncand; ++q) {
+        const int64_t j = cand[q];
+        const int64_t c = orc_scan_find(ckeys, ccap, dk[j]);
+        if (q >= admit) {                       /* left out: the count is kept */
+            if (c >= 0) ccounts[c] = ctot[q];
+            else {
+                const int64_t e = orc_scan_find(ckeys, ccap, ORC_EMPTY_KEY);
+                if (e >= 0) { ckeys[e] = dk[j]; ccounts[e] = ctot[q]; }
+            }
+            continue;
+        }
+        if (c >= 0) ccounts[c] = 0;
+        const uint64_t h = orc_mix64((uint64_t)dk[j]);
+        int64_t at = orc_home(h, capacity);
+        while (tkeys[at] != ORC_EMPTY_KEY && tkeys[at] != ORC_TOMBSTONE)
+            at = (at + 1 == capacity) ? 0 : at + 1;
+        tkeys[at] = dk[j];
+        tdig[at] = orc_digest(h);
+        memcpy(tvals + at * ORC_DIM, init_vals + df[j] * ORC_DIM, sizeof(float) * ORC_DIM);
+        if (mode == ORC_SCORE_STEP) tscores[at] = step;
+        if (mode == ORC_SCORE_LFU) tscores[at] = ctot[q];
+    }
+    for (int64_t i = 0; i < n; ++i)
+        slot_out[i] = (keys[i] == ORC_EMPTY_KEY || keys[i] == ORC_TOMBSTONE)
+                          ? -2 : orc_scan_find(tkeys, capacity, keys[i]);
+    counts_out[0] = admit;
+    counts_out[1] = nvict;
+    counts_out[2] = ncand - admit;
+    free(dk); free(df); free(dc); free(cand); free(ctot);
 }

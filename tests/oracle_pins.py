@@ -884,7 +884,144 @@ def pin_dlrm_fwd(orc):
                                                         rtol=1e-15, atol=0)
 
 
+def pin_hash_admit(orc):
+    """Frequency admission and score-driven eviction ("集成 DynamicEmb" §4.1
+    threshold, §4.2 STEP / LFU / NO_EVICTION) against the pinned insert, the
+    generator's convention and closed forms: with threshold 1 and room it is
+    the insert of the distinct ids; ids are admitted exactly at the call
+    where their running count reaches the threshold (LFU starting from that
+    count); a full table evicts the oldest (STEP) or least used (LFU) entries
+    stored before the call, lower slot first on equal scores, scores
+    saturating at 2^32 - 1; a used id is not the oldest any more; a new id
+    takes the first free slot (empty or tombstone) from its home; NO_EVICTION
+    admits nothing into a full table and keeps the counts; reserved ids are
+    neither stored nor counted; a full counter table counts no new id."""
+    NONE, STEP, LFU = orc.SCORE_NONE, orc.SCORE_STEP, orc.SCORE_LFU
+    rng = np.random.default_rng(4141)
+    vals = lambda n: rng.standard_normal((n, 16)).astype(np.float32)  # noqa: E731
+    # (1) threshold 1, room, NO_EVICTION: the insert of the distinct ids in
+    # first-occurrence order, with the values of their first occurrence
+    cap = 997
+    base = _distinct_keys(rng, 300)
+    keys = np.concatenate([base, base[::3], base[::7]])
+    v = vals(keys.size)
+    t, c = orc.empty_hash_table(cap), orc.empty_counter_table(2048)
+    slots, cnt = orc.hash_admit(t, c, keys, v, 1, NONE)
+    t2 = orc.empty_hash_table(cap)
+    s2 = orc.hash_insert(t2, base, v[:300])
+    for f in ("keys", "digests"):
+        assert np.array_equal(t[f], t2[f]), f
+    occ = t["keys"] != -1
+    assert np.array_equal(t["values"][occ], t2["values"][occ])
+    assert np.array_equal(slots[:300], s2) and list(cnt) == [300, 0, 0]
+    assert orc.hash_check(t["keys"], t["digests"]) == 0
+    # (2) running counts: admitted at the first call where the count reaches 3
+    t, c = orc.empty_hash_table(101), orc.empty_counter_table(101)
+    k = np.array([11, 22, 33], np.int64)
+    calls = [np.array([11, 22]), np.array([11, 33, 33]), np.array([22, 11, 33]), np.array([22, 22])]
+    admitted_at = {}
+    for step, kk in enumerate(calls):
+        sl, _ = orc.hash_admit(t, c, kk.astype(np.int64), vals(kk.size), 3, LFU, step)
+        for key in k:
+            s_ = orc.hash_find_slow(t, int(key))
+            if s_ >= 0 and int(key) not in admitted_at:
+                admitted_at[int(key)] = step
+                # LFU starts from the running count that reached the threshold
+                assert t["scores"][s_] == {11: 3, 33: 3, 22: 4}[int(key)], (key, t["scores"][s_])
+        for key, s_ in zip(kk, sl):
+            assert (s_ >= 0) == (int(key) in admitted_at)
+    assert admitted_at == {11: 2, 33: 2, 22: 3}
+    assert t["scores"][orc.hash_find_slow(t, 11)] == 3 and t["scores"][orc.hash_find_slow(t, 33)] == 3
+    assert t["scores"][orc.hash_find_slow(t, 22)] == 4          # 1 + 1 + 2 at admission
+    assert not np.any(c["counts"][np.isin(c["keys"], k)])      # counts reset on admission
+    # (3) STEP eviction: 16 ids admitted at steps 1..16 fill max_keys = 16;
+    # three new ids at step 100 evict the three oldest; an old id that is
+    # used in the same call is not among them
+    cap = 64
+    t, c = orc.empty_hash_table(cap), orc.empty_counter_table(256)
+    old = _distinct_keys(rng, 16)
+    for i, key in enumerate(old):
+        orc.hash_admit(t, c, np.array([key]), vals(1), 1, STEP, 1 + i, max_keys=16)
+    where = {int(key): orc.hash_find_slow(t, int(key)) for key in old}
+    # the first new id's home is the slot of old[1], which this call evicts:
+    # it must take that tombstone
+    cand_k = _distinct_keys(np.random.default_rng(8), 20000)
+    homes = synth.home_slot(synth.splitmix64_mix(cand_k), cap)
+    first = cand_k[np.nonzero(homes == where[int(old[1])])[0][0]]
+    rest = cand_k[(homes != where[int(old[1])]) & ~np.isin(cand_k, old)][:2]
+    new = np.concatenate([[first], rest]).astype(np.int64)
+    batch = np.concatenate([new, old[:1]])
+    sl, cnt = orc.hash_admit(t, c, batch, vals(4), 1, STEP, 100, max_keys=16)
+    assert list(cnt) == [3, 3, 0] and np.all(sl >= 0)
+    for i, key in enumerate(old):
+        s_ = orc.hash_find_slow(t, int(key))
+        assert (s_ < 0) == (i in (1, 2, 3)), i
+        if s_ >= 0:
+            assert s_ == where[int(key)]                       # survivors keep their slots
+    assert t["scores"][where[int(old[0])]] == 100
+    assert orc.hash_find_slow(t, int(first)) == where[int(old[1])]
+    assert orc.hash_check(t["keys"], t["digests"]) == 0
+    stored = (t["keys"] != -1) & (t["keys"] != -2)
+    assert stored.sum() == 16 and np.sum(t["keys"] == -2) <= 3
+    # new ids sit at the first free slot (empty or tombstone) from their home
+    h = synth.splitmix64_mix(new)
+    for key, home in zip(new, synth.home_slot(h, cap)):
+        s_ = orc.hash_find_slow(t, int(key))
+        q = int(home)
+        while q != s_:
+            assert t["keys"][q] not in (-1, -2)                # passed no free slot
+            q = (q + 1) % cap
+    # (4) LFU eviction: counts 5, 1, 3, 1 -> the two least used go, equal
+    # counts lower slot first; scores above 2^32 - 1 compare as equal
+    t, c = orc.empty_hash_table(16), orc.empty_counter_table(64)
+    ks = _distinct_keys(rng, 4)
+    for key, n_ in zip(ks, (5, 1, 3, 1)):
+        orc.hash_admit(t, c, np.full(n_, key, np.int64), vals(n_), 1, LFU, 0, max_keys=4)
+    sl_old = [orc.hash_find_slow(t, int(key)) for key in ks]
+    fresh = _distinct_keys(np.random.default_rng(9), 2)
+    _, cnt = orc.hash_admit(t, c, fresh, vals(2), 1, LFU, 0, max_keys=4)
+    assert list(cnt) == [2, 2, 0]
+    assert [orc.hash_find_slow(t, int(key)) >= 0 for key in ks] == [True, False, True, False]
+    t, c = orc.empty_hash_table(16), orc.empty_counter_table(64)
+    for key in ks[:3]:
+        orc.hash_admit(t, c, np.array([key]), vals(1), 1, LFU, 0, max_keys=3)
+    sl3 = [orc.hash_find_slow(t, int(key)) for key in ks[:3]]
+    t["scores"][sl3[0]], t["scores"][sl3[1]], t["scores"][sl3[2]] = 2**33, 2**40, 7
+    orc.hash_admit(t, c, ks[3:4], vals(1), 1, LFU, 0, max_keys=3)
+    gone = [i for i in range(3) if orc.hash_find_slow(t, int(ks[i])) < 0]
+    assert gone == [2]                                             # 7 is the least
+    s3 = orc.hash_find_slow(t, int(ks[3]))
+    left = {sl3[0]: 0, sl3[1]: 1, s3: 3}                          # slot -> id index
+    order = sorted(left)
+    # scores all at or above 2^32 - 1: equal after saturation, so the lowest
+    # slot goes even though its raw score is the largest
+    for sl_, sc in zip(order, (2**41, 2**34, 2**32 + 5)):
+        t["scores"][sl_] = sc
+    orc.hash_admit(t, c, fresh[:1], vals(1), 1, LFU, 0, max_keys=3)
+    gone = [i for i in (0, 1, 3) if orc.hash_find_slow(t, int(ks[i])) < 0]
+    assert gone == [left[order[0]]]
+    # (5) NO_EVICTION keeps a full table and the counts of those left out
+    t, c = orc.empty_hash_table(32), orc.empty_counter_table(64)
+    ks = _distinct_keys(rng, 6)
+    orc.hash_admit(t, c, ks[:4], vals(4), 1, NONE, max_keys=4)
+    before = _stored_map(t)
+    sl, cnt = orc.hash_admit(t, c, np.repeat(ks[4:], 2), vals(4), 2, NONE, max_keys=4)
+    assert list(cnt) == [0, 0, 2] and np.all(sl == -1) and _stored_map(t) == before
+    got = {int(key): int(n_) for key, n_ in zip(c["keys"], c["counts"]) if key != -1}
+    assert got[int(ks[4])] == 2 and got[int(ks[5])] == 2
+    sl, cnt = orc.hash_admit(t, c, ks[4:5], vals(1), 2, NONE, max_keys=4)    # 2 + 1, still left out
+    assert list(cnt) == [0, 0, 1] and sl[0] == -1
+    got = {int(key): int(n_) for key, n_ in zip(c["keys"], c["counts"]) if key != -1}
+    assert got[int(ks[4])] == 3
+    # (6) reserved ids; (7) a full counter table counts no new id
+    t, c = orc.empty_hash_table(32), orc.empty_counter_table(2)
+    sl, cnt = orc.hash_admit(t, c, np.array([-1, -2, 5, 6, 7, 5], np.int64), vals(6), 3, LFU)
+    assert sl[0] == -2 and sl[1] == -2 and np.all(sl[2:] == -1) and list(cnt) == [0, 0, 0]
+    assert sorted(c["keys"].tolist()) == [5, 6] and sorted(c["counts"].tolist()) == [1, 2]
+    assert not np.any(t["keys"] == -2)
+
+
 ALL_PINS = [pin_offsets, pin_floor_mod, pin_hash, pin_embbag_direct, pin_embbag_hash,
             pin_din_vs_padded, pin_din_closed_forms, pin_din_hash, pin_towers_closed_forms,
             pin_towers_library, pin_hash_insert, pin_dlrm_interact, pin_embbag_adagrad,
-            pin_din_bwd, pin_dlrm_fwd]
+            pin_din_bwd, pin_dlrm_fwd, pin_hash_admit]

@@ -136,6 +136,25 @@ MUTANTS = [
     ("DLRM sigmoid sign flipped", "prob[b] = 1.0 / (1.0 + exp(-lg));", "prob[b] = 1.0 / (1.0 + exp(lg));"),
     ("DLRM interaction squares the row", "acc += zb[(int64_t)i * d + k] * zb[(int64_t)j * d + k];",
      "acc += zb[(int64_t)i * d + k] * zb[(int64_t)i * d + k];"),
+    ("admission above, not at, the threshold", "if (total >= threshold) {", "if (total > threshold) {"),
+    ("admission counts an id once per batch", "dc[j] += 1;", "dc[j] = 1;"),
+    ("eviction takes the largest score", "if (x->score != y->score) return x->score < y->score ? -1 : 1;",
+     "if (x->score != y->score) return x->score > y->score ? -1 : 1;"),
+    ("eviction ties take the higher slot", "return (x->slot > y->slot) - (x->slot < y->slot);",
+     "return (x->slot < y->slot) - (x->slot > y->slot);"),
+    ("eviction scores not saturated", "v[nv].score = tscores[s] < 0xffffffffull ? tscores[s] : 0xffffffffull;",
+     "v[nv].score = tscores[s];"),
+    ("a used id keeps its STEP score", "if (mode == ORC_SCORE_STEP) tscores[s] = step;\n            if (mode == ORC_SCORE_LFU) tscores[s] += dc[j];",
+     "if (mode == ORC_SCORE_LFU) tscores[s] += dc[j];"),
+    ("an admitted LFU entry starts at 1", "if (mode == ORC_SCORE_LFU) tscores[at] = ctot[q];",
+     "if (mode == ORC_SCORE_LFU) tscores[at] = 1;"),
+    ("the count survives admission", "if (c >= 0) ccounts[c] = 0;", "if (0) ccounts[c] = 0;"),
+    ("admission never reuses a tombstone", "while (tkeys[at] != ORC_EMPTY_KEY && tkeys[at] != ORC_TOMBSTONE)",
+     "while (tkeys[at] != ORC_EMPTY_KEY)"),
+    ("the tombstone marker counts as an id",
+     "if (keys[i] == ORC_EMPTY_KEY || keys[i] == ORC_TOMBSTONE) continue;", "if (keys[i] == ORC_EMPTY_KEY) continue;"),
+    ("NO_EVICTION evicts", "if (mode != ORC_SCORE_NONE && ncand > room) {", "if (ncand > room) {"),
+    ("left-out candidates lose their counts", "if (c >= 0) ccounts[c] = ctot[q];", "if (c >= 0) ccounts[c] = 0;"),
 ]
 
 
