@@ -852,9 +852,12 @@ void orc_hash_admit(int64_t* tkeys, uint8_t* tdig, uint64_t* tscores, float* tva
         }
         if (c >= 0) ccounts[c] = 0;
         const uint64_t h = orc_mix64((uint64_t)dk[j]);
-        int64_t at = orc_home(h, capacity);
-        while (tkeys[at] != ORC_EMPTY_KEY && tkeys[at] != ORC_TOMBSTONE)
+        int64_t at = orc_home(h, capacity), probes = 0;
+        while (probes < capacity && tkeys[at] != ORC_EMPTY_KEY && tkeys[at] != ORC_TOMBSTONE) {
             at = (at + 1 == capacity) ? 0 : at + 1;
+            ++probes;
+        }
+        if (probes == capacity) continue;       /* cannot happen: room was counted */
         tkeys[at] = dk[j];
         tdig[at] = orc_digest(h);
         memcpy(tvals + at * ORC_DIM, init_vals + df[j] * ORC_DIM, sizeof(float) * ORC_DIM);

@@ -149,8 +149,9 @@ MUTANTS = [
     ("an admitted LFU entry starts at 1", "if (mode == ORC_SCORE_LFU) tscores[at] = ctot[q];",
      "if (mode == ORC_SCORE_LFU) tscores[at] = 1;"),
     ("the count survives admission", "if (c >= 0) ccounts[c] = 0;", "if (0) ccounts[c] = 0;"),
-    ("admission never reuses a tombstone", "while (tkeys[at] != ORC_EMPTY_KEY && tkeys[at] != ORC_TOMBSTONE)",
-     "while (tkeys[at] != ORC_EMPTY_KEY)"),
+    ("admission never reuses a tombstone",
+     "while (probes < capacity && tkeys[at] != ORC_EMPTY_KEY && tkeys[at] != ORC_TOMBSTONE) {",
+     "while (probes < capacity && tkeys[at] != ORC_EMPTY_KEY) {"),
     ("the tombstone marker counts as an id",
      "if (keys[i] == ORC_EMPTY_KEY || keys[i] == ORC_TOMBSTONE) continue;", "if (keys[i] == ORC_EMPTY_KEY) continue;"),
     ("NO_EVICTION evicts", "if (mode != ORC_SCORE_NONE && ncand > room) {", "if (ncand > room) {"),
