@@ -73,6 +73,7 @@ enum { REC_POOL_SUM = 0, REC_POOL_MEAN = 1 };                    /* rec_dlrm_fwd
 
 #define REC_DIM 16                        /* embedding width of every table */
 #define REC_EMPTY_KEY ((int64_t)-1)       /* empty hash slot; never a valid key */
+#define REC_TOMBSTONE_KEY ((int64_t)-2)   /* slot of an evicted key (rec_hash_admit); never a valid key */
 #define REC_MAX_TABLES 32                 /* tables per rec_embbag_fwd call */
 #define REC_MAX_SEQ_LEN 1024              /* largest max_len for the DIN calls */
 #define REC_MAX_B 16777215                /* largest batch for the DIN plan */
@@ -99,10 +100,12 @@ enum { REC_POOL_SUM = 0, REC_POOL_MEAN = 1 };                    /* rec_dlrm_fwd
  *              0xbf58476d1ce4e5b9, 0x94d049bb133111eb),
  *     home   = floor(h * rows / 2^64),
  *     digest = h & 0xff, or 1 if that is 0,
- *   every stored key sits at the first free slot of the linear, wrapping probe
- *   sequence home, home+1, ... at the time it was inserted (no deletes).  A
- *   lookup of key x returns the slot holding x, or -1 (a miss) on reaching an
- *   empty slot or after `rows` probes.  A miss yields the zero vector
+ *   every stored key sits on the linear, wrapping probe sequence home,
+ *   home+1, ... with no empty slot between its home and its slot.  A slot
+ *   whose key was evicted (rec_hash_admit) holds REC_TOMBSTONE_KEY and keeps
+ *   its nonzero digest: probes pass it.  A lookup of key x returns the slot
+ *   holding x, or -1 (a miss) on reaching an empty slot or after `rows`
+ *   probes; REC_EMPTY_KEY and REC_TOMBSTONE_KEY always miss.  A miss yields the zero vector
  *   (§3.2: the constant zero vector).  The raw id is the key (no modulo).
  *
  * Every table: dim == 16, rows >= 1 (REC_HASH: rows <= 2^31 - 1), values
@@ -259,7 +262,7 @@ size_t rec_hash_insert_workspace_bytes(int64_t n, int64_t capacity);
  *   slot_out   int64[n] or NULL: the slot the key is stored in, -1 when the
  *              table had no empty slot on the key's probe sequence (the pair
  *              is not stored: no eviction, the NO_EVICTION behaviour), -2 for
- *              REC_EMPTY_KEY (never stored)
+ *              REC_EMPTY_KEY and REC_TOMBSTONE_KEY (never stored)
  *   workspace  >= rec_hash_insert_workspace_bytes(n, table->rows) bytes of
  *              device memory, 256-byte aligned, contents on entry ignored
  * The result is that of inserting the pairs one after another in index
@@ -277,6 +280,70 @@ size_t rec_hash_insert_workspace_bytes(int64_t n, int64_t capacity);
 rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const float* values,
                            int64_t n, int32_t score_mode, uint64_t step, int64_t* slot_out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace rec_hash_admit needs for n ids into a table of
+ * `capacity` slots (about 40 B per id, plus 16 B per slot for the eviction
+ * sort unless score_mode is REC_SCORE_NONE); 0 for invalid arguments. */
+size_t rec_hash_admit_workspace_bytes(int64_t n, int64_t capacity, int32_t score_mode);
+
+/*
+ * Frequency admission and score-driven eviction for one batch of ids
+ * ("集成 DynamicEmb" §4.1: an id enters its table only once it has been seen
+ * `threshold` times, and reads the constant 0 vector until then; §4.2: STEP
+ * evicts the entry inserted earliest, LFU the one used least, NO_EVICTION
+ * never evicts, so a full table stops taking ids; §2, §7: an initializer
+ * gives a new row its values).  Rules, the ids of the call taken together:
+ *   - every id counts once per occurrence; REC_EMPTY_KEY and
+ *     REC_TOMBSTONE_KEY are ignored;
+ *   - a stored id is used: REC_SCORE_STEP sets its score to `step`,
+ *     REC_SCORE_LFU adds its occurrences; REC_SCORE_NONE (NO_EVICTION)
+ *     leaves scores alone;
+ *   - an id not stored adds its occurrences to its count in the counter
+ *     table (0 when absent) and becomes a candidate when the count reaches
+ *     `threshold`; otherwise the count is kept (a new id finding the counter
+ *     table full is not counted);
+ *   - the table holds at most max_keys ids.  Candidates are admitted in the
+ *     order of their first occurrence while there is room.  For those left,
+ *     STEP and LFU evict as many entries stored before the call, smallest
+ *     score first (scores saturated at 2^32 - 2 for the comparison; equal
+ *     scores: smaller id first, as signed integers), and admit as many more.
+ *     Candidates not admitted keep their counts;
+ *   - an evicted slot becomes a tombstone (key REC_TOMBSTONE_KEY, digest
+ *     kept, score 0); lookups pass it, new ids may take it;
+ *   - an admitted id takes an empty or tombstone slot of its probe sequence
+ *     with no empty slot before it, its digest, its values from init_values
+ *     at its first occurrence, the score `step` (STEP) or its count (LFU),
+ *     and its count becomes 0.
+ *   table        host descriptor, kind REC_HASH; keys, digests, values and (STEP,
+ *                LFU) scores are written
+ *   max_keys     0 .. capacity (capacity: the table may fill every slot)
+ *   counter_keys int64[counter_capacity], counter_counts uint64[...]: the
+ *                admission counters, kept by the caller across calls (start:
+ *                keys REC_EMPTY_KEY, counts 0); placement by the table
+ *                convention (no digests)
+ *   keys         int64[n];  init_values fp32 [n][16], 16-byte aligned (e.g.
+ *                N(0, 0.05) draws, the pages' initializer)
+ *   slot_out     int64[n] or NULL: the slot of each id after the call, -1 if
+ *                not stored, -2 for the reserved keys
+ *   counts_out   device int64[3] or NULL: ids admitted, entries evicted,
+ *                candidates left out
+ *   workspace    >= rec_hash_admit_workspace_bytes(n, capacity, score_mode),
+ *                256-byte aligned
+ * Every stored value, count and score, the victims and the admitted ids are
+ * the same run to run; which free slot a new id takes may depend on the order
+ * of concurrent claims (no lookup result does), and so may which new ids get
+ * a counter when the counter table overflows.  Nothing else may use the
+ * tables during the call.  Seven launches, 47 with STEP or LFU (the eviction
+ * sort's launches return at once when nothing is evicted).  n == 0 is a
+ * no-op.
+ * Errors: REC_EINVAL (null or misaligned arrays, bad table, score_mode,
+ * max_keys, threshold 0), REC_EUNSUPPORTED (n > 2^30), REC_EWORKSPACE.
+ */
+rec_status rec_hash_admit(const rec_table* table, int64_t max_keys, int64_t* counter_keys,
+                          uint64_t* counter_counts, int64_t counter_capacity, const int64_t* keys,
+                          const float* init_values, int64_t n, uint64_t threshold, int32_t score_mode,
+                          uint64_t step, int64_t* slot_out, int64_t* counts_out, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * DLRM dot-product interaction (DLRM essay, wmrh.cn/news/12459, §2.3: the

@@ -87,7 +87,7 @@ int64_t orc_hash_index(const int64_t* slot_keys, int64_t capacity,
     orc_pair* p = (orc_pair*)malloc(sizeof(orc_pair) * (size_t)(capacity > 0 ? capacity : 1));
     int64_t n = 0;
     for (int64_t s = 0; s < capacity; ++s)
-        if (slot_keys[s] != ORC_EMPTY_KEY) { p[n].key = slot_keys[s]; p[n].slot = s; ++n; }
+        if (slot_keys[s] != ORC_EMPTY_KEY && slot_keys[s] != ORC_TOMBSTONE) { p[n].key = slot_keys[s]; p[n].slot = s; ++n; }
     qsort(p, (size_t)n, sizeof(orc_pair), orc_pair_cmp);
     for (int64_t i = 0; i < n; ++i) { sorted_keys[i] = p[i].key; sorted_slots[i] = p[i].slot; }
     free(p);
@@ -747,7 +747,8 @@ void orc_dlrm_fwd(int64_t B, int32_t nd, int32_t d, int32_t S, const double* den
  *     first-occurrence order while there is room; for the rest, STEP and LFU
  *     first evict as many entries stored before the call as there are
  *     candidates left, the smallest scores first (scores compared after
- *     saturating at 2^32 - 1; equal scores: the lower slot first), and then
+ *     saturating at 2^32 - 2; equal scores: the smaller id first, so the
+ *     choice does not depend on where ids were placed), and then
  *     admit that many more; candidates still left keep their counts;
  *   - an evicted slot becomes a tombstone (key -2, digest kept, score 0):
  *     lookups pass it, inserts may reuse it; -1 and -2 are never stored;
@@ -767,13 +768,13 @@ static int64_t orc_scan_find(const int64_t* k, int64_t cap, int64_t key) {
     return -1;
 }
 
-typedef struct { uint64_t score; int64_t slot; } orc_victim;
+typedef struct { uint64_t score; int64_t key, slot; } orc_victim;
 
 static int orc_victim_cmp(const void* a, const void* b) {
     const orc_victim* x = (const orc_victim*)a;
     const orc_victim* y = (const orc_victim*)b;
     if (x->score != y->score) return x->score < y->score ? -1 : 1;
-    return (x->slot > y->slot) - (x->slot < y->slot);
+    return (x->key > y->key) - (x->key < y->key);
 }
 
 void orc_hash_admit(int64_t* tkeys, uint8_t* tdig, uint64_t* tscores, float* tvals,
@@ -826,7 +827,8 @@ void orc_hash_admit(int64_t* tkeys, uint8_t* tdig, uint64_t* tscores, float* tva
         int64_t nv = 0;
         for (int64_t s = 0; s < capacity; ++s) {
             if (tkeys[s] == ORC_EMPTY_KEY || tkeys[s] == ORC_TOMBSTONE) continue;
-            v[nv].score = tscores[s] < 0xffffffffull ? tscores[s] : 0xffffffffull;
+            v[nv].score = tscores[s] < 0xfffffffeull ? tscores[s] : 0xfffffffeull;
+            v[nv].key = tkeys[s];
             v[nv].slot = s;
             ++nv;
         }

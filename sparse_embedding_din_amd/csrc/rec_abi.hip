@@ -446,6 +446,89 @@ rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const fl
     return hip_status(launch_hash_insert(a, (hipStream_t)stream), "rec_hash_insert");
 }
 
+size_t rec_hash_admit_workspace_bytes(int64_t n, int64_t capacity, int32_t score_mode) {
+    if (n < 0 || n > ((int64_t)1 << 30) || capacity < 1 || capacity > 2147483647LL) return 0;
+    return admit_layout(n, capacity, score_mode != REC_SCORE_NONE).bytes;
+}
+
+rec_status rec_hash_admit(const rec_table* table, int64_t max_keys, int64_t* counter_keys,
+                          uint64_t* counter_counts, int64_t counter_capacity, const int64_t* keys,
+                          const float* init_values, int64_t n, uint64_t threshold, int32_t score_mode,
+                          uint64_t step, int64_t* slot_out, int64_t* counts_out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    const std::string f("rec_hash_admit");
+    if (!table) return fail(REC_EINVAL, f + ": table is NULL");
+    if (table->kind != REC_HASH) return fail(REC_EINVAL, f + ": table kind is not REC_HASH");
+    HashArgs t;
+    memset(&t, 0, sizeof(t));
+    rec_status st = prep_table(*table, "rec_hash_admit: table", &t.tab);
+    if (st != REC_OK) return st;
+    if (n < 0) return fail(REC_EINVAL, f + ": n < 0");
+    if (n > ((int64_t)1 << 30)) return fail(REC_EUNSUPPORTED, f + ": n above 2^30");
+    if (score_mode != REC_SCORE_NONE && score_mode != REC_SCORE_STEP && score_mode != REC_SCORE_LFU)
+        return fail(REC_EINVAL, f + ": unknown score_mode");
+    if (score_mode != REC_SCORE_NONE && !table->scores)
+        return fail(REC_EINVAL, f + ": this score_mode needs table scores");
+    if (table->scores && ((uintptr_t)table->scores & 7)) return fail(REC_EINVAL, f + ": scores not 8-byte aligned");
+    if (max_keys < 0 || max_keys > table->rows) return fail(REC_EINVAL, f + ": max_keys outside [0, capacity]");
+    if (threshold < 1) return fail(REC_EINVAL, f + ": threshold must be >= 1");
+    if (!counter_keys || !counter_counts || counter_capacity < 1)
+        return fail(REC_EINVAL, f + ": a counter table (keys, counts, capacity >= 1) is required");
+    if (((uintptr_t)counter_keys & 7) || ((uintptr_t)counter_counts & 7))
+        return fail(REC_EINVAL, f + ": counter arrays not 8-byte aligned");
+    if (n == 0) return ok();
+    if (!keys || !init_values) return fail(REC_EINVAL, f + ": keys and init_values are required");
+    if (!aligned16(init_values)) return fail(REC_EINVAL, f + ": init_values not 16-byte aligned");
+    const AdmitLayout L = admit_layout(n, table->rows, score_mode != REC_SCORE_NONE);
+    if (!workspace || workspace_bytes < L.bytes)
+        return fail(REC_EWORKSPACE, f + ": workspace missing or smaller than rec_hash_admit_workspace_bytes");
+    if ((uintptr_t)workspace & 255u) return fail(REC_EINVAL, f + ": workspace not 256-byte aligned");
+    char* w = (char*)workspace;
+    AdmitArgs a;
+    memset(&a, 0, sizeof(a));
+    a.tab = t.tab;
+    a.keys = const_cast<int64_t*>(table->keys);
+    a.digests = const_cast<uint8_t*>(table->digests);
+    a.scores = const_cast<uint64_t*>(table->scores);
+    a.values = const_cast<float*>(table->values);
+    a.capacity = table->rows;
+    a.max_keys = max_keys;
+    a.ckeys = counter_keys;
+    a.ccounts = counter_counts;
+    a.ccap = counter_capacity;
+    a.in_keys = keys;
+    a.init_values = init_values;
+    a.n = n;
+    a.threshold = threshold;
+    a.step = step;
+    a.mode = score_mode;
+    a.slot_out = slot_out;
+    a.counts_out = counts_out;
+    a.set_key = (int64_t*)(w + L.set_key);
+    a.set_cnt = (uint32_t*)(w + L.set_cnt);
+    a.set_first = (int32_t*)(w + L.set_first);
+    a.nset = L.nset;
+    a.flag = (int32_t*)(w + L.flag);
+    a.rank = (int32_t*)(w + L.rank);
+    a.total = (uint64_t*)(w + L.total);
+    a.cslot = (int64_t*)(w + L.cslot);
+    a.blk_cnt = (int32_t*)(w + L.blk_cnt);
+    a.nbn = L.nbn;
+    a.blk_stored = (int32_t*)(w + L.blk_stored);
+    a.nbs = L.nbs;
+    a.hdr = (int64_t*)(w + L.hdr);
+    uint32_t *k1 = nullptr, *v1 = nullptr, *hist = nullptr, *tot = nullptr;
+    if (score_mode != REC_SCORE_NONE) {
+        a.sort_k = (uint32_t*)(w + L.sort_k0);
+        a.sort_v = (uint32_t*)(w + L.sort_v0);
+        k1 = (uint32_t*)(w + L.sort_k1);
+        v1 = (uint32_t*)(w + L.sort_v1);
+        hist = (uint32_t*)(w + L.hist);
+        tot = (uint32_t*)(w + L.tot);
+    }
+    return hip_status(launch_hash_admit(a, k1, v1, hist, tot, (hipStream_t)stream), "rec_hash_admit");
+}
+
 rec_status rec_dlrm_interact(const float* z, int64_t B, int32_t F, int32_t d, float* out, void* stream) {
     if (B < 0) return fail(REC_EINVAL, "rec_dlrm_interact: B < 0");
     if (F < 1) return fail(REC_EINVAL, "rec_dlrm_interact: F < 1");

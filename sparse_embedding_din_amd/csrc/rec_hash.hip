@@ -33,8 +33,8 @@ __global__ __launch_bounds__(256) void k_hash_insert(const HashInsArgs a) {
     if (i < a.capacity) a.winner[i] = -1;
     if (i >= a.n) return;
     const int64_t key = a.in_keys[i];
-    int64_t slot = -2;                        // the empty marker is never stored
-    if (key != REC_EMPTY_KEY) {
+    int64_t slot = -2;                        // the reserved markers are never stored
+    if (key != REC_EMPTY_KEY && key != REC_TOMBSTONE_KEY) {
         const uint64_t h = mix64((uint64_t)key);
         int64_t at = hash_home(h, a.capacity);
         bool claimed = false;

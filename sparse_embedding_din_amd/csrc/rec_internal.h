@@ -97,6 +97,7 @@ __host__ __device__ inline uint32_t hash_digest(uint64_t h) {
 // the table, where 32 bytes would run past it, the window is read byte by
 // byte with the probe's wrap-around.
 __host__ __device__ inline int64_t hash_probe(const TabDev& t, int64_t key) {
+    if (key == REC_TOMBSTONE_KEY) return -1;          // reserved: marks evicted slots
     const uint64_t h = mix64((uint64_t)key);
     const uint32_t d = hash_digest(h);
     const int64_t n = t.rows;
@@ -346,6 +347,51 @@ constexpr int kDlrmMaxLdsFloats = 36864;
 int dlrm_stride(int d);
 hipError_t launch_dlrm_interact(const float* z, int64_t B, int F, int d, float* out, int num_cus,
                                 hipStream_t s);
+// Frequency admission and eviction (rec_admit.hip).
+struct AdmitArgs {
+    TabDev tab;                   // the table for lookups
+    int64_t* keys;                // the table's arrays, written
+    uint8_t* digests;
+    uint64_t* scores;             // NULL for REC_SCORE_NONE
+    float* values;
+    int64_t capacity, max_keys;
+    int64_t* ckeys;               // the counter table
+    uint64_t* ccounts;
+    int64_t ccap;
+    const int64_t* in_keys;       // the batch
+    const float* init_values;
+    int64_t n;
+    uint64_t threshold;
+    uint64_t step;
+    int32_t mode;
+    int64_t* slot_out;
+    int64_t* counts_out;
+    // workspace (admit_layout)
+    int64_t* set_key;
+    uint32_t* set_cnt;
+    int32_t* set_first;
+    int64_t nset;
+    int32_t* flag;
+    int32_t* rank;
+    uint64_t* total;
+    int64_t* cslot;
+    int32_t* blk_cnt;
+    int64_t nbn;
+    int32_t* blk_stored;
+    int64_t nbs;
+    int64_t* hdr;
+    uint32_t* sort_k;
+    uint32_t* sort_v;
+};
+struct AdmitLayout {
+    int64_t nset, nbn, nbs;
+    size_t set_key, set_cnt, set_first, flag, rank, total, cslot, blk_cnt, blk_stored, hdr;
+    size_t sort_k0, sort_v0, sort_k1, sort_v1, hist, tot, bytes;
+};
+AdmitLayout admit_layout(int64_t n, int64_t capacity, bool evict);
+hipError_t launch_hash_admit(AdmitArgs a, uint32_t* k1, uint32_t* v1, uint32_t* hist, uint32_t* tot,
+                             hipStream_t s);
+
 // The DLRM forward around the interaction (rec_dlrm_fwd.hip).
 constexpr int kDlrmMaxDense = 128;           // dense features
 constexpr int kDlrmMaxZ = 1024;              // (S + 1) * d floats per sample
@@ -401,6 +447,14 @@ struct BwdArgs {
 };
 
 int64_t bwd_sort_tiles(int64_t n);            // tiles of the radix sort (256 counters each)
+// Stable LSD radix sort of n (key, value) pairs over the low key_bits bits
+// of the keys, 8 bits per pass, ping-ponging between the two buffer pairs;
+// hist needs bwd_sort_tiles(n) * 256 words, tot 256.  With gate non-NULL,
+// every pass does nothing when *gate == 0 (read on the device).  Returns the
+// pair of buffers holding the result.
+hipError_t launch_radix_sort(uint32_t* kin, uint32_t* vin, uint32_t* kout, uint32_t* vout, int64_t n,
+                             int key_bits, uint32_t* hist, uint32_t* tot, const int64_t* gate,
+                             hipStream_t s, const uint32_t** keys_sorted, const uint32_t** vals_sorted);
 hipError_t launch_embbag_adagrad(BwdArgs a, const BwdTab* tabs, uint32_t* keys_out, uint32_t* src_out,
                                  uint32_t* sort_hist, uint32_t* sort_tot, int key_bits, hipStream_t s);
 

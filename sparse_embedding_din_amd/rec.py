@@ -27,6 +27,7 @@ REC_TOWER_PACKED_BYTES = 614400
 REC_NOALLOC_SCRATCH_BYTES = 33554432
 REC_DIM = 16
 REC_EMPTY_KEY = -1
+REC_TOMBSTONE_KEY = -2
 REC_MAX_TABLES = 32
 REC_MAX_SEQ_LEN = 1024
 REC_MAX_B = 16777215
@@ -34,6 +35,7 @@ REC_MAX_B = 16777215
 EXPORTS = ["rec_din_pack_mlp", "rec_lengths_to_offsets", "rec_embbag_fwd",
            "rec_kjt_sums_bytes", "rec_kjt_sums", "rec_embbag_fwd_kjt", "rec_hash_lookup",
            "rec_hash_insert_workspace_bytes", "rec_hash_insert", "rec_hash_clear",
+           "rec_hash_admit_workspace_bytes", "rec_hash_admit",
            "rec_dlrm_interact", "rec_dlrm_fwd",
            "rec_din_plan_bytes", "rec_din_plan", "rec_din_attn_workspace_bytes", "rec_din_attn_fwd",
            "rec_din_attn_fwd_plan",
@@ -119,6 +121,10 @@ def lib():
         L.rec_hash_insert.argtypes = [C.POINTER(rec_table), vp, vp, i64, i32, C.c_uint64, vp, vp,
                                       sz, vp]
         L.rec_hash_clear.argtypes = [C.POINTER(rec_table), vp]
+        L.rec_hash_admit_workspace_bytes.argtypes = [i64, i64, i32]
+        L.rec_hash_admit_workspace_bytes.restype = sz
+        L.rec_hash_admit.argtypes = [C.POINTER(rec_table), i64, vp, vp, i64, vp, vp, i64, C.c_uint64,
+                                     i32, C.c_uint64, vp, vp, vp, sz, vp]
         L.rec_dlrm_interact.argtypes = [vp, i64, i32, i32, vp, vp]
         L.rec_dlrm_fwd.argtypes = [C.POINTER(rec_dlrm_mlp), C.POINTER(rec_table),
                                    C.POINTER(C.c_int32), i64, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -152,7 +158,8 @@ def lib():
                                          vp, C.POINTER(C.c_int32), vp, i64, i64, vp, C.c_float,
                                          C.c_float, vp, sz, vp]
         for f in ("rec_lengths_to_offsets", "rec_embbag_fwd", "rec_kjt_sums", "rec_embbag_fwd_kjt",
-                  "rec_hash_lookup", "rec_hash_insert", "rec_hash_clear", "rec_dlrm_interact",
+                  "rec_hash_lookup", "rec_hash_insert", "rec_hash_clear", "rec_hash_admit",
+                  "rec_dlrm_interact",
                   "rec_dlrm_fwd",
                   "rec_din_plan",
                   "rec_din_attn_fwd", "rec_din_attn_fwd_plan", "rec_din_pack_mlp", "rec_sparse_din_fwd",
@@ -307,6 +314,21 @@ def rec_dlrm_fwd(mlp: rec_dlrm_mlp, tables: Sequence[rec_table], modes: Sequence
                               _p(values), _p(lengths), _p(offsets), _p(z), _p(inter), _p(logit),
                               _p(prob), _stream(stream)),
            "rec_dlrm_fwd")
+
+
+def rec_hash_admit_workspace_bytes(n: int, capacity: int, score_mode: int) -> int:
+    return int(lib().rec_hash_admit_workspace_bytes(n, capacity, score_mode))
+
+
+def rec_hash_admit(table_: rec_table, max_keys: int, counter_keys, counter_counts,
+                   counter_capacity: int, keys, init_values, n: int, threshold: int,
+                   score_mode: int, step: int = 0, slot_out=None, counts_out=None, workspace=None,
+                   workspace_bytes: int = 0, stream=None):
+    _check(lib().rec_hash_admit(C.byref(table_) if table_ is not None else None, max_keys,
+                                _p(counter_keys), _p(counter_counts), counter_capacity, _p(keys),
+                                _p(init_values), n, threshold, score_mode, step, _p(slot_out),
+                                _p(counts_out), _p(workspace), workspace_bytes, _stream(stream)),
+           "rec_hash_admit")
 
 
 def rec_hash_clear(table_: rec_table, stream=None):

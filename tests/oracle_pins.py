@@ -891,8 +891,8 @@ def pin_hash_admit(orc):
     the insert of the distinct ids; ids are admitted exactly at the call
     where their running count reaches the threshold (LFU starting from that
     count); a full table evicts the oldest (STEP) or least used (LFU) entries
-    stored before the call, lower slot first on equal scores, scores
-    saturating at 2^32 - 1; a used id is not the oldest any more; a new id
+    stored before the call, the smaller id first on equal scores, scores
+    saturating at 2^32 - 2; a used id is not the oldest any more; a new id
     takes the first free slot (empty or tombstone) from its home; NO_EVICTION
     admits nothing into a full table and keeps the counts; reserved ids are
     neither stored nor counted; a full counter table counts no new id."""
@@ -971,8 +971,9 @@ def pin_hash_admit(orc):
         while q != s_:
             assert t["keys"][q] not in (-1, -2)                # passed no free slot
             q = (q + 1) % cap
-    # (4) LFU eviction: counts 5, 1, 3, 1 -> the two least used go, equal
-    # counts lower slot first; scores above 2^32 - 1 compare as equal
+    # (4) LFU eviction: counts 5, 1, 3, 1 -> the two least used go; scores
+    # at or above 2^32 - 2 compare as equal, and equal scores go smaller id
+    # first
     t, c = orc.empty_hash_table(16), orc.empty_counter_table(64)
     ks = _distinct_keys(rng, 4)
     for key, n_ in zip(ks, (5, 1, 3, 1)):
@@ -991,15 +992,15 @@ def pin_hash_admit(orc):
     gone = [i for i in range(3) if orc.hash_find_slow(t, int(ks[i])) < 0]
     assert gone == [2]                                             # 7 is the least
     s3 = orc.hash_find_slow(t, int(ks[3]))
-    left = {sl3[0]: 0, sl3[1]: 1, s3: 3}                          # slot -> id index
+    left = {int(ks[0]): sl3[0], int(ks[1]): sl3[1], int(ks[3]): s3}   # id -> slot
     order = sorted(left)
-    # scores all at or above 2^32 - 1: equal after saturation, so the lowest
-    # slot goes even though its raw score is the largest
-    for sl_, sc in zip(order, (2**41, 2**34, 2**32 + 5)):
-        t["scores"][sl_] = sc
+    # scores all at or above 2^32 - 2: equal after saturation, so the
+    # smallest id goes even though its raw score is the largest
+    for k_, sc in zip(order, (2**41, 2**34, 2**32 - 2)):
+        t["scores"][left[k_]] = sc
     orc.hash_admit(t, c, fresh[:1], vals(1), 1, LFU, 0, max_keys=3)
-    gone = [i for i in (0, 1, 3) if orc.hash_find_slow(t, int(ks[i])) < 0]
-    assert gone == [left[order[0]]]
+    gone = [k_ for k_ in left if orc.hash_find_slow(t, k_) < 0]
+    assert gone == [order[0]]
     # (5) NO_EVICTION keeps a full table and the counts of those left out
     t, c = orc.empty_hash_table(32), orc.empty_counter_table(64)
     ks = _distinct_keys(rng, 6)

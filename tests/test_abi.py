@@ -670,3 +670,40 @@ def test_dlrm_fwd_errors(lib):
         assert call(**{k: None})[0] == R.REC_EINVAL, k
     assert call(z=FAKE_ODD)[0] == R.REC_EINVAL
     assert call(B=0, dense=None, values=None, lengths=None, offsets=None, z=None, logit=None)[0] == R.REC_OK
+
+
+def test_hash_admit_errors(lib):
+    """rec_hash_admit: argument errors are refused on the host."""
+    def tab(**kw):
+        t = _table(kind=R.REC_HASH, rows=1000, keys=FAKE, digests=FAKE)
+        t.scores = FAKE
+        for k, v in kw.items():
+            setattr(t, k, v)
+        return t
+    wb = R.rec_hash_admit_workspace_bytes(10, 1000, R.REC_SCORE_LFU)
+    assert wb > 0 and R.rec_hash_admit_workspace_bytes(10, 1000, R.REC_SCORE_NONE) < wb
+    assert R.rec_hash_admit_workspace_bytes(-1, 1000, 1) == 0
+    assert R.rec_hash_admit_workspace_bytes(10, 0, 1) == 0
+
+    def call(t=None, mk=1000, ck=FAKE, cc=FAKE, ccap=64, keys=FAKE, iv=FAKE, n=10, th=3,
+             mode=R.REC_SCORE_LFU, ws=FAKE, wsb=wb):
+        t = tab() if t is None else t
+        return _status(lib.rec_hash_admit, C.byref(t) if t != "null" else None, mk, ck, cc, ccap, keys,
+                       iv, n, th, mode, 7, None, None, ws, wsb, None)
+    assert call(t="null")[0] == R.REC_EINVAL
+    assert call(t=_table())[0] == R.REC_EINVAL                       # direct table
+    assert call(t=tab(scores=None))[0] == R.REC_EINVAL                # LFU needs scores
+    assert call(t=tab(scores=None), mode=R.REC_SCORE_NONE,
+                wsb=R.rec_hash_admit_workspace_bytes(10, 1000, 0), ws=None)[0] == R.REC_EWORKSPACE
+    assert call(mode=5)[0] == R.REC_EINVAL
+    assert call(mk=-1)[0] == R.REC_EINVAL and call(mk=1001)[0] == R.REC_EINVAL
+    assert call(th=0)[0] == R.REC_EINVAL
+    assert call(ck=None)[0] == R.REC_EINVAL and call(cc=None)[0] == R.REC_EINVAL
+    assert call(ccap=0)[0] == R.REC_EINVAL and call(ck=FAKE + 4)[0] == R.REC_EINVAL
+    assert call(n=-1)[0] == R.REC_EINVAL
+    assert call(n=(1 << 30) + 1)[0] == R.REC_EUNSUPPORTED
+    assert call(keys=None)[0] == R.REC_EINVAL and call(iv=None)[0] == R.REC_EINVAL
+    assert call(iv=FAKE_ODD)[0] == R.REC_EINVAL
+    assert call(ws=None)[0] == R.REC_EWORKSPACE and call(wsb=wb - 1)[0] == R.REC_EWORKSPACE
+    assert call(ws=FAKE + 16)[0] == R.REC_EINVAL
+    assert call(n=0, keys=None, iv=None, ws=None)[0] == R.REC_OK

@@ -140,9 +140,9 @@ MUTANTS = [
     ("admission counts an id once per batch", "dc[j] += 1;", "dc[j] = 1;"),
     ("eviction takes the largest score", "if (x->score != y->score) return x->score < y->score ? -1 : 1;",
      "if (x->score != y->score) return x->score > y->score ? -1 : 1;"),
-    ("eviction ties take the higher slot", "return (x->slot > y->slot) - (x->slot < y->slot);",
-     "return (x->slot < y->slot) - (x->slot > y->slot);"),
-    ("eviction scores not saturated", "v[nv].score = tscores[s] < 0xffffffffull ? tscores[s] : 0xffffffffull;",
+    ("eviction ties take the larger id", "return (x->key > y->key) - (x->key < y->key);",
+     "return (x->key < y->key) - (x->key > y->key);"),
+    ("eviction scores not saturated", "v[nv].score = tscores[s] < 0xfffffffeull ? tscores[s] : 0xfffffffeull;",
      "v[nv].score = tscores[s];"),
     ("a used id keeps its STEP score", "if (mode == ORC_SCORE_STEP) tscores[s] = step;\n            if (mode == ORC_SCORE_LFU) tscores[s] += dc[j];",
      "if (mode == ORC_SCORE_LFU) tscores[s] += dc[j];"),
