@@ -661,6 +661,65 @@ def main():
         print(f"[bench] hash rebuild: {nkeys} keys in {total_us:.1f} us ({ins_us:.2f} us per insert launch)",
               file=sys.stderr, flush=True)
 
+    admit = None
+    if not a.no_hash_rebuild:
+        # One admission step on the hash workload's first table ("集成
+        # DynamicEmb" §4.1, §4.2): capacity 300,000 holding 210,000 ids, a batch
+        # of 20,000 stored ids and 40,000 new ids seen twice, threshold 2, STEP
+        # scores, at most 210,000 ids -- so 40,000 admissions evict as many of
+        # the oldest entries.  Each timed call starts from a fresh copy.
+        hcfg = synth.WORKLOADS[5]
+        hm5 = model if cfg.hash_keys else synth.make_model(hcfg)
+        t0_ = hm5.tables[hcfg.hash_keys[0]]
+        rng_a = np.random.default_rng(31)
+        st_ = t0_["keys"] != R.REC_EMPTY_KEY
+        olds = t0_["keys"][st_]
+        fresh = np.unique(rng_a.integers(-2**62, 2**62, size=45000, dtype=np.int64))
+        fresh = fresh[~np.isin(fresh, olds)][:40000]
+        akeys = np.concatenate([rng_a.choice(olds, 20000, replace=False), fresh, fresh])
+        akeys = akeys[rng_a.permutation(akeys.size)]
+        ak = torch.from_numpy(akeys).to(dev)
+        av = torch.from_numpy((rng_a.standard_normal((akeys.size, 16)) * 0.05).astype(np.float32)).to(dev)
+        base_sc = np.zeros(int(t0_["rows"]), np.uint64)
+        base_sc[st_] = np.arange(int(st_.sum()), dtype=np.uint64) % 1000
+        src_t = PL.DeviceTables([dict(t0_, scores=base_sc)], dev)
+        work_t = PL.DeviceTables([dict(t0_, scores=base_sc)], dev)
+        cap_ = int(t0_["rows"])
+        ck_ = torch.empty(1 << 18, dtype=torch.int64, device=dev)
+        cc_ = torch.empty(1 << 18, dtype=torch.int64, device=dev)
+        a_wsb = R.rec_hash_admit_workspace_bytes(akeys.size, cap_, R.REC_SCORE_STEP)
+        a_ws = torch.empty(a_wsb, dtype=torch.uint8, device=dev)
+        a_cnt = torch.empty(3, dtype=torch.int64, device=dev)
+
+        def reset_tables():
+            for x, y in zip(work_t.tensors[0], src_t.tensors[0]):
+                x.copy_(y)
+            ck_.fill_(-1)
+            cc_.zero_()
+
+        def admit_call():
+            R.rec_hash_admit(work_t.desc[0], 210000, ck_, cc_, 1 << 18, ak, av, akeys.size, 2,
+                             R.REC_SCORE_STEP, 5000, None, a_cnt, a_ws, a_wsb, stream=stream)
+        with torch.cuda.stream(stream):
+            reps_ad = 10
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps_ad)]
+            for r in range(reps_ad + 2):
+                reset_tables()
+                if r >= 2:
+                    evs[r - 2][0].record(stream)
+                admit_call()
+                if r >= 2:
+                    evs[r - 2][1].record(stream)
+            torch.cuda.synchronize()
+        d_ad = np.array([x.elapsed_time(y) * 1e3 for x, y in evs])
+        admit = {"entry": "rec_hash_admit (STEP, threshold 2, max_keys 210,000, full table)",
+                 "ids": int(akeys.size), "admitted_evicted_left": [int(x) for x in a_cnt.cpu().tolist()],
+                 "call_us": float(d_ad.mean()), "ids_per_s": round(akeys.size / (d_ad.mean() * 1e-6), 1)}
+        print(f"[bench] hash admission: {d_ad.mean():.1f} us per call ({akeys.size} ids, "
+              f"{admit['admitted_evicted_left']})", file=sys.stderr, flush=True)
+        del src_t, work_t, a_ws
+
     adagrad = None
     if not a.no_adagrad:
         # The sparse half of a training step, beside the forward: gradients of
@@ -934,6 +993,7 @@ def main():
                         "plan_bytes": plan_bytes, "din_bytes": din_bytes, "din_flops": din_flops},
         "towers": towers,
         "hash_rebuild": rebuild,
+        "hash_admit": admit,
         "adagrad": adagrad,
         "din_bwd": din_bwd,
         "dlrm_interaction": interaction,
