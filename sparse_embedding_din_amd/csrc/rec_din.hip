@@ -549,6 +549,12 @@ __global__ __launch_bounds__(256) void k_din_pack(const uint16_t* __restrict__ w
     }
 }
 
+// Positions per round of a wave: two 16-position tiles when a wave has its
+// SIMD alone (each weight fragment read from LDS feeds two products), one
+// when two waves share a SIMD (the other wave's products hide each read's
+// latency, and the wave fits in half the registers).
+constexpr int kRoundTiles = kDinWaves >= 8 ? 1 : 2;
+
 template <int DT>
 __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
     constexpr bool kPacked = DT == REC_BF16_PACKED;
@@ -620,14 +626,14 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
     int64_t p0;
     int cnt;
     wave_range(gA, gE, gi < ng, p0, cnt);
-    Sub S[2];
+    Sub S[kRoundTiles];
     bool ready = cnt > 0;           // S holds the first round of the wave's range
     if (ready) {
-        Ent E[2];
+        Ent E[kRoundTiles];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) load_entries(a, src, p0, cnt, 16 * s + n, E[s]);
+        for (int s = 0; s < kRoundTiles; ++s) load_entries(a, src, p0, cnt, 16 * s + n, E[s]);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) load_data(a, src, E[s], p0, cnt, 16 * s + n, lane, S[s]);
+        for (int s = 0; s < kRoundTiles; ++s) load_data(a, src, E[s], p0, cnt, 16 * s + n, lane, S[s]);
     }
 
     if (kBF && !kPacked) {
@@ -691,51 +697,58 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
         for (int f = 0; f < 12; ++f) acc_open[f] = 0.f;
         if (lane == 0) pc[kPartialFloats + 2] = __int_as_float(-1);     // no tail piece yet
         if (cnt > 0 && !ready) {
-            Ent E[2];
+            Ent E[kRoundTiles];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) load_entries(a, src, p0, cnt, 16 * s + n, E[s]);
+            for (int s = 0; s < kRoundTiles; ++s) load_entries(a, src, p0, cnt, 16 * s + n, E[s]);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) load_data(a, src, E[s], p0, cnt, 16 * s + n, lane, S[s]);
+            for (int s = 0; s < kRoundTiles; ++s) load_data(a, src, E[s], p0, cnt, 16 * s + n, lane, S[s]);
             // Wait here: the compiler's wait counting merges this path with
             // the round loop's back edge, and loads still pending here would
             // make it wait for every load in flight (the next round's
             // prefetches included) at the first use of these registers.
             __builtin_amdgcn_s_waitcnt(0);
         }
-        for (int sb = 0; sb < cnt; sb += 32) {
+        for (int sb = 0; sb < cnt; sb += 16 * kRoundTiles) {
             int64_t q0 = p0;
-            int qc = cnt, qs = sb + 32;
+            int qc = cnt, qs = sb + 16 * kRoundTiles;
             if (qs >= cnt) {
                 q0 = p0n;
                 qc = cntn;
                 qs = 0;
             }
             const bool more = qs < qc;
-            Ent E[2];
+            Ent E[kRoundTiles];
             if (more) {
 #pragma unroll
-                for (int s = 0; s < 2; ++s) load_entries(a, src, q0, qc, qs + 16 * s + n, E[s]);
+                for (int s = 0; s < kRoundTiles; ++s) load_entries(a, src, q0, qc, qs + 16 * s + n, E[s]);
             }
-            float e[2];
-            const bool two = cnt - sb > 16;
-            mask_sub(S[0]);
-            mask_sub(S[1]);
-            if (kBF) {
-                if (two) mlp_bf16<2>(S, s_w1, s_w2, s_b1, s_b2, s_w3, a.b3, lane, e);
-                else mlp_bf16<1>(S, s_w1, s_w2, s_b1, s_b2, s_w3, a.b3, lane, e);
+            float e[kRoundTiles];
+            const bool two = kRoundTiles == 2 && cnt - sb > 16;
+#pragma unroll
+            for (int s = 0; s < kRoundTiles; ++s) mask_sub(S[s]);
+            if constexpr (kRoundTiles == 2) {
+                if (kBF) {
+                    if (two) mlp_bf16<2>(S, s_w1, s_w2, s_b1, s_b2, s_w3, a.b3, lane, e);
+                    else mlp_bf16<1>(S, s_w1, s_w2, s_b1, s_b2, s_w3, a.b3, lane, e);
+                } else {
+                    if (two) mlp_f32<2>(S, (const float*)a.w1, (const float*)a.w2, s_b1, s_b2, s_w3, a.b3, lane, e);
+                    else mlp_f32<1>(S, (const float*)a.w1, (const float*)a.w2, s_b1, s_b2, s_w3, a.b3, lane, e);
+                }
             } else {
-                if (two) mlp_f32<2>(S, (const float*)a.w1, (const float*)a.w2, s_b1, s_b2, s_w3, a.b3, lane, e);
+                if (kBF) mlp_bf16<1>(S, s_w1, s_w2, s_b1, s_b2, s_w3, a.b3, lane, e);
                 else mlp_f32<1>(S, (const float*)a.w1, (const float*)a.w2, s_b1, s_b2, s_w3, a.b3, lane, e);
             }
-            Sub Sn[2];
+            Sub Sn[kRoundTiles];
             if (more) {
 #pragma unroll
-                for (int s = 0; s < 2; ++s) load_data(a, src, E[s], q0, qc, qs + 16 * s + n, lane, Sn[s]);
+                for (int s = 0; s < kRoundTiles; ++s) load_data(a, src, E[s], q0, qc, qs + 16 * s + n, lane, Sn[s]);
             }
             softmax_tile(a, S[0], e[0], lane, gA, gT, pc, m_open, l_open, acc_open);
-            if (two) softmax_tile(a, S[1], e[1], lane, gA, gT, pc, m_open, l_open, acc_open);
-            S[0] = Sn[0];
-            S[1] = Sn[1];
+            if constexpr (kRoundTiles == 2) {
+                if (two) softmax_tile(a, S[1], e[1], lane, gA, gT, pc, m_open, l_open, acc_open);
+            }
+#pragma unroll
+            for (int s = 0; s < kRoundTiles; ++s) S[s] = Sn[s];
         }
         ready = cnt > 0 && cntn > 0;
         __syncthreads();

@@ -228,7 +228,7 @@ constexpr int kPlanSumWords = 2 + 2 * (kScanChunk / kPlanChunk);   // 130
 constexpr int kMinRange = 16;
 constexpr int kMaxRange = 1 << 20;
 constexpr int kPartialFloats = 52;       // a cut sample's piece: max, sum, 2 words, 48 sums
-constexpr int kDinWaves = 4;             // waves per attention workgroup (one per SIMD)
+constexpr int kDinWaves = 8;             // waves per attention workgroup (two per SIMD)
 constexpr int kMaxDinGroups = 4096;      // attention workgroups the plan provides for
 
 struct PlanLayout {

@@ -104,10 +104,11 @@ def test_din_plan(models, B, max_len, C):
     mask = np.ones(max(stride, 1), bool)
     mask[gidx] = False
     assert np.all(rg[:, mask] == -9)
-    # attention groups: nominal spans of four requested ranges, else P over
-    # the workgroups (one per CU), each start moved forward to a sample start
+    # attention groups: nominal spans of one requested range per wave of an
+    # attention workgroup (eight waves), else P over the workgroups (one per
+    # CU), each start moved forward to a sample start
     groups = torch.cuda.get_device_properties(0).multi_processor_count
-    span = 4 * C if C > 0 else max(1, -(-P // groups))
+    span = 8 * C if C > 0 else max(1, -(-P // groups))
     ng = -(-P // span)
     assert hdr[3] == ng
     off_group = a16(a16(off_prows + 12 * pmax) + 4 * B)
