@@ -513,16 +513,20 @@ def main():
     cold_us, _ = timed(lambda r: fwds[r % nb].run_whole(dbs[r % nb]), step_kinds, cold_reps, flush)
     # the step's wall time, warm and cold, one graph replay per step (a graph
     # per resident batch), events around each replay
-    step_graphs = []
-    for f, db in zip(fwds, dbs):
-        g1 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g1, stream=stream):
-            step(f, db)
-        step_graphs.append(g1)
-    torch.cuda.synchronize()
-    _, warm_step = timed(lambda r: step_graphs[r % nb].replay(), {}, reps)
-    _, cold_step = timed(lambda r: step_graphs[r % nb].replay(), {}, cold_reps, flush)
-    del step_graphs
+    if graph is not None:
+        step_graphs = []
+        for f, db in zip(fwds, dbs):
+            g1 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g1, stream=stream):
+                step(f, db)
+            step_graphs.append(g1)
+        torch.cuda.synchronize()
+        _, warm_step = timed(lambda r: step_graphs[r % nb].replay(), {}, reps)
+        _, cold_step = timed(lambda r: step_graphs[r % nb].replay(), {}, cold_reps, flush)
+        del step_graphs
+    else:
+        _, warm_step = timed(lambda r: step(fwds[r % nb], dbs[r % nb]), {}, reps)
+        _, cold_step = timed(lambda r: step(fwds[r % nb], dbs[r % nb]), {}, cold_reps, flush)
     cold_calls, _ = timed(calls_rep, {"embbag": R.REC_TIME_GATHER, "din_plan": R.REC_TIME_DIN_ATTN},
                           cold_reps, flush)
     del flush_buf
@@ -530,6 +534,7 @@ def main():
           + f"; calls: embbag={call_us['embbag']['mean']:.2f} din={call_us['din_plan']['mean']:.2f}"
           + f"; cold: " + ", ".join(f"{k}={v['mean']:.2f}" for k, v in cold_us.items())
           + f", step {cold_step['mean']:.2f} (warm {warm_step['mean']:.2f})", file=sys.stderr, flush=True)
+    step_timing = "one graph replay per step" if graph is not None else "one step enqueued per step"
 
     # algorithmic work of the average batch
     nnz = float(np.mean([b.values.size for b in batches]))
@@ -986,7 +991,7 @@ def main():
         "batches_in_flight": list(in_flight.values()),
         "kernels_us": kern_us,
         "calls_us": call_us,
-        "warm": {"step_us": warm_step, **warm_rates},
+        "warm": {"step_us": warm_step, "step_timing": step_timing, **warm_rates},
         "cold": {"step_us": cold_step, "kernels_us": cold_us, "calls_us": cold_calls, **cold_rates,
                  "flush": "1 GiB read before each step (L2s and the 256 MB MALL evicted)"},
         "algorithmic": {"gather_bytes": emb_bytes + plan_bytes, "embbag_bytes": emb_bytes,
