@@ -96,6 +96,9 @@ def parse():
     p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="write profiles/traffic_*.json from two rocprofv3 --pmc counter CSVs "
                         "(FETCH_SIZE, WRITE_SIZE) of a --calibrate-copy run, then exit")
+    p.add_argument("--profile-summary", metavar="DIR",
+                   help="write profiles/step_kernels_<workload>.md (and traffic_*.json) from the "
+                        "outputs of the rocprofv3 runs listed in it, found under DIR, then exit")
     return p.parse_args()
 
 
@@ -129,6 +132,8 @@ _BWD = ["rec_bwd.hip"] + _COMMON
 KERNEL_SOURCES = {"k_din_attn": _FWD, "k_embbag_fwd": _FWD, "k_fwd_gather": _FWD, "k_fwd_sums": _FWD,
                   "k_towers_bf16": ["rec_tower.hip", "rec_mfma.h"] + _COMMON,
                   "k_hash_insert": ["rec_hash.hip"] + _COMMON,
+                  "k_hash_insert_winner": ["rec_hash.hip"] + _COMMON,
+                  "k_hash_insert_values": ["rec_hash.hip"] + _COMMON,
                   "k_bwd_keys": _BWD, "k_sort_hist": _BWD, "k_sort_scan": _BWD, "k_sort_scatter": _BWD,
                   "k_bwd_chunks": _BWD, "k_bwd_cross": _BWD,
                   "k_dlrm_interact": ["rec_dlrm.hip", "rec_mfma.h"] + _COMMON,
@@ -143,14 +148,15 @@ CAL_ROWS = 1 << 20              # random 64-byte rows read (and written) by the 
 CAL_TABLE_ROWS = 3 << 20        # rows of its table (192 MiB, like the embedding tables)
 KERNELS = {"k_din_attn": "k_din_attn",
            "k_embbag_fwd": "k_embbag_fwd<", "k_fwd_gather": "k_fwd_gather", "k_fwd_sums": "k_fwd_sums",
-           "k_towers_bf16": "k_towers_bf16", "k_hash_insert": "k_hash_insert",
+           "k_towers_bf16": "k_towers_bf16", "k_hash_insert": "k_hash_insert(",
+           "k_hash_insert_winner": "k_hash_insert_winner", "k_hash_insert_values": "k_hash_insert_values",
            "k_bwd_keys": "k_bwd_keys", "k_sort_hist": "k_sort_hist", "k_sort_scan": "k_sort_scan",
            "k_sort_scatter": "k_sort_scatter", "k_bwd_chunks": "k_bwd_chunks",
            "k_bwd_cross": "k_bwd_cross", "k_dlrm_interact": "k_dlrm_interact",
            "k_dinb_prep": "k_dinb_prep",
            "k_dinb_map": "k_dinb_map", "k_dinb_fwd": "k_dinb_fwd", "k_dinb_soft": "k_dinb_soft",
            "k_dinb_bwdt": "k_dinb_bwdt", "k_dinb_gq": "k_dinb_gq", "k_dinb_wgrad": "k_dinb_wgrad",
-           "k_dinb_reduce": "k_dinb_reduce", "copy": "MulFunctor", "gather_cal": "ndexSelect",
+           "k_dinb_reduce": "k_dinb_reduce", "copy": "MulFunctor", "gather_cal": "vectorized_gather_kernel",
            "k_dlrm_embed": "k_dlrm_embed", "k_dlrm_top": "k_dlrm_top"}
 # kernels whose reads are mostly random 64-byte rows: their FETCH_SIZE is scaled
 # by the calibration gather's reading (random 64-byte rows), the others' by
@@ -221,6 +227,139 @@ def traffic_from(fetch_csv: str, write_csv: str, config: str):
         print(f"{k}: {b / 1e6:.3f} MB per launch ({d['scaled_by']}; raw {raw / 1e6:.3f} MB: fetch "
               f"{fetch[k]:.0f} KiB, write {write[k]:.0f} KiB)")
     print(f"copy scale: fetch {f_cal:.3f}, write {w_cal:.3f}; gather scale: fetch {g_cal}, write {gw_cal}")
+
+
+# The rocprofv3 runs whose summaries profiles/ holds, per workload; {c} is
+# the --config number.  Each runs bench.py as it is committed.
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_cfg{c} -o run --output-format csv "
+             "-- python3 bench.py --config {c} --steps 40 --warmup 8 --no-cpu --kernel-reps 40",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_FETCH_SIZE_cfg{c} -o run --output-format csv "
+             "-- python3 bench.py --config {c} --steps 8 --warmup 4 --no-cpu --no-graph --kernel-reps 8 "
+             "--calibrate-copy",
+    "write": "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_WRITE_SIZE_cfg{c} -o run --output-format csv "
+             "-- python3 bench.py --config {c} --steps 8 --warmup 4 --no-cpu --no-graph --kernel-reps 8 "
+             "--calibrate-copy",
+    "mfma": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES "
+            "GRBM_GUI_ACTIVE -d gpurun_out/pmc_MFMA_cfg{c} -o run --output-format csv "
+            "-- python3 bench.py --config {c} --steps 8 --warmup 4 --no-cpu --no-graph --kernel-reps 8",
+}
+CLOCK_HZ = 2.4e9                # MI355X peak engine clock
+SIMDS = 1024                    # 256 CUs x 4 SIMDs
+
+
+def _kernel_key(name: str):
+    for key, pat in KERNELS.items():
+        if pat in name:
+            return key
+    return None
+
+
+def _stats_line(v):
+    import statistics
+    return (len(v), statistics.fmean(v), statistics.median(v), min(v), max(v))
+
+
+def profile_summary(root: str, c: int, workload: str) -> str:
+    """profiles/step_kernels_<workload>.md from the outputs of PROFILE_COMMANDS
+    under `root` (the runs' -d folders): per-kernel durations of the whole
+    run (rocprofv3 --stats), the bench's warm kernel leg picked out of the
+    trace by its two spin-kernel markers, HBM traffic per launch (FETCH_SIZE
+    and WRITE_SIZE, calibrated) and the MFMA counters of the bf16 kernels."""
+    import csv
+    d = {k: os.path.join(root, f"{n}_cfg{c}") for k, n in
+         (("trace", "prof"), ("fetch", "pmc_FETCH_SIZE"), ("write", "pmc_WRITE_SIZE"), ("mfma", "pmc_MFMA"))}
+    cmd = {k: v.format(c=c) for k, v in PROFILE_COMMANDS.items()}
+    out = [f"# Kernel durations, HBM traffic and MFMA counters: {workload}", "",
+           "Made by `python3 bench.py --config %d --profile-summary gpurun_out` from the outputs of" % c,
+           "these runs (each on one MI355X, bench.py as committed):", "", "```"]
+    out += [cmd[k] for k in ("trace", "fetch", "write", "mfma")] + ["```", ""]
+
+    rows = list(csv.DictReader(open(os.path.join(d["trace"], "run_kernel_trace.csv"))))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    spins = [i for i, r in enumerate(rows) if "spin_kernel" in r["Kernel_Name"]]
+    leg = {}
+    if len(spins) >= 2:
+        for r in rows[spins[0] + 1: spins[1]]:
+            k = _kernel_key(r["Kernel_Name"])
+            if k:
+                leg.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out += ["## Warm kernel leg", "",
+            "The launches between the run's first two spin kernels: the leg whose attention launches",
+            "bench.py times with HIP events bound to the dispatch (`roofline.avg_launch_us`), back to",
+            "back over the resident batches (us):", "",
+            "| kernel | launches | mean | median | min | max |", "|---|---|---|---|---|---|"]
+    for k, v in leg.items():
+        n, m, md, lo, hi = _stats_line(v)
+        out.append(f"| {k} | {n} | {m:.2f} | {md:.2f} | {lo:.2f} | {hi:.2f} |")
+    out += ["", "## Every launch of the run (rocprofv3 --stats)", "",
+            "All launches of each kernel: the graph-replayed steps, the two- and four-stream legs",
+            "(where launches of different batches overlap and each runs longer), the warm and cold",
+            "(1 GiB read before each step) kernel legs and the side workloads (us):", "",
+            "| kernel | calls | avg | min | max |", "|---|---|---|---|---|"]
+    for r in csv.DictReader(open(os.path.join(d["trace"], "run_kernel_stats.csv"))):
+        n = r["Name"]
+        if "rec::" not in n:
+            continue
+        short = re.sub(r"\(.*$", "", n.replace("rec::(anonymous namespace)::", "")).replace("void ", "")
+        out.append(f"| {short} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+
+    fetch_csv = os.path.join(d["fetch"], "run_counter_collection.csv")
+    write_csv = os.path.join(d["write"], "run_counter_collection.csv")
+    out += ["", "## HBM traffic per launch", "",
+            "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged over the run's dispatches), each",
+            "divided by what the same counter reads for a calibration kernel of known traffic: a",
+            f"streaming copy ({CAL_BYTES >> 20} MiB read and written) for most kernels, a gather of",
+            f"{CAL_ROWS} random 64-byte rows of a {CAL_TABLE_ROWS * 64 >> 20} MiB table for the kernels whose reads",
+            "are mostly random embedding rows.  The figures are written to `traffic_<kernel>_" + workload + ".json`",
+            "beside this file with the hash of the kernel's sources; bench.py reports them only while",
+            "the sources are unchanged.", ""]
+    lines = []
+    import contextlib
+    import io
+    buf = io.StringIO()
+    with contextlib.redirect_stdout(buf):
+        traffic_from(fetch_csv, write_csv, workload)
+    lines = buf.getvalue().splitlines()
+    out += ["```"] + lines + ["```"]
+
+    acc = {}
+    dur = {}
+    for r in csv.DictReader(open(os.path.join(d["mfma"], "run_counter_collection.csv"))):
+        k = _kernel_key(r["Kernel_Name"])
+        if k not in ("k_din_attn", "k_towers_bf16"):
+            continue
+        acc.setdefault(k, {}).setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
+        dur.setdefault(k, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    out += ["", "## MFMA counters", "",
+            "Means per dispatch.  One v_mfma_f32_16x16x32_bf16 counts 32 in SQ_INSTS_VALU_MFMA_MOPS_BF16",
+            "(units of 512 flops) and 16 busy cycles in SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs), so",
+            "the busy fraction is busy / (1024 SIMDs x 2.4 GHz x duration); `warm` uses the warm leg's",
+            "mean duration above, `counted` the counter run's own (counter collection serialises",
+            "dispatches and lengthens them).  GRBM_GUI_ACTIVE is recorded as rocprofv3 reports it.", "",
+            "| kernel | dispatches | executed GFLOP | busy cycles | SQ_BUSY_CYCLES | GRBM_GUI_ACTIVE | counted us | busy frac (counted) | busy frac (warm) |",
+            "|---|---|---|---|---|---|---|---|---|"]
+    for k, cn in acc.items():
+        def mean(name):
+            v = list(cn.get(name, {}).values())
+            return sum(v) / len(v) if v else float("nan")
+        busy = mean("SQ_VALU_MFMA_BUSY_CYCLES")
+        mops = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        du = sum(dur[k].values()) / len(dur[k])
+        warm = statistics_mean(leg.get(k))
+        frac_c = busy / (SIMDS * CLOCK_HZ * du * 1e-6)
+        frac_w = busy / (SIMDS * CLOCK_HZ * warm * 1e-6) if warm else float("nan")
+        out.append(f"| {k} | {len(dur[k])} | {mops * 512 / 1e9:.3f} | {busy:.0f} | {mean('SQ_BUSY_CYCLES'):.0f} | "
+                   f"{mean('GRBM_GUI_ACTIVE'):.0f} | {du:.2f} | {frac_c:.4f} | {frac_w:.4f} |")
+    text = "\n".join(out) + "\n"
+    with open(os.path.join(ROOT, "profiles", f"step_kernels_{workload}.md"), "w") as f:
+        f.write(text)
+    return text
+
+
+def statistics_mean(v):
+    return sum(v) / len(v) if v else None
 
 
 _CPU = {}
@@ -301,6 +440,10 @@ def cpu_leg(cfg, model, batch, seconds: float, max_workers: int = 16):
 
 def main():
     a = parse()
+    if a.profile_summary:
+        import synth
+        print(profile_summary(a.profile_summary, a.config, synth.WORKLOADS[a.config].name))
+        return
     if a.traffic_from:
         import synth
         traffic_from(a.traffic_from[0], a.traffic_from[1], synth.WORKLOADS[a.config].name)
@@ -491,7 +634,14 @@ def main():
 
     reps = a.kernel_reps
     step_kinds = {"sums": R.REC_TIME_SUMS, "gather": R.REC_TIME_GATHER, "din": R.REC_TIME_DIN_ATTN}
+    # Two short spin kernels bracket this leg, so that a kernel trace of the
+    # same command can pick out its launches (the first two spin kernels of
+    # the run; the later legs' spins come after them).
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(1000)
     kern_us, _ = timed(lambda r: fwds[r % nb].run_whole(dbs[r % nb]), step_kinds, reps)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(1000)
 
     def calls_rep(r):
         f, db = fwds[r % nb], dbs[r % nb]
@@ -657,13 +807,15 @@ def main():
                    "tables": len(hk), "capacity": hcfg.hash_capacity, "keys": int(nkeys),
                    "us_all_tables": round(total_us, 2),
                    "keys_per_s": round(nkeys / (total_us * 1e-6), 1),
-                   "insert_avg_launch_us": round(ins_us, 3),
+                   "insert_call_us": round(ins_us, 3),
+                   "insert_launches": ["k_hash_insert", "k_hash_insert_winner", "k_hash_insert_values"],
                    "insert_algorithmic_gb_s": round(ins_gbs, 1),
                    "insert_hbm_frac": round(ins_gbs / HBM_PEAK_GBS, 4),
                    "bytes_per_key": INSERT_BYTES_PER_KEY,
-                   "traffic": load_traffic(["k_hash_insert"], shash, cfg.name),
+                   "traffic": load_traffic(["k_hash_insert", "k_hash_insert_winner", "k_hash_insert_values"],
+                                          shash, cfg.name),
                    "pages": "about 100-500 ms for 1.5M keys on the GPU (context, another machine)"}
-        print(f"[bench] hash rebuild: {nkeys} keys in {total_us:.1f} us ({ins_us:.2f} us per insert launch)",
+        print(f"[bench] hash rebuild: {nkeys} keys in {total_us:.1f} us ({ins_us:.2f} us per insert call)",
               file=sys.stderr, flush=True)
 
     admit = None
