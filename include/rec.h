@@ -77,7 +77,7 @@ enum { REC_POOL_SUM = 0, REC_POOL_MEAN = 1 };                    /* rec_dlrm_fwd
 #define REC_MAX_TABLES 32                 /* tables per rec_embbag_fwd call */
 #define REC_MAX_SEQ_LEN 1024              /* largest max_len for the DIN calls */
 #define REC_MAX_B 16777215                /* largest batch for the DIN plan */
-#define REC_DIN_PACKED_BYTES 131072       /* packed bf16 W1+W2 (rec_din_pack_mlp) */
+#define REC_DIN_PACKED_BYTES 106496       /* packed bf16 W1+W2 (rec_din_pack_mlp) */
 #define REC_TOWER_PACKED_BYTES 614400     /* packed bf16 tower weights (rec_tower_pack_mlp) */
 #define REC_NOALLOC_SCRATCH_BYTES 33554432 /* static scratch of rec_sparse_din_fwd_noalloc (32 MiB) */
 
@@ -131,14 +131,18 @@ typedef struct {
  *   b1 [256] fp32;  w2 [64][256] dtype `dtype`;  b2 [64] fp32
  *   w3 [64] fp32 (the 64 -> 1 score layer), b3 a host float
  * ReLU follows the 256- and 64-wide layers; the score has no activation.
- * dtype REC_BF16: w1/w2 are bf16 bit patterns; q-s and q*s are formed in fp32,
- * the 192 inputs and the 256 hidden activations are rounded to bf16 (round to
- * nearest even) and multiplied on the matrix cores with fp32 accumulation; the
+ * dtype REC_BF16: w1/w2 are bf16 bit patterns.  The first layer is evaluated
+ * through the identity W1 [q, s, q-s, q*s] = (W1q + W1d) q + (W1s - W1d) s +
+ * W1m (q*s) (W1q, W1s, W1d, W1m its four 48-column blocks): the two column
+ * sums are formed in fp32 and rounded to bf16 once; q, s and q*s (formed in
+ * fp32) and the 256 hidden activations are rounded to bf16 (round to nearest
+ * even) and multiplied on the matrix cores with fp32 accumulation; the
  * 64-wide layer, score, softmax and weighted sum stay fp32.
  * dtype REC_F32: every product and sum is fp32.
  * dtype REC_BF16_PACKED: as REC_BF16, but w1 points to the REC_DIN_PACKED_BYTES
- * image written by rec_din_pack_mlp (both layers, in the order the attention
- * kernel keeps them on chip) and w2 is not read.  Same results as REC_BF16.
+ * image written by rec_din_pack_mlp (both layers, the first one factored, in
+ * the order the attention kernel keeps them on chip) and w2 is not read.
+ * Same results as REC_BF16.
  * w1 and w2 16-byte aligned.
  */
 typedef struct {
@@ -157,7 +161,9 @@ typedef struct {
  * attention kernel: reads mlp->w1 [256][192] and mlp->w2 [64][256] (dtype
  * REC_BF16, plain layout) and writes their matrix-core operand order into
  * `packed` (device, 16-byte aligned, >= REC_DIN_PACKED_BYTES bytes).  Use it
- * with dtype REC_BF16_PACKED.  The values are copied unchanged.
+ * with dtype REC_BF16_PACKED.  W2 and W1m are copied unchanged; the blocks
+ * W1q + W1d and W1s - W1d are formed in fp32 and rounded to bf16 (see
+ * REC_BF16 above).
  * Errors: REC_EINVAL (null/misaligned pointers, dtype not REC_BF16),
  * REC_EWORKSPACE (packed_bytes too small).
  */

@@ -17,9 +17,9 @@
 //   1. reads the positions' sample, step and three resolved rows from the
 //      plan, then s (3 rows of 64 B) and q (3 x 16 floats of the pooled
 //      output); lane (n, g) holds features 12g..12g+11 of position n;
-//   2. forms the 192 inputs [q, s, q-s, q*s] in registers — never in memory;
+//   2. forms its inputs in registers — never in memory;
 //   3. runs the 192->256->64 MLP on the matrix cores with the weights as the
-//      A operand (bf16: staged once per workgroup in LDS, 128 KiB) and the
+//      A operand (bf16: staged once per workgroup in LDS, 104 KiB) and the
 //      positions as the B operand; the 256-wide layer is produced 32 units at
 //      a time and fed straight into the 64-wide layer, because a 16x16
 //      accumulator tile is already laid out as the next product's operand;
@@ -33,10 +33,16 @@
 // rescaling of partial softmax sums and writes the output.  Samples without
 // positions (listed by the plan) are zeroed by the workgroups before their
 // first group.
+// The first layer's input is [q, s, q-s, q*s] with W1 = [W1q | W1s | W1d |
+// W1m] (48 columns each).  Since W1d (q - s) = W1d q - W1d s, the bf16 path
+// evaluates the same sum as (W1q + W1d) q + (W1s - W1d) s + W1m (q*s): 144
+// inputs per position instead of 192, so a quarter fewer first-layer
+// products and weight bytes.  The two column sums are formed in fp32 from the
+// bf16 weights and rounded to bf16 once (rec_din_pack_mlp, or on chip for
+// unpacked weights).  The fp32 path keeps the 192 inputs.
 // Inside an MFMA the order of the K index is free as long as the A and B
-// operands agree, so each lane's 48 inputs are laid out to match its own 12
-// features, and the weights are permuted to the same order (rec_din_pack_mlp,
-// or on chip for unpacked weights).
+// operands agree, so each lane's 36 inputs are laid out to match its own 12
+// features, and the weights are permuted to the same order.
 #include "rec_internal.h"
 #include "rec_mfma.h"
 
@@ -234,6 +240,14 @@ __device__ inline float x_in(const Sub& S, int i) {
     return tau == 0 ? S.q[f] : (tau == 1 ? S.s[f] : (tau == 2 ? S.q[f] - S.s[f] : S.q[f] * S.s[f]));
 }
 
+// Input i (0..35) of a lane in the factored bf16 layer: block tau = i / 12 of
+// [q, s, q*s] at the lane's feature f = i % 12.  Column of the factored
+// weights: 48 tau + 12 g + f.
+__device__ inline float x_in3(const Sub& S, int i) {
+    const int tau = i / 12, f = i % 12;
+    return tau == 0 ? S.q[f] : (tau == 1 ? S.s[f] : S.q[f] * S.s[f]);
+}
+
 // e = w3 . relu(h2) + b3 for a lane's 16 units of h2 (bias already in),
 // summed over the four lane groups.
 __device__ inline float score_from_h2(const f32x4 (&acc2)[4], const float* w3s, float b3, int g) {
@@ -252,26 +266,57 @@ __device__ inline float score_from_h2(const f32x4 (&acc2)[4], const float* w3s, 
 }
 
 
-// Layer 1 for one hidden block: two 16-row tiles x NSUB position tiles, the
-// K loop (6 steps of 32) innermost in issue order so 2*NSUB independent
+// The factored W1 image in LDS, per hidden block hb of 32 units (576
+// 16-byte units): the full fragments (kb, rt) for K steps kb = 0..3 (inputs
+// 8 kb .. 8 kb + 7 of each lane), 64 lanes x 16 B each, then the half
+// fragments rt = 0, 1 (inputs 32..35), 64 lanes x 8 B each; W2 follows.
+constexpr int kW1BlockU4 = 576;
+constexpr int kW1U4 = 8 * kW1BlockU4;                 // 72 KiB
+constexpr int kW2U4 = 8 * 4 * 64;                     // 32 KiB
+constexpr int kWtU4 = kW1U4 + kW2U4;                  // 104 KiB
+static_assert(kWtU4 * 16 == REC_DIN_PACKED_BYTES, "packed image size");
+
+// One hidden block's first-layer fragments of a lane: full[kb * 2 + rt], half[rt].
+struct W1Frag {
+    uint4 full[8];
+    uint2 half[2];
+};
+
+__device__ inline void load_w1(const uint4* w1p, int hb, int lane, W1Frag& f) {
+    const uint4* b = w1p + hb * kW1BlockU4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.full[i] = b[i * 64 + lane];
+    const uint2* h = (const uint2*)(b + 512);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) f.half[rt] = h[rt * 64 + lane];
+}
+
+// Layer 1 for one hidden block: two 16-row tiles x NSUB position tiles, four
+// K steps of 32 and one of 16, innermost in issue order so 2*NSUB independent
 // accumulations are in flight.  The accumulators start from the block's bias
 // (the first product's C operand), so no separate bias add is needed.
 template <int NSUB>
-__device__ inline void l1_block(const bf16x8 (&xf)[NSUB][6], const uint4 (&w1)[12], const f32x4 bA,
-                                const f32x4 bB, f32x4 (&acc1)[NSUB][2]) {
+__device__ inline void l1_block(const bf16x8 (&xf)[NSUB][4], const s16x4 (&xh)[NSUB], const W1Frag& w1,
+                                const f32x4 bA, const f32x4 bB, f32x4 (&acc1)[NSUB][2]) {
 #pragma unroll
     for (int s = 0; s < NSUB; ++s) {
         acc1[s][0] = bA;
         acc1[s][1] = bB;
     }
 #pragma unroll
-    for (int kb = 0; kb < 6; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int s = 0; s < NSUB; ++s)
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
                 acc1[s][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, w1[kb * 2 + rt]), xf[s][kb], acc1[s][rt], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, w1.full[kb * 2 + rt]), xf[s][kb], acc1[s][rt], 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+            acc1[s][rt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(s16x4, w1.half[rt]), xh[s], acc1[s][rt], 0, 0, 0);
 }
 
 // The bf16 MLP for NSUB position tiles, software-pipelined over the eight
@@ -287,11 +332,17 @@ __device__ inline void mlp_bf16(const Sub* S, const uint4* w1p, const uint4* w2p
                                 const float* b2s, const float* w3s, float b3, int lane,
                                 float* e) {
     const int g = lane >> 4;
-    bf16x8 xf[NSUB][6];
+    bf16x8 xf[NSUB][4];
+    s16x4 xh[NSUB];
 #pragma unroll
-    for (int s = 0; s < NSUB; ++s)
+    for (int s = 0; s < NSUB; ++s) {
 #pragma unroll
-        for (int i = 0; i < 48; ++i) xf[s][i >> 3][i & 7] = (__bf16)x_in(S[s], i);
+        for (int i = 0; i < 32; ++i) xf[s][i >> 3][i & 7] = (__bf16)x_in3(S[s], i);
+        bf16x4 t;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = (__bf16)x_in3(S[s], 32 + i);
+        xh[s] = __builtin_bit_cast(s16x4, t);
+    }
     f32x4 acc2[NSUB][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -299,31 +350,29 @@ __device__ inline void mlp_bf16(const Sub* S, const uint4* w1p, const uint4* w2p
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) acc2[s][mt] = b2v;
     }
-    uint4 fw1[2][12], fw2[4];
+    W1Frag fw1[2];
+    uint4 fw2[4];
     f32x4 fb1[2][2];                // each block's b1 slice, read with its W1 fragments
     f32x4 acc1[2][NSUB][2];
-#pragma unroll
-    for (int i = 0; i < 12; ++i) fw1[0][i] = w1p[i * 64 + lane];
+    load_w1(w1p, 0, lane, fw1[0]);
     fb1[0][0] = *(const f32x4*)(b1s + 4 * g);
     fb1[0][1] = *(const f32x4*)(b1s + 16 + 4 * g);
-    l1_block<NSUB>(xf, fw1[0], fb1[0][0], fb1[0][1], acc1[0]);
+    l1_block<NSUB>(xf, xh, fw1[0], fb1[0][0], fb1[0][1], acc1[0]);
     fb1[1][0] = *(const f32x4*)(b1s + 32 + 4 * g);
     fb1[1][1] = *(const f32x4*)(b1s + 48 + 4 * g);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) fw1[1][i] = w1p[(12 + i) * 64 + lane];
+    load_w1(w1p, 1, lane, fw1[1]);
 #pragma unroll
     for (int hb = 0; hb < 8; ++hb) {
         __builtin_amdgcn_sched_barrier(0);
         const int cur = hb & 1, nxt = cur ^ 1;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) fw2[mt] = w2p[(hb * 4 + mt) * 64 + lane];
-        if (hb + 1 < 8) l1_block<NSUB>(xf, fw1[nxt], fb1[nxt][0], fb1[nxt][1], acc1[nxt]);
+        if (hb + 1 < 8) l1_block<NSUB>(xf, xh, fw1[nxt], fb1[nxt][0], fb1[nxt][1], acc1[nxt]);
         if (hb + 2 < 8) {
             // LDS reads complete in order: the b1 slice, needed first, goes first
             fb1[cur][0] = *(const f32x4*)(b1s + (hb + 2) * 32 + 4 * g);
             fb1[cur][1] = *(const f32x4*)(b1s + (hb + 2) * 32 + 16 + 4 * g);
-#pragma unroll
-            for (int i = 0; i < 12; ++i) fw1[cur][i] = w1p[((hb + 2) * 12 + i) * 64 + lane];
+            load_w1(w1p, hb + 2, lane, fw1[cur]);
         }
 #pragma unroll
         for (int s = 0; s < NSUB; ++s) {
@@ -499,54 +548,63 @@ __device__ inline void softmax_tile(const DinArgs& a, const Sub& S, float e, int
     }
 }
 
-// The packed A-operand image: 8-byte slots (hb, kb, rt, lane, half) of W1
-// followed by (hb, mt, lane, rt) of W2; a slot holds 4 consecutive bf16 of
-// one weight row.  W1 column k = 48 tau + 12 g + f is element i = 12 tau + f
-// of lane g*16 + m's 48 inputs (fragment kb = i / 8, slot half (i % 8) / 4);
-// W2 fragment element 4 rt + i is hidden unit hb*32 + rt*16 + 4g + i.
-__device__ inline void w1_slot_source(int d, int* row, int* col) {
-    const int half = d & 1, lane = (d >> 1) & 63, rest = d >> 7;
-    const int rt = rest & 1, hbkb = rest >> 1, kb = hbkb % 6, hb = hbkb / 6;
-    const int g = lane >> 4, m = lane & 15;
-    const int i0 = kb * 8 + half * 4;
-    *row = hb * 32 + rt * 16 + m;
-    *col = 48 * (i0 / 12) + 12 * g + (i0 % 12);
+// The packed A-operand image, in 8-byte slots of 4 consecutive bf16 of one
+// weight row: per hidden block hb, the factored W1's full fragments (kb, rt,
+// lane, half) and half fragments (rt, lane), then W2's (hb, mt, lane, rt).
+// Input i of lane g*16 + m (fragment kb = i / 8 for i < 32, the half
+// fragment for i = 32..35) is factored column 48 tau + 12 g + f (tau = i / 12,
+// f = i % 12); W2 fragment element 4 rt + i is hidden unit hb*32 + rt*16 +
+// 4g + i.
+constexpr int kW1Slots = 2 * kW1U4;               // 9216
+constexpr int kW2Slots = 2 * kW2U4;               // 4096
+
+__device__ inline float bf16_value(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Slot d < kW1Slots of the image: 4 factored first-layer weights, formed in
+// fp32 from the bf16 W1 [256][192] and rounded to bf16 (q: W1q + W1d; s:
+// W1s - W1d; q*s: W1m).
+__device__ inline uint2 w1_slot(const uint16_t* __restrict__ w1, int d) {
+    const int hb = d / (2 * kW1BlockU4), r = d % (2 * kW1BlockU4);
+    int lane, rt, i0;
+    if (r < 1024) {
+        const int frag = r >> 7;
+        lane = (r >> 1) & 63;
+        rt = frag & 1;
+        i0 = (frag >> 1) * 8 + (r & 1) * 4;
+    } else {
+        rt = (r - 1024) >> 6;
+        lane = r & 63;
+        i0 = 32;
+    }
+    const int row = hb * 32 + rt * 16 + (lane & 15);
+    const int tau = i0 / 12, c = 12 * (lane >> 4) + i0 % 12;
+    const uint16_t* w = w1 + row * 192;
+    bf16x4 v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        float x;
+        if (tau == 0) x = bf16_value(w[c + j]) + bf16_value(w[96 + c + j]);
+        else if (tau == 1) x = bf16_value(w[48 + c + j]) - bf16_value(w[96 + c + j]);
+        else x = bf16_value(w[144 + c + j]);
+        v[j] = (__bf16)x;
+    }
+    return __builtin_bit_cast(uint2, v);
 }
 
-__device__ inline void w2_slot_source(int d, int* row, int* col) {
+// Slot d < kW2Slots of the W2 part: W2 [64][256] values copied.
+__device__ inline uint2 w2_slot(const uint16_t* __restrict__ w2, int d) {
     const int rt = d & 1, lane = (d >> 1) & 63, rest = d >> 7;
     const int mt = rest & 3, hb = rest >> 2;
     const int g = lane >> 4, m = lane & 15;
-    *row = mt * 16 + m;
-    *col = hb * 32 + rt * 16 + 4 * g;
-}
-
-// Inverse maps: the slot holding W1[o][k..k+3] / W2[o][k..k+3] (k % 4 == 0).
-__device__ inline int w1_slot_of(int o, int k) {
-    const int tau = k / 48, c48 = k % 48, g = c48 / 12, f0 = c48 % 12;
-    const int i = 12 * tau + f0, kb = i >> 3, half = (i & 7) >> 2;
-    const int hb = o >> 5, rt = (o >> 4) & 1, m = o & 15;
-    return (((hb * 6 + kb) * 2 + rt) * 64 + g * 16 + m) * 2 + half;
-}
-
-__device__ inline int w2_slot_of(int o, int k) {
-    const int hb = k >> 5, rt = (k >> 4) & 1, g = (k >> 2) & 3;
-    const int mt = o >> 4, m = o & 15;
-    return ((hb * 4 + mt) * 64 + g * 16 + m) * 2 + rt;
+    return *(const uint2*)(w2 + (mt * 16 + m) * 256 + hb * 32 + rt * 16 + 4 * g);
 }
 
 __global__ __launch_bounds__(256) void k_din_pack(const uint16_t* __restrict__ w1,
                                                   const uint16_t* __restrict__ w2,
                                                   uint2* __restrict__ packed) {
     const int d = blockIdx.x * 256 + threadIdx.x;     // 8-byte slot
-    int row, col;
-    if (d < 12288) {
-        w1_slot_source(d, &row, &col);
-        packed[d] = *(const uint2*)(w1 + row * 192 + col);
-    } else if (d < 16384) {
-        w2_slot_source(d - 12288, &row, &col);
-        packed[d] = *(const uint2*)(w2 + row * 256 + col);
-    }
+    if (d < kW1Slots) packed[d] = w1_slot(w1, d);
+    else if (d < kW1Slots + kW2Slots) packed[d] = w2_slot(w2, d - kW1Slots);
 }
 
 // Positions per round of a wave: two 16-position tiles when a wave has its
@@ -560,12 +618,12 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
     constexpr bool kPacked = DT == REC_BF16_PACKED;
     constexpr bool kBF = DT == REC_BF16 || kPacked;
     constexpr int kThreads = 64 * kDinWaves;
-    __shared__ uint4 s_wt[kBF ? (8 * 6 * 2 + 8 * 4) * 64 : 1];
+    __shared__ uint4 s_wt[kBF ? kWtU4 : 1];
     __shared__ float s_b1[256];
     __shared__ float s_b2[64];
     __shared__ float s_w3[64];
     uint4* s_w1 = s_wt;
-    uint4* s_w2 = s_wt + 8 * 6 * 2 * 64;
+    uint4* s_w2 = s_wt + kW1U4;
 
     __shared__ __attribute__((aligned(16))) float s_piece[kDinWaves * 2 * kPartialFloats];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -581,27 +639,17 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
     __builtin_amdgcn_sched_barrier(0);      // keep those loads ahead of the staging
     // Weight staging depends on nothing else and completes under the group
     // bookkeeping and the first gathers.
-    constexpr int kW1Per = (kBF && !kPacked) ? 256 * 24 / kThreads : 0;
-    constexpr int kW2Per = (kBF && !kPacked) ? 64 * 32 / kThreads : 0;
-    uint4 v1[kW1Per > 0 ? kW1Per : 1], v2[kW2Per > 0 ? kW2Per : 1];
     if (kPacked) {
         // the packed image is the LDS image: copy it straight from memory into
         // LDS (global_load_lds, 1 KiB per wave instruction, no registers)
         const uint4* src = (const uint4*)a.w1;
-        constexpr int kChunks = (8 * 6 * 2 + 8 * 4) * 64;      // 16-byte chunks
+        static_assert(kWtU4 % kThreads == 0, "whole wave copies");
 #pragma unroll
-        for (int i = 0; i < kChunks / kThreads; ++i) {
+        for (int i = 0; i < kWtU4 / kThreads; ++i) {
             const int c0 = (i * kDinWaves + wave) * 64;
             __builtin_amdgcn_global_load_lds((const void*)(src + c0 + lane),
                                              (__attribute__((address_space(3))) void*)(s_wt + c0), 16, 0, 0);
         }
-    } else if (kBF) {
-        const uint4* w1g = (const uint4*)a.w1;
-        const uint4* w2g = (const uint4*)a.w2;
-#pragma unroll
-        for (int i = 0; i < kW1Per; ++i) v1[i] = w1g[threadIdx.x + i * kThreads];
-#pragma unroll
-        for (int i = 0; i < kW2Per; ++i) v2[i] = w2g[threadIdx.x + i * kThreads];
     }
     float vb1 = 0.f, vb2 = 0.f, vw3 = 0.f;
     if (threadIdx.x < 256) vb1 = a.b1[threadIdx.x];
@@ -637,25 +685,11 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
     }
 
     if (kBF && !kPacked) {
+        // plain bf16 weights: every thread forms its share of the image's slots
         uint2* d = (uint2*)s_wt;
-#pragma unroll
-        for (int i = 0; i < kW1Per; ++i) {
-            const int c = threadIdx.x + i * kThreads;       // 16-byte chunk of W1
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int slot = w1_slot_of(c / 24, 8 * (c % 24) + 4 * h);
-                d[slot] = h ? make_uint2(v1[i].z, v1[i].w) : make_uint2(v1[i].x, v1[i].y);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < kW2Per; ++i) {
-            const int c = threadIdx.x + i * kThreads;       // 16-byte chunk of W2
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int slot = 12288 + w2_slot_of(c >> 5, 8 * (c & 31) + 4 * h);
-                d[slot] = h ? make_uint2(v2[i].z, v2[i].w) : make_uint2(v2[i].x, v2[i].y);
-            }
-        }
+        for (int i = threadIdx.x; i < kW1Slots; i += kThreads) d[i] = w1_slot((const uint16_t*)a.w1, i);
+        for (int i = threadIdx.x; i < kW2Slots; i += kThreads)
+            d[kW1Slots + i] = w2_slot((const uint16_t*)a.w2, i);
     }
     if (threadIdx.x < 256) s_b1[threadIdx.x] = vb1;
     if (threadIdx.x < 64) {
@@ -804,7 +838,7 @@ hipError_t launch_din(const DinArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_din_pack(const void* w1, const void* w2, void* packed, hipStream_t s) {
-    hipLaunchKernelGGL(k_din_pack, dim3(16384 / 256), dim3(256), 0, s, (const uint16_t*)w1,
+    hipLaunchKernelGGL(k_din_pack, dim3((kW1Slots + kW2Slots) / 256), dim3(256), 0, s, (const uint16_t*)w1,
                        (const uint16_t*)w2, (uint2*)packed);
     return hipGetLastError();
 }

@@ -5,6 +5,8 @@
 //   A  8 bf16: row m of the 16 x 32 left tile, K elements 8g .. 8g+7
 //   B  8 bf16: column m of the 32 x 16 right tile, K elements 8g .. 8g+7
 //   C/D 4 fp32: column m of the 16 x 16 result, rows 4g .. 4g+3
+// v_mfma_f32_16x16x16_bf16 takes the same layout with 4 bf16 per lane (K
+// elements 4g .. 4g+3).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -16,6 +18,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));   // 4 bf16 bit patterns (16x16x16 operands)
 
 // max(RNE(a), 0), max(RNE(b), 0) as a bf16 pair.  Rounding to nearest keeps
 // the sign, so ReLU after rounding equals rounding after ReLU; on the bit

@@ -22,7 +22,7 @@ REC_SCORE_NONE, REC_SCORE_STEP, REC_SCORE_LFU = 0, 1, 2
 (REC_TIME_DIN_ATTN, REC_TIME_GATHER, REC_TIME_SUMS, REC_TIME_TOWERS,
  REC_TIME_DLRM_INTERACT, REC_TIME_DLRM_EMBED, REC_TIME_DLRM_TOP, REC_TIME_KINDS) = range(8)
 REC_POOL_SUM, REC_POOL_MEAN = 0, 1
-REC_DIN_PACKED_BYTES = 131072
+REC_DIN_PACKED_BYTES = 106496
 REC_TOWER_PACKED_BYTES = 614400
 REC_NOALLOC_SCRATCH_BYTES = 33554432
 REC_DIM = 16
