@@ -53,6 +53,9 @@ PLAN_BYTES_PER_SAMPLE = 4 + 4 + 8          # length in; packed start, sequence b
 DIN_BYTES_PER_SAMPLE = 4 + 8 + 4 + 192 + 192   # length, offset, packed start, query, output
 DIN_BYTES_WEIGHTS = 256 * 192 * 2 + 64 * 256 * 2 + (256 + 64 + 64) * 4
 DIN_FLOPS_PER_POS = 2 * (192 * 256 + 256 * 64 + 64)
+# what the bf16 kernel executes per position: its first layer takes 144 inputs
+# ((W1q + W1d) q + (W1s - W1d) s + W1m (q*s), the same sum)
+DIN_EXEC_FLOPS_PER_POS = 2 * (144 * 256 + 256 * 64 + 64)
 TOWER_FLOPS_PER_SAMPLE = 2 * (256 * 512 + 512 * 256 + 256 * 128 + 176 * 64 + 64)
 TOWER_WEIGHT_BYTES = 2 * (256 * 512 + 512 * 256 + 256 * 128 + 176 * 64)
 ADAGRAD_BYTES_PER_READ = 8 + 64            # raw id + the read's 64-byte output gradient
@@ -712,7 +715,11 @@ def main():
             "achieved": din_tflops, "peak": peak_mfma, "unit": "TFLOP/s",
             "frac": round(din_tflops / peak_mfma, 4),
             "traffic": load_traffic(["k_din_attn"], shash, cfg.name),
-            "per_launch": {"flops": din_flops, "bytes": din_bytes, "positions": P, "samples": B},
+            "per_launch": {"flops": din_flops, "bytes": din_bytes, "positions": P, "samples": B,
+                           "executed_flops": P * DIN_EXEC_FLOPS_PER_POS,
+                           "flops_note": "flops = the attention MLP as the pages define it (192 inputs); "
+                                         "the bf16 kernel executes executed_flops (144 inputs, the same "
+                                         "sum factored)"},
             "avg_launch_us": round(kern_us["din"]["mean"], 3),
             "timing": "mean kernel execution time of the attention launch over "
                       f"{kern_us['din']['n']} warm steps (HIP events bound to the dispatch)"}
