@@ -140,7 +140,7 @@ KERNEL_SOURCES = {"k_din_attn": _FWD, "k_embbag_fwd": _FWD, "k_fwd_gather": _FWD
                   "k_bwd_keys": _BWD, "k_sort_hist": _BWD, "k_sort_scan": _BWD, "k_sort_scatter": _BWD,
                   "k_bwd_chunks": _BWD, "k_bwd_cross": _BWD,
                   "k_dlrm_interact": ["rec_dlrm.hip", "rec_mfma.h"] + _COMMON,
-                  "k_dlrm_embed": ["rec_dlrm_fwd.hip"] + _COMMON, "k_dlrm_top": ["rec_dlrm_fwd.hip"] + _COMMON}
+                  "k_dlrm_fwd": ["rec_dlrm_fwd.hip", "rec_mfma.h"] + _COMMON}
 for _k in ("k_dinb_prep", "k_dinb_map", "k_dinb_fwd", "k_dinb_soft", "k_dinb_bwdt",
            "k_dinb_gq", "k_dinb_wgrad", "k_dinb_reduce"):
     KERNEL_SOURCES[_k] = ["rec_din_bwd.hip"] + _COMMON
@@ -160,12 +160,12 @@ KERNELS = {"k_din_attn": "k_din_attn",
            "k_dinb_map": "k_dinb_map", "k_dinb_fwd": "k_dinb_fwd", "k_dinb_soft": "k_dinb_soft",
            "k_dinb_bwdt": "k_dinb_bwdt", "k_dinb_gq": "k_dinb_gq", "k_dinb_wgrad": "k_dinb_wgrad",
            "k_dinb_reduce": "k_dinb_reduce", "copy": "MulFunctor", "gather_cal": "vectorized_gather_kernel",
-           "k_dlrm_embed": "k_dlrm_embed", "k_dlrm_top": "k_dlrm_top"}
+           "k_dlrm_fwd": "k_dlrm_fwd<"}
 # kernels whose reads are mostly random 64-byte rows: their FETCH_SIZE is scaled
 # by the calibration gather's reading (random 64-byte rows), the others' by
 # the calibration copy's (streaming)
 RANDOM_ROW_KERNELS = {"k_din_attn", "k_embbag_fwd", "k_fwd_gather", "k_bwd_chunks", "k_bwd_cross",
-                      "k_dlrm_embed"}
+                      "k_dlrm_fwd"}
 
 
 def load_traffic(kernels, shash: str, config: str):
@@ -1092,26 +1092,29 @@ def main():
             for _ in range(3):
                 dlrm_call()
             torch.cuda.synchronize()
-        dk, dcall = timed(dlrm_call, {"embed": R.REC_TIME_DLRM_EMBED, "top": R.REC_TIME_DLRM_TOP}, 40)
+        dk, dcall = timed(dlrm_call, {"fwd": R.REC_TIME_DLRM_FWD}, 40)
         nnz_d = float(dbt.values.size)
         F_ = S_ + 1
-        embed_bytes = (nnz_d * (8 + 4 * d_) + S_ * Bd * (4 + 8) + Bd * dcfg.n_dense * 4
-                       + Bd * F_ * d_ * 4)
-        top_bytes = Bd * F_ * d_ * 4 + Bd * 8
         np_ = F_ * (F_ + 1) // 2
-        top_flops = Bd * 2.0 * (np_ * d_ + np_ * 128 + 128 * 64 + 64)
-        dlrm = {"entry": "rec_dlrm_fwd (bags of width 96 + bottom MLP; interaction + top MLP)",
+        # algorithmic bytes: ids, rows, lengths and offsets, dense inputs, z out,
+        # logit and probability out (the weights, read once, are negligible)
+        d_bytes = (nnz_d * (8 + 4 * d_) + S_ * Bd * (4 + 8) + Bd * dcfg.n_dense * 4
+                   + Bd * F_ * d_ * 4 + Bd * 8)
+        d_flops = Bd * 2.0 * (dcfg.n_dense * 128 + 128 * d_ + np_ * d_ + np_ * 128 + 128 * 64 + 64)
+        fwd_us = dk["fwd"]["mean"]
+        dlrm = {"entry": "rec_dlrm_fwd (bags of width 96, bottom MLP, interaction, top MLP: one launch)",
                 "workload": f"{dcfg.name}: B={Bd}, 13 dense, tables {list(dcfg.sizes)} of width {d_}, "
                             f"bags 1-{dcfg.bag_max} ids, sum pooling",
-                "call_us": dcall, "kernels_us": dk,
-                "samples_s": round(Bd / (dcall["mean"] * 1e-6), 1),
-                "embed_algorithmic_bytes": embed_bytes,
-                "embed_gb_s": round(embed_bytes / (dk["embed"]["mean"] * 1e-6) / 1e9, 1),
-                "embed_hbm_frac": round(embed_bytes / (dk["embed"]["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                "top_bytes": top_bytes, "top_flops": top_flops,
-                "top_tflops": round(top_flops / (dk["top"]["mean"] * 1e-6) / 1e12, 2)}
-        print(f"[bench] DLRM forward: {dcall['mean']:.1f} us per call (embed {dk['embed']['mean']:.1f}, "
-              f"top {dk['top']['mean']:.1f})", file=sys.stderr, flush=True)
+                "call_us": dcall, "kernel_us": dk["fwd"],
+                "samples_s": round(Bd / (fwd_us * 1e-6), 1),
+                "algorithmic_bytes": d_bytes, "flops": d_flops,
+                "gb_s": round(d_bytes / (fwd_us * 1e-6) / 1e9, 1),
+                "hbm_frac": round(d_bytes / (fwd_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "tflops": round(d_flops / (fwd_us * 1e-6) / 1e12, 2),
+                "bound": "HBM (random 384-byte rows) and the per-workgroup weight stream from L2",
+                "traffic": load_traffic(["k_dlrm_fwd"], shash, cfg.name)}
+        print(f"[bench] DLRM forward: {fwd_us:.1f} us per launch ({dcall['mean']:.1f} us per call), "
+              f"{dlrm['gb_s']:.0f} GB/s of algorithmic bytes", file=sys.stderr, flush=True)
         del keep, zbuf
 
     # `value` is whole-job throughput: with two batches in flight when that is

@@ -67,8 +67,8 @@ enum { REC_DIRECT = 0, REC_HASH = 1 };   /* rec_table.kind */
 enum { REC_F32 = 0, REC_BF16 = 1, REC_BF16_PACKED = 2 };   /* rec_din_mlp.dtype */
 enum { REC_SCORE_NONE = 0, REC_SCORE_STEP = 1, REC_SCORE_LFU = 2 };   /* rec_hash_insert */
 enum { REC_TIME_DIN_ATTN = 0, REC_TIME_GATHER = 1, REC_TIME_SUMS = 2, REC_TIME_TOWERS = 3,
-       REC_TIME_DLRM_INTERACT = 4, REC_TIME_DLRM_EMBED = 5, REC_TIME_DLRM_TOP = 6,
-       REC_TIME_KINDS = 7 };                                        /* rec_time_next_launch */
+       REC_TIME_DLRM_INTERACT = 4, REC_TIME_DLRM_FWD = 5,
+       REC_TIME_KINDS = 6 };                                        /* rec_time_next_launch */
 enum { REC_POOL_SUM = 0, REC_POOL_MEAN = 1 };                    /* rec_dlrm_fwd bag modes */
 
 #define REC_DIM 16                        /* embedding width of every table */
@@ -417,7 +417,7 @@ typedef struct {
  *            input: bottom output first, then the bags in table order)
  *   inter    fp32 [B][(S+1)(S+2)/2] or NULL: the interaction output
  *   logit    fp32 [B];  prob fp32 [B] or NULL
- * Two launches (bags and bottom MLP; interaction and top MLP).
+ * One launch.
  * Errors: REC_EINVAL (null required pointers, misalignment, B < 0, a table
  * that is not direct or whose dim differs, unknown mode, sizes outside the
  * limits above).  B == 0 is a no-op.
@@ -830,8 +830,7 @@ rec_status rec_din_attn_bwd(const rec_table* seq_tables, const int64_t* seq_valu
  *                           rec_sparse_din_fwd)
  *   REC_TIME_TOWERS         the bf16 towers (rec_towers_fwd)
  *   REC_TIME_DLRM_INTERACT  the interaction (rec_dlrm_interact)
- *   REC_TIME_DLRM_EMBED     rec_dlrm_fwd's bags and bottom MLP
- *   REC_TIME_DLRM_TOP       rec_dlrm_fwd's interaction and top MLP
+ *   REC_TIME_DLRM_FWD       rec_dlrm_fwd (one launch)
  * The events (created by the caller with timing enabled, on the device of
  * the launch) are used by one launch and then forgotten; start == stop ==
  * NULL forgets them without a launch.  The setting is thread-local state of

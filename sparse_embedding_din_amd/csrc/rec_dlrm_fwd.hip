@@ -11,17 +11,20 @@
 // layers; the interaction's (S+1)(S+2)/2 outputs, j running from i; top ->
 // 128 -> 64 -> 1 with ReLU, ReLU and a sigmoid).
 //
-// Two launches, fp32 throughout:
-//   1. k_dlrm_embed: its first blocks pool the bags straight into the
-//      interaction input z [B][S+1][d] (vector t+1 of sample b is bag (t, b)),
-//      eight lanes per bag, each lane holding d/32 float4 columns of a row,
-//      so one wave instruction reads eight rows' worth of 128-byte runs; ids
-//      are loaded four at a time ahead of their rows.  The remaining blocks
-//      run the bottom MLP for 32 samples each (activations in LDS) into
-//      vector 0 of z.
-//   2. k_dlrm_top: 16 samples per workgroup: their z rows are staged in LDS,
-//      every pair (i <= j) is one thread's dot product over d, and the top
-//      MLP runs on the pairs in LDS; the logit and the probability go out.
+// One launch, fp32 throughout, 16 samples per 8-wave workgroup:
+//   - the bags pool straight into the interaction input z in LDS (vector t+1
+//     of a sample is bag (t, b)), eight lanes per bag, each lane holding d/32
+//     float4 columns of a row, so one wave instruction reads eight rows' worth
+//     of 128-byte runs; ids are loaded four at a time ahead of their rows;
+//   - the bottom MLP writes vector 0 of z; z goes out to memory once;
+//   - the interaction: per sample G = Z Z^T on the fp32 matrix cores (Z padded
+//     to 16 rows; the A and B operands of a product are the same register),
+//     whose upper triangle is the pair list;
+//   - the top MLP, then the logit and the probability.
+// The dense layers run on v_mfma_f32_16x16x4f32 with the weights as the A
+// operand read from memory (every workgroup reads the same few hundred KiB,
+// so they come from L2) and the activations in LDS as the B operand.
+#include "rec_mfma.h"
 #include "rec_internal.h"
 
 namespace rec {
@@ -29,151 +32,245 @@ namespace {
 
 constexpr int kBagLanes = 8;                 // lanes per bag
 constexpr int kIdRound = 4;                  // ids of a bag loaded per round
-constexpr int kBottomSamples = 32;
-constexpr int kTopSamples = 16;
+constexpr int kDenseSamples = 16;             // samples per workgroup
+constexpr int kDenseThreads = 512;            // eight waves: two per SIMD
 
-// One dense layer over activations in LDS: out[r][o] = act(b[o] + sum_i
-// W[o][i] in[r][i]) for r < rows, o < nout; W is [nout][nin] in global memory
-// (torch's Linear layout), read through the caches.
-__device__ inline void dense_layer(const float* in, int in_stride, int nin, const float* __restrict__ W,
-                                   const float* __restrict__ bias, int nout, float* out, int out_stride,
-                                   int rows, bool relu) {
-    for (int idx = threadIdx.x; idx < rows * nout; idx += blockDim.x) {
-        const int r = idx / nout, o = idx - r * nout;
-        const float* w = W + (int64_t)o * nin;
-        const float* x = in + r * in_stride;
-        float acc = bias[o];
-        for (int i = 0; i < nin; ++i) acc = fmaf(w[i], x[i], acc);
-        out[r * out_stride + o] = relu ? fmaxf(acc, 0.f) : acc;
+// NU chunks of 16 inputs (from input i0) of one 16-unit tile: the operands
+// of all of them are loaded, then their 4 * NU products run.  K order: in
+// step 4c + j, lane (m, k) takes input 16c + 4k + j, so a lane's four inputs
+// of a chunk are one float4 of its W row (one load covers 16 whole 64-byte
+// row pieces) and one 16-byte LDS read of its activations.
+template <int NU, bool kVec>
+__device__ inline void layer_chunks(const float* in, int ins, int nin, const float* wr, int i0, int m,
+                                    int kg, f32x4& acc) {
+    float4 av[NU], bv[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int i = i0 + 16 * u + 4 * kg;
+        if (kVec) {
+            const float4 w = *(const float4*)(wr + (i < nin ? i : 0));
+            av[u] = i < nin ? w : make_float4(0.f, 0.f, 0.f, 0.f);
+        } else {
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float w = wr[min(i + j, nin - 1)];
+                v[j] = i + j < nin ? w : 0.f;
+            }
+            av[u] = make_float4(v[0], v[1], v[2], v[3]);
+        }
+        bv[u] = *(const float4*)(in + m * ins + i);
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u].x, bv[u].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u].y, bv[u].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u].z, bv[u].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u].w, bv[u].w, acc, 0, 0, 0);
     }
 }
 
+template <bool kVec>
+__device__ inline void layer_part(const float* in, int ins, int nin, const float* wr, int i0, int nu, int m,
+                                  int kg, f32x4& acc) {
+    switch (nu) {                                          // uniform
+        case 1: layer_chunks<1, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        case 2: layer_chunks<2, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        case 3: layer_chunks<3, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        case 4: layer_chunks<4, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        case 5: layer_chunks<5, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        case 6: layer_chunks<6, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        case 7: layer_chunks<7, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        default: layer_chunks<8, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+    }
+}
+
+// One dense layer on the matrix cores: out[r][o] = act(bias[o] + sum_i W[o][i]
+// in[r][i]) for the workgroup's 16 rows r and o < nout (a multiple of 16),
+// with in and out in LDS (row strides ins, outs; in's rows hold zeros from
+// nin up to a multiple of 16) and W [nout][nin] in memory (torch.nn.Linear's
+// layout).  v_mfma_f32_16x16x4f32: A = 16 units x 4 inputs of W, B = 4 inputs
+// x 16 rows; the result's lane (n, k) holds units o0 + 4k .. +3 of row n.
+// Wave w takes the 16-unit tiles w, w + 8, ...; up to 8 chunks (128 inputs)
+// of a tile are loaded together ahead of their products.
+__device__ inline void mfma_layer(const float* in, int ins, int nin, const float* __restrict__ W,
+                                  const float* __restrict__ bias, int nout, float* out, int outs,
+                                  bool relu) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m = lane & 15, kg = lane >> 4;
+    const int nch = (nin + 15) / 16;
+    const bool vec = (nin & 3) == 0;                      // W rows are 16-byte aligned
+    for (int ot = wave; ot * 16 < nout; ot += kDenseThreads / 64) {
+        const int o0 = ot * 16;
+        f32x4 acc = *(const f32x4*)(bias + o0 + 4 * kg);
+        const float* wr = W + (int64_t)(o0 + m) * nin;
+        for (int c0 = 0; c0 < nch; c0 += 8) {
+            const int nu = min(8, nch - c0);
+            if (vec) layer_part<true>(in, ins, nin, wr, 16 * c0, nu, m, kg, acc);
+            else layer_part<false>(in, ins, nin, wr, 16 * c0, nu, m, kg, acc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float v = acc[j];
+            out[m * outs + o0 + 4 * kg + j] = relu ? fmaxf(v, 0.f) : v;
+        }
+    }
+}
+
+// The bags of the workgroup's samples b0 .. b0 + rows - 1 into z in LDS
+// (row stride zs, vector t + 1 = bag (t, b)): eight lanes per bag, lane c of a
+// bag holding float4 columns c, c + 8, ... of each row.
 template <int NF>
-__device__ inline void dlrm_bags(const DlrmArgs& a, int64_t blk) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t nbw = (a.B + 31) / 32;                  // 32-sample chunks per table
-    const int t = (int)(blk / nbw);
-    const int64_t b = (blk % nbw) * 32 + wave * kBagLanes + (lane >> 3);
-    const int c = lane & 7;
-    const bool live = b < a.B;
-    const int64_t bag = (int64_t)t * a.B + (live ? b : a.B - 1);
-    const TabDev tab = a.tab[t];
-    const int32_t len = live ? a.lengths[bag] : 0;
-    const int64_t off = a.offsets[bag];
+__device__ inline void bags_into_lds(const DlrmArgs& a, int64_t b0, int rows, float* s_z, int zs) {
+    const int lane = threadIdx.x & 63, c = lane & 7;
     const int d = a.dim;
-    float4 acc[NF];
+    const int nq = kDenseSamples * a.S;                      // bags of the workgroup
+    for (int q0 = (int)(threadIdx.x >> 6) * 8; q0 < nq; q0 += kDenseThreads / kBagLanes) {
+        // q0 is a multiple of 8, so the wave's eight bags share their table
+        const int q = q0 + (lane >> 3);
+        const int r = q % kDenseSamples;
+        const int t = __builtin_amdgcn_readfirstlane(q0 / kDenseSamples);
+        const bool live = q < nq && r < rows;
+        const int64_t b = b0 + (live ? r : 0);
+        const int64_t bag = (int64_t)t * a.B + b;
+        const TabDev& tab = a.tab[t];
+        const int32_t len = live ? a.lengths[bag] : 0;
+        const int64_t off = a.offsets[bag];
+        float4 acc[NF];
 #pragma unroll
-    for (int f = 0; f < NF; ++f) acc[f] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j0 = 0; __ballot(j0 < len) != 0; j0 += kIdRound) {
-        int64_t row[kIdRound];
+        for (int f = 0; f < NF; ++f) acc[f] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j0 = 0; __ballot(j0 < len) != 0; j0 += kIdRound) {
+            int64_t row[kIdRound];
 #pragma unroll
-        for (int u = 0; u < kIdRound; ++u) {
-            const int64_t raw = a.values[len > 0 ? off + min(j0 + u, len - 1) : 0];
-            row[u] = floor_mod_magic(raw, tab.rows, tab.magic, tab.shift);
+            for (int u = 0; u < kIdRound; ++u) {
+                const int64_t raw = a.values[len > 0 ? off + min(j0 + u, len - 1) : 0];
+                row[u] = floor_mod_magic(raw, tab.rows, tab.magic, tab.shift);
+            }
+            float4 v[kIdRound][NF];
+#pragma unroll
+            for (int u = 0; u < kIdRound; ++u) {
+                const float4* src = (const float4*)(tab.values + row[u] * d) + c;
+#pragma unroll
+                for (int f = 0; f < NF; ++f) v[u][f] = src[8 * f];
+            }
+#pragma unroll
+            for (int u = 0; u < kIdRound; ++u) {
+                const bool use = j0 + u < len;
+#pragma unroll
+                for (int f = 0; f < NF; ++f) {
+                    acc[f].x += use ? v[u][f].x : 0.f;
+                    acc[f].y += use ? v[u][f].y : 0.f;
+                    acc[f].z += use ? v[u][f].z : 0.f;
+                    acc[f].w += use ? v[u][f].w : 0.f;
+                }
+            }
         }
-        float4 v[kIdRound][NF];
-#pragma unroll
-        for (int u = 0; u < kIdRound; ++u) {
-            const float4* src = (const float4*)(tab.values + row[u] * d) + c;
-#pragma unroll
-            for (int f = 0; f < NF; ++f) v[u][f] = src[8 * f];
-        }
-#pragma unroll
-        for (int u = 0; u < kIdRound; ++u) {
-            const bool use = j0 + u < len;
+        if (!live) continue;
+        if (a.mode[t] == REC_POOL_MEAN && len > 0) {
+            const float inv = 1.f / (float)len;
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
-                acc[f].x += use ? v[u][f].x : 0.f;
-                acc[f].y += use ? v[u][f].y : 0.f;
-                acc[f].z += use ? v[u][f].z : 0.f;
-                acc[f].w += use ? v[u][f].w : 0.f;
+                acc[f].x *= inv;
+                acc[f].y *= inv;
+                acc[f].z *= inv;
+                acc[f].w *= inv;
+            }
+        }
+        float4* o = (float4*)(s_z + r * zs + (1 + t) * d) + c;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) o[8 * f] = acc[f];
+    }
+}
+
+__host__ __device__ inline int round16(int x) { return (x + 15) & ~15; }
+
+// Dynamic LDS of k_dlrm_fwd, in floats: z of the 16 samples (rows of F*d,
+// as in memory; later the top MLP's two hidden layers), then the bottom MLP's
+// input and hidden layer (later the interaction output), then the pair list
+// (two uint16 per pair).
+struct DenseLds {
+    int zs, xs, hs, is, np, zfl, bfl, bytes;
+};
+__host__ __device__ inline DenseLds dense_lds(int S, int d, int n_dense) {
+    DenseLds L;
+    const int F = S + 1;
+    L.zs = F * d;
+    L.xs = round16(n_dense) + 4;
+    L.hs = 128 + 4;
+    L.np = F * (F + 1) / 2;
+    L.is = round16(L.np) + 4;
+    const int top = kDenseSamples * (L.hs + 64 + 4);
+    L.zfl = max(kDenseSamples * L.zs, top);
+    L.bfl = max(kDenseSamples * (L.xs + L.hs), kDenseSamples * L.is);
+    L.bytes = 4 * (L.zfl + L.bfl) + 4 * L.np;
+    return L;
+}
+
+template <int NF>
+__global__ __launch_bounds__(kDenseThreads, 4) void k_dlrm_fwd(const DlrmArgs a) {
+    extern __shared__ __attribute__((aligned(16))) float s_dyn[];
+    const DenseLds Ld = dense_lds(a.S, a.dim, a.n_dense);
+    const int F = a.S + 1, d = a.dim, zw = F * d, zs = Ld.zs;
+    const int np = Ld.np, is = Ld.is, xs = Ld.xs, hs = Ld.hs;
+    float* s_z = s_dyn;
+    float* s_b = s_dyn + Ld.zfl;
+    float* s_x = s_b;
+    float* s_h = s_b + kDenseSamples * xs;
+    float* s_i = s_b;
+    float* s_t1 = s_z;
+    float* s_t2 = s_z + kDenseSamples * hs;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m = lane & 15, kg = lane >> 4;
+    const int64_t b0 = (int64_t)blockIdx.x * kDenseSamples;
+    const int rows = (int)min((int64_t)kDenseSamples, a.B - b0);
+    // dense inputs (rows past the batch and columns past n_dense read zeros)
+    for (int idx = threadIdx.x; idx < kDenseSamples * xs; idx += kDenseThreads) {
+        const int r = idx / xs, i = idx - r * xs;
+        const bool ok = r < rows && i < a.n_dense;
+        const float v = a.dense[ok ? (b0 + r) * a.n_dense + i : 0];
+        s_x[idx] = ok ? v : 0.f;
+    }
+    bags_into_lds<NF>(a, b0, rows, s_z, zs);
+    __syncthreads();
+    mfma_layer(s_x, xs, a.n_dense, a.wb1, a.bb1, 128, s_h, hs, true);
+    __syncthreads();
+    mfma_layer(s_h, hs, 128, a.wb2, a.bb2, d, s_z, zs, true);       // vector 0 of z
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < rows * zw / 4; idx += kDenseThreads)
+        ((float4*)(a.z + b0 * (int64_t)zw))[idx] = ((const float4*)s_z)[idx];
+    // the interaction: G = Z Z^T per sample, lane (n, k) of the result holding
+    // G[4k + j][n]; rows of Z past F read zeros
+    for (int r = wave; r < kDenseSamples; r += kDenseThreads / 64) {
+        f32x4 g = {0.f, 0.f, 0.f, 0.f};
+        const float* zr = s_z + r * zs + m * d + 4 * kg;
+        for (int c = 0; c < d / 16; ++c) {
+            const float4 v = m < F ? *(const float4*)(zr + 16 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+            g = __builtin_amdgcn_mfma_f32_16x16x4f32(v.x, v.x, g, 0, 0, 0);
+            g = __builtin_amdgcn_mfma_f32_16x16x4f32(v.y, v.y, g, 0, 0, 0);
+            g = __builtin_amdgcn_mfma_f32_16x16x4f32(v.z, v.z, g, 0, 0, 0);
+            g = __builtin_amdgcn_mfma_f32_16x16x4f32(v.w, v.w, g, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = 4 * kg + j, n = m;
+            if (i <= n && n < F) {
+                const int p = i * F - i * (i - 1) / 2 + (n - i);
+                s_i[r * is + p] = g[j];
+                if (a.inter && r < rows) a.inter[(b0 + r) * np + p] = g[j];
             }
         }
     }
-    if (!live) return;
-    if (a.mode[t] == REC_POOL_MEAN && len > 0) {
-        const float inv = 1.f / (float)len;
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            acc[f].x *= inv;
-            acc[f].y *= inv;
-            acc[f].z *= inv;
-            acc[f].w *= inv;
-        }
-    }
-    float4* o = (float4*)(a.z + (b * (int64_t)(a.S + 1) + 1 + t) * d) + c;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) o[8 * f] = acc[f];
-}
-
-__device__ inline void dlrm_bottom(const DlrmArgs& a, int64_t blk) {
-    __shared__ float s_x[kBottomSamples * kDlrmMaxDense];
-    __shared__ float s_h[kBottomSamples * 128];
-    const int64_t b0 = blk * kBottomSamples;
-    const int rows = (int)min((int64_t)kBottomSamples, a.B - b0);
-    for (int idx = threadIdx.x; idx < rows * a.n_dense; idx += blockDim.x)
-        s_x[idx] = a.dense[b0 * a.n_dense + idx];
-    __syncthreads();
-    dense_layer(s_x, a.n_dense, a.n_dense, a.wb1, a.bb1, 128, s_h, 128, rows, true);
-    __syncthreads();
-    const int F = a.S + 1;
-    for (int idx = threadIdx.x; idx < rows * a.dim; idx += blockDim.x) {
-        const int r = idx / a.dim, o = idx - r * a.dim;
-        const float* w = a.wb2 + (int64_t)o * 128;
-        const float* x = s_h + r * 128;
-        float acc = a.bb2[o];
-        for (int i = 0; i < 128; ++i) acc = fmaf(w[i], x[i], acc);
-        a.z[(b0 + r) * (int64_t)F * a.dim + o] = fmaxf(acc, 0.f);
-    }
-}
-
-template <int NF>
-__global__ __launch_bounds__(256) void k_dlrm_embed(const DlrmArgs a, int64_t nbag_blocks) {
-    if ((int64_t)blockIdx.x < nbag_blocks) dlrm_bags<NF>(a, blockIdx.x);
-    else dlrm_bottom(a, blockIdx.x - nbag_blocks);
-}
-
-__global__ __launch_bounds__(256) void k_dlrm_top(const DlrmArgs a) {
-    __shared__ __attribute__((aligned(16))) float s_z[kTopSamples * kDlrmMaxZ];
-    __shared__ float s_i[kTopSamples * kDlrmMaxPairs];
-    __shared__ float s_t1[kTopSamples * 128];
-    __shared__ float s_t2[kTopSamples * 64];
-    __shared__ uint16_t s_pi[kDlrmMaxPairs], s_pj[kDlrmMaxPairs];
-    const int F = a.S + 1, d = a.dim, zw = F * d;
-    const int np = F * (F + 1) / 2;
-    const int64_t b0 = (int64_t)blockIdx.x * kTopSamples;
-    const int rows = (int)min((int64_t)kTopSamples, a.B - b0);
-    // the pair list in row order: (0,0), (0,1), ..., (F-1,F-1)
-    if (threadIdx.x < F) {
-        const int i = threadIdx.x;
-        int p = i * F - i * (i - 1) / 2;
-        for (int j = i; j < F; ++j, ++p) {
-            s_pi[p] = (uint16_t)i;
-            s_pj[p] = (uint16_t)j;
-        }
-    }
-    const float4* src = (const float4*)(a.z + b0 * (int64_t)zw);
-    float4* dst = (float4*)s_z;
-    for (int idx = threadIdx.x; idx < rows * zw / 4; idx += blockDim.x) dst[idx] = src[idx];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < rows * np; idx += blockDim.x) {
-        const int r = idx / np, p = idx - r * np;
-        const float* zi = s_z + r * zw + s_pi[p] * d;
-        const float* zj = s_z + r * zw + s_pj[p] * d;
-        float acc = 0.f;
-        for (int k = 0; k < d; ++k) acc = fmaf(zi[k], zj[k], acc);
-        s_i[r * np + p] = acc;
-        if (a.inter) a.inter[(b0 + r) * np + p] = acc;
+    for (int idx = threadIdx.x; idx < kDenseSamples * (is - np); idx += kDenseThreads) {
+        const int r = idx / (is - np);
+        s_i[r * is + np + idx - r * (is - np)] = 0.f;           // the pad columns read zeros
     }
     __syncthreads();
-    dense_layer(s_i, np, np, a.wt1, a.bt1, 128, s_t1, 128, rows, true);
+    mfma_layer(s_i, is, np, a.wt1, a.bt1, 128, s_t1, hs, true);
     __syncthreads();
-    dense_layer(s_t1, 128, 128, a.wt2, a.bt2, 64, s_t2, 64, rows, true);
+    mfma_layer(s_t1, hs, 128, a.wt2, a.bt2, 64, s_t2, 64 + 4, true);
     __syncthreads();
     if (threadIdx.x < rows) {
         const int r = threadIdx.x;
         float l = a.bt3;
-        for (int i = 0; i < 64; ++i) l = fmaf(a.wt3[i], s_t2[r * 64 + i], l);
+        for (int i = 0; i < 64; ++i) l = fmaf(a.wt3[i], s_t2[r * (64 + 4) + i], l);
         a.logit[b0 + r] = l;
         if (a.prob) a.prob[b0 + r] = 1.f / (1.f + expf(-l));
     }
@@ -181,25 +278,32 @@ __global__ __launch_bounds__(256) void k_dlrm_top(const DlrmArgs a) {
 
 }  // namespace
 
-hipError_t launch_dlrm_fwd(const DlrmArgs& a, hipStream_t s) {
-    const int64_t nbag_blocks = (int64_t)a.S * ((a.B + 31) / 32);
-    const int64_t nbottom = (a.B + kBottomSamples - 1) / kBottomSamples;
-    const dim3 g1((unsigned)(nbag_blocks + nbottom)), blk(256);
-    switch (a.dim / 32) {
-        case 1: REC_LAUNCH(REC_TIME_DLRM_EMBED, k_dlrm_embed<1>, g1, blk, 0, s, a, nbag_blocks); break;
-        case 2: REC_LAUNCH(REC_TIME_DLRM_EMBED, k_dlrm_embed<2>, g1, blk, 0, s, a, nbag_blocks); break;
-        case 3: REC_LAUNCH(REC_TIME_DLRM_EMBED, k_dlrm_embed<3>, g1, blk, 0, s, a, nbag_blocks); break;
-        case 4: REC_LAUNCH(REC_TIME_DLRM_EMBED, k_dlrm_embed<4>, g1, blk, 0, s, a, nbag_blocks); break;
-        case 5: REC_LAUNCH(REC_TIME_DLRM_EMBED, k_dlrm_embed<5>, g1, blk, 0, s, a, nbag_blocks); break;
-        case 6: REC_LAUNCH(REC_TIME_DLRM_EMBED, k_dlrm_embed<6>, g1, blk, 0, s, a, nbag_blocks); break;
-        case 7: REC_LAUNCH(REC_TIME_DLRM_EMBED, k_dlrm_embed<7>, g1, blk, 0, s, a, nbag_blocks); break;
-        default: REC_LAUNCH(REC_TIME_DLRM_EMBED, k_dlrm_embed<8>, g1, blk, 0, s, a, nbag_blocks); break;
+template <int NF>
+hipError_t launch_dlrm_nf(const DlrmArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)((a.B + kDenseSamples - 1) / kDenseSamples)), blk(kDenseThreads);
+    const DenseLds L = dense_lds(a.S, a.dim, a.n_dense);
+    if (L.bytes > 64 * 1024) {
+        // beyond the default limit of dynamic LDS (at most about 100 KiB within
+        // rec_dlrm_fwd's limits)
+        const hipError_t e = hipFuncSetAttribute((const void*)k_dlrm_fwd<NF>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, L.bytes);
+        if (e != hipSuccess) return e;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const dim3 g2((unsigned)((a.B + kTopSamples - 1) / kTopSamples));
-    REC_LAUNCH(REC_TIME_DLRM_TOP, k_dlrm_top, g2, blk, 0, s, a);
+    REC_LAUNCH(REC_TIME_DLRM_FWD, k_dlrm_fwd<NF>, grid, blk, (size_t)L.bytes, s, a);
     return hipGetLastError();
+}
+
+hipError_t launch_dlrm_fwd(const DlrmArgs& a, hipStream_t s) {
+    switch (a.dim / 32) {
+        case 1: return launch_dlrm_nf<1>(a, s);
+        case 2: return launch_dlrm_nf<2>(a, s);
+        case 3: return launch_dlrm_nf<3>(a, s);
+        case 4: return launch_dlrm_nf<4>(a, s);
+        case 5: return launch_dlrm_nf<5>(a, s);
+        case 6: return launch_dlrm_nf<6>(a, s);
+        case 7: return launch_dlrm_nf<7>(a, s);
+        default: return launch_dlrm_nf<8>(a, s);
+    }
 }
 
 }  // namespace rec

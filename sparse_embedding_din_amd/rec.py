@@ -20,7 +20,7 @@ REC_DIRECT, REC_HASH = 0, 1
 REC_F32, REC_BF16, REC_BF16_PACKED = 0, 1, 2
 REC_SCORE_NONE, REC_SCORE_STEP, REC_SCORE_LFU = 0, 1, 2
 (REC_TIME_DIN_ATTN, REC_TIME_GATHER, REC_TIME_SUMS, REC_TIME_TOWERS,
- REC_TIME_DLRM_INTERACT, REC_TIME_DLRM_EMBED, REC_TIME_DLRM_TOP, REC_TIME_KINDS) = range(8)
+ REC_TIME_DLRM_INTERACT, REC_TIME_DLRM_FWD, REC_TIME_KINDS) = range(7)
 REC_POOL_SUM, REC_POOL_MEAN = 0, 1
 REC_DIN_PACKED_BYTES = 106496
 REC_TOWER_PACKED_BYTES = 614400
