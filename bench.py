@@ -1117,6 +1117,50 @@ def main():
               f"{dlrm['gb_s']:.0f} GB/s of algorithmic bytes", file=sys.stderr, flush=True)
         del keep, zbuf
 
+    dlrm_wide = None
+    if not a.no_dlrm:
+        # The interaction's measured shape as a whole model: 216 tables of width
+        # 96 and the dense vector (217 features), B = 4096; z and the
+        # interaction output go through memory.
+        wcfg = synth.DLRM_WORKLOADS[3]
+        wm = synth.make_dlrm(wcfg)
+        wb = synth.make_dlrm_batch(wm)
+        to = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
+        wkeep = [to(t) for t in wm.tables] + [to(getattr(wm, k)) for k in
+                                              ("wb1", "bb1", "wb2", "bb2", "wt1", "bt1", "wt2", "bt2", "wt3")]
+        Sw, dw = len(wm.tables), wcfg.dim
+        Fw = Sw + 1
+        npw = Fw * (Fw + 1) // 2
+        wmlp = R.dlrm_mlp(wcfg.n_dense, dw, Sw, *wkeep[Sw:], wm.bt3)
+        wtabs = [R.table(R.REC_DIRECT, t.shape[0], wkeep[i], dim=dw) for i, t in enumerate(wm.tables)]
+        Bw = wb.B
+        woff = to(np.concatenate([[0], np.cumsum(wb.lengths.astype(np.int64))[:-1]]))
+        wd, wv, wl = to(wb.dense), to(wb.values), to(wb.lengths)
+        wz = torch.empty(Bw, Fw, dw, dtype=torch.float32, device=dev)
+        wi = torch.empty(Bw, npw, dtype=torch.float32, device=dev)
+        wlg, wpr = torch.empty(Bw, dtype=torch.float32, device=dev), torch.empty(Bw, dtype=torch.float32, device=dev)
+
+        def wide_call(r=0):
+            R.rec_dlrm_fwd(wmlp, wtabs, list(wm.modes), Bw, wd, wv, wl, woff, wz, wi, wlg, wpr,
+                           stream=stream)
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                wide_call()
+            torch.cuda.synchronize()
+        wk, wcall = timed(wide_call, {"top": R.REC_TIME_DLRM_FWD}, 10)
+        w_flops = Bw * 2.0 * (wcfg.n_dense * 128 + 128 * dw + npw * dw + npw * 128 + 128 * 64 + 64)
+        dlrm_wide = {"entry": "rec_dlrm_fwd, wide model (z and the interaction through memory)",
+                     "workload": f"{wcfg.name}: B={Bw}, 216 tables of {wcfg.sizes[0]} rows, width {dw}, "
+                                 f"bags 1-{wcfg.bag_max} ids, {npw} pairs per sample",
+                     "call_us": wcall, "top_mlp_us": wk["top"],
+                     "samples_s": round(Bw / (wcall["mean"] * 1e-6), 1),
+                     "flops": w_flops, "tflops": round(w_flops / (wcall["mean"] * 1e-6) / 1e12, 2),
+                     "pages": "1.8 ms per forward of the 217 x 96 interaction on a V100, batch not given "
+                              "(context, another machine)"}
+        print(f"[bench] DLRM wide (217 features): {wcall['mean']:.1f} us per call of {Bw} samples "
+              f"(top MLP {wk['top']['mean']:.1f} us)", file=sys.stderr, flush=True)
+        del wkeep, wz, wi
+
     # `value` is whole-job throughput: with two batches in flight when that is
     # faster (every step is still one whole pass over one resident batch).
     single = {"ms_per_step": round(ms_per_step, 5), "gpu_ms_per_step": round(gpu_ms, 5),
@@ -1165,6 +1209,7 @@ def main():
         "din_bwd": din_bwd,
         "dlrm_interaction": interaction,
         "dlrm_forward": dlrm,
+        "dlrm_wide": dlrm_wide,
         "src_hash": shash,
     }
     if a.calibrate_copy:

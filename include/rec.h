@@ -376,7 +376,8 @@ rec_status rec_dlrm_interact(const float* z, int64_t B, int32_t F, int32_t d, fl
  * embedding width, per-feature EmbeddingBags pool the sparse ids, the
  * interaction layer takes the dot product of every pair (one triangle only),
  * a top MLP turns the dot products into the prediction; §3.2 a bag pools by
- * sum or by mean; §3.3, §4.2 the widths and the pair order, j running from i).
+ * sum or by mean; §3.3, §4.2 the widths and the pair order, j running from i;
+ * §3.1 the measured interaction of 217 features of width 96).
  * For sample b:
  *   h     = relu(wb2 relu(wb1 dense[b] + bb1) + bb2)        (d)
  *   e_t   = sum over bag (t, b) of table t's rows (REC_POOL_SUM), or that sum
@@ -390,7 +391,7 @@ rec_status rec_dlrm_interact(const float* z, int64_t B, int32_t F, int32_t d, fl
 typedef struct {
     int32_t n_dense;              /* dense features, 1..128 */
     int32_t dim;                  /* d: table width = bottom output, 32..256, multiple of 32 */
-    int32_t S;                    /* sparse features (tables), 1..31; (S+1)*dim <= 1024 */
+    int32_t S;                    /* sparse features (tables), 1..255 */
     int32_t reserved;
     const float* wb1;             /* [128][n_dense] (torch.nn.Linear.weight layout) */
     const float* bb1;             /* [128] */
@@ -415,12 +416,19 @@ typedef struct {
  *            lengths[t*B+b])), e.g. from rec_lengths_to_offsets
  *   z        fp32 [B][S+1][dim], 16-byte aligned: written (the interaction
  *            input: bottom output first, then the bags in table order)
- *   inter    fp32 [B][(S+1)(S+2)/2] or NULL: the interaction output
+ *   inter    fp32 [B][(S+1)(S+2)/2] or NULL: the interaction output (required
+ *            for a wide model, below)
  *   logit    fp32 [B];  prob fp32 [B] or NULL
- * One launch.
+ * S <= 31 and (S+1)*dim <= 1024: one launch, z held on chip per workgroup.
+ * Otherwise (a wide model, e.g. 216 tables of width 96: the 217-feature
+ * interaction) z and the interaction output go through memory: the bags
+ * (one launch per 32 tables), the bottom MLP, the interaction (as
+ * rec_dlrm_interact, whose limits apply: 32 * ceil((S+1)/32) rows of about
+ * dim + 4 floats within 144 KiB, e.g. dim <= 160 at S = 216) and the top MLP.
  * Errors: REC_EINVAL (null required pointers, misalignment, B < 0, a table
  * that is not direct or whose dim differs, unknown mode, sizes outside the
- * limits above).  B == 0 is a no-op.
+ * limits above, inter NULL for a wide model), REC_EUNSUPPORTED (a wide model
+ * beyond the interaction's LDS stage).  B == 0 is a no-op.
  */
 rec_status rec_dlrm_fwd(const rec_dlrm_mlp* mlp, const rec_table* tables, const int32_t* modes,
                         int64_t B, const float* dense, const int64_t* values,
@@ -830,7 +838,8 @@ rec_status rec_din_attn_bwd(const rec_table* seq_tables, const int64_t* seq_valu
  *                           rec_sparse_din_fwd)
  *   REC_TIME_TOWERS         the bf16 towers (rec_towers_fwd)
  *   REC_TIME_DLRM_INTERACT  the interaction (rec_dlrm_interact)
- *   REC_TIME_DLRM_FWD       rec_dlrm_fwd (one launch)
+ *   REC_TIME_DLRM_FWD       rec_dlrm_fwd's launch (for a wide model, the last
+ *                           of its launches: the top MLP)
  * The events (created by the caller with timing enabled, on the device of
  * the launch) are used by one launch and then forgotten; start == stop ==
  * NULL forgets them without a launch.  The setting is thread-local state of

@@ -6,6 +6,8 @@
 #include <mutex>
 #include <string>
 
+#include <vector>
+
 #include "rec_internal.h"
 
 using namespace rec;
@@ -552,10 +554,12 @@ rec_status rec_dlrm_fwd(const rec_dlrm_mlp* mlp, const rec_table* tables, const 
     if (!mlp || !tables || !modes) return fail(REC_EINVAL, f + ": mlp, tables and modes are required");
     if (B < 0) return fail(REC_EINVAL, f + ": B < 0");
     const int32_t S = mlp->S, d = mlp->dim, nd = mlp->n_dense;
-    if (S < 1 || S > 31) return fail(REC_EINVAL, f + ": S outside [1, 31]");
+    if (S < 1 || S > kDlrmMaxTables) return fail(REC_EINVAL, f + ": S outside [1, 255]");
     if (d < 32 || d > 256 || d % 32) return fail(REC_EINVAL, f + ": dim must be a multiple of 32 in [32, 256]");
     if (nd < 1 || nd > kDlrmMaxDense) return fail(REC_EINVAL, f + ": n_dense outside [1, 128]");
-    if ((S + 1) * d > kDlrmMaxZ) return fail(REC_EINVAL, f + ": (S + 1) * dim above 1024");
+    const bool wide = S > kDlrmMaxTablesFused || (S + 1) * d > kDlrmMaxZ;
+    if (wide && (int64_t)32 * ((S + 1 + 31) / 32) * dlrm_stride(d) > kDlrmMaxLdsFloats)
+        return fail(REC_EUNSUPPORTED, f + ": (S + 1) x dim does not fit the interaction's 144 KiB LDS stage");
     const void* arrays[] = {mlp->wb1, mlp->bb1, mlp->wb2, mlp->bb2, mlp->wt1, mlp->bt1, mlp->wt2,
                             mlp->bt2, mlp->wt3};
     for (const void* p : arrays) {
@@ -564,6 +568,8 @@ rec_status rec_dlrm_fwd(const rec_dlrm_mlp* mlp, const rec_table* tables, const 
     }
     DlrmArgs a;
     memset(&a, 0, sizeof(a));
+    std::vector<TabDev> tabs((size_t)S);
+    std::vector<int32_t> md((size_t)S);
     for (int t = 0; t < S; ++t) {
         const rec_table& tb = tables[t];
         if (tb.kind != REC_DIRECT) return fail(REC_EINVAL, f + ": tables must be REC_DIRECT");
@@ -571,16 +577,22 @@ rec_status rec_dlrm_fwd(const rec_dlrm_mlp* mlp, const rec_table* tables, const 
         if (tb.rows < 1) return fail(REC_EINVAL, f + ": rows must be >= 1");
         if (!tb.values || !aligned16(tb.values)) return fail(REC_EINVAL, f + ": table values NULL or misaligned");
         if (modes[t] != REC_POOL_SUM && modes[t] != REC_POOL_MEAN) return fail(REC_EINVAL, f + ": unknown mode");
-        a.tab[t].values = tb.values;
-        a.tab[t].rows = tb.rows;
-        a.tab[t].kind = REC_DIRECT;
-        floor_mod_prepare(tb.rows, &a.tab[t].magic, &a.tab[t].shift);
-        a.mode[t] = modes[t];
+        memset(&tabs[t], 0, sizeof(TabDev));
+        tabs[t].values = tb.values;
+        tabs[t].rows = tb.rows;
+        tabs[t].kind = REC_DIRECT;
+        floor_mod_prepare(tb.rows, &tabs[t].magic, &tabs[t].shift);
+        md[t] = modes[t];
+        if (t < 32) {
+            a.tab[t] = tabs[t];
+            a.mode[t] = md[t];
+        }
     }
     if (B == 0) return ok();
     if (!dense || !values || !lengths || !offsets || !z || !logit)
         return fail(REC_EINVAL, f + ": dense, values, lengths, offsets, z and logit are required");
     if (!aligned16(z)) return fail(REC_EINVAL, f + ": z not 16-byte aligned");
+    if (wide && !inter) return fail(REC_EINVAL, f + ": inter is required for more than 31 tables or (S + 1) * dim above 1024");
     a.B = B;
     a.S = S;
     a.dim = d;
@@ -603,6 +615,11 @@ rec_status rec_dlrm_fwd(const rec_dlrm_mlp* mlp, const rec_table* tables, const 
     a.inter = inter;
     a.logit = logit;
     a.prob = prob;
+    if (wide) {
+        const int cus = num_cus();
+        if (cus < 1) return fail(REC_EHIP, f + ": cannot query the device");
+        return hip_status(launch_dlrm_fwd_wide(a, tabs.data(), md.data(), cus, (hipStream_t)stream), "rec_dlrm_fwd");
+    }
     return hip_status(launch_dlrm_fwd(a, (hipStream_t)stream), "rec_dlrm_fwd");
 }
 

@@ -40,9 +40,9 @@ constexpr int kDenseThreads = 512;            // eight waves: two per SIMD
 // step 4c + j, lane (m, k) takes input 16c + 4k + j, so a lane's four inputs
 // of a chunk are one float4 of its W row (one load covers 16 whole 64-byte
 // row pieces) and one 16-byte LDS read of its activations.
-template <int NU, bool kVec>
+template <int NU, bool kVec, bool kGlobalIn = false>
 __device__ inline void layer_chunks(const float* in, int ins, int nin, const float* wr, int i0, int m,
-                                    int kg, f32x4& acc) {
+                                    int kg, int rows, f32x4& acc) {
     float4 av[NU], bv[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -59,7 +59,19 @@ __device__ inline void layer_chunks(const float* in, int ins, int nin, const flo
             }
             av[u] = make_float4(v[0], v[1], v[2], v[3]);
         }
-        bv[u] = *(const float4*)(in + m * ins + i);
+        if (kGlobalIn) {
+            // activations in memory, rows of nin floats with no alignment;
+            // rows past `rows` re-read the last one (their results are dropped)
+            float x[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float v = in[(int64_t)min(m, rows - 1) * ins + min(i + j, nin - 1)];
+                x[j] = i + j < nin ? v : 0.f;
+            }
+            bv[u] = make_float4(x[0], x[1], x[2], x[3]);
+        } else {
+            bv[u] = *(const float4*)(in + m * ins + i);
+        }
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -70,18 +82,18 @@ __device__ inline void layer_chunks(const float* in, int ins, int nin, const flo
     }
 }
 
-template <bool kVec>
+template <bool kVec, bool kGlobalIn = false>
 __device__ inline void layer_part(const float* in, int ins, int nin, const float* wr, int i0, int nu, int m,
-                                  int kg, f32x4& acc) {
+                                  int kg, int rows, f32x4& acc) {
     switch (nu) {                                          // uniform
-        case 1: layer_chunks<1, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
-        case 2: layer_chunks<2, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
-        case 3: layer_chunks<3, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
-        case 4: layer_chunks<4, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
-        case 5: layer_chunks<5, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
-        case 6: layer_chunks<6, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
-        case 7: layer_chunks<7, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
-        default: layer_chunks<8, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        case 1: layer_chunks<1, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
+        case 2: layer_chunks<2, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
+        case 3: layer_chunks<3, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
+        case 4: layer_chunks<4, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
+        case 5: layer_chunks<5, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
+        case 6: layer_chunks<6, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
+        case 7: layer_chunks<7, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
+        default: layer_chunks<8, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
     }
 }
 
@@ -93,9 +105,10 @@ __device__ inline void layer_part(const float* in, int ins, int nin, const float
 // x 16 rows; the result's lane (n, k) holds units o0 + 4k .. +3 of row n.
 // Wave w takes the 16-unit tiles w, w + 8, ...; up to 8 chunks (128 inputs)
 // of a tile are loaded together ahead of their products.
+template <bool kGlobalIn = false>
 __device__ inline void mfma_layer(const float* in, int ins, int nin, const float* __restrict__ W,
                                   const float* __restrict__ bias, int nout, float* out, int outs,
-                                  bool relu) {
+                                  bool relu, int rows = kDenseSamples) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m = lane & 15, kg = lane >> 4;
     const int nch = (nin + 15) / 16;
     const bool vec = (nin & 3) == 0;                      // W rows are 16-byte aligned
@@ -105,8 +118,8 @@ __device__ inline void mfma_layer(const float* in, int ins, int nin, const float
         const float* wr = W + (int64_t)(o0 + m) * nin;
         for (int c0 = 0; c0 < nch; c0 += 8) {
             const int nu = min(8, nch - c0);
-            if (vec) layer_part<true>(in, ins, nin, wr, 16 * c0, nu, m, kg, acc);
-            else layer_part<false>(in, ins, nin, wr, 16 * c0, nu, m, kg, acc);
+            if (vec) layer_part<true, kGlobalIn>(in, ins, nin, wr, 16 * c0, nu, m, kg, rows, acc);
+            else layer_part<false, kGlobalIn>(in, ins, nin, wr, 16 * c0, nu, m, kg, rows, acc);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -116,13 +129,59 @@ __device__ inline void mfma_layer(const float* in, int ins, int nin, const float
     }
 }
 
+// One bag's pooled row, lane c of its eight holding float4 columns c, c + 8,
+// ... (len 0 for a lane without a bag; the loop runs while any bag of the wave
+// has ids left).
+template <int NF>
+__device__ inline void bag_pool(const DlrmArgs& a, const TabDev& tab, int32_t mode, int64_t bag, int32_t len,
+                                int c, float4 (&acc)[NF]) {
+    const int d = a.dim;
+    const int64_t off = a.offsets[bag];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[f] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0; __ballot(j0 < len) != 0; j0 += kIdRound) {
+        int64_t row[kIdRound];
+#pragma unroll
+        for (int u = 0; u < kIdRound; ++u) {
+            const int64_t raw = a.values[len > 0 ? off + min(j0 + u, len - 1) : 0];
+            row[u] = floor_mod_magic(raw, tab.rows, tab.magic, tab.shift);
+        }
+        float4 v[kIdRound][NF];
+#pragma unroll
+        for (int u = 0; u < kIdRound; ++u) {
+            const float4* src = (const float4*)(tab.values + row[u] * d) + c;
+#pragma unroll
+            for (int f = 0; f < NF; ++f) v[u][f] = src[8 * f];
+        }
+#pragma unroll
+        for (int u = 0; u < kIdRound; ++u) {
+            const bool use = j0 + u < len;
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                acc[f].x += use ? v[u][f].x : 0.f;
+                acc[f].y += use ? v[u][f].y : 0.f;
+                acc[f].z += use ? v[u][f].z : 0.f;
+                acc[f].w += use ? v[u][f].w : 0.f;
+            }
+        }
+    }
+    if (mode == REC_POOL_MEAN && len > 0) {
+        const float inv = 1.f / (float)len;
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            acc[f].x *= inv;
+            acc[f].y *= inv;
+            acc[f].z *= inv;
+            acc[f].w *= inv;
+        }
+    }
+}
+
 // The bags of the workgroup's samples b0 .. b0 + rows - 1 into z in LDS
-// (row stride zs, vector t + 1 = bag (t, b)): eight lanes per bag, lane c of a
-// bag holding float4 columns c, c + 8, ... of each row.
+// (row stride zs, vector t + 1 = bag (t, b)).
 template <int NF>
 __device__ inline void bags_into_lds(const DlrmArgs& a, int64_t b0, int rows, float* s_z, int zs) {
     const int lane = threadIdx.x & 63, c = lane & 7;
-    const int d = a.dim;
     const int nq = kDenseSamples * a.S;                      // bags of the workgroup
     for (int q0 = (int)(threadIdx.x >> 6) * 8; q0 < nq; q0 += kDenseThreads / kBagLanes) {
         // q0 is a multiple of 8, so the wave's eight bags share their table
@@ -130,52 +189,12 @@ __device__ inline void bags_into_lds(const DlrmArgs& a, int64_t b0, int rows, fl
         const int r = q % kDenseSamples;
         const int t = __builtin_amdgcn_readfirstlane(q0 / kDenseSamples);
         const bool live = q < nq && r < rows;
-        const int64_t b = b0 + (live ? r : 0);
-        const int64_t bag = (int64_t)t * a.B + b;
-        const TabDev& tab = a.tab[t];
+        const int64_t bag = (int64_t)t * a.B + b0 + (live ? r : 0);
         const int32_t len = live ? a.lengths[bag] : 0;
-        const int64_t off = a.offsets[bag];
         float4 acc[NF];
-#pragma unroll
-        for (int f = 0; f < NF; ++f) acc[f] = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j0 = 0; __ballot(j0 < len) != 0; j0 += kIdRound) {
-            int64_t row[kIdRound];
-#pragma unroll
-            for (int u = 0; u < kIdRound; ++u) {
-                const int64_t raw = a.values[len > 0 ? off + min(j0 + u, len - 1) : 0];
-                row[u] = floor_mod_magic(raw, tab.rows, tab.magic, tab.shift);
-            }
-            float4 v[kIdRound][NF];
-#pragma unroll
-            for (int u = 0; u < kIdRound; ++u) {
-                const float4* src = (const float4*)(tab.values + row[u] * d) + c;
-#pragma unroll
-                for (int f = 0; f < NF; ++f) v[u][f] = src[8 * f];
-            }
-#pragma unroll
-            for (int u = 0; u < kIdRound; ++u) {
-                const bool use = j0 + u < len;
-#pragma unroll
-                for (int f = 0; f < NF; ++f) {
-                    acc[f].x += use ? v[u][f].x : 0.f;
-                    acc[f].y += use ? v[u][f].y : 0.f;
-                    acc[f].z += use ? v[u][f].z : 0.f;
-                    acc[f].w += use ? v[u][f].w : 0.f;
-                }
-            }
-        }
+        bag_pool<NF>(a, a.tab[t], a.mode[t], bag, len, c, acc);
         if (!live) continue;
-        if (a.mode[t] == REC_POOL_MEAN && len > 0) {
-            const float inv = 1.f / (float)len;
-#pragma unroll
-            for (int f = 0; f < NF; ++f) {
-                acc[f].x *= inv;
-                acc[f].y *= inv;
-                acc[f].z *= inv;
-                acc[f].w *= inv;
-            }
-        }
-        float4* o = (float4*)(s_z + r * zs + (1 + t) * d) + c;
+        float4* o = (float4*)(s_z + r * zs + (1 + t) * a.dim) + c;
 #pragma unroll
         for (int f = 0; f < NF; ++f) o[8 * f] = acc[f];
     }
@@ -278,6 +297,93 @@ __global__ __launch_bounds__(kDenseThreads, 4) void k_dlrm_fwd(const DlrmArgs a)
 
 }  // namespace
 
+// Wide models (more than 31 tables, or (S + 1) * d above 1024 floats per
+// sample): z and the interaction output go through memory.  Launches: the
+// bags, up to 32 tables per launch (a table group's descriptors are
+// a.tab[0 .. nt)); the bottom MLP; the interaction (rec_dlrm.hip); the top
+// MLP, whose first layer reads its inputs from memory.
+template <int NF>
+__global__ __launch_bounds__(256) void k_dlrm_bags_wide(const DlrmArgs a, int t0) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t nbw = (a.B + 31) / 32;                  // 32-sample chunks per table
+    const int t = (int)(blockIdx.x / nbw);                 // table of the group
+    const int64_t b = (blockIdx.x % nbw) * 32 + wave * kBagLanes + (lane >> 3);
+    const bool live = b < a.B;
+    const int64_t bag = (int64_t)(t0 + t) * a.B + (live ? b : 0);
+    const int32_t len = live ? a.lengths[bag] : 0;
+    float4 acc[NF];
+    bag_pool<NF>(a, a.tab[t], a.mode[t], bag, len, lane & 7, acc);
+    if (!live) return;
+    float4* o = (float4*)(a.z + (b * (int64_t)(a.S + 1) + 1 + t0 + t) * a.dim) + (lane & 7);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) o[8 * f] = acc[f];
+}
+
+__global__ __launch_bounds__(kDenseThreads) void k_dlrm_bottom(const DlrmArgs a) {
+    constexpr int kXs = kDlrmMaxDense + 4, kHs = 128 + 4, kOs = 256 + 4;
+    __shared__ __attribute__((aligned(16))) float s_x[kDenseSamples * kXs];
+    __shared__ __attribute__((aligned(16))) float s_h[kDenseSamples * kHs];
+    __shared__ __attribute__((aligned(16))) float s_o[kDenseSamples * kOs];
+    const int64_t b0 = (int64_t)blockIdx.x * kDenseSamples;
+    const int rows = (int)min((int64_t)kDenseSamples, a.B - b0);
+    const int xs = round16(a.n_dense) + 4;
+    for (int idx = threadIdx.x; idx < kDenseSamples * xs; idx += kDenseThreads) {
+        const int r = idx / xs, i = idx - r * xs;
+        const bool ok = r < rows && i < a.n_dense;
+        const float v = a.dense[ok ? (b0 + r) * a.n_dense + i : 0];
+        s_x[idx] = ok ? v : 0.f;
+    }
+    __syncthreads();
+    mfma_layer(s_x, xs, a.n_dense, a.wb1, a.bb1, 128, s_h, kHs, true);
+    __syncthreads();
+    mfma_layer(s_h, kHs, 128, a.wb2, a.bb2, a.dim, s_o, kOs, true);
+    __syncthreads();
+    const int d4 = a.dim / 4;
+    for (int idx = threadIdx.x; idx < rows * d4; idx += kDenseThreads) {
+        const int r = idx / d4, c = idx - r * d4;
+        ((float4*)(a.z + (b0 + r) * (int64_t)(a.S + 1) * a.dim))[c] = *(const float4*)(s_o + r * kOs + 4 * c);
+    }
+}
+
+__global__ __launch_bounds__(kDenseThreads) void k_dlrm_top_wide(const DlrmArgs a) {
+    constexpr int kHs = 128 + 4, kT2s = 64 + 4;
+    __shared__ __attribute__((aligned(16))) float s_t1[kDenseSamples * kHs];
+    __shared__ __attribute__((aligned(16))) float s_t2[kDenseSamples * kT2s];
+    const int F = a.S + 1;
+    const int64_t np = (int64_t)F * (F + 1) / 2;
+    const int64_t b0 = (int64_t)blockIdx.x * kDenseSamples;
+    const int rows = (int)min((int64_t)kDenseSamples, a.B - b0);
+    // rows past the batch re-read the last sample (their results are dropped)
+    mfma_layer<true>(a.inter + b0 * np, (int)np, (int)np, a.wt1, a.bt1, 128, s_t1, kHs, true, rows);
+    __syncthreads();
+    mfma_layer(s_t1, kHs, 128, a.wt2, a.bt2, 64, s_t2, kT2s, true);
+    __syncthreads();
+    if (threadIdx.x < rows) {
+        const int r = threadIdx.x;
+        float l = a.bt3;
+        for (int i = 0; i < 64; ++i) l = fmaf(a.wt3[i], s_t2[r * kT2s + i], l);
+        a.logit[b0 + r] = l;
+        if (a.prob) a.prob[b0 + r] = 1.f / (1.f + expf(-l));
+    }
+}
+
+template <int NF>
+hipError_t launch_bags_wide(const DlrmArgs& a, const TabDev* tabs, const int32_t* modes, hipStream_t s) {
+    const int64_t nbw = (a.B + 31) / 32;
+    for (int t0 = 0; t0 < a.S; t0 += 32) {
+        DlrmArgs g = a;
+        const int nt = min(32, a.S - t0);
+        for (int t = 0; t < nt; ++t) {
+            g.tab[t] = tabs[t0 + t];
+            g.mode[t] = modes[t0 + t];
+        }
+        hipLaunchKernelGGL(k_dlrm_bags_wide<NF>, dim3((unsigned)(nt * nbw)), dim3(256), 0, s, g, t0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 template <int NF>
 hipError_t launch_dlrm_nf(const DlrmArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)((a.B + kDenseSamples - 1) / kDenseSamples)), blk(kDenseThreads);
@@ -290,6 +396,30 @@ hipError_t launch_dlrm_nf(const DlrmArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     REC_LAUNCH(REC_TIME_DLRM_FWD, k_dlrm_fwd<NF>, grid, blk, (size_t)L.bytes, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dlrm_fwd_wide(const DlrmArgs& a, const TabDev* tabs, const int32_t* modes, int num_cus,
+                                hipStream_t s) {
+    hipError_t e;
+    switch (a.dim / 32) {
+        case 1: e = launch_bags_wide<1>(a, tabs, modes, s); break;
+        case 2: e = launch_bags_wide<2>(a, tabs, modes, s); break;
+        case 3: e = launch_bags_wide<3>(a, tabs, modes, s); break;
+        case 4: e = launch_bags_wide<4>(a, tabs, modes, s); break;
+        case 5: e = launch_bags_wide<5>(a, tabs, modes, s); break;
+        case 6: e = launch_bags_wide<6>(a, tabs, modes, s); break;
+        case 7: e = launch_bags_wide<7>(a, tabs, modes, s); break;
+        default: e = launch_bags_wide<8>(a, tabs, modes, s); break;
+    }
+    if (e != hipSuccess) return e;
+    const dim3 grid((unsigned)((a.B + kDenseSamples - 1) / kDenseSamples)), blk(kDenseThreads);
+    hipLaunchKernelGGL(k_dlrm_bottom, grid, blk, 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_dlrm_interact(a.z, a.B, a.S + 1, a.dim, a.inter, num_cus, s);
+    if (e != hipSuccess) return e;
+    REC_LAUNCH(REC_TIME_DLRM_FWD, k_dlrm_top_wide, grid, blk, 0, s, a);
     return hipGetLastError();
 }
 

@@ -413,6 +413,12 @@ struct DlrmArgs {
     float* prob;
 };
 hipError_t launch_dlrm_fwd(const DlrmArgs& a, hipStream_t s);
+// More than kDlrmMaxTablesFused tables or (S + 1) * d above kDlrmMaxZ: z and
+// the interaction output through memory; tabs/modes hold all S tables.
+constexpr int kDlrmMaxTablesFused = 31;
+constexpr int kDlrmMaxTables = 255;
+hipError_t launch_dlrm_fwd_wide(const DlrmArgs& a, const TabDev* tabs, const int32_t* modes, int num_cus,
+                                hipStream_t s);
 // Sparse backward + AdaGrad (rec_bwd.hip).  One table: its lookup
 // descriptor (direct floor-mod constants or hash keys/digests), the arrays
 // the step writes, and its first row in the flat row space of all tables.

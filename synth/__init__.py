@@ -443,6 +443,9 @@ class DlrmConfig:
 DLRM_WORKLOADS: Dict[int, DlrmConfig] = {
     1: DlrmConfig(101, "dlrm_sum_B8192", 8192),
     2: DlrmConfig(102, "dlrm_mixed_B8192", 8192, modes=(0, 1, 0, 1, 0, 1, 0, 1)),
+    # the interaction's measured shape (217 features of width 96): 216 tables
+    # (their sizes are not given; 5000 rows each here) and the dense vector
+    3: DlrmConfig(103, "dlrm_wide_F217_B4096", 4096, sizes=(5000,) * 216, modes=(0,) * 216),
 }
 
 

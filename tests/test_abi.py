@@ -646,14 +646,20 @@ def test_dlrm_fwd_errors(lib):
     assert call(tables=None)[0] == R.REC_EINVAL
     assert call(md=None)[0] == R.REC_EINVAL
     assert call(B=-1)[0] == R.REC_EINVAL
-    for kw in (dict(S=0), dict(S=32), dict(dim=48), dict(dim=16), dict(dim=288), dict(n_dense=0),
+    for kw in (dict(S=0), dict(S=256), dict(dim=48), dict(dim=16), dict(dim=288), dict(n_dense=0),
                dict(n_dense=129)):
         m = R.dlrm_mlp(kw.get("n_dense", nd), kw.get("dim", d), kw.get("S", S), *([FAKE] * 9), 0.0)
         s, msg = call(mlp=m, tables=[_table(rows=100, dim=kw.get("dim", d))] * max(kw.get("S", S), 1),
                       md=[0] * max(kw.get("S", S), 1))
         assert s == R.REC_EINVAL, kw
+    # wide models ((S+1) * dim above 1024, or more than 31 tables) need inter
     m = R.dlrm_mlp(nd, 128, 8, *([FAKE] * 9), 0.0)               # (S+1) * dim = 1152 > 1024
     assert call(mlp=m, tables=[_table(rows=100, dim=128)] * 8)[0] == R.REC_EINVAL
+    m = R.dlrm_mlp(nd, 96, 216, *([FAKE] * 9), 0.0)              # the 217-feature model
+    assert call(mlp=m, tables=[_table(rows=100, dim=96)] * 216, md=[0] * 216)[0] == R.REC_EINVAL
+    m = R.dlrm_mlp(nd, 224, 216, *([FAKE] * 9), 0.0)             # beyond the interaction's LDS stage
+    s, msg = call(mlp=m, tables=[_table(rows=100, dim=224)] * 216, md=[0] * 216, inter=FAKE)
+    assert s == R.REC_EUNSUPPORTED, msg
     m = R.dlrm_mlp(nd, d, S, *([FAKE] * 8), None, 0.0)
     assert call(mlp=m)[0] == R.REC_EINVAL
     m = R.dlrm_mlp(nd, d, S, FAKE_ODD, *([FAKE] * 8), 0.0)

@@ -5,7 +5,9 @@ interaction output and the logit against the size of their terms, the
 probability; the essay's example model (13 dense features, 8 tables, d = 96)
 at B = 8192 with all-sum and with mixed sum/mean bags; ragged and one-sample
 batches, empty bags, other widths and table counts; the same call twice,
-bit-identical."""
+bit-identical; wide models (z and the interaction through memory): the
+217-feature shape (216 tables of width 96) on a small batch and, at B = 4096,
+on sampled rows, and models wide by their table count or their width."""
 import dataclasses
 
 import numpy as np
@@ -105,3 +107,49 @@ def test_dlrm_fwd_deterministic():
     a, c = _gpu(m, b), _gpu(m, b)
     for k in a:
         assert np.array_equal(a[k].view(np.uint32), c[k].view(np.uint32)), k
+
+
+def _sub_batch(m, b, idx):
+    """The samples idx of batch b as a batch of their own (key-major)."""
+    S, B = len(m.tables), b.B
+    L = b.lengths.reshape(S, B)
+    starts = np.concatenate([[0], np.cumsum(b.lengths.astype(np.int64))])
+    vals = [b.values[starts[t * B + i]: starts[t * B + i] + L[t, i]] for t in range(S) for i in idx]
+    return synth.DlrmBatch(len(idx), b.dense[idx], L[:, idx].reshape(-1).copy(),
+                           np.concatenate(vals) if vals else np.zeros(0, np.int64))
+
+
+def test_dlrm_fwd_wide_217_small():
+    cfg = dataclasses.replace(synth.DLRM_WORKLOADS[3], sizes=tuple(20 + 7 * t for t in range(216)),
+                              modes=(0, 1) * 108)
+    m = synth.make_dlrm(cfg, bias=True)
+    b = synth.make_dlrm_batch(m, B=40)
+    _check(m, b, "F=217 d=96")
+
+
+@pytest.mark.parametrize("sizes,dim,modes", [((50,) * 40, 32, (1, 0) * 20),     # 40 tables
+                                             ((300,) * 12, 96, (0,) * 12)])      # (S+1) * d = 1248
+def test_dlrm_fwd_wide_by_tables_or_width(sizes, dim, modes):
+    cfg = dataclasses.replace(synth.DLRM_WORKLOADS[1], sizes=sizes, dim=dim, modes=modes)
+    m = synth.make_dlrm(cfg, bias=True, emb_scale=4.0)
+    b = synth.make_dlrm_batch(m, B=77)
+    _check(m, b, f"wide S={len(sizes)} d={dim}")
+
+
+def test_dlrm_fwd_wide_217_B4096_sampled():
+    """The 217-feature model at B = 4096 (the interaction's measured shape):
+    the oracle on 12 samples spread over the batch, compared row by row."""
+    cfg = dataclasses.replace(synth.DLRM_WORKLOADS[3], sizes=(500,) * 216)
+    m = synth.make_dlrm(cfg, bias=True)
+    b = synth.make_dlrm_batch(m)
+    got = _gpu(m, b)
+    idx = np.array([0, 1, 15, 16, 17, 1000, 2047, 2048, 3000, 4078, 4094, 4095])
+    sub = _sub_batch(m, b, idx)
+    ref = oracle.get().dlrm_fwd(m, sub.dense, sub.values, sub.lengths)
+    F = len(m.tables) + 1
+    ez = row_rel_err(got["z"][idx].reshape(len(idx) * F, -1), ref["z"].reshape(len(idx) * F, -1))
+    ei = float(np.max(np.abs(got["inter"][idx] - ref["inter"]) / np.maximum(ref["iscale"], 1e-30)))
+    el = float(np.max(np.abs(got["logit"][idx] - ref["logit"]) / np.maximum(ref["lscale"], 1e-30)))
+    say(f"dlrm fwd F=217 B=4096 sampled: z {ez:.1e}, interaction {ei:.1e}, logit {el:.1e}")
+    assert ez <= FP32_TOL and ei <= FP32_TOL and el <= FP32_TOL
+    assert np.all(np.isfinite(got["logit"])) and np.all((got["prob"] > 0) & (got["prob"] < 1))
