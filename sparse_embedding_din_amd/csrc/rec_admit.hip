@@ -37,6 +37,11 @@
 // Integer atomics only: every value stored, every count, the set of victims
 // and of admitted ids are the same run to run; which free slot a new id
 // takes may depend on the order of concurrent claims (lookups do not).
+// Probes read slots with cached (workgroup-scope) loads: within a launch a
+// slot only goes from free to a key, and a key that was stored before the
+// launch never moves, so a stale read can only show a now-taken slot as
+// free; the compare-and-swap that follows then fails and reports the key
+// that is there.  A device-scope load per probe went to memory every time.
 #include <limits.h>
 
 #include "rec_internal.h"
@@ -56,7 +61,7 @@ __device__ inline bool holds_key(int64_t k) { return !reserved_key(k); }
 __device__ inline int64_t set_entry(const AdmitArgs& a, int64_t key, bool insert) {
     int64_t e = (int64_t)(mix64((uint64_t)key) & (uint64_t)(a.nset - 1));
     for (int64_t probes = 0; probes < a.nset; ++probes) {
-        int64_t cur = __hip_atomic_load(a.set_key + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int64_t cur = __hip_atomic_load(a.set_key + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (cur == key) return e;
         if (cur == REC_EMPTY_KEY) {
             if (!insert) return -1;
@@ -76,7 +81,7 @@ __device__ inline int64_t set_entry(const AdmitArgs& a, int64_t key, bool insert
 __device__ inline int64_t counter_slot(const AdmitArgs& a, int64_t key, bool claim) {
     int64_t at = hash_home(mix64((uint64_t)key), a.ccap);
     for (int64_t probes = 0; probes < a.ccap; ++probes) {
-        const int64_t cur = __hip_atomic_load(a.ckeys + at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int64_t cur = __hip_atomic_load(a.ckeys + at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (cur == key) return at;
         if (cur == REC_EMPTY_KEY) {
             if (!claim) return -1;
@@ -264,7 +269,7 @@ __global__ __launch_bounds__(256) void k_admit_insert(const AdmitArgs a) {
     const uint64_t h = mix64((uint64_t)key);
     int64_t at = hash_home(h, a.capacity), slot = -1;
     for (int64_t probes = 0; probes < a.capacity; ++probes) {
-        int64_t cur = __hip_atomic_load(a.keys + at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        int64_t cur = __hip_atomic_load(a.keys + at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (cur == REC_EMPTY_KEY || cur == REC_TOMBSTONE_KEY) {
             if (__hip_atomic_compare_exchange_strong(a.keys + at, &cur, key, __ATOMIC_RELAXED,
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {

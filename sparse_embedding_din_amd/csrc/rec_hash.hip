@@ -12,7 +12,8 @@
 //      take the same slot, and a lane that loses the swap to its own key (a
 //      duplicate in the batch) has found it.  Keys only ever go from empty to
 //      a key, so a stale read can only show a slot as empty; the swap then
-//      fails and reports the key that is there.  The winner writes the
+//      fails and reports the key that is there (so the probe reads are
+//      cached, workgroup-scope loads).  The winner writes the
 //      digest; scores are updated (STEP: every lane writes the same step;
 //      LFU: one atomic add per pair).  With no empty slot on the whole
 //      sequence the pair is not stored (no eviction).  The same launch
@@ -40,7 +41,7 @@ __global__ __launch_bounds__(256) void k_hash_insert(const HashInsArgs a) {
         bool claimed = false;
         slot = -1;
         for (int64_t probes = 0; probes < a.capacity; ++probes) {
-            const int64_t cur = __hip_atomic_load(a.keys + at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int64_t cur = __hip_atomic_load(a.keys + at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             if (cur == key) {
                 slot = at;
                 break;
