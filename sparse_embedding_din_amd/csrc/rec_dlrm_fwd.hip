@@ -40,9 +40,9 @@ constexpr int kDenseThreads = 512;            // eight waves: two per SIMD
 // step 4c + j, lane (m, k) takes input 16c + 4k + j, so a lane's four inputs
 // of a chunk are one float4 of its W row (one load covers 16 whole 64-byte
 // row pieces) and one 16-byte LDS read of its activations.
-template <int NU, bool kVec, bool kGlobalIn = false>
+template <int NU, bool kVec>
 __device__ inline void layer_chunks(const float* in, int ins, int nin, const float* wr, int i0, int m,
-                                    int kg, int rows, f32x4& acc) {
+                                    int kg, f32x4& acc) {
     float4 av[NU], bv[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -59,19 +59,7 @@ __device__ inline void layer_chunks(const float* in, int ins, int nin, const flo
             }
             av[u] = make_float4(v[0], v[1], v[2], v[3]);
         }
-        if (kGlobalIn) {
-            // activations in memory, rows of nin floats with no alignment;
-            // rows past `rows` re-read the last one (their results are dropped)
-            float x[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float v = in[(int64_t)min(m, rows - 1) * ins + min(i + j, nin - 1)];
-                x[j] = i + j < nin ? v : 0.f;
-            }
-            bv[u] = make_float4(x[0], x[1], x[2], x[3]);
-        } else {
-            bv[u] = *(const float4*)(in + m * ins + i);
-        }
+        bv[u] = *(const float4*)(in + m * ins + i);
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -82,18 +70,18 @@ __device__ inline void layer_chunks(const float* in, int ins, int nin, const flo
     }
 }
 
-template <bool kVec, bool kGlobalIn = false>
+template <bool kVec>
 __device__ inline void layer_part(const float* in, int ins, int nin, const float* wr, int i0, int nu, int m,
-                                  int kg, int rows, f32x4& acc) {
+                                  int kg, f32x4& acc) {
     switch (nu) {                                          // uniform
-        case 1: layer_chunks<1, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
-        case 2: layer_chunks<2, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
-        case 3: layer_chunks<3, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
-        case 4: layer_chunks<4, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
-        case 5: layer_chunks<5, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
-        case 6: layer_chunks<6, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
-        case 7: layer_chunks<7, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
-        default: layer_chunks<8, kVec, kGlobalIn>(in, ins, nin, wr, i0, m, kg, rows, acc); break;
+        case 1: layer_chunks<1, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        case 2: layer_chunks<2, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        case 3: layer_chunks<3, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        case 4: layer_chunks<4, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        case 5: layer_chunks<5, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        case 6: layer_chunks<6, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        case 7: layer_chunks<7, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
+        default: layer_chunks<8, kVec>(in, ins, nin, wr, i0, m, kg, acc); break;
     }
 }
 
@@ -105,10 +93,9 @@ __device__ inline void layer_part(const float* in, int ins, int nin, const float
 // x 16 rows; the result's lane (n, k) holds units o0 + 4k .. +3 of row n.
 // Wave w takes the 16-unit tiles w, w + 8, ...; up to 8 chunks (128 inputs)
 // of a tile are loaded together ahead of their products.
-template <bool kGlobalIn = false>
 __device__ inline void mfma_layer(const float* in, int ins, int nin, const float* __restrict__ W,
                                   const float* __restrict__ bias, int nout, float* out, int outs,
-                                  bool relu, int rows = kDenseSamples) {
+                                  bool relu) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m = lane & 15, kg = lane >> 4;
     const int nch = (nin + 15) / 16;
     const bool vec = (nin & 3) == 0;                      // W rows are 16-byte aligned
@@ -118,8 +105,8 @@ __device__ inline void mfma_layer(const float* in, int ins, int nin, const float
         const float* wr = W + (int64_t)(o0 + m) * nin;
         for (int c0 = 0; c0 < nch; c0 += 8) {
             const int nu = min(8, nch - c0);
-            if (vec) layer_part<true, kGlobalIn>(in, ins, nin, wr, 16 * c0, nu, m, kg, rows, acc);
-            else layer_part<false, kGlobalIn>(in, ins, nin, wr, 16 * c0, nu, m, kg, rows, acc);
+            if (vec) layer_part<true>(in, ins, nin, wr, 16 * c0, nu, m, kg, acc);
+            else layer_part<false>(in, ins, nin, wr, 16 * c0, nu, m, kg, acc);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -345,18 +332,144 @@ __global__ __launch_bounds__(kDenseThreads) void k_dlrm_bottom(const DlrmArgs a)
     }
 }
 
+// A float4 of memory that is only 4-byte aligned (rows of an odd number of
+// floats); the hardware reads it with one 16-byte load.
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));
+
+// The wide first top layer runs in stages of kTopK inputs: W's 128 rows and
+// the 16 samples' inputs over the stage, staged in LDS (row stride kTopS
+// floats, two buffers).  Each of the 512 threads moves kTopLd float4s per
+// stage; a wave's float4s are two rows' 512-byte runs, so one load touches
+// few cache lines (reading the MFMA operands straight from memory, where one
+// load spans 16 rows, kept the address units busy nine tenths of the time).
+constexpr int kTopK = 128, kTopS = kTopK + 4;
+constexpr int kTopRows = 128 + kDenseSamples;                     // W rows, then x rows
+constexpr int kTopBuf = kTopRows * kTopS;                          // floats per buffer
+constexpr int kTopLd = kTopRows * (kTopK / 4) / kDenseThreads;    // float4s per thread
+static_assert(kTopRows * (kTopK / 4) % kDenseThreads == 0, "stage split");
+constexpr int kTopLdsBytes = 2 * kTopBuf * 4;                      // 152 KiB
+
+// Thread t's float4s of the stage at input k0: all of them exist (kEdge
+// false), or those past np read zeros (the last stage).
+template <bool kEdge>
+__device__ inline void top_stage_load(const float* W, const float* xb, int64_t np, int rows, int64_t k0,
+                                      f32x4u (&v)[kTopLd]) {
+#pragma unroll
+    for (int q = 0; q < kTopLd; ++q) {
+        const int idx = q * kDenseThreads + threadIdx.x;
+        const int r = idx / (kTopK / 4), c4 = idx % (kTopK / 4);
+        // rows past the batch re-read the last sample (their results are dropped)
+        const float* src = r < 128 ? W + (int64_t)r * np : xb + (int64_t)min(r - 128, rows - 1) * np;
+        const int64_t i = k0 + 4 * c4;
+        if (!kEdge) {
+            v[q] = *(const f32x4u*)(src + i);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float t = src[min(i + j, np - 1)];
+                v[q][j] = i + j < np ? t : 0.f;
+            }
+        }
+    }
+}
+
+__device__ inline void top_stage_store(float* buf, const f32x4u (&v)[kTopLd]) {
+#pragma unroll
+    for (int q = 0; q < kTopLd; ++q) {
+        const int idx = q * kDenseThreads + threadIdx.x;
+        const int r = idx / (kTopK / 4), c4 = idx % (kTopK / 4);
+        *(f32x4*)(buf + r * kTopS + 4 * c4) = f32x4{v[q][0], v[q][1], v[q][2], v[q][3]};
+    }
+}
+
+// The top MLP of a wide model, 16 samples per workgroup.  Its first layer
+// (np = F(F+1)/2 inputs read from memory, 23,653 for F = 217, to 128 units)
+// is the bulk of the work.  Per stage, wave w takes inputs 16w .. 16w + 15 of
+// the stage for all 128 units (eight 16-unit tiles: per lane eight W float4s
+// and one x float4 from LDS, 32 products), so every staged value is read
+// once; the next two stages' loads are in flight meanwhile (one stage ahead
+// left the waves waiting on memory: 433 us against 383 us for the 217-feature
+// model at B = 4096; one ahead from memory without LDS, 480 us; the first
+// version, eight waves over the 128 units each reading every input from
+// memory, 1.80 ms).  Each wave thus sums
+// one eighth of the inputs; the eight partial sums are added in LDS in wave
+// order, then bias and ReLU, and the 128 -> 64 -> 1 layers run as in the
+// one-launch kernel.
 __global__ __launch_bounds__(kDenseThreads) void k_dlrm_top_wide(const DlrmArgs a) {
-    constexpr int kHs = 128 + 4, kT2s = 64 + 4;
-    __shared__ __attribute__((aligned(16))) float s_t1[kDenseSamples * kHs];
-    __shared__ __attribute__((aligned(16))) float s_t2[kDenseSamples * kT2s];
+    extern __shared__ __attribute__((aligned(16))) float s_dyn[];
+    constexpr int kWaves = kDenseThreads / 64, kPs = 128, kT2s = 64 + 4;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int m = lane & 15, kg = lane >> 4;
     const int F = a.S + 1;
     const int64_t np = (int64_t)F * (F + 1) / 2;
     const int64_t b0 = (int64_t)blockIdx.x * kDenseSamples;
     const int rows = (int)min((int64_t)kDenseSamples, a.B - b0);
-    // rows past the batch re-read the last sample (their results are dropped)
-    mfma_layer<true>(a.inter + b0 * np, (int)np, (int)np, a.wt1, a.bt1, 128, s_t1, kHs, true, rows);
+    const float* xb = a.inter + b0 * np;
+    const int nst = (int)((np + kTopK - 1) / kTopK);
+    f32x4 acc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nfull = (int)(np / kTopK);                   // stages whose inputs all exist
+    // Two stages' loads are in flight while a third is computed: stage st is
+    // in LDS buffer st & 1, stage st + 1 in one register set, st + 2 in the
+    // other.
+    f32x4u va[kTopLd], vb[kTopLd];
+    auto load = [&](int sidx, f32x4u (&v)[kTopLd]) {
+        const int64_t k = (int64_t)sidx * kTopK;
+        if (sidx < nfull) top_stage_load<false>(a.wt1, xb, np, rows, k, v);
+        else if (sidx < nst) top_stage_load<true>(a.wt1, xb, np, rows, k, v);
+    };
+    auto compute = [&](const float* cur) {
+        const float* wl = cur + m * kTopS + 16 * wave + 4 * kg;
+        const f32x4 xv = *(const f32x4*)(cur + (128 + m) * kTopS + 16 * wave + 4 * kg);
+        f32x4 wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) wv[u] = *(const f32x4*)(wl + 16 * u * kTopS);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[u][j], xv[j], acc[u], 0, 0, 0);
+    };
+    float* buf0 = s_dyn;
+    float* buf1 = s_dyn + kTopBuf;
+    load(0, va);
+    top_stage_store(buf0, va);
+    load(1, va);
+    load(2, vb);
     __syncthreads();
-    mfma_layer(s_t1, kHs, 128, a.wt2, a.bt2, 64, s_t2, kT2s, true);
+    for (int st = 0; st < nst; st += 2) {
+        compute(buf0);                                     // stage st
+        if (st + 1 < nst) top_stage_store(buf1, va);
+        load(st + 3, va);
+        __syncthreads();
+        if (st + 1 >= nst) break;
+        compute(buf1);                                     // stage st + 1
+        if (st + 2 < nst) top_stage_store(buf0, vb);
+        load(st + 4, vb);
+        __syncthreads();
+    }
+    // lane (m, k) holds units 16u + 4k .. +3 of sample m; the partial sums
+    // [wave][sample][unit] reuse the stage buffers, then t1 takes the first
+    // slab and t2 the second
+    float* s_part = s_dyn;
+    float* s_t1 = s_part;
+    float* s_t2 = s_part + kDenseSamples * kPs;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+        *(f32x4*)(s_part + (wave * kDenseSamples + m) * kPs + 16 * u + 4 * kg) = acc[u];
+    __syncthreads();
+    for (int idx = 4 * threadIdx.x; idx < kDenseSamples * kPs; idx += 4 * kDenseThreads) {
+        f32x4 t = *(const f32x4*)(s_part + idx);
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) t += *(const f32x4*)(s_part + w * kDenseSamples * kPs + idx);
+        const f32x4 bb = *(const f32x4*)(a.bt1 + idx % kPs);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[j] = fmaxf(t[j] + bb[j], 0.f);
+        *(f32x4*)(s_t1 + idx) = t;                         // only this thread touches idx
+    }
+    __syncthreads();
+    mfma_layer(s_t1, kPs, 128, a.wt2, a.bt2, 64, s_t2, kT2s, true);
     __syncthreads();
     if (threadIdx.x < rows) {
         const int r = threadIdx.x;
@@ -419,7 +532,10 @@ hipError_t launch_dlrm_fwd_wide(const DlrmArgs& a, const TabDev* tabs, const int
     if (e != hipSuccess) return e;
     e = launch_dlrm_interact(a.z, a.B, a.S + 1, a.dim, a.inter, num_cus, s);
     if (e != hipSuccess) return e;
-    REC_LAUNCH(REC_TIME_DLRM_FWD, k_dlrm_top_wide, grid, blk, 0, s, a);
+    e = hipFuncSetAttribute((const void*)k_dlrm_top_wide, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kTopLdsBytes);
+    if (e != hipSuccess) return e;
+    REC_LAUNCH(REC_TIME_DLRM_FWD, k_dlrm_top_wide, grid, blk, (size_t)kTopLdsBytes, s, a);
     return hipGetLastError();
 }
 
