@@ -288,8 +288,9 @@ rec_status rec_hash_insert(const rec_table* table, const int64_t* keys, const fl
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace rec_hash_admit needs for n ids into a table of
- * `capacity` slots (about 40 B per id, plus 16 B per slot for the eviction
- * sort unless score_mode is REC_SCORE_NONE); 0 for invalid arguments. */
+ * `capacity` slots (about 40 B per id and 4 B per slot, plus 12.5 KiB for
+ * the eviction's selection unless score_mode is REC_SCORE_NONE); 0 for
+ * invalid arguments. */
 size_t rec_hash_admit_workspace_bytes(int64_t n, int64_t capacity, int32_t score_mode);
 
 /*
@@ -339,9 +340,9 @@ size_t rec_hash_admit_workspace_bytes(int64_t n, int64_t capacity, int32_t score
  * the same run to run; which free slot a new id takes may depend on the order
  * of concurrent claims (no lookup result does), and so may which new ids get
  * a counter when the counter table overflows.  Nothing else may use the
- * tables during the call.  Seven launches, 47 with STEP or LFU (the eviction
- * sort's launches return at once when nothing is evicted).  n == 0 is a
- * no-op.
+ * tables during the call.  Seven launches, 20 with STEP or LFU (the 13
+ * passes of the eviction's radix selection return at once when nothing is
+ * evicted).  n == 0 is a no-op.
  * Errors: REC_EINVAL (null or misaligned arrays, bad table, score_mode,
  * max_keys, threshold 0), REC_EUNSUPPORTED (n > 2^30), REC_EWORKSPACE.
  */

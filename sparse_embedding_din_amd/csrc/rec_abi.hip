@@ -519,16 +519,11 @@ rec_status rec_hash_admit(const rec_table* table, int64_t max_keys, int64_t* cou
     a.blk_stored = (int32_t*)(w + L.blk_stored);
     a.nbs = L.nbs;
     a.hdr = (int64_t*)(w + L.hdr);
-    uint32_t *k1 = nullptr, *v1 = nullptr, *hist = nullptr, *tot = nullptr;
     if (score_mode != REC_SCORE_NONE) {
-        a.sort_k = (uint32_t*)(w + L.sort_k0);
-        a.sort_v = (uint32_t*)(w + L.sort_v0);
-        k1 = (uint32_t*)(w + L.sort_k1);
-        v1 = (uint32_t*)(w + L.sort_v1);
-        hist = (uint32_t*)(w + L.hist);
-        tot = (uint32_t*)(w + L.tot);
+        a.sel_hist = (uint32_t*)(w + L.sel_hist);
+        a.sel_state = (int64_t*)(w + L.sel_state);
     }
-    return hip_status(launch_hash_admit(a, k1, v1, hist, tot, (hipStream_t)stream), "rec_hash_admit");
+    return hip_status(launch_hash_admit(a, (hipStream_t)stream), "rec_hash_admit");
 }
 
 rec_status rec_dlrm_interact(const float* z, int64_t B, int32_t F, int32_t d, float* out, void* stream) {

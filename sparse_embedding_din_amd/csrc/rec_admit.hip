@@ -22,13 +22,17 @@
 //   4. k_admit_blocks, k_admit_ranks: each candidate's rank in position
 //      order (counts per 1024 positions, then an exclusive scan), and the
 //      header: ids stored, candidates, room, entries to evict, ids admitted;
-//   5. a stable LSD radix sort of the slots (only when something must be
-//      evicted; the launches read the header and return otherwise) by the
-//      stored id's low word, then its high word (sign flipped, so signed
-//      order), then the saturated score, empty and tombstone slots last; so
-//      the sorted order is by (score, id), whatever slots the ids hold;
-//      k_admit_sortkeys writes each round's 32-bit keys;
-//   6. k_admit_evict: the first entries of that order become tombstones;
+//   5. k_admit_select, 13 passes (only when something must be evicted; the
+//      launches read the header and return otherwise): a radix selection of
+//      the E-th smallest stored entry by (saturated score, id as a signed
+//      integer), a 96-bit key taken 8 bits at a time from the top: pass p
+//      counts digit p of the keys that share the digits chosen so far and
+//      picks the digit where the E-th smallest lies; every block of the next
+//      pass redoes that pick from the counts (so no extra launch), block 0
+//      writes it down; ids are unique, so exactly E keys are at most the
+//      selected one;
+//   6. the last pass turns the slots whose key is at most that one into
+//      tombstones;
 //   7. k_admit_insert: candidates ranked below the admitted count claim the
 //      first empty or tombstone slot of their probe sequence with a 64-bit
 //      compare-and-swap (slots only fill in this phase, so every key keeps
@@ -42,6 +46,7 @@
 // launch never moves, so a stale read can only show a now-taken slot as
 // free; the compare-and-swap that follows then fails and reports the key
 // that is there.  A device-scope load per probe went to memory every time.
+// The insert's claiming probe reads eight slots per round trip.
 #include <limits.h>
 
 #include "rec_internal.h"
@@ -50,7 +55,8 @@ namespace rec {
 namespace {
 
 constexpr uint32_t kScoreSat = 0xfffffffeu;     // scores compare saturated here
-constexpr uint32_t kFreeKey = 0xffffffffu;      // sort key of empty and tombstone slots
+constexpr uint32_t kFreeKey = 0xffffffffu;      // score word of empty and tombstone slots
+constexpr int kSelPasses = 12;                  // 8-bit digits of the 96-bit eviction key
 enum { kHdrStored = 0, kHdrCand, kHdrRoom, kHdrEvict, kHdrAdmit };
 
 __device__ inline bool reserved_key(int64_t k) { return k == REC_EMPTY_KEY || k == REC_TOMBSTONE_KEY; }
@@ -120,6 +126,8 @@ __global__ __launch_bounds__(256) void k_admit_clear(const AdmitArgs a) {
         a.set_cnt[i] = 0;
         a.set_first[i] = INT_MAX;
     }
+    if (a.sel_hist)                                // the selection's counts start at zero
+        for (int64_t j = i; j < kSelPasses * 256; j += (int64_t)gridDim.x * 256) a.sel_hist[j] = 0;
     const int32_t held = i < a.capacity && holds_key(a.keys[i]) ? 1 : 0;
     const int32_t s = block_sum_i32(held, red);
     if (threadIdx.x == 0) a.blk_stored[blockIdx.x] = s;
@@ -224,36 +232,113 @@ __global__ __launch_bounds__(256) void k_admit_ranks(const AdmitArgs a) {
             a.hdr[kHdrRoom] = room;
             a.hdr[kHdrEvict] = ev;
             a.hdr[kHdrAdmit] = min(cand, room + ev);
+            if (a.sel_state) {
+                a.sel_state[0] = a.sel_state[1] = a.sel_state[2] = 0;
+                a.sel_state[3] = ev;
+            }
         }
     }
 }
 
-// Round 0: position i is slot i, keyed by the low word of its id.  Rounds 1
-// and 2 key position i by its slot's high id word (sign flipped) and then by
-// its saturated score (free slots last).
-__global__ __launch_bounds__(256) void k_admit_sortkeys(const AdmitArgs a, int round) {
-    if (a.hdr[kHdrEvict] == 0) return;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= a.capacity) return;
-    const uint32_t s = round == 0 ? (uint32_t)i : a.sort_v[i];
+// The 96-bit eviction key of slot s as three words, most significant first:
+// the saturated score (free slots above every stored entry), the id's high
+// word with the sign flipped and its low word, so unsigned word order is the
+// order by (score, signed id).
+__device__ inline void slot_key(const AdmitArgs& a, int64_t s, uint32_t (&w)[3]) {
     const int64_t k = a.keys[s];
-    if (round == 0) {
-        a.sort_k[i] = (uint32_t)(uint64_t)k;
-        a.sort_v[i] = s;
-    } else if (round == 1) {
-        a.sort_k[i] = (uint32_t)((uint64_t)k >> 32) ^ 0x80000000u;
-    } else {
-        const uint64_t sc = a.scores[s];
-        a.sort_k[i] = holds_key(k) ? (sc < kScoreSat ? (uint32_t)sc : kScoreSat) : kFreeKey;
-    }
+    const uint64_t sc = a.scores[s];
+    w[0] = holds_key(k) ? (sc < kScoreSat ? (uint32_t)sc : kScoreSat) : kFreeKey;
+    w[1] = (uint32_t)((uint64_t)k >> 32) ^ 0x80000000u;
+    w[2] = (uint32_t)(uint64_t)k;
 }
 
-__global__ __launch_bounds__(256) void k_admit_evict(const AdmitArgs a, const uint32_t* order) {
-    const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (v >= a.hdr[kHdrEvict]) return;
-    const uint32_t s = order[v];
-    a.keys[s] = REC_TOMBSTONE_KEY;                 // the digest stays: probes pass the slot
-    a.scores[s] = 0;
+// Digit p (0 .. 11, 8 bits each, most significant first) of a key.
+__device__ inline uint32_t key_digit(const uint32_t (&w)[3], int p) {
+    return (w[p >> 2] >> (24 - 8 * (p & 3))) & 255u;
+}
+
+// Whether a key's digits 0 .. p-1 are those of `pre`.
+__device__ inline bool key_prefix_eq(const uint32_t (&w)[3], const uint32_t (&pre)[3], int p) {
+    bool eq = true;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        const int nb = min(max(8 * p - 32 * q, 0), 32);        // bits of word q fixed so far
+        const uint32_t mask = nb == 0 ? 0u : (nb == 32 ? ~0u : ~0u << (32 - nb));
+        eq = eq && ((w[q] ^ pre[q]) & mask) == 0;
+    }
+    return eq;
+}
+
+// Pass p of the eviction's selection (grid over the slots, 256 threads).
+// State p (sel_state[4p .. 4p+3]): the key words of the digits chosen so far
+// (the rest zero) and the rank still sought among the keys with that prefix;
+// state 0 is (0, 0, 0, entries to evict), written by k_admit_ranks.
+__global__ __launch_bounds__(256) void k_admit_select(const AdmitArgs a, int p) {
+    if (a.hdr[kHdrEvict] == 0) return;
+    __shared__ uint32_t h[256];
+    __shared__ uint32_t wsum[4];
+    __shared__ uint32_t pick;
+    __shared__ int64_t need_s;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    uint32_t pre[3];
+    if (p == 0) {
+        pre[0] = pre[1] = pre[2] = 0;
+    } else {
+        // redo pass p-1's pick: the bin holding the sought rank
+        const int64_t* st = a.sel_state + 4 * (p - 1);
+        const int64_t need = st[3];
+        const uint32_t c = a.sel_hist[(p - 1) * 256 + t];
+        uint32_t inc = c;
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t u = __shfl_up(inc, d, 64);
+            if (lane >= d) inc += u;
+        }
+        if (lane == 63) wsum[wv] = inc;
+        if (t == 0) {                                      // (always overwritten below)
+            pick = 0;
+            need_s = need;
+        }
+        __syncthreads();
+        uint32_t ex = inc - c;
+        for (int k = 0; k < wv; ++k) ex += wsum[k];
+        if ((int64_t)ex < need && need <= (int64_t)ex + c) {   // exactly one bin
+            pick = (uint32_t)t;
+            need_s = need - ex;
+        }
+        __syncthreads();
+        const int q = (p - 1) >> 2, sh = 24 - 8 * ((p - 1) & 3);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) pre[k] = (uint32_t)st[k] | (k == q ? pick << sh : 0u);
+        if (blockIdx.x == 0 && t == 0) {
+            int64_t* nx = a.sel_state + 4 * p;
+            nx[0] = pre[0];
+            nx[1] = pre[1];
+            nx[2] = pre[2];
+            nx[3] = need_s;
+        }
+    }
+    const int64_t s = (int64_t)blockIdx.x * 256 + t;
+    if (p == 12) {
+        // the selected key is the E-th smallest: evict it and every smaller one
+        if (s >= a.capacity || !holds_key(a.keys[s])) return;
+        uint32_t w[3];
+        slot_key(a, s, w);
+        const bool le = w[0] != pre[0] ? w[0] < pre[0] : (w[1] != pre[1] ? w[1] < pre[1] : w[2] <= pre[2]);
+        if (le) {
+            a.keys[s] = REC_TOMBSTONE_KEY;                 // the digest stays: probes pass the slot
+            a.scores[s] = 0;
+        }
+        return;
+    }
+    h[t] = 0;
+    __syncthreads();
+    if (s < a.capacity) {
+        uint32_t w[3];
+        slot_key(a, s, w);
+        if (key_prefix_eq(w, pre, p)) atomicAdd(&h[key_digit(w, p)], 1u);
+    }
+    __syncthreads();
+    if (h[t]) atomicAdd(a.sel_hist + p * 256 + t, h[t]);
 }
 
 __global__ __launch_bounds__(256) void k_admit_insert(const AdmitArgs a) {
@@ -268,16 +353,23 @@ __global__ __launch_bounds__(256) void k_admit_insert(const AdmitArgs a) {
     }
     const uint64_t h = mix64((uint64_t)key);
     int64_t at = hash_home(h, a.capacity), slot = -1;
-    for (int64_t probes = 0; probes < a.capacity; ++probes) {
-        int64_t cur = __hip_atomic_load(a.keys + at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (cur == REC_EMPTY_KEY || cur == REC_TOMBSTONE_KEY) {
-            if (__hip_atomic_compare_exchange_strong(a.keys + at, &cur, key, __ATOMIC_RELAXED,
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-                slot = at;
-                break;
+    for (int64_t seen_n = 0; seen_n < a.capacity && slot < 0; seen_n += kKeyWin) {
+        int64_t w[kKeyWin];
+        key_window(a.keys, at, a.capacity, w);
+#pragma unroll
+        for (int j = 0; j < kKeyWin; ++j) {
+            if (slot >= 0 || seen_n + j >= a.capacity) continue;
+            int64_t cur = w[j];
+            if (cur == REC_EMPTY_KEY || cur == REC_TOMBSTONE_KEY) {
+                int64_t sj = at + j;
+                while (sj >= a.capacity) sj -= a.capacity;
+                if (__hip_atomic_compare_exchange_strong(a.keys + sj, &cur, key, __ATOMIC_RELAXED,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                    slot = sj;
             }
         }
-        at = at + 1 == a.capacity ? 0 : at + 1;
+        at += kKeyWin;
+        while (at >= a.capacity) at -= a.capacity;
     }
     if (slot < 0) return;                          // cannot happen: the room was counted
     a.digests[slot] = (uint8_t)hash_digest(h);
@@ -322,21 +414,16 @@ AdmitLayout admit_layout(int64_t n, int64_t capacity, bool evict) {
     L.blk_cnt = take(4 * (size_t)L.nbn);
     L.blk_stored = take(4 * (size_t)L.nbs);
     L.hdr = take(8 * 8);
-    L.sort_k0 = L.sort_v0 = L.sort_k1 = L.sort_v1 = L.hist = L.tot = 0;
+    L.sel_hist = L.sel_state = 0;
     if (evict) {
-        L.sort_k0 = take(4 * (size_t)capacity);
-        L.sort_v0 = take(4 * (size_t)capacity);
-        L.sort_k1 = take(4 * (size_t)capacity);
-        L.sort_v1 = take(4 * (size_t)capacity);
-        L.hist = take(4 * 256 * (size_t)bwd_sort_tiles(capacity));
-        L.tot = take(4 * 256);
+        L.sel_hist = take(4 * 256 * (size_t)kSelPasses);
+        L.sel_state = take(8 * 4 * (size_t)(kSelPasses + 1));
     }
     L.bytes = o;
     return L;
 }
 
-hipError_t launch_hash_admit(AdmitArgs a, uint32_t* k1, uint32_t* v1, uint32_t* hist, uint32_t* tot,
-                             hipStream_t s) {
+hipError_t launch_hash_admit(AdmitArgs a, hipStream_t s) {
     const dim3 blk(256);
     const unsigned gn = (unsigned)((a.n + 255) / 256);
     hipLaunchKernelGGL(k_admit_clear, dim3((unsigned)a.nbs), blk, 0, s, a);
@@ -344,20 +431,9 @@ hipError_t launch_hash_admit(AdmitArgs a, uint32_t* k1, uint32_t* v1, uint32_t* 
     hipLaunchKernelGGL(k_admit_classify, dim3(gn), blk, 0, s, a);
     hipLaunchKernelGGL(k_admit_blocks, dim3((unsigned)a.nbn), blk, 0, s, a);
     hipLaunchKernelGGL(k_admit_ranks, dim3((unsigned)a.nbn), blk, 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const uint32_t* order = nullptr;
     if (a.mode != REC_SCORE_NONE) {
         const dim3 gc((unsigned)((a.capacity + 255) / 256));
-        for (int round = 0; round < 3; ++round) {
-            // four 8-bit passes per round leave the result in (sort_k, sort_v)
-            hipLaunchKernelGGL(k_admit_sortkeys, gc, blk, 0, s, a, round);
-            const uint32_t* ks;
-            e = launch_radix_sort(a.sort_k, a.sort_v, k1, v1, a.capacity, 32, hist, tot, a.hdr + kHdrEvict,
-                                  s, &ks, &order);
-            if (e != hipSuccess) return e;
-        }
-        hipLaunchKernelGGL(k_admit_evict, dim3(gn), blk, 0, s, a, order);
+        for (int p = 0; p <= kSelPasses; ++p) hipLaunchKernelGGL(k_admit_select, gc, blk, 0, s, a, p);
     }
     hipLaunchKernelGGL(k_admit_insert, dim3(gn), blk, 0, s, a);
     hipLaunchKernelGGL(k_admit_lookup, dim3(gn), blk, 0, s, a);

@@ -12,8 +12,8 @@
 //      take the same slot, and a lane that loses the swap to its own key (a
 //      duplicate in the batch) has found it.  Keys only ever go from empty to
 //      a key, so a stale read can only show a slot as empty; the swap then
-//      fails and reports the key that is there (so the probe reads are
-//      cached, workgroup-scope loads).  The winner writes the
+//      fails and reports the key that is there (so the probe reads are plain
+//      cached loads, eight slots per round trip).  The winner writes the
 //      digest; scores are updated (STEP: every lane writes the same step;
 //      LFU: one atomic add per pair).  With no empty slot on the whole
 //      sequence the pair is not stored (no eviction).  The same launch
@@ -38,28 +38,34 @@ __global__ __launch_bounds__(256) void k_hash_insert(const HashInsArgs a) {
     if (key != REC_EMPTY_KEY && key != REC_TOMBSTONE_KEY) {
         const uint64_t h = mix64((uint64_t)key);
         int64_t at = hash_home(h, a.capacity);
-        bool claimed = false;
+        bool claimed = false, done = false;
         slot = -1;
-        for (int64_t probes = 0; probes < a.capacity; ++probes) {
-            const int64_t cur = __hip_atomic_load(a.keys + at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            if (cur == key) {
-                slot = at;
-                break;
-            }
-            if (cur == REC_EMPTY_KEY) {
-                int64_t seen = REC_EMPTY_KEY;
-                if (__hip_atomic_compare_exchange_strong(a.keys + at, &seen, key, __ATOMIC_RELAXED,
-                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-                    slot = at;
-                    claimed = true;
-                    break;
+        for (int64_t seen_n = 0; seen_n < a.capacity && !done; seen_n += kKeyWin) {
+            int64_t w[kKeyWin];
+            key_window(a.keys, at, a.capacity, w);
+#pragma unroll
+            for (int j = 0; j < kKeyWin; ++j) {
+                if (done || seen_n + j >= a.capacity) continue;
+                int64_t sj = at + j;
+                while (sj >= a.capacity) sj -= a.capacity;
+                if (w[j] == key) {
+                    slot = sj;
+                    done = true;
+                } else if (w[j] == REC_EMPTY_KEY) {
+                    int64_t seen = REC_EMPTY_KEY;
+                    if (__hip_atomic_compare_exchange_strong(a.keys + sj, &seen, key, __ATOMIC_RELAXED,
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                        slot = sj;
+                        claimed = true;
+                        done = true;
+                    } else if (seen == key) {
+                        slot = sj;
+                        done = true;
+                    }
                 }
-                if (seen == key) {
-                    slot = at;
-                    break;
-                }
             }
-            at = at + 1 == a.capacity ? 0 : at + 1;
+            at += kKeyWin;
+            while (at >= a.capacity) at -= a.capacity;
         }
         if (slot >= 0) {
             if (claimed) a.digests[slot] = (uint8_t)hash_digest(h);

@@ -159,6 +159,32 @@ __host__ __device__ inline int64_t hash_probe(const TabDev& t, int64_t key) {
     return -1;
 }
 
+// The keys of slots at .. at + kKeyWin - 1 in probe order (wrapping past the
+// end), for the claiming probes of the write side: one round trip examines
+// kKeyWin slots (four 16-byte loads) instead of one, which shortens the long
+// probe chains of a well-filled table.  Plain loads: the caller's
+// compare-and-swap settles any slot that changed since.
+constexpr int kKeyWin = 8;
+typedef int64_t i64x2u __attribute__((ext_vector_type(2), aligned(8)));
+
+__device__ inline void key_window(const int64_t* keys, int64_t at, int64_t cap, int64_t (&w)[kKeyWin]) {
+    if (at + kKeyWin <= cap) {
+#pragma unroll
+        for (int q = 0; q < kKeyWin / 2; ++q) {
+            const i64x2u v = *(const i64x2u*)(keys + at + 2 * q);
+            w[2 * q] = v.x;
+            w[2 * q + 1] = v.y;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kKeyWin; ++j) {
+            int64_t i = at + j;
+            while (i >= cap) i -= cap;                  // tables smaller than the window wrap again
+            w[j] = keys[i];
+        }
+    }
+}
+
 __device__ inline int64_t resolve_row(const TabDev& t, int64_t raw) {
     if (t.kind == REC_DIRECT) return floor_mod_magic(raw, t.rows, t.magic, t.shift);
     return hash_probe(t, raw);
@@ -380,17 +406,16 @@ struct AdmitArgs {
     int32_t* blk_stored;
     int64_t nbs;
     int64_t* hdr;
-    uint32_t* sort_k;
-    uint32_t* sort_v;
+    uint32_t* sel_hist;           // eviction selection: counts per pass, and
+    int64_t* sel_state;           // the chosen prefix and rank per pass (NULL for NO_EVICTION)
 };
 struct AdmitLayout {
     int64_t nset, nbn, nbs;
     size_t set_key, set_cnt, set_first, flag, rank, total, cslot, blk_cnt, blk_stored, hdr;
-    size_t sort_k0, sort_v0, sort_k1, sort_v1, hist, tot, bytes;
+    size_t sel_hist, sel_state, bytes;
 };
 AdmitLayout admit_layout(int64_t n, int64_t capacity, bool evict);
-hipError_t launch_hash_admit(AdmitArgs a, uint32_t* k1, uint32_t* v1, uint32_t* hist, uint32_t* tot,
-                             hipStream_t s);
+hipError_t launch_hash_admit(AdmitArgs a, hipStream_t s);
 
 // The DLRM forward around the interaction (rec_dlrm_fwd.hip).
 constexpr int kDlrmMaxDense = 128;           // dense features
