@@ -31,8 +31,9 @@
 //      pass redoes that pick from the counts (so no extra launch), block 0
 //      writes it down; ids are unique, so exactly E keys are at most the
 //      selected one;
-//   6. the last pass turns the slots whose key is at most that one into
-//      tombstones;
+//   6. the pass whose chosen bin holds exactly the keys still sought (at the
+//      latest the thirteenth) turns every stored key at most the bound into a
+//      tombstone, and the passes after it return at once;
 //   7. k_admit_insert: candidates ranked below the admitted count claim the
 //      first empty or tombstone slot of their probe sequence with a 64-bit
 //      compare-and-swap (slots only fill in this phase, so every key keeps
@@ -57,6 +58,8 @@ namespace {
 constexpr uint32_t kScoreSat = 0xfffffffeu;     // scores compare saturated here
 constexpr uint32_t kFreeKey = 0xffffffffu;      // score word of empty and tombstone slots
 constexpr int kSelPasses = 12;                  // 8-bit digits of the 96-bit eviction key
+constexpr int kSelDone = 4 * (kSelPasses + 1);  // sel_state word: the selection is complete
+constexpr int kSelBlocks = 512;
 enum { kHdrStored = 0, kHdrCand, kHdrRoom, kHdrEvict, kHdrAdmit };
 
 __device__ inline bool reserved_key(int64_t k) { return k == REC_EMPTY_KEY || k == REC_TOMBSTONE_KEY; }
@@ -235,6 +238,7 @@ __global__ __launch_bounds__(256) void k_admit_ranks(const AdmitArgs a) {
             if (a.sel_state) {
                 a.sel_state[0] = a.sel_state[1] = a.sel_state[2] = 0;
                 a.sel_state[3] = ev;
+                a.sel_state[kSelDone] = 0;
             }
         }
     }
@@ -269,21 +273,27 @@ __device__ inline bool key_prefix_eq(const uint32_t (&w)[3], const uint32_t (&pr
     return eq;
 }
 
-// Pass p of the eviction's selection (grid over the slots, 256 threads).
+// Pass p of the eviction's selection (at most kSelBlocks blocks of 256
+// threads striding over the slots: fewer blocks redo the pick, and a pass
+// after completion costs little more than its dispatch).
 // State p (sel_state[4p .. 4p+3]): the key words of the digits chosen so far
 // (the rest zero) and the rank still sought among the keys with that prefix;
-// state 0 is (0, 0, 0, entries to evict), written by k_admit_ranks.
+// state 0 is (0, 0, 0, entries to evict), written by k_admit_ranks.  The
+// selection is complete once the chosen bin holds exactly the keys still
+// sought (at the latest when all twelve digits are chosen): the key bound is
+// then the prefix with every later bit set, the pass evicts every stored key
+// at most that bound and sets the done word, and the later passes return.
 __global__ __launch_bounds__(256) void k_admit_select(const AdmitArgs a, int p) {
     if (a.hdr[kHdrEvict] == 0) return;
+    if (p > 0 && a.sel_state[kSelDone] != 0) return;       // complete in an earlier pass
     __shared__ uint32_t h[256];
     __shared__ uint32_t wsum[4];
-    __shared__ uint32_t pick;
+    __shared__ uint32_t pick, pick_cnt;
     __shared__ int64_t need_s;
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    uint32_t pre[3];
-    if (p == 0) {
-        pre[0] = pre[1] = pre[2] = 0;
-    } else {
+    const int64_t s0 = (int64_t)blockIdx.x * 256 + t, stride = (int64_t)gridDim.x * 256;
+    uint32_t pre[3] = {0u, 0u, 0u};
+    if (p > 0) {
         // redo pass p-1's pick: the bin holding the sought rank
         const int64_t* st = a.sel_state + 4 * (p - 1);
         const int64_t need = st[3];
@@ -296,6 +306,7 @@ __global__ __launch_bounds__(256) void k_admit_select(const AdmitArgs a, int p) 
         if (lane == 63) wsum[wv] = inc;
         if (t == 0) {                                      // (always overwritten below)
             pick = 0;
+            pick_cnt = 0;
             need_s = need;
         }
         __syncthreads();
@@ -303,36 +314,47 @@ __global__ __launch_bounds__(256) void k_admit_select(const AdmitArgs a, int p) 
         for (int k = 0; k < wv; ++k) ex += wsum[k];
         if ((int64_t)ex < need && need <= (int64_t)ex + c) {   // exactly one bin
             pick = (uint32_t)t;
+            pick_cnt = c;
             need_s = need - ex;
         }
         __syncthreads();
         const int q = (p - 1) >> 2, sh = 24 - 8 * ((p - 1) & 3);
 #pragma unroll
         for (int k = 0; k < 3; ++k) pre[k] = (uint32_t)st[k] | (k == q ? pick << sh : 0u);
+        const bool complete = need_s == (int64_t)pick_cnt;
+        if (complete) {
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {                  // every bit after digit p-1 set
+                const int nb = min(max(8 * p - 32 * k, 0), 32);
+                pre[k] |= nb == 32 ? 0u : (~0u >> nb);
+            }
+        }
         if (blockIdx.x == 0 && t == 0) {
             int64_t* nx = a.sel_state + 4 * p;
             nx[0] = pre[0];
             nx[1] = pre[1];
             nx[2] = pre[2];
             nx[3] = need_s;
+            if (complete) a.sel_state[kSelDone] = 1;
         }
-    }
-    const int64_t s = (int64_t)blockIdx.x * 256 + t;
-    if (p == 12) {
-        // the selected key is the E-th smallest: evict it and every smaller one
-        if (s >= a.capacity || !holds_key(a.keys[s])) return;
-        uint32_t w[3];
-        slot_key(a, s, w);
-        const bool le = w[0] != pre[0] ? w[0] < pre[0] : (w[1] != pre[1] ? w[1] < pre[1] : w[2] <= pre[2]);
-        if (le) {
-            a.keys[s] = REC_TOMBSTONE_KEY;                 // the digest stays: probes pass the slot
-            a.scores[s] = 0;
+        if (complete) {
+            for (int64_t s = s0; s < a.capacity; s += stride) {
+                if (!holds_key(a.keys[s])) continue;
+                uint32_t w[3];
+                slot_key(a, s, w);
+                const bool le =
+                    w[0] != pre[0] ? w[0] < pre[0] : (w[1] != pre[1] ? w[1] < pre[1] : w[2] <= pre[2]);
+                if (le) {
+                    a.keys[s] = REC_TOMBSTONE_KEY;         // the digest stays: probes pass the slot
+                    a.scores[s] = 0;
+                }
+            }
+            return;
         }
-        return;
     }
     h[t] = 0;
     __syncthreads();
-    if (s < a.capacity) {
+    for (int64_t s = s0; s < a.capacity; s += stride) {
         uint32_t w[3];
         slot_key(a, s, w);
         if (key_prefix_eq(w, pre, p)) atomicAdd(&h[key_digit(w, p)], 1u);
@@ -417,7 +439,7 @@ AdmitLayout admit_layout(int64_t n, int64_t capacity, bool evict) {
     L.sel_hist = L.sel_state = 0;
     if (evict) {
         L.sel_hist = take(4 * 256 * (size_t)kSelPasses);
-        L.sel_state = take(8 * 4 * (size_t)(kSelPasses + 1));
+        L.sel_state = take(8 * ((size_t)kSelDone + 1));
     }
     L.bytes = o;
     return L;
@@ -432,7 +454,7 @@ hipError_t launch_hash_admit(AdmitArgs a, hipStream_t s) {
     hipLaunchKernelGGL(k_admit_blocks, dim3((unsigned)a.nbn), blk, 0, s, a);
     hipLaunchKernelGGL(k_admit_ranks, dim3((unsigned)a.nbn), blk, 0, s, a);
     if (a.mode != REC_SCORE_NONE) {
-        const dim3 gc((unsigned)((a.capacity + 255) / 256));
+        const dim3 gc((unsigned)min((a.capacity + 255) / 256, (int64_t)kSelBlocks));
         for (int p = 0; p <= kSelPasses; ++p) hipLaunchKernelGGL(k_admit_select, gc, blk, 0, s, a, p);
     }
     hipLaunchKernelGGL(k_admit_insert, dim3(gn), blk, 0, s, a);
