@@ -203,3 +203,56 @@ def test_admit_on_the_hash_workload_table():
     assert gone == victims
     keep = np.array(sorted(set(was.tolist()) - victims))
     assert np.array_equal(g["keys"][keep], tab["keys"][keep])
+
+
+@pytest.mark.parametrize("case", ["low_byte", "signed", "saturated", "whole_group"])
+def test_admit_eviction_selection(case):
+    """Stored ids and scores arranged so that picking the victims (the
+    smallest (saturated score, signed id) entries) is decided at different
+    key digits: 200 ids under one score that differ only in their low byte
+    (decided at the last digit), ids of both signs under one score (the sign
+    flip), scores at and above 2^32 - 2 (equal once saturated, so the ids
+    decide), and a lowest-score group of exactly the entries to evict
+    (decided by the score alone).  Compared with the oracle."""
+    orc = oracle.get()
+    rng = np.random.default_rng({"low_byte": 1, "signed": 2, "saturated": 3, "whole_group": 4}[case])
+    cap, n_old, E = 2053, 1000, 100
+    ids = _pool(rng, n_old)
+    sc = rng.integers(1000, 2000, size=n_old).astype(np.uint64)
+    if case == "low_byte":
+        ids[:200] = np.int64(0x123456789ABCDE00) + np.arange(200, dtype=np.int64)
+        sc[:200] = 7
+    elif case == "signed":
+        ids[:300] = rng.integers(-1000, 1000, size=300, dtype=np.int64) * 1000003 + 17
+        sc[:300] = 5
+    elif case == "saturated":
+        sc[:400] = np.uint64(2**32 - 2) + rng.integers(0, 2**40, size=400).astype(np.uint64)
+        sc[400:] = np.uint64(2**32 - 3)
+        sc[400:900] = np.uint64(2**32 - 2)                  # equal to the saturated ones
+    else:
+        sc[:E] = 3
+    ids, first = np.unique(ids, return_index=True)         # each id once, with its score
+    sc = sc[first]
+    keep = (ids != -1) & (ids != -2)
+    ids, sc = ids[keep], sc[keep]
+    tab = orc.empty_hash_table(cap)
+    tab["scores"] = np.zeros(cap, np.uint64)
+    vals = (rng.standard_normal((ids.size, 16)) * 0.05).astype(np.float32)
+    slots = orc.hash_insert(tab, ids, vals)
+    assert (slots >= 0).all()
+    tab["scores"][slots] = sc
+    fresh = _pool(rng, 4 * E)
+    fresh = fresh[~np.isin(fresh, ids)][:E]
+    keys = rng.permutation(fresh)
+    new_vals = (rng.standard_normal((keys.size, 16)) * 0.05).astype(np.float32)
+    ref, cref = tab, orc.empty_counter_table(1024)
+    dev = Dev(ref, cref)
+    say(f"admit eviction selection ({case}): {ids.size} stored, evict {E}")
+    gslot, gcnt = dev.admit(keys, new_vals, 1, R.REC_SCORE_STEP, 9, ids.size)
+    oslot, ocnt = orc.hash_admit(ref, cref, keys, new_vals, 1, R.REC_SCORE_STEP, 9, ids.size)
+    assert list(ocnt) == [E, E, 0]
+    assert list(gcnt) == list(ocnt)
+    g, _, _ = dev.host()
+    assert orc.hash_check(g["keys"], g["digests"]) == 0
+    assert _map(g) == _map(ref)
+    assert np.array_equal(gslot < 0, oslot < 0)
