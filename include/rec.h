@@ -37,10 +37,11 @@
  *     arrays; hash tables laid out as described below.  Violations are
  *     undefined behaviour.
  *   - Results are deterministic: the same inputs give bit-identical outputs run
- *     to run.  No floating-point sum depends on the order of atomics.  Two
- *     places use atomics: rec_hash_insert (64-bit compare-and-swap to claim
- *     empty slots; it documents what its placement may depend on), and the
- *     DIN plan (rec_din_plan, rec_din_attn_fwd, rec_sparse_din_fwd), which
+ *     to run.  No floating-point sum depends on the order of atomics.  Three
+ *     places use atomics, all on integers: rec_hash_insert and
+ *     rec_hash_admit (64-bit compare-and-swap to claim free slots, counts and
+ *     first positions; each documents what its placement may depend on), and
+ *     the DIN plan (rec_din_plan, rec_din_attn_fwd, rec_sparse_din_fwd), which
  *     appends the samples without positions to a list with one atomic add per
  *     16 samples: the list's order may vary, but each of its samples only gets
  *     its zero output row, so no output depends on that order.

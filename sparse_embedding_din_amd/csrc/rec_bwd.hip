@@ -199,11 +199,21 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint32_t* keys, cons
     const uint32_t dstart = block_scan256(td, red, &sum) - td;          // digits below t
     base[t] = dstart + hist[(int64_t)t * ntiles + tile];
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    // every round's pair is loaded before the first round runs: loaded per
+    // round, the eight dependent loads between barriers bounded the launch
+    uint32_t kr[kSortRounds], vr[kSortRounds];
+#pragma unroll
+    for (int r = 0; r < kSortRounds; ++r) {
+        const int64_t idx = tile * kSortTile + r * kSortThreads + t;
+        kr[r] = idx < n ? keys[idx] : 0u;
+        vr[r] = idx < n ? vals[idx] : 0u;
+    }
+#pragma unroll
     for (int r = 0; r < kSortRounds; ++r) {
         const int64_t idx = tile * kSortTile + r * kSortThreads + t;
         const bool valid = idx < n;
-        const uint32_t k = valid ? keys[idx] : 0u;
-        const uint32_t v = valid ? vals[idx] : 0u;
+        const uint32_t k = kr[r];
+        const uint32_t v = vr[r];
         const uint32_t d = (k >> shift) & 255u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) wcnt[j][t] = 0;
