@@ -17,10 +17,10 @@
 //      descriptor is wave-uniform.
 //   2. a stable LSD radix sort of (key, source) pairs over the key's bits,
 //      8 bits per pass, each pass three launches: k_sort_hist (per tile of
-//      2048 pairs, the count of each digit), k_sort_scan (per digit, the
+//      1024 pairs, the count of each digit), k_sort_scan (per digit, the
 //      exclusive scan of its counts over the tiles, and its total), and
 //      k_sort_scatter (each pair to its digit's place, stable: a tile is
-//      ranked in 8 rounds of 256 pairs in order, each wave matching equal
+//      ranked in 4 rounds of 256 pairs in order, each wave matching equal
 //      digits by ballots, waves and rounds ordered by counters in LDS).
 //      Every counter is written by a kernel: no memset, no atomics.
 //   3. k_bwd_chunks: the sorted contributions in chunks of 16, one 16-lane
@@ -122,10 +122,12 @@ __device__ inline void load_tables(const BwdTabArr& tabs, int T, BwdTab* lt, uin
 }
 
 // ---------------------------------------------------------------------------
-// 2. radix sort passes.  A tile is 2048 pairs: round r (0..7), thread t holds
-// pair tile*2048 + r*256 + t, so the pairs of a tile are visited in order.
+// 2. radix sort passes.  A tile is 1024 pairs: round r (0..3), thread t holds
+// pair tile*1024 + r*256 + t, so the pairs of a tile are visited in order
+// (1024 rather than 2048: twice the workgroups for the scatter's serial
+// rounds, 101 against 105 us per AdaGrad call; 512 gave 105 us again).
 constexpr int kSortThreads = 256;
-constexpr int kSortRounds = 8;
+constexpr int kSortRounds = 4;
 constexpr int kSortTile = kSortThreads * kSortRounds;
 
 __global__ __launch_bounds__(256) void k_sort_hist(const uint32_t* keys, int64_t n, int shift,
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(256) void k_sort_scatter(const uint32_t* keys, cons
     base[t] = dstart + hist[(int64_t)t * ntiles + tile];
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     // every round's pair is loaded before the first round runs: loaded per
-    // round, the eight dependent loads between barriers bounded the launch
+    // round, the dependent loads between barriers bounded the launch
     uint32_t kr[kSortRounds], vr[kSortRounds];
 #pragma unroll
     for (int r = 0; r < kSortRounds; ++r) {
