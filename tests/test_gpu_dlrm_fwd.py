@@ -128,7 +128,10 @@ def test_dlrm_fwd_wide_217_small():
 
 
 @pytest.mark.parametrize("sizes,dim,modes", [((50,) * 40, 32, (1, 0) * 20),     # 40 tables
-                                             ((300,) * 12, 96, (0,) * 12)])      # (S+1) * d = 1248
+                                             ((300,) * 12, 96, (0,) * 12),       # (S+1) * d = 1248
+                                             # 255 features: 32,640 pairs, a whole number of the
+                                             # top layer's 128-input stages
+                                             ((40,) * 254, 32, (0, 1) * 127)])
 def test_dlrm_fwd_wide_by_tables_or_width(sizes, dim, modes):
     cfg = dataclasses.replace(synth.DLRM_WORKLOADS[1], sizes=sizes, dim=dim, modes=modes)
     m = synth.make_dlrm(cfg, bias=True, emb_scale=4.0)
