@@ -49,6 +49,7 @@ namespace rec {
 namespace {
 
 constexpr int kChunk = 16;       // sorted contributions per 16-lane group
+constexpr int kWalk = 8;         // chunks per lane per round of the cross-chunk walk (512 a round)
 
 struct BwdTabArr {
     BwdTab t[REC_MAX_TABLES];
@@ -341,16 +342,38 @@ __global__ __launch_bounds__(256) void k_bwd_chunks(BwdArgs a, BwdTabArr tabs) {
     const uint32_t src = in ? a.src[p] : 0xffffffffu;
     const bool head = in && (p == 0 || a.keys[p - 1] != key);
     const bool tail = in && (p + 1 >= n || a.keys[p + 1] != key);
+    // the previous chunk (always whole) and the key before it, loaded beside
+    // this chunk's: a run that crosses into this chunk from the previous one
+    // and began there is summed here whole
+    const uint32_t keyp = c > 0 ? a.keys[p - kChunk] : 0xffffffffu;
+    const uint32_t srcp = c > 0 ? a.src[p - kChunk] : 0xffffffffu;
+    const uint32_t kbb = c > 1 ? a.keys[p0 - kChunk - 1] : 0xffffffffu;
     const uint32_t hm = (uint32_t)(__ballot(head) >> gl) & 0xffffu;
-    Row16 x;
+    const uint32_t K0 = (uint32_t)__shfl((int)key, gl, 64);       // the chunk's first key
+    const uint32_t prevm = (uint32_t)(__ballot(c > 0 && keyp == K0) >> gl) & 0xffffu;   // a suffix
+    // the run of K0 crosses in (the previous chunk ends with K0), began in
+    // the previous chunk (before it, another key) and ends in this one
+    const bool cross_in = (prevm >> 15) & 1u;
+    const bool began_prev = cross_in && (!(prevm & 1u) || kbb != K0);
+    const bool k0_ends = (uint32_t)(__ballot(tail && (hm & ((2u << i) - 1u)) == 0u) >> gl) & 0xffffu;
+    const bool pair_run = began_prev && k0_ends;
+    Row16 x, xp;
     grad_row(x, a, src);
+    if (pair_run && ((prevm >> i) & 1u)) {
+        grad_row(xp, a, srcp);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xp.v[e] = 0.0f;
+    }
     // start of lane i's run inside the chunk (0 when it began earlier)
     const uint32_t upto = hm & ((2u << i) - 1u);
     const int s0 = upto ? 31 - __builtin_clz(upto) : 0;
-    // a run that ends here and began in this chunk is complete: its weights
-    // and accumulator are loaded now, beside the gradients
+    // a run that ends here and began in this chunk (or, whole here, in the
+    // previous one) is complete: its weights and accumulator are loaded now,
+    // beside the gradients
+    const bool whole = tail && (upto || pair_run);
     float* Gp = nullptr;
-    float* wp = (tail && upto && key < a.total_rows) ? locate(lt, lbase, a.T, key, &Gp) : nullptr;
+    float* wp = (whole && key < a.total_rows) ? locate(lt, lbase, a.T, key, &Gp) : nullptr;
     Row16 w, G;
     if (wp) {
         load_row(w, wp);
@@ -360,8 +383,25 @@ __global__ __launch_bounds__(256) void k_bwd_chunks(BwdArgs a, BwdTabArr tabs) {
     seg_step<2>(x, i - 2 >= s0);
     seg_step<4>(x, i - 4 >= s0);
     seg_step<8>(x, i - 8 >= s0);
+    if (pair_run) {
+        // the previous chunk's part of the run, summed over the group by a
+        // fixed tree (every lane ends with the sum)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            float v = xp.v[e];
+            v += __shfl_xor(v, 8, 16);
+            v += __shfl_xor(v, 4, 16);
+            v += __shfl_xor(v, 2, 16);
+            v += __shfl_xor(v, 1, 16);
+            xp.v[e] = v;
+        }
+    }
     if (tail) {
         if (upto) {
+            if (wp) adagrad_store(wp, Gp, w, G, x, a.lr, a.eps);
+        } else if (pair_run) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x.v[e] = xp.v[e] + x.v[e];
             if (wp) adagrad_store(wp, Gp, w, G, x, a.lr, a.eps);
         } else {
             store_row(a.hpart + c * REC_DIM, x);  // head piece of a run begun earlier
@@ -372,74 +412,97 @@ __global__ __launch_bounds__(256) void k_bwd_chunks(BwdArgs a, BwdTabArr tabs) {
 }
 
 // ---------------------------------------------------------------------------
-// 4. runs that cross chunks.  One 16-lane group per chunk; a group whose
-// chunk is the END of a crossing run (its first position continues the
-// previous chunk's run, which ends inside it) walks back 64 chunks per round:
-// lane i looks at chunks cc - i - 16u (u = 0..3), loading the key before each
-// chunk and its tail piece together, so a round is one memory round trip.
+// 4. runs that span three or more chunks.  One 16-lane group checks each
+// chunk; the wave walks back from each chunk of its groups that is the END
+// of such a run (its first position continues the previous chunk's run,
+// which ends inside it), 64 kWalk chunks per round, each lane loading its
+// chunks' last keys and tail pieces together, so a round is one memory round
+// trip (a 16-lane group walking 64 chunks per round took 19 us for the hot
+// rows of a three-row table, about 340 chunks long).
 __global__ __launch_bounds__(256) void k_bwd_cross(BwdArgs a, BwdTabArr tabs) {
     __shared__ BwdTab lt[REC_MAX_TABLES];
     __shared__ uint32_t lbase[REC_MAX_TABLES];
-    load_tables(tabs, a.T, lt, lbase);
     const int i = threadIdx.x & 15;
     const int gl = (threadIdx.x & 63) & ~15;
     const int64_t n = a.n;
     const int64_t nch = (n + kChunk - 1) / kChunk;
     const int64_t c1 = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    if (c1 < 1 || c1 >= nch) return;
     const int64_t p1 = c1 * kChunk;
-    const uint32_t K = a.keys[p1];
-    if (a.keys[p1 - 1] != K) return;              // no run crosses into this chunk
-    if (p1 + kChunk < n && a.keys[p1 + kChunk - 1] == K && a.keys[p1 + kChunk] == K)
-        return;                                   // the run goes on past this chunk
-    // lane 0 owns the step: its rows and the head piece load beside the walk
-    float* Gp = nullptr;
-    float* wp = (i == 0 && K < a.total_rows) ? locate(lt, lbase, a.T, K, &Gp) : nullptr;
-    Row16 w, G, h;
-    if (wp) {
-        load_row(w, wp);
-        load_row(G, Gp);
-        load_row(h, a.hpart + c1 * REC_DIM);
-    }
-    Row16 acc;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc.v[e] = 0.0f;
-    int64_t cc = c1 - 1;                          // newest chunk not yet summed
-    for (;;) {
-        Row16 part[4];
-        uint64_t before = 0;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t cb = cc - i - 16 * u;
-            const bool b = cb > 0 && a.keys[cb * kChunk - 1] == K;
-            if (cb >= 0) load_row(part[u], a.tpart + cb * REC_DIM);
-            before |= (uint64_t)((__ballot(b) >> gl) & 0xffffu) << (16 * u);
+    // Whether a run of at least three chunks ends in this chunk: it crosses
+    // in, did not begin in the previous chunk (those runs are summed by
+    // k_bwd_chunks) and does not go on past this chunk.  The five keys are
+    // loaded at once (clamped into the array), and a block with no such run
+    // returns before copying the table descriptors.
+    const bool valid = c1 >= 2 && c1 < nch;
+    auto kat = [&](int64_t q) { return a.keys[valid ? (q < n ? q : n - 1) : 0]; };
+    const uint32_t K = kat(p1), kb = kat(p1 - 1), kbb = kat(p1 - kChunk - 1);
+    const uint32_t ke = kat(p1 + kChunk - 1), kn = kat(p1 + kChunk);
+    const bool ends = valid && kb == K && kbb == K && !(p1 + kChunk < n && ke == K && kn == K);
+    if (!__syncthreads_or(ends)) return;          // (uniform: the whole block)
+    load_tables(tabs, a.T, lt, lbase);
+    // The wave's groups whose chunk ends such a run, one after another, each
+    // run walked by all 64 lanes; lane 0 owns its step, whose rows and head
+    // piece load beside the walk.  Chunk cb before the run's last chunk holds
+    // a piece of it exactly when its last key is the run's (the run then goes
+    // on from it, so its tail piece was written).  A round looks at kWalk
+    // chunks per lane (lane l: chunks cc - l - 64 u), adds the pieces of the
+    // run's chunks, and is the last round once one of its chunks is not the
+    // run's.
+    const int lane = threadIdx.x & 63;
+    uint64_t todo = __ballot(ends && i == 0);
+    while (todo) {
+        const int g0 = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        const int64_t cq = __shfl(c1, g0, 64);
+        const uint32_t Kq = (uint32_t)__shfl((int)K, g0, 64);
+        float* Gp = nullptr;
+        float* wp = (lane == 0 && Kq < a.total_rows) ? locate(lt, lbase, a.T, Kq, &Gp) : nullptr;
+        Row16 w, G, h;
+        if (wp) {
+            load_row(w, wp);
+            load_row(G, Gp);
+            load_row(h, a.hpart + cq * REC_DIM);
         }
-        // chunks cc .. cc - nb + 1 belong to the run; the last of them holds its start
-        const int nb = (~before) ? __builtin_ctzll(~before) + 1 : 64;
+        Row16 acc;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (i + 16 * u < nb) {
+        for (int e = 0; e < 16; ++e) acc.v[e] = 0.0f;
+        int64_t cc = cq - 1;                      // newest chunk not yet summed
+        for (;;) {
+            uint32_t lk[kWalk];
+            Row16 part[kWalk];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc.v[e] += part[u].v[e];
+            for (int u = 0; u < kWalk; ++u) {
+                const int64_t cb = cc - lane - 64 * u;
+                lk[u] = cb >= 0 ? a.keys[cb * kChunk + kChunk - 1] : ~Kq;
+                if (cb >= 0) load_row(part[u], a.tpart + cb * REC_DIM);
             }
+            bool out = false;
+#pragma unroll
+            for (int u = 0; u < kWalk; ++u) {
+                const bool mine = lk[u] == Kq;
+                out = out || !mine;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc.v[e] += mine ? part[u].v[e] : 0.0f;
+            }
+            if (__ballot(out)) break;
+            cc -= 64 * kWalk;
         }
-        if (~before) break;
-        cc -= 64;
-    }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        float v = acc.v[e];
-        v += __shfl_xor(v, 8, 16);
-        v += __shfl_xor(v, 4, 16);
-        v += __shfl_xor(v, 2, 16);
-        v += __shfl_xor(v, 1, 16);
-        acc.v[e] = v;
-    }
-    if (wp) {
+        for (int e = 0; e < 16; ++e) {
+            float v = acc.v[e];
+            v += __shfl_xor(v, 32, 64);
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 8, 64);
+            v += __shfl_xor(v, 4, 64);
+            v += __shfl_xor(v, 2, 64);
+            v += __shfl_xor(v, 1, 64);
+            acc.v[e] = v;
+        }
+        if (wp) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc.v[e] += h.v[e];
-        adagrad_store(wp, Gp, w, G, acc, a.lr, a.eps);
+            for (int e = 0; e < 16; ++e) acc.v[e] += h.v[e];
+            adagrad_store(wp, Gp, w, G, acc, a.lr, a.eps);
+        }
     }
 }
 
