@@ -15,11 +15,12 @@ Four resident batches rotate (so the L2 does not keep one batch's rows); one
 HIP graph holds a step for each of them and is replayed.  Within a step
 everything runs on one stream: inside a graph, a fork/join to a second stream
 costs more than the overlap it buys for the short plan (--side-stream to
-compare).  Across steps, several batches are kept in flight: batch k on
-stream k mod n (n = 2 and 4 are measured), one graph per stream, so one
-batch's gathers run beside another's attention; `value` is the fastest of
-these throughputs (config.streams says which), and the single-stream step is
-reported beside it.  Prints one JSON line.
+compare).  Across steps, several batches are kept in flight: sixteen
+resident batches (--flight-batches), batch k on stream k mod n (n = 2 and 4
+are measured), one graph per stream, so one batch's gathers run beside
+another's attention; `value` is the fastest of these throughputs
+(config.streams and config.rotating_batches say which), and the
+single-stream step is reported beside it.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config 2]
 """
@@ -70,6 +71,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", type=int, default=2)
     p.add_argument("--batches", type=int, default=4)
+    p.add_argument("--flight-batches", type=int, default=16,
+                   help="resident batches of the batches-in-flight legs (one graph per stream "
+                        "over every stream-th batch: a graph of one step per stream was bound by "
+                        "the host's replays)")
     p.add_argument("--range-positions", type=int, default=0)
     p.add_argument("--kernel-reps", type=int, default=100)
     p.add_argument("--cpu-seconds", type=float, default=8.0)
@@ -549,51 +554,68 @@ def main():
     print(f"[bench] timed {a.steps} steps: wall {wall_ms*1e3:.2f} us/step, "
           f"gpu {gpu_ms*1e3:.2f} us/step", file=sys.stderr, flush=True)
 
-    # Two batches in flight: the resident batches split over two streams (even
-    # and odd), one graph each, replayed alternately, so that one batch's
-    # gathers can run beside another's attention.  Reported beside the
-    # single-stream step.
+    # Batches in flight: a larger set of resident batches (the first `nb` are
+    # the ones above) split over ns streams (batch k on stream k mod ns), one
+    # graph per stream, replayed in turn, so that one batch's gathers can run
+    # beside another's attention.  W warmup steps and exactly K timed steps:
+    # whole rounds of the graphs, then the remainder as single steps on their
+    # streams.  Reported beside the single-stream step.
     two_stream = None
     in_flight = {}
+    nbf = max(a.flight_batches, nb)
+    dbs_f, fwds_f = dbs, fwds
+    if graph is not None and not a.no_two_streams and nbf > nb:
+        extra = [synth.make_batch(model, batch_index=i) for i in range(nb, nbf)]
+        dbs_f = dbs + [PL.DeviceBatch(b, dev) for b in extra]
+        fwds_f = fwds + [PL.SparseDinForward(tabs, mlp, B, cfg.max_len, dev, range_positions=a.range_positions)
+                         for _ in extra]
+        del extra
+        with torch.cuda.stream(stream):
+            for f, db in zip(fwds_f[nb:], dbs_f[nb:]):
+                step(f, db)
+        torch.cuda.synchronize()
     for ns in (2, 4):
-        if graph is None or nb % ns != 0 or a.no_two_streams:
+        if graph is None or nbf % ns != 0 or a.no_two_streams:
             continue
         strs = [torch.cuda.Stream() for _ in range(ns)]
         graphs = [torch.cuda.CUDAGraph() for _ in range(ns)]
         for i in range(ns):
             with torch.cuda.graph(graphs[i], stream=strs[i]):
-                for k in range(i, nb, ns):
-                    step(fwds[k], dbs[k])
+                for k in range(i, nbf, ns):
+                    step(fwds_f[k], dbs_f[k])
         torch.cuda.synchronize()
 
-        def run_k(n_rounds):
-            for _ in range(n_rounds):
+        def run_n(n):
+            for _ in range(n // nbf):
                 for i in range(ns):
                     with torch.cuda.stream(strs[i]):
                         graphs[i].replay()
+            for k in range(n - n // nbf * nbf):
+                with torch.cuda.stream(strs[k % ns]):
+                    step(fwds_f[k], dbs_f[k])
 
-        run_k(max(a.warmup // nb, 1))
+        run_n(a.warmup)
         torch.cuda.synchronize()
-        rounds = a.steps // nb
         s0, ea = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ends = [torch.cuda.Event() for _ in range(ns)]
         tw0 = time.perf_counter()
         s0.record(strs[0])
         for i in range(1, ns):
             strs[i].wait_event(s0)
-        run_k(rounds)
+        run_n(a.steps)
         for i in range(1, ns):
             ends[i].record(strs[i])
             strs[0].wait_event(ends[i])
         ea.record(strs[0])
         torch.cuda.synchronize()
         tw1 = time.perf_counter()
-        n2 = rounds * nb
+        n2 = a.steps
         in_flight[ns] = {"streams": ns, "ms_per_step": round((tw1 - tw0) * 1e3 / n2, 5),
                          "gpu_ms_per_step": round(s0.elapsed_time(ea) / n2, 5),
-                         "samples_s": round(B / ((tw1 - tw0) / n2), 1), "steps": n2,
+                         "samples_s": round(B / ((tw1 - tw0) / n2), 1), "steps": n2, "warmup": a.warmup,
+                         "rotating_batches": nbf,
                          "layout": f"batch k on stream k mod {ns}, one graph per stream"}
-        print(f"[bench] {ns} streams: wall {in_flight[ns]['ms_per_step'] * 1e3:.2f} us/step",
+        print(f"[bench] {ns} streams, {nbf} batches: wall {in_flight[ns]['ms_per_step'] * 1e3:.2f} us/step",
               file=sys.stderr, flush=True)
         del graphs
     if in_flight:
@@ -1161,13 +1183,15 @@ def main():
               f"(top MLP {wk['top']['mean']:.1f} us)", file=sys.stderr, flush=True)
         del wkeep, wz, wi
 
-    # `value` is whole-job throughput: with two batches in flight when that is
-    # faster (every step is still one whole pass over one resident batch).
+    # `value` is whole-job throughput: with batches in flight on several
+    # streams when that is faster (every step is still one whole pass over one
+    # resident batch).
     single = {"ms_per_step": round(ms_per_step, 5), "gpu_ms_per_step": round(gpu_ms, 5),
               "samples_s": round(B / (ms_per_step * 1e-3), 1)}
-    streams = 1
+    streams, rotating = 1, len(dbs)
     if two_stream is not None and two_stream["ms_per_step"] < ms_per_step:
         streams = two_stream["streams"]
+        rotating = two_stream["rotating_batches"]
         ms_per_step = two_stream["ms_per_step"]
         gpu_ms = two_stream["gpu_ms_per_step"]
     value = B / (ms_per_step * 1e-3)
@@ -1186,7 +1210,7 @@ def main():
         "data": "synthetic: seeded Taobao-shaped ids, tables N(0,0.05), Xavier MLP",
         "config": {"workload": f"{cfg.name}: {synth.describe(cfg)}",
                    "global_batch": B, "parallelism": "single GPU",
-                   "graph_replay": graph is not None, "rotating_batches": len(dbs),
+                   "graph_replay": graph is not None, "rotating_batches": rotating,
                    "streams": streams,
                    "plan_on_side_stream": side is not None,
                    "entry": "separate calls" if (a.calls or side is not None) else "rec_sparse_din_fwd"},
