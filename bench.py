@@ -15,11 +15,11 @@ Four resident batches rotate (so the L2 does not keep one batch's rows); one
 HIP graph holds a step for each of them and is replayed.  Within a step
 everything runs on one stream: inside a graph, a fork/join to a second stream
 costs more than the overlap it buys for the short plan (--side-stream to
-compare).  Across steps, several batches are kept in flight: sixteen
-resident batches (--flight-batches), batch k on stream k mod n (n = 2 and 4
-are measured), one graph per stream, so one batch's gathers run beside
-another's attention; `value` is the fastest of these throughputs
-(config.streams and config.rotating_batches say which), and the
+compare).  Across steps, several batches are kept in flight: over the four
+resident batches and over sixteen (--flight-batches), batch k on stream k
+mod n (n = 2 and 4 are measured), one graph per stream, so one batch's
+gathers run beside another's attention; `value` is the fastest of these
+throughputs (config.streams and config.rotating_batches say which), and the
 single-stream step is reported beside it.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--config 2]
@@ -554,12 +554,12 @@ def main():
     print(f"[bench] timed {a.steps} steps: wall {wall_ms*1e3:.2f} us/step, "
           f"gpu {gpu_ms*1e3:.2f} us/step", file=sys.stderr, flush=True)
 
-    # Batches in flight: a larger set of resident batches (the first `nb` are
-    # the ones above) split over ns streams (batch k on stream k mod ns), one
-    # graph per stream, replayed in turn, so that one batch's gathers can run
-    # beside another's attention.  W warmup steps and exactly K timed steps:
-    # whole rounds of the graphs, then the remainder as single steps on their
-    # streams.  Reported beside the single-stream step.
+    # Batches in flight: the resident batches (the `nb` above, and a larger
+    # set whose first `nb` are those) split over ns streams (batch k on stream
+    # k mod ns), one graph per stream, replayed in turn, so that one batch's
+    # gathers can run beside another's attention.  W warmup steps and exactly
+    # K timed steps: whole rounds of the graphs, then the remainder as single
+    # steps on their streams.  Reported beside the single-stream step.
     two_stream = None
     in_flight = {}
     nbf = max(a.flight_batches, nb)
@@ -574,23 +574,24 @@ def main():
             for f, db in zip(fwds_f[nb:], dbs_f[nb:]):
                 step(f, db)
         torch.cuda.synchronize()
-    for ns in (2, 4):
-        if graph is None or nbf % ns != 0 or a.no_two_streams:
+    legs = [(ns, nbl) for nbl in sorted({nb, nbf}) for ns in (2, 4)]
+    for ns, nbl in legs:
+        if graph is None or nbl % ns != 0 or a.no_two_streams:
             continue
         strs = [torch.cuda.Stream() for _ in range(ns)]
         graphs = [torch.cuda.CUDAGraph() for _ in range(ns)]
         for i in range(ns):
             with torch.cuda.graph(graphs[i], stream=strs[i]):
-                for k in range(i, nbf, ns):
+                for k in range(i, nbl, ns):
                     step(fwds_f[k], dbs_f[k])
         torch.cuda.synchronize()
 
         def run_n(n):
-            for _ in range(n // nbf):
+            for _ in range(n // nbl):
                 for i in range(ns):
                     with torch.cuda.stream(strs[i]):
                         graphs[i].replay()
-            for k in range(n - n // nbf * nbf):
+            for k in range(n - n // nbl * nbl):
                 with torch.cuda.stream(strs[k % ns]):
                     step(fwds_f[k], dbs_f[k])
 
@@ -610,12 +611,12 @@ def main():
         torch.cuda.synchronize()
         tw1 = time.perf_counter()
         n2 = a.steps
-        in_flight[ns] = {"streams": ns, "ms_per_step": round((tw1 - tw0) * 1e3 / n2, 5),
-                         "gpu_ms_per_step": round(s0.elapsed_time(ea) / n2, 5),
-                         "samples_s": round(B / ((tw1 - tw0) / n2), 1), "steps": n2, "warmup": a.warmup,
-                         "rotating_batches": nbf,
-                         "layout": f"batch k on stream k mod {ns}, one graph per stream"}
-        print(f"[bench] {ns} streams, {nbf} batches: wall {in_flight[ns]['ms_per_step'] * 1e3:.2f} us/step",
+        leg = {"streams": ns, "ms_per_step": round((tw1 - tw0) * 1e3 / n2, 5),
+               "gpu_ms_per_step": round(s0.elapsed_time(ea) / n2, 5),
+               "samples_s": round(B / ((tw1 - tw0) / n2), 1), "steps": n2, "warmup": a.warmup,
+               "rotating_batches": nbl, "layout": f"batch k on stream k mod {ns}, one graph per stream"}
+        in_flight[(ns, nbl)] = leg
+        print(f"[bench] {ns} streams, {nbl} batches: wall {leg['ms_per_step'] * 1e3:.2f} us/step",
               file=sys.stderr, flush=True)
         del graphs
     if in_flight:
