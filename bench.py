@@ -85,6 +85,7 @@ def parse():
                    help="run the sequence plan on a second stream (pays off when the plan is long, "
                         "e.g. hash-table sequence ids)")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-pcie", action="store_true", help="skip the host-resident-inputs leg")
     p.add_argument("--no-hash-rebuild", action="store_true",
                    help="skip timing the rebuild of the hash workload's tables (clear + insert)")
     p.add_argument("--no-dlrm", action="store_true",
@@ -747,6 +748,46 @@ def main():
             "timing": "mean kernel execution time of the attention launch over "
                       f"{kern_us['din']['n']} warm steps (HIP events bound to the dispatch)"}
 
+    # With host-resident inputs: batch 0's ids and lengths copied from pinned
+    # host memory to its device buffers before each step (and, second figure,
+    # the pooled output and the attention output copied back after it), on
+    # the step's stream.  For the record: the boundary takes device buffers,
+    # so `value` has inputs already in HBM.
+    pcie = None
+    if not a.no_pcie:
+        db0, f0 = dbs[0], fwds[0]
+        ins = [db0.values, db0.lengths, db0.seq_values, db0.seq_lengths]
+        hins = [torch.empty(x.shape, dtype=x.dtype, pin_memory=True) for x in ins]
+        for h, x in zip(hins, ins):
+            h.copy_(x.cpu())
+        houts = [torch.empty((B, f0.T * 16), dtype=torch.float32, pin_memory=True),
+                 torch.empty((B, 48), dtype=torch.float32, pin_memory=True)]
+        in_bytes = float(sum(x.numel() * x.element_size() for x in ins))
+        out_bytes = float(sum(h.numel() * h.element_size() for h in houts))
+
+        def h2d_step(r, back=False):
+            for h, x in zip(hins, ins):
+                x.copy_(h, non_blocking=True)
+            step(f0, db0)
+            if back:
+                houts[0].copy_(f0.pooled[:B], non_blocking=True)
+                houts[1].copy_(f0.att[:B], non_blocking=True)
+        timed(h2d_step, {}, 5)
+        _, pin_step = timed(h2d_step, {}, reps)
+        _, pio_step = timed(lambda r: h2d_step(r, True), {}, reps)
+        _, copy_only = timed(lambda r: [x.copy_(h, non_blocking=True) for h, x in zip(hins, ins)], {}, reps)
+        pcie = {"inputs_bytes": in_bytes, "outputs_bytes": out_bytes,
+                "step_with_inputs_us": pin_step, "step_with_inputs_and_outputs_us": pio_step,
+                "inputs_copy_us": copy_only,
+                "inputs_copy_gb_s": round(in_bytes / (copy_only["mean"] * 1e-6) / 1e9, 1),
+                "samples_s_with_inputs": round(B / (pin_step["mean"] * 1e-6), 1),
+                "samples_s_with_inputs_and_outputs": round(B / (pio_step["mean"] * 1e-6), 1),
+                "note": "one stream, eager launches, batch 0; pinned host buffers"}
+        print(f"[bench] with host inputs: {pin_step['mean']:.1f} us per step ({in_bytes / 1e6:.2f} MB in, "
+              f"{pcie['inputs_copy_gb_s']} GB/s); with outputs back: {pio_step['mean']:.1f} us",
+              file=sys.stderr, flush=True)
+        del hins, houts
+
     # The whole MultiTowerDIN forward (sparse step + towers), graph-replayed
     # the same way, for the record; `value` stays the sparse step.
     towers = None
@@ -1223,6 +1264,7 @@ def main():
         "kernels_us": kern_us,
         "calls_us": call_us,
         "warm": {"step_us": warm_step, "step_timing": step_timing, **warm_rates},
+        "host_inputs": pcie,
         "cold": {"step_us": cold_step, "kernels_us": cold_us, "calls_us": cold_calls, **cold_rates,
                  "flush": "1 GiB read before each step (L2s and the 256 MB MALL evicted)"},
         "algorithmic": {"gather_bytes": emb_bytes + plan_bytes, "embbag_bytes": emb_bytes,
