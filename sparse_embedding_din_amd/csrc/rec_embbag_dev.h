@@ -11,10 +11,12 @@
 // samples: lanes 0-31 take table 2p, lanes 32-63 table 2p+1, one bag per lane.
 // Both descriptors are wave-uniform, the lengths/offsets of a wave are two
 // 128-byte runs of the key-major KJT, and each sample's two 64-byte outputs
-// form one full 128-byte line.  Every load is issued unconditionally (indices
-// are clamped into the bag, rows of misses point at row 0) and masked
-// afterwards, so a lane has all of a round's id loads and then all of its row
-// loads in flight at once.
+// form one full 128-byte line.  A round resolves up to three ids per bag: a
+// lane loads the ids its bag still holds, then their rows, each under the
+// execution mask with no branch between the loads, so a lane has all of a
+// round's id loads and then all of its row loads in flight at once.  Lanes past
+// their bag's end (and misses) load nothing and add zeros: a bag of one id
+// issues one id load and one row instead of three of each.
 //
 // Given only the lengths (offsets == NULL), a wave derives its 64 bag offsets
 // itself from the KJT sums: the block sums before its block, the prefix of its
@@ -136,32 +138,41 @@ __device__ inline void k_embbag_fwd_body(const EmbArgs& a, int64_t bid) {
     for (int j0 = 0; __ballot(j0 < len) != 0; j0 += kUnroll) {
         int64_t raw[kUnroll], row[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            raw[u] = a.values[len > 0 ? off + min(j0 + u, len - 1) : 0];
+        for (int u = 0; u < kUnroll; ++u) {
+            raw[u] = 0;
+            if (j0 + u < len) raw[u] = a.values[off + j0 + u];
+        }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            if (kHash) {
-                row[u] = tl.kind == REC_HASH ? hash_probe(tl, raw[u]) : floor_mod_magic(raw[u], rows, magic, shift);
-            } else {
-                row[u] = floor_mod_magic(raw[u], rows, magic, shift);
+            row[u] = -1;
+            if (j0 + u < len) {
+                if (kHash) {
+                    row[u] = tl.kind == REC_HASH ? hash_probe(tl, raw[u]) : floor_mod_magic(raw[u], rows, magic, shift);
+                } else {
+                    row[u] = floor_mod_magic(raw[u], rows, magic, shift);
+                }
             }
         }
         float4 v[kUnroll][4];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const float4* src = (const float4*)(vals + (row[u] >= 0 ? row[u] : 0) * 16);
+            const bool use = j0 + u < len && row[u] >= 0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) v[u][r] = src[r];
+            for (int r = 0; r < 4; ++r) v[u][r] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (use) {
+                const float4* src = (const float4*)(vals + row[u] * 16);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[u][r] = src[r];
+            }
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const bool use = j0 + u < len && row[u] >= 0;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                acc[r].x += use ? v[u][r].x : 0.f;
-                acc[r].y += use ? v[u][r].y : 0.f;
-                acc[r].z += use ? v[u][r].z : 0.f;
-                acc[r].w += use ? v[u][r].w : 0.f;
+                acc[r].x += v[u][r].x;
+                acc[r].y += v[u][r].y;
+                acc[r].z += v[u][r].z;
+                acc[r].w += v[u][r].w;
             }
         }
         if (a.rows_out) {
