@@ -118,7 +118,9 @@ __device__ inline void mfma_layer(const float* in, int ins, int nin, const float
 
 // One bag's pooled row, lane c of its eight holding float4 columns c, c + 8,
 // ... (len 0 for a lane without a bag; the loop runs while any bag of the wave
-// has ids left).
+// has ids left).  A round's id and row loads are issued under the execution
+// mask, only for ids the bag still holds, so short bags issue no duplicate
+// loads; the other slots add zeros.
 template <int NF>
 __device__ inline void bag_pool(const DlrmArgs& a, const TabDev& tab, int32_t mode, int64_t bag, int32_t len,
                                 int c, float4 (&acc)[NF]) {
@@ -127,28 +129,32 @@ __device__ inline void bag_pool(const DlrmArgs& a, const TabDev& tab, int32_t mo
 #pragma unroll
     for (int f = 0; f < NF; ++f) acc[f] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j0 = 0; __ballot(j0 < len) != 0; j0 += kIdRound) {
-        int64_t row[kIdRound];
+        int64_t raw[kIdRound];
 #pragma unroll
         for (int u = 0; u < kIdRound; ++u) {
-            const int64_t raw = a.values[len > 0 ? off + min(j0 + u, len - 1) : 0];
-            row[u] = floor_mod_magic(raw, tab.rows, tab.magic, tab.shift);
+            raw[u] = 0;
+            if (j0 + u < len) raw[u] = a.values[off + j0 + u];
         }
         float4 v[kIdRound][NF];
 #pragma unroll
         for (int u = 0; u < kIdRound; ++u) {
-            const float4* src = (const float4*)(tab.values + row[u] * d) + c;
 #pragma unroll
-            for (int f = 0; f < NF; ++f) v[u][f] = src[8 * f];
+            for (int f = 0; f < NF; ++f) v[u][f] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j0 + u < len) {
+                const int64_t row = floor_mod_magic(raw[u], tab.rows, tab.magic, tab.shift);
+                const float4* src = (const float4*)(tab.values + row * d) + c;
+#pragma unroll
+                for (int f = 0; f < NF; ++f) v[u][f] = src[8 * f];
+            }
         }
 #pragma unroll
         for (int u = 0; u < kIdRound; ++u) {
-            const bool use = j0 + u < len;
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
-                acc[f].x += use ? v[u][f].x : 0.f;
-                acc[f].y += use ? v[u][f].y : 0.f;
-                acc[f].z += use ? v[u][f].z : 0.f;
-                acc[f].w += use ? v[u][f].w : 0.f;
+                acc[f].x += v[u][f].x;
+                acc[f].y += v[u][f].y;
+                acc[f].z += v[u][f].z;
+                acc[f].w += v[u][f].w;
             }
         }
     }
