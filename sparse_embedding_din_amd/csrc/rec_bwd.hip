@@ -423,7 +423,6 @@ __global__ __launch_bounds__(256) void k_bwd_cross(BwdArgs a, BwdTabArr tabs) {
     __shared__ BwdTab lt[REC_MAX_TABLES];
     __shared__ uint32_t lbase[REC_MAX_TABLES];
     const int i = threadIdx.x & 15;
-    const int gl = (threadIdx.x & 63) & ~15;
     const int64_t n = a.n;
     const int64_t nch = (n + kChunk - 1) / kChunk;
     const int64_t c1 = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);

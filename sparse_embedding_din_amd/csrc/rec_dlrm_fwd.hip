@@ -218,7 +218,9 @@ __host__ __device__ inline DenseLds dense_lds(int S, int d, int n_dense) {
 }
 
 template <int NF>
-__global__ __launch_bounds__(kDenseThreads, 4) void k_dlrm_fwd(const DlrmArgs a) {
+// At most 168 registers (three waves per SIMD): a workgroup of eight waves
+// holds a CU either way, and widths up to 224 then need no scratch.
+__global__ __launch_bounds__(kDenseThreads, 3) void k_dlrm_fwd(const DlrmArgs a) {
     extern __shared__ __attribute__((aligned(16))) float s_dyn[];
     const DenseLds Ld = dense_lds(a.S, a.dim, a.n_dense);
     const int F = a.S + 1, d = a.dim, zw = F * d, zs = Ld.zs;
