@@ -153,6 +153,7 @@ for _k in ("k_dinb_prep", "k_dinb_map", "k_dinb_fwd", "k_dinb_soft", "k_dinb_bwd
 
 
 CAL_BYTES = 64 << 20            # bytes read (and written) by the calibration copy
+COPY_PEAK_BYTES = 512 << 20     # bytes read (and written) by the measured copy rate
 CAL_ROWS = 1 << 20              # random 64-byte rows read (and written) by the calibration gather
 CAL_TABLE_ROWS = 3 << 20        # rows of its table (192 MiB, like the embedding tables)
 KERNELS = {"k_din_attn": "k_din_attn",
@@ -707,6 +708,19 @@ def main():
     cold_calls, _ = timed(calls_rep, {"embbag": R.REC_TIME_GATHER, "din_plan": R.REC_TIME_DIN_ATTN},
                           cold_reps, flush)
     del flush_buf
+    # the chip's copy rate, measured: a device-to-device copy of COPY_PEAK_BYTES
+    # (as many bytes read as written), so that the gathers' algorithmic GB/s
+    # read against what a plain stream reaches as well as against the peak
+    cp_src = torch.ones(COPY_PEAK_BYTES // 4, dtype=torch.float32, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    _, cp_us = timed(lambda r: cp_dst.copy_(cp_src), {}, 20)
+    copy_gbs = 2 * COPY_PEAK_BYTES / (cp_us["median"] * 1e-6) / 1e9
+    del cp_src, cp_dst
+    copy_peak = {"gb_s": round(copy_gbs, 1), "hbm_frac": round(copy_gbs / HBM_PEAK_GBS, 4),
+                 "bytes_read": COPY_PEAK_BYTES, "bytes_written": COPY_PEAK_BYTES, "us": cp_us,
+                 "how": "torch copy_ between two device tensors, median of 20 (events around each copy)"}
+    print(f"[bench] copy peak: {copy_gbs:.0f} GB/s ({COPY_PEAK_BYTES >> 20} MiB read and written)",
+          file=sys.stderr, flush=True)
     print(f"[bench] kernel us (warm): " + ", ".join(f"{k}={v['mean']:.2f}" for k, v in kern_us.items())
           + f"; calls: embbag={call_us['embbag']['mean']:.2f} din={call_us['din_plan']['mean']:.2f}"
           + f"; cold: " + ", ".join(f"{k}={v['mean']:.2f}" for k, v in cold_us.items())
@@ -732,7 +746,10 @@ def main():
                 "gather_hbm_frac": round((emb_bytes + plan_bytes) / (ku["gather"]["mean"] * 1e-6)
                                          / 1e9 / HBM_PEAK_GBS, 4),
                 "embbag_gb_s": round(emb_bytes / (cu["embbag"]["mean"] * 1e-6) / 1e9, 1),
-                "embbag_hbm_frac": round(emb_bytes / (cu["embbag"]["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                "embbag_hbm_frac": round(emb_bytes / (cu["embbag"]["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "gather_copy_frac": round((emb_bytes + plan_bytes) / (ku["gather"]["mean"] * 1e-6)
+                                          / 1e9 / copy_gbs, 4),
+                "embbag_copy_frac": round(emb_bytes / (cu["embbag"]["mean"] * 1e-6) / 1e9 / copy_gbs, 4)}
     warm_rates, cold_rates = rates(kern_us, call_us), rates(cold_us, cold_calls)
     din_tflops = warm_rates["din_tflops"]
     roof = {"kernel": "k_din_attn (the attention launch of rec_sparse_din_fwd)", "bound": "mfma",
@@ -1267,6 +1284,7 @@ def main():
         "host_inputs": pcie,
         "cold": {"step_us": cold_step, "kernels_us": cold_us, "calls_us": cold_calls, **cold_rates,
                  "flush": "1 GiB read before each step (L2s and the 256 MB MALL evicted)"},
+        "copy_peak": copy_peak,
         "algorithmic": {"gather_bytes": emb_bytes + plan_bytes, "embbag_bytes": emb_bytes,
                         "plan_bytes": plan_bytes, "din_bytes": din_bytes, "din_flops": din_flops},
         "towers": towers,
