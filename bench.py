@@ -253,8 +253,18 @@ PROFILE_COMMANDS = {
     "mfma": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES "
             "GRBM_GUI_ACTIVE -d gpurun_out/pmc_MFMA_cfg{c} -o run --output-format csv "
             "-- python3 bench.py --config {c} --steps 8 --warmup 4 --no-cpu --no-graph --kernel-reps 8",
+    "lds": "rocprofv3 --pmc SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS GRBM_GUI_ACTIVE "
+           "-d gpurun_out/pmc_LDS_cfg{c} -o run --output-format csv "
+           "-- python3 bench.py --config {c} --steps 8 --warmup 4 --no-cpu --no-graph --kernel-reps 8",
+    "ldsbw": "rocprofv3 --pmc SQ_INSTS_LDS_LOAD_BANDWIDTH -d gpurun_out/pmc_LDSBW_cfg{c} -o run "
+             "--output-format csv -- python3 bench.py --config {c} --steps 8 --warmup 4 --no-cpu --no-graph "
+             "--kernel-reps 8",
 }
 CLOCK_HZ = 2.4e9                # MI355X peak engine clock
+CUS = 256
+# kernels whose LDS counters the summary reports (the matrix-core kernels
+# that stream their weights or staged inputs through LDS)
+LDS_KERNELS = ("k_din_attn", "k_towers_bf16", "k_dinb_fwd", "k_dinb_bwdt", "k_dinb_wgrad")
 SIMDS = 1024                    # 256 CUs x 4 SIMDs
 
 
@@ -278,12 +288,15 @@ def profile_summary(root: str, c: int, workload: str) -> str:
     and WRITE_SIZE, calibrated) and the MFMA counters of the bf16 kernels."""
     import csv
     d = {k: os.path.join(root, f"{n}_cfg{c}") for k, n in
-         (("trace", "prof"), ("fetch", "pmc_FETCH_SIZE"), ("write", "pmc_WRITE_SIZE"), ("mfma", "pmc_MFMA"))}
+         (("trace", "prof"), ("fetch", "pmc_FETCH_SIZE"), ("write", "pmc_WRITE_SIZE"), ("mfma", "pmc_MFMA"),
+          ("lds", "pmc_LDS"), ("ldsbw", "pmc_LDSBW"))}
+    have_lds = all(os.path.exists(os.path.join(d[k], "run_counter_collection.csv")) for k in ("lds", "ldsbw"))
     cmd = {k: v.format(c=c) for k, v in PROFILE_COMMANDS.items()}
-    out = [f"# Kernel durations, HBM traffic and MFMA counters: {workload}", "",
+    out = [f"# Kernel durations, HBM traffic, MFMA and LDS counters: {workload}", "",
            "Made by `python3 bench.py --config %d --profile-summary gpurun_out` from the outputs of" % c,
            "these runs (each on one MI355X, bench.py as committed):", "", "```"]
-    out += [cmd[k] for k in ("trace", "fetch", "write", "mfma")] + ["```", ""]
+    out += [cmd[k] for k in ("trace", "fetch", "write", "mfma") + (("lds", "ldsbw") if have_lds else ())]
+    out += ["```", ""]
 
     rows = list(csv.DictReader(open(os.path.join(d["trace"], "run_kernel_trace.csv"))))
     rows.sort(key=lambda r: int(r["Dispatch_Id"]))
@@ -362,6 +375,45 @@ def profile_summary(root: str, c: int, workload: str) -> str:
         frac_w = busy / (SIMDS * CLOCK_HZ * warm * 1e-6) if warm else float("nan")
         out.append(f"| {k} | {len(dur[k])} | {mops * 512 / 1e9:.3f} | {busy:.0f} | {mean('SQ_BUSY_CYCLES'):.0f} | "
                    f"{mean('GRBM_GUI_ACTIVE'):.0f} | {du:.2f} | {frac_c:.4f} | {frac_w:.4f} |")
+    if have_lds:
+        lacc, ldur = {}, {}
+        for key in ("lds", "ldsbw"):
+            for r in csv.DictReader(open(os.path.join(d[key], "run_counter_collection.csv"))):
+                k = _kernel_key(r["Kernel_Name"])
+                if k not in LDS_KERNELS:
+                    continue
+                lacc.setdefault(k, {}).setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = \
+                    float(r["Counter_Value"])
+                if key == "lds":
+                    ldur.setdefault(k, {})[r["Dispatch_Id"]] = \
+                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        out += ["", "## LDS counters", "",
+                "Means per dispatch, from two counter runs (the LDS load bytes in a run of their own).",
+                "SQ_INSTS_LDS_LOAD_BANDWIDTH counts 64-byte units loaded from LDS, SQ_LDS_IDX_ACTIVE the",
+                "cycles the LDS of a CU is busy (summed over the CUs), SQ_LDS_BANK_CONFLICT the cycles of",
+                "those stalled on bank conflicts.  Active fraction = active / (256 CUs x 2.4 GHz x",
+                "duration); bytes per CU-cycle = loaded bytes / (256 x 2.4 GHz x duration); `warm` uses the",
+                "warm leg's mean duration where the kernel is in it, else the counter run's own.", "",
+                "| kernel | dispatches | LDS instructions | loaded MB | active cycles | bank-conflict cycles | "
+                "counted us | active frac (counted) | active frac (warm) | loaded B per CU-cycle (warm) |",
+                "|---|---|---|---|---|---|---|---|---|---|"]
+        for k in LDS_KERNELS:
+            if k not in lacc:
+                continue
+            cn = lacc[k]
+
+            def lmean(name):
+                v = list(cn.get(name, {}).values())
+                return sum(v) / len(v) if v else float("nan")
+            du = sum(ldur[k].values()) / len(ldur[k])
+            warm = statistics_mean(leg.get(k)) or du
+            act = lmean("SQ_LDS_IDX_ACTIVE")
+            loaded = lmean("SQ_INSTS_LDS_LOAD_BANDWIDTH") * 64
+            cyc_c = CUS * CLOCK_HZ * du * 1e-6
+            cyc_w = CUS * CLOCK_HZ * warm * 1e-6
+            out.append(f"| {k} | {len(ldur[k])} | {lmean('SQ_INSTS_LDS'):.0f} | {loaded / 1e6:.1f} | {act:.0f} | "
+                       f"{lmean('SQ_LDS_BANK_CONFLICT'):.0f} | {du:.2f} | {act / cyc_c:.4f} | {act / cyc_w:.4f} | "
+                       f"{loaded / cyc_w:.1f} |")
     text = "\n".join(out) + "\n"
     with open(os.path.join(ROOT, "profiles", f"step_kernels_{workload}.md"), "w") as f:
         f.write(text)
