@@ -8,12 +8,13 @@
 // Work split.  rec_din_plan resolved every sequence id to its row, laid the
 // batch out as P packed positions and cut [0, P) into groups: group g starts
 // at the sample start nearest to g * span (span = P over the workgroups of a
-// persistent grid, one 4-wave workgroup per CU, unless the caller asks for a
-// fixed range length), so no sample is cut between workgroups.  Workgroup k
-// takes groups k, k + grid, ...; a group's 16-position tiles are split as
-// evenly as possible over its four waves (one per SIMD), so every wave gets
-// about the same number of rows whatever the length mix.  A wave walks its
-// tiles (pairs while two are left), and per tile:
+// persistent grid, one 8-wave workgroup per CU (two waves per SIMD), unless
+// the caller asks for a fixed range length), so no sample is cut between
+// workgroups.  Workgroup k takes groups k, k + grid, ...; a group's
+// 16-position tiles are split as evenly as possible over its eight waves, so
+// every wave gets about the same number of rows whatever the length mix.  A
+// wave walks its tiles one per round (built with four waves, kRoundTiles = 2:
+// pairs while two are left), and per tile:
 //   1. reads the positions' sample, step and three resolved rows from the
 //      plan, then s (3 rows of 64 B) and q (3 x 16 floats of the pooled
 //      output); lane (n, g) holds features 12g..12g+11 of position n;
@@ -629,7 +630,7 @@ __global__ __launch_bounds__(64 * kDinWaves) void k_din_attn(const DinArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // Workgroup k takes the groups k, k + gridDim.x, ...: a group is the
     // positions between two sample starts about `span` apart, its tiles
-    // split over the four waves.  The group count (the plan computed it) and
+    // split over the eight waves.  The group count (the plan computed it) and
     // the first group's bounds are read at once (every workgroup has a slot;
     // one past the last group is not used), ahead of the weight staging, so
     // they are scalar loads that the staging's vector loads do not delay.
