@@ -10,10 +10,10 @@
 // samples: lanes 0-31 take table 2p, lanes 32-63 table 2p+1, one bag per lane.
 // Both descriptors are wave-uniform, the lengths/offsets of a wave are two
 // 128-byte runs of the key-major KJT, and each sample's two 64-byte outputs
-// form one full 128-byte line.  Every load is issued unconditionally (indices
-// are clamped into the bag, rows of misses point at row 0) and masked
-// afterwards, so a lane has all of a round's id loads and then all of its row
-// loads in flight at once.
+// form one full 128-byte line.  A round's id loads and then its row loads are
+// issued together under the execution mask, only for the ids each bag still
+// holds (misses load no row), so a lane has all of a round's loads of one kind
+// in flight at once and short bags issue no duplicate loads.
 //
 // Given only the lengths (offsets == NULL), a wave derives its 64 bag offsets
 // itself from the KJT sums: the sum of the block sums before its block and of
