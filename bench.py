@@ -9,8 +9,12 @@ made as one rec_sparse_din_fwd call (three kernel launches).  The rest of the
 MultiTowerDIN forward (deep tower + final MLP, rec_towers_fwd) is timed
 beside it and reported under "towers"; it is not part of the timed step.  So are
 the sparse backward with its AdaGrad step ("adagrad"), the DIN attention's
-backward ("din_bwd") and the DLRM interaction layer at 217 x 96
-("dlrm_interaction").
+backward ("din_bwd"), the hash tables' rebuild and admission ("hash_rebuild",
+"hash_admit"), the DLRM interaction layer at 217 x 96 ("dlrm_interaction")
+and the DLRM forwards ("dlrm_forward", "dlrm_wide").  Kernel times come warm
+and cold (1 GiB read before each step: "warm", "cold"), beside the chip's
+measured copy rate ("copy_peak") and a leg whose inputs start in pinned host
+memory ("host_inputs").
 Four resident batches rotate (so the L2 does not keep one batch's rows); one
 HIP graph holds a step for each of them and is replayed.  Within a step
 everything runs on one stream: inside a graph, a fork/join to a second stream
