@@ -47,7 +47,7 @@
 // launch never moves, so a stale read can only show a now-taken slot as
 // free; the compare-and-swap that follows then fails and reports the key
 // that is there.  A device-scope load per probe went to memory every time.
-// The insert's claiming probe reads eight slots per round trip.
+// The insert's claiming probe reads 32 slots per round trip.
 #include <limits.h>
 
 #include "rec_internal.h"
@@ -375,11 +375,11 @@ __global__ __launch_bounds__(256) void k_admit_insert(const AdmitArgs a) {
     }
     const uint64_t h = mix64((uint64_t)key);
     int64_t at = hash_home(h, a.capacity), slot = -1;
-    for (int64_t seen_n = 0; seen_n < a.capacity && slot < 0; seen_n += kKeyWin) {
-        int64_t w[kKeyWin];
+    for (int64_t seen_n = 0; seen_n < a.capacity && slot < 0; seen_n += kAdmitKeyWin) {
+        int64_t w[kAdmitKeyWin];
         key_window(a.keys, at, a.capacity, w);
 #pragma unroll
-        for (int j = 0; j < kKeyWin; ++j) {
+        for (int j = 0; j < kAdmitKeyWin; ++j) {
             if (slot >= 0 || seen_n + j >= a.capacity) continue;
             int64_t cur = w[j];
             if (cur == REC_EMPTY_KEY || cur == REC_TOMBSTONE_KEY) {
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256) void k_admit_insert(const AdmitArgs a) {
                     slot = sj;
             }
         }
-        at += kKeyWin;
+        at += kAdmitKeyWin;
         while (at >= a.capacity) at -= a.capacity;
     }
     if (slot < 0) return;                          // cannot happen: the room was counted

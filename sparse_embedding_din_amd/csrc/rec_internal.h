@@ -159,25 +159,31 @@ __host__ __device__ inline int64_t hash_probe(const TabDev& t, int64_t key) {
     return -1;
 }
 
-// The keys of slots at .. at + kKeyWin - 1 in probe order (wrapping past the
-// end), for the claiming probes of the write side: one round trip examines
-// kKeyWin slots (four 16-byte loads) instead of one, which shortens the long
-// probe chains of a well-filled table.  Plain loads: the caller's
-// compare-and-swap settles any slot that changed since.
+// The keys of slots at .. at + W - 1 in probe order (wrapping past the end),
+// for the claiming probes of the write side: one round trip examines W slots
+// (W / 2 16-byte loads) instead of one, which shortens the long probe chains
+// of a well-filled table.  Plain loads: the caller's compare-and-swap settles
+// any slot that changed since.  The rebuild's insert reads kKeyWin slots per
+// round trip; admission, which claims slots in a full table, reads
+// kAdmitKeyWin (wider windows slowed the rebuild: 313 -> 319 us at 16 slots,
+// 341 us at 32, while admission went from 159 to 155 and 151 us).
 constexpr int kKeyWin = 8;
+constexpr int kAdmitKeyWin = 32;
 typedef int64_t i64x2u __attribute__((ext_vector_type(2), aligned(8)));
 
-__device__ inline void key_window(const int64_t* keys, int64_t at, int64_t cap, int64_t (&w)[kKeyWin]) {
-    if (at + kKeyWin <= cap) {
+template <int W>
+__device__ inline void key_window(const int64_t* keys, int64_t at, int64_t cap, int64_t (&w)[W]) {
+    static_assert(W % 2 == 0, "pairs of keys");
+    if (at + W <= cap) {
 #pragma unroll
-        for (int q = 0; q < kKeyWin / 2; ++q) {
+        for (int q = 0; q < W / 2; ++q) {
             const i64x2u v = *(const i64x2u*)(keys + at + 2 * q);
             w[2 * q] = v.x;
             w[2 * q + 1] = v.y;
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < kKeyWin; ++j) {
+        for (int j = 0; j < W; ++j) {
             int64_t i = at + j;
             while (i >= cap) i -= cap;                  // tables smaller than the window wrap again
             w[j] = keys[i];
