@@ -722,8 +722,8 @@ typedef struct {
 } rec_adagrad_table;
 
 /* Bytes of workspace rec_embbag_adagrad needs for T tables, B samples, nnz
- * bag ids and P sequence positions (about 24.5 B per read: 16 B of keys and
- * sources, 8 B of partial sums, 0.5 B of digit counts); 0 for invalid
+ * bag ids and P sequence positions (about 25 B per read: 16 B of keys and
+ * sources, 8 B of partial sums, 1 B of digit counts); 0 for invalid
  * arguments or nnz + P == 0. */
 size_t rec_embbag_adagrad_workspace_bytes(int32_t T, int64_t B, int64_t nnz, int64_t P);
 
