@@ -93,7 +93,11 @@ def test_dlrm_fwd_ragged_and_empty_bags():
 
 
 @pytest.mark.parametrize("sizes,dim,nd,modes", [((7,), 32, 1, (1,)), ((300, 20, 5), 256, 3, (0, 1, 1)),
-                                                ((1000,) * 15, 64, 40, (1, 0) * 7 + (1,))])
+                                                ((1000,) * 15, 64, 40, (1, 0) * 7 + (1,)),
+                                                # five, six and seven float4 per lane of a row
+                                                ((100, 12), 160, 4, (0, 1)),
+                                                ((400, 30, 7, 3), 192, 2, (0, 1, 0, 1)),
+                                                ((250, 9, 60), 224, 5, (1, 1, 0))])
 def test_dlrm_fwd_shapes(sizes, dim, nd, modes):
     cfg = dataclasses.replace(synth.DLRM_WORKLOADS[1], sizes=sizes, dim=dim, n_dense=nd, modes=modes)
     m = synth.make_dlrm(cfg, bias=True, emb_scale=8.0)
