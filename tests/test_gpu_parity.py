@@ -175,6 +175,37 @@ def test_embbag_edges(models):
     assert row_rel_err(r.pooled, ref) <= 1e-6
 
 
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("cfg", [1, 5])
+def test_embbag_long_bags(models, cfg, fused):
+    """Bags of 0 to 40 ids (a bag lane runs up to 14 rounds of three ids, with
+    empty bags beside long ones in every wave), over direct tables and over
+    hash tables whose ids keep the workload's mix of hits and misses, with
+    offsets given and derived in the bags: resolved rows bit-exact, pooled
+    sums within the fp32 tolerance of the oracle's fp64 sums."""
+    m = models(cfg)
+    B = 300
+    b = synth.make_batch(m, B=B)
+    rng = np.random.default_rng(40 + cfg)
+    L = rng.integers(0, 41, size=(synth.T, B)).astype(np.int32)
+    L[rng.random((synth.T, B)) < 0.2] = 0
+    starts = np.concatenate([[0], np.cumsum(b.lengths)])
+    vals = []
+    for k in range(synth.T):
+        pool = b.values[starts[k * B]: starts[(k + 1) * B]]      # table k's ids as generated
+        vals.append(rng.choice(pool, size=int(L[k].sum())))
+    b.lengths = L.reshape(-1)
+    b.values = np.concatenate(vals)
+    r = Run(m, b, fused=fused)
+    orc = oracle.get()
+    rows, _ = oracle_rows(m, b)
+    assert np.array_equal(r.emb_rows, rows)
+    if cfg == 5:
+        assert np.any(rows < 0) and np.any(rows >= 0)            # hits and misses both present
+    ref = orc.embbag(m.tables, B, b.values, b.lengths, orc.lengths_to_offsets(b.lengths))
+    assert row_rel_err(r.pooled, ref) <= FP32_TOL
+
+
 @pytest.mark.parametrize("T,B", [(1, 1), (5, 2500), (16, 1025), (32, 3000), (3, 4096)])
 def test_embbag_kjt_shapes(models, T, B):
     """Offsets derived in the bags for odd table counts, batches that are not
