@@ -72,6 +72,24 @@ def test_dlrm_fwd_essay_model_B8192(w):
     _check(m, b, synth.DLRM_WORKLOADS[w].name)
 
 
+def test_dlrm_fwd_long_bags():
+    """Bags of up to 30 ids (eight rounds of four), a fifth of them empty,
+    sum and mean pooling side by side."""
+    cfg = dataclasses.replace(synth.DLRM_WORKLOADS[2], bag_max=30,
+                              modes=tuple(i % 2 for i in range(len(synth.DLRM_WORKLOADS[2].sizes))))
+    m = synth.make_dlrm(cfg, bias=True)
+    b = synth.make_dlrm_batch(m, B=200, batch_index=3)
+    S = len(m.tables)
+    rng = np.random.default_rng(30)
+    keep = rng.random((S, 200)) >= 0.2
+    L = np.where(keep, b.lengths.reshape(S, 200), 0).astype(np.int32)
+    starts = np.concatenate([[0], np.cumsum(b.lengths.astype(np.int64))])
+    vals = [b.values[starts[i]: starts[i] + L.reshape(-1)[i]] for i in range(S * 200)]
+    b2 = dataclasses.replace(b, lengths=L.reshape(-1).copy(), values=np.concatenate(vals))
+    assert L.max() > 24
+    _check(m, b2, "long bags")
+
+
 def test_dlrm_fwd_ragged_and_empty_bags():
     m = synth.make_dlrm(synth.DLRM_WORKLOADS[2], bias=True)
     for B in (1, 37, 1000):
