@@ -132,9 +132,8 @@ constexpr int kSortRounds = 4;
 constexpr int kSortTile = kSortThreads * kSortRounds;
 
 __global__ __launch_bounds__(256) void k_sort_hist(const uint32_t* keys, int64_t n, int shift,
-                                                   int64_t ntiles, uint32_t* hist, const int64_t* gate) {
+                                                   int64_t ntiles, uint32_t* hist) {
     __shared__ uint32_t h[256];
-    if (gate && *gate == 0) return;
     const int t = threadIdx.x;
     const int64_t tile = blockIdx.x;
     h[t] = 0;
@@ -168,10 +167,8 @@ __device__ inline uint32_t block_scan256(uint32_t v, uint32_t* red, uint32_t* to
 
 // Block d: exclusive scan of digit d's counts over the tiles, in place; its
 // total to tot[d].
-__global__ __launch_bounds__(256) void k_sort_scan(uint32_t* hist, int64_t ntiles, uint32_t* tot,
-                                                   const int64_t* gate) {
+__global__ __launch_bounds__(256) void k_sort_scan(uint32_t* hist, int64_t ntiles, uint32_t* tot) {
     __shared__ uint32_t red[4];
-    if (gate && *gate == 0) return;
     const int t = threadIdx.x;
     uint32_t* row = hist + (int64_t)blockIdx.x * ntiles;
     uint32_t carry = 0;
@@ -189,12 +186,10 @@ __global__ __launch_bounds__(256) void k_sort_scan(uint32_t* hist, int64_t ntile
 __global__ __launch_bounds__(256) void k_sort_scatter(const uint32_t* keys, const uint32_t* vals,
                                                       int64_t n, int shift, int64_t ntiles,
                                                       const uint32_t* hist, const uint32_t* tot,
-                                                      uint32_t* keys_out, uint32_t* vals_out,
-                                                      const int64_t* gate) {
+                                                      uint32_t* keys_out, uint32_t* vals_out) {
     __shared__ uint32_t base[256];        // where digit d's pairs of this tile start
     __shared__ uint32_t wcnt[4][256];     // this round: pairs of digit d in wave w
     __shared__ uint32_t red[4];
-    if (gate && *gate == 0) return;
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int64_t tile = blockIdx.x;
     uint32_t sum;
@@ -510,16 +505,16 @@ __global__ __launch_bounds__(256) void k_bwd_cross(BwdArgs a, BwdTabArr tabs) {
 int64_t bwd_sort_tiles(int64_t n) { return (n + kSortTile - 1) / kSortTile; }
 
 hipError_t launch_radix_sort(uint32_t* kin, uint32_t* vin, uint32_t* kout, uint32_t* vout, int64_t n,
-                             int key_bits, uint32_t* hist, uint32_t* tot, const int64_t* gate,
+                             int key_bits, uint32_t* hist, uint32_t* tot,
                              hipStream_t s, const uint32_t** keys_sorted, const uint32_t** vals_sorted) {
     // ping-pong between (kin, vin) and (kout, vout)
     const int64_t nt = bwd_sort_tiles(n);
     for (int shift = 0; shift < key_bits; shift += 8) {
         hipLaunchKernelGGL(k_sort_hist, dim3((unsigned)nt), dim3(kSortThreads), 0, s, kin, n, shift, nt,
-                           hist, gate);
-        hipLaunchKernelGGL(k_sort_scan, dim3(256), dim3(kSortThreads), 0, s, hist, nt, tot, gate);
+                           hist);
+        hipLaunchKernelGGL(k_sort_scan, dim3(256), dim3(kSortThreads), 0, s, hist, nt, tot);
         hipLaunchKernelGGL(k_sort_scatter, dim3((unsigned)nt), dim3(kSortThreads), 0, s, kin, vin, n, shift,
-                           nt, hist, tot, kout, vout, gate);
+                           nt, hist, tot, kout, vout);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         uint32_t* tk = kin; kin = kout; kout = tk;
@@ -543,7 +538,7 @@ hipError_t launch_embbag_adagrad(BwdArgs a, const BwdTab* tabs, uint32_t* keys_o
     if (e != hipSuccess) return e;
     const uint32_t *ks, *vs;
     e = launch_radix_sort(a.keys_in, a.src_in, keys_out, src_out, a.n, key_bits, sort_hist, sort_tot,
-                          nullptr, s, &ks, &vs);
+                          s, &ks, &vs);
     if (e != hipSuccess) return e;
     a.keys = ks;
     a.src = vs;

@@ -486,11 +486,10 @@ struct BwdArgs {
 int64_t bwd_sort_tiles(int64_t n);            // tiles of the radix sort (256 counters each)
 // Stable LSD radix sort of n (key, value) pairs over the low key_bits bits
 // of the keys, 8 bits per pass, ping-ponging between the two buffer pairs;
-// hist needs bwd_sort_tiles(n) * 256 words, tot 256.  With gate non-NULL,
-// every pass does nothing when *gate == 0 (read on the device).  Returns the
+// hist needs bwd_sort_tiles(n) * 256 words, tot 256.  Returns the
 // pair of buffers holding the result.
 hipError_t launch_radix_sort(uint32_t* kin, uint32_t* vin, uint32_t* kout, uint32_t* vout, int64_t n,
-                             int key_bits, uint32_t* hist, uint32_t* tot, const int64_t* gate,
+                             int key_bits, uint32_t* hist, uint32_t* tot,
                              hipStream_t s, const uint32_t** keys_sorted, const uint32_t** vals_sorted);
 hipError_t launch_embbag_adagrad(BwdArgs a, const BwdTab* tabs, uint32_t* keys_out, uint32_t* src_out,
                                  uint32_t* sort_hist, uint32_t* sort_tot, int key_bits, hipStream_t s);
