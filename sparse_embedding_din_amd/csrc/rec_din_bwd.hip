@@ -454,47 +454,58 @@ __global__ __launch_bounds__(256) void k_dinb_gq(DinBwdArgs a) {
 // 16 x 13 tiles of 16 x 16), dW2 (A = dz2, B = [h1, 1], 4 x 17 tiles) and dw3
 // (A = de, one row, B = [h2, 1], 5 tiles).  Wave w owns dW1's row tiles 2w and
 // 2w + 1, dW2's row tile w / 2 with nine of its column tiles (the ninth of the
-// odd waves lies past the edge and is dropped), and wave 7 the dw3 tiles; so
-// each position's rows are read once per workgroup, and the waves' reads of
-// the same [x, 1] and [h1, 1] rows meet in the cache.  Positions without a
-// sample, and columns past an edge, enter as zeros.  The range's sums go to
-// its slot of the split sums, which k_dinb_reduce adds in range order.
+// odd waves lies past the edge and is dropped), and wave 7 the dw3 tiles.
+// Each position's rows are staged once per workgroup in LDS and every wave
+// reads its operands there.  Positions without a sample, and columns past an
+// edge, enter as zeros.  The range's sums go to its slot of the split sums,
+// which k_dinb_reduce adds in range order.
 constexpr int kWgWaves = 8;
 
-// One step's operands of a lane: position pb + g of the range ending at p1.
-struct WgOps {
-    float A1[2], B1[13], A2, B2[9], A3, B3[5];
-};
+// A position's operand row in LDS: [x, 1] (193), dz1 (256), [h1, 1] (257),
+// dz2 (64), [h2, 1] (65), de (1), padded to a stride of 848 floats (848 mod 64
+// = 16, so the four positions a step reads fall in distinct banks).
+constexpr int kWgRow = kLdX + 256 + kLdH1 + 64 + kLdH2 + 1;     // 836
+constexpr int kWgStride = 848;
+constexpr int kWgStage = 16;                                   // positions per staged block
+constexpr int kWgPer = (kWgRow + 31) / 32;                     // floats per thread per stage (27)
+constexpr int kWgOffDZ1 = kLdX, kWgOffH1 = kWgOffDZ1 + 256, kWgOffDZ2 = kWgOffH1 + kLdH1,
+              kWgOffH2 = kWgOffDZ2 + 64, kWgOffDE = kWgOffH2 + kLdH2;
+static_assert(kWgStage * 32 == 64 * kWgWaves, "32 threads per staged position");
 
-__device__ inline void wg_load(const DinBwdArgs& a, int64_t pb, int64_t p1, int w, int n, int g,
-                               WgOps& o) {
-    const int64_t p = pb + g;
+// Thread t loads floats j = (t % 32) + 32 k of position pb + t / 32's row
+// (zeros past the range or for a position without a sample).
+__device__ inline void wg_stage_load(const DinBwdArgs& a, int64_t pb, int64_t p1, float (&v)[kWgPer]) {
+    const int t = threadIdx.x, l = t & 31;
+    const int64_t p = pb + (t >> 5);
     const bool ok = p < p1 && a.map[p] >= 0;
-    const int c2lo = (w & 1) ? 9 : 0, r2 = w >> 1;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) o.A1[t] = ok ? a.DZ1[p * 256 + 16 * (2 * w + t) + n] : 0.0f;
-#pragma unroll
-    for (int c = 0; c < 13; ++c) o.B1[c] = (ok && 16 * c + n < kLdX) ? a.X[p * kLdX + 16 * c + n] : 0.0f;
-    o.A2 = ok ? a.DZ2[p * 64 + 16 * r2 + n] : 0.0f;
-#pragma unroll
-    for (int c = 0; c < 9; ++c) {
-        const int col = 16 * (c2lo + c) + n;
-        o.B2[c] = (ok && col < kLdH1) ? a.H1[p * kLdH1 + col] : 0.0f;
-    }
-    o.A3 = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 5; ++c) o.B3[c] = 0.0f;
-    if (w == kWgWaves - 1) {
-        o.A3 = (ok && n == 0) ? a.DE[p] : 0.0f;
-#pragma unroll
-        for (int c = 0; c < 5; ++c) {
-            const int col = 16 * c + n;
-            o.B3[c] = (ok && col < kLdH2) ? a.H2[p * kLdH2 + col] : 0.0f;
+    for (int k = 0; k < kWgPer; ++k) {
+        const int j = l + 32 * k;
+        float x = 0.0f;
+        if (ok && j < kWgRow) {
+            if (j < kWgOffDZ1) x = a.X[p * kLdX + j];
+            else if (j < kWgOffH1) x = a.DZ1[p * 256 + (j - kWgOffDZ1)];
+            else if (j < kWgOffDZ2) x = a.H1[p * kLdH1 + (j - kWgOffH1)];
+            else if (j < kWgOffH2) x = a.DZ2[p * 64 + (j - kWgOffDZ2)];
+            else if (j < kWgOffDE) x = a.H2[p * kLdH2 + (j - kWgOffH2)];
+            else x = a.DE[p];
         }
+        v[k] = x;
+    }
+}
+
+__device__ inline void wg_stage_store(float* buf, const float (&v)[kWgPer]) {
+    const int t = threadIdx.x, l = t & 31;
+    float* row = buf + (t >> 5) * kWgStride;
+#pragma unroll
+    for (int k = 0; k < kWgPer; ++k) {
+        const int j = l + 32 * k;
+        if (j < kWgRow) row[j] = v[k];
     }
 }
 
 __global__ __launch_bounds__(64 * kWgWaves) void k_dinb_wgrad(DinBwdArgs a, int64_t chunk) {
+    __shared__ float s_op[2][kWgStage * kWgStride];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, n = lane & 15, g = lane >> 4;
     const int64_t p0 = (int64_t)blockIdx.x * chunk;
     const int64_t p1 = p0 + chunk < a.seq_stride ? p0 + chunk : a.seq_stride;
@@ -506,24 +517,55 @@ __global__ __launch_bounds__(64 * kWgWaves) void k_dinb_wgrad(DinBwdArgs a, int6
     for (int c = 0; c < 9; ++c) acc2[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 5; ++c) acc3[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    WgOps cur;
-    if (p0 < p1) wg_load(a, p0, p1, w, n, g, cur);
-    // the next step's operands are in flight while this step's products run
-    for (int64_t pb = p0; pb < p1; pb += 4) {
-        WgOps nxt = cur;
-        if (pb + 4 < p1) wg_load(a, pb + 4, p1, w, n, g, nxt);
+    // Stages of 16 positions through LDS: the workgroup reads each position's
+    // rows once (32 threads a row, coalesced), the next stage's loads in
+    // flight while this stage's products run.  Steps of four positions, in
+    // order, as the products were before: the sums are the same.
+    float v[kWgPer];
+    if (p0 < p1) {
+        wg_stage_load(a, p0, p1, v);
+        wg_stage_store(s_op[0], v);
+    }
+    __syncthreads();
+    int buf = 0;
+    for (int64_t sb = p0; sb < p1; sb += kWgStage) {
+        const bool more = sb + kWgStage < p1;
+        if (more) wg_stage_load(a, sb + kWgStage, p1, v);
+        const float* st = s_op[buf];
 #pragma unroll
-        for (int c = 0; c < 13; ++c) {
-            acc1[0][c] = mfma4(cur.A1[0], cur.B1[c], acc1[0][c]);
-            acc1[1][c] = mfma4(cur.A1[1], cur.B1[c], acc1[1][c]);
+        for (int k = 0; k < kWgStage / 4; ++k) {
+            if (sb + 4 * k >= p1) break;                     // uniform
+            const float* r = st + (4 * k + g) * kWgStride;   // position sb + 4k + g
+            float A1[2], B1[13], A2, B2[9];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) A1[t] = r[kWgOffDZ1 + 16 * (2 * w + t) + n];
+#pragma unroll
+            for (int c = 0; c < 13; ++c) B1[c] = 16 * c + n < kLdX ? r[16 * c + n] : 0.0f;
+            A2 = r[kWgOffDZ2 + 16 * r2 + n];
+#pragma unroll
+            for (int c = 0; c < 9; ++c) {
+                const int col = 16 * (c2lo + c) + n;
+                B2[c] = col < kLdH1 ? r[kWgOffH1 + col] : 0.0f;
+            }
+#pragma unroll
+            for (int c = 0; c < 13; ++c) {
+                acc1[0][c] = mfma4(A1[0], B1[c], acc1[0][c]);
+                acc1[1][c] = mfma4(A1[1], B1[c], acc1[1][c]);
+            }
+#pragma unroll
+            for (int c = 0; c < 9; ++c) acc2[c] = mfma4(A2, B2[c], acc2[c]);
+            if (w == kWgWaves - 1) {
+                const float A3 = n == 0 ? r[kWgOffDE] : 0.0f;
+#pragma unroll
+                for (int c = 0; c < 5; ++c) {
+                    const int col = 16 * c + n;
+                    acc3[c] = mfma4(A3, col < kLdH2 ? r[kWgOffH2 + col] : 0.0f, acc3[c]);
+                }
+            }
         }
-#pragma unroll
-        for (int c = 0; c < 9; ++c) acc2[c] = mfma4(cur.A2, cur.B2[c], acc2[c]);
-        if (w == kWgWaves - 1) {
-#pragma unroll
-            for (int c = 0; c < 5; ++c) acc3[c] = mfma4(cur.A3, cur.B3[c], acc3[c]);
-        }
-        cur = nxt;
+        if (more) wg_stage_store(s_op[buf ^ 1], v);
+        __syncthreads();
+        buf ^= 1;
     }
     // result element i of a tile: row 4 g + i, column n
     float* out = a.part + (int64_t)blockIdx.x * a.part_stride;
