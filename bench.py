@@ -254,8 +254,9 @@ PROFILE_COMMANDS = {
     "write": "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc_WRITE_SIZE_cfg{c} -o run --output-format csv "
              "-- python3 bench.py --config {c} --steps 8 --warmup 4 --no-cpu --no-graph --kernel-reps 8 "
              "--calibrate-copy",
-    "mfma": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES "
-            "GRBM_GUI_ACTIVE -d gpurun_out/pmc_MFMA_cfg{c} -o run --output-format csv "
+    "mfma": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+            "SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -d gpurun_out/pmc_MFMA_cfg{c} -o run "
+            "--output-format csv "
             "-- python3 bench.py --config {c} --steps 8 --warmup 4 --no-cpu --no-graph --kernel-reps 8",
     "lds": "rocprofv3 --pmc SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS GRBM_GUI_ACTIVE "
            "-d gpurun_out/pmc_LDS_cfg{c} -o run --output-format csv "
@@ -355,7 +356,7 @@ def profile_summary(root: str, c: int, workload: str) -> str:
     dur = {}
     for r in csv.DictReader(open(os.path.join(d["mfma"], "run_counter_collection.csv"))):
         k = _kernel_key(r["Kernel_Name"])
-        if k not in ("k_din_attn", "k_towers_bf16"):
+        if k not in ("k_din_attn", "k_towers_bf16", "k_dinb_fwd", "k_dinb_bwdt", "k_dinb_wgrad"):
             continue
         acc.setdefault(k, {}).setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
         dur.setdefault(k, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
@@ -363,8 +364,10 @@ def profile_summary(root: str, c: int, workload: str) -> str:
             "Means per dispatch.  One v_mfma_f32_16x16x32_bf16 counts 32 in SQ_INSTS_VALU_MFMA_MOPS_BF16",
             "(units of 512 flops) and 16 busy cycles in SQ_VALU_MFMA_BUSY_CYCLES (summed over SIMDs), so",
             "the busy fraction is busy / (1024 SIMDs x 2.4 GHz x duration); `warm` uses the warm leg's",
-            "mean duration above, `counted` the counter run's own (counter collection serialises",
-            "dispatches and lengthens them).  GRBM_GUI_ACTIVE is recorded as rocprofv3 reports it.", "",
+            "mean duration above (the counter run's own where the kernel is not in that leg), `counted`",
+            "the counter run's own (counter collection serialises dispatches and lengthens them).  The",
+            "attention backward's tiles (`k_dinb_*`) run fp32 products: their executed flops come from",
+            "SQ_INSTS_VALU_MFMA_MOPS_F32.  GRBM_GUI_ACTIVE is recorded as rocprofv3 reports it.", "",
             "| kernel | dispatches | executed GFLOP | busy cycles | SQ_BUSY_CYCLES | GRBM_GUI_ACTIVE | counted us | busy frac (counted) | busy frac (warm) |",
             "|---|---|---|---|---|---|---|---|---|"]
     for k, cn in acc.items():
@@ -372,9 +375,9 @@ def profile_summary(root: str, c: int, workload: str) -> str:
             v = list(cn.get(name, {}).values())
             return sum(v) / len(v) if v else float("nan")
         busy = mean("SQ_VALU_MFMA_BUSY_CYCLES")
-        mops = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        mops = mean("SQ_INSTS_VALU_MFMA_MOPS_F32" if k.startswith("k_dinb") else "SQ_INSTS_VALU_MFMA_MOPS_BF16")
         du = sum(dur[k].values()) / len(dur[k])
-        warm = statistics_mean(leg.get(k))
+        warm = statistics_mean(leg.get(k)) or du
         frac_c = busy / (SIMDS * CLOCK_HZ * du * 1e-6)
         frac_w = busy / (SIMDS * CLOCK_HZ * warm * 1e-6) if warm else float("nan")
         out.append(f"| {k} | {len(dur[k])} | {mops * 512 / 1e9:.3f} | {busy:.0f} | {mean('SQ_BUSY_CYCLES'):.0f} | "
